@@ -1,0 +1,193 @@
+/*
+ * poet.h -- C ABI of the MI355X (gfx950) POET reparameterized linear layer.
+ *
+ * The layer (POET pages: "Reparameterized LLM Training via Orthogonal Equivalence Transformation", the
+ * one-line method summary and the Approach section) keeps each weight as W = R * W0 * P, with W0 a fixed
+ * random m x n matrix (m = out features, n = in features) and R (m x m), P (n x n) learnable orthogonal
+ * factors. R and P are built from skew-symmetric generators Q by the truncated Cayley-Neumann series
+ *     R_k = (I + Q)(I + Q + Q^2 + ... + Q^k)
+ * ("Cayley-Neumann parameterization", Approach section; k = 0 keeps no term beyond the identity, the
+ * setting the "Measured effects" table reports as not converging). Each factor is made of primitives
+ * ("stochastic primitive optimization", Approach section):
+ *   POET-BS  block-diagonal primitives of size b (Key results: POET-BS with b = 256); when b does not
+ *            divide d the last block has size d mod b;
+ *   POET-FS  one dense s x s primitive acting on a sampled index set of s of the d indices, the identity
+ *            elsewhere (Key results: POET-FS with b = 1/2, i.e. s = d/2).
+ * The merge-then-reinitialize step (Approach section; the "Measured effects" table finds a period of 400
+ * steps best) folds R and P into W0, resets the generators to zero and, for POET-FS, samples fresh indices.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library never allocates device
+ *    memory. Scratch space comes from the caller's workspace `ws` of at least poet_workspace_bytes() bytes
+ *    (any alignment is accepted; the library aligns internally).
+ *  - Matrices are row-major. W0, W, the bf16 shadow and the weight-gradient use leading dimension ldw >= n;
+ *    X and dX use ldx >= n; Y and dY use ldy >= m (all in elements).
+ *  - Skew parameters theta (and gradients dtheta) are float32, packed per primitive as the strict upper
+ *    triangle in row-major order (0,1),(0,2),...,(c-2,c-1); Q_ij = theta_p, Q_ji = -theta_p. A side's
+ *    primitives are concatenated in order (BS: block 0 first).
+ *  - Primitives `prim` are float32, each stored as a bp x bp matrix (bp = b, or s for FS) padded with the
+ *    identity outside the leading c x c block of a short last BS block.
+ *  - Index sets are int32, strictly ascending, within [0, d). Invalid index sets (not ascending, out of
+ *    range, repeated) give unspecified numbers; gathers clamp every index into [0, d) so no access leaves
+ *    the caller's buffers.
+ *  - Every call is asynchronous on the caller's HIP stream (`stream` is a hipStream_t; NULL = default
+ *    stream) and never synchronizes. Arguments are validated on the host BEFORE anything is launched: on a
+ *    non-OK status nothing was enqueued and no output was touched. POET_E_HIP means a launch failed; the
+ *    stream's pending work is then undefined.
+ *  - Calls are reentrant; the only global state is a thread-local last-error message.
+ *  - Precision: act_dtype POET_F32 computes everything in float32 on fp32 MFMA. POET_BF16 feeds bf16
+ *    activations and a bf16 materialized W to bf16 MFMA with float32 accumulation; the factors are applied
+ *    as identity + delta so the identity part is added in float32. A side's dtype selects the operand type
+ *    of its power chain (the linear term 2Q is always added in float32). The merge is float32.
+ */
+#ifndef POET_H
+#define POET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POET_OK = 0,
+  POET_E_ARG = 1,         /* null pointer where one is required, or an out-of-range enum value */
+  POET_E_SHAPE = 2,       /* inconsistent or unsupported sizes / leading dimensions */
+  POET_E_DTYPE = 3,       /* unsupported dtype combination */
+  POET_E_WORKSPACE = 4,   /* ws_bytes smaller than poet_workspace_bytes() */
+  POET_E_HIP = 5,         /* a HIP launch or runtime call failed */
+  POET_E_UNSUPPORTED = 6  /* valid request this build does not implement */
+} poet_status;
+
+enum { POET_BS = 0, POET_FS = 1 };                 /* side modes */
+enum { POET_F32 = 0, POET_BF16 = 1 };              /* dtypes */
+enum { POET_SIDE_R = 0, POET_SIDE_P = 1 };         /* side ids used by the FS index sampler */
+enum { POET_OP_BUILD = 0, POET_OP_FWD = 1, POET_OP_BWD = 2, POET_OP_MERGE = 3 };
+
+/* Maximum supported Neumann terms and primitive size (a primitive must fit the kernels' tiling). */
+#define POET_MAX_K 16
+#define POET_MAX_PRIM 8192
+
+/* One orthogonal factor. mode: POET_BS or POET_FS. d: its dimension (m for R, n for P).
+ * b: BS block size (1 <= b <= d) or FS sample count s (1 <= s <= d). k: Neumann terms, 0 <= k <= POET_MAX_K.
+ * dtype: operand type of the power chain and of the saved powers (POET_F32 or POET_BF16). */
+typedef struct poet_side {
+  int32_t mode, d, b, k, dtype;
+} poet_side;
+
+/* One linear: W0 is m x n (out x in), X is T x n, Y is T x m. */
+typedef struct poet_layer {
+  int32_t m, n, T;
+  int32_t ldw, ldx, ldy;
+  int32_t act_dtype; /* POET_F32 or POET_BF16: type of X, Y, dY, dX, W and the W0 shadow */
+  poet_side R, P;    /* R.d must equal m and P.d must equal n */
+} poet_layer;
+
+/* ---- sizes (pure host functions; return 0 for an invalid side/layer) --------------------------------- */
+
+/* Number of packed skew parameters of a side: sum over primitives of c(c-1)/2. */
+size_t poet_theta_len(const poet_side* s);
+/* Number of primitives of a side: ceil(d/b) for BS, 1 for FS. */
+size_t poet_num_prims(const poet_side* s);
+/* Float32 elements of a side's primitive buffer: num_prims * bp * bp. */
+size_t poet_prim_len(const poet_side* s);
+/* Elements (of the side's dtype) of the saved powers Q^1..Q^k: k * prim_len (0 when k == 0). */
+size_t poet_powers_len(const poet_side* s);
+/* Workspace bytes a layer op needs (POET_OP_FWD, _BWD or _MERGE; POET_OP_BUILD gives 0, see
+ * poet_build_workspace_bytes). For POET_OP_FWD the figure assumes W_out == NULL, and for POET_OP_BWD that
+ * W == NULL (upper bounds). */
+size_t poet_workspace_bytes(const poet_layer* L, int op);
+/* Workspace bytes poet_sample_indices needs for dimension d. */
+size_t poet_sample_workspace_bytes(int32_t d);
+/* Workspace bytes poet_build_orthogonal needs: 0 when it is given a powers buffer or k == 0, otherwise
+ * room for the power chain (3 * prim_len elements of the side's dtype). */
+size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
+
+/* ---- the hot path ---------------------------------------------------------------------------------- */
+
+/* Build all primitives of one side from its skew parameters (truncated Cayley-Neumann series; Approach
+ * section of the POET pages).
+ *   theta  [poet_theta_len]  float32 in.
+ *   prim   [poet_prim_len]   float32 out: R_k = I + 2(Q + ... + Q^k) + Q^{k+1} per primitive, padded.
+ *   powers [poet_powers_len] out, side dtype, nullable: Q^1..Q^k of every primitive (power i of primitive
+ *          p at offset ((i-1)*num_prims + p)*bp*bp), needed by poet_linear_bwd when k >= 1.
+ *   qnorm  [num_prims]       float32 out, nullable: Frobenius norm of each primitive's Q. The series
+ *          converges for ||Q||_2 < 1; the pages warn it can diverge without enough terms (Limitations).
+ *   ws     at least poet_build_workspace_bytes(s, powers != NULL) bytes (may be NULL when that is 0). */
+poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float* prim, void* powers,
+                                  float* qnorm, void* ws, size_t ws_bytes, void* stream);
+
+/* Sample the FS index set of one side (the sampled sub-block of stochastic primitive optimization,
+ * Approach section; POET-FS with b = 1/2 in Key results). Counter-based: with SM one SplitMix64 output
+ * step (Steele, Lea and Flood, OOPSLA 2014), h = SM(SM(SM(SM(seed) ^ linear_id) ^ side) ^ epoch),
+ * key_i = SM(h ^ i); the s indices with the smallest (key_i, i) are written to idx [s] in ascending order.
+ * Bit-exact and deterministic. ws: at least poet_sample_workspace_bytes(d) bytes. */
+poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
+                                uint32_t epoch, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward of one POET linear (one-line method summary: W = R W0 P): materializes W (act dtype) and
+ * computes Y = X W^T.
+ *   W0     [m x ldw] float32 in.    primR/primP: built primitives of R and P (float32 in).
+ *   idxR/idxP: FS index sets [s] (int32 in); must be NULL for a BS side.
+ *   X      [T x ldx] act dtype in.  Y [T x ldy] act dtype out.
+ *   W_out  [m x ldw] act dtype out, nullable: keeps the materialized W (can be passed to the backward).
+ * T == 0 is allowed (only W is produced). */
+poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                            const int32_t* idxR, const int32_t* idxP, const void* X, void* Y, void* W_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one POET linear to its input and to the skew parameters: dX = dY W, the weight-space
+ * gradient G = dY^T X, the primitive blocks of dL/dR = G (W0 P)^T and dL/dP = (R W0)^T G, the Neumann
+ * adjoint and the skew projection d theta_p = dQ_ij - dQ_ji.
+ *   powersR/powersP: saved powers from poet_build_orthogonal (may be NULL when that side's k == 0).
+ *   W      [m x ldw] act dtype in, nullable: the W_out of the matching forward; recomputed when NULL.
+ *   X [T x ldx], dY [T x ldy] act dtype in.  dX [T x ldx] act dtype out, nullable (then not computed).
+ *   dthetaR [poet_theta_len(R)], dthetaP [poet_theta_len(P)] float32 out (overwritten, not accumulated). */
+poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                            const void* powersR, const void* powersP, const int32_t* idxR,
+                            const int32_t* idxP, const void* W, const void* X, const void* dY, void* dX,
+                            float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes, void* stream);
+
+/* Merge-then-reinitialize (Approach section; period 400 in the "Measured effects" table):
+ *   W0 <- R W0 P in float32 (in place), using the same truncated primitives the forward pass uses;
+ *   W0_shadow [m x ldw] act dtype out, nullable: a copy of the merged W0 in the act dtype;
+ *   thetaR, thetaP <- 0 (so R = P = I afterwards);
+ *   FS sides: idxR/idxP are read for the merge, then overwritten with the index set sampled for
+ *   (seed, linear_id, side, epoch_next). BS sides pass NULL index pointers. */
+poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* thetaR, float* thetaP,
+                       const float* primR, const float* primP, int32_t* idxR, int32_t* idxP, uint64_t seed,
+                       uint32_t linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- diagnostics ------------------------------------------------------------------------------------ */
+
+/* Kernel classes timed by the optional launch profiler. */
+enum {
+  POET_K_TOKEN_FWD = 0,  /* Y = X W^T */
+  POET_K_TOKEN_DX = 1,   /* dX = dY W */
+  POET_K_TOKEN_GW = 2,   /* G = dY^T X (the weight-space gradient) */
+  POET_K_CHAIN = 3,      /* Cayley-Neumann power chain */
+  POET_K_ADJOINT = 4,    /* Neumann adjoint */
+  POET_K_APPLY = 5,      /* applying R and P to W0 (materialize, merge) */
+  POET_K_CONTRACT = 6,   /* primitive-gradient contractions */
+  POET_K_MISC = 7,       /* packing, projection, gather/scatter, conversion, sampling */
+  POET_K_NCLASS = 8
+};
+/* Start (on != 0: clears previous records) or stop recording a HIP event pair around every kernel launch the
+ * library issues, on the launch's own stream. Process-wide; intended for benchmarking, adds one event pair
+ * per launch while on. */
+void poet_profile_enable(int on);
+/* Sum over the recorded launches of class kclass: launch count, total duration in ms (waits for the recorded
+ * events) and the algorithmic floating-point operations of those launches (2*M*N*K per GEMM; 0 for
+ * data-movement classes) and algorithmic bytes (operands read once, results written once).
+ * Returns POET_E_ARG for a bad class, POET_E_HIP if an event query fails. */
+poet_status poet_profile_query(int kclass, int64_t* launches, double* total_ms, double* flops, double* bytes);
+const char* poet_status_string(poet_status st);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* poet_last_error(void);
+const char* poet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POET_H */

@@ -1,0 +1,291 @@
+"""Thin ctypes binding of the POET C ABI (``include/poet.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of ``libpoet.so``. The functions
+carry the C names and take torch tensors that live on the GPU (torch provides device memory and the current
+HIP stream). Before each call the binding checks that every tensor is a contiguous device tensor of the
+expected dtype holding at least the bytes the call will touch, so that a wrong buffer becomes a Python
+exception instead of an out-of-bounds access. A missing library raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpoet.so")
+
+POET_OK, POET_E_ARG, POET_E_SHAPE, POET_E_DTYPE, POET_E_WORKSPACE, POET_E_HIP, POET_E_UNSUPPORTED = range(7)
+POET_BS, POET_FS = 0, 1
+POET_F32, POET_BF16 = 0, 1
+POET_SIDE_R, POET_SIDE_P = 0, 1
+POET_OP_BUILD, POET_OP_FWD, POET_OP_BWD, POET_OP_MERGE = range(4)
+POET_MAX_K, POET_MAX_PRIM = 16, 8192
+
+EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len", "poet_workspace_bytes",
+           "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
+           "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
+           "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query")
+POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
+    POET_K_MISC = range(8)
+KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc")
+
+
+class PoetError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class poet_side(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("d", ctypes.c_int32), ("b", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class poet_layer(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("T", ctypes.c_int32), ("ldw", ctypes.c_int32),
+                ("ldx", ctypes.c_int32), ("ldy", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("R", poet_side), ("P", poet_side)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpoet.so (built by ``orthogonal_reparameterized_amd.build``); raise when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"POET HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32, U32, U64, VP = (ctypes.POINTER, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64,
+                               ctypes.c_void_p)
+    for nm in ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len"):
+        getattr(L, nm).argtypes = [P(poet_side)]
+        getattr(L, nm).restype = S
+    L.poet_workspace_bytes.argtypes = [P(poet_layer), ctypes.c_int]
+    L.poet_workspace_bytes.restype = S
+    L.poet_sample_workspace_bytes.argtypes = [I32]
+    L.poet_sample_workspace_bytes.restype = S
+    L.poet_build_workspace_bytes.argtypes = [P(poet_side), ctypes.c_int]
+    L.poet_build_workspace_bytes.restype = S
+    L.poet_build_orthogonal.argtypes = [P(poet_side), VP, VP, VP, VP, VP, S, VP]
+    L.poet_sample_indices.argtypes = [I32, I32, U64, U32, U32, U32, VP, VP, S, VP]
+    L.poet_linear_fwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_merge.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, U64, U32, U32, VP, S, VP]
+    for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge"):
+        getattr(L, nm).restype = ctypes.c_int
+    L.poet_status_string.argtypes = [ctypes.c_int]
+    L.poet_status_string.restype = ctypes.c_char_p
+    L.poet_last_error.restype = ctypes.c_char_p
+    L.poet_version.restype = ctypes.c_char_p
+    L.poet_profile_enable.argtypes = [ctypes.c_int]
+    L.poet_profile_enable.restype = None
+    L.poet_profile_query.argtypes = [ctypes.c_int, P(ctypes.c_int64), P(ctypes.c_double), P(ctypes.c_double),
+                                     P(ctypes.c_double)]
+    L.poet_profile_query.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ---- structs -------------------------------------------------------------------------------------------
+
+def side(mode: int, d: int, b: int, k: int, dtype: int) -> poet_side:
+    return poet_side(mode, d, b, k, dtype)
+
+
+def side_of(spec) -> poet_side:
+    """poet_side from any object with mode, d, b, k, dtype attributes."""
+    return poet_side(spec.mode, spec.d, spec.b, spec.k, spec.dtype)
+
+
+def layer(m: int, n: int, T: int, R: poet_side, P: poet_side, act_dtype: int, ldw: Optional[int] = None,
+          ldx: Optional[int] = None, ldy: Optional[int] = None) -> poet_layer:
+    return poet_layer(m, n, T, ldw or n, ldx or n, ldy or m, act_dtype, R, P)
+
+
+# ---- sizes ---------------------------------------------------------------------------------------------
+
+def poet_theta_len(s: poet_side) -> int:
+    return lib().poet_theta_len(ctypes.byref(s))
+
+
+def poet_num_prims(s: poet_side) -> int:
+    return lib().poet_num_prims(ctypes.byref(s))
+
+
+def poet_prim_len(s: poet_side) -> int:
+    return lib().poet_prim_len(ctypes.byref(s))
+
+
+def poet_powers_len(s: poet_side) -> int:
+    return lib().poet_powers_len(ctypes.byref(s))
+
+
+def poet_workspace_bytes(L: poet_layer, op: int) -> int:
+    return lib().poet_workspace_bytes(ctypes.byref(L), op)
+
+
+def poet_sample_workspace_bytes(d: int) -> int:
+    return lib().poet_sample_workspace_bytes(d)
+
+
+def poet_build_workspace_bytes(s: poet_side, with_powers: bool) -> int:
+    return lib().poet_build_workspace_bytes(ctypes.byref(s), int(bool(with_powers)))
+
+
+def poet_status_string(st: int) -> str:
+    return lib().poet_status_string(st).decode()
+
+
+def poet_last_error() -> str:
+    return lib().poet_last_error().decode()
+
+
+def poet_version() -> str:
+    return lib().poet_version().decode()
+
+
+def poet_profile_enable(on: bool) -> None:
+    lib().poet_profile_enable(int(bool(on)))
+
+
+def poet_profile_query(kclass: int) -> dict:
+    n, ms, fl, by = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().poet_profile_query(kclass, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)),
+           "poet_profile_query")
+    return {"launches": n.value, "ms": ms.value, "flops": fl.value, "bytes": by.value}
+
+
+# ---- marshalling -------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt_name(dt: int) -> str:
+    return "bfloat16" if dt == POET_BF16 else "float32"
+
+
+def _ptr(t, name: str, nbytes: int, dtype: Optional[str] = None, allow_none: bool = False):
+    """Device pointer of tensor t after checking device, contiguity, dtype and size."""
+    if t is None:
+        if allow_none or nbytes == 0:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(st: int, where: str):
+    if st != POET_OK:
+        raise PoetError(st, where, f"{poet_status_string(st)}; {poet_last_error()}")
+
+
+def _esz(dt: int) -> int:
+    return 2 if dt == POET_BF16 else 4
+
+
+def _side_sizes(s: poet_side):
+    return poet_theta_len(s), poet_num_prims(s), poet_prim_len(s), poet_powers_len(s)
+
+
+# ---- calls ----------------------------------------------------------------------------------------------
+
+def poet_build_orthogonal(s: poet_side, theta, prim, powers=None, qnorm=None, ws=None, stream=None):
+    nth, npr, npl, npw = _side_sizes(s)
+    need_ws = poet_build_workspace_bytes(s, powers is not None)
+    st = lib().poet_build_orthogonal(
+        ctypes.byref(s), _ptr(theta, "theta", 4 * nth, "float32"), _ptr(prim, "prim", 4 * npl, "float32"),
+        _ptr(powers, "powers", npw * _esz(s.dtype), _dt_name(s.dtype), allow_none=True),
+        _ptr(qnorm, "qnorm", 4 * npr, "float32", allow_none=True), _ptr(ws, "ws", need_ws, allow_none=True),
+        need_ws if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_build_orthogonal")
+
+
+def poet_sample_indices(d: int, s: int, seed: int, linear_id: int, side_id: int, epoch: int, idx, ws,
+                        stream=None):
+    need = poet_sample_workspace_bytes(d)
+    st = lib().poet_sample_indices(d, s, seed, linear_id, side_id, epoch, _ptr(idx, "idx", 4 * s, "int32"),
+                                   _ptr(ws, "ws", need), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_sample_indices")
+
+
+def _layer_bytes(L: poet_layer):
+    e = _esz(L.act_dtype)
+    rowsz = lambda rows, ld, cols, es: 0 if rows == 0 else ((rows - 1) * ld + cols) * es  # noqa: E731
+    return {"W0": rowsz(L.m, L.ldw, L.n, 4), "W": rowsz(L.m, L.ldw, L.n, e), "X": rowsz(L.T, L.ldx, L.n, e),
+            "Y": rowsz(L.T, L.ldy, L.m, e)}
+
+
+def poet_linear_fwd(L: poet_layer, W0, primR, primP, idxR, idxP, X, Y, W_out=None, ws=None, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_FWD)
+    st = lib().poet_linear_fwd(
+        ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32", allow_none=True), _ptr(idxP, "idxP", 4 * L.P.b, "int32", allow_none=True),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Y, "Y", b["Y"], act, allow_none=L.T == 0),
+        _ptr(W_out, "W_out", b["W"], act, allow_none=True), _ptr(ws, "ws", need if W_out is None else 0, allow_none=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_fwd")
+
+
+def poet_linear_bwd(L: poet_layer, W0, primR, primP, powersR, powersP, idxR, idxP, W, X, dY, dX, dthetaR, dthetaP,
+                    ws=None, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_BWD)
+    st = lib().poet_linear_bwd(
+        ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(powersR, "powersR", poet_powers_len(L.R) * _esz(L.R.dtype), _dt_name(L.R.dtype), allow_none=True),
+        _ptr(powersP, "powersP", poet_powers_len(L.P) * _esz(L.P.dtype), _dt_name(L.P.dtype), allow_none=True),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32", allow_none=True), _ptr(idxP, "idxP", 4 * L.P.b, "int32", allow_none=True),
+        _ptr(W, "W", b["W"], act, allow_none=True),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dX, "dX", b["X"], act, allow_none=True),
+        _ptr(dthetaR, "dthetaR", 4 * poet_theta_len(L.R), "float32"),
+        _ptr(dthetaP, "dthetaP", 4 * poet_theta_len(L.P), "float32"),
+        _ptr(ws, "ws", need if W is None else 0, allow_none=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd")
+
+
+def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR, idxP, seed: int, linear_id: int,
+               epoch_next: int, ws=None, stream=None):
+    b = _layer_bytes(L)
+    need = poet_workspace_bytes(L, POET_OP_MERGE)
+    st = lib().poet_merge(
+        ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+        _ptr(W0_shadow, "W0_shadow", b["W"], _dt_name(L.act_dtype), allow_none=True),
+        _ptr(thetaR, "thetaR", 4 * poet_theta_len(L.R), "float32"),
+        _ptr(thetaP, "thetaP", 4 * poet_theta_len(L.P), "float32"),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32", allow_none=True), _ptr(idxP, "idxP", 4 * L.P.b, "int32", allow_none=True),
+        seed, linear_id, epoch_next, _ptr(ws, "ws", need, allow_none=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_merge")

@@ -1,0 +1,76 @@
+// Internal declarations shared by the library's translation units (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace poet {
+
+enum DType : int { F32 = 0, BF16 = 1 };
+
+__host__ __device__ inline size_t dtype_size(int dt) { return dt == BF16 ? 2 : 4; }
+
+// A batched GEMM  out = alpha * op(A) op(B) + beta * D ;  C <- out (if C) ;  Acc += gamma * out (if Acc).
+//   A is M x K: a_kmajor -> A(i,k) = A[i*lda + k] (row-major), else A(i,k) = A[k*lda + i].
+//   B is K x N: b_kmajor -> B(k,j) = B[j*ldb + k] (stored N x K), else B(k,j) = B[k*ldb + j].
+//   a_sub_eye / b_sub_eye subtract the identity from the (square-block) operand on load, so a factor
+//   F = I + dF is applied as its delta dF and the identity part is added in float32 through D.
+//   Batch z offsets every operand by its stride s*; with *tot > 0 the extent of batch z along that dimension
+//   is min(dim, tot - z*dim) (the short last block of a block-diagonal factor).
+//   compute selects the MFMA type: F32 -> v_mfma_f32_32x32x2_f32, BF16 -> v_mfma_f32_32x32x16_bf16 (operands
+//   rounded to bf16 when staged into LDS, float32 accumulation).
+struct GemmDesc {
+  int M = 0, N = 0, K = 0;
+  int Mtot = 0, Ntot = 0, Ktot = 0;
+  int batch = 1;
+  const void* A = nullptr; int64_t lda = 0, sA = 0; int a_dt = F32; int a_kmajor = 1; int a_sub_eye = 0;
+  const void* B = nullptr; int64_t ldb = 0, sB = 0; int b_dt = F32; int b_kmajor = 1; int b_sub_eye = 0;
+  void* C = nullptr; int64_t ldc = 0, sC = 0; int c_dt = F32;
+  const float* D = nullptr; int64_t ldd = 0, sD = 0;
+  float* Acc = nullptr; int64_t ldacc = 0, sAcc = 0;
+  float alpha = 1.f, beta = 0.f, gamma = 0.f;
+  int compute = F32;
+  int kclass = 7;  // profiler kernel class (POET_K_* in poet.h)
+};
+
+// launch profiler (profiler.hip): no-ops unless poet_profile_enable(1) was called
+int prof_begin(int kclass, hipStream_t st, double flops, double bytes);
+void prof_end(int rec, hipStream_t st);
+struct ProfScope {
+  int rec;
+  hipStream_t st;
+  ProfScope(int c, hipStream_t s, double f, double b) : rec(prof_begin(c, s, f, b)), st(s) {}
+  ~ProfScope() { prof_end(rec, st); }
+};
+
+hipError_t launch_gemm(const GemmDesc& g, hipStream_t st);
+
+// ---- elementwise / data-movement kernels (kernels_misc.hip) ------------------------------------------
+// theta -> prim = I + coef*Q (coef 1 for k = 0, else 2) and, when q_out != null, Q in dtype q_dt.
+hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim,
+                             void* q_out, int q_dt, hipStream_t st);
+hipError_t launch_qnorm(const float* theta, int mode, int d, int bp, int nprim, float* qnorm, hipStream_t st);
+// dtheta_p = X_ij - X_ji with X = dQ + G1 (G1 nullable) for i < j < c of every primitive.
+hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d, int bp, int nprim,
+                               float* dtheta, hipStream_t st);
+hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
+// dst (rows x cols, ld_dst, dtype dst_dt) <- src (float32, ld_src)
+hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows,
+                          int cols, hipStream_t st);
+// dst[r][j] = src[r][idx[j]]  (rows x s), src float32 with ld_src
+hipError_t launch_gather_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                              float* dst, int64_t ld_dst, hipStream_t st);
+// dst[r][idx[j]] = src[r][j]
+hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                               float* dst, int64_t ld_dst, hipStream_t st);
+// dst[i][c] = src[idx[i]][c]  (s x cols)
+hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
+                              int cols, float* dst, int64_t ld_dst, hipStream_t st);
+// dst[idx[i]][c] = src[i][c], dst of dtype dst_dt
+hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
+                               void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
+hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st);
+uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch);
+
+}  // namespace poet

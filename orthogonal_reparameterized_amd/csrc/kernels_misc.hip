@@ -1,0 +1,290 @@
+// Elementwise and data-movement kernels of the POET layer: skew packing, the skew projection of the
+// gradient, FS index gather/scatter, dtype conversion, and the counter-based FS index sampler.
+// All are memory-bound; threads walk the contiguous dimension so that every wavefront access is coalesced.
+#include "internal.h"
+
+namespace poet {
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid_for(size_t n, int per_block = kThreads, int cap = 65535 * 8) {
+  size_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)(g > (size_t)cap ? cap : g);
+}
+
+// size of primitive p of a side
+__device__ __forceinline__ int prim_size(int mode, int d, int bp, int p) {
+  return mode == 1 ? bp : min(bp, d - p * bp);
+}
+
+// packed position of (i, j), i < j < c, in row-major strict-upper order
+__device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
+  return (int64_t)i * c - (int64_t)i * (i + 1) / 2 + (j - i - 1);
+}
+
+// every primitive before p is a full bp x bp block
+__device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
+
+__global__ void k_theta_prep(const float* __restrict__ theta, int mode, int d, int bp, int nprim, float coef,
+                             float* __restrict__ prim, void* __restrict__ qout, int q_dt) {
+  const int64_t total = (int64_t)nprim * bp * bp;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(e / ((int64_t)bp * bp));
+    const int rem = (int)(e - (int64_t)p * bp * bp);
+    const int i = rem / bp, j = rem % bp;
+    const int c = prim_size(mode, d, bp, p);
+    float q = 0.f;
+    if (i < c && j < c && i != j) {
+      const int64_t off = theta_off(bp, p);
+      q = i < j ? theta[off + tri_pos(i, j, c)] : -theta[off + tri_pos(j, i, c)];
+    }
+    prim[e] = (i == j ? 1.f : 0.f) + coef * q;
+    if (qout) {
+      if (q_dt == BF16) reinterpret_cast<__bf16*>(qout)[e] = (__bf16)q;
+      else reinterpret_cast<float*>(qout)[e] = q;
+    }
+  }
+}
+
+__global__ void k_qnorm(const float* __restrict__ theta, int mode, int d, int bp, float* __restrict__ qnorm) {
+  __shared__ float red[kThreads];
+  const int p = blockIdx.x;
+  const int c = prim_size(mode, d, bp, p);
+  const int64_t off = theta_off(bp, p), n = (int64_t)c * (c - 1) / 2;
+  float s = 0.f;
+  for (int64_t t = threadIdx.x; t < n; t += kThreads) {
+    const float v = theta[off + t];
+    s += v * v;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) qnorm[p] = sqrtf(2.f * red[0]);
+}
+
+__global__ void k_skew_project(const float* __restrict__ dQ, const float* __restrict__ G1, int mode, int d,
+                               int bp, int nprim, float* __restrict__ dtheta) {
+  const int64_t total = (int64_t)nprim * bp * bp;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(e / ((int64_t)bp * bp));
+    const int rem = (int)(e - (int64_t)p * bp * bp);
+    const int i = rem / bp, j = rem % bp;
+    const int c = prim_size(mode, d, bp, p);
+    if (i < j && j < c) {
+      const int64_t base = (int64_t)p * bp * bp;
+      const int64_t ij = base + (int64_t)i * bp + j, ji = base + (int64_t)j * bp + i;
+      float a = dQ[ij], b = dQ[ji];
+      if (G1) { a += G1[ij]; b += G1[ji]; }
+      dtheta[theta_off(bp, p) + tri_pos(i, j, c)] = a - b;
+    }
+  }
+}
+
+__global__ void k_fill(float* __restrict__ p, size_t n, float v) {
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) p[e] = v;
+}
+
+__global__ void k_convert(const float* __restrict__ src, int64_t ld_src, void* __restrict__ dst, int64_t ld_dst,
+                          int dst_dt, int rows, int cols) {
+  for (int r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
+      const float v = src[(int64_t)r * ld_src + c];
+      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + c] = (__bf16)v;
+      else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + c] = v;
+    }
+}
+
+__device__ __forceinline__ int clampi(int v, int lim) { return v < 0 ? 0 : (v >= lim ? lim - 1 : v); }
+
+__global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
+                              int s, int dlim, float* __restrict__ dst, int64_t ld_dst) {
+  for (int r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x)
+      dst[(int64_t)r * ld_dst + j] = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
+}
+
+__global__ void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
+                               int s, int dlim, float* __restrict__ dst, int64_t ld_dst) {
+  for (int r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x)
+      dst[(int64_t)r * ld_dst + clampi(idx[j], dlim)] = src[(int64_t)r * ld_src + j];
+}
+
+__global__ void k_gather_rows(const void* __restrict__ src, int src_dt, int64_t ld_src, const int32_t* __restrict__ idx,
+                              int s, int dlim, int cols, float* __restrict__ dst, int64_t ld_dst) {
+  for (int i = blockIdx.y; i < s; i += gridDim.y) {
+    const int64_t row = (int64_t)clampi(idx[i], dlim) * ld_src;
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
+      const float v = src_dt == BF16 ? (float)reinterpret_cast<const __bf16*>(src)[row + c]
+                                     : reinterpret_cast<const float*>(src)[row + c];
+      dst[(int64_t)i * ld_dst + c] = v;
+    }
+  }
+}
+
+__global__ void k_scatter_rows(const float* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ idx, int s,
+                               int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
+  for (int i = blockIdx.y; i < s; i += gridDim.y) {
+    const int64_t row = (int64_t)clampi(idx[i], dlim) * ld_dst;
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
+      const float v = src[(int64_t)i * ld_src + c];
+      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[row + c] = (__bf16)v;
+      else reinterpret_cast<float*>(dst)[row + c] = v;
+    }
+  }
+}
+
+// ---- counter-based index sampler -------------------------------------------------------------------------
+// SplitMix64 output step (Steele, Lea and Flood, OOPSLA 2014): advance by the golden gamma and finalize.
+__host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// flags[i] = 1 when fewer than s indices j have (key_j, j) < (key_i, i)
+__global__ void k_sample_rank(int d, int s, uint64_t h, int32_t* __restrict__ flags) {
+  __shared__ uint64_t kj[kThreads];
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  const uint64_t ki = splitmix64(h ^ (uint64_t)(i < d ? i : 0));
+  int rank = 0;
+  for (int j0 = 0; j0 < d; j0 += kThreads) {
+    const int j = j0 + threadIdx.x;
+    kj[threadIdx.x] = j < d ? splitmix64(h ^ (uint64_t)j) : 0ull;
+    __syncthreads();
+    const int jn = min(kThreads, d - j0);
+    for (int t = 0; t < jn; ++t) {
+      const uint64_t kv = kj[t];
+      const int jj = j0 + t;
+      rank += (kv < ki) || (kv == ki && jj < i);
+    }
+    __syncthreads();
+  }
+  if (i < d) flags[i] = rank < s ? 1 : 0;
+}
+
+// one workgroup: stream compaction of the flagged indices in ascending order
+__global__ void k_sample_compact(int d, const int32_t* __restrict__ flags, int32_t* __restrict__ idx) {
+  constexpr int NT = 1024;
+  __shared__ int sc[NT];
+  int base = 0;
+  for (int c0 = 0; c0 < d; c0 += NT) {
+    const int i = c0 + threadIdx.x;
+    const int f = i < d ? flags[i] : 0;
+    sc[threadIdx.x] = f;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int v = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+      __syncthreads();
+      sc[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (f) idx[base + sc[threadIdx.x] - 1] = i;
+    const int tot = sc[NT - 1];
+    __syncthreads();
+    base += tot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim, void* q_out,
+                             int q_dt, hipStream_t st) {
+  const size_t total = (size_t)nprim * bp * bp;
+  ProfScope prof(7, st, 0, (double)total * (4 + 4 + (q_out ? dtype_size(q_dt) : 0)));
+  hipLaunchKernelGGL(k_theta_prep, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim,
+                     k == 0 ? 1.f : 2.f, prim, q_out, q_dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_qnorm(const float* theta, int mode, int d, int bp, int nprim, float* qnorm, hipStream_t st) {
+  ProfScope prof(7, st, 0, (double)nprim * bp * (bp - 1) * 2.0);
+  hipLaunchKernelGGL(k_qnorm, dim3(nprim), dim3(kThreads), 0, st, theta, mode, d, bp, qnorm);
+  return hipGetLastError();
+}
+
+hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d, int bp, int nprim, float* dtheta,
+                               hipStream_t st) {
+  const size_t total = (size_t)nprim * bp * bp;
+  ProfScope prof(7, st, 0, (double)total * (G1 ? 8 : 4) + (double)total * 2);
+  hipLaunchKernelGGL(k_skew_project, dim3(grid_for(total)), dim3(kThreads), 0, st, dQ, G1, mode, d, bp, nprim, dtheta);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)n * 4);
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(n)), dim3(kThreads), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+static dim3 row_grid(int cols, int rows) { return dim3((cols + kThreads - 1) / kThreads, rows < 65535 ? rows : 65535); }
+
+hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows, int cols,
+                          hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)rows * cols * (4 + dtype_size(dst_dt)));
+  hipLaunchKernelGGL(k_convert, row_grid(cols, rows), dim3(kThreads), 0, st, src, ld_src, dst, ld_dst, dst_dt, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim, float* dst,
+                              int64_t ld_dst, hipStream_t st) {
+  if (rows <= 0 || s <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)rows * s * 8);
+  hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                               float* dst, int64_t ld_dst, hipStream_t st) {
+  if (rows <= 0 || s <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)rows * s * 8);
+  hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
+                              float* dst, int64_t ld_dst, hipStream_t st) {
+  if (s <= 0 || cols <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)s * cols * (4 + dtype_size(src_dt)));
+  hipLaunchKernelGGL(k_gather_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, src_dt, ld_src, idx, s, dlim, cols,
+                     dst, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols, void* dst,
+                               int dst_dt, int64_t ld_dst, hipStream_t st) {
+  if (s <= 0 || cols <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)s * cols * (4 + dtype_size(dst_dt)));
+  hipLaunchKernelGGL(k_scatter_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, ld_src, idx, s, dlim, cols, dst,
+                     dst_dt, ld_dst);
+  return hipGetLastError();
+}
+
+uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch) {
+  uint64_t h = splitmix64(seed);
+  h = splitmix64(h ^ (uint64_t)linear_id);
+  h = splitmix64(h ^ (uint64_t)side);
+  return splitmix64(h ^ (uint64_t)epoch);
+}
+
+hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st) {
+  if (d <= 0 || s <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)d * 4 + (double)s * 4);
+  hipLaunchKernelGGL(k_sample_rank, dim3((d + kThreads - 1) / kThreads), dim3(kThreads), 0, st, d, s, h, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sample_compact, dim3(1), dim3(1024), 0, st, d, flags, idx);
+  return hipGetLastError();
+}
+
+}  // namespace poet

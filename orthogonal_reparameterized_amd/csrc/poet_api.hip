@@ -1,0 +1,538 @@
+// C ABI of the POET layer: host-side validation, workspace planning and the launch sequence of each call.
+// Nothing here computes on the host; every step of the method runs in the kernels of this library.
+#include <cstdarg>
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "../../include/poet.h"
+#include "internal.h"
+
+using namespace poet;
+
+namespace {
+
+thread_local std::string g_err;
+thread_local poet_status g_last = POET_OK;
+
+poet_status fail(poet_status st, const char* fmt, ...) {
+  g_last = st;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                        \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) return fail(POET_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+struct SideInfo {
+  int mode = 0, d = 0, bp = 0, nprim = 0, k = 0, dtype = 0;
+  size_t theta_len = 0, prim_len = 0, powers_len = 0;
+};
+
+bool side_info(const poet_side* s, SideInfo* o, const char* name) {
+  if (!s) return fail(POET_E_ARG, "%s: null side", name), false;
+  if (s->mode != POET_BS && s->mode != POET_FS) return fail(POET_E_ARG, "%s: bad mode %d", name, s->mode), false;
+  if (s->dtype != POET_F32 && s->dtype != POET_BF16) return fail(POET_E_DTYPE, "%s: bad dtype %d", name, s->dtype), false;
+  if (s->d < 1) return fail(POET_E_SHAPE, "%s: d = %d must be >= 1", name, s->d), false;
+  if (s->b < 1 || s->b > s->d) return fail(POET_E_SHAPE, "%s: b = %d must be in [1, d = %d]", name, s->b, s->d), false;
+  if (s->b > POET_MAX_PRIM) return fail(POET_E_UNSUPPORTED, "%s: primitive size %d > %d", name, s->b, POET_MAX_PRIM), false;
+  if (s->k < 0 || s->k > POET_MAX_K) return fail(POET_E_SHAPE, "%s: k = %d must be in [0, %d]", name, s->k, POET_MAX_K), false;
+  o->mode = s->mode; o->d = s->d; o->bp = s->b; o->k = s->k; o->dtype = s->dtype;
+  o->nprim = s->mode == POET_FS ? 1 : (s->d + s->b - 1) / s->b;
+  size_t th = 0;
+  for (int p = 0; p < o->nprim; ++p) {
+    const size_t c = s->mode == POET_FS ? (size_t)s->b : (size_t)std::min(s->b, s->d - p * s->b);
+    th += c * (c - 1) / 2;
+  }
+  o->theta_len = th;
+  o->prim_len = (size_t)o->nprim * o->bp * o->bp;
+  o->powers_len = (size_t)o->k * o->prim_len;
+  return true;
+}
+
+bool layer_info(const poet_layer* L, SideInfo* R, SideInfo* P) {
+  if (!L) return fail(POET_E_ARG, "null layer"), false;
+  if (L->m < 1 || L->n < 1) return fail(POET_E_SHAPE, "m = %d and n = %d must be >= 1", L->m, L->n), false;
+  if (L->T < 0) return fail(POET_E_SHAPE, "T = %d must be >= 0", L->T), false;
+  if (L->ldw < L->n || L->ldx < L->n || L->ldy < L->m)
+    return fail(POET_E_SHAPE, "leading dims ldw=%d ldx=%d ldy=%d too small for m=%d n=%d", L->ldw, L->ldx, L->ldy, L->m,
+                L->n), false;
+  if (L->act_dtype != POET_F32 && L->act_dtype != POET_BF16)
+    return fail(POET_E_DTYPE, "bad act_dtype %d", L->act_dtype), false;
+  if (L->m > 65535 * 64 || L->n > 65535 * 64 || L->T > 65535 * 64)
+    return fail(POET_E_UNSUPPORTED, "dimension beyond the kernels' grid limits"), false;
+  if (!side_info(&L->R, R, "R") || !side_info(&L->P, P, "P")) return false;
+  if (R->d != L->m) return fail(POET_E_SHAPE, "R.d = %d must equal m = %d", R->d, L->m), false;
+  if (P->d != L->n) return fail(POET_E_SHAPE, "P.d = %d must equal n = %d", P->d, L->n), false;
+  return true;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only measures.
+struct Arena {
+  char* base;
+  size_t off = 0;
+  explicit Arena(void* b) : base(reinterpret_cast<char*>(b)) {
+    if (base) {  // align the first block
+      const uintptr_t u = reinterpret_cast<uintptr_t>(base);
+      off = align_up(u, 256) - u;
+    }
+  }
+  template <class T>
+  T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  void* take_bytes(size_t bytes) { return take<char>(bytes); }
+  size_t used() const { return off + 256; }  // slack for the initial alignment
+};
+
+// ------------------------------------------------------------------------------------------------------------
+// Applying a factor. apply_P: T = W0 P (float32 out). apply_R: out = R src (src float32, out dtype out_dt).
+// BS: one batched GEMM over the blocks, identity + delta (the delta is the primitive minus I, the identity part
+// is the float32 addend). FS: gather the sampled columns/rows, GEMM with the primitive's delta, scatter back.
+// ------------------------------------------------------------------------------------------------------------
+struct FsBufs {
+  float *Ac = nullptr, *C1 = nullptr;  // m x sP
+  float *Br = nullptr, *C2 = nullptr;  // sR x n
+};
+
+void plan_fs(Arena& a, const poet_layer& L, const SideInfo& R, const SideInfo& P, FsBufs* f) {
+  if (P.mode == POET_FS) { f->Ac = a.take<float>((size_t)L.m * P.bp); f->C1 = a.take<float>((size_t)L.m * P.bp); }
+  if (R.mode == POET_FS) { f->Br = a.take<float>((size_t)R.bp * L.n); f->C2 = a.take<float>((size_t)R.bp * L.n); }
+}
+
+hipError_t apply_P(const poet_layer& L, const SideInfo& P, const float* W0, const float* prim, const int32_t* idx,
+                   float* T, int compute, const FsBufs& f, hipStream_t st) {
+  const int m = L.m, n = L.n;
+  GemmDesc g;
+  g.compute = compute;
+  g.kclass = POET_K_APPLY;
+  if (P.mode == POET_BS) {
+    g.M = m; g.N = P.bp; g.K = P.bp; g.Ntot = n; g.Ktot = n; g.batch = P.nprim;
+    g.A = W0; g.lda = L.ldw; g.sA = P.bp; g.a_dt = F32; g.a_kmajor = 1;
+    g.B = prim; g.ldb = P.bp; g.sB = (int64_t)P.bp * P.bp; g.b_dt = F32; g.b_kmajor = 0; g.b_sub_eye = 1;
+    g.D = W0; g.ldd = L.ldw; g.sD = P.bp; g.beta = 1.f;
+    g.C = T; g.ldc = L.ldw; g.sC = P.bp; g.c_dt = F32;
+    return launch_gemm(g, st);
+  }
+  const int s = P.bp;
+  hipError_t e = launch_gather_cols(W0, L.ldw, m, idx, s, n, f.Ac, s, st);
+  if (e != hipSuccess) return e;
+  g.M = m; g.N = s; g.K = s;
+  g.A = f.Ac; g.lda = s; g.a_dt = F32; g.a_kmajor = 1;
+  g.B = prim; g.ldb = s; g.b_dt = F32; g.b_kmajor = 0; g.b_sub_eye = 1;
+  g.D = f.Ac; g.ldd = s; g.beta = 1.f;
+  g.C = f.C1; g.ldc = s; g.c_dt = F32;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  if ((e = launch_convert(W0, L.ldw, T, L.ldw, F32, m, n, st)) != hipSuccess) return e;
+  return launch_scatter_cols(f.C1, s, m, idx, s, n, T, L.ldw, st);
+}
+
+hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, const float* prim, const int32_t* idx,
+                   void* out, int out_dt, int64_t ldo, int compute, const FsBufs& f, hipStream_t st) {
+  const int m = L.m, n = L.n;
+  GemmDesc g;
+  g.compute = compute;
+  g.kclass = POET_K_APPLY;
+  if (R.mode == POET_BS) {
+    g.M = R.bp; g.N = n; g.K = R.bp; g.Mtot = m; g.Ktot = m; g.batch = R.nprim;
+    g.A = prim; g.lda = R.bp; g.sA = (int64_t)R.bp * R.bp; g.a_dt = F32; g.a_kmajor = 1; g.a_sub_eye = 1;
+    g.B = src; g.ldb = L.ldw; g.sB = (int64_t)R.bp * L.ldw; g.b_dt = F32; g.b_kmajor = 0;
+    g.D = src; g.ldd = L.ldw; g.sD = (int64_t)R.bp * L.ldw; g.beta = 1.f;
+    g.C = out; g.ldc = ldo; g.sC = (int64_t)R.bp * ldo; g.c_dt = out_dt;
+    return launch_gemm(g, st);
+  }
+  const int s = R.bp;
+  hipError_t e = launch_gather_rows(src, F32, L.ldw, idx, s, m, n, f.Br, n, st);
+  if (e != hipSuccess) return e;
+  g.M = s; g.N = n; g.K = s;
+  g.A = prim; g.lda = s; g.a_dt = F32; g.a_kmajor = 1; g.a_sub_eye = 1;
+  g.B = f.Br; g.ldb = n; g.b_dt = F32; g.b_kmajor = 0;
+  g.D = f.Br; g.ldd = n; g.beta = 1.f;
+  g.C = f.C2; g.ldc = n; g.c_dt = F32;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  if ((e = launch_convert(src, L.ldw, out, ldo, out_dt, m, n, st)) != hipSuccess) return e;
+  return launch_scatter_rows(f.C2, n, idx, s, m, n, out, out_dt, ldo, st);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Backward through the truncated Cayley-Neumann series of one side, then the skew projection.
+// With R_k = I + sum_i a_i Q^i (a_i = 2 for i <= k, a_{k+1} = 1) and saved powers P_i = Q^i, the reverse
+// recursion G_{k+1} = dR, G_{i-1} = a_{i-1} dR + Q^T G_i, dQ = G_1 + sum_{i>=2} G_i P_{i-1}^T
+// uses Q^T = -Q and P_i^T = (-1)^i P_i, so every product is a plain row-major GEMM.
+// ------------------------------------------------------------------------------------------------------------
+struct AdjBufs {
+  float *dQ = nullptr, *Ga = nullptr, *Gb = nullptr;
+};
+
+hipError_t neumann_adjoint(const SideInfo& S, const float* dRb, const void* powers, float* dtheta, const AdjBufs& b,
+                           hipStream_t st) {
+  if (S.theta_len == 0) return hipSuccess;
+  if (S.k == 0) return launch_skew_project(dRb, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+  const int64_t pp = (int64_t)S.bp * S.bp;
+  const size_t esz = dtype_size(S.dtype);
+  const char* pw = reinterpret_cast<const char*>(powers);
+  const float* Gcur = dRb;
+  float* bufs[2] = {b.Ga, b.Gb};
+  int nb = 0;
+  hipError_t e;
+  for (int i = S.k + 1; i >= 2; --i) {
+    GemmDesc g;  // dQ (+)= (-1)^(i-1) G_i P_{i-1}
+    g.kclass = POET_K_ADJOINT;
+    g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
+    g.A = Gcur; g.lda = S.bp; g.sA = pp; g.a_dt = F32; g.a_kmajor = 1;
+    g.B = pw + (size_t)(i - 2) * S.prim_len * esz; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
+    g.alpha = ((i - 1) & 1) ? -1.f : 1.f;
+    if (i != S.k + 1) { g.D = b.dQ; g.ldd = S.bp; g.sD = pp; g.beta = 1.f; }
+    g.C = b.dQ; g.ldc = S.bp; g.sC = pp; g.c_dt = F32;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    GemmDesc h;  // G_{i-1} = 2 dR - Q G_i
+    h.kclass = POET_K_ADJOINT;
+    h.compute = S.dtype; h.M = h.N = h.K = S.bp; h.batch = S.nprim;
+    h.A = pw; h.lda = S.bp; h.sA = pp; h.a_dt = S.dtype; h.a_kmajor = 1;
+    h.B = Gcur; h.ldb = S.bp; h.sB = pp; h.b_dt = F32; h.b_kmajor = 0;
+    h.alpha = -1.f; h.D = dRb; h.ldd = S.bp; h.sD = pp; h.beta = 2.f;
+    h.C = bufs[nb]; h.ldc = S.bp; h.sC = pp; h.c_dt = F32;
+    if ((e = launch_gemm(h, st)) != hipSuccess) return e;
+    Gcur = bufs[nb];
+    nb ^= 1;
+  }
+  return launch_skew_project(b.dQ, Gcur, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Workspace plans (the same code sizes and carves the workspace)
+// ------------------------------------------------------------------------------------------------------------
+struct FwdPlan {
+  void* W = nullptr;
+  float* T = nullptr;
+  FsBufs fs;
+};
+size_t plan_fwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, bool need_W, FwdPlan* p) {
+  Arena a(ws);
+  if (need_W) p->W = a.take_bytes((size_t)L.m * L.ldw * dtype_size(L.act_dtype));
+  p->T = a.take<float>((size_t)L.m * L.ldw);
+  plan_fs(a, L, R, P, &p->fs);
+  return a.used();
+}
+
+struct BwdPlan {
+  void* W = nullptr;
+  float *T = nullptr, *RW0 = nullptr, *G = nullptr, *dRb = nullptr, *dPb = nullptr;
+  AdjBufs adj;
+  FsBufs fs;
+  float *Gr = nullptr, *Zr = nullptr, *Acp = nullptr, *Gc = nullptr;
+};
+size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, bool need_W, BwdPlan* p) {
+  Arena a(ws);
+  const size_t mn = (size_t)L.m * L.ldw;
+  if (need_W) p->W = a.take_bytes(mn * dtype_size(L.act_dtype));
+  p->T = a.take<float>(mn);
+  p->RW0 = a.take<float>(mn);
+  p->G = a.take<float>(mn);
+  p->dRb = a.take<float>(R.prim_len);
+  p->dPb = a.take<float>(P.prim_len);
+  const size_t pl = std::max(R.prim_len, P.prim_len);
+  p->adj.dQ = a.take<float>(pl);
+  p->adj.Ga = a.take<float>(pl);
+  p->adj.Gb = a.take<float>(pl);
+  plan_fs(a, L, R, P, &p->fs);
+  if (R.mode == POET_FS) { p->Gr = a.take<float>((size_t)R.bp * L.n); p->Zr = a.take<float>((size_t)R.bp * L.n); }
+  if (P.mode == POET_FS) { p->Acp = a.take<float>((size_t)L.m * P.bp); p->Gc = a.take<float>((size_t)L.m * P.bp); }
+  return a.used();
+}
+
+struct MergePlan {
+  float *T = nullptr, *Wn = nullptr;
+  int32_t* flags = nullptr;
+  FsBufs fs;
+};
+size_t plan_merge(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, MergePlan* p) {
+  Arena a(ws);
+  const size_t mn = (size_t)L.m * L.ldw;
+  p->T = a.take<float>(mn);
+  p->Wn = a.take<float>(mn);
+  plan_fs(a, L, R, P, &p->fs);
+  if (R.mode == POET_FS || P.mode == POET_FS) p->flags = a.take<int32_t>((size_t)std::max(L.m, L.n));
+  return a.used();
+}
+
+bool check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) return fail(POET_E_WORKSPACE, "workspace of %zu bytes < %zu needed", have, need), false;
+  if (!ws && need > 0) return fail(POET_E_ARG, "null workspace"), false;
+  return true;
+}
+
+bool check_idx(const SideInfo& S, const void* idx, const char* name) {
+  if (S.mode == POET_FS && !idx) return fail(POET_E_ARG, "%s: FS side needs an index set", name), false;
+  if (S.mode == POET_BS && idx) return fail(POET_E_ARG, "%s: BS side takes no index set", name), false;
+  return true;
+}
+
+}  // namespace
+
+// ============================================================================================================
+extern "C" {
+
+size_t poet_theta_len(const poet_side* s) {
+  SideInfo i;
+  return side_info(s, &i, "side") ? i.theta_len : 0;
+}
+size_t poet_num_prims(const poet_side* s) {
+  SideInfo i;
+  return side_info(s, &i, "side") ? (size_t)i.nprim : 0;
+}
+size_t poet_prim_len(const poet_side* s) {
+  SideInfo i;
+  return side_info(s, &i, "side") ? i.prim_len : 0;
+}
+size_t poet_powers_len(const poet_side* s) {
+  SideInfo i;
+  return side_info(s, &i, "side") ? i.powers_len : 0;
+}
+size_t poet_build_workspace_bytes(const poet_side* s, int with_powers) {
+  SideInfo i;
+  if (!side_info(s, &i, "side")) return 0;
+  if (with_powers || i.k == 0) return 0;
+  return 3 * align_up(i.prim_len * dtype_size(i.dtype), 256) + 256;
+}
+size_t poet_sample_workspace_bytes(int32_t d) { return d > 0 ? align_up((size_t)d * 4, 256) + 256 : 0; }
+
+size_t poet_workspace_bytes(const poet_layer* L, int op) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return 0;
+  switch (op) {
+    case POET_OP_BUILD: return 0;
+    case POET_OP_FWD: { FwdPlan p; return plan_fwd(*L, R, P, nullptr, true, &p); }
+    case POET_OP_BWD: { BwdPlan p; return plan_bwd(*L, R, P, nullptr, true, &p); }
+    case POET_OP_MERGE: { MergePlan p; return plan_merge(*L, R, P, nullptr, &p); }
+    default: fail(POET_E_ARG, "bad op %d", op); return 0;
+  }
+}
+
+poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float* prim, void* powers, float* qnorm,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  SideInfo S;
+  if (!side_info(s, &S, "side")) return g_last;
+  if (!prim) return fail(POET_E_ARG, "null prim");
+  if (!theta && S.theta_len > 0) return fail(POET_E_ARG, "null theta");
+  const size_t need = poet_build_workspace_bytes(s, powers != nullptr);
+  if (!check_ws(ws, ws_bytes, need)) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t esz = dtype_size(S.dtype);
+  char* pw = reinterpret_cast<char*>(powers);
+  char* scratch[3] = {nullptr, nullptr, nullptr};
+  if (!powers && S.k > 0) {
+    Arena a(ws);
+    for (int i = 0; i < 3; ++i) scratch[i] = reinterpret_cast<char*>(a.take_bytes(S.prim_len * esz));
+  }
+  const char* Qp = powers ? pw : scratch[0];
+  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)Qp : nullptr, S.dtype, st));
+  if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
+  const int64_t pp = (int64_t)S.bp * S.bp;
+  for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i ; prim += a_{i+1} P_{i+1}
+    GemmDesc g;
+    g.kclass = POET_K_CHAIN;
+    g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
+    g.A = Qp; g.lda = S.bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
+    const char* Pi = powers ? pw + (size_t)(i - 1) * S.prim_len * esz : (i == 1 ? scratch[0] : scratch[1 + (i & 1)]);
+    g.B = Pi; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
+    if (i + 1 <= S.k) {
+      g.C = powers ? (void*)(pw + (size_t)i * S.prim_len * esz) : (void*)scratch[1 + ((i + 1) & 1)];
+      g.ldc = S.bp; g.sC = pp; g.c_dt = S.dtype;
+    }
+    g.Acc = prim; g.ldacc = S.bp; g.sAcc = pp; g.gamma = (i + 1 <= S.k) ? 2.f : 1.f;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  return POET_OK;
+}
+
+poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
+                                uint32_t epoch, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (d < 1 || s < 0 || s > d) return fail(POET_E_SHAPE, "need d >= 1 and 0 <= s <= d (d=%d s=%d)", d, s);
+  if (!idx && s > 0) return fail(POET_E_ARG, "null idx");
+  if (!check_ws(ws, ws_bytes, poet_sample_workspace_bytes(d))) return g_last;
+  Arena a(ws);
+  int32_t* flags = a.take<int32_t>((size_t)d);
+  HIP_TRY(launch_sample(d, s, sampler_hash(seed, linear_id, side, epoch), flags, idx,
+                        reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
+poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                            const int32_t* idxR, const int32_t* idxP, const void* X, void* Y, void* W_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!W0 || !primR || !primP) return fail(POET_E_ARG, "null W0 or primitive");
+  if (L->T > 0 && (!X || !Y)) return fail(POET_E_ARG, "null X or Y");
+  if (!check_idx(R, idxR, "R") || !check_idx(P, idxP, "P")) return g_last;
+  FwdPlan p;
+  const size_t need = plan_fwd(*L, R, P, nullptr, W_out == nullptr, &p);
+  if (!check_ws(ws, ws_bytes, need)) return g_last;
+  plan_fwd(*L, R, P, ws, W_out == nullptr, &p);
+  void* W = W_out ? W_out : p.W;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int act = L->act_dtype;
+  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
+  HIP_TRY(apply_R(*L, R, p.T, primR, idxR, W, act, L->ldw, act, p.fs, st));
+  if (L->T > 0) {  // Y = X W^T
+    GemmDesc g;
+    g.kclass = POET_K_TOKEN_FWD;
+    g.compute = act; g.M = L->T; g.N = L->m; g.K = L->n;
+    g.A = X; g.lda = L->ldx; g.a_dt = act; g.a_kmajor = 1;
+    g.B = W; g.ldb = L->ldw; g.b_dt = act; g.b_kmajor = 1;
+    g.C = Y; g.ldc = L->ldy; g.c_dt = act;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  return POET_OK;
+}
+
+poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                            const void* powersR, const void* powersP, const int32_t* idxR, const int32_t* idxP,
+                            const void* Win, const void* X, const void* dY, void* dX, float* dthetaR, float* dthetaP,
+                            void* ws, size_t ws_bytes, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!W0 || !primR || !primP) return fail(POET_E_ARG, "null W0 or primitive");
+  if (L->T > 0 && (!X || !dY)) return fail(POET_E_ARG, "null X or dY");
+  if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
+  if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
+    return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  if (!check_idx(R, idxR, "R") || !check_idx(P, idxP, "P")) return g_last;
+  BwdPlan p;
+  const size_t need = plan_bwd(*L, R, P, nullptr, Win == nullptr, &p);
+  if (!check_ws(ws, ws_bytes, need)) return g_last;
+  plan_bwd(*L, R, P, ws, Win == nullptr, &p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int act = L->act_dtype, m = L->m, n = L->n;
+  const int64_t ldw = L->ldw;
+  // Z = W0 P (needed by the R-side gradient) and, when not given, W = R Z
+  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
+  const void* W = Win;
+  if (!W) {
+    HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.W, act, ldw, act, p.fs, st));
+    W = p.W;
+  }
+  // R W0 (needed by the P-side gradient)
+  HIP_TRY(apply_R(*L, R, W0, primR, idxR, p.RW0, F32, ldw, act, p.fs, st));
+  if (dX && L->T > 0) {  // dX = dY W
+    GemmDesc g;
+    g.kclass = POET_K_TOKEN_DX;
+    g.compute = act; g.M = L->T; g.N = n; g.K = m;
+    g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 1;
+    g.B = W; g.ldb = ldw; g.b_dt = act; g.b_kmajor = 0;
+    g.C = dX; g.ldc = L->ldx; g.c_dt = act;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  {  // G = dY^T X  (K = T; T == 0 gives G = 0)
+    GemmDesc g;
+    g.kclass = POET_K_TOKEN_GW;
+    g.compute = act; g.M = m; g.N = n; g.K = L->T;
+    g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 0;
+    g.B = X; g.ldb = L->ldx; g.b_dt = act; g.b_kmajor = 0;
+    g.C = p.G; g.ldc = ldw; g.c_dt = F32;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  // primitive blocks of dL/dR = G Z^T
+  if (R.theta_len > 0) {
+    GemmDesc g;
+    g.kclass = POET_K_CONTRACT;
+    g.compute = act;
+    if (R.mode == POET_BS) {
+      HIP_TRY(launch_fill(p.dRb, R.prim_len, 0.f, st));
+      g.M = g.N = R.bp; g.K = n; g.Mtot = g.Ntot = m; g.batch = R.nprim;
+      g.A = p.G; g.lda = ldw; g.sA = (int64_t)R.bp * ldw; g.a_dt = F32; g.a_kmajor = 1;
+      g.B = p.T; g.ldb = ldw; g.sB = (int64_t)R.bp * ldw; g.b_dt = F32; g.b_kmajor = 1;
+      g.C = p.dRb; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
+    } else {
+      HIP_TRY(launch_gather_rows(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, n, st));
+      HIP_TRY(launch_gather_rows(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, n, st));
+      g.M = g.N = R.bp; g.K = n;
+      g.A = p.Gr; g.lda = n; g.a_dt = F32; g.a_kmajor = 1;
+      g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
+      g.C = p.dRb; g.ldc = R.bp; g.c_dt = F32;
+    }
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(neumann_adjoint(R, p.dRb, powersR, dthetaR, p.adj, st));
+  }
+  // primitive blocks of dL/dP = (R W0)^T G
+  if (P.theta_len > 0) {
+    GemmDesc g;
+    g.kclass = POET_K_CONTRACT;
+    g.compute = act;
+    if (P.mode == POET_BS) {
+      HIP_TRY(launch_fill(p.dPb, P.prim_len, 0.f, st));
+      g.M = g.N = P.bp; g.K = m; g.Mtot = g.Ntot = n; g.batch = P.nprim;
+      g.A = p.RW0; g.lda = ldw; g.sA = P.bp; g.a_dt = F32; g.a_kmajor = 0;
+      g.B = p.G; g.ldb = ldw; g.sB = P.bp; g.b_dt = F32; g.b_kmajor = 0;
+      g.C = p.dPb; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
+    } else {
+      HIP_TRY(launch_gather_cols(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, P.bp, st));
+      HIP_TRY(launch_gather_cols(p.G, ldw, m, idxP, P.bp, n, p.Gc, P.bp, st));
+      g.M = g.N = P.bp; g.K = m;
+      g.A = p.Acp; g.lda = P.bp; g.a_dt = F32; g.a_kmajor = 0;
+      g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
+      g.C = p.dPb; g.ldc = P.bp; g.c_dt = F32;
+    }
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(neumann_adjoint(P, p.dPb, powersP, dthetaP, p.adj, st));
+  }
+  return POET_OK;
+}
+
+poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* thetaR, float* thetaP,
+                       const float* primR, const float* primP, int32_t* idxR, int32_t* idxP, uint64_t seed,
+                       uint32_t linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!W0 || !primR || !primP) return fail(POET_E_ARG, "null W0 or primitive");
+  if ((R.theta_len > 0 && !thetaR) || (P.theta_len > 0 && !thetaP)) return fail(POET_E_ARG, "null theta");
+  if (!check_idx(R, idxR, "R") || !check_idx(P, idxP, "P")) return g_last;
+  MergePlan p;
+  const size_t need = plan_merge(*L, R, P, nullptr, &p);
+  if (!check_ws(ws, ws_bytes, need)) return g_last;
+  plan_merge(*L, R, P, ws, &p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, F32, p.fs, st));
+  HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.Wn, F32, L->ldw, F32, p.fs, st));
+  HIP_TRY(launch_convert(p.Wn, L->ldw, W0, L->ldw, F32, L->m, L->n, st));
+  if (W0_shadow) HIP_TRY(launch_convert(p.Wn, L->ldw, W0_shadow, L->ldw, L->act_dtype, L->m, L->n, st));
+  if (R.theta_len > 0) HIP_TRY(launch_fill(thetaR, R.theta_len, 0.f, st));
+  if (P.theta_len > 0) HIP_TRY(launch_fill(thetaP, P.theta_len, 0.f, st));
+  if (R.mode == POET_FS)
+    HIP_TRY(launch_sample(R.d, R.bp, sampler_hash(seed, linear_id, POET_SIDE_R, epoch_next), p.flags, idxR, st));
+  if (P.mode == POET_FS)
+    HIP_TRY(launch_sample(P.d, P.bp, sampler_hash(seed, linear_id, POET_SIDE_P, epoch_next), p.flags, idxP, st));
+  return POET_OK;
+}
+
+const char* poet_status_string(poet_status st) {
+  switch (st) {
+    case POET_OK: return "POET_OK";
+    case POET_E_ARG: return "POET_E_ARG: invalid argument";
+    case POET_E_SHAPE: return "POET_E_SHAPE: inconsistent or unsupported shape";
+    case POET_E_DTYPE: return "POET_E_DTYPE: unsupported dtype";
+    case POET_E_WORKSPACE: return "POET_E_WORKSPACE: workspace too small";
+    case POET_E_HIP: return "POET_E_HIP: HIP runtime or launch failure";
+    case POET_E_UNSUPPORTED: return "POET_E_UNSUPPORTED: not implemented for these arguments";
+  }
+  return "unknown poet_status";
+}
+
+const char* poet_last_error(void) { return g_err.c_str(); }
+const char* poet_version(void) { return "poet-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+"""Device-resident state of one POET linear and the calls of one training step on it.
+
+``PoetLinear`` owns the GPU buffers of one linear (the fixed weight W0, the skew parameters of R and P, the
+FS index sets, the built primitives, the saved Neumann powers and one shared workspace) and issues the C-ABI
+calls through the binding. It does no arithmetic of its own.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import binding as B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _tdt(dt: int):
+    torch = _torch()
+    return torch.bfloat16 if dt == B.POET_BF16 else torch.float32
+
+
+class PoetLinear:
+    """One POET linear W = R W0 P on the GPU.
+
+    R, P are ``poet_side`` structs; W0 is an (m, n) float32 host array (numpy or torch). ``ldw`` pads W0's rows
+    (a multiple of 64 elements keeps every row 128-byte aligned). Index sets of FS sides are drawn on the GPU
+    with ``poet_sample_indices`` for epoch 0 unless given.
+    """
+
+    def __init__(self, m: int, n: int, T: int, R: B.poet_side, P: B.poet_side, act_dtype: int, W0,
+                 thetaR=None, thetaP=None, seed: int = 0, linear_id: int = 0, ldw: Optional[int] = None,
+                 ldx: Optional[int] = None, ldy: Optional[int] = None, idxR=None, idxP=None, device: str = "cuda"):
+        torch = _torch()
+        self.dev = torch.device(device)
+        self.L = B.layer(m, n, T, R, P, act_dtype, ldw, ldx, ldy)
+        self.m, self.n, self.T = m, n, T
+        self.seed, self.linear_id, self.epoch = seed, linear_id, 0
+        self.act = _tdt(act_dtype)
+        W0 = torch.as_tensor(W0, dtype=torch.float32)
+        self.W0 = torch.zeros((m, self.L.ldw), dtype=torch.float32, device=self.dev)
+        self.W0[:, :n] = W0.to(self.dev)
+        nR, nP = B.poet_theta_len(R), B.poet_theta_len(P)
+        self.thetaR = (torch.zeros(nR) if thetaR is None else torch.as_tensor(thetaR, dtype=torch.float32)).to(self.dev)
+        self.thetaP = (torch.zeros(nP) if thetaP is None else torch.as_tensor(thetaP, dtype=torch.float32)).to(self.dev)
+        self.primR = torch.empty(B.poet_prim_len(R), dtype=torch.float32, device=self.dev)
+        self.primP = torch.empty(B.poet_prim_len(P), dtype=torch.float32, device=self.dev)
+        self.powersR = torch.empty(max(B.poet_powers_len(R), 1), dtype=_tdt(R.dtype), device=self.dev)
+        self.powersP = torch.empty(max(B.poet_powers_len(P), 1), dtype=_tdt(P.dtype), device=self.dev)
+        self.qnormR = torch.empty(B.poet_num_prims(R), dtype=torch.float32, device=self.dev)
+        self.qnormP = torch.empty(B.poet_num_prims(P), dtype=torch.float32, device=self.dev)
+        self.dthetaR = torch.empty(max(nR, 1), dtype=torch.float32, device=self.dev)
+        self.dthetaP = torch.empty(max(nP, 1), dtype=torch.float32, device=self.dev)
+        wsb = max(B.poet_workspace_bytes(self.L, op) for op in (B.POET_OP_FWD, B.POET_OP_BWD, B.POET_OP_MERGE))
+        wsb = max(wsb, B.poet_sample_workspace_bytes(max(m, n)))
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+        self.idxR = self.idxP = None
+        if R.mode == B.POET_FS:
+            self.idxR = torch.empty(R.b, dtype=torch.int32, device=self.dev)
+            if idxR is None:
+                B.poet_sample_indices(m, R.b, seed, linear_id, B.POET_SIDE_R, 0, self.idxR, self.ws)
+            else:
+                self.idxR.copy_(torch.as_tensor(idxR, dtype=torch.int32))
+        if P.mode == B.POET_FS:
+            self.idxP = torch.empty(P.b, dtype=torch.int32, device=self.dev)
+            if idxP is None:
+                B.poet_sample_indices(n, P.b, seed, linear_id, B.POET_SIDE_P, 0, self.idxP, self.ws)
+            else:
+                self.idxP.copy_(torch.as_tensor(idxP, dtype=torch.int32))
+
+    def _powers(self, side: str):
+        s = self.L.R if side == "R" else self.L.P
+        if B.poet_powers_len(s) == 0:
+            return None
+        return self.powersR if side == "R" else self.powersP
+
+    def build(self, stream=None, qnorm: bool = False):
+        B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
+                                None, stream)
+        B.poet_build_orthogonal(self.L.P, self.thetaP, self.primP, self._powers("P"), self.qnormP if qnorm else None,
+                                None, stream)
+
+    def alloc_act(self, rows: int, ld: int):
+        return _torch().empty((rows, ld), dtype=self.act, device=self.dev)
+
+    def alloc_W(self):
+        return _torch().empty((self.m, self.L.ldw), dtype=self.act, device=self.dev)
+
+    def forward(self, X, Y, W_out=None, stream=None):
+        B.poet_linear_fwd(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, X, Y, W_out, self.ws, stream)
+
+    def backward(self, X, dY, dX, W=None, stream=None):
+        B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
+                          self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
+
+    def merge(self, shadow=None, stream=None):
+        self.epoch += 1
+        B.poet_merge(self.L, self.W0, shadow, self.thetaR, self.thetaP, self.primR, self.primP, self.idxR, self.idxP,
+                     self.seed, self.linear_id, self.epoch, self.ws, stream)

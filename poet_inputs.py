@@ -172,5 +172,14 @@ def gen_linear(cfg_id: int, layer: int, lin: LinearSpec, theta_std: float = THET
     return W0, tR, tP, X, dY
 
 
+def gen_weights(cfg_id: int, layer: int, lin: LinearSpec, theta_std: float = THETA_STD):
+    """W0, thetaR, thetaP of one linear (the same draws gen_linear makes), without the activations."""
+    j = lin.linear_id % 7
+    W0 = row_normalized_gaussian(rng_for(cfg_id, layer, j, KIND_W0), lin.m, lin.n)
+    tR = (rng_for(cfg_id, layer, j, KIND_THETA_R).standard_normal(n_theta(lin.R)) * theta_std).astype(np.float32)
+    tP = (rng_for(cfg_id, layer, j, KIND_THETA_P).standard_normal(n_theta(lin.P)) * theta_std).astype(np.float32)
+    return W0, tR, tP
+
+
 def pad_ld(n: int, mult: int = 64) -> int:
     return (n + mult - 1) // mult * mult

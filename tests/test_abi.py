@@ -1,0 +1,147 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol ``include/poet.h`` declares, its
+size functions agree with the oracle's parameter layout, and invalid arguments are rejected on the host with
+the documented status before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle as O
+from orthogonal_reparameterized_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "poet.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(poet_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = B.lib()
+    names = header_functions()
+    assert len(names) >= 14
+    for nm in names:
+        assert hasattr(L, nm), nm
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (poet_[a-z_]+)\b", out))
+    assert set(names) <= exported
+    assert set(B.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in B.poet_version()
+    for st in range(7):
+        assert B.poet_status_string(st).startswith("POET_")
+    assert "unknown" in B.poet_status_string(99)
+
+
+@pytest.mark.parametrize("mode,d,b", [(0, 256, 32), (0, 1376, 64), (0, 5461, 256), (0, 7, 7), (0, 10, 1),
+                                      (1, 5461, 2730), (1, 2048, 1024), (1, 1, 1)])
+@pytest.mark.parametrize("k,dt", [(0, 0), (5, 1)])
+def test_sizes_match_oracle_layout(mode, d, b, k, dt):
+    s = B.side(mode, d, b, k, dt)
+    assert B.poet_theta_len(s) == O.theta_len(mode, d, b)
+    nprim = len(O.block_sizes(mode, d, b))
+    assert B.poet_num_prims(s) == nprim
+    assert B.poet_prim_len(s) == nprim * b * b
+    assert B.poet_powers_len(s) == k * nprim * b * b
+    assert B.poet_build_workspace_bytes(s, True) == 0
+    assert B.poet_build_workspace_bytes(s, False) == (0 if k == 0 else B.poet_build_workspace_bytes(s, False))
+
+
+@pytest.mark.parametrize("bad", [dict(mode=2), dict(d=0), dict(b=0), dict(b=300), dict(k=-1), dict(k=17),
+                                 dict(dtype=5), dict(b=9000, d=9000)])
+def test_bad_side_sizes_are_zero(bad):
+    kw = dict(mode=0, d=256, b=32, k=3, dtype=0)
+    kw.update(bad)
+    s = B.side(**kw)
+    assert B.poet_theta_len(s) == 0 and B.poet_prim_len(s) == 0
+    assert B.poet_last_error() != ""
+
+
+def _layer(**over):
+    kw = dict(m=256, n=128, T=64, R=B.side(0, 256, 32, 3, 0), P=B.side(0, 128, 32, 3, 0), act_dtype=0)
+    kw.update(over)
+    return B.layer(**kw)
+
+
+def test_workspace_sizes_positive_and_monotone():
+    L = _layer()
+    for op in (B.POET_OP_FWD, B.POET_OP_BWD, B.POET_OP_MERGE):
+        assert B.poet_workspace_bytes(L, op) > 0
+    assert B.poet_workspace_bytes(L, B.POET_OP_BUILD) == 0
+    big = _layer(ldw=192)
+    assert B.poet_workspace_bytes(big, B.POET_OP_BWD) > B.poet_workspace_bytes(L, B.POET_OP_BWD)
+    assert B.poet_workspace_bytes(L, 9) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _fwd(L, ws_bytes=1 << 40, idxR=None, idxP=None, X=FAKE, W0=FAKE):
+    return B.lib().poet_linear_fwd(ctypes.byref(L), W0, FAKE, FAKE, idxR, idxP, X, FAKE, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(m=0), B.POET_E_SHAPE),
+    (dict(T=-1), B.POET_E_SHAPE),
+    (dict(ldw=100), B.POET_E_SHAPE),
+    (dict(ldx=100), B.POET_E_SHAPE),
+    (dict(ldy=200), B.POET_E_SHAPE),
+    (dict(act_dtype=3), B.POET_E_DTYPE),
+    (dict(R=B.side(0, 128, 32, 3, 0)), B.POET_E_SHAPE),
+    (dict(P=B.side(0, 128, 32, 99, 0)), B.POET_E_SHAPE),
+    (dict(P=B.side(7, 128, 32, 3, 0)), B.POET_E_ARG),
+    (dict(P=B.side(0, 128, 32, 3, 4)), B.POET_E_DTYPE),
+])
+def test_fwd_rejects_bad_layer(over, status):
+    assert _fwd(_layer(**over)) == status
+    assert B.poet_last_error() != ""
+
+
+def test_fwd_rejects_bad_pointers_and_workspace():
+    L = _layer()
+    assert _fwd(L, W0=None) == B.POET_E_ARG
+    assert _fwd(L, X=None) == B.POET_E_ARG
+    assert _fwd(L, idxR=FAKE) == B.POET_E_ARG  # BS side takes no index set
+    assert _fwd(L, ws_bytes=16) == B.POET_E_WORKSPACE
+    Lfs = _layer(R=B.side(1, 256, 128, 3, 0))
+    assert _fwd(Lfs) == B.POET_E_ARG  # FS side needs an index set
+    assert B.lib().poet_linear_fwd(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, None,
+                                   B.poet_workspace_bytes(L, B.POET_OP_FWD), None) == B.POET_E_ARG
+
+
+def test_bwd_and_merge_reject_bad_arguments():
+    L = _layer()
+    lb = B.lib()
+    ws = B.poet_workspace_bytes(L, B.POET_OP_BWD)
+    # saved powers are required for k >= 1
+    assert lb.poet_linear_bwd(ctypes.byref(L), FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, FAKE, None,
+                              FAKE, FAKE, FAKE, ws, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, None,
+                              None, FAKE, FAKE, ws, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, None,
+                              FAKE, FAKE, FAKE, ws - 1024, None) == B.POET_E_WORKSPACE
+    wm = B.poet_workspace_bytes(L, B.POET_OP_MERGE)
+    assert lb.poet_merge(ctypes.byref(L), FAKE, None, None, FAKE, FAKE, FAKE, None, None, 1, 2, 3, FAKE, wm,
+                         None) == B.POET_E_ARG
+    assert lb.poet_merge(ctypes.byref(L), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 3, FAKE, 8,
+                         None) == B.POET_E_WORKSPACE
+
+
+def test_build_and_sampler_reject_bad_arguments():
+    lb = B.lib()
+    s = B.side(0, 256, 32, 3, 0)
+    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, None, FAKE, None, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, FAKE, None, None, None, 0, None) == B.POET_E_WORKSPACE
+    bad = B.side(0, 256, 0, 3, 0)
+    assert lb.poet_build_orthogonal(ctypes.byref(bad), FAKE, FAKE, FAKE, None, None, 0, None) == B.POET_E_SHAPE
+    assert lb.poet_sample_indices(10, 11, 1, 2, 3, 4, FAKE, FAKE, 1 << 20, None) == B.POET_E_SHAPE
+    assert lb.poet_sample_indices(0, 0, 1, 2, 3, 4, FAKE, FAKE, 1 << 20, None) == B.POET_E_SHAPE
+    assert lb.poet_sample_indices(100, 10, 1, 2, 3, 4, FAKE, FAKE, 4, None) == B.POET_E_WORKSPACE
+    assert lb.poet_sample_indices(100, 10, 1, 2, 3, 4, None, FAKE, 1 << 20, None) == B.POET_E_ARG

@@ -1,0 +1,213 @@
+"""GPU parity of the POET layer against the CPU oracle, through the C ABI.
+
+Every case feeds identical seeded inputs (from poet_inputs) to the HIP path and to the oracle; FS index sets are
+drawn by the oracle and passed in (the GPU sampler is checked bit-exactly on its own). Sizes span several tiles
+and ragged tails; the LLaMA-60M block is checked in full. Bars: relative Frobenius error <= 1e-5 for float32
+paths, <= 2e-2 for bf16 activations with float32 accumulation; bit-exact for indices and identity cases.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import poet_inputs as PI
+from tests.gpu_util import TOL, announce, gpu_linear, make_linear, oracle_indices, put_act, rel, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from orthogonal_reparameterized_amd import binding as B
+    B.lib()
+
+
+def run_case(lin, cfg_id=99, seed=7, pad=0, theta_std=PI.THETA_STD, check_merge=True, pass_W=True, tag=""):
+    announce(f"{tag} linear {lin.name} m={lin.m} n={lin.n} T={lin.T} mode={lin.R.mode} b=({lin.R.b},{lin.P.b}) "
+             f"k={lin.R.k} dt={lin.act_dtype} pad={pad}")
+    W0, tR, tP, X, dY = PI.gen_linear(cfg_id, 0, lin, theta_std=theta_std)
+    iR, iP = oracle_indices(lin, seed)
+    sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+    ref_f = O.linear_fwd(sR, sP, W0, tR, tP, iR, iP, X)
+    ref_b = O.linear_bwd(sR, sP, W0, tR, tP, iR, iP, X, dY)
+
+    pl = gpu_linear(lin, W0, tR, tP, iR, iP, seed=seed, pad=pad)
+    pl.build()
+    Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+    Y, dX, W = pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx), pl.alloc_W()
+    pl.forward(Xd, Y, W_out=W)
+    pl.backward(Xd, dYd, dX, W=W if pass_W else None)
+    torch.cuda.synchronize()
+    tol = TOL[lin.act_dtype]
+    out = {}
+    # primitives against the oracle's (padded) primitives
+    for nm, side, th, prim in (("R", lin.R, tR, pl.primR), ("P", lin.P, tP, pl.primP)):
+        ref = O.pack_prims(side.mode, side.d, side.b, O.build_orthogonal(side.mode, side.d, side.b, side.k, th))
+        e = rel(to_np(prim).reshape(ref.shape), ref)
+        out["prim" + nm] = e
+        assert e <= (1e-5 if side.dtype == PI.DT_F32 else 1e-4), (nm, e)
+    out["W"] = rel(to_np(W)[:, :lin.n], ref_f["W"])
+    out["Y"] = rel(to_np(Y)[:, :lin.m], ref_f["Y"]) if lin.T else 0.0
+    out["dX"] = rel(to_np(dX)[:, :lin.n], ref_b["dX"]) if lin.T else 0.0
+    out["dthetaR"] = rel(to_np(pl.dthetaR)[:len(tR)], ref_b["dthetaR"]) if len(tR) else 0.0
+    out["dthetaP"] = rel(to_np(pl.dthetaP)[:len(tP)], ref_b["dthetaP"]) if len(tP) else 0.0
+    for key in ("W", "Y", "dX", "dthetaR", "dthetaP"):
+        assert out[key] <= tol, (key, out[key], tol)
+    if check_merge:
+        shadow = pl.alloc_W()
+        pl.merge(shadow=shadow)
+        torch.cuda.synchronize()
+        mg = O.merge(sR, sP, W0, tR, tP, iR, iP, seed, lin.linear_id, 1)
+        out["merge"] = rel(to_np(pl.W0)[:, :lin.n], mg["W0"])
+        assert out["merge"] <= 1e-5, out["merge"]  # the merge is float32 for every act dtype
+        assert np.all(to_np(pl.thetaR) == 0) and np.all(to_np(pl.thetaP) == 0)
+        if lin.R.mode == PI.MODE_FS:
+            np.testing.assert_array_equal(pl.idxR.cpu().numpy(), mg["idxR"])
+            np.testing.assert_array_equal(pl.idxP.cpu().numpy(), mg["idxP"])
+        sh = to_np(shadow)[:, :lin.n]
+        w0n = to_np(pl.W0)[:, :lin.n]
+        if lin.act_dtype == PI.DT_F32:
+            np.testing.assert_array_equal(sh, w0n)
+        else:
+            np.testing.assert_array_equal(sh, PI.round_bf16(w0n))
+    return out, pl
+
+
+# -------------------------------------------------------------------------------------------------- float32
+def test_single_linear_256_bs32_fp32():
+    """The 256 x 256 single-linear workload: BS b = 32, k = 3, float32, 64 tokens; fwd, bwd, merge."""
+    wl = PI.WORKLOADS[1]
+    lin = wl.linears()[0]
+    run_case(lin, cfg_id=1, seed=wl.seed, tag="cfg-256")
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 5])
+def test_bs_ragged_fp32(k):
+    lin = make_linear("ragged", 200, 150, 77, PI.MODE_BS, 32, 64, k, PI.DT_F32)
+    run_case(lin, pad=16, pass_W=(k % 2 == 0), tag=f"bs-ragged-k{k}")
+
+
+@pytest.mark.parametrize("bR,bP", [(1, 1), (7, 5), (200, 150)])
+def test_bs_degenerate_blocks_fp32(bR, bP):
+    # size-1 blocks (no parameters at all), odd sizes, and a single block covering the whole dimension
+    lin = make_linear("blocks", 200, 150, 33, PI.MODE_BS, bR, bP, 3, PI.DT_F32)
+    run_case(lin, tag=f"bs-blocks-{bR}-{bP}")
+
+
+@pytest.mark.parametrize("k", [0, 3])
+def test_fs_fp32(k):
+    lin = make_linear("fs", 200, 150, 65, PI.MODE_FS, 100, 75, k, PI.DT_F32, linear_id=5)
+    run_case(lin, pad=8, tag=f"fs-k{k}")
+
+
+def test_empty_tokens_fp32():
+    lin = make_linear("empty", 96, 80, 0, PI.MODE_BS, 32, 32, 2, PI.DT_F32)
+    out, pl = run_case(lin, check_merge=False, tag="T=0")
+    assert np.all(to_np(pl.dthetaR) == 0) and np.all(to_np(pl.dthetaP) == 0)
+
+
+# -------------------------------------------------------------------------------------------------- bf16
+@pytest.mark.parametrize("mode,bR,bP", [(PI.MODE_BS, 64, 64), (PI.MODE_BS, 96, 40), (PI.MODE_FS, 130, 95)])
+def test_bf16_small(mode, bR, bP):
+    lin = make_linear("bf16", 272, 190, 300, mode, bR, bP, 4, PI.DT_BF16, linear_id=3)
+    run_case(lin, pad=2, tag=f"bf16-{mode}")
+
+
+def test_bf16_acts_fp32_chain():
+    lin = make_linear("mixed", 160, 224, 128, PI.MODE_BS, 64, 32, 5, PI.DT_BF16, side_dt=PI.DT_F32)
+    run_case(lin, tag="bf16-act-fp32-chain")
+
+
+def test_llama60m_block_bs64_full():
+    """All 7 linears of the LLaMA-60M block (q/k/v/o 512x512, gate/up 1376x512, down 512x1376), BS b = 64,
+    k = 4, bf16, 8192 tokens, checked in full."""
+    wl = PI.WORKLOADS[2]
+    for lin in wl.linears():
+        run_case(lin, cfg_id=2, seed=wl.seed, pad=PI.pad_ld(lin.n) - lin.n if lin.n % 64 else 0,
+                 check_merge=lin.name in ("gate", "down"), tag="llama60m")
+
+
+# -------------------------------------------------------------------------------------------------- identities
+@pytest.mark.parametrize("dt", [PI.DT_F32, PI.DT_BF16])
+@pytest.mark.parametrize("mode", [PI.MODE_BS, PI.MODE_FS])
+def test_zero_theta_gives_w0_bitwise(dt, mode):
+    b = 48 if mode == PI.MODE_BS else 60
+    lin = make_linear("zero", 120, 100, 16, mode, b, b, 3, dt)
+    announce(f"zero-theta mode={mode} dt={dt}")
+    W0, _, _, X, _ = PI.gen_linear(5, 0, lin)
+    iR, iP = oracle_indices(lin, 3)
+    pl = gpu_linear(lin, W0, None, None, iR, iP)
+    pl.build()
+    W = pl.alloc_W()
+    Y = pl.alloc_act(lin.T, pl.L.ldy)
+    pl.forward(put_act(pl, X, pl.L.ldx), Y, W_out=W)
+    torch.cuda.synchronize()
+    want = W0 if dt == PI.DT_F32 else PI.round_bf16(W0)
+    np.testing.assert_array_equal(to_np(W)[:, :lin.n], want)
+
+
+def test_determinism_bitwise():
+    lin = make_linear("det", 256, 192, 200, PI.MODE_BS, 64, 64, 5, PI.DT_BF16)
+    outs = []
+    for rep in range(2):
+        announce(f"determinism rep {rep}")
+        W0, tR, tP, X, dY = PI.gen_linear(11, 0, lin)
+        pl = gpu_linear(lin, W0, tR, tP, None, None)
+        pl.build()
+        Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+        Y, dX = pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx)
+        pl.forward(Xd, Y)
+        pl.backward(Xd, dYd, dX)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (pl.primR, pl.primP, Y, dX, pl.dthetaR, pl.dthetaP)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# -------------------------------------------------------------------------------------------------- sampler
+@pytest.mark.parametrize("d,s", [(1, 1), (7, 3), (256, 128), (1000, 1), (2048, 1024), (5461, 2730), (6848, 3424),
+                                 (300, 300)])
+def test_sampler_bit_exact(d, s):
+    from orthogonal_reparameterized_amd import binding as B
+    announce(f"sampler d={d} s={s}")
+    ws = torch.empty(B.poet_sample_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    for (seed, lid, side, ep) in [(0, 0, 0, 0), (4000, 12, 1, 3), (2 ** 63 + 5, 2 ** 32 - 1, 0, 77)]:
+        idx = torch.full((s,), -1, dtype=torch.int32, device="cuda")
+        B.poet_sample_indices(d, s, seed, lid, side, ep, idx, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), O.sample_indices(d, s, seed, lid, side, ep))
+
+
+# -------------------------------------------------------------------------------------------------- invariants
+@pytest.mark.parametrize("mode,d,b,k,dt", [(PI.MODE_BS, 5461, 256, 5, PI.DT_BF16), (PI.MODE_FS, 2048, 1024, 5, PI.DT_BF16),
+                                           (PI.MODE_BS, 256, 32, 3, PI.DT_F32), (PI.MODE_BS, 512, 64, 2, PI.DT_F32)])
+def test_orthogonality_closed_form(mode, d, b, k, dt):
+    """R_k^T R_k - I equals -Q^(2k+2) (k even) or -2Q^(k+1) + Q^(2k+2) (k odd); at std 1e-3 that is below the
+    float32 rounding of R_k (~1e-7). A bf16 power chain adds the rounding of Q as a product operand (relative
+    2^-9 per entry), which perturbs the Q^2 term by about 2 * 2^-9 * ||Q||_2^2 and enters R^T R twice; the
+    bound below is that figure plus float32 rounding."""
+    from orthogonal_reparameterized_amd import binding as B
+    announce(f"orthogonality mode={mode} d={d} b={b} k={k}")
+    s = B.side(mode, d, b, k, dt)
+    theta = (np.random.default_rng(9).standard_normal(B.poet_theta_len(s)) * 1e-3).astype(np.float32)
+    th = torch.from_numpy(theta).cuda()
+    prim = torch.empty(B.poet_prim_len(s), dtype=torch.float32, device="cuda")
+    pw = torch.empty(max(B.poet_powers_len(s), 1), dtype=torch.bfloat16 if dt else torch.float32, device="cuda")
+    qn = torch.empty(B.poet_num_prims(s), dtype=torch.float32, device="cuda")
+    B.poet_build_orthogonal(s, th, prim, pw if k else None, qn)
+    torch.cuda.synchronize()
+    P = to_np(prim).reshape(-1, b, b).astype(np.float64)
+    sizes = O.block_sizes(mode, d, b)
+    off = 0
+    for p, c in enumerate(sizes):
+        nt = c * (c - 1) // 2
+        qn2 = np.linalg.norm(O.skew_from_theta(theta[off:off + nt], c), 2)
+        tol = 1e-6 + (2.0 ** -7 * qn2 ** 2 if dt == PI.DT_BF16 else 0.0)
+        err = np.abs(P[p].T @ P[p] - np.eye(b)).max()
+        assert err < tol, (p, err, tol)
+        # per-primitive Frobenius norm of Q
+        assert to_np(qn)[p] == pytest.approx(np.sqrt(2 * np.sum(theta[off:off + nt].astype(np.float64) ** 2)), rel=1e-5)
+        off += nt
