@@ -21,7 +21,9 @@
  *    memory. Scratch space comes from the caller's workspace `ws` of at least poet_workspace_bytes() bytes
  *    (any alignment is accepted; the library aligns internally).
  *  - Matrices are row-major. W0, W, the bf16 shadow and the weight-gradient use leading dimension ldw >= n;
- *    X and dX use ldx >= n; Y and dY use ldy >= m (all in elements).
+ *    X and dX use ldx >= n; Y and dY use ldy >= m (all in elements). A buffer holds whole rows: rows * ld
+ *    elements (kernels may read, never write, the padding of a row). bf16 operands whose leading dimension is
+ *    a multiple of 8 elements and whose base is 16-byte aligned take the fast token-GEMM path.
  *  - Skew parameters theta (and gradients dtheta) are float32, packed per primitive as the strict upper
  *    triangle in row-major order (0,1),(0,2),...,(c-2,c-1); Q_ij = theta_p, Q_ji = -theta_p. A side's
  *    primitives are concatenated in order (BS: block 0 first).

@@ -235,7 +235,8 @@ def poet_sample_indices(d: int, s: int, seed: int, linear_id: int, side_id: int,
 
 def _layer_bytes(L: poet_layer):
     e = _esz(L.act_dtype)
-    rowsz = lambda rows, ld, cols, es: 0 if rows == 0 else ((rows - 1) * ld + cols) * es  # noqa: E731
+    # every row-major buffer holds whole rows of its leading dimension (the kernels may read a row's padding)
+    rowsz = lambda rows, ld, cols, es: rows * ld * es  # noqa: E731
     return {"W0": rowsz(L.m, L.ldw, L.n, 4), "W": rowsz(L.m, L.ldw, L.n, e), "X": rowsz(L.T, L.ldx, L.n, e),
             "Y": rowsz(L.T, L.ldy, L.m, e)}
 

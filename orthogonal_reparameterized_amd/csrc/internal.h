@@ -46,6 +46,17 @@ struct ProfScope {
 
 hipError_t launch_gemm(const GemmDesc& g, hipStream_t st);
 
+// Token GEMM on bf16 MFMA (gemm_tokens.hip): C (M x N, bf16 or float32) = A (M x K) B (K x N), both bf16, with
+// the same orientation flags as GemmDesc. Needs lda, ldb multiples of 8 and 16-byte aligned A, B.
+struct TokGemm {
+  int M = 0, N = 0, K = 0;
+  const __bf16* A = nullptr; int64_t lda = 0; int a_kmajor = 1;
+  const __bf16* B = nullptr; int64_t ldb = 0; int b_kmajor = 1;
+  void* C = nullptr; int64_t ldc = 0; int c_f32 = 0;
+};
+bool tok_gemm_supported(const TokGemm& p);
+hipError_t launch_tok_gemm(const TokGemm& p, int kclass, hipStream_t st);
+
 // ---- elementwise / data-movement kernels (kernels_misc.hip) ------------------------------------------
 // theta -> prim = I + coef*Q (coef 1 for k = 0, else 2) and, when q_out != null, Q in dtype q_dt.
 hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim,

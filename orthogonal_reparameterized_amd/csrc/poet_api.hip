@@ -269,6 +269,20 @@ size_t plan_merge(const poet_layer& L, const SideInfo& R, const SideInfo& P, voi
   return a.used();
 }
 
+// Token GEMMs run on the dedicated 256x256 bf16 kernel when the operands qualify (bf16, 16-byte aligned rows),
+// otherwise on the generic kernel (float32 activations, odd leading dimensions).
+hipError_t token_gemm(const GemmDesc& g, hipStream_t st) {
+  if (g.compute == BF16 && g.a_dt == BF16 && g.b_dt == BF16 && g.batch == 1 && !g.D && !g.Acc && g.alpha == 1.f) {
+    TokGemm t;
+    t.M = g.M; t.N = g.N; t.K = g.K;
+    t.A = reinterpret_cast<const __bf16*>(g.A); t.lda = g.lda; t.a_kmajor = g.a_kmajor;
+    t.B = reinterpret_cast<const __bf16*>(g.B); t.ldb = g.ldb; t.b_kmajor = g.b_kmajor;
+    t.C = g.C; t.ldc = g.ldc; t.c_f32 = g.c_dt == F32;
+    if (tok_gemm_supported(t)) return launch_tok_gemm(t, g.kclass, st);
+  }
+  return launch_gemm(g, st);
+}
+
 bool check_ws(void* ws, size_t have, size_t need) {
   if (have < need) return fail(POET_E_WORKSPACE, "workspace of %zu bytes < %zu needed", have, need), false;
   if (!ws && need > 0) return fail(POET_E_ARG, "null workspace"), false;
@@ -395,7 +409,7 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
     g.A = X; g.lda = L->ldx; g.a_dt = act; g.a_kmajor = 1;
     g.B = W; g.ldb = L->ldw; g.b_dt = act; g.b_kmajor = 1;
     g.C = Y; g.ldc = L->ldy; g.c_dt = act;
-    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(token_gemm(g, st));
   }
   return POET_OK;
 }
@@ -435,7 +449,7 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 1;
     g.B = W; g.ldb = ldw; g.b_dt = act; g.b_kmajor = 0;
     g.C = dX; g.ldc = L->ldx; g.c_dt = act;
-    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(token_gemm(g, st));
   }
   {  // G = dY^T X  (K = T; T == 0 gives G = 0)
     GemmDesc g;
@@ -444,7 +458,7 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 0;
     g.B = X; g.ldb = L->ldx; g.b_dt = act; g.b_kmajor = 0;
     g.C = p.G; g.ldc = ldw; g.c_dt = F32;
-    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(token_gemm(g, st));
   }
   // primitive blocks of dL/dR = G Z^T
   if (R.theta_len > 0) {

@@ -1,0 +1,70 @@
+"""GPU parity at the full LLaMA-1.3B shapes, in the launch configuration the benchmark times (bf16, row pitch
+padded to 64 elements, 16384 tokens).
+
+The oracle computes the materialized weight in full and the token outputs on a seeded sample of 256 token rows
+(tokens are independent rows of Y = X W^T and dX = dY W, so the sample is exact, not an approximation). The
+skew-parameter gradients need the full weight-space gradient dY^T X and are compared in full. Bar: relative
+Frobenius error <= 2e-2 (bf16 activations, float32 accumulation).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import poet_inputs as PI
+from tests.gpu_util import TOL, announce, gpu_linear, oracle_indices, put_act, rel, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(cfg_id, name):
+    wl = PI.WORKLOADS[cfg_id]
+    lin = [l for l in wl.linears() if l.name == name][0]
+    announce(f"fullsize cfg={wl.name} linear={name} m={lin.m} n={lin.n} T={lin.T}")
+    W0, tR, tP, X, dY = PI.gen_linear(cfg_id, 0, lin)
+    iR, iP = oracle_indices(lin, wl.seed)
+    pad = PI.pad_ld(max(lin.m, lin.n)) - max(lin.m, lin.n)
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetLinear
+    pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
+                    seed=wl.seed, linear_id=lin.linear_id, ldw=PI.pad_ld(lin.n), ldx=PI.pad_ld(lin.n),
+                    ldy=PI.pad_ld(lin.m), idxR=iR, idxP=iP)
+    del pad
+    pl.build()
+    Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+    Y, dX, W = pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx), pl.alloc_W()
+    pl.forward(Xd, Y, W_out=W)
+    pl.backward(Xd, dYd, dX, W=W)
+    torch.cuda.synchronize()
+
+    sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+    rows = np.sort(np.random.default_rng(1234).choice(lin.T, 256, replace=False))
+    f = O.linear_fwd(sR, sP, W0, tR, tP, iR, iP, X[rows])
+    Wref = f["W"]
+    g = O.linear_bwd(sR, sP, W0, tR, tP, iR, iP, X, dY)
+    errs = {
+        "W": rel(to_np(W)[:, :lin.n], Wref),
+        "Y_rows": rel(to_np(Y)[rows, :lin.m], f["Y"]),
+        "dX_rows": rel(to_np(dX)[rows, :lin.n], g["dX"][rows]),
+        "dthetaR": rel(to_np(pl.dthetaR)[:len(tR)], g["dthetaR"]),
+        "dthetaP": rel(to_np(pl.dthetaP)[:len(tP)], g["dthetaP"]),
+    }
+    announce(f"fullsize errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL[lin.act_dtype], (k, v)
+
+
+@pytest.mark.parametrize("name", ["gate", "down", "q"])
+def test_llama1p3b_bs256_fullsize(name):
+    _run(3, name)
+
+
+@pytest.mark.parametrize("name", ["up", "o"])
+def test_llama1p3b_fs_half_fullsize(name):
+    _run(4, name)
