@@ -103,7 +103,7 @@ size_t poet_workspace_bytes(const poet_layer* L, int op);
 /* Workspace bytes poet_sample_indices needs for dimension d. */
 size_t poet_sample_workspace_bytes(int32_t d);
 /* Workspace bytes poet_build_orthogonal needs: 0 when it is given a powers buffer or k == 0, otherwise
- * room for the power chain (3 * prim_len elements of the side's dtype). */
+ * room for the power chain (k * prim_len elements of the side's dtype). */
 size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
 
 /* ---- the hot path ---------------------------------------------------------------------------------- */
@@ -162,6 +162,29 @@ poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* t
                        uint32_t linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ------------------------------------------------------------------------------------ */
+
+/* One internal GEMM of the library, exposed for kernel-level testing (not part of the layer's hot path):
+ *   out = alpha * op(A) op(B) + beta * D ;  C <- out ;  C2 <- out ;  Acc += gamma * out
+ * A is M x K: a_kmajor != 0 -> A(i,k) = A[i*lda + k], else A[k*lda + i]. B is K x N: b_kmajor != 0 ->
+ * B(k,j) = B[j*ldb + k], else B[k*ldb + j]. Batch z offsets each operand by z times its stride s*; with
+ * Mtot/Ntot/Ktot > 0 the extent of batch z is min(M, Mtot - z*M) (same for N, K). C, C2, D, Acc may be NULL.
+ * a_dt, b_dt, c_dt, c2_dt: POET_F32 or POET_BF16; compute: the MFMA operand type. part / part_elems: float32
+ * scratch that allows split-K on the bf16 path (NULL disables it). All pointers are device pointers.
+ * force_generic != 0 runs the generic kernel even where the bf16 fast kernel applies; *used_fast (nullable)
+ * reports which kernel ran. Validation is minimal (sizes >= 0, non-null A and B): this entry is for tests. */
+typedef struct poet_gemm_desc {
+  int32_t M, N, K, Mtot, Ntot, Ktot, batch;
+  const void* A; int64_t lda, sA; int32_t a_dt, a_kmajor;
+  const void* B; int64_t ldb, sB; int32_t b_dt, b_kmajor;
+  void* C; int64_t ldc, sC; int32_t c_dt;
+  void* C2; int64_t ldc2, sC2; int32_t c2_dt;
+  const float* D; int64_t ldd, sD;
+  float* Acc; int64_t ldacc, sAcc;
+  float alpha, beta, gamma;
+  int32_t compute;
+  float* part; size_t part_elems;
+} poet_gemm_desc;
+poet_status poet_debug_gemm(const poet_gemm_desc* d, int force_generic, int* used_fast, void* stream);
 
 /* Kernel classes timed by the optional launch profiler. */
 enum {

@@ -25,7 +25,7 @@ POET_MAX_K, POET_MAX_PRIM = 16, 8192
 EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len", "poet_workspace_bytes",
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
-           "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query")
+           "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC = range(8)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc")
@@ -46,6 +46,21 @@ class poet_layer(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("T", ctypes.c_int32), ("ldw", ctypes.c_int32),
                 ("ldx", ctypes.c_int32), ("ldy", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("R", poet_side), ("P", poet_side)]
+
+
+class poet_gemm_desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("Mtot", ctypes.c_int32),
+                ("Ntot", ctypes.c_int32), ("Ktot", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("sA", ctypes.c_int64), ("a_dt", ctypes.c_int32),
+                ("a_kmajor", ctypes.c_int32),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("sB", ctypes.c_int64), ("b_dt", ctypes.c_int32),
+                ("b_kmajor", ctypes.c_int32),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("sC", ctypes.c_int64), ("c_dt", ctypes.c_int32),
+                ("C2", ctypes.c_void_p), ("ldc2", ctypes.c_int64), ("sC2", ctypes.c_int64), ("c2_dt", ctypes.c_int32),
+                ("D", ctypes.c_void_p), ("ldd", ctypes.c_int64), ("sD", ctypes.c_int64),
+                ("Acc", ctypes.c_void_p), ("ldacc", ctypes.c_int64), ("sAcc", ctypes.c_int64),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("gamma", ctypes.c_float),
+                ("compute", ctypes.c_int32), ("part", ctypes.c_void_p), ("part_elems", ctypes.c_size_t)]
 
 
 _lib = None
@@ -86,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.poet_profile_query.argtypes = [ctypes.c_int, P(ctypes.c_int64), P(ctypes.c_double), P(ctypes.c_double),
                                      P(ctypes.c_double)]
     L.poet_profile_query.restype = ctypes.c_int
+    L.poet_debug_gemm.argtypes = [P(poet_gemm_desc), ctypes.c_int, P(ctypes.c_int), VP]
+    L.poet_debug_gemm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -150,6 +167,15 @@ def poet_version() -> str:
 
 def poet_profile_enable(on: bool) -> None:
     lib().poet_profile_enable(int(bool(on)))
+
+
+def poet_debug_gemm(desc: poet_gemm_desc, force_generic: bool = False, stream=None) -> bool:
+    """Run one internal GEMM (kernel-level tests). The caller fills the descriptor with device pointers whose
+    buffers it has sized for the described extents. Returns whether the bf16 fast kernel ran."""
+    used = ctypes.c_int(0)
+    _check(lib().poet_debug_gemm(ctypes.byref(desc), int(bool(force_generic)), ctypes.byref(used), _stream(stream)),
+           "poet_debug_gemm")
+    return bool(used.value)
 
 
 def poet_profile_query(kclass: int) -> dict:

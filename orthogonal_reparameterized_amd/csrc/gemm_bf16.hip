@@ -1,0 +1,356 @@
+// bf16 x bf16 -> float32 GEMM on gfx950 MFMA, used for every bf16 contraction of the POET layer:
+//   token GEMMs        Y = X W^T, dX = dY W, G = dY^T X (K = tokens)
+//   weight side        factors applied to W0, primitive-gradient contractions, Cayley-Neumann power chain
+//                      and its adjoint (batched over the primitives of a side)
+//
+// Workgroup tile 256 x 256 x 64, 4 waves in a 2 x 2 grid, each wave 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16.
+// Operands go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16
+// bytes at the wave's LDS base + 16 l, from any global address it chooses), in a two-stage ring: the DMA of
+// K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile. Both stage layouts are 32 KB:
+//   K-major operand: 256 rows x 128 B; the 16-byte chunk index is XOR-ed with f(row mod 32) =
+//     (row & 7) ^ ((row >> 3) & 3): 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
+//     groups, so the ds_read_b128 fragments are conflict-free;
+//   M/N-major operand: 64 k-rows x 512 B; the 64-byte block index is XOR-ed with (k-row & 3), so the 4 k-rows a
+//     16-lane group reads with ds_read_b64_tr_b16 fall in 4 different 64-byte bank windows (in each 16-lane
+//     group, lane j supplies the address of 4 consecutive elements of k-row j/4; lane i receives the elements
+//     of column i of those 4 k-rows: an MFMA fragment of the transposed operand).
+// Rows or columns past M / N are fetched from a clamped (valid) address: they only reach outputs that are
+// never stored. The K tail of the last tile is zeroed in LDS after its DMA lands.
+//
+// Work decomposition: (batch, split, tile) triples in one 1-D grid. Workgroup id w runs on XCD w % 8, so each
+// XCD takes a contiguous range of that order: neighbouring tiles on one XCD share A rows in its L2. With
+// split-K each split writes its float32 partial tile; a second kernel sums the partials in split order (so
+// results do not depend on timing) and applies the epilogue.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace poet {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int STAGE = 256 * BK * 2;  // bytes of one operand's stage (both layouts)
+
+struct FastArgs {
+  GemmDesc g;
+  int ntm, ntn, splits, kchunk;
+  int use_part;  // write float32 partial tiles; a second kernel reduces them and applies the epilogue
+};
+
+// an epilogue the main kernel stores directly: out = acc into C (no addend, scale, second copy or accumulate)
+inline bool plain_epilogue(const GemmDesc& g) { return !g.D && !g.C2 && !g.Acc && g.alpha == 1.f && g.C; }
+
+__device__ __forceinline__ int swz(int r32) { return (r32 & 7) ^ ((r32 >> 3) & 3); }
+
+// Direct global->LDS DMA of one 256 x 64 operand tile. Per-thread source offsets are fixed for the K loop.
+template <bool KMAJ>
+struct Operand {
+  const char* base;  // operand base (bytes)
+  uint32_t ld2;      // leading dimension in bytes
+  int R, K;
+  uint32_t off[8];   // byte offset of this lane's source for DMA instruction j: row base (K-major) / column
+  int chk;           // K-major: logical 16-byte chunk this lane fetches
+
+  __device__ __forceinline__ void init(const __bf16* b, int64_t ld, int r0, int R_, int K_, int wave, int lane) {
+    base = reinterpret_cast<const char*>(b);
+    ld2 = (uint32_t)(ld * 2);
+    R = R_; K = K_;
+    if constexpr (KMAJ) {
+      // instruction j of wave w fills rows 8 (4 j + w) + lane / 8, physical chunk lane % 8, whose logical
+      // chunk (k offset / 8 inside the tile) is chk
+      const int r32 = 8 * wave + (lane >> 3);
+      chk = (lane & 7) ^ swz(r32);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = min(r0 + 32 * j + r32, R - 1);
+        off[j] = (uint32_t)row * ld2;
+      }
+    } else {
+      // instruction j of wave w fills k-rows 2 (4 j + w) + lane / 32, physical 16-byte chunk lane % 32
+      const int pc = lane & 31;
+      const int kr4 = (2 * wave + (lane >> 5)) & 3;
+      const int lch = (((pc >> 2) ^ kr4) << 2) | (pc & 3);
+      const int rmax = ((R + 7) / 8) * 8 - 8;
+      const int col = min(r0 + lch * 8, rmax);
+      chk = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) off[j] = (uint32_t)col * 2;  // k-row added per tile
+    }
+  }
+
+  __device__ __forceinline__ void dma(char* __restrict__ st, int k0, int wave, int lane) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      char* dst = st + (4 * j + wave) * 1024;
+      uint32_t o;
+      if constexpr (KMAJ) {
+        const int kmax = ((K + 7) / 8) * 8 - 8;  // keep the 16-byte read inside the row's first ceil8(K) elements
+        o = off[j] + (uint32_t)min(k0 + 8 * chk, kmax) * 2;
+      } else {
+        const int kr = min(k0 + 2 * (4 * j + wave) + (lane >> 5), K - 1);
+        o = off[j] + (uint32_t)kr * ld2;
+      }
+      __builtin_amdgcn_global_load_lds((gbl_void*)(base + o), (lds_void*)dst, 16, 0, 0);
+    }
+  }
+
+  // zero the part of a staged tile that lies at k >= kend (kv = kend - k0 valid k values, 0 < kv < 64)
+  __device__ __forceinline__ void zero_tail(char* __restrict__ st, int kv, int tid) const {
+    if constexpr (KMAJ) {
+      const int row = tid, s = swz(row & 31);
+      for (int k = kv; k < BK; ++k)
+        *reinterpret_cast<short*>(st + row * 128 + (((k >> 3) ^ s) << 4) + (k & 7) * 2) = 0;
+    } else {
+      for (int e = kv * 32 + tid; e < BK * 32; e += 256)
+        *reinterpret_cast<u32x4*>(st + e * 16) = u32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// MFMA operand fragment for rows [rb, rb + 32) (rb a multiple of 32) and k-step ks of a staged tile.
+template <bool KMAJ>
+__device__ __forceinline__ bf16x8 frag(const char* __restrict__ st, int rb, int ks, int lane) {
+  if constexpr (KMAJ) {
+    const int r32 = lane & 31;
+    const int ch = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(st + (rb + r32) * 128 + ((ch ^ swz(r32)) << 4));
+  } else {
+    const int j = lane & 15;
+    const int kr = ks * 16 + (lane >> 5) * 8 + (j >> 2);
+    const int within = ((lane >> 4) & 1) * 32 + (j & 3) * 8;
+    const int blk = (rb >> 5) ^ (j >> 2);
+    const char* p = st + kr * 512 + blk * 64 + within;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 512));
+    const i16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, c);
+  }
+}
+
+__device__ __forceinline__ void store_out(void* C, int dt, int64_t i, float v) {
+  if (dt == BF16) reinterpret_cast<__bf16*>(C)[i] = (__bf16)v;
+  else reinterpret_cast<float*>(C)[i] = v;
+}
+
+// out = alpha * acc + beta * D ; C <- out ; C2 <- out ; Acc += gamma * out
+__device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, int col, float acc) {
+  float out = g.alpha * acc;
+  if (g.D) out += g.beta * g.D[(int64_t)z * g.sD + (int64_t)row * g.ldd + col];
+  if (g.C) store_out(g.C, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col, out);
+  if (g.C2) store_out(g.C2, g.c2_dt, (int64_t)z * g.sC2 + (int64_t)row * g.ldc2 + col, out);
+  if (g.Acc) g.Acc[(int64_t)z * g.sAcc + (int64_t)row * g.ldacc + col] += g.gamma * out;
+}
+
+// store a wave's 128 x 128 accumulator tile (lane base offset `base`, row pitch ld) as dtype dt
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, int dt, int64_t base, int64_t ld,
+                                           int rlim, int clim) {
+  if (!C) return;
+  if (dt == BF16) {
+    __bf16* cb = reinterpret_cast<__bf16*>(C) + base;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
+        if (dr < rlim) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b * 32 < clim) cb[(int64_t)dr * ld + b * 32] = (__bf16)acc[a][b][r];
+        }
+      }
+  } else {
+    float* cb = reinterpret_cast<float*>(C) + base;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
+        if (dr < rlim) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b * 32 < clim) cb[(int64_t)dr * ld + b * 32] = acc[a][b][r];
+        }
+      }
+  }
+}
+
+template <bool AK, bool BK_>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(const FastArgs fa_) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
+  const GemmDesc& g = fa_.g;
+  const int ntm = fa_.ntm, ntn = fa_.ntn, splits = fa_.splits;
+  const int ntiles = g.batch * splits * ntm * ntn;
+  const int per = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  const int tn = t % ntn, tm = (t / ntn) % ntm, zs = t / (ntn * ntm);
+  const int s = zs % splits, z = zs / splits;
+  int M = g.M, N = g.N, K = g.K;
+  if (g.Mtot > 0) M = min(M, g.Mtot - z * g.M);
+  if (g.Ntot > 0) N = min(N, g.Ntot - z * g.N);
+  if (g.Ktot > 0) K = min(K, g.Ktot - z * g.K);
+  const int m0 = tm * BM, n0 = tn * BN;
+  if (m0 >= M || n0 >= N) return;
+  const int kb = s * fa_.kchunk, ke = min(K, kb + fa_.kchunk);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+
+  Operand<AK> oa;
+  Operand<BK_> ob;
+  oa.init(reinterpret_cast<const __bf16*>(g.A) + (int64_t)z * g.sA, g.lda, m0, M, ke, wave, lane);
+  ob.init(reinterpret_cast<const __bf16*>(g.B) + (int64_t)z * g.sB, g.ldb, n0, N, ke, wave, lane);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int nk = kb < ke ? (ke - kb + BK - 1) / BK : 0;
+  if (nk > 0) {
+    oa.dma(smem, kb, wave, lane);
+    ob.dma(smem + STAGE, kb, wave, lane);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    char* sa = smem + (kt & 1) * 2 * STAGE;
+    char* sb = sa + STAGE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int kv = ke - (kb + kt * BK);
+    if (kv < BK) {  // last, partial K tile
+      oa.zero_tail(sa, kv, tid);
+      ob.zero_tail(sb, kv, tid);
+      __syncthreads();
+    }
+    if (kt + 1 < nk) {
+      char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
+      oa.dma(na, kb + (kt + 1) * BK, wave, lane);
+      ob.dma(na + STAGE, kb + (kt + 1) * BK, wave, lane);
+    }
+    // fragments of k-step ks + 1 are read from LDS while the 16 MFMAs of k-step ks run
+    bf16x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(sa, wr + a * 32, 0, lane);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(sb, wc + b * 32, 0, lane);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
+      }
+      // the next k-step's LDS reads stay ahead of this k-step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][b], acc[a][b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // accumulator r of lane l in a 32x32 tile is C[(r/4)*8 + (l/32)*4 + r%4][l%32]
+  const int row0 = m0 + wr + (lane >> 5) * 4, col0 = n0 + wc + (lane & 31);
+  const int rlim = M - row0, clim = N - col0;
+  if (fa_.use_part) {  // raw partial tile; the reduction kernel sums the splits and applies the epilogue
+    float* pb = g.part + ((int64_t)(s * g.batch + z) * g.M + row0) * g.N + col0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
+        if (dr < rlim) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b * 32 < clim) pb[(int64_t)dr * g.N + b * 32] = acc[a][b][r];
+        }
+      }
+    return;
+  }
+  store_tile(acc, g.C, g.c_dt, (int64_t)z * g.sC + (int64_t)row0 * g.ldc + col0, g.ldc, rlim, clim);
+}
+
+// Sum the split-K partials of every output element in split order, then apply the epilogue.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) {
+  const GemmDesc& g = fa_.g;
+  const int64_t mn = (int64_t)g.M * g.N, total = (int64_t)g.batch * mn;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int z = (int)(e / mn);
+    const int64_t rc = e - (int64_t)z * mn;
+    const int row = (int)(rc / g.N), col = (int)(rc - (int64_t)row * g.N);
+    int M = g.M, N = g.N;
+    if (g.Mtot > 0) M = min(M, g.Mtot - z * g.M);
+    if (g.Ntot > 0) N = min(N, g.Ntot - z * g.N);
+    if (row >= M || col >= N) continue;
+    float sum = 0.f;
+    for (int s = 0; s < fa_.splits; ++s) sum += g.part[(int64_t)(s * g.batch + z) * mn + rc];
+    epilogue_one(g, z, row, col, sum);
+  }
+}
+
+}  // namespace
+
+bool fast_gemm_eligible(const GemmDesc& g) {
+  auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (g.compute != BF16 || g.a_dt != BF16 || g.b_dt != BF16 || g.a_sub_eye || g.b_sub_eye) return false;
+  if (g.M < 128 || g.N < 128 || g.batch < 1) return false;
+  if (!plain_epilogue(g) && (!g.part || g.part_elems < (size_t)g.batch * g.M * g.N)) return false;
+  if (g.lda % 8 || g.ldb % 8 || g.sA % 8 || g.sB % 8 || !al(g.A) || !al(g.B)) return false;
+  // 32-bit byte offsets inside one batch's operands
+  const double ea = 2.0 * (g.a_kmajor ? g.M : g.K) * (double)g.lda, eb = 2.0 * (g.b_kmajor ? g.N : g.K) * (double)g.ldb;
+  return ea < 2.0e9 && eb < 2.0e9;
+}
+
+hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  FastArgs fa;
+  fa.g = g;
+  fa.ntm = (g.M + BM - 1) / BM;
+  fa.ntn = (g.N + BN - 1) / BN;
+  const int tiles = g.batch * fa.ntm * fa.ntn;
+  const int nk = (g.K + BK - 1) / BK;
+  // split K until one round of the machine (256 CUs, one workgroup each) is covered, keeping >= 2 K-tiles per
+  // split and the partials within the scratch the caller provided
+  int S = 1;
+  while (tiles * S < 200 && nk >= 4 * S && S < 16 &&
+         (size_t)(2 * S) * g.batch * (size_t)g.M * g.N <= g.part_elems && g.part)
+    S *= 2;
+  fa.splits = S;
+  fa.kchunk = ((nk + S - 1) / S) * BK;
+  fa.use_part = (S > 1 || !plain_epilogue(g)) ? 1 : 0;
+  const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
+  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) +
+                                  (double)g.M * g.N * ((g.C ? dtype_size(g.c_dt) : 0) + (g.D ? 4 : 0) +
+                                                       (g.C2 ? dtype_size(g.c2_dt) : 0) + (g.Acc ? 8 : 0)));
+  ProfScope prof(g.kclass, st, flops, bytes);
+  const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
+  if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), grid, block, 0, st, fa);
+  else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), grid, block, 0, st, fa);
+  else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), grid, block, 0, st, fa);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, block, 0, st, fa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !fa.use_part) return e;
+  const int64_t total = (int64_t)g.batch * g.M * g.N;
+  const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
+  return hipGetLastError();
+}
+
+}  // namespace poet

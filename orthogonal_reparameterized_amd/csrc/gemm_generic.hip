@@ -139,6 +139,11 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const GemmDesc g) {
             if (g.c_dt == BF16) reinterpret_cast<__bf16*>(g.C)[ci] = (__bf16)out;
             else reinterpret_cast<float*>(g.C)[ci] = out;
           }
+          if (g.C2) {
+            const int64_t ci = (int64_t)z * g.sC2 + (int64_t)i * g.ldc2 + j;
+            if (g.c2_dt == BF16) reinterpret_cast<__bf16*>(g.C2)[ci] = (__bf16)out;
+            else reinterpret_cast<float*>(g.C2)[ci] = out;
+          }
           if (g.Acc) g.Acc[za + (int64_t)i * g.ldacc + j] += g.gamma * out;
         }
       }
@@ -159,9 +164,15 @@ hipError_t launch_t(const GemmDesc& g, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmDesc& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  if (fast_gemm_eligible(g)) return launch_fast_gemm(g, st);
+  return launch_generic_gemm(g, st);
+}
+
+hipError_t launch_generic_gemm(const GemmDesc& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   const double mn = (double)g.M * g.N, bt = g.batch;
   const double bytes = bt * ((double)g.M * g.K * dtype_size(g.a_dt) + (double)g.K * g.N * dtype_size(g.b_dt) +
-                             (g.C ? mn * dtype_size(g.c_dt) : 0.0) + (g.D ? mn * 4.0 : 0.0) + (g.Acc ? mn * 8.0 : 0.0));
+                             (g.C ? mn * dtype_size(g.c_dt) : 0.0) + (g.C2 ? mn * dtype_size(g.c2_dt) : 0.0) + (g.D ? mn * 4.0 : 0.0) + (g.Acc ? mn * 8.0 : 0.0));
   ProfScope prof(g.kclass, st, 2.0 * mn * g.K * bt, bytes);
   const bool small = g.M <= 64 || g.N <= 64;
   if (g.compute == BF16) return small ? launch_t<64, 64, true>(g, st) : launch_t<128, 128, true>(g, st);

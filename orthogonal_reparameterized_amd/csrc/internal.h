@@ -32,7 +32,16 @@ struct GemmDesc {
   float alpha = 1.f, beta = 0.f, gamma = 0.f;
   int compute = F32;
   int kclass = 7;  // profiler kernel class (POET_K_* in poet.h)
+  // optional second copy of the output (e.g. a float32 and a bf16 version of the same product)
+  void* C2 = nullptr; int64_t ldc2 = 0, sC2 = 0; int c2_dt = F32;
+  // optional float32 scratch for split-K partial sums on the bf16 fast path (deterministic reduction)
+  float* part = nullptr; size_t part_elems = 0;
 };
+
+// Fast path for bf16 x bf16 products (gemm_bf16.hip): 256x256x64 tiles, batched, split-K. Returns false (and
+// launches nothing) when the descriptor does not qualify; launch_gemm then uses the generic kernel.
+bool fast_gemm_eligible(const GemmDesc& g);
+hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
 
 // launch profiler (profiler.hip): no-ops unless poet_profile_enable(1) was called
 int prof_begin(int kclass, hipStream_t st, double flops, double bytes);
@@ -45,17 +54,9 @@ struct ProfScope {
 };
 
 hipError_t launch_gemm(const GemmDesc& g, hipStream_t st);
+hipError_t launch_generic_gemm(const GemmDesc& g, hipStream_t st);  // never the fast path
 
-// Token GEMM on bf16 MFMA (gemm_tokens.hip): C (M x N, bf16 or float32) = A (M x K) B (K x N), both bf16, with
-// the same orientation flags as GemmDesc. Needs lda, ldb multiples of 8 and 16-byte aligned A, B.
-struct TokGemm {
-  int M = 0, N = 0, K = 0;
-  const __bf16* A = nullptr; int64_t lda = 0; int a_kmajor = 1;
-  const __bf16* B = nullptr; int64_t ldb = 0; int b_kmajor = 1;
-  void* C = nullptr; int64_t ldc = 0; int c_f32 = 0;
-};
-bool tok_gemm_supported(const TokGemm& p);
-hipError_t launch_tok_gemm(const TokGemm& p, int kclass, hipStream_t st);
+
 
 // ---- elementwise / data-movement kernels (kernels_misc.hip) ------------------------------------------
 // theta -> prim = I + coef*Q (coef 1 for k = 0, else 2) and, when q_out != null, Q in dtype q_dt.
@@ -82,6 +83,15 @@ hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
                                void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st);
+// prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1} with prim holding P_{k+1} on entry (k >= 1), Q from theta
+hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
+                                 int dt, float* prim, hipStream_t st);
+// out = bf16(prim - I) for nprim bp x bp primitives (the delta of a factor as an MFMA operand)
+hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, __bf16* out, hipStream_t st);
+// Coefficient polynomials of the two-phase Neumann adjoint, stacked per primitive as a (k+1) bp x bp matrix:
+//   block j = sum_{t} a_{t+j+1} (-1)^{t+j} Q^t over t = 0..k-j (t >= 1 for j = 0), Q^0 = I, Q^t = powers[t-1],
+// with a_i = 2 for i <= k and a_{k+1} = 1. Written in dtype dt (the powers' dtype).
+hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int k, void* out, hipStream_t st);
 uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch);
 
 }  // namespace poet

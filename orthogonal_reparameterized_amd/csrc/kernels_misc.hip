@@ -194,7 +194,87 @@ __global__ void k_sample_compact(int d, const int32_t* __restrict__ flags, int32
   }
 }
 
+__global__ void k_delta_bf16(const float* __restrict__ prim, int64_t total, int bp, __bf16* __restrict__ out) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int rem = (int)(e % ((int64_t)bp * bp));
+    out[e] = (__bf16)(prim[e] - ((rem / bp) == (rem % bp) ? 1.f : 0.f));
+  }
+}
+
+__device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
+  return dt == BF16 ? (float)reinterpret_cast<const __bf16*>(p)[i] : reinterpret_cast<const float*>(p)[i];
+}
+
+// element (p, j, r, c) of the stacked coefficient matrices; see launch_adjoint_coefs
+__global__ void k_adjoint_coefs(const void* __restrict__ powers, int dt, int nprim, int bp, int k,
+                                void* __restrict__ out) {
+  const int64_t pp = (int64_t)bp * bp, per = (int64_t)(k + 1) * pp, total = (int64_t)nprim * per;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(e / per);
+    const int64_t q = e - (int64_t)p * per;
+    const int j = (int)(q / pp);
+    const int rc = (int)(q - (int64_t)j * pp);
+    const int r = rc / bp, c = rc % bp;
+    float v = 0.f;
+    for (int t = (j == 0 ? 1 : 0); t <= k - j; ++t) {
+      const int i = t + j + 1;
+      const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
+      const float pt = t == 0 ? (r == c ? 1.f : 0.f) : ld_dt(powers, dt, ((int64_t)(t - 1) * nprim + p) * pp + rc);
+      v += a * pt;
+    }
+    if (dt == BF16) reinterpret_cast<__bf16*>(out)[e] = (__bf16)v;
+    else reinterpret_cast<float*>(out)[e] = v;
+  }
+}
+
+// prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
+// (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1
+__global__ void k_chain_finalize(const float* __restrict__ theta, int mode, int d, int bp, int nprim, int k,
+                                 const void* __restrict__ powers, int dt, float* __restrict__ prim) {
+  const int64_t pp = (int64_t)bp * bp, total = (int64_t)nprim * pp;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(e / pp);
+    const int rem = (int)(e - (int64_t)p * pp);
+    const int i = rem / bp, j = rem % bp;
+    const int c = prim_size(mode, d, bp, p);
+    float q = 0.f;
+    if (i < c && j < c && i != j) {
+      const int64_t off = theta_off(bp, p);
+      q = i < j ? theta[off + tri_pos(i, j, c)] : -theta[off + tri_pos(j, i, c)];
+    }
+    float s = 0.f;
+    for (int t = 2; t <= k; ++t) s += ld_dt(powers, dt, (int64_t)(t - 1) * total + e);
+    prim[e] = (i == j ? 1.f : 0.f) + 2.f * q + 2.f * s + prim[e];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
+                                 int dt, float* prim, hipStream_t st) {
+  const int64_t total = (int64_t)nprim * bp * bp;
+  if (total == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)total * (8 + 4 + (k - 1) * dtype_size(dt)));
+  hipLaunchKernelGGL(k_chain_finalize, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim, k, powers,
+                     dt, prim);
+  return hipGetLastError();
+}
+
+hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, __bf16* out, hipStream_t st) {
+  const int64_t total = (int64_t)nprim * bp * bp;
+  if (total == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)total * 6);
+  hipLaunchKernelGGL(k_delta_bf16, dim3(grid_for(total)), dim3(kThreads), 0, st, prim, total, bp, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int k, void* out, hipStream_t st) {
+  const int64_t total = (int64_t)nprim * (k + 1) * bp * bp;
+  if (total == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)total * dtype_size(dt) * 2);
+  hipLaunchKernelGGL(k_adjoint_coefs, dim3(grid_for(total)), dim3(kThreads), 0, st, powers, dt, nprim, bp, k, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim, void* q_out,
                              int q_dt, hipStream_t st) {

@@ -168,69 +168,138 @@ hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, con
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// Backward through the truncated Cayley-Neumann series of one side, then the skew projection.
-// With R_k = I + sum_i a_i Q^i (a_i = 2 for i <= k, a_{k+1} = 1) and saved powers P_i = Q^i, the reverse
-// recursion G_{k+1} = dR, G_{i-1} = a_{i-1} dR + Q^T G_i, dQ = G_1 + sum_{i>=2} G_i P_{i-1}^T
-// uses Q^T = -Q and P_i^T = (-1)^i P_i, so every product is a plain row-major GEMM.
+// bf16 application of block-diagonal factors (both sides POET-BS, bf16 activations). The factor deltas and a
+// bf16 copy of W0 are MFMA operands; the identity parts are added in float32 through the epilogue addend.
+//   apply_P_b: T = W0 + W0 dP  -> Tb (bf16) and, when Tf != null, Tf (float32)
+//   apply_R_b: out = src + dR src, with src given as a bf16 operand (srcb) and in float32 (srcf)
 // ------------------------------------------------------------------------------------------------------------
-struct AdjBufs {
-  float *dQ = nullptr, *Ga = nullptr, *Gb = nullptr;
+struct Part {  // float32 scratch through which the bf16 kernel applies addend epilogues and split-K
+  float* p = nullptr;
+  size_t n = 0;
 };
 
-hipError_t neumann_adjoint(const SideInfo& S, const float* dRb, const void* powers, float* dtheta, const AdjBufs& b,
+// part elements the bf16 factor applications need: one float32 product per output element (block-padded)
+size_t apply_part_elems(const poet_layer& L, const SideInfo& R, const SideInfo& P) {
+  return std::max((size_t)P.nprim * P.bp * L.m, (size_t)R.nprim * R.bp * L.n);
+}
+
+hipError_t apply_P_b(const poet_layer& L, const SideInfo& P, const float* W0, const __bf16* W0b, const __bf16* dPb,
+                     __bf16* Tb, float* Tf, const Part& part, hipStream_t st) {
+  GemmDesc g;
+  g.part = part.p; g.part_elems = part.n;
+  g.kclass = POET_K_APPLY;
+  g.compute = BF16;
+  g.M = L.m; g.N = P.bp; g.K = P.bp; g.Ntot = L.n; g.Ktot = L.n; g.batch = P.nprim;
+  g.A = W0b; g.lda = L.ldw; g.sA = P.bp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = dPb; g.ldb = P.bp; g.sB = (int64_t)P.bp * P.bp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.D = W0; g.ldd = L.ldw; g.sD = P.bp; g.beta = 1.f;
+  g.C = Tb; g.ldc = L.ldw; g.sC = P.bp; g.c_dt = BF16;
+  if (Tf) { g.C2 = Tf; g.ldc2 = L.ldw; g.sC2 = P.bp; g.c2_dt = F32; }
+  return launch_gemm(g, st);
+}
+
+hipError_t apply_R_b(const poet_layer& L, const SideInfo& R, const __bf16* srcb, const float* srcf, const __bf16* dRb,
+                     void* out, int out_dt, const Part& part, hipStream_t st) {
+  GemmDesc g;
+  g.part = part.p; g.part_elems = part.n;
+  g.kclass = POET_K_APPLY;
+  g.compute = BF16;
+  g.M = R.bp; g.N = L.n; g.K = R.bp; g.Mtot = L.m; g.Ktot = L.m; g.batch = R.nprim;
+  g.A = dRb; g.lda = R.bp; g.sA = (int64_t)R.bp * R.bp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = srcb; g.ldb = L.ldw; g.sB = (int64_t)R.bp * L.ldw; g.b_dt = BF16; g.b_kmajor = 0;
+  g.D = srcf; g.ldd = L.ldw; g.sD = (int64_t)R.bp * L.ldw; g.beta = 1.f;
+  g.C = out; g.ldc = L.ldw; g.sC = (int64_t)R.bp * L.ldw; g.c_dt = out_dt;
+  return launch_gemm(g, st);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Backward through the truncated Cayley-Neumann series of one side, then the skew projection.
+// R_k = I + sum_{i=1}^{k+1} a_i Q^i with a_i = 2 (i <= k), a_{k+1} = 1. The gradient of <dR, R_k> is
+//   dQ = sum_i a_i sum_{j<i} (Q^T)^j dR (Q^T)^{i-1-j} = sum_{j=0}^{k} H_j C_j,
+//   H_j = Q^j dR,   C_j = sum_{t=0}^{k-j} a_{t+j+1} (-1)^{t+j} Q^t     (using Q^T = -Q).
+// Phase 1 builds H_1..H_k by k products with Q (H_0 = dR); phase 2 is one product with K = (k+1) b against the
+// stacked C_j (polynomials in Q formed elementwise from the saved powers). The identity term a_1 dR of H_0 C_0
+// is added in float32 through the epilogue addend, so only the higher-order corrections carry operand rounding.
+// ------------------------------------------------------------------------------------------------------------
+struct AdjBufs {
+  float* dQ = nullptr;
+  void* H = nullptr;   // nprim x b x (k+1) b, side dtype
+  void* Cs = nullptr;  // nprim x (k+1) b x b, side dtype
+  float* part = nullptr;
+  size_t part_elems = 0;
+};
+
+size_t adj_elems(const SideInfo& S) { return (size_t)S.nprim * S.bp * S.bp * (S.k + 1); }
+
+hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powers, float* dtheta, const AdjBufs& b,
                            hipStream_t st) {
   if (S.theta_len == 0) return hipSuccess;
-  if (S.k == 0) return launch_skew_project(dRb, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
-  const int64_t pp = (int64_t)S.bp * S.bp;
+  if (S.k == 0) return launch_skew_project(dRg, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+  const int bp = S.bp, k = S.k, ldh = (k + 1) * bp;
+  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
   const size_t esz = dtype_size(S.dtype);
-  const char* pw = reinterpret_cast<const char*>(powers);
-  const float* Gcur = dRb;
-  float* bufs[2] = {b.Ga, b.Gb};
-  int nb = 0;
-  hipError_t e;
-  for (int i = S.k + 1; i >= 2; --i) {
-    GemmDesc g;  // dQ (+)= (-1)^(i-1) G_i P_{i-1}
+  char* H = reinterpret_cast<char*>(b.H);
+  hipError_t e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
+  if (e != hipSuccess) return e;
+  for (int j = 0; j < k; ++j) {  // H_{j+1} = Q H_j
+    GemmDesc g;
     g.kclass = POET_K_ADJOINT;
-    g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
-    g.A = Gcur; g.lda = S.bp; g.sA = pp; g.a_dt = F32; g.a_kmajor = 1;
-    g.B = pw + (size_t)(i - 2) * S.prim_len * esz; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
-    g.alpha = ((i - 1) & 1) ? -1.f : 1.f;
-    if (i != S.k + 1) { g.D = b.dQ; g.ldd = S.bp; g.sD = pp; g.beta = 1.f; }
-    g.C = b.dQ; g.ldc = S.bp; g.sC = pp; g.c_dt = F32;
+    g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
+    g.A = powers; g.lda = bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
+    g.B = H + (size_t)j * bp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
+    g.C = H + (size_t)(j + 1) * bp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
     if ((e = launch_gemm(g, st)) != hipSuccess) return e;
-    GemmDesc h;  // G_{i-1} = 2 dR - Q G_i
-    h.kclass = POET_K_ADJOINT;
-    h.compute = S.dtype; h.M = h.N = h.K = S.bp; h.batch = S.nprim;
-    h.A = pw; h.lda = S.bp; h.sA = pp; h.a_dt = S.dtype; h.a_kmajor = 1;
-    h.B = Gcur; h.ldb = S.bp; h.sB = pp; h.b_dt = F32; h.b_kmajor = 0;
-    h.alpha = -1.f; h.D = dRb; h.ldd = S.bp; h.sD = pp; h.beta = 2.f;
-    h.C = bufs[nb]; h.ldc = S.bp; h.sC = pp; h.c_dt = F32;
-    if ((e = launch_gemm(h, st)) != hipSuccess) return e;
-    Gcur = bufs[nb];
-    nb ^= 1;
   }
-  return launch_skew_project(b.dQ, Gcur, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+  if ((e = launch_adjoint_coefs(powers, S.dtype, S.nprim, bp, k, b.Cs, st)) != hipSuccess) return e;
+  GemmDesc g;  // dQ = a_1 dR + [H_0 .. H_k] [C_0; ..; C_k]
+  g.kclass = POET_K_ADJOINT;
+  g.compute = S.dtype; g.M = g.N = bp; g.K = (k + 1) * bp; g.batch = S.nprim;
+  g.A = H; g.lda = ldh; g.sA = hs; g.a_dt = S.dtype; g.a_kmajor = 1;
+  g.B = b.Cs; g.ldb = bp; g.sB = (int64_t)(k + 1) * pp; g.b_dt = S.dtype; g.b_kmajor = 0;
+  g.D = dRg; g.ldd = bp; g.sD = pp; g.beta = 2.f;  // a_1 = 2 for k >= 1
+  g.C = b.dQ; g.ldc = bp; g.sC = pp; g.c_dt = F32;
+  g.part = b.part; g.part_elems = b.part_elems;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  return launch_skew_project(b.dQ, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
 }
 
 // ------------------------------------------------------------------------------------------------------------
 // Workspace plans (the same code sizes and carves the workspace)
 // ------------------------------------------------------------------------------------------------------------
+// bf16 block-diagonal path: both sides POET-BS and bf16 activations
+bool bs_bf16(const poet_layer& L, const SideInfo& R, const SideInfo& P) {
+  return L.act_dtype == BF16 && R.mode == POET_BS && P.mode == POET_BS;
+}
+
 struct FwdPlan {
   void* W = nullptr;
-  float* T = nullptr;
+  float* T = nullptr;                    // W0 P, float32
+  __bf16 *W0b = nullptr, *Tb = nullptr;  // bf16 path: W0 and W0 P as bf16 operands
+  __bf16 *dRb = nullptr, *dPb = nullptr; // bf16 path: factor deltas
+  Part part;                             // bf16 path: epilogue scratch of the factor applications
   FsBufs fs;
 };
 size_t plan_fwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, bool need_W, FwdPlan* p) {
   Arena a(ws);
-  if (need_W) p->W = a.take_bytes((size_t)L.m * L.ldw * dtype_size(L.act_dtype));
-  p->T = a.take<float>((size_t)L.m * L.ldw);
+  const size_t mn = (size_t)L.m * L.ldw;
+  if (need_W) p->W = a.take_bytes(mn * dtype_size(L.act_dtype));
+  p->T = a.take<float>(mn);
+  if (bs_bf16(L, R, P)) {
+    p->W0b = a.take<__bf16>(mn);
+    p->Tb = a.take<__bf16>(mn);
+    p->dRb = a.take<__bf16>(R.prim_len);
+    p->dPb = a.take<__bf16>(P.prim_len);
+    p->part.n = apply_part_elems(L, R, P);
+    p->part.p = a.take<float>(p->part.n);
+  }
   plan_fs(a, L, R, P, &p->fs);
   return a.used();
 }
 
 struct BwdPlan {
   void* W = nullptr;
-  float *T = nullptr, *RW0 = nullptr, *G = nullptr, *dRb = nullptr, *dPb = nullptr;
+  float *T = nullptr, *RW0 = nullptr, *G = nullptr, *dRg = nullptr, *dPg = nullptr;
+  __bf16 *W0b = nullptr, *Tb = nullptr, *RW0b = nullptr, *Gb = nullptr, *dRb = nullptr, *dPb = nullptr;
   AdjBufs adj;
   FsBufs fs;
   float *Gr = nullptr, *Zr = nullptr, *Acp = nullptr, *Gc = nullptr;
@@ -239,15 +308,29 @@ size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void*
   Arena a(ws);
   const size_t mn = (size_t)L.m * L.ldw;
   if (need_W) p->W = a.take_bytes(mn * dtype_size(L.act_dtype));
-  p->T = a.take<float>(mn);
-  p->RW0 = a.take<float>(mn);
-  p->G = a.take<float>(mn);
-  p->dRb = a.take<float>(R.prim_len);
-  p->dPb = a.take<float>(P.prim_len);
-  const size_t pl = std::max(R.prim_len, P.prim_len);
-  p->adj.dQ = a.take<float>(pl);
-  p->adj.Ga = a.take<float>(pl);
-  p->adj.Gb = a.take<float>(pl);
+  const bool fast = bs_bf16(L, R, P);
+  if (fast) {
+    if (need_W) p->T = a.take<float>(mn);
+    p->W0b = a.take<__bf16>(mn);
+    p->Tb = a.take<__bf16>(mn);
+    p->RW0b = a.take<__bf16>(mn);
+    p->Gb = a.take<__bf16>(mn);
+    p->dRb = a.take<__bf16>(R.prim_len);
+    p->dPb = a.take<__bf16>(P.prim_len);
+  } else {
+    p->T = a.take<float>(mn);
+    p->RW0 = a.take<float>(mn);
+    p->G = a.take<float>(mn);
+  }
+  p->dRg = a.take<float>(R.prim_len);
+  p->dPg = a.take<float>(P.prim_len);
+  p->adj.dQ = a.take<float>(std::max(R.prim_len, P.prim_len));
+  const size_t hb = std::max(adj_elems(R) * dtype_size(R.dtype), adj_elems(P) * dtype_size(P.dtype));
+  p->adj.H = a.take_bytes(hb);
+  p->adj.Cs = a.take_bytes(hb);
+  // split-K partial sums: the weight gradient with up to 4 splits, or the primitive products with up to 16
+  p->adj.part_elems = std::max({4 * mn, 16 * std::max(R.prim_len, P.prim_len), apply_part_elems(L, R, P)});
+  p->adj.part = a.take<float>(p->adj.part_elems);
   plan_fs(a, L, R, P, &p->fs);
   if (R.mode == POET_FS) { p->Gr = a.take<float>((size_t)R.bp * L.n); p->Zr = a.take<float>((size_t)R.bp * L.n); }
   if (P.mode == POET_FS) { p->Acp = a.take<float>((size_t)L.m * P.bp); p->Gc = a.take<float>((size_t)L.m * P.bp); }
@@ -267,20 +350,6 @@ size_t plan_merge(const poet_layer& L, const SideInfo& R, const SideInfo& P, voi
   plan_fs(a, L, R, P, &p->fs);
   if (R.mode == POET_FS || P.mode == POET_FS) p->flags = a.take<int32_t>((size_t)std::max(L.m, L.n));
   return a.used();
-}
-
-// Token GEMMs run on the dedicated 256x256 bf16 kernel when the operands qualify (bf16, 16-byte aligned rows),
-// otherwise on the generic kernel (float32 activations, odd leading dimensions).
-hipError_t token_gemm(const GemmDesc& g, hipStream_t st) {
-  if (g.compute == BF16 && g.a_dt == BF16 && g.b_dt == BF16 && g.batch == 1 && !g.D && !g.Acc && g.alpha == 1.f) {
-    TokGemm t;
-    t.M = g.M; t.N = g.N; t.K = g.K;
-    t.A = reinterpret_cast<const __bf16*>(g.A); t.lda = g.lda; t.a_kmajor = g.a_kmajor;
-    t.B = reinterpret_cast<const __bf16*>(g.B); t.ldb = g.ldb; t.b_kmajor = g.b_kmajor;
-    t.C = g.C; t.ldc = g.ldc; t.c_f32 = g.c_dt == F32;
-    if (tok_gemm_supported(t)) return launch_tok_gemm(t, g.kclass, st);
-  }
-  return launch_gemm(g, st);
 }
 
 bool check_ws(void* ws, size_t have, size_t need) {
@@ -320,7 +389,7 @@ size_t poet_build_workspace_bytes(const poet_side* s, int with_powers) {
   SideInfo i;
   if (!side_info(s, &i, "side")) return 0;
   if (with_powers || i.k == 0) return 0;
-  return 3 * align_up(i.prim_len * dtype_size(i.dtype), 256) + 256;
+  return align_up((size_t)i.k * i.prim_len * dtype_size(i.dtype), 256) + 512;
 }
 size_t poet_sample_workspace_bytes(int32_t d) { return d > 0 ? align_up((size_t)d * 4, 256) + 256 : 0; }
 
@@ -346,30 +415,29 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   if (!check_ws(ws, ws_bytes, need)) return g_last;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const size_t esz = dtype_size(S.dtype);
+  // powers P_1 = Q, ..., P_k (the caller's buffer, or the workspace when the caller keeps none)
   char* pw = reinterpret_cast<char*>(powers);
-  char* scratch[3] = {nullptr, nullptr, nullptr};
   if (!powers && S.k > 0) {
     Arena a(ws);
-    for (int i = 0; i < 3; ++i) scratch[i] = reinterpret_cast<char*>(a.take_bytes(S.prim_len * esz));
+    pw = reinterpret_cast<char*>(a.take_bytes((size_t)S.k * S.prim_len * esz));
   }
-  const char* Qp = powers ? pw : scratch[0];
-  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)Qp : nullptr, S.dtype, st));
+  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype, st));
   if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
+  if (S.k == 0) return POET_OK;  // R_0 = I + Q
   const int64_t pp = (int64_t)S.bp * S.bp;
-  for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i ; prim += a_{i+1} P_{i+1}
+  for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i; the last power goes straight into prim (float32)
     GemmDesc g;
     g.kclass = POET_K_CHAIN;
     g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
-    g.A = Qp; g.lda = S.bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
-    const char* Pi = powers ? pw + (size_t)(i - 1) * S.prim_len * esz : (i == 1 ? scratch[0] : scratch[1 + (i & 1)]);
-    g.B = Pi; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
-    if (i + 1 <= S.k) {
-      g.C = powers ? (void*)(pw + (size_t)i * S.prim_len * esz) : (void*)scratch[1 + ((i + 1) & 1)];
-      g.ldc = S.bp; g.sC = pp; g.c_dt = S.dtype;
-    }
-    g.Acc = prim; g.ldacc = S.bp; g.sAcc = pp; g.gamma = (i + 1 <= S.k) ? 2.f : 1.f;
+    g.A = pw; g.lda = S.bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
+    g.B = pw + (size_t)(i - 1) * S.prim_len * esz; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
+    if (i < S.k) { g.C = pw + (size_t)i * S.prim_len * esz; g.c_dt = S.dtype; }
+    else { g.C = prim; g.c_dt = F32; }
+    g.ldc = S.bp; g.sC = pp;
     HIP_TRY(launch_gemm(g, st));
   }
+  // prim = I + 2Q + 2(P_2 + ... + P_k) + P_{k+1}, the linear term exact from theta
+  HIP_TRY(launch_chain_finalize(theta, S.mode, S.d, S.bp, S.nprim, S.k, pw, S.dtype, prim, st));
   return POET_OK;
 }
 
@@ -400,8 +468,16 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
   void* W = W_out ? W_out : p.W;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int act = L->act_dtype;
-  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
-  HIP_TRY(apply_R(*L, R, p.T, primR, idxR, W, act, L->ldw, act, p.fs, st));
+  if (bs_bf16(*L, R, P)) {
+    HIP_TRY(launch_convert(W0, L->ldw, p.W0b, L->ldw, BF16, L->m, L->n, st));
+    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));
+    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, p.dPb, st));
+    HIP_TRY(apply_P_b(*L, P, W0, p.W0b, p.dPb, p.Tb, p.T, p.part, st));
+    HIP_TRY(apply_R_b(*L, R, p.Tb, p.T, p.dRb, W, act, p.part, st));
+  } else {
+    HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
+    HIP_TRY(apply_R(*L, R, p.T, primR, idxR, W, act, L->ldw, act, p.fs, st));
+  }
   if (L->T > 0) {  // Y = X W^T
     GemmDesc g;
     g.kclass = POET_K_TOKEN_FWD;
@@ -409,7 +485,7 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
     g.A = X; g.lda = L->ldx; g.a_dt = act; g.a_kmajor = 1;
     g.B = W; g.ldb = L->ldw; g.b_dt = act; g.b_kmajor = 1;
     g.C = Y; g.ldc = L->ldy; g.c_dt = act;
-    HIP_TRY(token_gemm(g, st));
+    HIP_TRY(launch_gemm(g, st));
   }
   return POET_OK;
 }
@@ -433,15 +509,29 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int act = L->act_dtype, m = L->m, n = L->n;
   const int64_t ldw = L->ldw;
-  // Z = W0 P (needed by the R-side gradient) and, when not given, W = R Z
-  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
+  const bool fast = bs_bf16(*L, R, P);
   const void* W = Win;
-  if (!W) {
-    HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.W, act, ldw, act, p.fs, st));
-    W = p.W;
+  if (fast) {
+    // bf16 operands: W0, the factor deltas, Z = W0 P (R-side gradient), R W0 (P-side gradient), G
+    HIP_TRY(launch_convert(W0, ldw, p.W0b, ldw, BF16, m, n, st));
+    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));
+    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, p.dPb, st));
+    HIP_TRY(apply_P_b(*L, P, W0, p.W0b, p.dPb, p.Tb, W ? nullptr : p.T, Part{p.adj.part, p.adj.part_elems}, st));
+    if (!W) {
+      HIP_TRY(apply_R_b(*L, R, p.Tb, p.T, p.dRb, p.W, act, Part{p.adj.part, p.adj.part_elems}, st));
+      W = p.W;
+    }
+    HIP_TRY(apply_R_b(*L, R, p.W0b, W0, p.dRb, p.RW0b, BF16, Part{p.adj.part, p.adj.part_elems}, st));
+  } else {
+    // Z = W0 P (needed by the R-side gradient) and, when not given, W = R Z
+    HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
+    if (!W) {
+      HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.W, act, ldw, act, p.fs, st));
+      W = p.W;
+    }
+    // R W0 (needed by the P-side gradient)
+    HIP_TRY(apply_R(*L, R, W0, primR, idxR, p.RW0, F32, ldw, act, p.fs, st));
   }
-  // R W0 (needed by the P-side gradient)
-  HIP_TRY(apply_R(*L, R, W0, primR, idxR, p.RW0, F32, ldw, act, p.fs, st));
   if (dX && L->T > 0) {  // dX = dY W
     GemmDesc g;
     g.kclass = POET_K_TOKEN_DX;
@@ -449,7 +539,7 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 1;
     g.B = W; g.ldb = ldw; g.b_dt = act; g.b_kmajor = 0;
     g.C = dX; g.ldc = L->ldx; g.c_dt = act;
-    HIP_TRY(token_gemm(g, st));
+    HIP_TRY(launch_gemm(g, st));
   }
   {  // G = dY^T X  (K = T; T == 0 gives G = 0)
     GemmDesc g;
@@ -457,52 +547,66 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.compute = act; g.M = m; g.N = n; g.K = L->T;
     g.A = dY; g.lda = L->ldy; g.a_dt = act; g.a_kmajor = 0;
     g.B = X; g.ldb = L->ldx; g.b_dt = act; g.b_kmajor = 0;
-    g.C = p.G; g.ldc = ldw; g.c_dt = F32;
-    HIP_TRY(token_gemm(g, st));
+    if (fast) { g.C = p.Gb; g.c_dt = BF16; } else { g.C = p.G; g.c_dt = F32; }
+    g.ldc = ldw;
+    g.part = p.adj.part; g.part_elems = p.adj.part_elems;
+    HIP_TRY(launch_gemm(g, st));
   }
   // primitive blocks of dL/dR = G Z^T
   if (R.theta_len > 0) {
     GemmDesc g;
     g.kclass = POET_K_CONTRACT;
     g.compute = act;
+    g.part = p.adj.part; g.part_elems = p.adj.part_elems;
     if (R.mode == POET_BS) {
-      HIP_TRY(launch_fill(p.dRb, R.prim_len, 0.f, st));
+      HIP_TRY(launch_fill(p.dRg, R.prim_len, 0.f, st));
       g.M = g.N = R.bp; g.K = n; g.Mtot = g.Ntot = m; g.batch = R.nprim;
-      g.A = p.G; g.lda = ldw; g.sA = (int64_t)R.bp * ldw; g.a_dt = F32; g.a_kmajor = 1;
-      g.B = p.T; g.ldb = ldw; g.sB = (int64_t)R.bp * ldw; g.b_dt = F32; g.b_kmajor = 1;
-      g.C = p.dRb; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
+      if (fast) {
+        g.A = p.Gb; g.a_dt = BF16; g.B = p.Tb; g.b_dt = BF16;
+      } else {
+        g.A = p.G; g.a_dt = F32; g.B = p.T; g.b_dt = F32;
+      }
+      g.lda = ldw; g.sA = (int64_t)R.bp * ldw; g.a_kmajor = 1;
+      g.ldb = ldw; g.sB = (int64_t)R.bp * ldw; g.b_kmajor = 1;
+      g.C = p.dRg; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
     } else {
       HIP_TRY(launch_gather_rows(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, n, st));
       HIP_TRY(launch_gather_rows(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, n, st));
       g.M = g.N = R.bp; g.K = n;
       g.A = p.Gr; g.lda = n; g.a_dt = F32; g.a_kmajor = 1;
       g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
-      g.C = p.dRb; g.ldc = R.bp; g.c_dt = F32;
+      g.C = p.dRg; g.ldc = R.bp; g.c_dt = F32;
     }
     HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(neumann_adjoint(R, p.dRb, powersR, dthetaR, p.adj, st));
+    HIP_TRY(neumann_adjoint(R, p.dRg, powersR, dthetaR, p.adj, st));
   }
   // primitive blocks of dL/dP = (R W0)^T G
   if (P.theta_len > 0) {
     GemmDesc g;
     g.kclass = POET_K_CONTRACT;
     g.compute = act;
+    g.part = p.adj.part; g.part_elems = p.adj.part_elems;
     if (P.mode == POET_BS) {
-      HIP_TRY(launch_fill(p.dPb, P.prim_len, 0.f, st));
+      HIP_TRY(launch_fill(p.dPg, P.prim_len, 0.f, st));
       g.M = g.N = P.bp; g.K = m; g.Mtot = g.Ntot = n; g.batch = P.nprim;
-      g.A = p.RW0; g.lda = ldw; g.sA = P.bp; g.a_dt = F32; g.a_kmajor = 0;
-      g.B = p.G; g.ldb = ldw; g.sB = P.bp; g.b_dt = F32; g.b_kmajor = 0;
-      g.C = p.dPb; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
+      if (fast) {
+        g.A = p.RW0b; g.a_dt = BF16; g.B = p.Gb; g.b_dt = BF16;
+      } else {
+        g.A = p.RW0; g.a_dt = F32; g.B = p.G; g.b_dt = F32;
+      }
+      g.lda = ldw; g.sA = P.bp; g.a_kmajor = 0;
+      g.ldb = ldw; g.sB = P.bp; g.b_kmajor = 0;
+      g.C = p.dPg; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
     } else {
       HIP_TRY(launch_gather_cols(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, P.bp, st));
       HIP_TRY(launch_gather_cols(p.G, ldw, m, idxP, P.bp, n, p.Gc, P.bp, st));
       g.M = g.N = P.bp; g.K = m;
       g.A = p.Acp; g.lda = P.bp; g.a_dt = F32; g.a_kmajor = 0;
       g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
-      g.C = p.dPb; g.ldc = P.bp; g.c_dt = F32;
+      g.C = p.dPg; g.ldc = P.bp; g.c_dt = F32;
     }
     HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(neumann_adjoint(P, p.dPb, powersP, dthetaP, p.adj, st));
+    HIP_TRY(neumann_adjoint(P, p.dPg, powersP, dthetaP, p.adj, st));
   }
   return POET_OK;
 }
@@ -530,6 +634,28 @@ poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* t
     HIP_TRY(launch_sample(R.d, R.bp, sampler_hash(seed, linear_id, POET_SIDE_R, epoch_next), p.flags, idxR, st));
   if (P.mode == POET_FS)
     HIP_TRY(launch_sample(P.d, P.bp, sampler_hash(seed, linear_id, POET_SIDE_P, epoch_next), p.flags, idxP, st));
+  return POET_OK;
+}
+
+poet_status poet_debug_gemm(const poet_gemm_desc* d, int force_generic, int* used_fast, void* stream) {
+  if (!d) return fail(POET_E_ARG, "null descriptor");
+  if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 0) return fail(POET_E_SHAPE, "negative size");
+  if (!d->A || !d->B) return fail(POET_E_ARG, "null A or B");
+  GemmDesc g;
+  g.M = d->M; g.N = d->N; g.K = d->K; g.Mtot = d->Mtot; g.Ntot = d->Ntot; g.Ktot = d->Ktot; g.batch = d->batch;
+  g.A = d->A; g.lda = d->lda; g.sA = d->sA; g.a_dt = d->a_dt; g.a_kmajor = d->a_kmajor;
+  g.B = d->B; g.ldb = d->ldb; g.sB = d->sB; g.b_dt = d->b_dt; g.b_kmajor = d->b_kmajor;
+  g.C = d->C; g.ldc = d->ldc; g.sC = d->sC; g.c_dt = d->c_dt;
+  g.C2 = d->C2; g.ldc2 = d->ldc2; g.sC2 = d->sC2; g.c2_dt = d->c2_dt;
+  g.D = d->D; g.ldd = d->ldd; g.sD = d->sD;
+  g.Acc = d->Acc; g.ldacc = d->ldacc; g.sAcc = d->sAcc;
+  g.alpha = d->alpha; g.beta = d->beta; g.gamma = d->gamma;
+  g.compute = d->compute;
+  g.part = d->part; g.part_elems = d->part_elems;
+  const bool fast = !force_generic && fast_gemm_eligible(g);
+  if (used_fast) *used_fast = fast ? 1 : 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(fast ? launch_gemm(g, st) : launch_generic_gemm(g, st));
   return POET_OK;
 }
 
