@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4])
     ap.add_argument("--merge-period", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
+                         "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the POET layer path is single-GPU (data-parallel sharding is a "
@@ -187,6 +190,14 @@ def main():
         "stage_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
         "stage_launches_per_step": {k: v["launches"] // args.steps for k, v in prof.items()},
     }
+    if args.calib_copy_mib > 0:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = nbytes
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -184,7 +184,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, i
   }
 }
 
-template <bool AK, bool BK_>
+// TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
+template <bool AK, bool BK_, int TAG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(const FastArgs fa_) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
   const GemmDesc& g = fa_.g;
@@ -341,10 +342,16 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
                                                        (g.C2 ? dtype_size(g.c2_dt) : 0) + (g.Acc ? 8 : 0)));
   ProfScope prof(g.kclass, st, flops, bytes);
   const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
-  if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), grid, block, 0, st, fa);
-  else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), grid, block, 0, st, fa);
-  else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), grid, block, 0, st, fa);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, block, 0, st, fa);
+  if (g.kclass == 0 && g.a_kmajor && g.b_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 1>), grid, block, 0, st, fa);
+  else if (g.kclass == 1 && g.a_kmajor && !g.b_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 2>), grid, block, 0, st, fa);
+  else if (g.kclass == 2 && !g.a_kmajor && !g.b_kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 3>), grid, block, 0, st, fa);
+  else if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 0>), grid, block, 0, st, fa);
+  else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 0>), grid, block, 0, st, fa);
+  else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true, 0>), grid, block, 0, st, fa);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fa.use_part) return e;
   const int64_t total = (int64_t)g.batch * g.M * g.N;
