@@ -43,6 +43,39 @@ struct GemmDesc {
 bool fast_gemm_eligible(const GemmDesc& g);
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
 
+// Power chain X_{j+1} = Q X_j, j = 0..steps-1, of nprim primitives of size bp <= 256 (power_chain.hip), with Q
+// the bf16 blocks A (row pitch bp, stride sA).
+//   build:   X_0 = Q; Q^{j+1} (bf16) is written at Y + j*jstep for j = 1..steps-1 (row pitch ldy, stride sy), and
+//            prim (float32 bp x bp blocks, holding I + 2Q on entry) becomes I + 2Q + 2(Q^2 + .. + Q^steps) + Q^{steps+1}.
+//   adjoint: X_0 from the float32 blocks X0 (row pitch ldx0, stride sx0); X_j (bf16) is written at Y + j*jstep for
+//            j = 1..steps, and for j = 0 when write_x0.
+struct ChainArgs {
+  int bp = 0, nprim = 0, steps = 0;
+  int build = 0;
+  float* prim = nullptr;
+  const __bf16* A = nullptr; int64_t sA = 0;
+  const float* X0 = nullptr; int64_t ldx0 = 0, sx0 = 0;
+  __bf16* Y = nullptr; int64_t ldy = 0, sy = 0, jstep = 0;
+  int write_x0 = 0;
+};
+bool power_chain_eligible(int bp, int dt, const void* A);  // A: the power/Q buffer (16-byte aligned)
+hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st);
+
+// Fused application of block-diagonal factors on both sides (bs_apply.hip), blocks bpR, bpP <= 256, W0 float32
+// m x n with row pitch ldw (rows readable up to a multiple of 4 columns), primitives float32 bp x bp blocks:
+// Tb = bf16(W0 P), W = R W0 P (dtype w_dt), RW0b = bf16(R W0), each written (row pitch ldw) when non-null.
+struct ApplyArgs {
+  int m = 0, n = 0, bpR = 0, nR = 0, bpP = 0, nP = 0;
+  const float* W0 = nullptr; int64_t ldw = 0;
+  const float* primR = nullptr;
+  const float* primP = nullptr;
+  __bf16* Tb = nullptr;
+  void* W = nullptr; int w_dt = BF16;
+  __bf16* RW0b = nullptr;
+};
+bool bs_apply_eligible(int bpR, int bpP, const float* W0, int64_t ldw, const float* primR, const float* primP);
+hipError_t launch_bs_apply(const ApplyArgs& c, hipStream_t st);
+
 // launch profiler (profiler.hip): no-ops unless poet_profile_enable(1) was called
 int prof_begin(int kclass, hipStream_t st, double flops, double bytes);
 void prof_end(int rec, hipStream_t st);

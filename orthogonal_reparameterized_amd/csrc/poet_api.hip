@@ -239,9 +239,19 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
   const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
   const size_t esz = dtype_size(S.dtype);
   char* H = reinterpret_cast<char*>(b.H);
-  hipError_t e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
+  hipError_t e = hipSuccess;
+  if (power_chain_eligible(bp, S.dtype, powers)) {  // H_0 = dR and H_{j+1} = Q H_j in one launch
+    ChainArgs c;
+    c.bp = bp; c.nprim = S.nprim; c.steps = k;
+    c.A = reinterpret_cast<const __bf16*>(powers); c.sA = pp;
+    c.X0 = dRg; c.ldx0 = bp; c.sx0 = pp;
+    c.Y = reinterpret_cast<__bf16*>(H); c.ldy = ldh; c.sy = hs; c.jstep = bp; c.write_x0 = 1;
+    e = launch_power_chain(c, POET_K_ADJOINT, st);
+  } else {
+    e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
+  }
   if (e != hipSuccess) return e;
-  for (int j = 0; j < k; ++j) {  // H_{j+1} = Q H_j
+  for (int j = 0; j < k && !power_chain_eligible(bp, S.dtype, powers); ++j) {  // H_{j+1} = Q H_j
     GemmDesc g;
     g.kclass = POET_K_ADJOINT;
     g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
@@ -261,6 +271,15 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
   g.part = b.part; g.part_elems = b.part_elems;
   if ((e = launch_gemm(g, st)) != hipSuccess) return e;
   return launch_skew_project(b.dQ, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+}
+
+ApplyArgs apply_args(const poet_layer& L, const SideInfo& R, const SideInfo& P, const float* W0, const float* primR,
+                     const float* primP, __bf16* Tb, void* W, int w_dt, __bf16* RW0b) {
+  ApplyArgs a;
+  a.m = L.m; a.n = L.n; a.bpR = R.bp; a.nR = R.nprim; a.bpP = P.bp; a.nP = P.nprim;
+  a.W0 = W0; a.ldw = L.ldw; a.primR = primR; a.primP = primP;
+  a.Tb = Tb; a.W = W; a.w_dt = w_dt; a.RW0b = RW0b;
+  return a;
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -421,8 +440,18 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
     Arena a(ws);
     pw = reinterpret_cast<char*>(a.take_bytes((size_t)S.k * S.prim_len * esz));
   }
-  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype, st));
   if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
+  // prim = I + coef Q (coef 2 for k >= 1) with Q exact from theta, and the first saved power Q
+  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype, st));
+  if (S.k > 0 && power_chain_eligible(S.bp, S.dtype, pw)) {
+    // the k products and the rest of the series in one launch, Q resident in LDS
+    ChainArgs c;
+    c.bp = S.bp; c.nprim = S.nprim; c.steps = S.k; c.build = 1; c.prim = prim;
+    c.A = reinterpret_cast<const __bf16*>(pw); c.sA = (int64_t)S.bp * S.bp;
+    c.Y = reinterpret_cast<__bf16*>(pw); c.ldy = S.bp; c.sy = (int64_t)S.bp * S.bp; c.jstep = (int64_t)S.prim_len;
+    HIP_TRY(launch_power_chain(c, POET_K_CHAIN, st));
+    return POET_OK;
+  }
   if (S.k == 0) return POET_OK;  // R_0 = I + Q
   const int64_t pp = (int64_t)S.bp * S.bp;
   for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i; the last power goes straight into prim (float32)
@@ -468,7 +497,9 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
   void* W = W_out ? W_out : p.W;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int act = L->act_dtype;
-  if (bs_bf16(*L, R, P)) {
+  if (bs_bf16(*L, R, P) && bs_apply_eligible(R.bp, P.bp, W0, L->ldw, primR, primP)) {
+    HIP_TRY(launch_bs_apply(apply_args(*L, R, P, W0, primR, primP, nullptr, W, act, nullptr), st));
+  } else if (bs_bf16(*L, R, P)) {
     HIP_TRY(launch_convert(W0, L->ldw, p.W0b, L->ldw, BF16, L->m, L->n, st));
     HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));
     HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, p.dPb, st));
@@ -511,7 +542,12 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
   const int64_t ldw = L->ldw;
   const bool fast = bs_bf16(*L, R, P);
   const void* W = Win;
-  if (fast) {
+  if (fast && bs_apply_eligible(R.bp, P.bp, W0, ldw, primR, primP)) {
+    // bf16 operands of the gradient: Z = W0 P (R side), R W0 (P side), and W when it is not given
+    void* Wout = W ? nullptr : p.W;
+    HIP_TRY(launch_bs_apply(apply_args(*L, R, P, W0, primR, primP, p.Tb, Wout, act, p.RW0b), st));
+    if (!W) W = p.W;
+  } else if (fast) {
     // bf16 operands: W0, the factor deltas, Z = W0 P (R-side gradient), R W0 (P-side gradient), G
     HIP_TRY(launch_convert(W0, ldw, p.W0b, ldw, BF16, m, n, st));
     HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));

@@ -1,0 +1,157 @@
+// Power chain X_{j+1} = Q X_j (j = 0 .. steps-1) of every primitive of a side, in one launch, for primitives of
+// size bp <= 256 (POET-BS blocks). It serves two steps of the layer:
+//   the Cayley-Neumann build   X_0 = Q, so X_j = Q^{j+1}. The kernel writes the saved powers Q^2 .. Q^k (bf16)
+//     and completes the factor R_k = I + 2 Q + 2 (Q^2 + .. + Q^k) + Q^{k+1} in float32 on top of I + 2 Q, which
+//     the caller has written with the linear term exact from theta.
+//   the Neumann adjoint        X_0 = dR, so X_j = Q^j dR = H_j, written (bf16) side by side for j = 0..steps.
+// Q comes from the saved bf16 power Q (the caller's first saved power).
+// Column strips are independent (X_{j+1}[:, S] = Q X_j[:, S]), so one workgroup owns one 64-column strip of one
+// primitive through all steps: Q stays resident in LDS (bp x bp bf16, up to 128 KB), the strip lives transposed
+// in LDS (64 x bp bf16, 32 KB) and is overwritten by each new power after a barrier. Products run on
+// v_mfma_f32_32x32x16_bf16 with float32 accumulation; each power is rounded to bf16 before it feeds the next
+// product (as a bf16 operand would be).
+#include "strip_mma.h"
+
+namespace poet {
+namespace {
+
+using namespace strip;
+
+template <bool BUILD>
+__global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
+  __shared__ __attribute__((aligned(16))) char smem[A_BYTES + X_BYTES];  // 160 KB
+  char* Aq = smem;            // Q[i][k]
+  char* Xs = smem + A_BYTES;  // X[k][n] stored as Xs[n][k]
+  const int bp = c.bp, nstrips = (bp + SW - 1) / SW;
+  const int p = blockIdx.x / nstrips, n0 = (blockIdx.x % nstrips) * SW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rowsA = min(MAXB, (bp + 63) / 64 * 64);  // rows the waves read
+  const int kpad = kpad_of(bp);                      // K extent of the products (zero beyond bp)
+
+  // Q -> LDS from the bf16 blocks: thread = (16-byte chunk tid % 32, first row tid / 32), 8 rows apart; loads
+  // are unconditional at a valid address and issued in groups of 8 before their LDS stores
+  {
+    const __bf16* Ab = c.A + (int64_t)p * c.sA;
+    const int ch = tid & 31;
+    const bool chin = ch * 8 < bp;
+    for (int i0 = tid >> 5; i0 < rowsA; i0 += 64) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 8;
+        const bool in = chin && i < bp;
+        v[u] = *reinterpret_cast<const u32x4*>(Ab + (in ? (int64_t)i * bp + ch * 8 : 0));
+        if (!in) v[u] = u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 8;
+        if (ch * 8 < kpad) *reinterpret_cast<u32x4*>(Aq + i * ROWB + ((ch ^ (i & 15)) << 4)) = v[u];
+      }
+    }
+  }
+  if constexpr (BUILD) {
+    __syncthreads();
+    // X_0 = Q strip, transposed from the staged Q: thread = (column n = tid % 64, rows tid / 64 + 4t)
+    const int n = tid & 63;
+    for (int k = tid >> 6; k < kpad; k += 4) sts(Xs, n, k, n0 + n < bp ? lds(Aq, k, n0 + n) : (__bf16)0.f);
+  } else {
+    // X_0 strip -> LDS (transposed) in float32 chunks of 4 columns: thread = (chunk tid % 16, rows tid / 16 + 16t);
+    // H_0 = bf16(X_0) to the output when asked
+    const float* X0 = c.X0 + (int64_t)p * c.sx0;
+    const int n = (tid & 15) * 4, gn = n0 + n;
+    for (int k0 = tid >> 4; k0 < kpad; k0 += 64) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * 16;
+        const bool in = k < bp && gn < bp;
+        v[u] = *reinterpret_cast<const f32x4*>(X0 + (in ? (int64_t)k * c.ldx0 + gn : 0));
+        if (!in) v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * 16;
+        if (k >= kpad) continue;
+        bf16x4 b;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          b[t] = (__bf16)v[u][t];
+          sts(Xs, n + t, k, b[t]);
+        }
+        if (c.write_x0 && k < bp && gn < bp)
+          *reinterpret_cast<bf16x4*>(c.Y + (int64_t)p * c.sy + (int64_t)k * c.ldy + gn) = b;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wr = wave * 64;  // this wave's 64 rows of the strip
+  // BUILD: S = I + 2Q (the caller's prim) + 2 (Q^2 + .. + Q^k) with the bf16 powers, at this lane's outputs; the 64
+  // loads are unconditional (index 0 stands in outside the block) so that they overlap
+  f32x16 S[2][2];
+  zero(S);
+  if constexpr (BUILD) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = acc_row(wr, a, r, lane), gn = n0 + acc_col(b, lane);
+          const bool in = i < bp && gn < bp;
+          S[a][b][r] = c.prim[in ? (int64_t)p * bp * bp + (int64_t)i * bp + gn : 0];
+        }
+  }
+  for (int j = 1; j <= c.steps; ++j) {
+    f32x16 acc[2][2];
+    zero(acc);
+    if (wr < bp) mma_strip(Aq, Xs, wr, kpad, lane, acc);
+    __syncthreads();  // every wave is done reading the strip of X_{j-1}
+    const bool last = j == c.steps;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int n = acc_col(b, lane), gn = n0 + n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // 4 consecutive rows per group of accumulators
+          const int i0 = acc_row(wr, a, q * 4, lane);
+          bf16x4 v4;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = q * 4 + t, i = i0 + t;
+            const float v = acc[a][b][r];
+            v4[t] = (__bf16)v;
+            if (i >= bp || gn >= bp) continue;
+            if (BUILD && last) {
+              c.prim[(int64_t)p * bp * bp + (int64_t)i * bp + gn] = S[a][b][r] + v;
+            } else {
+              c.Y[(int64_t)p * c.sy + (int64_t)j * c.jstep + (int64_t)i * c.ldy + gn] = v4[t];
+              if (BUILD) S[a][b][r] += 2.f * (float)v4[t];
+            }
+          }
+          if (!last) *reinterpret_cast<bf16x4*>(Xs + loff(n, i0)) = v4;  // next operand (rows >= bp stay zero)
+        }
+      }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool power_chain_eligible(int bp, int dt, const void* A) {
+  return dt == BF16 && bp > 0 && bp <= MAXB && bp % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0;
+}
+
+hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st) {
+  if (c.nprim <= 0 || c.steps <= 0) return hipSuccess;
+  const double flops = 2.0 * c.bp * (double)c.bp * c.bp * c.steps * c.nprim;
+  ProfScope prof(kclass, st, flops, (double)c.nprim * c.bp * c.bp * 2.0 * (c.steps + 2));
+  const int nstrips = (c.bp + SW - 1) / SW;
+  if (c.build) hipLaunchKernelGGL(power_chain_kernel<true>, dim3(c.nprim * nstrips), dim3(NT), 0, st, c);
+  else hipLaunchKernelGGL(power_chain_kernel<false>, dim3(c.nprim * nstrips), dim3(NT), 0, st, c);
+  return hipGetLastError();
+}
+
+}  // namespace poet

@@ -116,6 +116,15 @@ def test_bf16_small(mode, bR, bP):
     run_case(lin, pad=2, tag=f"bf16-{mode}")
 
 
+@pytest.mark.parametrize("bR,bP,k", [(200, 136, 8), (256, 24, 1), (248, 8, 2)])
+def test_bf16_bs_block_sizes(bR, bP, k):
+    """bf16 BS sides whose blocks are not multiples of the 64-column strips of the power chain (ragged strips,
+    idle waves, a short last block), with long and short chains."""
+    lin = make_linear(f"bf16-bs-{bR}-{bP}", 2 * bR + 17, 3 * bP + 5, 190, PI.MODE_BS, bR, bP, k, PI.DT_BF16,
+                      linear_id=5)
+    run_case(lin, pad=6, tag=f"bf16-bs-{bR}-{bP}-k{k}")
+
+
 def test_bf16_acts_fp32_chain():
     lin = make_linear("mixed", 160, 224, 128, PI.MODE_BS, 64, 32, 5, PI.DT_BF16, side_dt=PI.DT_F32)
     run_case(lin, tag="bf16-act-fp32-chain")
