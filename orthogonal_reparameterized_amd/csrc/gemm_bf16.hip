@@ -6,7 +6,8 @@
 // Workgroup tile 256 x 256 x 64, 4 waves in a 2 x 2 grid, each wave 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16.
 // Operands go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16
 // bytes at the wave's LDS base + 16 l, from any global address it chooses), in a two-stage ring: the DMA of
-// K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile. Both stage layouts are 32 KB:
+// K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile, placed before the last k-step so that the
+// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs. Both stage layouts are 32 KB:
 //   K-major operand: 256 rows x 128 B; the 16-byte chunk index is XOR-ed with f(row mod 32) =
 //     (row & 7) ^ ((row >> 3) & 3): 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
 //     groups, so the ds_read_b128 fragments are conflict-free;
@@ -15,7 +16,8 @@
 //     group, lane j supplies the address of 4 consecutive elements of k-row j/4; lane i receives the elements
 //     of column i of those 4 k-rows: an MFMA fragment of the transposed operand).
 // Rows or columns past M / N are fetched from a clamped (valid) address: they only reach outputs that are
-// never stored. The K tail of the last tile is zeroed in LDS after its DMA lands.
+// never stored. The K tail of the last tile is zeroed in LDS after its DMA lands. A wave's finished 128 x 128
+// tile leaves through LDS as row-contiguous vector stores.
 //
 // Work decomposition: (batch, split, tile) triples in one 1-D grid. Workgroup id w runs on XCD w % 8, so each
 // XCD takes a contiguous range of that order: neighbouring tiles on one XCD share A rows in its L2. With
@@ -33,6 +35,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -51,6 +54,11 @@ struct FastArgs {
 inline bool plain_epilogue(const GemmDesc& g) { return !g.D && !g.C2 && !g.Acc && g.alpha == 1.f && g.C; }
 
 __device__ __forceinline__ int swz(int r32) { return (r32 & 7) ^ ((r32 >> 3) & 3); }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8), issued through the
+// builtin so that the compiler's own wait insertion accounts for them
+constexpr int WAIT_LGKM0 = 0xC07F;  // lgkmcnt(0)
+constexpr int WAIT_VM0 = 0x0F70;    // vmcnt(0)
 
 // Direct global->LDS DMA of one 256 x 64 operand tile. Per-thread source offsets are fixed for the K loop.
 template <bool KMAJ>
@@ -151,36 +159,58 @@ __device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, 
   if (g.Acc) g.Acc[(int64_t)z * g.sAcc + (int64_t)row * g.ldacc + col] += g.gamma * out;
 }
 
-// store a wave's 128 x 128 accumulator tile (lane base offset `base`, row pitch ld) as dtype dt
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, int dt, int64_t base, int64_t ld,
-                                           int rlim, int clim) {
-  if (!C) return;
-  if (dt == BF16) {
-    __bf16* cb = reinterpret_cast<__bf16*>(C) + base;
+// Store a wave's 128 x 128 accumulator tile at out (row pitch ld elements, dtype dt; rlim x clim of it valid)
+// through the wave's EP_BYTES of LDS, one 32-row band at a time: the band is written in accumulator order
+// (row pitch EP floats, so the two half-waves land in disjoint banks) and read back as row-contiguous float4
+// chunks, which go out as 16-byte (float32) or 8-byte (bf16) stores when the row is aligned for them.
+constexpr int EP = 136, EP_BYTES = 32 * EP * 4;
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* lds, void* out, int dt, int64_t ld,
+                                               int rlim, int clim, int lane) {
+  float* ep = reinterpret_cast<float*>(lds);
+  const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(out) % (dt == BF16 ? 8 : 16)) == 0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 4; ++a) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
-        if (dr < rlim) {
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b * 32 < clim) cb[(int64_t)dr * ld + b * 32] = (__bf16)acc[a][b][r];
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * EP + b * 32 + (lane & 31)] = acc[a][b][r];
+    __syncthreads();
+    f32x4 vv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = lane + 64 * u;
+      vv[u] = *reinterpret_cast<const f32x4*>(ep + (c >> 5) * EP + (c & 31) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = lane + 64 * u, rr = c >> 5, c4 = (c & 31) * 4, row = a * 32 + rr;
+      if (row >= rlim || c4 >= clim) continue;
+      const f32x4 v = vv[u];
+      const int64_t o = (int64_t)row * ld + c4;
+      if (dt == BF16) {
+        __bf16* q = reinterpret_cast<__bf16*>(out) + o;
+        if (vec && c4 + 4 <= clim) {
+          bf16x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = (__bf16)v[t];
+          *reinterpret_cast<bf16x4*>(q) = w;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (c4 + t < clim) q[t] = (__bf16)v[t];
+        }
+      } else {
+        float* q = reinterpret_cast<float*>(out) + o;
+        if (vec && c4 + 4 <= clim) {
+          *reinterpret_cast<f32x4*>(q) = v;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (c4 + t < clim) q[t] = v[t];
         }
       }
-  } else {
-    float* cb = reinterpret_cast<float*>(C) + base;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
-        if (dr < rlim) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b * 32 < clim) cb[(int64_t)dr * ld + b * 32] = acc[a][b][r];
-        }
-      }
+    }
+    __syncthreads();
   }
 }
 
@@ -221,42 +251,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nk = kb < ke ? (ke - kb + BK - 1) / BK : 0;
+  // Two-stage ring: the DMA of tile t+1 is in flight while tile t is multiplied. The barrier that retires tile
+  // t's stage (and confirms tile t+1) sits before the MFMAs of tile t's last k-step, so the DMA of tile t+2 and
+  // the LDS reads of tile t+1's first fragments are issued while those MFMAs run.
+  bf16x8 fa[2][4], fb[2][4];
   if (nk > 0) {
     oa.dma(smem, kb, wave, lane);
     ob.dma(smem + STAGE, kb, wave, lane);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    __syncthreads();
+    const int kv = ke - kb;
+    if (kv < BK) {  // the first tile is partial (and the only one)
+      oa.zero_tail(smem, kv, tid);
+      ob.zero_tail(smem + STAGE, kv, tid);
+      __syncthreads();
+    }
+    if (nk > 1) {
+      oa.dma(smem + 2 * STAGE, kb + BK, wave, lane);
+      ob.dma(smem + 3 * STAGE, kb + BK, wave, lane);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(smem, wr + a * 32, 0, lane);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(smem + STAGE, wc + b * 32, 0, lane);
   }
   for (int kt = 0; kt < nk; ++kt) {
     char* sa = smem + (kt & 1) * 2 * STAGE;
     char* sb = sa + STAGE;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int kv = ke - (kb + kt * BK);
-    if (kv < BK) {  // last, partial K tile
-      oa.zero_tail(sa, kv, tid);
-      ob.zero_tail(sb, kv, tid);
-      __syncthreads();
-    }
-    if (kt + 1 < nk) {
-      char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
-      oa.dma(na, kb + (kt + 1) * BK, wave, lane);
-      ob.dma(na + STAGE, kb + (kt + 1) * BK, wave, lane);
-    }
-    // fragments of k-step ks + 1 are read from LDS while the 16 MFMAs of k-step ks run
-    bf16x8 fa[2][4], fb[2][4];
+    // k-steps 0..2: fragments of k-step ks + 1 are read from LDS while the 16 MFMAs of k-step ks run
 #pragma unroll
-    for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(sa, wr + a * 32, 0, lane);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(sb, wc + b * 32, 0, lane);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
       const int c = ks & 1;
-      if (ks + 1 < BK / 16) {
+      // k-step ks's fragments were issued a k-step ago: retire them here, so that the MFMAs below need no wait on
+      // the (up to 16) reads issued next, which a 4-bit LDS counter could not express
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
+      for (int a = 0; a < 4; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
-      }
-      // the next k-step's LDS reads stay ahead of this k-step's MFMAs
+      for (int b = 0; b < 4; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -265,27 +298,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][b], acc[a][b], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kt + 1 < nk) {
+      // tile kt+1 has landed (its DMA is the only one in flight) and every wave has read tile kt
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+      __syncthreads();
+      char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
+      if (kt + 2 < nk) {
+        oa.dma(sa, kb + (kt + 2) * BK, wave, lane);
+        ob.dma(sb, kb + (kt + 2) * BK, wave, lane);
+      }
+      const int kv = ke - (kb + (kt + 1) * BK);
+      if (kv < BK) {  // tile kt+1 is the last one and partial
+        oa.zero_tail(na, kv, tid);
+        ob.zero_tail(na + STAGE, kv, tid);
+        __syncthreads();
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // last k-step; tile kt+1's first fragments are read behind its first 4 MFMAs (12 MFMAs before their use)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][b], acc[0][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      const char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(na, wr + a * 32, 0, lane);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(na + STAGE, wc + b * 32, 0, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 1; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][a], fb[1][b], acc[a][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // accumulator r of lane l in a 32x32 tile is C[(r/4)*8 + (l/32)*4 + r%4][l%32]
-  const int row0 = m0 + wr + (lane >> 5) * 4, col0 = n0 + wc + (lane & 31);
-  const int rlim = M - row0, clim = N - col0;
+  // the wave's 128 x 128 tile goes out through LDS (every wave is past its last fragment read first)
+  __syncthreads();
+  const int wrow0 = m0 + wr, wcol0 = n0 + wc;
   if (fa_.use_part) {  // raw partial tile; the reduction kernel sums the splits and applies the epilogue
-    float* pb = g.part + ((int64_t)(s * g.batch + z) * g.M + row0) * g.N + col0;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dr = a * 32 + (r >> 2) * 8 + (r & 3);
-        if (dr < rlim) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b * 32 < clim) pb[(int64_t)dr * g.N + b * 32] = acc[a][b][r];
-        }
-      }
+    float* pb = g.part + ((int64_t)(s * g.batch + z) * g.M + wrow0) * g.N + wcol0;
+    store_tile_lds(acc, smem + wave * EP_BYTES, pb, F32, g.N, M - wrow0, N - wcol0, lane);
     return;
   }
-  store_tile(acc, g.C, g.c_dt, (int64_t)z * g.sC + (int64_t)row0 * g.ldc + col0, g.ldc, rlim, clim);
+  if (!g.C) return;
+  char* cb = reinterpret_cast<char*>(g.C) + ((int64_t)z * g.sC + (int64_t)wrow0 * g.ldc + wcol0) * dtype_size(g.c_dt);
+  store_tile_lds(acc, smem + wave * EP_BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane);
 }
 
 // Sum the split-K partials of every output element in split order, then apply the epilogue.

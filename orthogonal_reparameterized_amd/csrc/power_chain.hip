@@ -87,28 +87,40 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
   __syncthreads();
 
   const int wr = wave * 64;  // this wave's 64 rows of the strip
-  // BUILD: S = I + 2Q (the caller's prim) + 2 (Q^2 + .. + Q^k) with the bf16 powers, at this lane's outputs; the 64
-  // loads are unconditional (index 0 stands in outside the block) so that they overlap
-  f32x16 S[2][2];
-  zero(S);
-  if constexpr (BUILD) {
+  // BUILD: S = I + 2Q (the caller's prim) + 2 (Q^2 + .. + Q^k) with the bf16 powers, at this lane's outputs (plain
+  // registers, updated without branches); the 64 loads are unconditional (index 0 stands in outside the block)
+  float S[2][2][16];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r) {
+        S[a][b][r] = 0.f;
+        if constexpr (BUILD) {
           const int i = acc_row(wr, a, r, lane), gn = n0 + acc_col(b, lane);
           const bool in = i < bp && gn < bp;
           S[a][b][r] = c.prim[in ? (int64_t)p * bp * bp + (int64_t)i * bp + gn : 0];
         }
-  }
+      }
   for (int j = 1; j <= c.steps; ++j) {
     f32x16 acc[2][2];
     zero(acc);
     if (wr < bp) mma_strip(Aq, Xs, wr, kpad, lane, acc);
     __syncthreads();  // every wave is done reading the strip of X_{j-1}
     const bool last = j == c.steps;
+    if (BUILD && last) {  // R_k = S + Q^{k+1}
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = acc_row(wr, a, r, lane), gn = n0 + acc_col(b, lane);
+            if (i < bp && gn < bp) c.prim[(int64_t)p * bp * bp + (int64_t)i * bp + gn] = S[a][b][r] + acc[a][b][r];
+          }
+      break;
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -120,17 +132,12 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
           bf16x4 v4;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const int r = q * 4 + t, i = i0 + t;
-            const float v = acc[a][b][r];
-            v4[t] = (__bf16)v;
-            if (i >= bp || gn >= bp) continue;
-            if (BUILD && last) {
-              c.prim[(int64_t)p * bp * bp + (int64_t)i * bp + gn] = S[a][b][r] + v;
-            } else {
-              c.Y[(int64_t)p * c.sy + (int64_t)j * c.jstep + (int64_t)i * c.ldy + gn] = v4[t];
-              if (BUILD) S[a][b][r] += 2.f * (float)v4[t];
-            }
+            v4[t] = (__bf16)acc[a][b][q * 4 + t];
+            if (BUILD) S[a][b][q * 4 + t] += 2.f * (float)v4[t];
           }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (i0 + t < bp && gn < bp) c.Y[(int64_t)p * c.sy + (int64_t)j * c.jstep + (int64_t)(i0 + t) * c.ldy + gn] = v4[t];
           if (!last) *reinterpret_cast<bf16x4*>(Xs + loff(n, i0)) = v4;  // next operand (rows >= bp stay zero)
         }
       }
