@@ -374,11 +374,23 @@ bool fast_gemm_eligible(const GemmDesc& g) {
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (g.compute != BF16 || g.a_dt != BF16 || g.b_dt != BF16 || g.a_sub_eye || g.b_sub_eye) return false;
   if (g.M < 128 || g.N < 128 || g.batch < 1) return false;
-  if (!plain_epilogue(g) && (!g.part || g.part_elems < (size_t)g.batch * g.M * g.N)) return false;
+  if ((!plain_epilogue(g) || g.defer_reduce) && (!g.part || g.part_elems < (size_t)g.batch * g.M * g.N)) return false;
   if (g.lda % 8 || g.ldb % 8 || g.sA % 8 || g.sB % 8 || !al(g.A) || !al(g.B)) return false;
   // 32-bit byte offsets inside one batch's operands
   const double ea = 2.0 * (g.a_kmajor ? g.M : g.K) * (double)g.lda, eb = 2.0 * (g.b_kmajor ? g.N : g.K) * (double)g.ldb;
   return ea < 2.0e9 && eb < 2.0e9;
+}
+
+int fast_gemm_splits(const GemmDesc& g) {
+  // split K until one round of the machine (256 CUs, one workgroup each) is covered, keeping >= 2 K-tiles per
+  // split and the partials within the scratch the caller provided
+  const int tiles = g.batch * ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  const int nk = (g.K + BK - 1) / BK;
+  int S = 1;
+  while (tiles * S < 200 && nk >= 4 * S && S < 16 &&
+         (size_t)(2 * S) * g.batch * (size_t)g.M * g.N <= g.part_elems && g.part)
+    S *= 2;
+  return S;
 }
 
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
@@ -389,15 +401,10 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   fa.ntn = (g.N + BN - 1) / BN;
   const int tiles = g.batch * fa.ntm * fa.ntn;
   const int nk = (g.K + BK - 1) / BK;
-  // split K until one round of the machine (256 CUs, one workgroup each) is covered, keeping >= 2 K-tiles per
-  // split and the partials within the scratch the caller provided
-  int S = 1;
-  while (tiles * S < 200 && nk >= 4 * S && S < 16 &&
-         (size_t)(2 * S) * g.batch * (size_t)g.M * g.N <= g.part_elems && g.part)
-    S *= 2;
+  const int S = fast_gemm_splits(g);
   fa.splits = S;
   fa.kchunk = ((nk + S - 1) / S) * BK;
-  fa.use_part = (S > 1 || !plain_epilogue(g)) ? 1 : 0;
+  fa.use_part = (S > 1 || !plain_epilogue(g) || g.defer_reduce) ? 1 : 0;
   const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
   const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) +
                                   (double)g.M * g.N * ((g.C ? dtype_size(g.c_dt) : 0) + (g.D ? 4 : 0) +
@@ -415,7 +422,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true, 0>), grid, block, 0, st, fa);
   else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !fa.use_part) return e;
+  if (e != hipSuccess || !fa.use_part || g.defer_reduce) return e;
   const int64_t total = (int64_t)g.batch * g.M * g.N;
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);

@@ -36,11 +36,15 @@ struct GemmDesc {
   void* C2 = nullptr; int64_t ldc2 = 0, sC2 = 0; int c2_dt = F32;
   // optional float32 scratch for split-K partial sums on the bf16 fast path (deterministic reduction)
   float* part = nullptr; size_t part_elems = 0;
+  // fast path only: leave the raw split-K partials in part (split s of batch z at part + (s*batch + z)*M*N, rows of
+  // N floats; only the valid extent of each batch is written) for the caller to reduce; no epilogue is applied
+  int defer_reduce = 0;
 };
 
 // Fast path for bf16 x bf16 products (gemm_bf16.hip): 256x256x64 tiles, batched, split-K. Returns false (and
 // launches nothing) when the descriptor does not qualify; launch_gemm then uses the generic kernel.
 bool fast_gemm_eligible(const GemmDesc& g);
+int fast_gemm_splits(const GemmDesc& g);  // split-K count the fast path uses for g
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
 
 // Power chain X_{j+1} = Q X_j, j = 0..steps-1, of nprim primitives of size bp <= 256 (power_chain.hip), with Q
@@ -99,6 +103,11 @@ hipError_t launch_qnorm(const float* theta, int mode, int d, int bp, int nprim, 
 // dtheta_p = X_ij - X_ji with X = dQ + G1 (G1 nullable) for i < j < c of every primitive.
 hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d, int bp, int nprim,
                                float* dtheta, hipStream_t st);
+// dtheta_p = X_ij - X_ji, X = (sum over nsplit float32 partials in split order) + beta D, for i < j < c of every
+// primitive; split s of primitive p at part + s*split_stride + p*bp*bp (row pitch bp), D float32 bp x bp blocks
+// (nullable: no addend).
+hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
+                              int d, int bp, int nprim, float* dtheta, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
 // dst (rows x cols, ld_dst, dtype dst_dt) <- src (float32, ld_src)
 hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows,

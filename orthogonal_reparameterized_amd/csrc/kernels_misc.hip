@@ -87,6 +87,58 @@ __global__ void k_skew_project(const float* __restrict__ dQ, const float* __rest
   }
 }
 
+// dtheta of primitive p = blockIdx.y from NS split-K partials: X = sum_s part[s] (split order) + beta D, then
+// X_ij - X_ji. Workgroup x takes the pair of 32 x 32 tiles (ti, tj), ti <= tj: both are read row-wise (coalesced,
+// the 8 NS loads of a thread issued together), the (tj, ti) tile is transposed through LDS.
+template <int NS>
+__global__ __launch_bounds__(256) void k_reduce_skew(const float* __restrict__ part, int64_t split_stride,
+                                                     const float* __restrict__ D, float beta, int mode, int d, int bp,
+                                                     float* __restrict__ dtheta) {
+  __shared__ float tr[32][33];
+  const int p = blockIdx.y;
+  int ti = 0, rem = blockIdx.x;  // blockIdx.x enumerates ti <= tj row by row
+  const int nt = (bp + 31) / 32;
+  while (rem >= nt - ti) { rem -= nt - ti; ++ti; }
+  const int tj = ti + rem;
+  const int c = prim_size(mode, d, bp, p);
+  const int64_t base = (int64_t)p * bp * bp;
+  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;  // rows row0 + 8 q
+  float xa[4], xb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = row0 + 8 * q;
+    const int ia = ti * 32 + r, ja = tj * 32 + col;  // element of tile (ti, tj)
+    const int ib = tj * 32 + r, jb = ti * 32 + col;  // element of tile (tj, ti)
+    const bool ina = ia < bp && ja < bp, inb = ib < bp && jb < bp;
+    const int64_t oa = base + (ina ? (int64_t)ia * bp + ja : 0), ob = base + (inb ? (int64_t)ib * bp + jb : 0);
+    float va[NS], vb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      va[s] = part[s * split_stride + oa];
+      vb[s] = part[s * split_stride + ob];
+    }
+    xa[q] = va[0];
+    xb[q] = vb[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) {
+      xa[q] += va[s];
+      xb[q] += vb[s];
+    }
+    if (D) {
+      xa[q] += beta * D[oa];
+      xb[q] += beta * D[ob];
+    }
+    tr[col][r] = xb[q];  // transposed: tr[jb - 32 ti][ib - 32 tj]
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = row0 + 8 * q;
+    const int i = ti * 32 + r, j = tj * 32 + col;
+    if (i < j && j < c) dtheta[theta_off(bp, p) + tri_pos(i, j, c)] = xa[q] - tr[r][col];
+  }
+}
+
 __global__ void k_fill(float* __restrict__ p, size_t n, float v) {
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) p[e] = v;
 }
@@ -206,25 +258,35 @@ __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
 }
 
 // element (p, j, r, c) of the stacked coefficient matrices; see launch_adjoint_coefs
-__global__ void k_adjoint_coefs(const void* __restrict__ powers, int dt, int nprim, int bp, int k,
-                                void* __restrict__ out) {
-  const int64_t pp = (int64_t)bp * bp, per = (int64_t)(k + 1) * pp, total = (int64_t)nprim * per;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int p = (int)(e / per);
-    const int64_t q = e - (int64_t)p * per;
-    const int j = (int)(q / pp);
-    const int rc = (int)(q - (int64_t)j * pp);
-    const int r = rc / bp, c = rc % bp;
-    float v = 0.f;
-    for (int t = (j == 0 ? 1 : 0); t <= k - j; ++t) {
-      const int i = t + j + 1;
-      const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
-      const float pt = t == 0 ? (r == c ? 1.f : 0.f) : ld_dt(powers, dt, ((int64_t)(t - 1) * nprim + p) * pp + rc);
-      v += a * pt;
+// Block j of primitive p (blockIdx.y = p (k+1) + j); thread x covers VEC consecutive elements of the bp x bp block
+// (32-bit index math: a block holds at most 2^16 elements of one row-major primitive).
+template <typename T, int VEC>
+__global__ void k_adjoint_coefs(const T* __restrict__ powers, int nprim, int bp, int k, T* __restrict__ out) {
+  const int pp = bp * bp;
+  const int rc0 = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
+  if (rc0 >= pp) return;
+  const int p = blockIdx.y / (k + 1), j = blockIdx.y - p * (k + 1);
+  float v[VEC];
+#pragma unroll
+  for (int u = 0; u < VEC; ++u) v[u] = 0.f;
+  if (j > 0) {  // t = 0 term: a_{j+1} (-1)^j I
+    const float a = (j + 1 <= k ? 2.f : 1.f) * ((j & 1) ? -1.f : 1.f);
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const int rc = rc0 + u;
+      if (rc / bp == rc % bp) v[u] = a;
     }
-    if (dt == BF16) reinterpret_cast<__bf16*>(out)[e] = (__bf16)v;
-    else reinterpret_cast<float*>(out)[e] = v;
   }
+  for (int t = 1; t <= k - j; ++t) {
+    const int i = t + j + 1;
+    const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
+    const T* src = powers + ((size_t)(t - 1) * nprim + p) * pp + rc0;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) v[u] += a * (float)src[u];
+  }
+  T* dst = out + ((size_t)p * (k + 1) + j) * pp + rc0;
+#pragma unroll
+  for (int u = 0; u < VEC; ++u) dst[u] = (T)v[u];
 }
 
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
@@ -271,8 +333,22 @@ hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, __bf16* out, 
 hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int k, void* out, hipStream_t st) {
   const int64_t total = (int64_t)nprim * (k + 1) * bp * bp;
   if (total == 0) return hipSuccess;
+  if ((int64_t)bp * bp > (1 << 30) || (int64_t)nprim * (k + 1) > 65535) return hipErrorInvalidValue;
   ProfScope prof(7, st, 0, (double)total * dtype_size(dt) * 2);
-  hipLaunchKernelGGL(k_adjoint_coefs, dim3(grid_for(total)), dim3(kThreads), 0, st, powers, dt, nprim, bp, k, out);
+  const int pp = bp * bp;
+  if (dt == BF16 && pp % 4 == 0) {
+    const dim3 grid((pp / 4 + kThreads - 1) / kThreads, nprim * (k + 1));
+    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 4>), grid, dim3(kThreads), 0, st,
+                       reinterpret_cast<const __bf16*>(powers), nprim, bp, k, reinterpret_cast<__bf16*>(out));
+  } else if (dt == BF16) {
+    const dim3 grid((pp + kThreads - 1) / kThreads, nprim * (k + 1));
+    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 1>), grid, dim3(kThreads), 0, st,
+                       reinterpret_cast<const __bf16*>(powers), nprim, bp, k, reinterpret_cast<__bf16*>(out));
+  } else {
+    const dim3 grid((pp + kThreads - 1) / kThreads, nprim * (k + 1));
+    hipLaunchKernelGGL((k_adjoint_coefs<float, 1>), grid, dim3(kThreads), 0, st,
+                       reinterpret_cast<const float*>(powers), nprim, bp, k, reinterpret_cast<float*>(out));
+  }
   return hipGetLastError();
 }
 
@@ -296,6 +372,23 @@ hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d
   const size_t total = (size_t)nprim * bp * bp;
   ProfScope prof(7, st, 0, (double)total * (G1 ? 8 : 4) + (double)total * 2);
   hipLaunchKernelGGL(k_skew_project, dim3(grid_for(total)), dim3(kThreads), 0, st, dQ, G1, mode, d, bp, nprim, dtheta);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
+                              int d, int bp, int nprim, float* dtheta, hipStream_t st) {
+  if (nprim <= 0) return hipSuccess;
+  if (nprim > 65535 || (int64_t)bp * bp > (1 << 30)) return hipErrorInvalidValue;
+  ProfScope prof(7, st, 0, (double)nprim * bp * bp * 4.0 * (nsplit + 1) + (double)nprim * bp * (bp - 1) * 2.0);
+  const int nt = (bp + 31) / 32;
+  const dim3 grid(nt * (nt + 1) / 2, nprim);
+  switch (nsplit) {
+#define POET_RS(NS) \
+  case NS: hipLaunchKernelGGL(k_reduce_skew<NS>, grid, dim3(kThreads), 0, st, part, split_stride, D, beta, mode, d, bp, dtheta); break;
+    POET_RS(1) POET_RS(2) POET_RS(4) POET_RS(8) POET_RS(16)
+#undef POET_RS
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

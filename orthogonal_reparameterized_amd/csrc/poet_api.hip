@@ -234,13 +234,15 @@ size_t adj_elems(const SideInfo& S) { return (size_t)S.nprim * S.bp * S.bp * (S.
 hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powers, float* dtheta, const AdjBufs& b,
                            hipStream_t st) {
   if (S.theta_len == 0) return hipSuccess;
+  const int64_t pp = (int64_t)S.bp * S.bp;
   if (S.k == 0) return launch_skew_project(dRg, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
   const int bp = S.bp, k = S.k, ldh = (k + 1) * bp;
-  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
+  const int64_t hs = (int64_t)bp * ldh;
   const size_t esz = dtype_size(S.dtype);
   char* H = reinterpret_cast<char*>(b.H);
   hipError_t e = hipSuccess;
-  if (power_chain_eligible(bp, S.dtype, powers)) {  // H_0 = dR and H_{j+1} = Q H_j in one launch
+  const bool chain = power_chain_eligible(bp, S.dtype, powers);
+  if (chain) {  // H_0 = dR and H_{j+1} = Q H_j in one launch
     ChainArgs c;
     c.bp = bp; c.nprim = S.nprim; c.steps = k;
     c.A = reinterpret_cast<const __bf16*>(powers); c.sA = pp;
@@ -249,26 +251,33 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
     e = launch_power_chain(c, POET_K_ADJOINT, st);
   } else {
     e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
+    for (int j = 0; j < k && e == hipSuccess; ++j) {  // H_{j+1} = Q H_j
+      GemmDesc g;
+      g.kclass = POET_K_ADJOINT;
+      g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
+      g.A = powers; g.lda = bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
+      g.B = H + (size_t)j * bp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
+      g.C = H + (size_t)(j + 1) * bp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
+      e = launch_gemm(g, st);
+    }
   }
   if (e != hipSuccess) return e;
-  for (int j = 0; j < k && !power_chain_eligible(bp, S.dtype, powers); ++j) {  // H_{j+1} = Q H_j
-    GemmDesc g;
-    g.kclass = POET_K_ADJOINT;
-    g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
-    g.A = powers; g.lda = bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
-    g.B = H + (size_t)j * bp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
-    g.C = H + (size_t)(j + 1) * bp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
-    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
-  }
   if ((e = launch_adjoint_coefs(powers, S.dtype, S.nprim, bp, k, b.Cs, st)) != hipSuccess) return e;
   GemmDesc g;  // dQ = a_1 dR + [H_0 .. H_k] [C_0; ..; C_k]
   g.kclass = POET_K_ADJOINT;
   g.compute = S.dtype; g.M = g.N = bp; g.K = (k + 1) * bp; g.batch = S.nprim;
   g.A = H; g.lda = ldh; g.sA = hs; g.a_dt = S.dtype; g.a_kmajor = 1;
   g.B = b.Cs; g.ldb = bp; g.sB = (int64_t)(k + 1) * pp; g.b_dt = S.dtype; g.b_kmajor = 0;
-  g.D = dRg; g.ldd = bp; g.sD = pp; g.beta = 2.f;  // a_1 = 2 for k >= 1
   g.C = b.dQ; g.ldc = bp; g.sC = pp; g.c_dt = F32;
   g.part = b.part; g.part_elems = b.part_elems;
+  g.defer_reduce = 1;
+  if (fast_gemm_eligible(g)) {  // the split-K partials go straight into the skew projection with a_1 dR = 2 dR
+    const int ns = fast_gemm_splits(g);
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+    return launch_reduce_skew(b.part, ns, S.nprim * pp, dRg, 2.f, S.mode, S.d, S.bp, S.nprim, dtheta, st);
+  }
+  g.defer_reduce = 0;
+  g.D = dRg; g.ldd = bp; g.sD = pp; g.beta = 2.f;  // a_1 = 2 for k >= 1
   if ((e = launch_gemm(g, st)) != hipSuccess) return e;
   return launch_skew_project(b.dQ, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
 }
@@ -280,6 +289,16 @@ ApplyArgs apply_args(const poet_layer& L, const SideInfo& R, const SideInfo& P, 
   a.W0 = W0; a.ldw = L.ldw; a.primR = primR; a.primP = primP;
   a.Tb = Tb; a.W = W; a.w_dt = w_dt; a.RW0b = RW0b;
   return a;
+}
+
+// The primitive-gradient contraction g (output dR blocks, reduced over its K splits across the whole machine), then
+// the adjoint. A ragged last block writes only its true extent, so dR is zero-filled first.
+hipError_t contract_and_adjoint(const SideInfo& S, const GemmDesc& g, float* dR, const void* powers, float* dtheta,
+                                const AdjBufs& b, hipStream_t st) {
+  hipError_t e;
+  if (S.mode == POET_BS && (e = launch_fill(dR, S.prim_len, 0.f, st)) != hipSuccess) return e;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  return neumann_adjoint(S, dR, powers, dtheta, b, st);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -595,7 +614,6 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.compute = act;
     g.part = p.adj.part; g.part_elems = p.adj.part_elems;
     if (R.mode == POET_BS) {
-      HIP_TRY(launch_fill(p.dRg, R.prim_len, 0.f, st));
       g.M = g.N = R.bp; g.K = n; g.Mtot = g.Ntot = m; g.batch = R.nprim;
       if (fast) {
         g.A = p.Gb; g.a_dt = BF16; g.B = p.Tb; g.b_dt = BF16;
@@ -613,8 +631,7 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
       g.C = p.dRg; g.ldc = R.bp; g.c_dt = F32;
     }
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(neumann_adjoint(R, p.dRg, powersR, dthetaR, p.adj, st));
+    HIP_TRY(contract_and_adjoint(R, g, p.dRg, powersR, dthetaR, p.adj, st));
   }
   // primitive blocks of dL/dP = (R W0)^T G
   if (P.theta_len > 0) {
@@ -623,7 +640,6 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.compute = act;
     g.part = p.adj.part; g.part_elems = p.adj.part_elems;
     if (P.mode == POET_BS) {
-      HIP_TRY(launch_fill(p.dPg, P.prim_len, 0.f, st));
       g.M = g.N = P.bp; g.K = m; g.Mtot = g.Ntot = n; g.batch = P.nprim;
       if (fast) {
         g.A = p.RW0b; g.a_dt = BF16; g.B = p.Gb; g.b_dt = BF16;
@@ -641,8 +657,7 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
       g.C = p.dPg; g.ldc = P.bp; g.c_dt = F32;
     }
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(neumann_adjoint(P, p.dPg, powersP, dthetaP, p.adj, st));
+    HIP_TRY(contract_and_adjoint(P, g, p.dPg, powersP, dthetaP, p.adj, st));
   }
   return POET_OK;
 }

@@ -84,6 +84,42 @@ __device__ __forceinline__ void mma_strip(const char* Aq, const char* Xs, int wr
   }
 }
 
+// acc[a][b] += A[wr + 32a + (0..31)][0:kpad] . X[0:kpad][c0 + 32b + (0..31)] for NB column tiles (b < NB); the
+// same pipelining as mma_strip.
+template <int NB>
+__device__ __forceinline__ void mma_strip_n(const char* Aq, const char* Xs, int wr, int c0, int kpad, int lane,
+                                            f32x16 (&acc)[2][NB]) {
+  const int ra = wr + (lane & 31), rb = c0 + (lane & 31), kh = (lane >> 5) * 8;
+  const int ksteps = kpad / 16;  // even
+  bf16x8 a0[2], b0[NB], a1[2], b1[NB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) a0[t] = *reinterpret_cast<const bf16x8*>(Aq + loff(ra + 32 * t, kh));
+#pragma unroll
+  for (int t = 0; t < NB; ++t) b0[t] = *reinterpret_cast<const bf16x8*>(Xs + loff(rb + 32 * t, kh));
+  for (int ks = 0; ks < ksteps; ks += 2) {
+    const int k1 = (ks + 1) * 16 + kh;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) a1[t] = *reinterpret_cast<const bf16x8*>(Aq + loff(ra + 32 * t, k1));
+#pragma unroll
+    for (int t = 0; t < NB; ++t) b1[t] = *reinterpret_cast<const bf16x8*>(Xs + loff(rb + 32 * t, k1));
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[a], b0[b], acc[a][b], 0, 0, 0);
+    if (ks + 2 < ksteps) {
+      const int k2 = (ks + 2) * 16 + kh;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) a0[t] = *reinterpret_cast<const bf16x8*>(Aq + loff(ra + 32 * t, k2));
+#pragma unroll
+      for (int t = 0; t < NB; ++t) b0[t] = *reinterpret_cast<const bf16x8*>(Xs + loff(rb + 32 * t, k2));
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[a], b1[b], acc[a][b], 0, 0, 0);
+  }
+}
+
 // row / column (within the wave's 64 x 64 tile origin (wr, 0)) of accumulator register r of tile (a, b)
 __device__ __forceinline__ int acc_row(int wr, int a, int r, int lane) { return wr + a * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 __device__ __forceinline__ int acc_col(int b, int lane) { return b * 32 + (lane & 31); }

@@ -116,7 +116,7 @@ def test_bf16_small(mode, bR, bP):
     run_case(lin, pad=2, tag=f"bf16-{mode}")
 
 
-@pytest.mark.parametrize("bR,bP,k", [(200, 136, 8), (256, 24, 1), (248, 8, 2)])
+@pytest.mark.parametrize("bR,bP,k", [(200, 136, 8), (256, 24, 1), (248, 8, 2), (160, 128, 0)])
 def test_bf16_bs_block_sizes(bR, bP, k):
     """bf16 BS sides whose blocks are not multiples of the 64-column strips of the power chain (ragged strips,
     idle waves, a short last block), with long and short chains."""
