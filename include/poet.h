@@ -94,7 +94,8 @@ size_t poet_theta_len(const poet_side* s);
 size_t poet_num_prims(const poet_side* s);
 /* Float32 elements of a side's primitive buffer: num_prims * bp * bp. */
 size_t poet_prim_len(const poet_side* s);
-/* Elements (of the side's dtype) of the saved powers Q^1..Q^k: k * prim_len (0 when k == 0). */
+/* Elements (of the side's dtype) of the saved powers Q^1..Q^k: k * num_prims * bp * ldp, where the row pitch ldp
+ * is bp for float32 sides and bp rounded up to a multiple of 8 for bf16 sides (0 when k == 0). */
 size_t poet_powers_len(const poet_side* s);
 /* Workspace bytes a layer op needs (POET_OP_FWD, _BWD or _MERGE; POET_OP_BUILD gives 0, see
  * poet_build_workspace_bytes). For POET_OP_FWD the figure assumes W_out == NULL, and for POET_OP_BWD that
@@ -102,8 +103,10 @@ size_t poet_powers_len(const poet_side* s);
 size_t poet_workspace_bytes(const poet_layer* L, int op);
 /* Workspace bytes poet_sample_indices needs for dimension d. */
 size_t poet_sample_workspace_bytes(int32_t d);
-/* Workspace bytes poet_build_orthogonal needs: 0 when it is given a powers buffer or k == 0, otherwise
- * room for the power chain (k * prim_len elements of the side's dtype). */
+/* Workspace bytes poet_build_orthogonal needs: 0 when k == 0; otherwise room for the power chain
+ * (poet_powers_len elements of the side's dtype) when it is given no powers buffer, plus, for bf16 sides whose
+ * chain runs as separate products (FS, or BS blocks above 256 or not a multiple of 8), split-K scratch of
+ * 8 * poet_prim_len floats. */
 size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
 
 /* ---- the hot path ---------------------------------------------------------------------------------- */
@@ -113,7 +116,8 @@ size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
  *   theta  [poet_theta_len]  float32 in.
  *   prim   [poet_prim_len]   float32 out: R_k = I + 2(Q + ... + Q^k) + Q^{k+1} per primitive, padded.
  *   powers [poet_powers_len] out, side dtype, nullable: Q^1..Q^k of every primitive (power i of primitive
- *          p at offset ((i-1)*num_prims + p)*bp*bp), needed by poet_linear_bwd when k >= 1.
+ *          p at offset ((i-1)*num_prims + p)*bp*ldp, row pitch ldp, see poet_powers_len; the pad columns
+ *          are unspecified), needed by poet_linear_bwd when k >= 1.
  *   qnorm  [num_prims]       float32 out, nullable: Frobenius norm of each primitive's Q. The series
  *          converges for ||Q||_2 < 1; the pages warn it can diverge without enough terms (Limitations).
  *   ws     at least poet_build_workspace_bytes(s, powers != NULL) bytes (may be NULL when that is 0). */

@@ -243,6 +243,8 @@ def _side_sizes(s: poet_side):
 def poet_build_orthogonal(s: poet_side, theta, prim, powers=None, qnorm=None, ws=None, stream=None):
     nth, npr, npl, npw = _side_sizes(s)
     need_ws = poet_build_workspace_bytes(s, powers is not None)
+    if ws is None and need_ws > 0:  # scratch for the caller that passes none (device memory from torch)
+        ws = _torch().empty(need_ws, dtype=_torch().uint8, device=prim.device)
     st = lib().poet_build_orthogonal(
         ctypes.byref(s), _ptr(theta, "theta", 4 * nth, "float32"), _ptr(prim, "prim", 4 * npl, "float32"),
         _ptr(powers, "powers", npw * _esz(s.dtype), _dt_name(s.dtype), allow_none=True),

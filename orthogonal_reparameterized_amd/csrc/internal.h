@@ -98,7 +98,7 @@ hipError_t launch_generic_gemm(const GemmDesc& g, hipStream_t st);  // never the
 // ---- elementwise / data-movement kernels (kernels_misc.hip) ------------------------------------------
 // theta -> prim = I + coef*Q (coef 1 for k = 0, else 2) and, when q_out != null, Q in dtype q_dt.
 hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim,
-                             void* q_out, int q_dt, hipStream_t st);
+                             void* q_out, int q_dt, int ldq, hipStream_t st);  // q_out: bp x ldq blocks
 hipError_t launch_qnorm(const float* theta, int mode, int d, int bp, int nprim, float* qnorm, hipStream_t st);
 // dtheta_p = X_ij - X_ji with X = dQ + G1 (G1 nullable) for i < j < c of every primitive.
 hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d, int bp, int nprim,
@@ -125,15 +125,22 @@ hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
                                void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st);
-// prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1} with prim holding P_{k+1} on entry (k >= 1), Q from theta
+// prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1} with prim holding P_{k+1} on entry (k >= 1), Q from theta;
+// powers[t-1] = P_t as bp x ldp blocks
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
-                                 int dt, float* prim, hipStream_t st);
-// out = bf16(prim - I) for nprim bp x bp primitives (the delta of a factor as an MFMA operand)
-hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, __bf16* out, hipStream_t st);
-// Coefficient polynomials of the two-phase Neumann adjoint, stacked per primitive as a (k+1) bp x bp matrix:
-//   block j = sum_{t} a_{t+j+1} (-1)^{t+j} Q^t over t = 0..k-j (t >= 1 for j = 0), Q^0 = I, Q^t = powers[t-1],
-// with a_i = 2 for i <= k and a_{k+1} = 1. Written in dtype dt (the powers' dtype).
-hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int k, void* out, hipStream_t st);
+                                 int dt, int ldp, float* prim, hipStream_t st);
+// out = bf16(prim - I) for nprim bp x bp primitives (the delta of a factor as an MFMA operand), written as bp x ldo
+// blocks with zero columns past bp
+hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf16* out, hipStream_t st);
+// Coefficient polynomials of the two-phase Neumann adjoint, stacked per primitive as (k+1) ldp x ldp blocks (rows
+// and columns past bp zero): block j = sum_{t} a_{t+j+1} (-1)^{t+j} Q^t over t = 0..k-j (t >= 1 for j = 0),
+// Q^0 = I, Q^t = powers[t-1] (bp x ldp blocks), with a_i = 2 for i <= k and a_{k+1} = 1. Dtype dt (the powers').
+hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int ldp, int k, void* out, hipStream_t st);
+// gathers into a typed destination (dst_dt)
+hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
+hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
+                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch);
 
 }  // namespace poet

@@ -28,7 +28,7 @@ __device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
 __device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
 
 __global__ void k_theta_prep(const float* __restrict__ theta, int mode, int d, int bp, int nprim, float coef,
-                             float* __restrict__ prim, void* __restrict__ qout, int q_dt) {
+                             float* __restrict__ prim, void* __restrict__ qout, int q_dt, int ldq) {
   const int64_t total = (int64_t)nprim * bp * bp;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -43,8 +43,9 @@ __global__ void k_theta_prep(const float* __restrict__ theta, int mode, int d, i
     }
     prim[e] = (i == j ? 1.f : 0.f) + coef * q;
     if (qout) {
-      if (q_dt == BF16) reinterpret_cast<__bf16*>(qout)[e] = (__bf16)q;
-      else reinterpret_cast<float*>(qout)[e] = q;
+      const int64_t o = ((int64_t)p * bp + i) * ldq + j;
+      if (q_dt == BF16) reinterpret_cast<__bf16*>(qout)[o] = (__bf16)q;
+      else reinterpret_cast<float*>(qout)[o] = q;
     }
   }
 }
@@ -156,10 +157,13 @@ __global__ void k_convert(const float* __restrict__ src, int64_t ld_src, void* _
 __device__ __forceinline__ int clampi(int v, int lim) { return v < 0 ? 0 : (v >= lim ? lim - 1 : v); }
 
 __global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
-                              int s, int dlim, float* __restrict__ dst, int64_t ld_dst) {
+                              int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
   for (int r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x)
-      dst[(int64_t)r * ld_dst + j] = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x) {
+      const float v = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
+      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + j] = (__bf16)v;
+      else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + j] = v;
+    }
 }
 
 __global__ void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
@@ -170,13 +174,14 @@ __global__ void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, in
 }
 
 __global__ void k_gather_rows(const void* __restrict__ src, int src_dt, int64_t ld_src, const int32_t* __restrict__ idx,
-                              int s, int dlim, int cols, float* __restrict__ dst, int64_t ld_dst) {
+                              int s, int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
   for (int i = blockIdx.y; i < s; i += gridDim.y) {
     const int64_t row = (int64_t)clampi(idx[i], dlim) * ld_src;
     for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
       const float v = src_dt == BF16 ? (float)reinterpret_cast<const __bf16*>(src)[row + c]
                                      : reinterpret_cast<const float*>(src)[row + c];
-      dst[(int64_t)i * ld_dst + c] = v;
+      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)i * ld_dst + c] = (__bf16)v;
+      else reinterpret_cast<float*>(dst)[(int64_t)i * ld_dst + c] = v;
     }
   }
 }
@@ -246,11 +251,14 @@ __global__ void k_sample_compact(int d, const int32_t* __restrict__ flags, int32
   }
 }
 
-__global__ void k_delta_bf16(const float* __restrict__ prim, int64_t total, int bp, __bf16* __restrict__ out) {
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int rem = (int)(e % ((int64_t)bp * bp));
-    out[e] = (__bf16)(prim[e] - ((rem / bp) == (rem % bp) ? 1.f : 0.f));
-  }
+// out (bp x ldo rows per primitive, columns past bp zero) = bf16(prim - I); blockIdx.y = primitive
+__global__ void k_delta_bf16(const float* __restrict__ prim, int bp, int ldo, __bf16* __restrict__ out) {
+  const int p = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= bp * ldo) return;
+  const int i = e / ldo, j = e - i * ldo;
+  const float v = j < bp ? prim[((int64_t)p * bp + i) * bp + j] - (i == j ? 1.f : 0.f) : 0.f;
+  out[(int64_t)p * bp * ldo + e] = (__bf16)v;
 }
 
 __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
@@ -258,33 +266,35 @@ __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
 }
 
 // element (p, j, r, c) of the stacked coefficient matrices; see launch_adjoint_coefs
-// Block j of primitive p (blockIdx.y = p (k+1) + j); thread x covers VEC consecutive elements of the bp x bp block
-// (32-bit index math: a block holds at most 2^16 elements of one row-major primitive).
+// Block j of primitive p (blockIdx.y = p (k+1) + j), stored ldp x ldp (rows and columns past bp zero); thread x
+// covers VEC consecutive elements of it (32-bit index math). Powers are bp x ldp blocks.
 template <typename T, int VEC>
-__global__ void k_adjoint_coefs(const T* __restrict__ powers, int nprim, int bp, int k, T* __restrict__ out) {
-  const int pp = bp * bp;
+__global__ void k_adjoint_coefs(const T* __restrict__ powers, int nprim, int bp, int ldp, int k, T* __restrict__ out) {
+  const int pq = ldp * ldp;
   const int rc0 = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
-  if (rc0 >= pp) return;
+  if (rc0 >= pq) return;
   const int p = blockIdx.y / (k + 1), j = blockIdx.y - p * (k + 1);
+  const int r = rc0 / ldp, c0 = rc0 - r * ldp;  // VEC divides ldp: the VEC elements share the row
   float v[VEC];
 #pragma unroll
   for (int u = 0; u < VEC; ++u) v[u] = 0.f;
-  if (j > 0) {  // t = 0 term: a_{j+1} (-1)^j I
-    const float a = (j + 1 <= k ? 2.f : 1.f) * ((j & 1) ? -1.f : 1.f);
+  if (r < bp) {
+    if (j > 0) {  // t = 0 term: a_{j+1} (-1)^j I
+      const float a = (j + 1 <= k ? 2.f : 1.f) * ((j & 1) ? -1.f : 1.f);
 #pragma unroll
-    for (int u = 0; u < VEC; ++u) {
-      const int rc = rc0 + u;
-      if (rc / bp == rc % bp) v[u] = a;
+      for (int u = 0; u < VEC; ++u)
+        if (c0 + u == r) v[u] = a;
+    }
+    for (int t = 1; t <= k - j; ++t) {
+      const int i = t + j + 1;
+      const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
+      const T* src = powers + ((size_t)(t - 1) * nprim + p) * bp * ldp + (size_t)r * ldp + c0;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u)
+        if (c0 + u < bp) v[u] += a * (float)src[u];
     }
   }
-  for (int t = 1; t <= k - j; ++t) {
-    const int i = t + j + 1;
-    const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
-    const T* src = powers + ((size_t)(t - 1) * nprim + p) * pp + rc0;
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) v[u] += a * (float)src[u];
-  }
-  T* dst = out + ((size_t)p * (k + 1) + j) * pp + rc0;
+  T* dst = out + ((size_t)p * (k + 1) + j) * pq + rc0;
 #pragma unroll
   for (int u = 0; u < VEC; ++u) dst[u] = (T)v[u];
 }
@@ -292,7 +302,7 @@ __global__ void k_adjoint_coefs(const T* __restrict__ powers, int nprim, int bp,
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
 // (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1
 __global__ void k_chain_finalize(const float* __restrict__ theta, int mode, int d, int bp, int nprim, int k,
-                                 const void* __restrict__ powers, int dt, float* __restrict__ prim) {
+                                 const void* __restrict__ powers, int dt, int ldp, float* __restrict__ prim) {
   const int64_t pp = (int64_t)bp * bp, total = (int64_t)nprim * pp;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(e / pp);
@@ -305,7 +315,7 @@ __global__ void k_chain_finalize(const float* __restrict__ theta, int mode, int 
       q = i < j ? theta[off + tri_pos(i, j, c)] : -theta[off + tri_pos(j, i, c)];
     }
     float s = 0.f;
-    for (int t = 2; t <= k; ++t) s += ld_dt(powers, dt, (int64_t)(t - 1) * total + e);
+    for (int t = 2; t <= k; ++t) s += ld_dt(powers, dt, (((int64_t)(t - 1) * nprim + p) * bp + i) * ldp + j);
     prim[e] = (i == j ? 1.f : 0.f) + 2.f * q + 2.f * s + prim[e];
   }
 }
@@ -313,51 +323,52 @@ __global__ void k_chain_finalize(const float* __restrict__ theta, int mode, int 
 }  // namespace
 
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
-                                 int dt, float* prim, hipStream_t st) {
+                                 int dt, int ldp, float* prim, hipStream_t st) {
   const int64_t total = (int64_t)nprim * bp * bp;
   if (total == 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)total * (8 + 4 + (k - 1) * dtype_size(dt)));
   hipLaunchKernelGGL(k_chain_finalize, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim, k, powers,
-                     dt, prim);
+                     dt, ldp, prim);
   return hipGetLastError();
 }
 
-hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, __bf16* out, hipStream_t st) {
-  const int64_t total = (int64_t)nprim * bp * bp;
-  if (total == 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)total * 6);
-  hipLaunchKernelGGL(k_delta_bf16, dim3(grid_for(total)), dim3(kThreads), 0, st, prim, total, bp, out);
+hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf16* out, hipStream_t st) {
+  if (nprim <= 0 || bp <= 0) return hipSuccess;
+  if (nprim > 65535 || (int64_t)bp * ldo > (1 << 30)) return hipErrorInvalidValue;
+  ProfScope prof(7, st, 0, (double)nprim * bp * (4.0 * bp + 2.0 * ldo));
+  const dim3 grid((bp * ldo + kThreads - 1) / kThreads, nprim);
+  hipLaunchKernelGGL(k_delta_bf16, grid, dim3(kThreads), 0, st, prim, bp, ldo, out);
   return hipGetLastError();
 }
 
-hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int k, void* out, hipStream_t st) {
-  const int64_t total = (int64_t)nprim * (k + 1) * bp * bp;
+hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int ldp, int k, void* out, hipStream_t st) {
+  const int64_t total = (int64_t)nprim * (k + 1) * ldp * ldp;
   if (total == 0) return hipSuccess;
-  if ((int64_t)bp * bp > (1 << 30) || (int64_t)nprim * (k + 1) > 65535) return hipErrorInvalidValue;
+  if ((int64_t)ldp * ldp > (1 << 30) || (int64_t)nprim * (k + 1) > 65535) return hipErrorInvalidValue;
   ProfScope prof(7, st, 0, (double)total * dtype_size(dt) * 2);
-  const int pp = bp * bp;
-  if (dt == BF16 && pp % 4 == 0) {
-    const dim3 grid((pp / 4 + kThreads - 1) / kThreads, nprim * (k + 1));
+  const int pq = ldp * ldp;
+  if (dt == BF16 && ldp % 4 == 0) {
+    const dim3 grid((pq / 4 + kThreads - 1) / kThreads, nprim * (k + 1));
     hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 4>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const __bf16*>(powers), nprim, bp, k, reinterpret_cast<__bf16*>(out));
+                       reinterpret_cast<const __bf16*>(powers), nprim, bp, ldp, k, reinterpret_cast<__bf16*>(out));
   } else if (dt == BF16) {
-    const dim3 grid((pp + kThreads - 1) / kThreads, nprim * (k + 1));
+    const dim3 grid((pq + kThreads - 1) / kThreads, nprim * (k + 1));
     hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 1>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const __bf16*>(powers), nprim, bp, k, reinterpret_cast<__bf16*>(out));
+                       reinterpret_cast<const __bf16*>(powers), nprim, bp, ldp, k, reinterpret_cast<__bf16*>(out));
   } else {
-    const dim3 grid((pp + kThreads - 1) / kThreads, nprim * (k + 1));
+    const dim3 grid((pq + kThreads - 1) / kThreads, nprim * (k + 1));
     hipLaunchKernelGGL((k_adjoint_coefs<float, 1>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const float*>(powers), nprim, bp, k, reinterpret_cast<float*>(out));
+                       reinterpret_cast<const float*>(powers), nprim, bp, ldp, k, reinterpret_cast<float*>(out));
   }
   return hipGetLastError();
 }
 
 hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim, void* q_out,
-                             int q_dt, hipStream_t st) {
+                             int q_dt, int ldq, hipStream_t st) {
   const size_t total = (size_t)nprim * bp * bp;
   ProfScope prof(7, st, 0, (double)total * (4 + 4 + (q_out ? dtype_size(q_dt) : 0)));
   hipLaunchKernelGGL(k_theta_prep, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim,
-                     k == 0 ? 1.f : 2.f, prim, q_out, q_dt);
+                     k == 0 ? 1.f : 2.f, prim, q_out, q_dt, ldq);
   return hipGetLastError();
 }
 
@@ -409,12 +420,18 @@ hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t l
   return hipGetLastError();
 }
 
+hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
+  if (rows <= 0 || s <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
+  hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
+                     dst_dt, ld_dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim, float* dst,
                               int64_t ld_dst, hipStream_t st) {
-  if (rows <= 0 || s <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)rows * s * 8);
-  hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst, ld_dst);
-  return hipGetLastError();
+  return launch_gather_cols_to(src, ld_src, rows, idx, s, dlim, dst, F32, ld_dst, st);
 }
 
 hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
@@ -425,13 +442,18 @@ hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const
   return hipGetLastError();
 }
 
+hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
+                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
+  if (s <= 0 || cols <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt)));
+  hipLaunchKernelGGL(k_gather_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, src_dt, ld_src, idx, s, dlim, cols,
+                     dst, dst_dt, ld_dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
                               float* dst, int64_t ld_dst, hipStream_t st) {
-  if (s <= 0 || cols <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)s * cols * (4 + dtype_size(src_dt)));
-  hipLaunchKernelGGL(k_gather_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, src_dt, ld_src, idx, s, dlim, cols,
-                     dst, ld_dst);
-  return hipGetLastError();
+  return launch_gather_rows_to(src, src_dt, ld_src, idx, s, dlim, cols, dst, F32, ld_dst, st);
 }
 
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols, void* dst,

@@ -34,6 +34,8 @@ poet_status fail(poet_status st, const char* fmt, ...) {
 
 struct SideInfo {
   int mode = 0, d = 0, bp = 0, nprim = 0, k = 0, dtype = 0;
+  int ldp = 0;      // row pitch of the saved powers and the adjoint's work blocks (bf16: bp rounded up to 8)
+  size_t plen = 0;  // elements of one saved power over all primitives: nprim * bp * ldp
   size_t theta_len = 0, prim_len = 0, powers_len = 0;
 };
 
@@ -54,7 +56,9 @@ bool side_info(const poet_side* s, SideInfo* o, const char* name) {
   }
   o->theta_len = th;
   o->prim_len = (size_t)o->nprim * o->bp * o->bp;
-  o->powers_len = (size_t)o->k * o->prim_len;
+  o->ldp = o->dtype == POET_BF16 ? (o->bp + 7) / 8 * 8 : o->bp;
+  o->plen = (size_t)o->nprim * o->bp * o->ldp;
+  o->powers_len = (size_t)o->k * o->plen;
   return true;
 }
 
@@ -106,11 +110,27 @@ struct Arena {
 struct FsBufs {
   float *Ac = nullptr, *C1 = nullptr;  // m x sP
   float *Br = nullptr, *C2 = nullptr;  // sR x n
+  // bf16 operands of the fast kernel (rows padded to multiples of 8) and the scratch of its addend epilogue
+  __bf16 *Acb = nullptr, *dPb = nullptr;  // m x ldpP, sP x ldpP
+  __bf16 *Brb = nullptr, *dRb = nullptr;  // sR x ldn, sR x ldpR
+  float* part = nullptr;
+  size_t part_elems = 0;
 };
+
+inline int pad8(int x) { return (x + 7) / 8 * 8; }
+
+// bf16 FS factor application on the fast kernel: bf16 activations and a bf16 side
+bool fs_bf16(const poet_layer& L, const SideInfo& S) { return S.mode == POET_FS && L.act_dtype == BF16 && S.dtype == BF16; }
 
 void plan_fs(Arena& a, const poet_layer& L, const SideInfo& R, const SideInfo& P, FsBufs* f) {
   if (P.mode == POET_FS) { f->Ac = a.take<float>((size_t)L.m * P.bp); f->C1 = a.take<float>((size_t)L.m * P.bp); }
   if (R.mode == POET_FS) { f->Br = a.take<float>((size_t)R.bp * L.n); f->C2 = a.take<float>((size_t)R.bp * L.n); }
+  if (fs_bf16(L, P)) { f->Acb = a.take<__bf16>((size_t)L.m * P.ldp); f->dPb = a.take<__bf16>((size_t)P.bp * P.ldp); }
+  if (fs_bf16(L, R)) { f->Brb = a.take<__bf16>((size_t)R.bp * pad8(L.n)); f->dRb = a.take<__bf16>((size_t)R.bp * R.ldp); }
+  if (fs_bf16(L, P) || fs_bf16(L, R)) {
+    f->part_elems = std::max(fs_bf16(L, P) ? (size_t)L.m * P.bp : 0, fs_bf16(L, R) ? (size_t)R.bp * L.n : 0);
+    f->part = a.take<float>(f->part_elems);
+  }
 }
 
 hipError_t apply_P(const poet_layer& L, const SideInfo& P, const float* W0, const float* prim, const int32_t* idx,
@@ -131,10 +151,18 @@ hipError_t apply_P(const poet_layer& L, const SideInfo& P, const float* W0, cons
   hipError_t e = launch_gather_cols(W0, L.ldw, m, idx, s, n, f.Ac, s, st);
   if (e != hipSuccess) return e;
   g.M = m; g.N = s; g.K = s;
-  g.A = f.Ac; g.lda = s; g.a_dt = F32; g.a_kmajor = 1;
-  g.B = prim; g.ldb = s; g.b_dt = F32; g.b_kmajor = 0; g.b_sub_eye = 1;
   g.D = f.Ac; g.ldd = s; g.beta = 1.f;
   g.C = f.C1; g.ldc = s; g.c_dt = F32;
+  if (f.Acb && compute == BF16) {  // C1 = W0[:, I] + bf16(W0[:, I]) bf16(G_P - I) on the fast kernel
+    if ((e = launch_gather_cols_to(W0, L.ldw, m, idx, s, n, f.Acb, BF16, P.ldp, st)) != hipSuccess) return e;
+    if ((e = launch_delta_bf16(prim, 1, s, P.ldp, f.dPb, st)) != hipSuccess) return e;
+    g.A = f.Acb; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+    g.B = f.dPb; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+    g.part = f.part; g.part_elems = f.part_elems;
+  } else {
+    g.A = f.Ac; g.lda = s; g.a_dt = F32; g.a_kmajor = 1;
+    g.B = prim; g.ldb = s; g.b_dt = F32; g.b_kmajor = 0; g.b_sub_eye = 1;
+  }
   if ((e = launch_gemm(g, st)) != hipSuccess) return e;
   if ((e = launch_convert(W0, L.ldw, T, L.ldw, F32, m, n, st)) != hipSuccess) return e;
   return launch_scatter_cols(f.C1, s, m, idx, s, n, T, L.ldw, st);
@@ -158,10 +186,18 @@ hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, con
   hipError_t e = launch_gather_rows(src, F32, L.ldw, idx, s, m, n, f.Br, n, st);
   if (e != hipSuccess) return e;
   g.M = s; g.N = n; g.K = s;
-  g.A = prim; g.lda = s; g.a_dt = F32; g.a_kmajor = 1; g.a_sub_eye = 1;
-  g.B = f.Br; g.ldb = n; g.b_dt = F32; g.b_kmajor = 0;
   g.D = f.Br; g.ldd = n; g.beta = 1.f;
   g.C = f.C2; g.ldc = n; g.c_dt = F32;
+  if (f.Brb && compute == BF16) {  // C2 = src[I, :] + bf16(G_R - I) bf16(src[I, :]) on the fast kernel
+    if ((e = launch_gather_rows_to(src, F32, L.ldw, idx, s, m, n, f.Brb, BF16, pad8(n), st)) != hipSuccess) return e;
+    if ((e = launch_delta_bf16(prim, 1, s, R.ldp, f.dRb, st)) != hipSuccess) return e;
+    g.A = f.dRb; g.lda = R.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+    g.B = f.Brb; g.ldb = pad8(n); g.b_dt = BF16; g.b_kmajor = 0;
+    g.part = f.part; g.part_elems = f.part_elems;
+  } else {
+    g.A = prim; g.lda = s; g.a_dt = F32; g.a_kmajor = 1; g.a_sub_eye = 1;
+    g.B = f.Br; g.ldb = n; g.b_dt = F32; g.b_kmajor = 0;
+  }
   if ((e = launch_gemm(g, st)) != hipSuccess) return e;
   if ((e = launch_convert(src, L.ldw, out, ldo, out_dt, m, n, st)) != hipSuccess) return e;
   return launch_scatter_rows(f.C2, n, idx, s, m, n, out, out_dt, ldo, st);
@@ -223,25 +259,29 @@ hipError_t apply_R_b(const poet_layer& L, const SideInfo& R, const __bf16* srcb,
 // ------------------------------------------------------------------------------------------------------------
 struct AdjBufs {
   float* dQ = nullptr;
-  void* H = nullptr;   // nprim x b x (k+1) b, side dtype
-  void* Cs = nullptr;  // nprim x (k+1) b x b, side dtype
+  void* H = nullptr;   // nprim x bp x (k+1) ldp, side dtype
+  void* Cs = nullptr;  // nprim x (k+1) ldp x ldp, side dtype
   float* part = nullptr;
   size_t part_elems = 0;
 };
 
-size_t adj_elems(const SideInfo& S) { return (size_t)S.nprim * S.bp * S.bp * (S.k + 1); }
+size_t adj_h_elems(const SideInfo& S) { return (size_t)S.nprim * S.bp * S.ldp * (S.k + 1); }
+size_t adj_c_elems(const SideInfo& S) { return (size_t)S.nprim * S.ldp * S.ldp * (S.k + 1); }
 
+// H_j sits at column j ldp of the H rows (16-byte aligned operands for the bf16 kernel); with ldp > bp the gap
+// columns are zeroed, and the matching rows of the coefficient stack are zero, so the phase-2 product can run
+// over K = (k+1) ldp.
 hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powers, float* dtheta, const AdjBufs& b,
                            hipStream_t st) {
   if (S.theta_len == 0) return hipSuccess;
   const int64_t pp = (int64_t)S.bp * S.bp;
   if (S.k == 0) return launch_skew_project(dRg, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
-  const int bp = S.bp, k = S.k, ldh = (k + 1) * bp;
-  const int64_t hs = (int64_t)bp * ldh;
+  const int bp = S.bp, k = S.k, ldp = S.ldp, ldh = (k + 1) * ldp;
+  const int64_t hs = (int64_t)bp * ldh, ps = (int64_t)bp * ldp;
   const size_t esz = dtype_size(S.dtype);
   char* H = reinterpret_cast<char*>(b.H);
   hipError_t e = hipSuccess;
-  const bool chain = power_chain_eligible(bp, S.dtype, powers);
+  const bool chain = ldp == bp && power_chain_eligible(bp, S.dtype, powers);
   if (chain) {  // H_0 = dR and H_{j+1} = Q H_j in one launch
     ChainArgs c;
     c.bp = bp; c.nprim = S.nprim; c.steps = k;
@@ -250,24 +290,30 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
     c.Y = reinterpret_cast<__bf16*>(H); c.ldy = ldh; c.sy = hs; c.jstep = bp; c.write_x0 = 1;
     e = launch_power_chain(c, POET_K_ADJOINT, st);
   } else {
+    if (ldp > bp) {  // zero the gap columns once (the products below write only the first bp of each block)
+      // (zero bits; ldh is even, so the bf16 block is a whole number of floats)
+      if (S.dtype == BF16) e = launch_fill(reinterpret_cast<float*>(H), (size_t)S.nprim * hs / 2, 0.f, st);
+      if (e != hipSuccess) return e;
+    }
     e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
     for (int j = 0; j < k && e == hipSuccess; ++j) {  // H_{j+1} = Q H_j
       GemmDesc g;
       g.kclass = POET_K_ADJOINT;
       g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
-      g.A = powers; g.lda = bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
-      g.B = H + (size_t)j * bp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
-      g.C = H + (size_t)(j + 1) * bp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
+      g.A = powers; g.lda = ldp; g.sA = ps; g.a_dt = S.dtype; g.a_kmajor = 1;
+      g.B = H + (size_t)j * ldp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
+      g.C = H + (size_t)(j + 1) * ldp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
+      g.part = b.part; g.part_elems = b.part_elems;  // split K when the grid is small
       e = launch_gemm(g, st);
     }
   }
   if (e != hipSuccess) return e;
-  if ((e = launch_adjoint_coefs(powers, S.dtype, S.nprim, bp, k, b.Cs, st)) != hipSuccess) return e;
+  if ((e = launch_adjoint_coefs(powers, S.dtype, S.nprim, bp, ldp, k, b.Cs, st)) != hipSuccess) return e;
   GemmDesc g;  // dQ = a_1 dR + [H_0 .. H_k] [C_0; ..; C_k]
   g.kclass = POET_K_ADJOINT;
-  g.compute = S.dtype; g.M = g.N = bp; g.K = (k + 1) * bp; g.batch = S.nprim;
+  g.compute = S.dtype; g.M = g.N = bp; g.K = (k + 1) * ldp; g.batch = S.nprim;
   g.A = H; g.lda = ldh; g.sA = hs; g.a_dt = S.dtype; g.a_kmajor = 1;
-  g.B = b.Cs; g.ldb = bp; g.sB = (int64_t)(k + 1) * pp; g.b_dt = S.dtype; g.b_kmajor = 0;
+  g.B = b.Cs; g.ldb = ldp; g.sB = (int64_t)(k + 1) * ldp * ldp; g.b_dt = S.dtype; g.b_kmajor = 0;
   g.C = b.dQ; g.ldc = bp; g.sC = pp; g.c_dt = F32;
   g.part = b.part; g.part_elems = b.part_elems;
   g.defer_reduce = 1;
@@ -363,15 +409,17 @@ size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void*
   p->dRg = a.take<float>(R.prim_len);
   p->dPg = a.take<float>(P.prim_len);
   p->adj.dQ = a.take<float>(std::max(R.prim_len, P.prim_len));
-  const size_t hb = std::max(adj_elems(R) * dtype_size(R.dtype), adj_elems(P) * dtype_size(P.dtype));
-  p->adj.H = a.take_bytes(hb);
-  p->adj.Cs = a.take_bytes(hb);
+  p->adj.H = a.take_bytes(std::max(adj_h_elems(R) * dtype_size(R.dtype), adj_h_elems(P) * dtype_size(P.dtype)));
+  p->adj.Cs = a.take_bytes(std::max(adj_c_elems(R) * dtype_size(R.dtype), adj_c_elems(P) * dtype_size(P.dtype)));
   // split-K partial sums: the weight gradient with up to 4 splits, or the primitive products with up to 16
   p->adj.part_elems = std::max({4 * mn, 16 * std::max(R.prim_len, P.prim_len), apply_part_elems(L, R, P)});
   p->adj.part = a.take<float>(p->adj.part_elems);
   plan_fs(a, L, R, P, &p->fs);
-  if (R.mode == POET_FS) { p->Gr = a.take<float>((size_t)R.bp * L.n); p->Zr = a.take<float>((size_t)R.bp * L.n); }
-  if (P.mode == POET_FS) { p->Acp = a.take<float>((size_t)L.m * P.bp); p->Gc = a.take<float>((size_t)L.m * P.bp); }
+  // FS gathers: float32, or bf16 with padded rows in the same room
+  const size_t gr = std::max((size_t)R.bp * L.n, ((size_t)R.bp * pad8(L.n) + 1) / 2);
+  const size_t gc = std::max((size_t)L.m * P.bp, ((size_t)L.m * P.ldp + 1) / 2);
+  if (R.mode == POET_FS) { p->Gr = a.take<float>(gr); p->Zr = a.take<float>(gr); }
+  if (P.mode == POET_FS) { p->Acp = a.take<float>(gc); p->Gc = a.take<float>(gc); }
   return a.used();
 }
 
@@ -423,11 +471,20 @@ size_t poet_powers_len(const poet_side* s) {
   SideInfo i;
   return side_info(s, &i, "side") ? i.powers_len : 0;
 }
+// split-K scratch of the build's power-chain GEMMs: bf16 sides the fused chain kernel does not take (FS, or BS
+// blocks above 256 or not a multiple of 8); room for up to 8 splits of one power
+size_t build_part_elems(const SideInfo& i) {
+  const bool gemm_chain = i.dtype == BF16 && i.k > 0 && !(i.ldp == i.bp && i.bp <= 256 && i.bp % 8 == 0);
+  return gemm_chain ? 8 * i.prim_len : 0;
+}
+
 size_t poet_build_workspace_bytes(const poet_side* s, int with_powers) {
   SideInfo i;
   if (!side_info(s, &i, "side")) return 0;
-  if (with_powers || i.k == 0) return 0;
-  return align_up((size_t)i.k * i.prim_len * dtype_size(i.dtype), 256) + 512;
+  if (i.k == 0) return 0;
+  const size_t pw = with_powers ? 0 : align_up(i.powers_len * dtype_size(i.dtype), 256);
+  const size_t part = build_part_elems(i) * sizeof(float);
+  return pw + part == 0 ? 0 : pw + part + 512;
 }
 size_t poet_sample_workspace_bytes(int32_t d) { return d > 0 ? align_up((size_t)d * 4, 256) + 256 : 0; }
 
@@ -453,39 +510,42 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   if (!check_ws(ws, ws_bytes, need)) return g_last;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const size_t esz = dtype_size(S.dtype);
-  // powers P_1 = Q, ..., P_k (the caller's buffer, or the workspace when the caller keeps none)
+  // powers P_1 = Q, ..., P_k (the caller's buffer, or the workspace when the caller keeps none), then the split-K
+  // scratch of the GEMM chain
   char* pw = reinterpret_cast<char*>(powers);
-  if (!powers && S.k > 0) {
-    Arena a(ws);
-    pw = reinterpret_cast<char*>(a.take_bytes((size_t)S.k * S.prim_len * esz));
-  }
+  Arena a(ws);
+  if (!powers && S.k > 0) pw = reinterpret_cast<char*>(a.take_bytes(S.powers_len * esz));
+  const size_t part_elems = build_part_elems(S);
+  float* part = part_elems ? a.take<float>(part_elems) : nullptr;
   if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
   // prim = I + coef Q (coef 2 for k >= 1) with Q exact from theta, and the first saved power Q
-  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype, st));
-  if (S.k > 0 && power_chain_eligible(S.bp, S.dtype, pw)) {
+  HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype,
+                            S.ldp, st));
+  if (S.k > 0 && S.ldp == S.bp && power_chain_eligible(S.bp, S.dtype, pw)) {
     // the k products and the rest of the series in one launch, Q resident in LDS
     ChainArgs c;
     c.bp = S.bp; c.nprim = S.nprim; c.steps = S.k; c.build = 1; c.prim = prim;
     c.A = reinterpret_cast<const __bf16*>(pw); c.sA = (int64_t)S.bp * S.bp;
-    c.Y = reinterpret_cast<__bf16*>(pw); c.ldy = S.bp; c.sy = (int64_t)S.bp * S.bp; c.jstep = (int64_t)S.prim_len;
+    c.Y = reinterpret_cast<__bf16*>(pw); c.ldy = S.bp; c.sy = (int64_t)S.bp * S.bp; c.jstep = (int64_t)S.plen;
     HIP_TRY(launch_power_chain(c, POET_K_CHAIN, st));
     return POET_OK;
   }
   if (S.k == 0) return POET_OK;  // R_0 = I + Q
   const int64_t pp = (int64_t)S.bp * S.bp;
+  const int64_t ps = (int64_t)S.bp * S.ldp;
   for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i; the last power goes straight into prim (float32)
     GemmDesc g;
     g.kclass = POET_K_CHAIN;
     g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
-    g.A = pw; g.lda = S.bp; g.sA = pp; g.a_dt = S.dtype; g.a_kmajor = 1;
-    g.B = pw + (size_t)(i - 1) * S.prim_len * esz; g.ldb = S.bp; g.sB = pp; g.b_dt = S.dtype; g.b_kmajor = 0;
-    if (i < S.k) { g.C = pw + (size_t)i * S.prim_len * esz; g.c_dt = S.dtype; }
-    else { g.C = prim; g.c_dt = F32; }
-    g.ldc = S.bp; g.sC = pp;
+    g.A = pw; g.lda = S.ldp; g.sA = ps; g.a_dt = S.dtype; g.a_kmajor = 1;
+    g.B = pw + (size_t)(i - 1) * S.plen * esz; g.ldb = S.ldp; g.sB = ps; g.b_dt = S.dtype; g.b_kmajor = 0;
+    if (i < S.k) { g.C = pw + (size_t)i * S.plen * esz; g.c_dt = S.dtype; g.ldc = S.ldp; g.sC = ps; }
+    else { g.C = prim; g.c_dt = F32; g.ldc = S.bp; g.sC = pp; }
+    g.part = part; g.part_elems = part_elems;
     HIP_TRY(launch_gemm(g, st));
   }
   // prim = I + 2Q + 2(P_2 + ... + P_k) + P_{k+1}, the linear term exact from theta
-  HIP_TRY(launch_chain_finalize(theta, S.mode, S.d, S.bp, S.nprim, S.k, pw, S.dtype, prim, st));
+  HIP_TRY(launch_chain_finalize(theta, S.mode, S.d, S.bp, S.nprim, S.k, pw, S.dtype, S.ldp, prim, st));
   return POET_OK;
 }
 
@@ -520,8 +580,8 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
     HIP_TRY(launch_bs_apply(apply_args(*L, R, P, W0, primR, primP, nullptr, W, act, nullptr), st));
   } else if (bs_bf16(*L, R, P)) {
     HIP_TRY(launch_convert(W0, L->ldw, p.W0b, L->ldw, BF16, L->m, L->n, st));
-    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));
-    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, p.dPb, st));
+    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, R.bp, p.dRb, st));
+    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, P.bp, p.dPb, st));
     HIP_TRY(apply_P_b(*L, P, W0, p.W0b, p.dPb, p.Tb, p.T, p.part, st));
     HIP_TRY(apply_R_b(*L, R, p.Tb, p.T, p.dRb, W, act, p.part, st));
   } else {
@@ -569,8 +629,8 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
   } else if (fast) {
     // bf16 operands: W0, the factor deltas, Z = W0 P (R-side gradient), R W0 (P-side gradient), G
     HIP_TRY(launch_convert(W0, ldw, p.W0b, ldw, BF16, m, n, st));
-    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, p.dRb, st));
-    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, p.dPb, st));
+    HIP_TRY(launch_delta_bf16(primR, R.nprim, R.bp, R.bp, p.dRb, st));
+    HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, P.bp, p.dPb, st));
     HIP_TRY(apply_P_b(*L, P, W0, p.W0b, p.dPb, p.Tb, W ? nullptr : p.T, Part{p.adj.part, p.adj.part_elems}, st));
     if (!W) {
       HIP_TRY(apply_R_b(*L, R, p.Tb, p.T, p.dRb, p.W, act, Part{p.adj.part, p.adj.part_elems}, st));
@@ -624,12 +684,20 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       g.ldb = ldw; g.sB = (int64_t)R.bp * ldw; g.b_kmajor = 1;
       g.C = p.dRg; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
     } else {
-      HIP_TRY(launch_gather_rows(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, n, st));
-      HIP_TRY(launch_gather_rows(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, n, st));
       g.M = g.N = R.bp; g.K = n;
-      g.A = p.Gr; g.lda = n; g.a_dt = F32; g.a_kmajor = 1;
-      g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
       g.C = p.dRg; g.ldc = R.bp; g.c_dt = F32;
+      if (fs_bf16(*L, R)) {  // gathered rows as bf16 operands (row pitch padded to 8) on the fast kernel
+        const int ldn = pad8(n);
+        HIP_TRY(launch_gather_rows_to(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, BF16, ldn, st));
+        HIP_TRY(launch_gather_rows_to(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, BF16, ldn, st));
+        g.A = p.Gr; g.lda = ldn; g.a_dt = BF16; g.a_kmajor = 1;
+        g.B = p.Zr; g.ldb = ldn; g.b_dt = BF16; g.b_kmajor = 1;
+      } else {
+        HIP_TRY(launch_gather_rows(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, n, st));
+        HIP_TRY(launch_gather_rows(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, n, st));
+        g.A = p.Gr; g.lda = n; g.a_dt = F32; g.a_kmajor = 1;
+        g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
+      }
     }
     HIP_TRY(contract_and_adjoint(R, g, p.dRg, powersR, dthetaR, p.adj, st));
   }
@@ -650,12 +718,19 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       g.ldb = ldw; g.sB = P.bp; g.b_kmajor = 0;
       g.C = p.dPg; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
     } else {
-      HIP_TRY(launch_gather_cols(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, P.bp, st));
-      HIP_TRY(launch_gather_cols(p.G, ldw, m, idxP, P.bp, n, p.Gc, P.bp, st));
       g.M = g.N = P.bp; g.K = m;
-      g.A = p.Acp; g.lda = P.bp; g.a_dt = F32; g.a_kmajor = 0;
-      g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
       g.C = p.dPg; g.ldc = P.bp; g.c_dt = F32;
+      if (fs_bf16(*L, P)) {  // gathered columns as bf16 operands (row pitch ldp) on the fast kernel
+        HIP_TRY(launch_gather_cols_to(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, BF16, P.ldp, st));
+        HIP_TRY(launch_gather_cols_to(p.G, ldw, m, idxP, P.bp, n, p.Gc, BF16, P.ldp, st));
+        g.A = p.Acp; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 0;
+        g.B = p.Gc; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+      } else {
+        HIP_TRY(launch_gather_cols(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, P.bp, st));
+        HIP_TRY(launch_gather_cols(p.G, ldw, m, idxP, P.bp, n, p.Gc, P.bp, st));
+        g.A = p.Acp; g.lda = P.bp; g.a_dt = F32; g.a_kmajor = 0;
+        g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
+      }
     }
     HIP_TRY(contract_and_adjoint(P, g, p.dPg, powersP, dthetaP, p.adj, st));
   }

@@ -53,7 +53,8 @@ class PoetLinear:
         self.dthetaR = torch.empty(max(nR, 1), dtype=torch.float32, device=self.dev)
         self.dthetaP = torch.empty(max(nP, 1), dtype=torch.float32, device=self.dev)
         wsb = max(B.poet_workspace_bytes(self.L, op) for op in (B.POET_OP_FWD, B.POET_OP_BWD, B.POET_OP_MERGE))
-        wsb = max(wsb, B.poet_sample_workspace_bytes(max(m, n)))
+        wsb = max(wsb, B.poet_sample_workspace_bytes(max(m, n)), B.poet_build_workspace_bytes(R, True),
+                  B.poet_build_workspace_bytes(P, True))
         self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
         self.idxR = self.idxP = None
         if R.mode == B.POET_FS:
@@ -77,9 +78,9 @@ class PoetLinear:
 
     def build(self, stream=None, qnorm: bool = False):
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
-                                None, stream)
+                                self.ws, stream)
         B.poet_build_orthogonal(self.L.P, self.thetaP, self.primP, self._powers("P"), self.qnormP if qnorm else None,
-                                None, stream)
+                                self.ws, stream)
 
     def alloc_act(self, rows: int, ld: int):
         return _torch().empty((rows, ld), dtype=self.act, device=self.dev)
