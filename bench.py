@@ -143,19 +143,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(8)}
+    prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
     B.poet_profile_enable(False)
 
-    # merge-then-reinitialize of every linear, timed on its own and amortized over its period
+    # merge-then-reinitialize of every linear, timed on its own and amortized over its period; its kernels are
+    # profiled separately (algorithmic HBM bytes: every element of W0 read and written once, float32)
+    # (one untimed merge first: the first call of each kernel pays its load; the work of a merge does not depend
+    # on the state it leaves, and a third, profiled merge gives the per-class kernel times)
     log("merge")
-    torch.cuda.synchronize()
-    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    m0.record()
-    for e in lins:
-        e["pl"].merge()
-    m1.record()
-    torch.cuda.synchronize()
-    ms_merge = m0.elapsed_time(m1)
+    for rep in range(3):
+        torch.cuda.synchronize()
+        B.poet_profile_enable(rep == 2)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for e in lins:
+            e["pl"].merge()
+        m1.record()
+        torch.cuda.synchronize()
+        if rep == 1:
+            ms_merge = m0.elapsed_time(m1)
+    mprof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
+    B.poet_profile_enable(False)
+    merge_bytes = sum(8.0 * e["spec"].m * e["spec"].n for e in lins)
+    merge_info = {"ms_all_linears": round(ms_merge, 4), "algorithmic_bytes": merge_bytes,
+                  "achieved_GBps": round(merge_bytes / (ms_merge / 1e3) / 1e9, 1),
+                  "hbm_frac": round(merge_bytes / (ms_merge / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "kernel_ms": {k: round(v["ms"], 4) for k, v in mprof.items() if v["launches"]},
+                  "kernel_launches": {k: v["launches"] for k, v in mprof.items() if v["launches"]}}
 
     ms_total = ms_step + ms_merge / args.merge_period
     tokens_per_s = T / (ms_total / 1e3)
@@ -183,7 +197,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "avg_launch_ms": round(avg_ms, 4), "launches": d["launches"],
                      "flops_per_launch": d["flops"] / max(d["launches"], 1)},
-        "ms_fwd_bwd": round(ms_step, 4), "ms_merge_all_linears": round(ms_merge, 4),
+        "ms_fwd_bwd": round(ms_step, 4), "ms_merge_all_linears": round(ms_merge, 4), "merge": merge_info,
         "host_wall_s": round(wall, 3),
         "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
         "step_mfu": round(algorithmic_flops(lins) / (ms_total / 1e3) / 1e12 / peak, 4),

@@ -80,6 +80,16 @@ struct ApplyArgs {
 bool bs_apply_eligible(int bpR, int bpP, const float* W0, int64_t ldw, const float* primR, const float* primP);
 hipError_t launch_bs_apply(const ApplyArgs& c, hipStream_t st);
 
+// In-place merge pass of a block-diagonal factor (bs_merge.hip), blocks bp <= 256, float32 accuracy:
+//   rside = 0:  W[:, J] <- W[:, J] F_J for every block J of the columns (F = P, blocks along n)
+//   rside = 1:  W[I, :] <- F_I W[I, :] for every block I of the rows (F = R, blocks along m); also writes
+//               shadow (dtype sh_dt, row pitch ld_sh) when non-null
+// prim: nblk float32 bp x bp blocks; split: bs_merge_split_bytes(bp, nblk) bytes of scratch.
+bool bs_merge_eligible(int bp, int m, int64_t ld);  // W0 (m x ld floats) under 2 GB
+size_t bs_merge_split_bytes(int bp, int nblk);
+hipError_t launch_bs_merge_pass(float* W, int64_t ld, int m, int n, int rside, int bp, int nblk, const float* prim,
+                                char* split, void* shadow, int sh_dt, int64_t ld_sh, hipStream_t st);
+
 // launch profiler (profiler.hip): no-ops unless poet_profile_enable(1) was called
 int prof_begin(int kclass, hipStream_t st, double flops, double bytes);
 void prof_end(int rec, hipStream_t st);

@@ -424,12 +424,21 @@ size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void*
 }
 
 struct MergePlan {
+  bool inplace = false;   // both sides block-diagonal with blocks <= 256: two in-place passes over W0
+  char* split = nullptr;  // their pre-split factor deltas
   float *T = nullptr, *Wn = nullptr;
   int32_t* flags = nullptr;
   FsBufs fs;
 };
 size_t plan_merge(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, MergePlan* p) {
   Arena a(ws);
+  p->inplace = R.mode == POET_BS && P.mode == POET_BS && bs_merge_eligible(R.bp, L.m, L.ldw) &&
+                bs_merge_eligible(P.bp, L.m, L.ldw);
+  if (p->inplace) {
+    p->split = reinterpret_cast<char*>(
+        a.take_bytes(std::max(bs_merge_split_bytes(R.bp, R.nprim), bs_merge_split_bytes(P.bp, P.nprim))));
+    return a.used();
+  }
   const size_t mn = (size_t)L.m * L.ldw;
   p->T = a.take<float>(mn);
   p->Wn = a.take<float>(mn);
@@ -750,10 +759,16 @@ poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* t
   if (!check_ws(ws, ws_bytes, need)) return g_last;
   plan_merge(*L, R, P, ws, &p);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, F32, p.fs, st));
-  HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.Wn, F32, L->ldw, F32, p.fs, st));
-  HIP_TRY(launch_convert(p.Wn, L->ldw, W0, L->ldw, F32, L->m, L->n, st));
-  if (W0_shadow) HIP_TRY(launch_convert(p.Wn, L->ldw, W0_shadow, L->ldw, L->act_dtype, L->m, L->n, st));
+  if (p.inplace) {  // W0 <- W0 P, then W0 <- R W0 (writing the shadow), in place
+    HIP_TRY(launch_bs_merge_pass(W0, L->ldw, L->m, L->n, 0, P.bp, P.nprim, primP, p.split, nullptr, F32, 0, st));
+    HIP_TRY(launch_bs_merge_pass(W0, L->ldw, L->m, L->n, 1, R.bp, R.nprim, primR, p.split, W0_shadow, L->act_dtype,
+                                 L->ldw, st));
+  } else {
+    HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, F32, p.fs, st));
+    HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.Wn, F32, L->ldw, F32, p.fs, st));
+    HIP_TRY(launch_convert(p.Wn, L->ldw, W0, L->ldw, F32, L->m, L->n, st));
+    if (W0_shadow) HIP_TRY(launch_convert(p.Wn, L->ldw, W0_shadow, L->ldw, L->act_dtype, L->m, L->n, st));
+  }
   if (R.theta_len > 0) HIP_TRY(launch_fill(thetaR, R.theta_len, 0.f, st));
   if (P.theta_len > 0) HIP_TRY(launch_fill(thetaP, P.theta_len, 0.f, st));
   if (R.mode == POET_FS)

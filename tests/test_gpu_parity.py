@@ -125,6 +125,17 @@ def test_bf16_bs_block_sizes(bR, bP, k):
     run_case(lin, pad=6, tag=f"bf16-bs-{bR}-{bP}-k{k}")
 
 
+@pytest.mark.parametrize("m,n,bR,bP,dt,pad", [(300, 520, 256, 100, PI.DT_F32, 3), (1000, 700, 256, 256, PI.DT_BF16, 0),
+                                             (257, 129, 128, 64, PI.DT_BF16, 5), (140, 96, 20, 36, PI.DT_F32, 0)])
+def test_bs_merge_large_theta(m, n, bR, bP, dt, pad):
+    """The in-place merge at theta std 0.02, where the factor deltas are large enough that a dropped low-order
+    term of the split products (about 2^-9 |dF| relative) or a misplaced element fails the float32 bar: ragged
+    last blocks, blocks not a multiple of 8 (unaligned rows), padded rows, both shadow dtypes. The sides are
+    float32 (a bf16 power chain's rounding at this theta exceeds the primitive bar, which is set for std 1e-3)."""
+    lin = make_linear(f"merge-{m}-{n}", m, n, 64, PI.MODE_BS, bR, bP, 3, dt, linear_id=2, side_dt=PI.DT_F32)
+    run_case(lin, pad=pad, theta_std=0.02, tag=f"bs-merge-{m}x{n}-{bR}-{bP}")
+
+
 def test_bf16_acts_fp32_chain():
     lin = make_linear("mixed", 160, 224, 128, PI.MODE_BS, 64, 32, 5, PI.DT_BF16, side_dt=PI.DT_F32)
     run_case(lin, tag="bf16-act-fp32-chain")
