@@ -29,19 +29,21 @@ def log(msg):
     sys.stderr.flush()
 
 
-def build_block(wl, torch, B, PI, PoetLinear):
+def build_block(wl, torch, B, PI, PoetLinear, path="auto"):
     lins = []
     for lin in wl.linears(0):
         W0, tR, tP = PI.gen_weights(wl.cfg_id, 0, lin)
         ldw, ldx, ldy = PI.pad_ld(lin.n), PI.pad_ld(lin.n), PI.pad_ld(lin.m)
         pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
-                        seed=wl.seed, linear_id=lin.linear_id, ldw=ldw, ldx=ldx, ldy=ldy)
+                        seed=wl.seed, linear_id=lin.linear_id, ldw=ldw, ldx=ldx, ldy=ldy, path=path)
         g = torch.Generator(device="cuda")
         g.manual_seed(1000 * wl.cfg_id + lin.linear_id)
         X = torch.randn((lin.T, ldx), generator=g, device="cuda", dtype=torch.float32).to(pl.act)
         dY = torch.randn((lin.T, ldy), generator=g, device="cuda", dtype=torch.float32).to(pl.act)
+        # the tensor the forward keeps for the backward: Z = X P^T W0^T (activation-side path) or W
+        keep = pl.alloc_act(lin.T, ldy) if pl.act_path else pl.alloc_W()
         lins.append({"spec": lin, "pl": pl, "X": X, "dY": dY, "Y": pl.alloc_act(lin.T, ldy),
-                     "dX": pl.alloc_act(lin.T, ldx), "W": pl.alloc_W()})
+                     "dX": pl.alloc_act(lin.T, ldx), "keep": keep})
     return lins
 
 
@@ -49,8 +51,12 @@ def step(lins):
     for e in lins:
         pl = e["pl"]
         pl.build()
-        pl.forward(e["X"], e["Y"], W_out=e["W"])
-        pl.backward(e["X"], e["dY"], e["dX"], W=e["W"])
+        if pl.act_path:
+            pl.forward_act(e["X"], e["Y"], e["keep"])
+            pl.backward_act(e["X"], e["keep"], e["dY"], e["dX"])
+        else:
+            pl.forward(e["X"], e["Y"], W_out=e["keep"])
+            pl.backward(e["X"], e["dY"], e["dX"], W=e["keep"])
 
 
 def algorithmic_flops(lins):
@@ -103,6 +109,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4])
     ap.add_argument("--merge-period", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=["auto", "weight", "act"],
+                    help="apply R and P to the activations around the W0 GEMM (act), materialize W (weight), or "
+                         "the activation side wherever it is supported (auto)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -121,7 +130,7 @@ def main():
     B.lib()
     wl = PI.WORKLOADS[args.workload]
     log(f"workload {wl.name}: allocating")
-    lins = build_block(wl, torch, B, PI, PoetLinear)
+    lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
     torch.cuda.synchronize()
     T = wl.T
 
@@ -164,7 +173,8 @@ def main():
             ms_merge = m0.elapsed_time(m1)
     mprof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
     B.poet_profile_enable(False)
-    merge_bytes = sum(8.0 * e["spec"].m * e["spec"].n for e in lins)
+    # (plus the bf16 copy of W0 the activation-side path reads, written by the same merge)
+    merge_bytes = sum((10.0 if e["pl"].act_path else 8.0) * e["spec"].m * e["spec"].n for e in lins)
     merge_info = {"ms_all_linears": round(ms_merge, 4), "algorithmic_bytes": merge_bytes,
                   "achieved_GBps": round(merge_bytes / (ms_merge / 1e3) / 1e9, 1),
                   "hbm_frac": round(merge_bytes / (ms_merge / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -192,6 +202,8 @@ def main():
         "config": {"workload": wl.name, "hidden": wl.hidden, "ffn": wl.ffn, "tokens": T,
                    "mode": "BS" if wl.mode == PI.MODE_BS else "FS",
                    "block": wl.b, "fraction": wl.frac, "k": wl.k, "linears": len(lins),
+                   "factor_application": "activations" if all(e["pl"].act_path for e in lins) else
+                   ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
                    "merge_period": args.merge_period},
         "roofline": {"bound": "mfma", "kernel": f"gemm ({dom})", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,

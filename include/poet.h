@@ -65,7 +65,7 @@ typedef enum {
 enum { POET_BS = 0, POET_FS = 1 };                 /* side modes */
 enum { POET_F32 = 0, POET_BF16 = 1 };              /* dtypes */
 enum { POET_SIDE_R = 0, POET_SIDE_P = 1 };         /* side ids used by the FS index sampler */
-enum { POET_OP_BUILD = 0, POET_OP_FWD = 1, POET_OP_BWD = 2, POET_OP_MERGE = 3 };
+enum { POET_OP_BUILD = 0, POET_OP_FWD = 1, POET_OP_BWD = 2, POET_OP_MERGE = 3, POET_OP_FWD_ACT = 4, POET_OP_BWD_ACT = 5 };
 
 /* Maximum supported Neumann terms and primitive size (a primitive must fit the kernels' tiling). */
 #define POET_MAX_K 16
@@ -97,7 +97,7 @@ size_t poet_prim_len(const poet_side* s);
 /* Elements (of the side's dtype) of the saved powers Q^1..Q^k: k * num_prims * bp * ldp, where the row pitch ldp
  * is bp for float32 sides and bp rounded up to a multiple of 8 for bf16 sides (0 when k == 0). */
 size_t poet_powers_len(const poet_side* s);
-/* Workspace bytes a layer op needs (POET_OP_FWD, _BWD or _MERGE; POET_OP_BUILD gives 0, see
+/* Workspace bytes a layer op needs (POET_OP_FWD, _BWD, _MERGE, _FWD_ACT or _BWD_ACT; POET_OP_BUILD gives 0, see
  * poet_build_workspace_bytes). For POET_OP_FWD the figure assumes W_out == NULL, and for POET_OP_BWD that
  * W == NULL (upper bounds). */
 size_t poet_workspace_bytes(const poet_layer* L, int op);
@@ -154,6 +154,32 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
                             const void* powersR, const void* powersP, const int32_t* idxR,
                             const int32_t* idxP, const void* W, const void* X, const void* dY, void* dX,
                             float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- activation-side application ---------------------------------------------------------------------
+ * The same layer with the factors applied to the activations around the W0 GEMM (W is never formed); the
+ * products of the weight-side calls above, associated the other way (W = R W0 P from the method summary):
+ *   forward   X' = X P^T,  Z = X' W0^T,  Y = Z R^T
+ *   backward  dZ = dY R,  dX' = dZ W0,  dX = dX' P,  dL/dR = blocks of dY^T Z,  dL/dP = blocks of dX'^T X,
+ *             then the Neumann adjoint and skew projection as in poet_linear_bwd.
+ * Both sides POET-BS and bf16 activations (poet_act_path_supported); every product is a bf16 GEMM with float32
+ * accumulation and the primitives enter as bf16 copies. W0b is W0 in bf16 (row pitch ldw), made once by
+ * poet_weight_shadow and kept current by passing it as poet_merge's W0_shadow. Workspaces: POET_OP_FWD_ACT and
+ * POET_OP_BWD_ACT of poet_workspace_bytes. */
+int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below apply to L, else 0 */
+
+/* W0_shadow [m x ldw] act dtype out: W0 rounded to the act dtype (round to nearest even). */
+poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream);
+
+/* X [T x ldx] in, Y [T x ldy] out, Z [T x ldy] out: X P^T W0^T, kept for the backward (all bf16). */
+poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream);
+
+/* X [T x ldx], Z [T x ldy] (from the forward), dY [T x ldy] in; dX [T x ldx] out, nullable; dthetaR, dthetaP
+ * float32 out (overwritten). powersR/powersP as in poet_linear_bwd. */
+poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* powersR, const void* powersP, const void* X, const void* Z,
+                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Merge-then-reinitialize (Approach section; period 400 in the "Measured effects" table):
  *   W0 <- R W0 P in float32 (in place), using the same truncated primitives the forward pass uses;

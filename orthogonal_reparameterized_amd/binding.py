@@ -19,13 +19,14 @@ POET_OK, POET_E_ARG, POET_E_SHAPE, POET_E_DTYPE, POET_E_WORKSPACE, POET_E_HIP, P
 POET_BS, POET_FS = 0, 1
 POET_F32, POET_BF16 = 0, 1
 POET_SIDE_R, POET_SIDE_P = 0, 1
-POET_OP_BUILD, POET_OP_FWD, POET_OP_BWD, POET_OP_MERGE = range(4)
+POET_OP_BUILD, POET_OP_FWD, POET_OP_BWD, POET_OP_MERGE, POET_OP_FWD_ACT, POET_OP_BWD_ACT = range(6)
 POET_MAX_K, POET_MAX_PRIM = 16, 8192
 
 EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len", "poet_workspace_bytes",
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
-           "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm")
+           "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
+           "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE = range(9)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
@@ -90,7 +91,12 @@ def lib() -> ctypes.CDLL:
     L.poet_linear_fwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_merge.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, U64, U32, U32, VP, S, VP]
-    for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge"):
+    L.poet_act_path_supported.argtypes = [P(poet_layer)]
+    L.poet_weight_shadow.argtypes = [P(poet_layer), VP, VP, VP]
+    L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge",
+               "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act"):
         getattr(L, nm).restype = ctypes.c_int
     L.poet_status_string.argtypes = [ctypes.c_int]
     L.poet_status_string.restype = ctypes.c_char_p
@@ -302,6 +308,48 @@ def poet_linear_bwd(L: poet_layer, W0, primR, primP, powersR, powersP, idxR, idx
         _ptr(ws, "ws", need if W is None else 0, allow_none=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_linear_bwd")
+
+
+def poet_act_path_supported(L: poet_layer) -> bool:
+    return bool(lib().poet_act_path_supported(ctypes.byref(L)))
+
+
+def poet_weight_shadow(L: poet_layer, W0, W0_shadow, stream=None):
+    b = _layer_bytes(L)
+    st = lib().poet_weight_shadow(ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+                                  _ptr(W0_shadow, "W0_shadow", b["W"], _dt_name(L.act_dtype)), _stream(stream))
+    _check(st, "poet_weight_shadow")
+
+
+def poet_linear_fwd_act(L: poet_layer, W0b, primR, primP, X, Y, Z, ws=None, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_FWD_ACT)
+    st = lib().poet_linear_fwd_act(
+        ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Y, "Y", b["Y"], act, allow_none=L.T == 0),
+        _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0), _ptr(ws, "ws", need, allow_none=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_fwd_act")
+
+
+def poet_linear_bwd_act(L: poet_layer, W0b, primR, primP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP,
+                        ws=None, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_BWD_ACT)
+    st = lib().poet_linear_bwd_act(
+        ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(powersR, "powersR", poet_powers_len(L.R) * _esz(L.R.dtype), _dt_name(L.R.dtype), allow_none=True),
+        _ptr(powersP, "powersP", poet_powers_len(L.P) * _esz(L.P.dtype), _dt_name(L.P.dtype), allow_none=True),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0), _ptr(dX, "dX", b["X"], act, allow_none=True),
+        _ptr(dthetaR, "dthetaR", 4 * poet_theta_len(L.R), "float32"),
+        _ptr(dthetaP, "dthetaP", 4 * poet_theta_len(L.P), "float32"),
+        _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd_act")
 
 
 def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR, idxP, seed: int, linear_id: int,

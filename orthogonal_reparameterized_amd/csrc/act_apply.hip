@@ -1,0 +1,287 @@
+// Block-diagonal factor applied to bf16 activations (POET reparameterization W = R W0 P with the factors moved
+// onto the activations: X P^T, Z R^T, dY R, dX' P):
+//   out[t, block] = in[t, block] F_block^T   (trans)   or   in[t, block] F_block,
+// for every block of the factor (size c = min(bp, d - b bp), bp <= 256) and every token t. F is the float32
+// primitive, rounded to bf16 as the MFMA operand (k_act_operand writes it as bf16 rows); accumulation is float32
+// and the output is rounded to bf16.
+//
+// Weight-stationary: a workgroup owns one block and a run of 32-token tiles. Its 4 waves each hold 64 output
+// columns of the block's operand (all of K, 16 k-steps x 2 column tiles of bf16x8 fragments: 128 registers),
+// loaded and rounded once. The 32 x 256 activation tiles stream through a four-stage LDS ring by DMA
+// (global_load_lds), three tiles' copies in flight while the current one is multiplied
+// (v_mfma_f32_32x32x16_bf16, 32 tokens x 64 columns per wave per tile); the finished tile goes back through the
+// stage it was read from and leaves as coalesced 16-byte row chunks. Rows past the last token are read from the
+// last token (finite values, never stored); columns of a block narrower than the k-steps cover are zeroed in LDS
+// after the copy lands (row padding may hold any bits, NaN included).
+#include <algorithm>
+
+#include "poet.h"
+#include "strip_mma.h"
+
+namespace poet {
+namespace {
+
+using namespace strip;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+constexpr int AT = 256;             // threads (4 waves)
+constexpr int TM = 32;              // tokens per tile
+constexpr int TILE_BYTES = TM * ROWB;  // 16 KB
+constexpr int NST = 4;                 // ring stages: copies run up to NST - 1 tiles ahead
+constexpr int WAIT_VM0 = 0x0F70;
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor word 3
+constexpr uint32_t OOB = 0x80000000u;    // an offset past the end of the output buffer (under 2 GB)
+// s_waitcnt immediate for vmcnt(n), lgkmcnt and expcnt left free (gfx9 encoding: vmcnt bits 3:0 and 15:14)
+constexpr int vm_wait(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+
+struct ActArgs {
+  const __bf16* in; int64_t ldi;
+  __bf16* out; int64_t ldo;
+  const __bf16* Bt; // nblk bp x bp blocks of bf16 operand rows: Bt[j][k] = B(k, j)
+  int T, d, bp, nblk;
+  int tiles_per_wg; // token tiles per workgroup
+  int ngrp;         // token groups: ceil(ceil(T / TM) / tiles_per_wg)
+};
+
+// Operand rows for the kernel below: Bt[b][j][k] = bf16(B(k, j)) with B(k, j) = F_b[j][k] (trans) or F_b[k][j],
+// for j, k < c (the block's size) and zero elsewhere in the bp x bp block. Consecutive threads take consecutive
+// k (trans: coalesced reads) or consecutive j (no trans: the strided side is the read of F, coalesced in j).
+__global__ void k_act_operand(const float* __restrict__ F, int bp, int d, int nblk, int trans, __bf16* __restrict__ Bt) {
+  const int64_t per = (int64_t)bp * bp, total = per * nblk;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(e / per);
+    const int rem = (int)(e % per);
+    const int c = min(bp, d - b * bp);
+    int j, k;
+    if (trans) { j = rem / bp; k = rem % bp; } else { k = rem / bp; j = rem % bp; }
+    const bool in = j < c && k < c;
+    const float f = F[(int64_t)b * per + (in ? (trans ? (int64_t)j * bp + k : (int64_t)k * bp + j) : 0)];
+    Bt[(int64_t)b * per + (int64_t)j * bp + k] = (__bf16)(in ? f : 0.f);
+  }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its global ones (a
+// __syncthreads() also drains every copy and store in flight, which would serialize the next tile's DMA with the
+// current tile's MFMAs). The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// NK: k-steps of 16 covering the block size (4, 8 or 16); every loop over them is unrolled without conditions
+template <int NK>
+__global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
+  __shared__ __attribute__((aligned(16))) char ring[NST * TILE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = a.nblk * a.ngrp;
+  // XCD-aware order: hardware workgroup b runs on XCD b % 8 and takes logical id (b % 8) per + b / 8
+  const int per = (nb + 7) / 8;
+  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (L >= nb) return;
+  // logical id = (token group, block) with the block fastest: the workgroups running together on an XCD cover
+  // whole rows of the same tokens (DRAM pages are read whole), and all blocks' operands fit in its L2
+  const int blk = L % a.nblk, grp = L / a.nblk;
+  const int b0 = blk * a.bp, c = min(a.bp, a.d - b0);
+  const int ntile = (a.T + TM - 1) / TM;
+  const int tile0 = grp * a.tiles_per_wg, tile1 = min(ntile, tile0 + a.tiles_per_wg);
+  const int kh = (lane >> 5) * 8, j32 = lane & 31;
+
+  // ---- DMA of token tile `tile` into ring stage `st`: instruction q (of 4) of wave w fills LDS bytes (4q + w) KB
+  // + 16 lane, i.e. row 8q + h (h = 2w + lane / 32), physical chunk lane % 32, logical chunk (lane % 32) ^ (row % 16)
+  const int h = wave * 2 + (lane >> 5);
+  // chunks past the block's columns read its last whole chunk instead (finite activations, which meet a zero
+  // operand); a partial last chunk is read as it is and its tail cleared in LDS
+  const int last_chunk = (c - 1) >> 3, fill_chunk = max((c >> 3) - 1, 0);
+  int lch[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int lc = j32 ^ (8 * e + h);
+    lch[e] = lc <= last_chunk ? lc : fill_chunk;
+  }
+  const char* inb = reinterpret_cast<const char*>(a.in) + (int64_t)b0 * 2;  // uniform base; 32-bit offsets below
+  auto dma = [&](int tile, int st) {
+#pragma unroll
+    for (int q = 0; q < TM / 8; ++q) {
+      const uint32_t row = (uint32_t)min(tile * TM + 8 * q + h, a.T - 1);
+      const uint32_t off = row * (uint32_t)a.ldi * 2u + 16u * (uint32_t)lch[q & 1];
+      __builtin_amdgcn_global_load_lds((gbl_void*)(inb + off), (lds_void*)(ring + st * TILE_BYTES + (q * 4 + wave) * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // columns of a staged tile to clear: the tail [c, 8 ceil(c / 8)) of a partial last chunk; for a block narrower
+  // than one chunk, everything from c on (its only chunk is partial, and every copy reads it)
+  const int z0 = c, z1 = c < 8 ? 16 * NK : (c + 7) & ~7;
+  const bool ragged = z1 > z0;
+  auto zero_tail = [&](int st) {
+    char* base = ring + st * TILE_BYTES;
+    const int w = z1 - z0;  // columns to clear per row
+    for (int e = tid; e < TM * w; e += AT) {
+      const int row = e / w, k = z0 + e % w;
+      sts(base, row, k, (__bf16)0.f);
+    }
+  };
+
+  // the first NST - 1 tiles' copies run while the operand is loaded
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (tile0 + i < tile1) dma(tile0 + i, i);
+
+  // ---- resident operand: B(k, j) for this wave's columns j = 64 wave + 32 u + j32 and k = 16 ks + kh + v, from the
+  // bf16 rows Bt[j][k] = B(k, j) (one 16-byte load per fragment). Bt is zero outside the block's c x c corner and
+  // the fragments are zero for k >= bp, so B vanishes for every k >= c.
+  const __bf16* Bt = a.Bt + (int64_t)blk * a.bp * a.bp;
+  bf16x8 bfr[2][NK];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = min(wave * 64 + u * 32 + j32, a.bp - 1);  // columns past bp: never stored, any finite value
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      // k past bp: zero (the staged activations there hold copies of a real chunk, not zeros)
+      const int k = ks * 16 + kh;
+      const bf16x8 f = *reinterpret_cast<const bf16x8*>(Bt + (int64_t)j * a.bp + min(k, a.bp - 8));
+      bfr[u][ks] = k < a.bp ? f : bf16x8{};
+    }
+  }
+
+  // output through a raw buffer resource: every thread issues the same number of stores per tile (positions
+  // outside the matrix go to an offset past the buffer's end, which the hardware drops), so the wait at the top of
+  // the next tile can leave exactly those stores in flight and wait only for the copy issued before them
+  const __amdgpu_buffer_rsrc_t Ob =
+      __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)((uint32_t)a.T * (uint32_t)a.ldo * 2u), RSRC_WORD3);
+  const bool whole = (c & 7) == 0;  // every 16-byte chunk of the block is whole: one 16-byte store per chunk
+  // Each thread issues, per tile, its copy of tile + NST - 1 (TM/8 instructions) and then its stores of the tile
+  // (SQ per tile: one 16-byte store per row chunk, plus seven 2-byte stores for a partial last chunk). The copy of
+  // tile t was issued three iterations earlier (or before the loop, then complete at the first wait), followed by
+  // the stores of t-3, t-2, t-1 and the copies of t+1, t+2 where those exist: waiting until at most that many are
+  // outstanding retires exactly the copy of t. With a partial chunk that count exceeds what the counter can hold;
+  // the wait then leaves the last tile's stores and one copy outstanding (retiring the copy of t+1 early as well).
+  constexpr int SQ = TM / 8, SQP = 8 * (TM / 8), CP = TM / 8;
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int st = (tile - tile0) % NST;
+    const int later = (tile + 1 < tile1) + (tile + 2 < tile1);  // copies issued after this tile's
+    if (tile == tile0) {
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    } else if (whole) {
+      if (later == 2) __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQ + 2 * CP));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQ + CP));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQ));
+    } else {
+      if (tile + 2 < tile1) __builtin_amdgcn_s_waitcnt(vm_wait(SQP + CP));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(SQP));
+    }
+    lds_barrier();  // the tile's copy has landed everywhere; every wave is done with the previous tile's stage
+    if (tile + NST - 1 < tile1) dma(tile + NST - 1, (st + NST - 1) % NST);
+    if (ragged) {
+      zero_tail(st);
+      lds_barrier();
+    }
+    const char* A = ring + st * TILE_BYTES;
+    // fragment address of k-step ks: row (r * 32 + j32), chunk (2 ks + lane / 32) ^ (j32 & 15); the swizzle key passes
+    // through an empty asm statement so that the 16 per-step addresses are recomputed (one XOR each), not kept live
+    uint32_t xkey = (uint32_t)(j32 & 15);
+    asm volatile("" : "+v"(xkey));
+    const uint32_t hb = (uint32_t)(lane >> 5);
+    auto frag_at = [&](int r, int ks) {
+      const uint32_t o = (uint32_t)(r * 32 + j32) * ROWB + ((((uint32_t)(2 * ks) | hb) ^ xkey) << 4);
+      return *reinterpret_cast<const bf16x8*>(A + o);
+    };
+    bf16x4 outv[2][4];  // [u][i / 4]: four consecutive tokens of one column, rounded to bf16
+    {
+      f32x16 acc[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+      // k-steps pipelined by hand: the fragment of step ks + 1 is read while step ks multiplies, and a scheduling
+      // barrier per step keeps the compiler from hoisting every read (and its registers) to the top
+      bf16x8 af[2];
+      af[0] = frag_at(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 1 < NK) af[(ks + 1) & 1] = frag_at(0, ks + 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1], bfr[u][ks], acc[u], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) outv[u][q][e] = (__bf16)acc[u][q * 4 + e];
+    }
+    // the output tile leaves through LDS: every wave is done reading stage st, which then holds the tile as rows of
+    // 512 B (the same swizzled layout), read back as 16-byte row chunks and stored coalesced
+    lds_barrier();
+    char* O = ring + st * TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // token 8q + 4 (lane / 32) + e, column 64 wave + 32 u + j32
+          sts(O, q * 8 + (lane >> 5) * 4 + e, wave * 64 + u * 32 + j32, outv[u][q][e]);
+    lds_barrier();
+    {
+#pragma unroll
+      for (int q = 0; q < TM / 8; ++q) {  // chunk lane % 32 of row 8 q + h
+        const int row = 8 * q + h, t = tile * TM + row;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(O + row * ROWB + ((j32 ^ (row & 15)) << 4));
+        const int col = 8 * j32;  // first column of the chunk (logical chunk j32)
+        const uint32_t o = ((uint32_t)t * (uint32_t)a.ldo + (uint32_t)(b0 + col)) * 2u;
+        // whole chunks: one 16-byte store; a partial last chunk: its elements one by one (seven at most)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), Ob, t < a.T && col + 8 <= c ? o : OOB, 0, 0);
+        if (!whole) {
+          // element e is the low (e even) or high half of 32-bit word e / 2, extracted with integer shifts (a
+          // direct element extraction from the bf16 vector fed to the 16-bit store lost the high halves)
+          const bool part = t < a.T && col < c && col + 8 > c;
+          const u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+          for (int e = 0; e < 7; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), Ob,
+                                                  part && col + e < c ? o + 2u * e : OOB, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool act_apply_eligible(int bp, const void* in, int64_t ldi, const void* out, int64_t ldo, int T) {
+  auto al = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  return bp >= 8 && bp <= MAXB && bp % 8 == 0 && ldi % 8 == 0 && ldo % 8 == 0 && al(in) && al(out) &&
+         (double)T * ldi * 2 < 4294967296.0 &&  // 32-bit byte offsets into the input
+         (double)T * ldo * 2 < 2147483648.0;    // the output buffer under 2 GB
+}
+
+hipError_t launch_act_operand(const float* F, int bp, int d, int nblk, bool trans, __bf16* Bt, hipStream_t st) {
+  const int64_t total = (int64_t)nblk * bp * bp;
+  if (total == 0) return hipSuccess;
+  ProfScope prof(POET_K_MISC, st, 0.0, 6.0 * total);
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, 2048);
+  hipLaunchKernelGGL(k_act_operand, dim3(grid), dim3(256), 0, st, F, bp, d, nblk, trans ? 1 : 0, Bt);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_apply(const __bf16* in, int64_t ldi, __bf16* out, int64_t ldo, const __bf16* Bt, int T, int d,
+                            int bp, int nblk, hipStream_t st) {
+  if (T <= 0 || nblk <= 0) return hipSuccess;
+  ActArgs a;
+  a.in = in; a.ldi = ldi; a.out = out; a.ldo = ldo; a.Bt = Bt; a.T = T; a.d = d; a.bp = bp; a.nblk = nblk;
+  // token tiles per workgroup: about two workgroups per CU over the whole launch, at least two tiles each (so that
+  // the operand load is shared by some tiles)
+  const int ntile = (T + TM - 1) / TM;
+  const int want = std::max(1, 512 / nblk);
+  a.tiles_per_wg = std::max(2, (ntile + want - 1) / want);
+  a.ngrp = (ntile + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  const int64_t nb = (int64_t)nblk * a.ngrp;
+  ProfScope prof(POET_K_APPLY, st, 2.0 * T * (double)bp * d, 4.0 * T * (double)d);
+  const unsigned grid = (unsigned)((nb + 7) / 8 * 8);
+  if (bp <= 64) hipLaunchKernelGGL((act_apply_kernel<4>), dim3(grid), dim3(AT), 0, st, a);
+  else if (bp <= 128) hipLaunchKernelGGL((act_apply_kernel<8>), dim3(grid), dim3(AT), 0, st, a);
+  else hipLaunchKernelGGL((act_apply_kernel<16>), dim3(grid), dim3(AT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace poet

@@ -90,6 +90,15 @@ size_t bs_merge_split_bytes(int bp, int nblk);
 hipError_t launch_bs_merge_pass(float* W, int64_t ld, int m, int n, int rside, int bp, int nblk, const float* prim,
                                 char* split, void* shadow, int sh_dt, int64_t ld_sh, hipStream_t st);
 
+// Block-diagonal factor applied to bf16 activations (act_apply.hip): out[t, block] = in[t, block] B_block for T
+// tokens of dimension d, blocks bp <= 256 (a multiple of 8), with the operand B = F^T (trans) or F given as bf16
+// rows Bt[j][k] = B(k, j) by launch_act_operand from the nblk float32 bp x bp primitives F. Row pitches ldi, ldo
+// multiples of 8, in and out 16-byte aligned, the input under 4 GB.
+bool act_apply_eligible(int bp, const void* in, int64_t ldi, const void* out, int64_t ldo, int T);
+hipError_t launch_act_operand(const float* F, int bp, int d, int nblk, bool trans, __bf16* Bt, hipStream_t st);
+hipError_t launch_act_apply(const __bf16* in, int64_t ldi, __bf16* out, int64_t ldo, const __bf16* Bt, int T, int d,
+                            int bp, int nblk, hipStream_t st);
+
 // launch profiler (profiler.hip): no-ops unless poet_profile_enable(1) was called
 int prof_begin(int kclass, hipStream_t st, double flops, double bytes);
 void prof_end(int rec, hipStream_t st);

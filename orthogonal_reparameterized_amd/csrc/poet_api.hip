@@ -423,6 +423,97 @@ size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void*
   return a.used();
 }
 
+// ------------------------------------------------------------------------------------------------------------
+// Activation-side application (both sides POET-BS, bf16 activations). The factors act on the activations around
+// the W0 GEMM and W is never formed:
+//   forward   X' = X P^T,  Z = X' W0^T,  Y = Z R^T
+//   backward  dZ = dY R,  dX' = dZ W0,  dX = dX' P;  dL/dR = blocks of dY^T Z,  dL/dP = blocks of dX'^T X
+// (the same products as the weight-side path, associated the other way: G W0P^T = dY^T X P^T W0^T = dY^T Z).
+// Every product is a bf16 GEMM with float32 accumulation; the factors enter as bf16 copies of the primitives.
+// ------------------------------------------------------------------------------------------------------------
+bool act_path_ok(const poet_layer& L, const SideInfo& R, const SideInfo& P) {
+  return L.act_dtype == BF16 && R.mode == POET_BS && P.mode == POET_BS;
+}
+
+struct ActFwdPlan {
+  __bf16 *Xp = nullptr, *Rb = nullptr, *Pb = nullptr;
+};
+size_t plan_fwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, ActFwdPlan* p) {
+  Arena a(ws);
+  p->Xp = a.take<__bf16>((size_t)L.T * L.ldx);
+  p->Rb = a.take<__bf16>(R.prim_len);
+  p->Pb = a.take<__bf16>(P.prim_len);
+  return a.used();
+}
+
+struct ActBwdPlan {
+  __bf16 *dZ = nullptr, *dXp = nullptr, *Rb = nullptr, *Pb = nullptr;
+  float *dRg = nullptr, *dPg = nullptr;
+  AdjBufs adj;
+};
+size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, ActBwdPlan* p) {
+  Arena a(ws);
+  p->dZ = a.take<__bf16>((size_t)L.T * L.ldy);
+  p->dXp = a.take<__bf16>((size_t)L.T * L.ldx);
+  p->Rb = a.take<__bf16>(R.prim_len);
+  p->Pb = a.take<__bf16>(P.prim_len);
+  p->dRg = a.take<float>(R.prim_len);
+  p->dPg = a.take<float>(P.prim_len);
+  p->adj.dQ = a.take<float>(std::max(R.prim_len, P.prim_len));
+  p->adj.H = a.take_bytes(std::max(adj_h_elems(R) * dtype_size(R.dtype), adj_h_elems(P) * dtype_size(P.dtype)));
+  p->adj.Cs = a.take_bytes(std::max(adj_c_elems(R) * dtype_size(R.dtype), adj_c_elems(P) * dtype_size(P.dtype)));
+  // split-K partial sums of the token-axis contractions (up to 16 splits) and of the adjoint products
+  p->adj.part_elems = 16 * std::max(R.prim_len, P.prim_len);
+  p->adj.part = a.take<float>(p->adj.part_elems);
+  return a.used();
+}
+
+// out[:, block] = in[:, block] F_block^T (trans) or in[:, block] F_block, over the blocks of side S (T rows)
+GemmDesc act_apply(const SideInfo& S, int T, const void* in, int64_t ldi, const __bf16* Fb, bool trans, void* out,
+                   int64_t ldo) {
+  GemmDesc g;
+  g.kclass = POET_K_APPLY;
+  g.compute = BF16;
+  g.M = T; g.N = S.bp; g.K = S.bp; g.Ntot = g.Ktot = S.d; g.batch = S.nprim;
+  g.A = in; g.lda = ldi; g.sA = S.bp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = Fb; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_dt = BF16; g.b_kmajor = trans ? 1 : 0;
+  g.C = out; g.ldc = ldo; g.sC = S.bp; g.c_dt = BF16;
+  return g;
+}
+
+// diagonal blocks of A^T B over the T tokens: dF_block = A[:, block]^T B[:, block], float32 bp x bp blocks
+GemmDesc act_contract(const SideInfo& S, int T, const void* A, int64_t lda, const void* B, int64_t ldb, float* dF,
+                      const AdjBufs& adj) {
+  GemmDesc g;
+  g.kclass = POET_K_CONTRACT;
+  g.compute = BF16;
+  g.M = g.N = S.bp; g.K = T; g.Mtot = g.Ntot = S.d; g.batch = S.nprim;
+  g.A = A; g.lda = lda; g.sA = S.bp; g.a_dt = BF16; g.a_kmajor = 0;
+  g.B = B; g.ldb = ldb; g.sB = S.bp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.C = dF; g.ldc = S.bp; g.sC = (int64_t)S.bp * S.bp; g.c_dt = F32;
+  g.part = adj.part; g.part_elems = adj.part_elems;
+  return g;
+}
+
+// bf16 copies of a side's primitives (the full factor, identity included)
+hipError_t prims_bf16(const SideInfo& S, const float* prim, __bf16* out, hipStream_t st) {
+  return launch_convert(prim, S.bp, out, S.bp, BF16, S.nprim * S.bp, S.bp, st);
+}
+
+// out = in F^T (trans) or in F over the blocks of side S: the weight-stationary kernel where it applies (its bf16
+// operand rows written to Fb first), else a batched GEMM on a bf16 copy of the primitives (in Fb)
+hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, const float* prim, __bf16* Fb, bool trans,
+                      void* out, int64_t ldo, hipStream_t st) {
+  hipError_t e;
+  if (act_apply_eligible(S.bp, in, ldi, out, ldo, T)) {
+    if ((e = launch_act_operand(prim, S.bp, S.d, S.nprim, trans, Fb, st)) != hipSuccess) return e;
+    return launch_act_apply(reinterpret_cast<const __bf16*>(in), ldi, reinterpret_cast<__bf16*>(out), ldo, Fb, T,
+                            S.d, S.bp, S.nprim, st);
+  }
+  if ((e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
+  return launch_gemm(act_apply(S, T, in, ldi, Fb, trans, out, ldo), st);
+}
+
 struct MergePlan {
   bool inplace = false;   // both sides block-diagonal with blocks <= 256: two in-place passes over W0
   char* split = nullptr;  // their pre-split factor deltas
@@ -505,6 +596,8 @@ size_t poet_workspace_bytes(const poet_layer* L, int op) {
     case POET_OP_FWD: { FwdPlan p; return plan_fwd(*L, R, P, nullptr, true, &p); }
     case POET_OP_BWD: { BwdPlan p; return plan_bwd(*L, R, P, nullptr, true, &p); }
     case POET_OP_MERGE: { MergePlan p; return plan_merge(*L, R, P, nullptr, &p); }
+    case POET_OP_FWD_ACT: { ActFwdPlan p; return plan_fwd_act(*L, R, P, nullptr, &p); }
+    case POET_OP_BWD_ACT: { ActBwdPlan p; return plan_bwd_act(*L, R, P, nullptr, &p); }
     default: fail(POET_E_ARG, "bad op %d", op); return 0;
   }
 }
@@ -743,6 +836,88 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     }
     HIP_TRY(contract_and_adjoint(P, g, p.dPg, powersP, dthetaP, p.adj, st));
   }
+  return POET_OK;
+}
+
+int poet_act_path_supported(const poet_layer* L) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return 0;
+  return act_path_ok(*L, R, P) ? 1 : 0;
+}
+
+poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!W0 || !W0_shadow) return fail(POET_E_ARG, "null W0 or shadow");
+  HIP_TRY(launch_convert(W0, L->ldw, W0_shadow, L->ldw, L->act_dtype, L->m, L->n,
+                         reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
+poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
+  if (!W0b || !primR || !primP) return fail(POET_E_ARG, "null W0 shadow or primitive");
+  if (L->T > 0 && (!X || !Y || !Z)) return fail(POET_E_ARG, "null X, Y or Z");
+  ActFwdPlan p;
+  if (!check_ws(ws, ws_bytes, plan_fwd_act(*L, R, P, nullptr, &p))) return g_last;
+  plan_fwd_act(*L, R, P, ws, &p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (L->T == 0) return POET_OK;
+  const int T = L->T;
+  HIP_TRY(act_factor(P, T, X, L->ldx, primP, p.Pb, true, p.Xp, L->ldx, st));  // X' = X P^T
+  {  // Z = X' W0^T
+    GemmDesc g;
+    g.kclass = POET_K_TOKEN_FWD;
+    g.compute = BF16; g.M = T; g.N = L->m; g.K = L->n;
+    g.A = p.Xp; g.lda = L->ldx; g.a_dt = BF16; g.a_kmajor = 1;
+    g.B = W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 1;
+    g.C = Z; g.ldc = L->ldy; g.c_dt = BF16;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  HIP_TRY(act_factor(R, T, Z, L->ldy, primR, p.Rb, true, Y, L->ldy, st));  // Y = Z R^T
+  return POET_OK;
+}
+
+poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* powersR, const void* powersP, const void* X, const void* Z,
+                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes,
+                                void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
+  if (!W0b || !primR || !primP) return fail(POET_E_ARG, "null W0 shadow or primitive");
+  if (L->T > 0 && (!X || !Z || !dY)) return fail(POET_E_ARG, "null X, Z or dY");
+  if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
+  if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
+    return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  ActBwdPlan p;
+  if (!check_ws(ws, ws_bytes, plan_bwd_act(*L, R, P, nullptr, &p))) return g_last;
+  plan_bwd_act(*L, R, P, ws, &p);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int T = L->T;
+  if (T > 0) {
+    HIP_TRY(act_factor(R, T, dY, L->ldy, primR, p.Rb, false, p.dZ, L->ldy, st));  // dZ = dY R
+    {  // dX' = dZ W0
+      GemmDesc g;
+      g.kclass = POET_K_TOKEN_DX;
+      g.compute = BF16; g.M = T; g.N = L->n; g.K = L->m;
+      g.A = p.dZ; g.lda = L->ldy; g.a_dt = BF16; g.a_kmajor = 1;
+      g.B = W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 0;
+      g.C = p.dXp; g.ldc = L->ldx; g.c_dt = BF16;
+      HIP_TRY(launch_gemm(g, st));
+    }
+    if (dX) HIP_TRY(act_factor(P, T, p.dXp, L->ldx, primP, p.Pb, false, dX, L->ldx, st));  // dX = dX' P
+  }
+  // primitive blocks of dL/dR = dY^T Z and dL/dP = dX'^T X (zero when T == 0), then the adjoint
+  if (R.theta_len > 0)
+    HIP_TRY(contract_and_adjoint(R, act_contract(R, T, dY, L->ldy, Z, L->ldy, p.dRg, p.adj), p.dRg, powersR,
+                                 dthetaR, p.adj, st));
+  if (P.theta_len > 0)
+    HIP_TRY(contract_and_adjoint(P, act_contract(P, T, p.dXp, L->ldx, X, L->ldx, p.dPg, p.adj), p.dPg, powersP,
+                                 dthetaP, p.adj, st));
   return POET_OK;
 }
 

@@ -27,14 +27,25 @@ class PoetLinear:
     R, P are ``poet_side`` structs; W0 is an (m, n) float32 host array (numpy or torch). ``ldw`` pads W0's rows
     (a multiple of 64 elements keeps every row 128-byte aligned). Index sets of FS sides are drawn on the GPU
     with ``poet_sample_indices`` for epoch 0 unless given.
+
+    ``path`` picks how the factors are applied: "weight" materializes W = R W0 P (poet_linear_fwd/_bwd), "act"
+    applies them to the activations around the W0 GEMM (poet_linear_fwd_act/_bwd_act, which keep a bf16 copy
+    of W0 that the merge refreshes), "auto" takes "act" wherever the library supports it.
     """
 
     def __init__(self, m: int, n: int, T: int, R: B.poet_side, P: B.poet_side, act_dtype: int, W0,
                  thetaR=None, thetaP=None, seed: int = 0, linear_id: int = 0, ldw: Optional[int] = None,
-                 ldx: Optional[int] = None, ldy: Optional[int] = None, idxR=None, idxP=None, device: str = "cuda"):
+                 ldx: Optional[int] = None, ldy: Optional[int] = None, idxR=None, idxP=None, device: str = "cuda",
+                 path: str = "weight"):
         torch = _torch()
         self.dev = torch.device(device)
         self.L = B.layer(m, n, T, R, P, act_dtype, ldw, ldx, ldy)
+        if path not in ("weight", "act", "auto"):
+            raise ValueError(f"path must be 'weight', 'act' or 'auto', not {path!r}")
+        supported = B.poet_act_path_supported(self.L)
+        if path == "act" and not supported:
+            raise ValueError("the activation-side path needs POET-BS sides and bf16 activations")
+        self.act_path = path == "act" or (path == "auto" and supported)
         self.m, self.n, self.T = m, n, T
         self.seed, self.linear_id, self.epoch = seed, linear_id, 0
         self.act = _tdt(act_dtype)
@@ -52,10 +63,15 @@ class PoetLinear:
         self.qnormP = torch.empty(B.poet_num_prims(P), dtype=torch.float32, device=self.dev)
         self.dthetaR = torch.empty(max(nR, 1), dtype=torch.float32, device=self.dev)
         self.dthetaP = torch.empty(max(nP, 1), dtype=torch.float32, device=self.dev)
-        wsb = max(B.poet_workspace_bytes(self.L, op) for op in (B.POET_OP_FWD, B.POET_OP_BWD, B.POET_OP_MERGE))
+        ops = (B.POET_OP_FWD_ACT, B.POET_OP_BWD_ACT) if self.act_path else (B.POET_OP_FWD, B.POET_OP_BWD)
+        wsb = max(B.poet_workspace_bytes(self.L, op) for op in ops + (B.POET_OP_MERGE,))
         wsb = max(wsb, B.poet_sample_workspace_bytes(max(m, n)), B.poet_build_workspace_bytes(R, True),
                   B.poet_build_workspace_bytes(P, True))
         self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+        self.W0b = None
+        if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
+            self.W0b = torch.empty((m, self.L.ldw), dtype=self.act, device=self.dev)
+            B.poet_weight_shadow(self.L, self.W0, self.W0b)
         self.idxR = self.idxP = None
         if R.mode == B.POET_FS:
             self.idxR = torch.empty(R.b, dtype=torch.int32, device=self.dev)
@@ -95,7 +111,19 @@ class PoetLinear:
         B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
 
+    def forward_act(self, X, Y, Z, stream=None):
+        """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act."""
+        B.poet_linear_fwd_act(self.L, self.W0b, self.primR, self.primP, X, Y, Z, self.ws, stream)
+
+    def backward_act(self, X, Z, dY, dX, stream=None):
+        B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
+                              dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
+
     def merge(self, shadow=None, stream=None):
+        """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
+        when given, receives the merged W0 in the act dtype as well)."""
         self.epoch += 1
-        B.poet_merge(self.L, self.W0, shadow, self.thetaR, self.thetaP, self.primR, self.primP, self.idxR, self.idxP,
-                     self.seed, self.linear_id, self.epoch, self.ws, stream)
+        B.poet_merge(self.L, self.W0, self.W0b if shadow is None else shadow, self.thetaR, self.thetaP, self.primR,
+                     self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch, self.ws, stream)
+        if shadow is not None and self.W0b is not None:
+            B.poet_weight_shadow(self.L, self.W0, self.W0b, stream)

@@ -153,3 +153,29 @@ def test_build_and_sampler_reject_bad_arguments():
     assert lb.poet_sample_indices(0, 0, 1, 2, 3, 4, FAKE, FAKE, 1 << 20, None) == B.POET_E_SHAPE
     assert lb.poet_sample_indices(100, 10, 1, 2, 3, 4, FAKE, FAKE, 4, None) == B.POET_E_WORKSPACE
     assert lb.poet_sample_indices(100, 10, 1, 2, 3, 4, None, FAKE, 1 << 20, None) == B.POET_E_ARG
+
+
+def test_act_path_rejects_bad_arguments():
+    lb = B.lib()
+    L = _layer(act_dtype=1)
+    assert B.poet_act_path_supported(L)
+    assert not B.poet_act_path_supported(_layer(act_dtype=0))  # float32 activations: weight-side path only
+    Lfs = _layer(act_dtype=1, R=B.side(1, 256, 128, 3, 1))
+    assert not B.poet_act_path_supported(Lfs)
+    wf = B.poet_workspace_bytes(L, B.POET_OP_FWD_ACT)
+    wb = B.poet_workspace_bytes(L, B.POET_OP_BWD_ACT)
+    assert wf > 0 and wb > 0
+    assert lb.poet_linear_fwd_act(ctypes.byref(Lfs), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf,
+                                  None) == B.POET_E_UNSUPPORTED
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wf, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf - 1024,
+                                  None) == B.POET_E_WORKSPACE
+    # saved powers are required for k >= 1; Z is required with tokens
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                  FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
+                                  FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                  FAKE, wb - 1024, None) == B.POET_E_WORKSPACE
+    assert lb.poet_weight_shadow(ctypes.byref(L), None, FAKE, None) == B.POET_E_ARG

@@ -23,7 +23,7 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(cfg_id, name):
+def _run(cfg_id, name, path="weight"):
     wl = PI.WORKLOADS[cfg_id]
     lin = [l for l in wl.linears() if l.name == name][0]
     announce(f"fullsize cfg={wl.name} linear={name} m={lin.m} n={lin.n} T={lin.T}")
@@ -34,13 +34,20 @@ def _run(cfg_id, name):
     from orthogonal_reparameterized_amd.layer import PoetLinear
     pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
                     seed=wl.seed, linear_id=lin.linear_id, ldw=PI.pad_ld(lin.n), ldx=PI.pad_ld(lin.n),
-                    ldy=PI.pad_ld(lin.m), idxR=iR, idxP=iP)
+                    ldy=PI.pad_ld(lin.m), idxR=iR, idxP=iP, path=path)
     del pad
     pl.build()
     Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
-    Y, dX, W = pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx), pl.alloc_W()
-    pl.forward(Xd, Y, W_out=W)
-    pl.backward(Xd, dYd, dX, W=W)
+    Y, dX = pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx)
+    W = None
+    if path == "act":
+        Z = pl.alloc_act(lin.T, pl.L.ldy)
+        pl.forward_act(Xd, Y, Z)
+        pl.backward_act(Xd, Z, dYd, dX)
+    else:
+        W = pl.alloc_W()
+        pl.forward(Xd, Y, W_out=W)
+        pl.backward(Xd, dYd, dX, W=W)
     torch.cuda.synchronize()
 
     sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
@@ -49,7 +56,7 @@ def _run(cfg_id, name):
     Wref = f["W"]
     g = O.linear_bwd(sR, sP, W0, tR, tP, iR, iP, X, dY)
     errs = {
-        "W": rel(to_np(W)[:, :lin.n], Wref),
+        "W": rel(to_np(W)[:, :lin.n], Wref) if W is not None else 0.0,
         "Y_rows": rel(to_np(Y)[rows, :lin.m], f["Y"]),
         "dX_rows": rel(to_np(dX)[rows, :lin.n], g["dX"][rows]),
         "dthetaR": rel(to_np(pl.dthetaR)[:len(tR)], g["dthetaR"]),
@@ -63,6 +70,12 @@ def _run(cfg_id, name):
 @pytest.mark.parametrize("name", ["gate", "down", "q"])
 def test_llama1p3b_bs256_fullsize(name):
     _run(3, name)
+
+
+@pytest.mark.parametrize("name", ["gate", "down"])
+def test_llama1p3b_bs256_fullsize_act_path(name):
+    """The activation-side path, as the benchmark runs it, on the same sampled references."""
+    _run(3, name, path="act")
 
 
 @pytest.mark.parametrize("name", ["up", "o"])
