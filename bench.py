@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4])
     ap.add_argument("--merge-period", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph (the default launches every step)")
     ap.add_argument("--path", default="auto", choices=["auto", "weight", "act"],
                     help="apply R and P to the activations around the W0 GEMM (act), materialize W (weight), or "
                          "the activation side wherever it is supported (auto)")
@@ -139,19 +141,47 @@ def main():
         step(lins)
     torch.cuda.synchronize()
 
-    # timed region: the profiler brackets every launch with events on the launch stream
+    # one step captured into a HIP graph (torch's CUDAGraph over the HIP stream the library launches on): replays
+    # issue the same kernels with the same arguments without the host's per-launch cost
+    graph = None
+    if args.graph:
+        log("capturing one step into a graph")
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step(lins)  # a step on the capture stream first (the library's first launch on a stream)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(lins)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K steps (graph replays, or eager launches) with nothing else on the stream
     log(f"timed {args.steps} steps")
-    B.poet_profile_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        step(lins)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(lins)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    # the same K steps again with the library's launch profiler on (an event pair around every launch, on the
+    # launch stream): per-class kernel times and the dominant kernel's launch duration. The events add gaps
+    # between launches, not kernel time, so this pass is kept out of the timed region above.
+    log(f"profiled {args.steps} steps")
+    B.poet_profile_enable(True)
+    for _ in range(args.steps):
+        step(lins)
+    torch.cuda.synchronize()
     prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
     B.poet_profile_enable(False)
 
@@ -210,7 +240,8 @@ def main():
                      "avg_launch_ms": round(avg_ms, 4), "launches": d["launches"],
                      "flops_per_launch": d["flops"] / max(d["launches"], 1)},
         "ms_fwd_bwd": round(ms_step, 4), "ms_merge_all_linears": round(ms_merge, 4), "merge": merge_info,
-        "host_wall_s": round(wall, 3),
+        "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
+        "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
         "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
         "step_mfu": round(algorithmic_flops(lins) / (ms_total / 1e3) / 1e12 / peak, 4),
         "stage_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
