@@ -224,7 +224,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int per = (ntiles + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (t >= ntiles) return;
-  const int tn = t % ntn, tm = (t / ntn) % ntm, zs = t / (ntn * ntm);
+  // tile order inside one (batch, split): patches of GM row bands x GN column tiles, patch after patch along N,
+  // then the next GM row bands. An XCD's workgroups run a contiguous range of this order together, so they share
+  // the K-slices of a few A row bands and a few B column tiles in its L2 (column-fastest order over a wide N
+  // would stream all of B once per row band)
+  const int zs = t / (ntn * ntm), tl = t % (ntn * ntm);
+  int tm, tn;
+  {
+    constexpr int GM = 4, GN = 8;
+    const int sr = tl / (GM * ntn), rem = tl % (GM * ntn);
+    const int rows = min(GM, ntm - GM * sr);
+    const int ngn = (ntn + GN - 1) / GN;
+    const int gi = min(rem / (rows * GN), ngn - 1);
+    const int r2 = rem - rows * GN * gi;
+    const int w = min(GN, ntn - gi * GN);
+    tm = GM * sr + r2 / w;
+    tn = gi * GN + r2 % w;
+  }
   const int s = zs % splits, z = zs / splits;
   int M = g.M, N = g.N, K = g.K;
   if (g.Mtot > 0) M = min(M, g.Mtot - z * g.M);
