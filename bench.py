@@ -59,6 +59,22 @@ def step(lins):
             pl.backward(e["X"], e["dY"], e["dX"], W=e["keep"])
 
 
+def measured_traffic(tag: str):
+    """HBM bytes per launch of a token-GEMM class from the committed rocprofv3 counter summary of this workload,
+    or None when the summary is missing, is for another kernel class, or was taken on a different version of the
+    GEMM source (its sha256 no longer matches)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "token_gemm_traffic_llama1.3b_bs256.json")
+    try:
+        doc = json.load(open(path))
+        src = open(os.path.join(ROOT, doc["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != doc["source_sha256"]:
+            return None
+        return doc["kernels"][tag]["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def algorithmic_flops(lins):
     """2MNK of the three token GEMMs of every linear (Y, dX and the weight gradient)."""
     return sum(3 * 2.0 * e["spec"].T * e["spec"].m * e["spec"].n for e in lins)
@@ -236,7 +252,8 @@ def main():
                    ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
                    "merge_period": args.merge_period},
         "roofline": {"bound": "mfma", "kernel": f"gemm ({dom})", "achieved": round(achieved, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(dom) if wl.cfg_id == 3 and all(e["pl"].act_path for e in lins) else None,
                      "avg_launch_ms": round(avg_ms, 4), "launches": d["launches"],
                      "flops_per_launch": d["flops"] / max(d["launches"], 1)},
         "ms_fwd_bwd": round(ms_step, 4), "ms_merge_all_linears": round(ms_merge, 4), "merge": merge_info,

@@ -128,6 +128,9 @@ hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d
 hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
                               int d, int bp, int nprim, float* dtheta, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
+// prim[p] (bp x bp) = diagonal sub-block p % g of super-block p / g (g bp x g bp, row pitch sb = g bp) of sup, zero
+// past a ragged last block (dimension d)
+hipError_t launch_extract_diag(const float* sup, int sb, int g, int bp, int d, int nprim, float* prim, hipStream_t st);
 // dst (rows x cols, ld_dst, dtype dst_dt) <- src (float32, ld_src)
 hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows,
                           int cols, hipStream_t st);

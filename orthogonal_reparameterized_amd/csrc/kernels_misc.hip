@@ -403,6 +403,29 @@ hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_strid
   return hipGetLastError();
 }
 
+// Diagonal blocks of super-block products: super-block u (size sb = g bp, row pitch sb) holds the products of
+// blocks u g .. u g + g - 1; block p = u g + i is its diagonal sub-block i, copied to prim[p] (bp x bp; the extent
+// past a ragged last block's size c is zero).
+__global__ void k_extract_diag(const float* __restrict__ sup, int sb, int g, int bp, int d, int nprim,
+                               float* __restrict__ prim) {
+  const int64_t total = (int64_t)nprim * bp * bp;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(e / ((int64_t)bp * bp)), rem = (int)(e % ((int64_t)bp * bp));
+    const int r = rem / bp, c = rem % bp;
+    const int u = p / g, i = p % g;
+    const int cp = min(bp, d - p * bp);
+    prim[e] = (r < cp && c < cp) ? sup[(int64_t)u * sb * sb + (int64_t)(i * bp + r) * sb + i * bp + c] : 0.f;
+  }
+}
+
+hipError_t launch_extract_diag(const float* sup, int sb, int g, int bp, int d, int nprim, float* prim, hipStream_t st) {
+  const size_t n = (size_t)nprim * bp * bp;
+  if (n == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)n * 8);
+  hipLaunchKernelGGL(k_extract_diag, dim3(grid_for(n)), dim3(kThreads), 0, st, sup, sb, g, bp, d, nprim, prim);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st) {
   if (n == 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)n * 4);

@@ -446,9 +446,22 @@ size_t plan_fwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, v
   return a.used();
 }
 
+// Blocks below 128 (the bf16 kernel's smallest tile) are contracted g = floor(256 / bp) at a time: the product of a
+// super-block of g adjacent blocks (size g bp, 129..256) runs on the fast kernel and its g diagonal sub-blocks are
+// kept (the off-diagonal products are extra MFMA work in a pass bound by reading the two token-major operands).
+int super_group(const SideInfo& S) { return S.bp < 128 ? 256 / S.bp : 1; }
+size_t super_elems(const SideInfo& S) {
+  const int g = super_group(S);
+  if (g == 1) return 0;
+  const size_t sb = (size_t)g * S.bp, nsb = (S.nprim + g - 1) / g;
+  return nsb * sb * sb;
+}
+
 struct ActBwdPlan {
   __bf16 *dZ = nullptr, *dXp = nullptr, *Rb = nullptr, *Pb = nullptr;
   float *dRg = nullptr, *dPg = nullptr;
+  float* sup = nullptr;  // super-block products of small blocks
+  size_t sup_elems = 0;
   AdjBufs adj;
 };
 size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, ActBwdPlan* p) {
@@ -459,11 +472,13 @@ size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, v
   p->Pb = a.take<__bf16>(P.prim_len);
   p->dRg = a.take<float>(R.prim_len);
   p->dPg = a.take<float>(P.prim_len);
+  p->sup_elems = std::max(super_elems(R), super_elems(P));
+  p->sup = p->sup_elems ? a.take<float>(p->sup_elems) : nullptr;
   p->adj.dQ = a.take<float>(std::max(R.prim_len, P.prim_len));
   p->adj.H = a.take_bytes(std::max(adj_h_elems(R) * dtype_size(R.dtype), adj_h_elems(P) * dtype_size(P.dtype)));
   p->adj.Cs = a.take_bytes(std::max(adj_c_elems(R) * dtype_size(R.dtype), adj_c_elems(P) * dtype_size(P.dtype)));
   // split-K partial sums of the token-axis contractions (up to 16 splits) and of the adjoint products
-  p->adj.part_elems = 16 * std::max(R.prim_len, P.prim_len);
+  p->adj.part_elems = 16 * std::max({R.prim_len, P.prim_len, p->sup_elems});
   p->adj.part = a.take<float>(p->adj.part_elems);
   return a.used();
 }
@@ -493,6 +508,21 @@ GemmDesc act_contract(const SideInfo& S, int T, const void* A, int64_t lda, cons
   g.C = dF; g.ldc = S.bp; g.sC = (int64_t)S.bp * S.bp; g.c_dt = F32;
   g.part = adj.part; g.part_elems = adj.part_elems;
   return g;
+}
+
+// dF = blocks of A^T B over the tokens, then the adjoint (small blocks through super-block products)
+hipError_t act_contract_adjoint(const SideInfo& S, int T, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                float* dF, const void* powers, float* dtheta, const ActBwdPlan& p, hipStream_t st) {
+  const int g = super_group(S);
+  if (g == 1) return contract_and_adjoint(S, act_contract(S, T, A, lda, B, ldb, dF, p.adj), dF, powers, dtheta, p.adj, st);
+  SideInfo U = S;  // the super-block view: blocks of g bp
+  U.bp = g * S.bp;
+  U.nprim = (S.nprim + g - 1) / g;
+  GemmDesc gd = act_contract(U, T, A, lda, B, ldb, p.sup, p.adj);
+  hipError_t e;
+  if ((e = launch_gemm(gd, st)) != hipSuccess) return e;
+  if ((e = launch_extract_diag(p.sup, U.bp, g, S.bp, S.d, S.nprim, dF, st)) != hipSuccess) return e;
+  return neumann_adjoint(S, dF, powers, dtheta, p.adj, st);
 }
 
 // bf16 copies of a side's primitives (the full factor, identity included)
@@ -912,12 +942,8 @@ poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const floa
     if (dX) HIP_TRY(act_factor(P, T, p.dXp, L->ldx, primP, p.Pb, false, dX, L->ldx, st));  // dX = dX' P
   }
   // primitive blocks of dL/dR = dY^T Z and dL/dP = dX'^T X (zero when T == 0), then the adjoint
-  if (R.theta_len > 0)
-    HIP_TRY(contract_and_adjoint(R, act_contract(R, T, dY, L->ldy, Z, L->ldy, p.dRg, p.adj), p.dRg, powersR,
-                                 dthetaR, p.adj, st));
-  if (P.theta_len > 0)
-    HIP_TRY(contract_and_adjoint(P, act_contract(P, T, p.dXp, L->ldx, X, L->ldx, p.dPg, p.adj), p.dPg, powersP,
-                                 dthetaP, p.adj, st));
+  if (R.theta_len > 0) HIP_TRY(act_contract_adjoint(R, T, dY, L->ldy, Z, L->ldy, p.dRg, powersR, dthetaR, p, st));
+  if (P.theta_len > 0) HIP_TRY(act_contract_adjoint(P, T, p.dXp, L->ldx, X, L->ldx, p.dPg, powersP, dthetaP, p, st));
   return POET_OK;
 }
 
