@@ -47,7 +47,15 @@ def build_block(wl, torch, B, PI, PoetLinear, path="auto"):
     return lins
 
 
-def step(lins):
+def step(lins, group=None):
+    if group is not None:  # the block's per-side steps in shared launches: build, then per linear, then adjoint
+        group.build()
+        for e in lins:
+            pl = e["pl"]
+            pl.forward_act(e["X"], e["Y"], e["keep"])
+            pl.backward_act_prims(e["X"], e["keep"], e["dY"], e["dX"])
+        group.finish_backward()
+        return
     for e in lins:
         pl = e["pl"]
         pl.build()
@@ -130,6 +138,10 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "weight", "act"],
                     help="apply R and P to the activations around the W0 GEMM (act), materialize W (weight), or "
                          "the activation side wherever it is supported (auto)")
+    ap.add_argument("--no-group", action="store_true",
+                    help="build and finish the backward of each linear on its own (the default runs the per-side "
+                         "steps of all linears of the block in shared launches where every linear takes the "
+                         "activation-side path)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -142,19 +154,22 @@ def main():
     import torch
     import poet_inputs as PI
     from orthogonal_reparameterized_amd import binding as B
-    from orthogonal_reparameterized_amd.layer import PoetLinear
+    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
 
     torch.cuda.set_device(0)
     B.lib()
     wl = PI.WORKLOADS[args.workload]
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
+    group = None
+    if not args.no_group and all(e["pl"].act_path for e in lins):
+        group = PoetGroup([e["pl"] for e in lins])
     torch.cuda.synchronize()
     T = wl.T
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step(lins)
+        step(lins, group)
     torch.cuda.synchronize()
 
     # one step captured into a HIP graph (torch's CUDAGraph over the HIP stream the library launches on): replays
@@ -165,12 +180,12 @@ def main():
         s_cap = torch.cuda.Stream()
         s_cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s_cap):
-            step(lins)  # a step on the capture stream first (the library's first launch on a stream)
+            step(lins, group)  # a step on the capture stream first (the library's first launch on a stream)
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(lins)
+            step(lins, group)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -185,7 +200,7 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            step(lins)
+            step(lins, group)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -196,7 +211,7 @@ def main():
     log(f"profiled {args.steps} steps")
     B.poet_profile_enable(True)
     for _ in range(args.steps):
-        step(lins)
+        step(lins, group)
     torch.cuda.synchronize()
     prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
     B.poet_profile_enable(False)
@@ -250,7 +265,7 @@ def main():
                    "block": wl.b, "fraction": wl.frac, "k": wl.k, "linears": len(lins),
                    "factor_application": "activations" if all(e["pl"].act_path for e in lins) else
                    ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
-                   "merge_period": args.merge_period},
+                   "grouped_side_steps": group is not None, "merge_period": args.merge_period},
         "roofline": {"bound": "mfma", "kernel": f"gemm ({dom})", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(dom) if wl.cfg_id == 3 and all(e["pl"].act_path for e in lins) else None,

@@ -181,6 +181,38 @@ poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const floa
                                 const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/* As poet_linear_bwd_act, but it stops at the primitive gradients and leaves the Neumann adjoint to
+ * poet_adjoint_group, so that the adjoints of many linears run together:
+ *   dprimR [poet_prim_len(R)], dprimP [poet_prim_len(P)] float32 out: the bp x bp blocks of dL/dR (blocks of
+ *   dY^T Z) and dL/dP (blocks of dX'^T X); entries outside a ragged last block's extent are zero.
+ * Workspace: POET_OP_BWD_ACT. */
+poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                      const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
+                                      float* dprimP, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- grouped calls ------------------------------------------------------------------------------------
+ * The per-block steps of many sides (for instance both sides of every linear of a transformer block) in shared
+ * launches, so that their blocks fill the GPU together instead of one small grid per side. Each side keeps its
+ * own buffers; the tables are host arrays of count device pointers, entry i belonging to sides[i]. Results are
+ * those of the one-side calls (the adjoint's split-K summation order may differ). */
+
+/* poet_build_orthogonal for count sides (no qnorm). powers[i] is required for every side with k >= 1.
+ * ws: at least poet_build_group_workspace_bytes(count, sides) bytes (may be NULL when that is 0). */
+size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides);
+poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
+                                        float* const* prim, void* const* powers, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/* The Neumann adjoint and skew projection of count sides (the last step of the backward to the skew
+ * parameters, Approach section): dprim[i] float32 in (poet_linear_bwd_act_prims), powers[i] the saved powers
+ * of sides[i] (required when k >= 1), dtheta[i] [poet_theta_len] float32 out (overwritten). Sides with
+ * theta_len 0 are skipped (their pointers may be NULL).
+ * ws: at least poet_adjoint_group_workspace_bytes(count, sides) bytes. */
+size_t poet_adjoint_group_workspace_bytes(int32_t count, const poet_side* sides);
+poet_status poet_adjoint_group(int32_t count, const poet_side* sides, const float* const* dprim,
+                               const void* const* powers, float* const* dtheta, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Merge-then-reinitialize (Approach section; period 400 in the "Measured effects" table):
  *   W0 <- R W0 P in float32 (in place), using the same truncated primitives the forward pass uses;
  *   W0_shadow [m x ldw] act dtype out, nullable: a copy of the merged W0 in the act dtype;

@@ -26,7 +26,9 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
-           "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act")
+           "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
+           "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
+           "poet_adjoint_group_workspace_bytes", "poet_adjoint_group")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE = range(9)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
@@ -95,6 +97,13 @@ def lib() -> ctypes.CDLL:
     L.poet_weight_shadow.argtypes = [P(poet_layer), VP, VP, VP]
     L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_build_group_workspace_bytes.argtypes = [I32, P(poet_side)]
+    L.poet_build_group_workspace_bytes.restype = S
+    L.poet_build_orthogonal_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
+    L.poet_adjoint_group_workspace_bytes.restype = S
+    L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
     for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge",
                "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act"):
         getattr(L, nm).restype = ctypes.c_int
@@ -350,6 +359,85 @@ def poet_linear_bwd_act(L: poet_layer, W0b, primR, primP, powersR, powersP, X, Z
         _ptr(dthetaP, "dthetaP", 4 * poet_theta_len(L.P), "float32"),
         _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_linear_bwd_act")
+
+
+def poet_linear_bwd_act_prims(L: poet_layer, W0b, primR, primP, X, Z, dY, dX, dprimR, dprimP, ws=None, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_BWD_ACT)
+    st = lib().poet_linear_bwd_act_prims(
+        ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0), _ptr(dX, "dX", b["X"], act, allow_none=True),
+        _ptr(dprimR, "dprimR", 4 * poet_prim_len(L.R), "float32"),
+        _ptr(dprimP, "dprimP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd_act_prims")
+
+
+def _side_array(sides):
+    arr = (poet_side * max(1, len(sides)))()
+    for i, s in enumerate(sides):
+        arr[i] = s
+    return arr
+
+
+def _ptr_table(ts, names, sizes, dtypes, allow_none):
+    tab = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        p = _ptr(t, names[i], sizes[i], dtypes[i], allow_none=allow_none[i])
+        tab[i] = None if p is None else p.value
+    return tab
+
+
+def poet_build_group_workspace_bytes(sides) -> int:
+    return int(lib().poet_build_group_workspace_bytes(len(sides), _side_array(sides)))
+
+
+def poet_adjoint_group_workspace_bytes(sides) -> int:
+    return int(lib().poet_adjoint_group_workspace_bytes(len(sides), _side_array(sides)))
+
+
+def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=None):
+    """poet_build_orthogonal for every side in ``sides`` (lists of equal length; powers required for k >= 1)."""
+    n = len(sides)
+    if not (len(thetas) == len(prims) == len(powers) == n):
+        raise ValueError("sides, thetas, prims and powers must have the same length")
+    need = poet_build_group_workspace_bytes(sides)
+    if ws is None and need > 0:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=prims[0].device)
+    th = _ptr_table(thetas, [f"thetas[{i}]" for i in range(n)], [4 * poet_theta_len(s) for s in sides],
+                    ["float32"] * n, [False] * n)
+    pr = _ptr_table(prims, [f"prims[{i}]" for i in range(n)], [4 * poet_prim_len(s) for s in sides],
+                    ["float32"] * n, [False] * n)
+    pw = _ptr_table(powers, [f"powers[{i}]" for i in range(n)],
+                    [poet_powers_len(s) * _esz(s.dtype) for s in sides], [_dt_name(s.dtype) for s in sides],
+                    [s.k == 0 for s in sides])
+    st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, _ptr(ws, "ws", need, allow_none=True),
+                                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_build_orthogonal_group")
+
+
+def poet_adjoint_group(sides, dprims, powers, dthetas, ws=None, stream=None):
+    """Neumann adjoint + skew projection of every side in ``sides`` from its primitive gradient."""
+    n = len(sides)
+    if not (len(dprims) == len(powers) == len(dthetas) == n):
+        raise ValueError("sides, dprims, powers and dthetas must have the same length")
+    need = poet_adjoint_group_workspace_bytes(sides)
+    if ws is None and need > 0:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=dprims[0].device)
+    skip = [poet_theta_len(s) == 0 for s in sides]
+    dp = _ptr_table(dprims, [f"dprims[{i}]" for i in range(n)], [4 * poet_prim_len(s) for s in sides],
+                    ["float32"] * n, skip)
+    pw = _ptr_table(powers, [f"powers[{i}]" for i in range(n)],
+                    [poet_powers_len(s) * _esz(s.dtype) for s in sides], [_dt_name(s.dtype) for s in sides],
+                    [sk or s.k == 0 for sk, s in zip(skip, sides)])
+    dt = _ptr_table(dthetas, [f"dthetas[{i}]" for i in range(n)], [4 * poet_theta_len(s) for s in sides],
+                    ["float32"] * n, skip)
+    st = lib().poet_adjoint_group(n, _side_array(sides), dp, pw, dt, _ptr(ws, "ws", need, allow_none=True),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_adjoint_group")
 
 
 def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR, idxP, seed: int, linear_id: int,

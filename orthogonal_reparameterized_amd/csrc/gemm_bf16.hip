@@ -48,6 +48,11 @@ struct FastArgs {
   GemmDesc g;
   int ntm, ntn, splits, kchunk;
   int use_part;  // write float32 partial tiles; a second kernel reduces them and applies the epilogue
+  // a second problem of the same shape in the same launch (batch entries batch1 .. g.batch - 1): its operands and
+  // output sit at these byte offsets from g's, with their own leading dimensions and extents
+  int batch1 = 0;
+  int64_t offA2 = 0, offB2 = 0, offC2 = 0, lda2 = 0, ldb2 = 0;
+  int Mtot2 = 0, Ntot2 = 0;
 };
 
 // an epilogue the main kernel stores directly: out = acc into C (no addend, scale, second copy or accumulate)
@@ -215,7 +220,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* 
 }
 
 // TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
-template <bool AK, bool BK_, int TAG>
+// PAIR: the launch holds two problems (FastArgs batch1 and the offsets of the second).
+template <bool AK, bool BK_, int TAG, bool PAIR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(const FastArgs fa_) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
   const GemmDesc& g = fa_.g;
@@ -241,10 +247,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     tm = GM * sr + r2 / w;
     tn = gi * GN + r2 % w;
   }
-  const int s = zs % splits, z = zs / splits;
+  const int s = zs % splits, zg = zs / splits;  // zg: batch entry over both problems (indexes the partials)
+  int z = zg;
+  const char* Ab = reinterpret_cast<const char*>(g.A);
+  const char* Bb = reinterpret_cast<const char*>(g.B);
+  char* Cb = reinterpret_cast<char*>(g.C);
+  int64_t lda = g.lda, ldb = g.ldb;
+  int Mtot = g.Mtot, Ntot = g.Ntot;
+  if constexpr (PAIR) {
+    if (z >= fa_.batch1) {
+      z -= fa_.batch1;
+      Ab += fa_.offA2; Bb += fa_.offB2; Cb += fa_.offC2;
+      lda = fa_.lda2; ldb = fa_.ldb2; Mtot = fa_.Mtot2; Ntot = fa_.Ntot2;
+    }
+  }
   int M = g.M, N = g.N, K = g.K;
-  if (g.Mtot > 0) M = min(M, g.Mtot - z * g.M);
-  if (g.Ntot > 0) N = min(N, g.Ntot - z * g.N);
+  if (Mtot > 0) M = min(M, Mtot - z * g.M);
+  if (Ntot > 0) N = min(N, Ntot - z * g.N);
   if (g.Ktot > 0) K = min(K, g.Ktot - z * g.K);
   const int m0 = tm * BM, n0 = tn * BN;
   if (m0 >= M || n0 >= N) return;
@@ -255,8 +274,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Operand<AK> oa;
   Operand<BK_> ob;
-  oa.init(reinterpret_cast<const __bf16*>(g.A) + (int64_t)z * g.sA, g.lda, m0, M, ke, wave, lane);
-  ob.init(reinterpret_cast<const __bf16*>(g.B) + (int64_t)z * g.sB, g.ldb, n0, N, ke, wave, lane);
+  oa.init(reinterpret_cast<const __bf16*>(Ab) + (int64_t)z * g.sA, lda, m0, M, ke, wave, lane);
+  ob.init(reinterpret_cast<const __bf16*>(Bb) + (int64_t)z * g.sB, ldb, n0, N, ke, wave, lane);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -357,12 +376,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __syncthreads();
   const int wrow0 = m0 + wr, wcol0 = n0 + wc;
   if (fa_.use_part) {  // raw partial tile; the reduction kernel sums the splits and applies the epilogue
-    float* pb = g.part + ((int64_t)(s * g.batch + z) * g.M + wrow0) * g.N + wcol0;
+    float* pb = g.part + ((int64_t)(s * g.batch + zg) * g.M + wrow0) * g.N + wcol0;
     store_tile_lds(acc, smem + wave * EP_BYTES, pb, F32, g.N, M - wrow0, N - wcol0, lane);
     return;
   }
   if (!g.C) return;
-  char* cb = reinterpret_cast<char*>(g.C) + ((int64_t)z * g.sC + (int64_t)wrow0 * g.ldc + wcol0) * dtype_size(g.c_dt);
+  char* cb = Cb + ((int64_t)z * g.sC + (int64_t)wrow0 * g.ldc + wcol0) * dtype_size(g.c_dt);
   store_tile_lds(acc, smem + wave * EP_BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane);
 }
 
@@ -371,16 +390,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) 
   const GemmDesc& g = fa_.g;
   const int64_t mn = (int64_t)g.M * g.N, total = (int64_t)g.batch * mn;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int z = (int)(e / mn);
-    const int64_t rc = e - (int64_t)z * mn;
+    const int zg = (int)(e / mn);
+    const int64_t rc = e - (int64_t)zg * mn;
     const int row = (int)(rc / g.N), col = (int)(rc - (int64_t)row * g.N);
+    const bool second = fa_.batch1 > 0 && zg >= fa_.batch1;  // second problem of a pair (plain epilogue)
+    const int z = second ? zg - fa_.batch1 : zg;
     int M = g.M, N = g.N;
-    if (g.Mtot > 0) M = min(M, g.Mtot - z * g.M);
-    if (g.Ntot > 0) N = min(N, g.Ntot - z * g.N);
+    const int Mtot = second ? fa_.Mtot2 : g.Mtot, Ntot = second ? fa_.Ntot2 : g.Ntot;
+    if (Mtot > 0) M = min(M, Mtot - z * g.M);
+    if (Ntot > 0) N = min(N, Ntot - z * g.N);
     if (row >= M || col >= N) continue;
     float sum = 0.f;
-    for (int s = 0; s < fa_.splits; ++s) sum += g.part[(int64_t)(s * g.batch + z) * mn + rc];
-    epilogue_one(g, z, row, col, sum);
+    for (int s = 0; s < fa_.splits; ++s) sum += g.part[(int64_t)(s * g.batch + zg) * mn + rc];
+    if (fa_.batch1 > 0) {
+      char* cb = reinterpret_cast<char*>(g.C) + (second ? fa_.offC2 : 0);
+      store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col, sum);
+    } else {
+      epilogue_one(g, z, row, col, sum);
+    }
   }
 }
 
@@ -439,6 +466,48 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fa.use_part || g.defer_reduce) return e;
+  const int64_t total = (int64_t)g.batch * g.M * g.N;
+  const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
+  return hipGetLastError();
+}
+
+bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b) {
+  if (!fast_gemm_eligible(a) || !fast_gemm_eligible(b)) return false;
+  if (!plain_epilogue(a) || !plain_epilogue(b) || a.defer_reduce || b.defer_reduce) return false;
+  if (a.a_kmajor || a.b_kmajor || b.a_kmajor || b.b_kmajor) return false;  // the token-axis contraction's layout
+  if (a.M != b.M || a.N != b.N || a.K != b.K || a.Ktot != b.Ktot || a.sA != b.sA || a.sB != b.sB) return false;
+  if (a.ldc != b.ldc || a.sC != b.sC || a.c_dt != b.c_dt) return false;
+  // the partials of both problems (at least 2 splits) in the first one's scratch
+  return a.part && a.part_elems >= (size_t)2 * (a.batch + b.batch) * a.M * a.N;
+}
+
+hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
+  GemmDesc g = a;
+  g.batch = a.batch + b.batch;
+  if (g.batch <= 0) return hipSuccess;
+  FastArgs fa;
+  fa.g = g;
+  fa.ntm = (g.M + BM - 1) / BM;
+  fa.ntn = (g.N + BN - 1) / BN;
+  const int tiles = g.batch * fa.ntm * fa.ntn;
+  const int nk = (g.K + BK - 1) / BK;
+  const int S = fast_gemm_splits(g);
+  fa.splits = S;
+  fa.kchunk = ((nk + S - 1) / S) * BK;
+  fa.use_part = S > 1 ? 1 : 0;
+  fa.batch1 = a.batch;
+  fa.offA2 = reinterpret_cast<const char*>(b.A) - reinterpret_cast<const char*>(a.A);
+  fa.offB2 = reinterpret_cast<const char*>(b.B) - reinterpret_cast<const char*>(a.B);
+  fa.offC2 = reinterpret_cast<const char*>(b.C) - reinterpret_cast<const char*>(a.C);
+  fa.lda2 = b.lda; fa.ldb2 = b.ldb; fa.Mtot2 = b.Mtot; fa.Ntot2 = b.Ntot;
+  const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
+  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (double)g.M * g.N * 4.0);
+  ProfScope prof(g.kclass, st, flops, bytes);
+  const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
+  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0, true>), grid, block, 0, st, fa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !fa.use_part) return e;
   const int64_t total = (int64_t)g.batch * g.M * g.N;
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);

@@ -46,6 +46,10 @@ struct GemmDesc {
 bool fast_gemm_eligible(const GemmDesc& g);
 int fast_gemm_splits(const GemmDesc& g);  // split-K count the fast path uses for g
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
+// Two problems of one shape in one launch (the R- and P-side token-axis contractions of a linear): both M-major
+// operands, plain epilogue; the split-K partials of both go to a's scratch.
+bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b);
+hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream_t st);
 
 // Power chain X_{j+1} = Q X_j, j = 0..steps-1, of nprim primitives of size bp <= 256 (power_chain.hip), with Q
 // the bf16 blocks A (row pitch bp, stride sA).
@@ -64,6 +68,47 @@ struct ChainArgs {
 };
 bool power_chain_eligible(int bp, int dt, const void* A);  // A: the power/Q buffer (16-byte aligned)
 hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st);
+// A kernel reads its side's entry of a table at a dynamic index; without this the compiler reloads each field from
+// the kernel arguments at every use. Copied once through keep_s, the fields stay in scalar registers.
+template <class T>
+__device__ __forceinline__ T keep_s(T v) {
+  if constexpr (sizeof(T) == 8) {
+    uint64_t u = __builtin_bit_cast(uint64_t, v);
+    asm volatile("" : "+s"(u));
+    return __builtin_bit_cast(T, u);
+  } else {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    asm volatile("" : "+s"(u));
+    return __builtin_bit_cast(T, u);
+  }
+}
+
+// Up to MAXG sides in one launch (all with the same build flag; each side keeps its own sizes and buffers).
+constexpr int MAXG = 16;
+struct ChainGroup {
+  int n = 0;
+  ChainArgs a[MAXG];
+};
+hipError_t launch_power_chain_group(const ChainGroup& g, int kclass, hipStream_t st);
+
+// ---- side tables: one launch over up to MAXG sides (the per-block kernels of several linears together) ----
+struct PrepSide {
+  const float* theta = nullptr; float* prim = nullptr; void* q = nullptr;
+  int q_dt = BF16, ldq = 0, mode = 0, d = 0, bp = 0, nprim = 0;
+  float coef = 2.f;
+};
+struct PrepGroup { int n = 0; PrepSide s[MAXG]; };
+hipError_t launch_theta_prep_group(const PrepGroup& g, hipStream_t st);
+
+struct CoefSide { const void* powers = nullptr; void* out = nullptr; int nprim = 0; };
+struct CoefGroup { int n = 0, bp = 0, ldp = 0, k = 0; CoefSide s[MAXG]; };  // one (bp, ldp, k) for all sides
+hipError_t launch_adjoint_coefs_group(const CoefGroup& g, int dt, hipStream_t st);
+
+// dtheta of each side from split-K partials part[s * split_stride + (boff + p) bp^2 + ...] plus beta D
+struct SkewSide { const float* D = nullptr; float* dtheta = nullptr; int mode = 0, d = 0, nprim = 0, boff = 0; };
+struct SkewGroup { int n = 0, bp = 0; const float* part = nullptr; int64_t split_stride = 0; float beta = 0.f; SkewSide s[MAXG]; };
+hipError_t launch_reduce_skew_group(const SkewGroup& g, int nsplit, hipStream_t st);
+
 
 // Fused application of block-diagonal factors on both sides (bs_apply.hip), blocks bpR, bpP <= 256, W0 float32
 // m x n with row pitch ldw (rows readable up to a multiple of 4 columns), primitives float32 bp x bp blocks:

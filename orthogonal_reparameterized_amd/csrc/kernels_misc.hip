@@ -1,6 +1,8 @@
 // Elementwise and data-movement kernels of the POET layer: skew packing, the skew projection of the
 // gradient, FS index gather/scatter, dtype conversion, and the counter-based FS index sampler.
 // All are memory-bound; threads walk the contiguous dimension so that every wavefront access is coalesced.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace poet {
@@ -27,25 +29,33 @@ __device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
 // every primitive before p is a full bp x bp block
 __device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
 
-__global__ void k_theta_prep(const float* __restrict__ theta, int mode, int d, int bp, int nprim, float coef,
-                             float* __restrict__ prim, void* __restrict__ qout, int q_dt, int ldq) {
-  const int64_t total = (int64_t)nprim * bp * bp;
+// prim = I + coef Q and the first saved power Q (dtype q_dt, row pitch ldq) of side blockIdx.y of the table
+__global__ void k_theta_prep(const PrepGroup G) {
+  PrepSide a;
+  {
+    const PrepSide& t = G.s[blockIdx.y];
+    a.theta = keep_s(t.theta); a.prim = keep_s(t.prim); a.q = keep_s(t.q); a.q_dt = keep_s(t.q_dt);
+    a.ldq = keep_s(t.ldq); a.mode = keep_s(t.mode); a.d = keep_s(t.d); a.bp = keep_s(t.bp);
+    a.nprim = keep_s(t.nprim); a.coef = keep_s(t.coef);
+  }
+  const int bp = a.bp;
+  const int64_t total = (int64_t)a.nprim * bp * bp;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(e / ((int64_t)bp * bp));
     const int rem = (int)(e - (int64_t)p * bp * bp);
     const int i = rem / bp, j = rem % bp;
-    const int c = prim_size(mode, d, bp, p);
+    const int c = prim_size(a.mode, a.d, bp, p);
     float q = 0.f;
     if (i < c && j < c && i != j) {
       const int64_t off = theta_off(bp, p);
-      q = i < j ? theta[off + tri_pos(i, j, c)] : -theta[off + tri_pos(j, i, c)];
+      q = i < j ? a.theta[off + tri_pos(i, j, c)] : -a.theta[off + tri_pos(j, i, c)];
     }
-    prim[e] = (i == j ? 1.f : 0.f) + coef * q;
-    if (qout) {
-      const int64_t o = ((int64_t)p * bp + i) * ldq + j;
-      if (q_dt == BF16) reinterpret_cast<__bf16*>(qout)[o] = (__bf16)q;
-      else reinterpret_cast<float*>(qout)[o] = q;
+    a.prim[e] = (i == j ? 1.f : 0.f) + a.coef * q;
+    if (a.q) {
+      const int64_t o = ((int64_t)p * bp + i) * a.ldq + j;
+      if (a.q_dt == BF16) reinterpret_cast<__bf16*>(a.q)[o] = (__bf16)q;
+      else reinterpret_cast<float*>(a.q)[o] = q;
     }
   }
 }
@@ -88,21 +98,30 @@ __global__ void k_skew_project(const float* __restrict__ dQ, const float* __rest
   }
 }
 
-// dtheta of primitive p = blockIdx.y from NS split-K partials: X = sum_s part[s] (split order) + beta D, then
-// X_ij - X_ji. Workgroup x takes the pair of 32 x 32 tiles (ti, tj), ti <= tj: both are read row-wise (coalesced,
-// the 8 NS loads of a thread issued together), the (tj, ti) tile is transposed through LDS.
+// dtheta of primitive p = blockIdx.y of side blockIdx.z from NS split-K partials: X = sum_s part[s] (split order) +
+// beta D, then X_ij - X_ji. The side's blocks sit at block offset boff of the partials (split stride split_stride).
+// Workgroup x takes the pair of 32 x 32 tiles (ti, tj), ti <= tj: both are read row-wise (coalesced, the NS loads
+// of a thread issued together), the (tj, ti) tile is transposed through LDS.
 template <int NS>
-__global__ __launch_bounds__(256) void k_reduce_skew(const float* __restrict__ part, int64_t split_stride,
-                                                     const float* __restrict__ D, float beta, int mode, int d, int bp,
-                                                     float* __restrict__ dtheta) {
+__global__ __launch_bounds__(256) void k_reduce_skew(const SkewGroup G) {
   __shared__ float tr[32][33];
+  SkewSide a;
+  {
+    const SkewSide& t = G.s[blockIdx.z];
+    a.D = keep_s(t.D); a.dtheta = keep_s(t.dtheta); a.mode = keep_s(t.mode); a.d = keep_s(t.d);
+    a.nprim = keep_s(t.nprim); a.boff = keep_s(t.boff);
+  }
   const int p = blockIdx.y;
+  if (p >= a.nprim) return;
+  const int bp = G.bp;
   int ti = 0, rem = blockIdx.x;  // blockIdx.x enumerates ti <= tj row by row
   const int nt = (bp + 31) / 32;
   while (rem >= nt - ti) { rem -= nt - ti; ++ti; }
   const int tj = ti + rem;
-  const int c = prim_size(mode, d, bp, p);
+  const int c = prim_size(a.mode, a.d, bp, p);
   const int64_t base = (int64_t)p * bp * bp;
+  const float* part = G.part + (int64_t)a.boff * bp * bp;
+  const int64_t split_stride = G.split_stride;
   const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;  // rows row0 + 8 q
   float xa[4], xb[4];
 #pragma unroll
@@ -125,9 +144,9 @@ __global__ __launch_bounds__(256) void k_reduce_skew(const float* __restrict__ p
       xa[q] += va[s];
       xb[q] += vb[s];
     }
-    if (D) {
-      xa[q] += beta * D[oa];
-      xb[q] += beta * D[ob];
+    if (a.D) {
+      xa[q] += G.beta * a.D[oa];
+      xb[q] += G.beta * a.D[ob];
     }
     tr[col][r] = xb[q];  // transposed: tr[jb - 32 ti][ib - 32 tj]
   }
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(256) void k_reduce_skew(const float* __restrict__ p
   for (int q = 0; q < 4; ++q) {
     const int r = row0 + 8 * q;
     const int i = ti * 32 + r, j = tj * 32 + col;
-    if (i < j && j < c) dtheta[theta_off(bp, p) + tri_pos(i, j, c)] = xa[q] - tr[r][col];
+    if (i < j && j < c) a.dtheta[theta_off(bp, p) + tri_pos(i, j, c)] = xa[q] - tr[r][col];
   }
 }
 
@@ -266,10 +285,19 @@ __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
 }
 
 // element (p, j, r, c) of the stacked coefficient matrices; see launch_adjoint_coefs
-// Block j of primitive p (blockIdx.y = p (k+1) + j), stored ldp x ldp (rows and columns past bp zero); thread x
-// covers VEC consecutive elements of it (32-bit index math). Powers are bp x ldp blocks.
+// Block j of primitive p (blockIdx.y = p (k+1) + j) of side blockIdx.z, stored ldp x ldp (rows and columns past bp
+// zero); thread x covers VEC consecutive elements of it (32-bit index math). Powers are bp x ldp blocks.
 template <typename T, int VEC>
-__global__ void k_adjoint_coefs(const T* __restrict__ powers, int nprim, int bp, int ldp, int k, T* __restrict__ out) {
+__global__ void k_adjoint_coefs(const CoefGroup G) {
+  CoefSide sd;
+  {
+    const CoefSide& t = G.s[blockIdx.z];
+    sd.powers = keep_s(t.powers); sd.out = keep_s(t.out); sd.nprim = keep_s(t.nprim);
+  }
+  const int nprim = sd.nprim, bp = G.bp, ldp = G.ldp, k = G.k;
+  if ((int)blockIdx.y >= nprim * (k + 1)) return;
+  const T* __restrict__ powers = reinterpret_cast<const T*>(sd.powers);
+  T* __restrict__ out = reinterpret_cast<T*>(sd.out);
   const int pq = ldp * ldp;
   const int rc0 = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
   if (rc0 >= pq) return;
@@ -341,35 +369,64 @@ hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf
   return hipGetLastError();
 }
 
-hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int ldp, int k, void* out, hipStream_t st) {
-  const int64_t total = (int64_t)nprim * (k + 1) * ldp * ldp;
-  if (total == 0) return hipSuccess;
-  if ((int64_t)ldp * ldp > (1 << 30) || (int64_t)nprim * (k + 1) > 65535) return hipErrorInvalidValue;
-  ProfScope prof(7, st, 0, (double)total * dtype_size(dt) * 2);
-  const int pq = ldp * ldp;
-  if (dt == BF16 && ldp % 4 == 0) {
-    const dim3 grid((pq / 4 + kThreads - 1) / kThreads, nprim * (k + 1));
-    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 4>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const __bf16*>(powers), nprim, bp, ldp, k, reinterpret_cast<__bf16*>(out));
-  } else if (dt == BF16) {
-    const dim3 grid((pq + kThreads - 1) / kThreads, nprim * (k + 1));
-    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 1>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const __bf16*>(powers), nprim, bp, ldp, k, reinterpret_cast<__bf16*>(out));
-  } else {
-    const dim3 grid((pq + kThreads - 1) / kThreads, nprim * (k + 1));
-    hipLaunchKernelGGL((k_adjoint_coefs<float, 1>), grid, dim3(kThreads), 0, st,
-                       reinterpret_cast<const float*>(powers), nprim, bp, ldp, k, reinterpret_cast<float*>(out));
+hipError_t launch_adjoint_coefs_group(const CoefGroup& g, int dt, hipStream_t st) {
+  if (g.n <= 0) return hipSuccess;
+  if (g.n > MAXG) return hipErrorInvalidValue;
+  const int ldp = g.ldp, k = g.k, pq = ldp * ldp;
+  int ny = 0;
+  double total = 0;
+  for (int i = 0; i < g.n; ++i) {
+    ny = std::max(ny, g.s[i].nprim * (k + 1));
+    total += (double)g.s[i].nprim * (k + 1) * pq;
   }
+  if (total == 0) return hipSuccess;
+  if ((int64_t)ldp * ldp > (1 << 30) || ny > 65535) return hipErrorInvalidValue;
+  ProfScope prof(7, st, 0, total * dtype_size(dt) * 2);
+  if (dt == BF16 && ldp % 4 == 0) {
+    const dim3 grid((pq / 4 + kThreads - 1) / kThreads, ny, g.n);
+    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 4>), grid, dim3(kThreads), 0, st, g);
+  } else if (dt == BF16) {
+    const dim3 grid((pq + kThreads - 1) / kThreads, ny, g.n);
+    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 1>), grid, dim3(kThreads), 0, st, g);
+  } else {
+    const dim3 grid((pq + kThreads - 1) / kThreads, ny, g.n);
+    hipLaunchKernelGGL((k_adjoint_coefs<float, 1>), grid, dim3(kThreads), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int ldp, int k, void* out, hipStream_t st) {
+  CoefGroup g;
+  g.n = 1; g.bp = bp; g.ldp = ldp; g.k = k;
+  g.s[0].powers = powers; g.s[0].out = out; g.s[0].nprim = nprim;
+  return launch_adjoint_coefs_group(g, dt, st);
+}
+
+hipError_t launch_theta_prep_group(const PrepGroup& g, hipStream_t st) {
+  if (g.n <= 0) return hipSuccess;
+  if (g.n > MAXG) return hipErrorInvalidValue;
+  size_t most = 0;
+  double bytes = 0;
+  for (int i = 0; i < g.n; ++i) {
+    const PrepSide& a = g.s[i];
+    const size_t total = (size_t)a.nprim * a.bp * a.bp;
+    most = std::max(most, total);
+    bytes += (double)total * (4 + 4 + (a.q ? dtype_size(a.q_dt) : 0));
+  }
+  if (most == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, bytes);
+  hipLaunchKernelGGL(k_theta_prep, dim3(grid_for(most, kThreads, 4096), g.n), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_theta_prep(const float* theta, int mode, int d, int bp, int nprim, int k, float* prim, void* q_out,
                              int q_dt, int ldq, hipStream_t st) {
-  const size_t total = (size_t)nprim * bp * bp;
-  ProfScope prof(7, st, 0, (double)total * (4 + 4 + (q_out ? dtype_size(q_dt) : 0)));
-  hipLaunchKernelGGL(k_theta_prep, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim,
-                     k == 0 ? 1.f : 2.f, prim, q_out, q_dt, ldq);
-  return hipGetLastError();
+  PrepGroup g;
+  g.n = 1;
+  PrepSide& a = g.s[0];
+  a.theta = theta; a.prim = prim; a.q = q_out; a.q_dt = q_dt; a.ldq = ldq;
+  a.mode = mode; a.d = d; a.bp = bp; a.nprim = nprim; a.coef = k == 0 ? 1.f : 2.f;
+  return launch_theta_prep_group(g, st);
 }
 
 hipError_t launch_qnorm(const float* theta, int mode, int d, int bp, int nprim, float* qnorm, hipStream_t st) {
@@ -386,21 +443,39 @@ hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
-                              int d, int bp, int nprim, float* dtheta, hipStream_t st) {
-  if (nprim <= 0) return hipSuccess;
-  if (nprim > 65535 || (int64_t)bp * bp > (1 << 30)) return hipErrorInvalidValue;
-  ProfScope prof(7, st, 0, (double)nprim * bp * bp * 4.0 * (nsplit + 1) + (double)nprim * bp * (bp - 1) * 2.0);
+hipError_t launch_reduce_skew_group(const SkewGroup& g, int nsplit, hipStream_t st) {
+  if (g.n <= 0) return hipSuccess;
+  if (g.n > MAXG) return hipErrorInvalidValue;
+  const int bp = g.bp;
+  int ny = 0;
+  double blocks = 0;
+  for (int i = 0; i < g.n; ++i) {
+    ny = std::max(ny, g.s[i].nprim);
+    blocks += g.s[i].nprim;
+  }
+  if (ny == 0) return hipSuccess;
+  if (ny > 65535 || (int64_t)bp * bp > (1 << 30)) return hipErrorInvalidValue;
+  ProfScope prof(7, st, 0, blocks * bp * bp * 4.0 * (nsplit + 1) + blocks * bp * (bp - 1) * 2.0);
   const int nt = (bp + 31) / 32;
-  const dim3 grid(nt * (nt + 1) / 2, nprim);
+  const dim3 grid(nt * (nt + 1) / 2, ny, g.n);
   switch (nsplit) {
 #define POET_RS(NS) \
-  case NS: hipLaunchKernelGGL(k_reduce_skew<NS>, grid, dim3(kThreads), 0, st, part, split_stride, D, beta, mode, d, bp, dtheta); break;
+  case NS: hipLaunchKernelGGL(k_reduce_skew<NS>, grid, dim3(kThreads), 0, st, g); break;
     POET_RS(1) POET_RS(2) POET_RS(4) POET_RS(8) POET_RS(16)
 #undef POET_RS
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
+                              int d, int bp, int nprim, float* dtheta, hipStream_t st) {
+  if (nprim <= 0) return hipSuccess;
+  SkewGroup g;
+  g.n = 1; g.part = part; g.split_stride = split_stride; g.beta = beta; g.bp = bp;
+  SkewSide& a = g.s[0];
+  a.D = D; a.dtheta = dtheta; a.mode = mode; a.d = d; a.nprim = nprim; a.boff = 0;
+  return launch_reduce_skew_group(g, nsplit, st);
 }
 
 // Diagonal blocks of super-block products: super-block u (size sb = g bp, row pitch sb) holds the products of

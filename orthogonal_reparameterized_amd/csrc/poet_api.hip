@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/poet.h"
 #include "internal.h"
@@ -339,11 +340,21 @@ ApplyArgs apply_args(const poet_layer& L, const SideInfo& R, const SideInfo& P, 
 
 // The primitive-gradient contraction g (output dR blocks, reduced over its K splits across the whole machine), then
 // the adjoint. A ragged last block writes only its true extent, so dR is zero-filled first.
+// a ragged last block of a BS side is written only over its extent: zero the rest of its bp x bp block first
+hipError_t clear_ragged(const SideInfo& S, float* dR, hipStream_t st) {
+  if (S.mode != POET_BS || S.d % S.bp == 0) return hipSuccess;
+  const size_t pp = (size_t)S.bp * S.bp;
+  return launch_fill(dR + (S.nprim - 1) * pp, pp, 0.f, st);
+}
+hipError_t contract_only(const SideInfo& S, const GemmDesc& g, float* dR, hipStream_t st) {
+  hipError_t e;
+  if ((e = clear_ragged(S, dR, st)) != hipSuccess) return e;
+  return launch_gemm(g, st);
+}
 hipError_t contract_and_adjoint(const SideInfo& S, const GemmDesc& g, float* dR, const void* powers, float* dtheta,
                                 const AdjBufs& b, hipStream_t st) {
   hipError_t e;
-  if (S.mode == POET_BS && (e = launch_fill(dR, S.prim_len, 0.f, st)) != hipSuccess) return e;
-  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  if ((e = contract_only(S, g, dR, st)) != hipSuccess) return e;
   return neumann_adjoint(S, dR, powers, dtheta, b, st);
 }
 
@@ -477,8 +488,9 @@ size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, v
   p->adj.dQ = a.take<float>(std::max(R.prim_len, P.prim_len));
   p->adj.H = a.take_bytes(std::max(adj_h_elems(R) * dtype_size(R.dtype), adj_h_elems(P) * dtype_size(P.dtype)));
   p->adj.Cs = a.take_bytes(std::max(adj_c_elems(R) * dtype_size(R.dtype), adj_c_elems(P) * dtype_size(P.dtype)));
-  // split-K partial sums of the token-axis contractions (up to 16 splits) and of the adjoint products
-  p->adj.part_elems = 16 * std::max({R.prim_len, P.prim_len, p->sup_elems});
+  // split-K partial sums of the token-axis contractions (up to 16 splits of both sides' blocks, which can share
+  // one launch) and of the adjoint products
+  p->adj.part_elems = 16 * std::max({R.prim_len + P.prim_len, p->sup_elems});
   p->adj.part = a.take<float>(p->adj.part_elems);
   return a.used();
 }
@@ -510,19 +522,23 @@ GemmDesc act_contract(const SideInfo& S, int T, const void* A, int64_t lda, cons
   return g;
 }
 
-// dF = blocks of A^T B over the tokens, then the adjoint (small blocks through super-block products)
+// dF = blocks of A^T B over the tokens (small blocks through super-block products), then the adjoint unless dtheta
+// is null (the caller finishes the primitive gradient dF itself, e.g. with poet_adjoint_group)
 hipError_t act_contract_adjoint(const SideInfo& S, int T, const void* A, int64_t lda, const void* B, int64_t ldb,
                                 float* dF, const void* powers, float* dtheta, const ActBwdPlan& p, hipStream_t st) {
   const int g = super_group(S);
-  if (g == 1) return contract_and_adjoint(S, act_contract(S, T, A, lda, B, ldb, dF, p.adj), dF, powers, dtheta, p.adj, st);
-  SideInfo U = S;  // the super-block view: blocks of g bp
-  U.bp = g * S.bp;
-  U.nprim = (S.nprim + g - 1) / g;
-  GemmDesc gd = act_contract(U, T, A, lda, B, ldb, p.sup, p.adj);
   hipError_t e;
-  if ((e = launch_gemm(gd, st)) != hipSuccess) return e;
-  if ((e = launch_extract_diag(p.sup, U.bp, g, S.bp, S.d, S.nprim, dF, st)) != hipSuccess) return e;
-  return neumann_adjoint(S, dF, powers, dtheta, p.adj, st);
+  if (g == 1) {
+    if ((e = contract_only(S, act_contract(S, T, A, lda, B, ldb, dF, p.adj), dF, st)) != hipSuccess) return e;
+  } else {
+    SideInfo U = S;  // the super-block view: blocks of g bp
+    U.bp = g * S.bp;
+    U.nprim = (S.nprim + g - 1) / g;
+    GemmDesc gd = act_contract(U, T, A, lda, B, ldb, p.sup, p.adj);
+    if ((e = launch_gemm(gd, st)) != hipSuccess) return e;
+    if ((e = launch_extract_diag(p.sup, U.bp, g, S.bp, S.d, S.nprim, dF, st)) != hipSuccess) return e;
+  }
+  return dtheta ? neumann_adjoint(S, dF, powers, dtheta, p.adj, st) : hipSuccess;
 }
 
 // bf16 copies of a side's primitives (the full factor, identity included)
@@ -572,6 +588,144 @@ bool check_ws(void* ws, size_t have, size_t need) {
   if (have < need) return fail(POET_E_WORKSPACE, "workspace of %zu bytes < %zu needed", have, need), false;
   if (!ws && need > 0) return fail(POET_E_ARG, "null workspace"), false;
   return true;
+}
+
+// ---- grouped calls: the per-block kernels of many sides (e.g. every linear of a transformer block) in shared
+// launches of up to MAXG sides each ----
+bool group_sides(int32_t count, const poet_side* sides, std::vector<SideInfo>* out) {
+  if (count < 0) return fail(POET_E_ARG, "count = %d must be >= 0", count), false;
+  if (count > 0 && !sides) return fail(POET_E_ARG, "null sides"), false;
+  out->resize(count);
+  char name[32];
+  for (int i = 0; i < count; ++i) {
+    snprintf(name, sizeof name, "sides[%d]", i);
+    if (!side_info(&sides[i], &(*out)[i], name)) return false;
+  }
+  return true;
+}
+
+// the fused chain kernel takes the side (BS or FS, bf16, primitive <= 256 and a multiple of 8, unpadded powers)
+bool chain_side(const SideInfo& S, const void* powers) {
+  return S.k > 0 && S.ldp == S.bp && power_chain_eligible(S.bp, S.dtype, powers);
+}
+
+// adjoint chunks: sides sharing (bp, k) whose adjoint runs on the fused chain, at most MAXG per chunk
+struct AdjChunk {
+  int bp = 0, k = 0, nb = 0;
+  std::vector<int> idx;
+};
+std::vector<AdjChunk> adjoint_chunks(const std::vector<SideInfo>& S, const void* const* powers, std::vector<int>* solo) {
+  std::vector<AdjChunk> ch;
+  for (int i = 0; i < (int)S.size(); ++i) {
+    if (S[i].theta_len == 0) continue;
+    const void* pw = powers ? powers[i] : reinterpret_cast<const void*>(256);  // sizing: assume aligned powers
+    if (!chain_side(S[i], pw)) { solo->push_back(i); continue; }
+    AdjChunk* c = nullptr;
+    for (auto& x : ch)
+      if (x.bp == S[i].bp && x.k == S[i].k && (int)x.idx.size() < MAXG) c = &x;
+    if (!c) { ch.emplace_back(); c = &ch.back(); c->bp = S[i].bp; c->k = S[i].k; }
+    c->idx.push_back(i);
+    c->nb += S[i].nprim;
+  }
+  return ch;
+}
+
+// scratch of one chunk: H_0..H_k and the coefficient stack of every block (bf16), the adjoint product's split-K
+// partials (up to 4 splits; at least one float32 block per primitive, which also serves the unsplit generic path)
+struct AdjChunkBufs {
+  __bf16 *H = nullptr, *Cs = nullptr;
+  float* part = nullptr;
+  size_t part_elems = 0;
+};
+size_t plan_adj_chunk(const AdjChunk& c, void* ws, AdjChunkBufs* b) {
+  Arena a(ws);
+  const size_t pp = (size_t)c.bp * c.bp, nb = (size_t)c.nb;
+  b->H = a.take<__bf16>(nb * pp * (c.k + 1));
+  b->Cs = a.take<__bf16>(nb * pp * (c.k + 1));
+  b->part_elems = 4 * nb * pp;
+  b->part = a.take<float>(b->part_elems);
+  return a.used();
+}
+
+// scratch of one side's own adjoint (sides the chunks do not take)
+size_t plan_adj_solo(const SideInfo& S, void* ws, AdjBufs* b) {
+  Arena a(ws);
+  b->dQ = a.take<float>(S.prim_len);
+  b->H = a.take_bytes(adj_h_elems(S) * dtype_size(S.dtype));
+  b->Cs = a.take_bytes(adj_c_elems(S) * dtype_size(S.dtype));
+  b->part_elems = 4 * S.prim_len;
+  b->part = a.take<float>(b->part_elems);
+  return a.used();
+}
+
+size_t adjoint_group_bytes(const std::vector<SideInfo>& S, const void* const* powers) {
+  std::vector<int> solo;
+  const auto ch = adjoint_chunks(S, powers, &solo);
+  size_t need = 0;
+  AdjChunkBufs cb;
+  for (const auto& c : ch) need = std::max(need, plan_adj_chunk(c, nullptr, &cb));
+  AdjBufs sb;
+  for (size_t i = 0; i < S.size(); ++i)  // any side may end up on its own (misaligned powers)
+    if (S[i].theta_len > 0 && S[i].k > 0) need = std::max(need, plan_adj_solo(S[i], nullptr, &sb));
+  return need;
+}
+
+// the Neumann adjoint and skew projection of one chunk (see neumann_adjoint for the algebra)
+hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, const float* const* dprim,
+                         const void* const* powers, float* const* dtheta, const AdjChunkBufs& b, hipStream_t st) {
+  const int bp = c.bp, k = c.k, ldh = (k + 1) * bp;
+  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
+  hipError_t e;
+  {  // H_0 = dR and H_{j+1} = Q H_j for every block of the chunk
+    ChainGroup g;
+    int boff = 0;
+    for (int i : c.idx) {
+      ChainArgs& a = g.a[g.n++];
+      a.bp = bp; a.nprim = S[i].nprim; a.steps = k;
+      a.A = reinterpret_cast<const __bf16*>(powers[i]); a.sA = pp;
+      a.X0 = dprim[i]; a.ldx0 = bp; a.sx0 = pp;
+      a.Y = b.H + (size_t)boff * hs; a.ldy = ldh; a.sy = hs; a.jstep = bp; a.write_x0 = 1;
+      boff += S[i].nprim;
+    }
+    if ((e = launch_power_chain_group(g, POET_K_ADJOINT, st)) != hipSuccess) return e;
+  }
+  {  // the coefficient stacks C_0..C_k from the saved powers
+    CoefGroup g;
+    g.bp = bp; g.ldp = bp; g.k = k;
+    int boff = 0;
+    for (int i : c.idx) {
+      CoefSide& a = g.s[g.n++];
+      a.powers = powers[i]; a.out = b.Cs + (size_t)boff * (k + 1) * pp; a.nprim = S[i].nprim;
+      boff += S[i].nprim;
+    }
+    if ((e = launch_adjoint_coefs_group(g, BF16, st)) != hipSuccess) return e;
+  }
+  GemmDesc g;  // [H_0 .. H_k] [C_0; ..; C_k] for all blocks of the chunk as one batch
+  g.kclass = POET_K_ADJOINT;
+  g.compute = BF16; g.M = g.N = bp; g.K = ldh; g.batch = c.nb;
+  g.A = b.H; g.lda = ldh; g.sA = hs; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = b.Cs; g.ldb = bp; g.sB = (int64_t)(k + 1) * pp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.C = b.part; g.ldc = bp; g.sC = pp; g.c_dt = F32;
+  g.part = b.part; g.part_elems = b.part_elems;
+  int ns = 1;
+  g.defer_reduce = 1;
+  if (fast_gemm_eligible(g)) {  // split-K partials, reduced with a_1 dR = 2 dR inside the skew projection
+    ns = fast_gemm_splits(g);
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  } else {  // the product itself lands in the partial buffer (one split)
+    g.defer_reduce = 0;
+    g.part = nullptr; g.part_elems = 0;
+    if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  }
+  SkewGroup sg;
+  sg.bp = bp; sg.part = b.part; sg.split_stride = (int64_t)c.nb * pp; sg.beta = 2.f;  // a_1 = 2 for k >= 1
+  int boff = 0;
+  for (int i : c.idx) {
+    SkewSide& a = sg.s[sg.n++];
+    a.D = dprim[i]; a.dtheta = dtheta[i]; a.mode = S[i].mode; a.d = S[i].d; a.nprim = S[i].nprim; a.boff = boff;
+    boff += S[i].nprim;
+  }
+  return launch_reduce_skew_group(sg, ns, st);
 }
 
 bool check_idx(const SideInfo& S, const void* idx, const char* name) {
@@ -911,18 +1065,26 @@ poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const floa
   return POET_OK;
 }
 
-poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* powersR, const void* powersP, const void* X, const void* Z,
-                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+// the activation-side backward; with dprimR/dprimP given it stops at the primitive gradients
+poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP, const void* powersR,
+                    const void* powersP, const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
+                    float* dthetaP, float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
   if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
   if (!W0b || !primR || !primP) return fail(POET_E_ARG, "null W0 shadow or primitive");
   if (L->T > 0 && (!X || !Z || !dY)) return fail(POET_E_ARG, "null X, Z or dY");
-  if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
-  if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
-    return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  const bool prims_only = dprimR || dprimP;
+  if (prims_only) {
+    if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  } else {
+    if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
+    if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
+      return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  }
   ActBwdPlan p;
   if (!check_ws(ws, ws_bytes, plan_bwd_act(*L, R, P, nullptr, &p))) return g_last;
   plan_bwd_act(*L, R, P, ws, &p);
@@ -941,9 +1103,135 @@ poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const floa
     }
     if (dX) HIP_TRY(act_factor(P, T, p.dXp, L->ldx, primP, p.Pb, false, dX, L->ldx, st));  // dX = dX' P
   }
-  // primitive blocks of dL/dR = dY^T Z and dL/dP = dX'^T X (zero when T == 0), then the adjoint
+  // primitive blocks of dL/dR = dY^T Z and dL/dP = dX'^T X (zero when T == 0), then the adjoint; the two
+  // contractions share one launch when their shapes allow
+  float* dR = prims_only ? dprimR : p.dRg;
+  float* dP = prims_only ? dprimP : p.dPg;
+  if (super_group(R) == 1 && super_group(P) == 1 && R.theta_len > 0 && P.theta_len > 0) {
+    const GemmDesc gR = act_contract(R, T, dY, L->ldy, Z, L->ldy, dR, p.adj);
+    const GemmDesc gP = act_contract(P, T, p.dXp, L->ldx, X, L->ldx, dP, p.adj);
+    if (fast_gemm_pair_eligible(gR, gP)) {
+      HIP_TRY(clear_ragged(R, dR, st));
+      HIP_TRY(clear_ragged(P, dP, st));
+      HIP_TRY(launch_fast_gemm_pair(gR, gP, st));
+      if (prims_only) return POET_OK;
+      HIP_TRY(neumann_adjoint(R, dR, powersR, dthetaR, p.adj, st));
+      HIP_TRY(neumann_adjoint(P, dP, powersP, dthetaP, p.adj, st));
+      return POET_OK;
+    }
+  }
+  if (prims_only) {
+    HIP_TRY(act_contract_adjoint(R, T, dY, L->ldy, Z, L->ldy, dprimR, nullptr, nullptr, p, st));
+    HIP_TRY(act_contract_adjoint(P, T, p.dXp, L->ldx, X, L->ldx, dprimP, nullptr, nullptr, p, st));
+    return POET_OK;
+  }
   if (R.theta_len > 0) HIP_TRY(act_contract_adjoint(R, T, dY, L->ldy, Z, L->ldy, p.dRg, powersR, dthetaR, p, st));
   if (P.theta_len > 0) HIP_TRY(act_contract_adjoint(P, T, p.dXp, L->ldx, X, L->ldx, p.dPg, powersP, dthetaP, p, st));
+  return POET_OK;
+}
+}  // namespace
+
+extern "C" {
+
+poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* powersR, const void* powersP, const void* X, const void* Z,
+                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return bwd_act(L, W0b, primR, primP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP, nullptr, nullptr, ws,
+                 ws_bytes, stream);
+}
+
+poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                      const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
+                                      float* dprimP, void* ws, size_t ws_bytes, void* stream) {
+  if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  return bwd_act(L, W0b, primR, primP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr, dprimR, dprimP, ws, ws_bytes,
+                 stream);
+}
+
+size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return 0;
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) need = std::max(need, poet_build_workspace_bytes(&sides[i], 1));
+  return need;
+}
+
+poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
+                                        float* const* prim, void* const* powers, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return g_last;
+  if (count == 0) return POET_OK;
+  if (!theta || !prim || !powers) return fail(POET_E_ARG, "null pointer table");
+  for (int i = 0; i < count; ++i) {
+    if (!prim[i]) return fail(POET_E_ARG, "null prim[%d]", i);
+    if (!theta[i] && S[i].theta_len > 0) return fail(POET_E_ARG, "null theta[%d]", i);
+    if (!powers[i] && S[i].k > 0) return fail(POET_E_ARG, "null powers[%d] (required when k >= 1)", i);
+  }
+  if (!check_ws(ws, ws_bytes, poet_build_group_workspace_bytes(count, sides))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // sides on the fused chain (and k = 0 sides, which need only I + Q) share launches; the rest build one by one
+  std::vector<int> grouped;
+  for (int i = 0; i < count; ++i) {
+    if (S[i].k == 0 || chain_side(S[i], powers[i])) grouped.push_back(i);
+    else if (poet_build_orthogonal(&sides[i], theta[i], prim[i], powers[i], nullptr, ws, ws_bytes, stream) != POET_OK)
+      return g_last;
+  }
+  for (size_t c0 = 0; c0 < grouped.size(); c0 += MAXG) {
+    const size_t c1 = std::min(grouped.size(), c0 + MAXG);
+    PrepGroup pg;
+    ChainGroup cg;
+    for (size_t u = c0; u < c1; ++u) {
+      const int i = grouped[u];
+      const SideInfo& T = S[i];
+      PrepSide& a = pg.s[pg.n++];
+      a.theta = theta[i]; a.prim = prim[i]; a.q = T.k > 0 ? powers[i] : nullptr; a.q_dt = T.dtype; a.ldq = T.ldp;
+      a.mode = T.mode; a.d = T.d; a.bp = T.bp; a.nprim = T.nprim; a.coef = T.k == 0 ? 1.f : 2.f;
+      if (T.k == 0) continue;
+      ChainArgs& c = cg.a[cg.n++];
+      c.bp = T.bp; c.nprim = T.nprim; c.steps = T.k; c.build = 1; c.prim = prim[i];
+      c.A = reinterpret_cast<const __bf16*>(powers[i]); c.sA = (int64_t)T.bp * T.bp;
+      c.Y = reinterpret_cast<__bf16*>(powers[i]); c.ldy = T.bp; c.sy = (int64_t)T.bp * T.bp; c.jstep = (int64_t)T.plen;
+    }
+    HIP_TRY(launch_theta_prep_group(pg, st));
+    HIP_TRY(launch_power_chain_group(cg, POET_K_CHAIN, st));
+  }
+  return POET_OK;
+}
+
+size_t poet_adjoint_group_workspace_bytes(int32_t count, const poet_side* sides) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return 0;
+  return adjoint_group_bytes(S, nullptr);
+}
+
+poet_status poet_adjoint_group(int32_t count, const poet_side* sides, const float* const* dprim,
+                               const void* const* powers, float* const* dtheta, void* ws, size_t ws_bytes,
+                               void* stream) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return g_last;
+  if (count == 0) return POET_OK;
+  if (!dprim || !powers || !dtheta) return fail(POET_E_ARG, "null pointer table");
+  for (int i = 0; i < count; ++i) {
+    if (S[i].theta_len == 0) continue;
+    if (!dprim[i] || !dtheta[i]) return fail(POET_E_ARG, "null dprim[%d] or dtheta[%d]", i, i);
+    if (!powers[i] && S[i].k > 0) return fail(POET_E_ARG, "null powers[%d] (required when k >= 1)", i);
+  }
+  if (!check_ws(ws, ws_bytes, adjoint_group_bytes(S, nullptr))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::vector<int> solo;
+  const auto chunks = adjoint_chunks(S, powers, &solo);
+  for (const auto& c : chunks) {
+    AdjChunkBufs b;
+    plan_adj_chunk(c, ws, &b);
+    HIP_TRY(adjoint_chunk(c, S, dprim, powers, dtheta, b, st));
+  }
+  for (int i : solo) {
+    AdjBufs b;
+    plan_adj_solo(S[i], ws, &b);
+    HIP_TRY(neumann_adjoint(S[i], dprim[i], powers[i], dtheta[i], b, st));
+  }
   return POET_OK;
 }
 

@@ -5,11 +5,15 @@
 //     the caller has written with the linear term exact from theta.
 //   the Neumann adjoint        X_0 = dR, so X_j = Q^j dR = H_j, written (bf16) side by side for j = 0..steps.
 // Q comes from the saved bf16 power Q (the caller's first saved power).
+// Several sides can share one launch (a table of up to MAXG sides, side = blockIdx.y), so that the blocks of all
+// the linears of a transformer block fill the machine together.
 // Column strips are independent (X_{j+1}[:, S] = Q X_j[:, S]), so one workgroup owns one 64-column strip of one
 // primitive through all steps: Q stays resident in LDS (bp x bp bf16, up to 128 KB), the strip lives transposed
 // in LDS (64 x bp bf16, 32 KB) and is overwritten by each new power after a barrier. Products run on
 // v_mfma_f32_32x32x16_bf16 with float32 accumulation; each power is rounded to bf16 before it feeds the next
 // product (as a bf16 operand would be).
+#include <algorithm>
+
 #include "strip_mma.h"
 
 namespace poet {
@@ -17,12 +21,25 @@ namespace {
 
 using namespace strip;
 
+// barrier for LDS hazards only: the global stores of the powers are left in flight (nothing here reads them back)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <bool BUILD>
-__global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
+__global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
   __shared__ __attribute__((aligned(16))) char smem[A_BYTES + X_BYTES];  // 160 KB
   char* Aq = smem;            // Q[i][k]
   char* Xs = smem + A_BYTES;  // X[k][n] stored as Xs[n][k]
+  ChainArgs c;
+  {
+    const ChainArgs& t = G.a[blockIdx.y];
+    c.bp = keep_s(t.bp); c.nprim = keep_s(t.nprim); c.steps = keep_s(t.steps); c.build = BUILD;
+    c.prim = keep_s(t.prim); c.A = keep_s(t.A); c.sA = keep_s(t.sA);
+    c.X0 = keep_s(t.X0); c.ldx0 = keep_s(t.ldx0); c.sx0 = keep_s(t.sx0);
+    c.Y = keep_s(t.Y); c.ldy = keep_s(t.ldy); c.sy = keep_s(t.sy); c.jstep = keep_s(t.jstep);
+    c.write_x0 = keep_s(t.write_x0);
+  }
   const int bp = c.bp, nstrips = (bp + SW - 1) / SW;
+  if ((int)blockIdx.x >= c.nprim * nstrips) return;
   const int p = blockIdx.x / nstrips, n0 = (blockIdx.x % nstrips) * SW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rowsA = min(MAXB, (bp + 63) / 64 * 64);  // rows the waves read
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
     f32x16 acc[2][2];
     zero(acc);
     if (wr < bp) mma_strip(Aq, Xs, wr, kpad, lane, acc);
-    __syncthreads();  // every wave is done reading the strip of X_{j-1}
+    lds_barrier();  // every wave is done reading the strip of X_{j-1}
     const bool last = j == c.steps;
     if (BUILD && last) {  // R_k = S + Q^{k+1}
 #pragma unroll
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainArgs c) {
           if (!last) *reinterpret_cast<bf16x4*>(Xs + loff(n, i0)) = v4;  // next operand (rows >= bp stay zero)
         }
       }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -151,14 +168,34 @@ bool power_chain_eligible(int bp, int dt, const void* A) {
   return dt == BF16 && bp > 0 && bp <= MAXB && bp % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0;
 }
 
-hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st) {
-  if (c.nprim <= 0 || c.steps <= 0) return hipSuccess;
-  const double flops = 2.0 * c.bp * (double)c.bp * c.bp * c.steps * c.nprim;
-  ProfScope prof(kclass, st, flops, (double)c.nprim * c.bp * c.bp * 2.0 * (c.steps + 2));
-  const int nstrips = (c.bp + SW - 1) / SW;
-  if (c.build) hipLaunchKernelGGL(power_chain_kernel<true>, dim3(c.nprim * nstrips), dim3(NT), 0, st, c);
-  else hipLaunchKernelGGL(power_chain_kernel<false>, dim3(c.nprim * nstrips), dim3(NT), 0, st, c);
+hipError_t launch_power_chain_group(const ChainGroup& g, int kclass, hipStream_t st) {
+  if (g.n <= 0 || g.n > MAXG) return g.n == 0 ? hipSuccess : hipErrorInvalidValue;
+  int gx = 0, build = -1;
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < g.n; ++i) {
+    const ChainArgs& c = g.a[i];
+    if (c.bp <= 0 || c.bp > MAXB) return hipErrorInvalidValue;
+    if (build >= 0 && build != c.build) return hipErrorInvalidValue;
+    build = c.build;
+    if (c.nprim <= 0 || c.steps <= 0) continue;
+    gx = std::max(gx, c.nprim * ((c.bp + SW - 1) / SW));
+    flops += 2.0 * c.bp * (double)c.bp * c.bp * c.steps * c.nprim;
+    bytes += (double)c.nprim * c.bp * c.bp * 2.0 * (c.steps + 2);
+  }
+  if (gx == 0) return hipSuccess;
+  ProfScope prof(kclass, st, flops, bytes);
+  // sides with fewer workgroups than the widest one leave the excess of their row of the grid at once
+  const dim3 grid(gx, g.n);
+  if (build) hipLaunchKernelGGL(power_chain_kernel<true>, grid, dim3(NT), 0, st, g);
+  else hipLaunchKernelGGL(power_chain_kernel<false>, grid, dim3(NT), 0, st, g);
   return hipGetLastError();
+}
+
+hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st) {
+  ChainGroup g;
+  g.n = 1;
+  g.a[0] = c;
+  return launch_power_chain_group(g, kclass, st);
 }
 
 }  // namespace poet

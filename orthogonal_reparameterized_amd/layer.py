@@ -119,6 +119,16 @@ class PoetLinear:
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
                               dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
 
+    def backward_act_prims(self, X, Z, dY, dX, stream=None):
+        """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
+        PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
+        if getattr(self, "dprimR", None) is None:
+            torch = _torch()
+            self.dprimR = torch.empty(B.poet_prim_len(self.L.R), dtype=torch.float32, device=self.dev)
+            self.dprimP = torch.empty(B.poet_prim_len(self.L.P), dtype=torch.float32, device=self.dev)
+        B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
+                                    self.ws, stream)
+
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
         when given, receives the merged W0 in the act dtype as well)."""
@@ -127,3 +137,36 @@ class PoetLinear:
                      self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch, self.ws, stream)
         if shadow is not None and self.W0b is not None:
             B.poet_weight_shadow(self.L, self.W0, self.W0b, stream)
+
+
+class PoetGroup:
+    """The per-block steps of several POET linears (e.g. the seven of a transformer block) in shared launches.
+
+    ``build`` runs the Cayley-Neumann build of both sides of every linear (poet_build_orthogonal_group);
+    ``finish_backward`` runs the Neumann adjoint and skew projection of every side from the primitive gradients
+    that ``PoetLinear.backward_act_prims`` left (poet_adjoint_group). Results match the per-linear calls."""
+
+    def __init__(self, linears):
+        torch = _torch()
+        self.linears = list(linears)
+        if not self.linears:
+            raise ValueError("PoetGroup needs at least one linear")
+        self.sides = [s for pl in self.linears for s in (pl.L.R, pl.L.P)]
+        dev = self.linears[0].dev
+        need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides))
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def build(self, stream=None):
+        thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]
+        prims = [t for pl in self.linears for t in (pl.primR, pl.primP)]
+        powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
+        B.poet_build_orthogonal_group(self.sides, thetas, prims, powers, self.ws, stream)
+
+    def finish_backward(self, stream=None):
+        for pl in self.linears:
+            if getattr(pl, "dprimR", None) is None:
+                raise RuntimeError("finish_backward needs backward_act_prims on every linear of the group first")
+        dprims = [t for pl in self.linears for t in (pl.dprimR, pl.dprimP)]
+        powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
+        dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]
+        B.poet_adjoint_group(self.sides, dprims, powers, dthetas, self.ws, stream)

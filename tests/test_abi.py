@@ -179,3 +179,36 @@ def test_act_path_rejects_bad_arguments():
     assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                   FAKE, wb - 1024, None) == B.POET_E_WORKSPACE
     assert lb.poet_weight_shadow(ctypes.byref(L), None, FAKE, None) == B.POET_E_ARG
+
+
+def test_group_calls_reject_bad_arguments():
+    lb = B.lib()
+    sides = [B.side(0, 512, 256, 5, 1), B.side(0, 384, 128, 4, 1), B.side(1, 300, 128, 3, 1)]
+    arr = (B.poet_side * 3)(*sides)
+    wb = B.poet_build_group_workspace_bytes(sides)
+    wa = B.poet_adjoint_group_workspace_bytes(sides)
+    # fused-chain sides with caller powers need no build scratch; the adjoint needs its H / C stacks
+    assert wb == 0 and wa > 0
+    # sides sharing (block, k) share one chunk: its scratch grows with the blocks it holds
+    assert B.poet_adjoint_group_workspace_bytes(sides[:1] * 4) > B.poet_adjoint_group_workspace_bytes(sides[:1])
+    assert lb.poet_build_group_workspace_bytes(-1, arr) == 0
+    bad = (B.poet_side * 1)(B.side(0, 64, 128, 3, 1))  # block larger than the side
+    assert lb.poet_build_group_workspace_bytes(1, bad) == 0
+    tab = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    nul = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert lb.poet_build_orthogonal_group(-1, arr, tab, tab, tab, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(0, None, None, None, None, None, 0, None) == B.POET_OK
+    assert lb.poet_build_orthogonal_group(3, arr, None, tab, tab, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, nul, tab, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, nul, None, 0, None) == B.POET_E_ARG  # powers for k >= 1
+    assert lb.poet_build_orthogonal_group(1, bad, tab, tab, tab, None, 0, None) == B.POET_E_SHAPE
+    assert lb.poet_adjoint_group(3, arr, tab, tab, nul, FAKE, wa, None) == B.POET_E_ARG
+    assert lb.poet_adjoint_group(3, arr, tab, nul, tab, FAKE, wa, None) == B.POET_E_ARG
+    assert lb.poet_adjoint_group(3, arr, tab, tab, tab, FAKE, wa - 1, None) == B.POET_E_WORKSPACE
+    assert lb.poet_adjoint_group(3, arr, tab, tab, tab, None, wa, None) == B.POET_E_ARG
+    L = _layer(act_dtype=1)
+    wbw = B.poet_workspace_bytes(L, B.POET_OP_BWD_ACT)
+    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                        wbw, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                        wbw - 1024, None) == B.POET_E_WORKSPACE

@@ -1,0 +1,172 @@
+"""GPU checks of the grouped calls through the C ABI: poet_build_orthogonal_group, poet_linear_bwd_act_prims and
+poet_adjoint_group.
+
+The grouped build runs the same per-block arithmetic as the one-side build, so its primitives and saved powers
+must equal those of poet_build_orthogonal bit for bit, for every kind of side (fused-chain sides that share the
+launches, and sides the group hands to the one-side path). The grouped adjoint is checked against the oracle's
+Neumann adjoint and skew projection on the same primitive gradients (bar: 1e-5 relative for float32 sides,
+2e-2 for bf16 sides), and a block of linears run with backward_act_prims + finish_backward must reproduce the
+per-linear backward (the adjoint's split-K summation order may differ, hence a 1e-5 relative bar rather than
+equality).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import poet_inputs as PI
+from tests.gpu_util import TOL, announce, make_linear, put_act, rel, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# (mode, d, b, k, dtype): fused-chain sides of several block sizes (one ragged), an FS side, and sides the group
+# leaves to the one-side path (float32, a block size that is not a multiple of 8) or that need no chain (k = 0)
+SIDES = [
+    (PI.MODE_BS, 520, 256, 5, PI.DT_BF16),
+    (PI.MODE_BS, 384, 128, 4, PI.DT_BF16),
+    (PI.MODE_BS, 200, 64, 3, PI.DT_BF16),
+    (PI.MODE_FS, 300, 128, 5, PI.DT_BF16),
+    (PI.MODE_BS, 200, 64, 3, PI.DT_F32),
+    (PI.MODE_BS, 300, 100, 2, PI.DT_BF16),
+    (PI.MODE_BS, 256, 64, 0, PI.DT_BF16),
+]
+
+
+def _sides():
+    from orthogonal_reparameterized_amd import binding as B
+    return [B.side(*s) for s in SIDES]
+
+
+def _thetas(std, seed=5):
+    rng = np.random.default_rng(seed)
+    out = []
+    for mode, d, b, k, dt in SIDES:
+        n = PI.n_theta(PI.SideSpec(mode, d, b, k, dt))
+        out.append((rng.standard_normal(n) * std).astype(np.float32))
+    return out
+
+
+def _alloc(s):
+    from orthogonal_reparameterized_amd import binding as B
+    dt = torch.bfloat16 if s.dtype == B.POET_BF16 else torch.float32
+    prim = torch.zeros(B.poet_prim_len(s), dtype=torch.float32, device="cuda")
+    powers = torch.zeros(max(B.poet_powers_len(s), 1), dtype=dt, device="cuda") if s.k > 0 else None
+    return prim, powers
+
+
+def _build_all(sides, thetas_d, grouped):
+    from orthogonal_reparameterized_amd import binding as B
+    bufs = [_alloc(s) for s in sides]
+    if grouped:
+        B.poet_build_orthogonal_group(sides, thetas_d, [b[0] for b in bufs], [b[1] for b in bufs])
+    else:
+        for s, th, (prim, pw) in zip(sides, thetas_d, bufs):
+            B.poet_build_orthogonal(s, th, prim, pw)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def test_build_group_equals_one_side_builds():
+    announce("group build vs one-side builds")
+    sides = _sides()
+    thetas_d = [torch.from_numpy(t).cuda() for t in _thetas(0.02)]
+    single = _build_all(sides, thetas_d, grouped=False)
+    group = _build_all(sides, thetas_d, grouped=True)
+    for i, ((pa, wa), (pb, wb)) in enumerate(zip(single, group)):
+        assert torch.equal(pa, pb), f"prim of side {i} {SIDES[i]}"
+        if wa is not None:
+            assert torch.equal(wa, wb), f"powers of side {i} {SIDES[i]}"
+
+
+def _oracle_dtheta(side_spec, theta, dprim):
+    mode, d, b, k, dt = side_spec
+    out, off = [], 0
+    for p, c in enumerate(O.block_sizes(mode, d, b)):
+        nt = c * (c - 1) // 2
+        Q = O.skew_from_theta(theta[off:off + nt].astype(np.float64), c)
+        dR = dprim[p * b * b:(p + 1) * b * b].reshape(b, b)[:c, :c].astype(np.float64)
+        out.append(O.skew_project(O.neumann_adjoint(Q, dR, k)))
+        off += nt
+    return np.concatenate(out) if out else np.zeros(0)
+
+
+@pytest.mark.parametrize("std", [1e-3, 0.02])
+def test_adjoint_group_against_oracle(std):
+    from orthogonal_reparameterized_amd import binding as B
+    announce(f"group adjoint vs oracle theta std {std}")
+    sides = _sides()
+    thetas = _thetas(std, seed=7)
+    thetas_d = [torch.from_numpy(t).cuda() for t in thetas]
+    bufs = _build_all(sides, thetas_d, grouped=True)
+    rng = np.random.default_rng(11)
+    dprims, dprims_d, dthetas_d = [], [], []
+    for spec, s in zip(SIDES, sides):
+        g = rng.standard_normal(B.poet_prim_len(s)).astype(np.float32)
+        dprims.append(g)
+        dprims_d.append(torch.from_numpy(g).cuda())
+        dthetas_d.append(torch.full((max(B.poet_theta_len(s), 1),), float("nan"), device="cuda"))
+    B.poet_adjoint_group(sides, dprims_d, [b[1] for b in bufs], dthetas_d)
+    torch.cuda.synchronize()
+    for i, spec in enumerate(SIDES):
+        n = B.poet_theta_len(sides[i])
+        ref = _oracle_dtheta(spec, thetas[i], dprims[i])
+        err = rel(to_np(dthetas_d[i])[:n], ref)
+        announce(f"side {spec}: rel {err:.3e}")
+        assert err <= TOL[spec[4]], (spec, err)
+
+
+def test_block_backward_grouped_matches_per_linear():
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
+    announce("grouped block backward vs per-linear backward")
+    specs = [make_linear("q", 520, 384, 300, PI.MODE_BS, 256, 128, 5, PI.DT_BF16, linear_id=0),
+             make_linear("gate", 600, 520, 300, PI.MODE_BS, 256, 256, 5, PI.DT_BF16, linear_id=4),
+             make_linear("small", 256, 192, 300, PI.MODE_BS, 64, 48, 3, PI.DT_BF16, linear_id=2)]
+    lins, acts, refs = [], [], []
+    for lin in specs:
+        W0, tR, tP, X, dY = PI.gen_linear(98, 0, lin, theta_std=0.01)
+        pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
+                        linear_id=lin.linear_id, path="act")
+        lins.append(pl)
+        Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+        acts.append((Xd, dYd, pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldy),
+                     pl.alloc_act(lin.T, pl.L.ldx)))
+        sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+        refs.append(O.linear_bwd(sR, sP, W0, tR, tP, None, None, X, dY))
+    group = PoetGroup(lins)
+    # per-linear build and backward
+    for pl, (Xd, dYd, Y, Z, dX) in zip(lins, acts):
+        pl.build()
+        pl.forward_act(Xd, Y, Z)
+        pl.backward_act(Xd, Z, dYd, dX)
+    torch.cuda.synchronize()
+    per = [(pl.primR.clone(), pl.primP.clone(), pl.dthetaR.clone(), pl.dthetaP.clone(), a[4].clone())
+           for pl, a in zip(lins, acts)]
+    # grouped build, per-linear backward to the primitive gradients, grouped adjoint
+    for pl in lins:
+        pl.dthetaR.fill_(float("nan"))
+        pl.dthetaP.fill_(float("nan"))
+    group.build()
+    for pl, (Xd, dYd, Y, Z, dX) in zip(lins, acts):
+        pl.forward_act(Xd, Y, Z)
+        pl.backward_act_prims(Xd, Z, dYd, dX)
+    group.finish_backward()
+    torch.cuda.synchronize()
+    for pl, lin, a, p, ref in zip(lins, specs, acts, per, refs):
+        assert torch.equal(pl.primR, p[0]) and torch.equal(pl.primP, p[1]), lin.name
+        assert torch.equal(a[4], p[4]), lin.name  # dX does not depend on the grouping
+        nR, nP = B.poet_theta_len(pl.L.R), B.poet_theta_len(pl.L.P)
+        eR = rel(to_np(pl.dthetaR)[:nR], to_np(p[2])[:nR])
+        eP = rel(to_np(pl.dthetaP)[:nP], to_np(p[3])[:nP])
+        oR = rel(to_np(pl.dthetaR)[:nR], ref["dthetaR"])
+        oP = rel(to_np(pl.dthetaP)[:nP], ref["dthetaP"])
+        announce(f"{lin.name}: grouped vs per-linear {eR:.2e} {eP:.2e}; vs oracle {oR:.2e} {oP:.2e}")
+        assert eR <= 1e-5 and eP <= 1e-5, (lin.name, eR, eP)
+        assert oR <= TOL[PI.DT_BF16] and oP <= TOL[PI.DT_BF16], (lin.name, oR, oP)
