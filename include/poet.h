@@ -170,16 +170,22 @@ int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below app
 /* W0_shadow [m x ldw] act dtype out: W0 rounded to the act dtype (round to nearest even). */
 poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream);
 
+/* opsR/opsP (nullable, bf16 in): operand copies of the primitives, 2 * poet_prim_len(side) elements: block p
+ * of F at offset p*bp*bp (row-major, F(i, j) at i*bp + j) and its transpose at num_prims*bp*bp + p*bp*bp, both
+ * zero outside the block's c x c corner; poet_build_orthogonal_group writes them. NULL: the call makes them
+ * in its workspace from primR/primP. */
+
 /* X [T x ldx] in, Y [T x ldy] out, Z [T x ldy] out: X P^T W0^T, kept for the backward (all bf16). */
 poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream);
+                                const void* opsR, const void* opsP, const void* X, void* Y, void* Z, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* X [T x ldx], Z [T x ldy] (from the forward), dY [T x ldy] in; dX [T x ldx] out, nullable; dthetaR, dthetaP
  * float32 out (overwritten). powersR/powersP as in poet_linear_bwd. */
 poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* powersR, const void* powersP, const void* X, const void* Z,
-                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws,
-                                size_t ws_bytes, void* stream);
+                                const void* opsR, const void* opsP, const void* powersR, const void* powersP,
+                                const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
+                                float* dthetaP, void* ws, size_t ws_bytes, void* stream);
 
 /* As poet_linear_bwd_act, but it stops at the primitive gradients and leaves the Neumann adjoint to
  * poet_adjoint_group, so that the adjoints of many linears run together:
@@ -187,8 +193,9 @@ poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const floa
  *   dY^T Z) and dL/dP (blocks of dX'^T X); entries outside a ragged last block's extent are zero.
  * Workspace: POET_OP_BWD_ACT. */
 poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                      const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
-                                      float* dprimP, void* ws, size_t ws_bytes, void* stream);
+                                      const void* opsR, const void* opsP, const void* X, const void* Z,
+                                      const void* dY, void* dX, float* dprimR, float* dprimP, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /* ---- grouped calls ------------------------------------------------------------------------------------
  * The per-block steps of many sides (for instance both sides of every linear of a transformer block) in shared
@@ -197,11 +204,13 @@ poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, cons
  * those of the one-side calls (the adjoint's split-K summation order may differ). */
 
 /* poet_build_orthogonal for count sides (no qnorm). powers[i] is required for every side with k >= 1.
+ * ops: nullable table; where ops[i] is non-NULL (BS sides only) it receives the bf16 operand copies of side i's
+ * primitives that the activation-side calls take (layout above poet_linear_fwd_act).
  * ws: at least poet_build_group_workspace_bytes(count, sides) bytes (may be NULL when that is 0). */
 size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides);
 poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
-                                        float* const* prim, void* const* powers, void* ws, size_t ws_bytes,
-                                        void* stream);
+                                        float* const* prim, void* const* powers, void* const* ops, void* ws,
+                                        size_t ws_bytes, void* stream);
 
 /* The Neumann adjoint and skew projection of count sides (the last step of the backward to the skew
  * parameters, Approach section): dprim[i] float32 in (poet_linear_bwd_act_prims), powers[i] the saved powers

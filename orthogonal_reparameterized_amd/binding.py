@@ -95,12 +95,12 @@ def lib() -> ctypes.CDLL:
     L.poet_merge.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, U64, U32, U32, VP, S, VP]
     L.poet_act_path_supported.argtypes = [P(poet_layer)]
     L.poet_weight_shadow.argtypes = [P(poet_layer), VP, VP, VP]
-    L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
-    L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
-    L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_build_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_build_group_workspace_bytes.restype = S
-    L.poet_build_orthogonal_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_build_orthogonal_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), VP, S, VP]
     L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
@@ -330,13 +330,19 @@ def poet_weight_shadow(L: poet_layer, W0, W0_shadow, stream=None):
     _check(st, "poet_weight_shadow")
 
 
-def poet_linear_fwd_act(L: poet_layer, W0b, primR, primP, X, Y, Z, ws=None, stream=None):
+def _ops(t, name, s: poet_side):
+    """Operand copies of a side's primitives (2 * prim_len bf16), or None."""
+    return _ptr(t, name, 4 * poet_prim_len(s), "bfloat16", allow_none=True)
+
+
+def poet_linear_fwd_act(L: poet_layer, W0b, primR, primP, X, Y, Z, ws=None, stream=None, opsR=None, opsP=None):
     b = _layer_bytes(L)
     act = _dt_name(L.act_dtype)
     need = poet_workspace_bytes(L, POET_OP_FWD_ACT)
     st = lib().poet_linear_fwd_act(
         ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
         _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ops(opsR, "opsR", L.R), _ops(opsP, "opsP", L.P),
         _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Y, "Y", b["Y"], act, allow_none=L.T == 0),
         _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0), _ptr(ws, "ws", need, allow_none=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
@@ -344,13 +350,14 @@ def poet_linear_fwd_act(L: poet_layer, W0b, primR, primP, X, Y, Z, ws=None, stre
 
 
 def poet_linear_bwd_act(L: poet_layer, W0b, primR, primP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP,
-                        ws=None, stream=None):
+                        ws=None, stream=None, opsR=None, opsP=None):
     b = _layer_bytes(L)
     act = _dt_name(L.act_dtype)
     need = poet_workspace_bytes(L, POET_OP_BWD_ACT)
     st = lib().poet_linear_bwd_act(
         ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
         _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ops(opsR, "opsR", L.R), _ops(opsP, "opsP", L.P),
         _ptr(powersR, "powersR", poet_powers_len(L.R) * _esz(L.R.dtype), _dt_name(L.R.dtype), allow_none=True),
         _ptr(powersP, "powersP", poet_powers_len(L.P) * _esz(L.P.dtype), _dt_name(L.P.dtype), allow_none=True),
         _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0),
@@ -361,13 +368,15 @@ def poet_linear_bwd_act(L: poet_layer, W0b, primR, primP, powersR, powersP, X, Z
     _check(st, "poet_linear_bwd_act")
 
 
-def poet_linear_bwd_act_prims(L: poet_layer, W0b, primR, primP, X, Z, dY, dX, dprimR, dprimP, ws=None, stream=None):
+def poet_linear_bwd_act_prims(L: poet_layer, W0b, primR, primP, X, Z, dY, dX, dprimR, dprimP, ws=None, stream=None,
+                              opsR=None, opsP=None):
     b = _layer_bytes(L)
     act = _dt_name(L.act_dtype)
     need = poet_workspace_bytes(L, POET_OP_BWD_ACT)
     st = lib().poet_linear_bwd_act_prims(
         ctypes.byref(L), _ptr(W0b, "W0b", b["W"], act),
         _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ops(opsR, "opsR", L.R), _ops(opsP, "opsP", L.P),
         _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0),
         _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0), _ptr(dX, "dX", b["X"], act, allow_none=True),
         _ptr(dprimR, "dprimR", 4 * poet_prim_len(L.R), "float32"),
@@ -399,11 +408,12 @@ def poet_adjoint_group_workspace_bytes(sides) -> int:
     return int(lib().poet_adjoint_group_workspace_bytes(len(sides), _side_array(sides)))
 
 
-def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=None):
-    """poet_build_orthogonal for every side in ``sides`` (lists of equal length; powers required for k >= 1)."""
+def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=None, ops=None):
+    """poet_build_orthogonal for every side in ``sides`` (lists of equal length; powers required for k >= 1);
+    ``ops`` (optional list, entries may be None) receives the bf16 operand copies of the BS sides' primitives."""
     n = len(sides)
-    if not (len(thetas) == len(prims) == len(powers) == n):
-        raise ValueError("sides, thetas, prims and powers must have the same length")
+    if not (len(thetas) == len(prims) == len(powers) == n) or (ops is not None and len(ops) != n):
+        raise ValueError("sides, thetas, prims, powers (and ops) must have the same length")
     need = poet_build_group_workspace_bytes(sides)
     if ws is None and need > 0:
         ws = _torch().empty(need, dtype=_torch().uint8, device=prims[0].device)
@@ -414,7 +424,9 @@ def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=No
     pw = _ptr_table(powers, [f"powers[{i}]" for i in range(n)],
                     [poet_powers_len(s) * _esz(s.dtype) for s in sides], [_dt_name(s.dtype) for s in sides],
                     [s.k == 0 for s in sides])
-    st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, _ptr(ws, "ws", need, allow_none=True),
+    op = None if ops is None else _ptr_table(ops, [f"ops[{i}]" for i in range(n)],
+                                             [4 * poet_prim_len(s) for s in sides], ["bfloat16"] * n, [True] * n)
+    st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, op, _ptr(ws, "ws", need, allow_none=True),
                                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_build_orthogonal_group")
 

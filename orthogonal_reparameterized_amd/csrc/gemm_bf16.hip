@@ -247,7 +247,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     tm = GM * sr + r2 / w;
     tn = gi * GN + r2 % w;
   }
-  const int s = zs % splits, zg = zs / splits;  // zg: batch entry over both problems (indexes the partials)
+  // zg: batch entry over both problems (indexes the partials). With one tile per batch entry (the token-axis
+  // contractions, one bp x bp block each) the entries of one K range are adjacent, so the workgroups an XCD runs
+  // together read whole rows of the token-major operands rather than one block's columns of many rows
+  const bool zfast = ntm * ntn == 1;
+  const int s = zfast ? zs / g.batch : zs % splits, zg = zfast ? zs % g.batch : zs / splits;
   int z = zg;
   const char* Ab = reinterpret_cast<const char*>(g.A);
   const char* Bb = reinterpret_cast<const char*>(g.B);

@@ -65,6 +65,11 @@ struct ChainArgs {
   const float* X0 = nullptr; int64_t ldx0 = 0, sx0 = 0;
   __bf16* Y = nullptr; int64_t ldy = 0, sy = 0, jstep = 0;
   int write_x0 = 0;
+  // build only, nullable: bf16 copies of the finished primitives for the activation-side products, zero outside
+  // each block's c x c corner (c = min(bp, d - p bp) for BS, bp for FS): ops[p][i][j] = R_p(i, j) and, at offset
+  // nprim bp^2, ops[p][j][i] (the transpose)
+  __bf16* ops = nullptr;
+  int d = 0, mode = 0;
 };
 bool power_chain_eligible(int bp, int dt, const void* A);  // A: the power/Q buffer (16-byte aligned)
 hipError_t launch_power_chain(const ChainArgs& c, int kclass, hipStream_t st);

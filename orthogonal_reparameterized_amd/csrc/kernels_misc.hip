@@ -284,10 +284,11 @@ __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
   return dt == BF16 ? (float)reinterpret_cast<const __bf16*>(p)[i] : reinterpret_cast<const float*>(p)[i];
 }
 
-// element (p, j, r, c) of the stacked coefficient matrices; see launch_adjoint_coefs
-// Block j of primitive p (blockIdx.y = p (k+1) + j) of side blockIdx.z, stored ldp x ldp (rows and columns past bp
-// zero); thread x covers VEC consecutive elements of it (32-bit index math). Powers are bp x ldp blocks.
-template <typename T, int VEC>
+// The stacked coefficient matrices C_0..C_k of primitive p = blockIdx.y of side blockIdx.z (see launch_adjoint_coefs),
+// each stored ldp x ldp (rows and columns past bp zero). Thread x covers VEC consecutive elements (r, c0..c0+VEC) of
+// every C_j: it reads the k saved powers at those elements once (powers are bp x ldp blocks) and writes the k + 1
+// coefficient blocks from registers. KMAX bounds k (unrolled, so the powers stay in registers).
+template <typename T, int VEC, int KMAX>
 __global__ void k_adjoint_coefs(const CoefGroup G) {
   CoefSide sd;
   {
@@ -295,36 +296,53 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
     sd.powers = keep_s(t.powers); sd.out = keep_s(t.out); sd.nprim = keep_s(t.nprim);
   }
   const int nprim = sd.nprim, bp = G.bp, ldp = G.ldp, k = G.k;
-  if ((int)blockIdx.y >= nprim * (k + 1)) return;
+  const int p = blockIdx.y;
+  if (p >= nprim) return;
   const T* __restrict__ powers = reinterpret_cast<const T*>(sd.powers);
   T* __restrict__ out = reinterpret_cast<T*>(sd.out);
   const int pq = ldp * ldp;
   const int rc0 = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
   if (rc0 >= pq) return;
-  const int p = blockIdx.y / (k + 1), j = blockIdx.y - p * (k + 1);
   const int r = rc0 / ldp, c0 = rc0 - r * ldp;  // VEC divides ldp: the VEC elements share the row
-  float v[VEC];
+  float q[KMAX][VEC];  // q[t-1] = Q^t at this thread's elements
 #pragma unroll
-  for (int u = 0; u < VEC; ++u) v[u] = 0.f;
-  if (r < bp) {
-    if (j > 0) {  // t = 0 term: a_{j+1} (-1)^j I
-      const float a = (j + 1 <= k ? 2.f : 1.f) * ((j & 1) ? -1.f : 1.f);
+  for (int t = 1; t <= KMAX; ++t) {
 #pragma unroll
-      for (int u = 0; u < VEC; ++u)
-        if (c0 + u == r) v[u] = a;
-    }
-    for (int t = 1; t <= k - j; ++t) {
-      const int i = t + j + 1;
-      const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
+    for (int u = 0; u < VEC; ++u) q[t - 1][u] = 0.f;
+    if (t <= k && r < bp) {
       const T* src = powers + ((size_t)(t - 1) * nprim + p) * bp * ldp + (size_t)r * ldp + c0;
 #pragma unroll
       for (int u = 0; u < VEC; ++u)
-        if (c0 + u < bp) v[u] += a * (float)src[u];
+        if (c0 + u < bp) q[t - 1][u] = (float)src[u];
     }
   }
-  T* dst = out + ((size_t)p * (k + 1) + j) * pq + rc0;
+  // C_j = [j > 0] a_{j+1} (-1)^j I + sum_{t=1}^{k-j} a_{t+j+1} (-1)^{t+j} Q^t, with a_i = 2 (i <= k), a_{k+1} = 1
 #pragma unroll
-  for (int u = 0; u < VEC; ++u) dst[u] = (T)v[u];
+  for (int j = 0; j <= KMAX; ++j) {
+    if (j > k) break;
+    float v[VEC];
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) v[u] = 0.f;
+    if (r < bp) {
+      if (j > 0) {
+        const float a = (j + 1 <= k ? 2.f : 1.f) * ((j & 1) ? -1.f : 1.f);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+          if (c0 + u == r) v[u] = a;
+      }
+#pragma unroll
+      for (int t = 1; t <= KMAX; ++t) {
+        if (t > k - j) break;
+        const int i = t + j + 1;
+        const float a = (i <= k ? 2.f : 1.f) * (((t + j) & 1) ? -1.f : 1.f);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) v[u] += a * q[t - 1][u];
+      }
+    }
+    T* dst = out + ((size_t)p * (k + 1) + j) * pq + rc0;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) dst[u] = (T)v[u];
+  }
 }
 
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
@@ -373,25 +391,30 @@ hipError_t launch_adjoint_coefs_group(const CoefGroup& g, int dt, hipStream_t st
   if (g.n <= 0) return hipSuccess;
   if (g.n > MAXG) return hipErrorInvalidValue;
   const int ldp = g.ldp, k = g.k, pq = ldp * ldp;
+  if (k < 1 || k > 16) return hipErrorInvalidValue;
   int ny = 0;
   double total = 0;
   for (int i = 0; i < g.n; ++i) {
-    ny = std::max(ny, g.s[i].nprim * (k + 1));
-    total += (double)g.s[i].nprim * (k + 1) * pq;
+    ny = std::max(ny, g.s[i].nprim);
+    total += (double)g.s[i].nprim * pq;
   }
   if (total == 0) return hipSuccess;
   if ((int64_t)ldp * ldp > (1 << 30) || ny > 65535) return hipErrorInvalidValue;
-  ProfScope prof(7, st, 0, total * dtype_size(dt) * 2);
+  ProfScope prof(7, st, 0, total * dtype_size(dt) * (2 * k + 1));
+#define POET_COEF(T_, V_, KM_)                                                                          \
+  hipLaunchKernelGGL((k_adjoint_coefs<T_, V_, KM_>), dim3((pq / V_ + kThreads - 1) / kThreads, ny, g.n), \
+                     dim3(kThreads), 0, st, g)
   if (dt == BF16 && ldp % 4 == 0) {
-    const dim3 grid((pq / 4 + kThreads - 1) / kThreads, ny, g.n);
-    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 4>), grid, dim3(kThreads), 0, st, g);
+    if (k <= 8) POET_COEF(__bf16, 4, 8);
+    else POET_COEF(__bf16, 4, 16);
   } else if (dt == BF16) {
-    const dim3 grid((pq + kThreads - 1) / kThreads, ny, g.n);
-    hipLaunchKernelGGL((k_adjoint_coefs<__bf16, 1>), grid, dim3(kThreads), 0, st, g);
+    if (k <= 8) POET_COEF(__bf16, 1, 8);
+    else POET_COEF(__bf16, 1, 16);
   } else {
-    const dim3 grid((pq + kThreads - 1) / kThreads, ny, g.n);
-    hipLaunchKernelGGL((k_adjoint_coefs<float, 1>), grid, dim3(kThreads), 0, st, g);
+    if (k <= 8) POET_COEF(float, 1, 8);
+    else POET_COEF(float, 1, 16);
   }
+#undef POET_COEF
   return hipGetLastError();
 }
 

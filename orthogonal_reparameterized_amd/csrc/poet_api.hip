@@ -546,18 +546,21 @@ hipError_t prims_bf16(const SideInfo& S, const float* prim, __bf16* out, hipStre
   return launch_convert(prim, S.bp, out, S.bp, BF16, S.nprim * S.bp, S.bp, st);
 }
 
-// out = in F^T (trans) or in F over the blocks of side S: the weight-stationary kernel where it applies (its bf16
-// operand rows written to Fb first), else a batched GEMM on a bf16 copy of the primitives (in Fb)
-hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, const float* prim, __bf16* Fb, bool trans,
-                      void* out, int64_t ldo, hipStream_t st) {
+// out = in F^T (trans) or in F over the blocks of side S: the weight-stationary kernel where it applies, else a
+// batched GEMM. Its bf16 operand comes from ops (the caller's copies of F and F^T, zero outside each block's
+// corner) or is written to the scratch Fb first.
+hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, const float* prim, const void* ops,
+                      __bf16* Fb, bool trans, void* out, int64_t ldo, hipStream_t st) {
   hipError_t e;
+  const __bf16* opsF = reinterpret_cast<const __bf16*>(ops);
   if (act_apply_eligible(S.bp, in, ldi, out, ldo, T)) {
-    if ((e = launch_act_operand(prim, S.bp, S.d, S.nprim, trans, Fb, st)) != hipSuccess) return e;
-    return launch_act_apply(reinterpret_cast<const __bf16*>(in), ldi, reinterpret_cast<__bf16*>(out), ldo, Fb, T,
+    const __bf16* Bt = opsF ? opsF + (trans ? 0 : S.prim_len) : Fb;  // rows Bt[j][k] = B(k, j)
+    if (!opsF && (e = launch_act_operand(prim, S.bp, S.d, S.nprim, trans, Fb, st)) != hipSuccess) return e;
+    return launch_act_apply(reinterpret_cast<const __bf16*>(in), ldi, reinterpret_cast<__bf16*>(out), ldo, Bt, T,
                             S.d, S.bp, S.nprim, st);
   }
-  if ((e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
-  return launch_gemm(act_apply(S, T, in, ldi, Fb, trans, out, ldo), st);
+  if (!opsF && (e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
+  return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF : Fb, trans, out, ldo), st);
 }
 
 struct MergePlan {
@@ -1039,7 +1042,8 @@ poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_sh
 }
 
 poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream) {
+                                const void* opsR, const void* opsP, const void* X, void* Y, void* Z, void* ws,
+                                size_t ws_bytes, void* stream) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
   if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
@@ -1051,7 +1055,7 @@ poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const floa
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (L->T == 0) return POET_OK;
   const int T = L->T;
-  HIP_TRY(act_factor(P, T, X, L->ldx, primP, p.Pb, true, p.Xp, L->ldx, st));  // X' = X P^T
+  HIP_TRY(act_factor(P, T, X, L->ldx, primP, opsP, p.Pb, true, p.Xp, L->ldx, st));  // X' = X P^T
   {  // Z = X' W0^T
     GemmDesc g;
     g.kclass = POET_K_TOKEN_FWD;
@@ -1061,7 +1065,7 @@ poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const floa
     g.C = Z; g.ldc = L->ldy; g.c_dt = BF16;
     HIP_TRY(launch_gemm(g, st));
   }
-  HIP_TRY(act_factor(R, T, Z, L->ldy, primR, p.Rb, true, Y, L->ldy, st));  // Y = Z R^T
+  HIP_TRY(act_factor(R, T, Z, L->ldy, primR, opsR, p.Rb, true, Y, L->ldy, st));  // Y = Z R^T
   return POET_OK;
 }
 
@@ -1069,7 +1073,8 @@ poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const floa
 
 namespace {
 // the activation-side backward; with dprimR/dprimP given it stops at the primitive gradients
-poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP, const void* powersR,
+poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP, const void* opsR,
+                    const void* opsP, const void* powersR,
                     const void* powersP, const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
                     float* dthetaP, float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream) {
   SideInfo R, P;
@@ -1091,7 +1096,7 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int T = L->T;
   if (T > 0) {
-    HIP_TRY(act_factor(R, T, dY, L->ldy, primR, p.Rb, false, p.dZ, L->ldy, st));  // dZ = dY R
+    HIP_TRY(act_factor(R, T, dY, L->ldy, primR, opsR, p.Rb, false, p.dZ, L->ldy, st));  // dZ = dY R
     {  // dX' = dZ W0
       GemmDesc g;
       g.kclass = POET_K_TOKEN_DX;
@@ -1101,7 +1106,7 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
       g.C = p.dXp; g.ldc = L->ldx; g.c_dt = BF16;
       HIP_TRY(launch_gemm(g, st));
     }
-    if (dX) HIP_TRY(act_factor(P, T, p.dXp, L->ldx, primP, p.Pb, false, dX, L->ldx, st));  // dX = dX' P
+    if (dX) HIP_TRY(act_factor(P, T, p.dXp, L->ldx, primP, opsP, p.Pb, false, dX, L->ldx, st));  // dX = dX' P
   }
   // primitive blocks of dL/dR = dY^T Z and dL/dP = dX'^T X (zero when T == 0), then the adjoint; the two
   // contractions share one launch when their shapes allow
@@ -1134,19 +1139,20 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
 extern "C" {
 
 poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* powersR, const void* powersP, const void* X, const void* Z,
-                                const void* dY, void* dX, float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes,
-                                void* stream) {
-  return bwd_act(L, W0b, primR, primP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP, nullptr, nullptr, ws,
-                 ws_bytes, stream);
+                                const void* opsR, const void* opsP, const void* powersR, const void* powersP,
+                                const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
+                                float* dthetaP, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_act(L, W0b, primR, primP, opsR, opsP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP, nullptr, nullptr,
+                 ws, ws_bytes, stream);
 }
 
 poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                      const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
-                                      float* dprimP, void* ws, size_t ws_bytes, void* stream) {
+                                      const void* opsR, const void* opsP, const void* X, const void* Z,
+                                      const void* dY, void* dX, float* dprimR, float* dprimP, void* ws,
+                                      size_t ws_bytes, void* stream) {
   if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
-  return bwd_act(L, W0b, primR, primP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr, dprimR, dprimP, ws, ws_bytes,
-                 stream);
+  return bwd_act(L, W0b, primR, primP, opsR, opsP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr, dprimR, dprimP,
+                 ws, ws_bytes, stream);
 }
 
 size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
@@ -1158,8 +1164,8 @@ size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
 }
 
 poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
-                                        float* const* prim, void* const* powers, void* ws, size_t ws_bytes,
-                                        void* stream) {
+                                        float* const* prim, void* const* powers, void* const* ops, void* ws,
+                                        size_t ws_bytes, void* stream) {
   std::vector<SideInfo> S;
   if (!group_sides(count, sides, &S)) return g_last;
   if (count == 0) return POET_OK;
@@ -1168,13 +1174,16 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     if (!prim[i]) return fail(POET_E_ARG, "null prim[%d]", i);
     if (!theta[i] && S[i].theta_len > 0) return fail(POET_E_ARG, "null theta[%d]", i);
     if (!powers[i] && S[i].k > 0) return fail(POET_E_ARG, "null powers[%d] (required when k >= 1)", i);
+    if (ops && ops[i] && S[i].mode != POET_BS) return fail(POET_E_ARG, "ops[%d] given for an FS side", i);
   }
   if (!check_ws(ws, ws_bytes, poet_build_group_workspace_bytes(count, sides))) return g_last;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // sides on the fused chain (and k = 0 sides, which need only I + Q) share launches; the rest build one by one
   std::vector<int> grouped;
+  auto side_ops = [&](int i) -> __bf16* { return ops ? reinterpret_cast<__bf16*>(ops[i]) : nullptr; };
   for (int i = 0; i < count; ++i) {
-    if (S[i].k == 0 || chain_side(S[i], powers[i])) grouped.push_back(i);
+    if (chain_side(S[i], powers[i])) { grouped.push_back(i); continue; }  // the chain also writes the ops
+    if (S[i].k == 0) grouped.push_back(i);
     else if (poet_build_orthogonal(&sides[i], theta[i], prim[i], powers[i], nullptr, ws, ws_bytes, stream) != POET_OK)
       return g_last;
   }
@@ -1193,9 +1202,17 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
       c.bp = T.bp; c.nprim = T.nprim; c.steps = T.k; c.build = 1; c.prim = prim[i];
       c.A = reinterpret_cast<const __bf16*>(powers[i]); c.sA = (int64_t)T.bp * T.bp;
       c.Y = reinterpret_cast<__bf16*>(powers[i]); c.ldy = T.bp; c.sy = (int64_t)T.bp * T.bp; c.jstep = (int64_t)T.plen;
+      c.ops = side_ops(i); c.d = T.d; c.mode = T.mode;
     }
     HIP_TRY(launch_theta_prep_group(pg, st));
     HIP_TRY(launch_power_chain_group(cg, POET_K_CHAIN, st));
+  }
+  // the operand copies of sides the chain did not finish (k = 0, or built one by one)
+  for (int i = 0; i < count; ++i) {
+    __bf16* o = side_ops(i);
+    if (!o || chain_side(S[i], powers[i])) continue;
+    HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, true, o, st));
+    HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, false, o + S[i].prim_len, st));
   }
   return POET_OK;
 }

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
     c.X0 = keep_s(t.X0); c.ldx0 = keep_s(t.ldx0); c.sx0 = keep_s(t.sx0);
     c.Y = keep_s(t.Y); c.ldy = keep_s(t.ldy); c.sy = keep_s(t.sy); c.jstep = keep_s(t.jstep);
     c.write_x0 = keep_s(t.write_x0);
+    c.ops = keep_s(t.ops); c.d = keep_s(t.d); c.mode = keep_s(t.mode);
   }
   const int bp = c.bp, nstrips = (bp + SW - 1) / SW;
   if ((int)blockIdx.x >= c.nprim * nstrips) return;
@@ -127,15 +128,51 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
     lds_barrier();  // every wave is done reading the strip of X_{j-1}
     const bool last = j == c.steps;
     if (BUILD && last) {  // R_k = S + Q^{k+1}
+      // The finished strip leaves through LDS (both regions are free: every wave is past its last product):
+      // float32 rows [i][n] (pitch RP floats: the two half-waves of a write land in different banks) in the Q
+      // region, and, for the operand copies, the bf16 strip transposed in the strip buffer. Then every store to
+      // global memory is a coalesced 16-byte chunk.
+      constexpr int RP = 72;
+      float* Rs = reinterpret_cast<float*>(Aq);
+      const int cb = c.mode == 1 ? bp : min(bp, c.d - p * bp);  // the block's size (zero outside it in ops)
+      const bool ops = c.ops != nullptr;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int i = acc_row(wr, a, r, lane), gn = n0 + acc_col(b, lane);
-            if (i < bp && gn < bp) c.prim[(int64_t)p * bp * bp + (int64_t)i * bp + gn] = S[a][b][r] + acc[a][b][r];
+            const int i = acc_row(wr, a, r, lane), n = acc_col(b, lane);
+            const float v = S[a][b][r] + acc[a][b][r];
+            Rs[i * RP + n] = v;
+            if (ops && i < bp) sts(Xs, n, i, (__bf16)(i < cb && n0 + n < cb ? v : 0.f));
           }
+      lds_barrier();
+      const int nv = min(SW, bp - n0);  // columns of this strip inside the block
+      float* prim = c.prim + (int64_t)p * bp * bp;
+      __bf16* opsF = ops ? c.ops + (int64_t)p * bp * bp : nullptr;
+      for (int e = tid; e < bp * (SW / 4); e += NT) {  // rows i, 4-column chunks
+        const int i = e / (SW / 4), n4 = (e % (SW / 4)) * 4;
+        if (n4 >= nv) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Rs + i * RP + n4);
+        *reinterpret_cast<f32x4*>(prim + (int64_t)i * bp + n0 + n4) = v;
+        if (ops) {
+          bf16x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = (__bf16)(i < cb && n0 + n4 + t < cb ? v[t] : 0.f);
+          *reinterpret_cast<bf16x4*>(opsF + (int64_t)i * bp + n0 + n4) = w;
+        }
+      }
+      if (ops) {  // the transpose: rows ops[nprim bp^2 + p bp^2 + n0 + n][0..bp) from the strip buffer
+        __bf16* opsT = c.ops + (int64_t)c.nprim * bp * bp + (int64_t)p * bp * bp;
+        const int nch = bp / 8;
+        for (int e = tid; e < SW * nch; e += NT) {
+          const int n = e / nch, ch = e - n * nch;
+          if (n < nv)
+            *reinterpret_cast<u32x4*>(opsT + (int64_t)(n0 + n) * bp + ch * 8) =
+                *reinterpret_cast<const u32x4*>(Xs + n * ROWB + ((ch ^ (n & 15)) << 4));
+        }
+      }
       break;
     }
 #pragma unroll

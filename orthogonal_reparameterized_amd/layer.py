@@ -69,6 +69,9 @@ class PoetLinear:
                   B.poet_build_workspace_bytes(P, True))
         self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
         self.W0b = None
+        # bf16 operand copies of the primitives (both orientations), written by PoetGroup.build; None until then
+        # (and after a one-linear build, which leaves them stale)
+        self.opsR = self.opsP = None
         if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
             self.W0b = torch.empty((m, self.L.ldw), dtype=self.act, device=self.dev)
             B.poet_weight_shadow(self.L, self.W0, self.W0b)
@@ -93,6 +96,7 @@ class PoetLinear:
         return self.powersR if side == "R" else self.powersP
 
     def build(self, stream=None, qnorm: bool = False):
+        self.opsR = self.opsP = None  # the one-side build does not write them
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
                                 self.ws, stream)
         B.poet_build_orthogonal(self.L.P, self.thetaP, self.primP, self._powers("P"), self.qnormP if qnorm else None,
@@ -112,12 +116,14 @@ class PoetLinear:
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
 
     def forward_act(self, X, Y, Z, stream=None):
-        """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act."""
-        B.poet_linear_fwd_act(self.L, self.W0b, self.primR, self.primP, X, Y, Z, self.ws, stream)
+        """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
+        operand copies of the primitives come from the last PoetGroup.build, when one made them."""
+        B.poet_linear_fwd_act(self.L, self.W0b, self.primR, self.primP, X, Y, Z, self.ws, stream,
+                              opsR=self.opsR, opsP=self.opsP)
 
     def backward_act(self, X, Z, dY, dX, stream=None):
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
-                              dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
+                              dY, dX, self.dthetaR, self.dthetaP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
     def backward_act_prims(self, X, Z, dY, dX, stream=None):
         """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
@@ -127,7 +133,7 @@ class PoetLinear:
             self.dprimR = torch.empty(B.poet_prim_len(self.L.R), dtype=torch.float32, device=self.dev)
             self.dprimP = torch.empty(B.poet_prim_len(self.L.P), dtype=torch.float32, device=self.dev)
         B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
-                                    self.ws, stream)
+                                    self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
@@ -153,6 +159,12 @@ class PoetGroup:
             raise ValueError("PoetGroup needs at least one linear")
         self.sides = [s for pl in self.linears for s in (pl.L.R, pl.L.P)]
         dev = self.linears[0].dev
+        # operand copies for the activation-side calls of BS sides (2 * prim_len bf16 per side)
+        self._ops = {}
+        for pl in self.linears:
+            if pl.act_path:
+                self._ops[id(pl)] = tuple(torch.empty(2 * B.poet_prim_len(s), dtype=torch.bfloat16, device=dev)
+                                          for s in (pl.L.R, pl.L.P))
         need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides))
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
@@ -160,7 +172,10 @@ class PoetGroup:
         thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]
         prims = [t for pl in self.linears for t in (pl.primR, pl.primP)]
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
-        B.poet_build_orthogonal_group(self.sides, thetas, prims, powers, self.ws, stream)
+        ops = [o for pl in self.linears for o in self._ops.get(id(pl), (None, None))]
+        B.poet_build_orthogonal_group(self.sides, thetas, prims, powers, self.ws, stream, ops=ops)
+        for pl in self.linears:
+            pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
 
     def finish_backward(self, stream=None):
         for pl in self.linears:

@@ -165,19 +165,21 @@ def test_act_path_rejects_bad_arguments():
     wf = B.poet_workspace_bytes(L, B.POET_OP_FWD_ACT)
     wb = B.poet_workspace_bytes(L, B.POET_OP_BWD_ACT)
     assert wf > 0 and wb > 0
-    assert lb.poet_linear_fwd_act(ctypes.byref(Lfs), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf,
+    assert lb.poet_linear_fwd_act(ctypes.byref(Lfs), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, wf,
                                   None) == B.POET_E_UNSUPPORTED
-    assert lb.poet_linear_fwd_act(ctypes.byref(L), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf, None) == B.POET_E_ARG
-    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wf, None) == B.POET_E_ARG
-    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf - 1024,
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, wf,
+                                  None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, wf,
+                                  None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, wf - 1024,
                                   None) == B.POET_E_WORKSPACE
     # saved powers are required for k >= 1; Z is required with tokens
-    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
-                                  FAKE, wb, None) == B.POET_E_ARG
-    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
-                                  FAKE, wb, None) == B.POET_E_ARG
-    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
-                                  FAKE, wb - 1024, None) == B.POET_E_WORKSPACE
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, FAKE, FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, None,
+                                  FAKE, FAKE, FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, FAKE, FAKE, wb - 1024, None) == B.POET_E_WORKSPACE
     assert lb.poet_weight_shadow(ctypes.byref(L), None, FAKE, None) == B.POET_E_ARG
 
 
@@ -196,19 +198,21 @@ def test_group_calls_reject_bad_arguments():
     assert lb.poet_build_group_workspace_bytes(1, bad) == 0
     tab = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
     nul = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
-    assert lb.poet_build_orthogonal_group(-1, arr, tab, tab, tab, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(0, None, None, None, None, None, 0, None) == B.POET_OK
-    assert lb.poet_build_orthogonal_group(3, arr, None, tab, tab, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(3, arr, tab, nul, tab, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, nul, None, 0, None) == B.POET_E_ARG  # powers for k >= 1
-    assert lb.poet_build_orthogonal_group(1, bad, tab, tab, tab, None, 0, None) == B.POET_E_SHAPE
+    assert lb.poet_build_orthogonal_group(-1, arr, tab, tab, tab, None, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(0, None, None, None, None, None, None, 0, None) == B.POET_OK
+    assert lb.poet_build_orthogonal_group(3, arr, None, tab, tab, None, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, nul, tab, None, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, nul, None, None, 0, None) == B.POET_E_ARG  # powers for k >= 1
+    assert lb.poet_build_orthogonal_group(1, bad, tab, tab, tab, None, None, 0, None) == B.POET_E_SHAPE
+    fs_ops = (ctypes.c_void_p * 3)(None, None, FAKE)  # operand copies exist for BS sides only
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, tab, fs_ops, None, 0, None) == B.POET_E_ARG
     assert lb.poet_adjoint_group(3, arr, tab, tab, nul, FAKE, wa, None) == B.POET_E_ARG
     assert lb.poet_adjoint_group(3, arr, tab, nul, tab, FAKE, wa, None) == B.POET_E_ARG
     assert lb.poet_adjoint_group(3, arr, tab, tab, tab, FAKE, wa - 1, None) == B.POET_E_WORKSPACE
     assert lb.poet_adjoint_group(3, arr, tab, tab, tab, None, wa, None) == B.POET_E_ARG
     L = _layer(act_dtype=1)
     wbw = B.poet_workspace_bytes(L, B.POET_OP_BWD_ACT)
-    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
-                                        wbw, None) == B.POET_E_ARG
-    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
-                                        wbw - 1024, None) == B.POET_E_WORKSPACE
+    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None,
+                                        FAKE, FAKE, wbw, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE,
+                                        FAKE, FAKE, wbw - 1024, None) == B.POET_E_WORKSPACE

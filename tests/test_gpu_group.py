@@ -53,6 +53,11 @@ def _thetas(std, seed=5):
     return out
 
 
+def B_prim_len(s):
+    from orthogonal_reparameterized_amd import binding as B
+    return B.poet_prim_len(s)
+
+
 def _alloc(s):
     from orthogonal_reparameterized_amd import binding as B
     dt = torch.bfloat16 if s.dtype == B.POET_BF16 else torch.float32
@@ -61,11 +66,11 @@ def _alloc(s):
     return prim, powers
 
 
-def _build_all(sides, thetas_d, grouped):
+def _build_all(sides, thetas_d, grouped, ops=None):
     from orthogonal_reparameterized_amd import binding as B
     bufs = [_alloc(s) for s in sides]
     if grouped:
-        B.poet_build_orthogonal_group(sides, thetas_d, [b[0] for b in bufs], [b[1] for b in bufs])
+        B.poet_build_orthogonal_group(sides, thetas_d, [b[0] for b in bufs], [b[1] for b in bufs], ops=ops)
     else:
         for s, th, (prim, pw) in zip(sides, thetas_d, bufs):
             B.poet_build_orthogonal(s, th, prim, pw)
@@ -78,11 +83,25 @@ def test_build_group_equals_one_side_builds():
     sides = _sides()
     thetas_d = [torch.from_numpy(t).cuda() for t in _thetas(0.02)]
     single = _build_all(sides, thetas_d, grouped=False)
-    group = _build_all(sides, thetas_d, grouped=True)
+    # operand copies for the BS sides (written by the chain kernel, or by the conversion for the other sides)
+    ops = [torch.full((2 * B_prim_len(s),), float("nan"), dtype=torch.bfloat16, device="cuda") if spec[0] == PI.MODE_BS
+           else None for spec, s in zip(SIDES, sides)]
+    group = _build_all(sides, thetas_d, grouped=True, ops=ops)
     for i, ((pa, wa), (pb, wb)) in enumerate(zip(single, group)):
         assert torch.equal(pa, pb), f"prim of side {i} {SIDES[i]}"
         if wa is not None:
             assert torch.equal(wa, wb), f"powers of side {i} {SIDES[i]}"
+        if ops[i] is None:
+            continue
+        # ops = bf16(F) and bf16(F^T) per block, zero outside the block's c x c corner, bit for bit
+        mode, d, b, k, dt = SIDES[i]
+        F = to_np(pa).reshape(-1, b, b)
+        want = np.zeros_like(F)
+        for p, c in enumerate(O.block_sizes(mode, d, b)):
+            want[p, :c, :c] = PI.round_bf16(F[p, :c, :c])
+        got = to_np(ops[i]).reshape(2, -1, b, b)
+        np.testing.assert_array_equal(got[0], want, err_msg=f"ops of side {i} {SIDES[i]}")
+        np.testing.assert_array_equal(got[1], want.transpose(0, 2, 1), err_msg=f"transposed ops of side {i}")
 
 
 def _oracle_dtheta(side_spec, theta, dprim):
