@@ -28,6 +28,9 @@ class PoetLinear:
     (a multiple of 64 elements keeps every row 128-byte aligned). Index sets of FS sides are drawn on the GPU
     with ``poet_sample_indices`` for epoch 0 unless given.
 
+    ``ws`` (optional) is a uint8 device tensor shared with other linears whose calls run one after another on
+    one stream (``PoetLinear.workspace_bytes`` gives the size one linear needs).
+
     ``path`` picks how the factors are applied: "weight" materializes W = R W0 P (poet_linear_fwd/_bwd), "act"
     applies them to the activations around the W0 GEMM (poet_linear_fwd_act/_bwd_act, which keep a bf16 copy
     of W0 that the merge refreshes), "auto" takes "act" wherever the library supports it.
@@ -36,7 +39,7 @@ class PoetLinear:
     def __init__(self, m: int, n: int, T: int, R: B.poet_side, P: B.poet_side, act_dtype: int, W0,
                  thetaR=None, thetaP=None, seed: int = 0, linear_id: int = 0, ldw: Optional[int] = None,
                  ldx: Optional[int] = None, ldy: Optional[int] = None, idxR=None, idxP=None, device: str = "cuda",
-                 path: str = "weight"):
+                 path: str = "weight", ws=None):
         torch = _torch()
         self.dev = torch.device(device)
         self.L = B.layer(m, n, T, R, P, act_dtype, ldw, ldx, ldy)
@@ -63,11 +66,14 @@ class PoetLinear:
         self.qnormP = torch.empty(B.poet_num_prims(P), dtype=torch.float32, device=self.dev)
         self.dthetaR = torch.empty(max(nR, 1), dtype=torch.float32, device=self.dev)
         self.dthetaP = torch.empty(max(nP, 1), dtype=torch.float32, device=self.dev)
-        ops = (B.POET_OP_FWD_ACT, B.POET_OP_BWD_ACT) if self.act_path else (B.POET_OP_FWD, B.POET_OP_BWD)
-        wsb = max(B.poet_workspace_bytes(self.L, op) for op in ops + (B.POET_OP_MERGE,))
-        wsb = max(wsb, B.poet_sample_workspace_bytes(max(m, n)), B.poet_build_workspace_bytes(R, True),
-                  B.poet_build_workspace_bytes(P, True))
-        self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+        wsb = PoetLinear.workspace_bytes(m, n, T, R, P, act_dtype, self.L.ldw, self.L.ldx, self.L.ldy,
+                                         "act" if self.act_path else "weight")
+        if ws is None:
+            self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
+        else:  # shared with other linears whose calls run in order on one stream
+            if ws.numel() * ws.element_size() < wsb:
+                raise ValueError(f"shared workspace holds {ws.numel() * ws.element_size()} bytes, this linear needs {wsb}")
+            self.ws = ws
         self.W0b = None
         # bf16 operand copies of the primitives (both orientations), written by PoetGroup.build; None until then
         # (and after a one-linear build, which leaves them stale)
@@ -88,6 +94,17 @@ class PoetLinear:
                 B.poet_sample_indices(n, P.b, seed, linear_id, B.POET_SIDE_P, 0, self.idxP, self.ws)
             else:
                 self.idxP.copy_(torch.as_tensor(idxP, dtype=torch.int32))
+
+    @staticmethod
+    def workspace_bytes(m: int, n: int, T: int, R: B.poet_side, P: B.poet_side, act_dtype: int, ldw=None, ldx=None,
+                        ldy=None, path: str = "weight") -> int:
+        """Bytes of the workspace one linear of this shape needs (what the constructor allocates)."""
+        L = B.layer(m, n, T, R, P, act_dtype, ldw, ldx, ldy)
+        act = path == "act" or (path == "auto" and B.poet_act_path_supported(L))
+        ops = (B.POET_OP_FWD_ACT, B.POET_OP_BWD_ACT) if act else (B.POET_OP_FWD, B.POET_OP_BWD)
+        wsb = max(B.poet_workspace_bytes(L, op) for op in ops + (B.POET_OP_MERGE,))
+        return max(wsb, B.poet_sample_workspace_bytes(max(m, n)), B.poet_build_workspace_bytes(R, True),
+                   B.poet_build_workspace_bytes(P, True))
 
     def _powers(self, side: str):
         s = self.L.R if side == "R" else self.L.P

@@ -81,3 +81,48 @@ def test_llama1p3b_bs256_fullsize_act_path(name):
 @pytest.mark.parametrize("name", ["up", "o"])
 def test_llama1p3b_fs_half_fullsize(name):
     _run(4, name)
+
+
+def test_llama3b_fs_half_fullsize_q():
+    """One linear of the LLaMA-3B block (q: 2560 x 2560, POET-FS b = 1/2, s = 1280 per side, k = 5, bf16) at
+    32768 tokens, in the benchmark's launch configuration. (The 6848-wide linears have s = 3424; the oracle's
+    literal double-sum adjoint at that size takes minutes on the host, so their full-size check is the
+    24-layer stack test's sampled one.)"""
+    _run(5, "q")
+
+
+def test_llama60m_block_grouped_act_path():
+    """The LLaMA-60M block (7 linears, BS b = 64, k = 4, bf16, 8192 tokens) as the benchmark runs it: activation
+    side, grouped build and adjoint over all 14 sides; every output checked in full against the oracle."""
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
+    wl = PI.WORKLOADS[2]
+    announce(f"grouped act-path block cfg={wl.name}")
+    lins, data = [], []
+    for lin in wl.linears(0):
+        W0, tR, tP, X, dY = PI.gen_linear(2, 0, lin)
+        pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
+                        seed=wl.seed, linear_id=lin.linear_id, ldw=PI.pad_ld(lin.n), ldx=PI.pad_ld(lin.n),
+                        ldy=PI.pad_ld(lin.m), path="act")
+        assert pl.act_path
+        Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+        bufs = (Xd, dYd, pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx))
+        lins.append(pl)
+        data.append((lin, W0, tR, tP, X, dY, bufs))
+    group = PoetGroup(lins)
+    group.build()
+    for pl, (lin, W0, tR, tP, X, dY, (Xd, dYd, Y, Z, dX)) in zip(lins, data):
+        pl.forward_act(Xd, Y, Z)
+        pl.backward_act_prims(Xd, Z, dYd, dX)
+    group.finish_backward()
+    torch.cuda.synchronize()
+    for pl, (lin, W0, tR, tP, X, dY, (Xd, dYd, Y, Z, dX)) in zip(lins, data):
+        sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+        f = O.linear_fwd(sR, sP, W0, tR, tP, None, None, X)
+        g = O.linear_bwd(sR, sP, W0, tR, tP, None, None, X, dY)
+        errs = {"Y": rel(to_np(Y)[:, :lin.m], f["Y"]), "dX": rel(to_np(dX)[:, :lin.n], g["dX"]),
+                "dthetaR": rel(to_np(pl.dthetaR)[:len(tR)], g["dthetaR"]),
+                "dthetaP": rel(to_np(pl.dthetaP)[:len(tP)], g["dthetaP"])}
+        announce(f"{lin.name}: {errs}")
+        for k, v in errs.items():
+            assert v <= TOL[lin.act_dtype], (lin.name, k, v)
