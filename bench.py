@@ -52,8 +52,12 @@ def step(lins, group=None):
         group.build()
         for e in lins:
             pl = e["pl"]
-            pl.forward_act(e["X"], e["Y"], e["keep"])
-            pl.backward_act_prims(e["X"], e["keep"], e["dY"], e["dX"])
+            if pl.act_path:
+                pl.forward_act(e["X"], e["Y"], e["keep"])
+                pl.backward_act_prims(e["X"], e["keep"], e["dY"], e["dX"])
+            else:
+                pl.forward(e["X"], e["Y"], W_out=e["keep"])
+                pl.backward_prims(e["X"], e["dY"], e["dX"], W=e["keep"])
         group.finish_backward()
         return
     for e in lins:
@@ -140,8 +144,7 @@ def main():
                          "the activation side wherever it is supported (auto)")
     ap.add_argument("--no-group", action="store_true",
                     help="build and finish the backward of each linear on its own (the default runs the per-side "
-                         "steps of all linears of the block in shared launches where every linear takes the "
-                         "activation-side path)")
+                         "steps of all linears of the block in shared launches)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -161,9 +164,7 @@ def main():
     wl = PI.WORKLOADS[args.workload]
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
-    group = None
-    if not args.no_group and all(e["pl"].act_path for e in lins):
-        group = PoetGroup([e["pl"] for e in lins])
+    group = None if args.no_group else PoetGroup([e["pl"] for e in lins])
     torch.cuda.synchronize()
     T = wl.T
 

@@ -155,6 +155,15 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
                             const int32_t* idxP, const void* W, const void* X, const void* dY, void* dX,
                             float* dthetaR, float* dthetaP, void* ws, size_t ws_bytes, void* stream);
 
+/* As poet_linear_bwd, but it stops at the primitive gradients and leaves the Neumann adjoint to
+ * poet_adjoint_group: dprimR [poet_prim_len(R)], dprimP [poet_prim_len(P)] float32 out, the primitive blocks of
+ * dL/dR and dL/dP (BS: entries outside a ragged last block's extent are zero; FS: the s x s block on the index
+ * set). Workspace: POET_OP_BWD. */
+poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                                  const int32_t* idxR, const int32_t* idxP, const void* W, const void* X,
+                                  const void* dY, void* dX, float* dprimR, float* dprimP, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* ---- activation-side application ---------------------------------------------------------------------
  * The same layer with the factors applied to the activations around the W0 GEMM (W is never formed); the
  * products of the weight-side calls above, associated the other way (W = R W0 P from the method summary):

@@ -28,7 +28,7 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
-           "poet_adjoint_group_workspace_bytes", "poet_adjoint_group")
+           "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE = range(9)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.poet_weight_shadow.argtypes = [P(poet_layer), VP, VP, VP]
     L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_build_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_build_group_workspace_bytes.restype = S
@@ -317,6 +318,25 @@ def poet_linear_bwd(L: poet_layer, W0, primR, primP, powersR, powersP, idxR, idx
         _ptr(ws, "ws", need if W is None else 0, allow_none=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_linear_bwd")
+
+
+def poet_linear_bwd_prims(L: poet_layer, W0, primR, primP, idxR, idxP, W, X, dY, dX, dprimR, dprimP, ws=None,
+                          stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_BWD)
+    st = lib().poet_linear_bwd_prims(
+        ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32", allow_none=True), _ptr(idxP, "idxP", 4 * L.P.b, "int32", allow_none=True),
+        _ptr(W, "W", b["W"], act, allow_none=True),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dX, "dX", b["X"], act, allow_none=True),
+        _ptr(dprimR, "dprimR", 4 * poet_prim_len(L.R), "float32"),
+        _ptr(dprimP, "dprimP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(ws, "ws", need if W is None else 0, allow_none=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd_prims")
 
 
 def poet_act_path_supported(L: poet_layer) -> bool:

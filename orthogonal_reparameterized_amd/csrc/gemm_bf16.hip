@@ -44,15 +44,21 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = 256 * BK * 2;  // bytes of one operand's stage (both layouts)
 
+constexpr int MAXGP = 16;
+struct GroupEntry {
+  int64_t offA = 0, offB = 0, offC = 0, lda = 0, ldb = 0;
+  int b0 = 0, Mtot = 0, Ntot = 0, pad = 0;
+};
+
 struct FastArgs {
   GemmDesc g;
   int ntm, ntn, splits, kchunk;
   int use_part;  // write float32 partial tiles; a second kernel reduces them and applies the epilogue
-  // a second problem of the same shape in the same launch (batch entries batch1 .. g.batch - 1): its operands and
-  // output sit at these byte offsets from g's, with their own leading dimensions and extents
-  int batch1 = 0;
-  int64_t offA2 = 0, offB2 = 0, offC2 = 0, lda2 = 0, ldb2 = 0;
-  int Mtot2 = 0, Ntot2 = 0;
+  // nprob > 0: the launch holds nprob problems of g's shape (M, N, K, strides, output type); problem p owns batch
+  // entries [prob[p].b0, prob[p + 1].b0) and reads / writes its operands at byte offsets from g's, with its own
+  // leading dimensions and extents
+  int nprob = 0;
+  GroupEntry prob[MAXGP];
 };
 
 // an epilogue the main kernel stores directly: out = acc into C (no addend, scale, second copy or accumulate)
@@ -220,8 +226,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* 
 }
 
 // TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
-// PAIR: the launch holds two problems (FastArgs batch1 and the offsets of the second).
-template <bool AK, bool BK_, int TAG, bool PAIR = false>
+// GROUP: the launch holds several problems of one shape (FastArgs nprob and prob).
+template <bool AK, bool BK_, int TAG, bool GROUP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(const FastArgs fa_) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
   const GemmDesc& g = fa_.g;
@@ -258,12 +264,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   char* Cb = reinterpret_cast<char*>(g.C);
   int64_t lda = g.lda, ldb = g.ldb;
   int Mtot = g.Mtot, Ntot = g.Ntot;
-  if constexpr (PAIR) {
-    if (z >= fa_.batch1) {
-      z -= fa_.batch1;
-      Ab += fa_.offA2; Bb += fa_.offB2; Cb += fa_.offC2;
-      lda = fa_.lda2; ldb = fa_.ldb2; Mtot = fa_.Mtot2; Ntot = fa_.Ntot2;
-    }
+  if constexpr (GROUP) {
+    int p = 0;
+    for (int q = 1; q < fa_.nprob; ++q)
+      if (zg >= fa_.prob[q].b0) p = q;
+    const GroupEntry& e = fa_.prob[p];
+    z = zg - keep_s(e.b0);
+    Ab += keep_s(e.offA); Bb += keep_s(e.offB); Cb += keep_s(e.offC);
+    lda = keep_s(e.lda); ldb = keep_s(e.ldb); Mtot = keep_s(e.Mtot); Ntot = keep_s(e.Ntot);
   }
   int M = g.M, N = g.N, K = g.K;
   if (Mtot > 0) M = min(M, Mtot - z * g.M);
@@ -397,17 +405,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) 
     const int zg = (int)(e / mn);
     const int64_t rc = e - (int64_t)zg * mn;
     const int row = (int)(rc / g.N), col = (int)(rc - (int64_t)row * g.N);
-    const bool second = fa_.batch1 > 0 && zg >= fa_.batch1;  // second problem of a pair (plain epilogue)
-    const int z = second ? zg - fa_.batch1 : zg;
+    int p = 0;  // problem of a grouped launch (plain epilogue)
+    for (int q = 1; q < fa_.nprob; ++q)
+      if (zg >= fa_.prob[q].b0) p = q;
+    const int z = fa_.nprob > 0 ? zg - fa_.prob[p].b0 : zg;
     int M = g.M, N = g.N;
-    const int Mtot = second ? fa_.Mtot2 : g.Mtot, Ntot = second ? fa_.Ntot2 : g.Ntot;
+    const int Mtot = fa_.nprob > 0 ? fa_.prob[p].Mtot : g.Mtot, Ntot = fa_.nprob > 0 ? fa_.prob[p].Ntot : g.Ntot;
     if (Mtot > 0) M = min(M, Mtot - z * g.M);
     if (Ntot > 0) N = min(N, Ntot - z * g.N);
     if (row >= M || col >= N) continue;
     float sum = 0.f;
     for (int s = 0; s < fa_.splits; ++s) sum += g.part[(int64_t)(s * g.batch + zg) * mn + rc];
-    if (fa_.batch1 > 0) {
-      char* cb = reinterpret_cast<char*>(g.C) + (second ? fa_.offC2 : 0);
+    if (fa_.nprob > 0) {
+      char* cb = reinterpret_cast<char*>(g.C) + fa_.prob[p].offC;
       store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col, sum);
     } else {
       epilogue_one(g, z, row, col, sum);
@@ -476,21 +486,42 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b) {
-  if (!fast_gemm_eligible(a) || !fast_gemm_eligible(b)) return false;
-  if (!plain_epilogue(a) || !plain_epilogue(b) || a.defer_reduce || b.defer_reduce) return false;
-  if (a.a_kmajor || a.b_kmajor || b.a_kmajor || b.b_kmajor) return false;  // the token-axis contraction's layout
-  if (a.M != b.M || a.N != b.N || a.K != b.K || a.Ktot != b.Ktot || a.sA != b.sA || a.sB != b.sB) return false;
-  if (a.ldc != b.ldc || a.sC != b.sC || a.c_dt != b.c_dt) return false;
-  // the partials of both problems (at least 2 splits) in the first one's scratch
-  return a.part && a.part_elems >= (size_t)2 * (a.batch + b.batch) * a.M * a.N;
+bool fast_gemm_group_eligible(const GemmDesc* pr, int n) {
+  if (n < 1 || n > MAXGP) return false;
+  const GemmDesc& a = pr[0];
+  size_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const GemmDesc& b = pr[i];
+    if (!fast_gemm_eligible(b) || !plain_epilogue(b) || b.defer_reduce) return false;
+    if (b.a_kmajor != a.a_kmajor || b.b_kmajor != a.b_kmajor || b.M != a.M || b.N != a.N || b.K != a.K ||
+        b.Ktot != a.Ktot || b.sA != a.sA || b.sB != a.sB || b.ldc != a.ldc || b.sC != a.sC || b.c_dt != a.c_dt)
+      return false;
+    blocks += (size_t)b.batch;
+  }
+  // the split-K partials of every problem (at least 2 splits) in the first one's scratch
+  return a.part && a.part_elems >= 2 * blocks * a.M * a.N;
 }
 
-hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
-  GemmDesc g = a;
-  g.batch = a.batch + b.batch;
-  if (g.batch <= 0) return hipSuccess;
+bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b) {
+  const GemmDesc pr[2] = {a, b};
+  return fast_gemm_group_eligible(pr, 2);
+}
+
+hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
+  GemmDesc g = pr[0];
+  g.batch = 0;
   FastArgs fa;
+  fa.nprob = n;
+  for (int i = 0; i < n; ++i) {
+    GroupEntry& e = fa.prob[i];
+    e.b0 = g.batch;
+    e.offA = reinterpret_cast<const char*>(pr[i].A) - reinterpret_cast<const char*>(pr[0].A);
+    e.offB = reinterpret_cast<const char*>(pr[i].B) - reinterpret_cast<const char*>(pr[0].B);
+    e.offC = reinterpret_cast<const char*>(pr[i].C) - reinterpret_cast<const char*>(pr[0].C);
+    e.lda = pr[i].lda; e.ldb = pr[i].ldb; e.Mtot = pr[i].Mtot; e.Ntot = pr[i].Ntot;
+    g.batch += pr[i].batch;
+  }
+  if (g.batch <= 0 || g.M <= 0 || g.N <= 0) return hipSuccess;
   fa.g = g;
   fa.ntm = (g.M + BM - 1) / BM;
   fa.ntn = (g.N + BN - 1) / BN;
@@ -500,22 +531,25 @@ hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream
   fa.splits = S;
   fa.kchunk = ((nk + S - 1) / S) * BK;
   fa.use_part = S > 1 ? 1 : 0;
-  fa.batch1 = a.batch;
-  fa.offA2 = reinterpret_cast<const char*>(b.A) - reinterpret_cast<const char*>(a.A);
-  fa.offB2 = reinterpret_cast<const char*>(b.B) - reinterpret_cast<const char*>(a.B);
-  fa.offC2 = reinterpret_cast<const char*>(b.C) - reinterpret_cast<const char*>(a.C);
-  fa.lda2 = b.lda; fa.ldb2 = b.ldb; fa.Mtot2 = b.Mtot; fa.Ntot2 = b.Ntot;
   const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
-  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (double)g.M * g.N * 4.0);
+  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (double)g.M * g.N * dtype_size(g.c_dt));
   ProfScope prof(g.kclass, st, flops, bytes);
   const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
-  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0, true>), grid, block, 0, st, fa);
+  if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 0, true>), grid, block, 0, st, fa);
+  else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 0, true>), grid, block, 0, st, fa);
+  else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true, 0, true>), grid, block, 0, st, fa);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0, true>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fa.use_part) return e;
   const int64_t total = (int64_t)g.batch * g.M * g.N;
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
   return hipGetLastError();
+}
+
+hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
+  const GemmDesc pr[2] = {a, b};
+  return launch_fast_gemm_group(pr, 2, st);
 }
 
 }  // namespace poet

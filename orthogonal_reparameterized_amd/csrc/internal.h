@@ -46,8 +46,12 @@ struct GemmDesc {
 bool fast_gemm_eligible(const GemmDesc& g);
 int fast_gemm_splits(const GemmDesc& g);  // split-K count the fast path uses for g
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
-// Two problems of one shape in one launch (the R- and P-side token-axis contractions of a linear): both M-major
-// operands, plain epilogue; the split-K partials of both go to a's scratch.
+// Up to 16 problems of one shape (M, N, K, operand orientations, batch strides, output pitch and type) in one
+// launch, each with its own operands, leading dimensions, extents and batch count (e.g. the R- and P-side
+// token-axis contractions of a linear, or one power-chain step of many FS sides); plain epilogue; the split-K
+// partials of all go to the first problem's scratch.
+bool fast_gemm_group_eligible(const GemmDesc* probs, int n);
+hipError_t launch_fast_gemm_group(const GemmDesc* probs, int n, hipStream_t st);
 bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b);
 hipError_t launch_fast_gemm_pair(const GemmDesc& a, const GemmDesc& b, hipStream_t st);
 
@@ -113,6 +117,14 @@ hipError_t launch_adjoint_coefs_group(const CoefGroup& g, int dt, hipStream_t st
 struct SkewSide { const float* D = nullptr; float* dtheta = nullptr; int mode = 0, d = 0, nprim = 0, boff = 0; };
 struct SkewGroup { int n = 0, bp = 0; const float* part = nullptr; int64_t split_stride = 0; float beta = 0.f; SkewSide s[MAXG]; };
 hipError_t launch_reduce_skew_group(const SkewGroup& g, int nsplit, hipStream_t st);
+
+// prim += I + 2 Q + 2 (P_2 + .. + P_k) for the sides of a GEMM-built chain (prim holds P_{k+1} on entry)
+struct FinSide {
+  const float* theta = nullptr; const void* powers = nullptr; float* prim = nullptr;
+  int mode = 0, d = 0, bp = 0, nprim = 0, k = 0, dt = BF16, ldp = 0;
+};
+struct FinGroup { int n = 0; FinSide s[MAXG]; };
+hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st);
 
 
 // Fused application of block-diagonal factors on both sides (bs_apply.hip), blocks bpR, bpP <= 256, W0 float32

@@ -346,36 +346,60 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
 }
 
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
-// (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1
-__global__ void k_chain_finalize(const float* __restrict__ theta, int mode, int d, int bp, int nprim, int k,
-                                 const void* __restrict__ powers, int dt, int ldp, float* __restrict__ prim) {
+// (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1. Side blockIdx.y of the table.
+__global__ void k_chain_finalize(const FinGroup G) {
+  FinSide a;
+  {
+    const FinSide& t = G.s[blockIdx.y];
+    a.theta = keep_s(t.theta); a.powers = keep_s(t.powers); a.prim = keep_s(t.prim); a.mode = keep_s(t.mode);
+    a.d = keep_s(t.d); a.bp = keep_s(t.bp); a.nprim = keep_s(t.nprim); a.k = keep_s(t.k); a.dt = keep_s(t.dt);
+    a.ldp = keep_s(t.ldp);
+  }
+  const int bp = a.bp, k = a.k, nprim = a.nprim;
   const int64_t pp = (int64_t)bp * bp, total = (int64_t)nprim * pp;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(e / pp);
     const int rem = (int)(e - (int64_t)p * pp);
     const int i = rem / bp, j = rem % bp;
-    const int c = prim_size(mode, d, bp, p);
+    const int c = prim_size(a.mode, a.d, bp, p);
     float q = 0.f;
     if (i < c && j < c && i != j) {
       const int64_t off = theta_off(bp, p);
-      q = i < j ? theta[off + tri_pos(i, j, c)] : -theta[off + tri_pos(j, i, c)];
+      q = i < j ? a.theta[off + tri_pos(i, j, c)] : -a.theta[off + tri_pos(j, i, c)];
     }
     float s = 0.f;
-    for (int t = 2; t <= k; ++t) s += ld_dt(powers, dt, (((int64_t)(t - 1) * nprim + p) * bp + i) * ldp + j);
-    prim[e] = (i == j ? 1.f : 0.f) + 2.f * q + 2.f * s + prim[e];
+    for (int t = 2; t <= k; ++t) s += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * nprim + p) * bp + i) * a.ldp + j);
+    a.prim[e] = (i == j ? 1.f : 0.f) + 2.f * q + 2.f * s + a.prim[e];
   }
 }
 
 }  // namespace
 
+hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st) {
+  if (g.n <= 0) return hipSuccess;
+  if (g.n > MAXG) return hipErrorInvalidValue;
+  int64_t most = 0;
+  double bytes = 0;
+  for (int i = 0; i < g.n; ++i) {
+    const FinSide& a = g.s[i];
+    const int64_t total = (int64_t)a.nprim * a.bp * a.bp;
+    most = std::max(most, total);
+    bytes += (double)total * (8 + 4 + (a.k - 1) * dtype_size(a.dt));
+  }
+  if (most == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, bytes);
+  hipLaunchKernelGGL(k_chain_finalize, dim3(grid_for((size_t)most, kThreads, 4096), g.n), dim3(kThreads), 0, st, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
                                  int dt, int ldp, float* prim, hipStream_t st) {
-  const int64_t total = (int64_t)nprim * bp * bp;
-  if (total == 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)total * (8 + 4 + (k - 1) * dtype_size(dt)));
-  hipLaunchKernelGGL(k_chain_finalize, dim3(grid_for(total)), dim3(kThreads), 0, st, theta, mode, d, bp, nprim, k, powers,
-                     dt, ldp, prim);
-  return hipGetLastError();
+  FinGroup g;
+  g.n = 1;
+  FinSide& a = g.s[0];
+  a.theta = theta; a.powers = powers; a.prim = prim; a.mode = mode; a.d = d; a.bp = bp; a.nprim = nprim; a.k = k;
+  a.dt = dt; a.ldp = ldp;
+  return launch_chain_finalize_group(g, st);
 }
 
 hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf16* out, hipStream_t st) {

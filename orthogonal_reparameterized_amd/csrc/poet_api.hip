@@ -612,9 +612,39 @@ bool chain_side(const SideInfo& S, const void* powers) {
   return S.k > 0 && S.ldp == S.bp && power_chain_eligible(S.bp, S.dtype, powers);
 }
 
+// build chunks: sides whose chain runs as GEMMs (k >= 1, bf16, not on the fused chain, primitives of at least 128
+// so the fast kernel takes the products) sharing (bp, ldp, k), at most MAXG per chunk; each power step of a chunk
+// is one grouped GEMM. Sizing passes powers = nullptr (aligned buffers assumed).
+struct BuildChunk {
+  int bp = 0, ldp = 0, k = 0;
+  size_t prim_elems = 0;
+  std::vector<int> idx;
+};
+bool gemm_chain_side(const SideInfo& S, const void* powers) {
+  const bool al = !powers || (reinterpret_cast<uintptr_t>(powers) & 15) == 0;
+  return S.k > 0 && S.dtype == BF16 && S.bp >= 128 && al && !chain_side(S, powers ? powers : (const void*)256);
+}
+std::vector<BuildChunk> build_chunks(const std::vector<SideInfo>& S, void* const* powers) {
+  std::vector<BuildChunk> ch;
+  for (int i = 0; i < (int)S.size(); ++i) {
+    if (!gemm_chain_side(S[i], powers ? powers[i] : nullptr)) continue;
+    BuildChunk* c = nullptr;
+    for (auto& x : ch)
+      if (x.bp == S[i].bp && x.ldp == S[i].ldp && x.k == S[i].k && (int)x.idx.size() < MAXG) c = &x;
+    if (!c) { ch.emplace_back(); c = &ch.back(); c->bp = S[i].bp; c->ldp = S[i].ldp; c->k = S[i].k; }
+    c->idx.push_back(i);
+    c->prim_elems += S[i].prim_len;
+  }
+  return ch;
+}
+// split-K scratch of a chunk's power products: up to 4 splits of every block
+size_t build_chunk_part_elems(const BuildChunk& c) { return 8 * c.prim_elems; }
+
 // adjoint chunks: sides sharing (bp, k) whose adjoint runs on the fused chain, at most MAXG per chunk
+// fused: the H chain runs on the fused chain kernel (blocks <= 256, ldp = bp); otherwise as grouped GEMMs (ldp >= bp)
 struct AdjChunk {
-  int bp = 0, k = 0, nb = 0;
+  int bp = 0, ldp = 0, k = 0, nb = 0;
+  bool fused = true;
   std::vector<int> idx;
 };
 std::vector<AdjChunk> adjoint_chunks(const std::vector<SideInfo>& S, const void* const* powers, std::vector<int>* solo) {
@@ -622,11 +652,15 @@ std::vector<AdjChunk> adjoint_chunks(const std::vector<SideInfo>& S, const void*
   for (int i = 0; i < (int)S.size(); ++i) {
     if (S[i].theta_len == 0) continue;
     const void* pw = powers ? powers[i] : reinterpret_cast<const void*>(256);  // sizing: assume aligned powers
-    if (!chain_side(S[i], pw)) { solo->push_back(i); continue; }
+    const bool fused = chain_side(S[i], pw);
+    if (!fused && !gemm_chain_side(S[i], powers ? powers[i] : nullptr)) { solo->push_back(i); continue; }
     AdjChunk* c = nullptr;
     for (auto& x : ch)
-      if (x.bp == S[i].bp && x.k == S[i].k && (int)x.idx.size() < MAXG) c = &x;
-    if (!c) { ch.emplace_back(); c = &ch.back(); c->bp = S[i].bp; c->k = S[i].k; }
+      if (x.fused == fused && x.bp == S[i].bp && x.ldp == S[i].ldp && x.k == S[i].k && (int)x.idx.size() < MAXG) c = &x;
+    if (!c) {
+      ch.emplace_back(); c = &ch.back();
+      c->bp = S[i].bp; c->ldp = S[i].ldp; c->k = S[i].k; c->fused = fused;
+    }
     c->idx.push_back(i);
     c->nb += S[i].nprim;
   }
@@ -643,8 +677,8 @@ struct AdjChunkBufs {
 size_t plan_adj_chunk(const AdjChunk& c, void* ws, AdjChunkBufs* b) {
   Arena a(ws);
   const size_t pp = (size_t)c.bp * c.bp, nb = (size_t)c.nb;
-  b->H = a.take<__bf16>(nb * pp * (c.k + 1));
-  b->Cs = a.take<__bf16>(nb * pp * (c.k + 1));
+  b->H = a.take<__bf16>(nb * c.bp * (size_t)c.ldp * (c.k + 1));
+  b->Cs = a.take<__bf16>(nb * (size_t)c.ldp * c.ldp * (c.k + 1));
   b->part_elems = 4 * nb * pp;
   b->part = a.take<float>(b->part_elems);
   return a.used();
@@ -673,13 +707,14 @@ size_t adjoint_group_bytes(const std::vector<SideInfo>& S, const void* const* po
   return need;
 }
 
-// the Neumann adjoint and skew projection of one chunk (see neumann_adjoint for the algebra)
+// the Neumann adjoint and skew projection of one chunk (see neumann_adjoint for the algebra): H_j of every block
+// side by side (row pitch (k+1) ldp), the coefficient stacks, one product over all blocks, one projection
 hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, const float* const* dprim,
                          const void* const* powers, float* const* dtheta, const AdjChunkBufs& b, hipStream_t st) {
-  const int bp = c.bp, k = c.k, ldh = (k + 1) * bp;
-  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
+  const int bp = c.bp, k = c.k, ldp = c.ldp, ldh = (k + 1) * ldp;
+  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh, ps = (int64_t)bp * ldp;
   hipError_t e;
-  {  // H_0 = dR and H_{j+1} = Q H_j for every block of the chunk
+  if (c.fused) {  // H_0 = dR and H_{j+1} = Q H_j for every block of the chunk in one launch
     ChainGroup g;
     int boff = 0;
     for (int i : c.idx) {
@@ -691,14 +726,45 @@ hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, cons
       boff += S[i].nprim;
     }
     if ((e = launch_power_chain_group(g, POET_K_ADJOINT, st)) != hipSuccess) return e;
+  } else {  // H_0 = bf16(dR), then one grouped product per step: H_{j+1} = Q H_j with each side's own Q
+    if (ldp > bp && (e = launch_fill(reinterpret_cast<float*>(b.H), (size_t)c.nb * hs / 2, 0.f, st)) != hipSuccess)
+      return e;  // the gap columns past bp stay zero (zero bits; hs is even)
+    int boff = 0;
+    for (int i : c.idx) {
+      if ((e = launch_convert(dprim[i], bp, b.H + (size_t)boff * hs, ldh, BF16, S[i].nprim * bp, bp, st)) != hipSuccess)
+        return e;
+      boff += S[i].nprim;
+    }
+    const int n = (int)c.idx.size();
+    for (int j = 0; j < k; ++j) {
+      GemmDesc pr[MAXG];
+      boff = 0;
+      for (int u = 0; u < n; ++u) {
+        const int i = c.idx[u];
+        GemmDesc& g = pr[u];
+        g.kclass = POET_K_ADJOINT;
+        g.compute = BF16; g.M = g.N = g.K = bp; g.batch = S[i].nprim;
+        g.A = powers[i]; g.lda = ldp; g.sA = ps; g.a_dt = BF16; g.a_kmajor = 1;
+        g.B = b.H + (size_t)boff * hs + (size_t)j * ldp; g.ldb = ldh; g.sB = hs; g.b_dt = BF16; g.b_kmajor = 0;
+        g.C = b.H + (size_t)boff * hs + (size_t)(j + 1) * ldp; g.ldc = ldh; g.sC = hs; g.c_dt = BF16;
+        g.part = b.part; g.part_elems = b.part_elems;
+        boff += S[i].nprim;
+      }
+      if (fast_gemm_group_eligible(pr, n)) {
+        if ((e = launch_fast_gemm_group(pr, n, st)) != hipSuccess) return e;
+      } else {
+        for (int u = 0; u < n; ++u)
+          if ((e = launch_gemm(pr[u], st)) != hipSuccess) return e;
+      }
+    }
   }
   {  // the coefficient stacks C_0..C_k from the saved powers
     CoefGroup g;
-    g.bp = bp; g.ldp = bp; g.k = k;
+    g.bp = bp; g.ldp = ldp; g.k = k;
     int boff = 0;
     for (int i : c.idx) {
       CoefSide& a = g.s[g.n++];
-      a.powers = powers[i]; a.out = b.Cs + (size_t)boff * (k + 1) * pp; a.nprim = S[i].nprim;
+      a.powers = powers[i]; a.out = b.Cs + (size_t)boff * (k + 1) * ldp * ldp; a.nprim = S[i].nprim;
       boff += S[i].nprim;
     }
     if ((e = launch_adjoint_coefs_group(g, BF16, st)) != hipSuccess) return e;
@@ -707,7 +773,7 @@ hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, cons
   g.kclass = POET_K_ADJOINT;
   g.compute = BF16; g.M = g.N = bp; g.K = ldh; g.batch = c.nb;
   g.A = b.H; g.lda = ldh; g.sA = hs; g.a_dt = BF16; g.a_kmajor = 1;
-  g.B = b.Cs; g.ldb = bp; g.sB = (int64_t)(k + 1) * pp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.B = b.Cs; g.ldb = ldp; g.sB = (int64_t)(k + 1) * ldp * ldp; g.b_dt = BF16; g.b_kmajor = 0;
   g.C = b.part; g.ldc = bp; g.sC = pp; g.c_dt = F32;
   g.part = b.part; g.part_elems = b.part_elems;
   int ns = 1;
@@ -889,17 +955,26 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
   return POET_OK;
 }
 
-poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
-                            const void* powersR, const void* powersP, const int32_t* idxR, const int32_t* idxP,
-                            const void* Win, const void* X, const void* dY, void* dX, float* dthetaR, float* dthetaP,
-                            void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// the weight-side backward; with dprimR/dprimP given it stops at the primitive gradients
+poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                       const void* powersR, const void* powersP, const int32_t* idxR, const int32_t* idxP,
+                       const void* Win, const void* X, const void* dY, void* dX, float* dthetaR, float* dthetaP,
+                       float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
   if (!W0 || !primR || !primP) return fail(POET_E_ARG, "null W0 or primitive");
   if (L->T > 0 && (!X || !dY)) return fail(POET_E_ARG, "null X or dY");
-  if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
-  if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
-    return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  const bool prims_only = dprimR || dprimP;
+  if (prims_only) {
+    if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  } else {
+    if ((R.theta_len > 0 && !dthetaR) || (P.theta_len > 0 && !dthetaP)) return fail(POET_E_ARG, "null dtheta");
+    if ((R.k > 0 && R.theta_len > 0 && !powersR) || (P.k > 0 && P.theta_len > 0 && !powersP))
+      return fail(POET_E_ARG, "saved powers are required when k >= 1");
+  }
   if (!check_idx(R, idxR, "R") || !check_idx(P, idxP, "P")) return g_last;
   BwdPlan p;
   const size_t need = plan_bwd(*L, R, P, nullptr, Win == nullptr, &p);
@@ -956,8 +1031,10 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
     g.part = p.adj.part; g.part_elems = p.adj.part_elems;
     HIP_TRY(launch_gemm(g, st));
   }
-  // primitive blocks of dL/dR = G Z^T
-  if (R.theta_len > 0) {
+  // primitive blocks of dL/dR = G Z^T (into the caller's dprimR when the adjoint is left to the caller)
+  float* dRg = prims_only ? dprimR : p.dRg;
+  float* dPg = prims_only ? dprimP : p.dPg;
+  if (R.theta_len > 0 || prims_only) {
     GemmDesc g;
     g.kclass = POET_K_CONTRACT;
     g.compute = act;
@@ -971,10 +1048,10 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       }
       g.lda = ldw; g.sA = (int64_t)R.bp * ldw; g.a_kmajor = 1;
       g.ldb = ldw; g.sB = (int64_t)R.bp * ldw; g.b_kmajor = 1;
-      g.C = p.dRg; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
+      g.C = dRg; g.ldc = R.bp; g.sC = (int64_t)R.bp * R.bp; g.c_dt = F32;
     } else {
       g.M = g.N = R.bp; g.K = n;
-      g.C = p.dRg; g.ldc = R.bp; g.c_dt = F32;
+      g.C = dRg; g.ldc = R.bp; g.c_dt = F32;
       if (fs_bf16(*L, R)) {  // gathered rows as bf16 operands (row pitch padded to 8) on the fast kernel
         const int ldn = pad8(n);
         HIP_TRY(launch_gather_rows_to(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, BF16, ldn, st));
@@ -988,10 +1065,11 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
         g.B = p.Zr; g.ldb = n; g.b_dt = F32; g.b_kmajor = 1;
       }
     }
-    HIP_TRY(contract_and_adjoint(R, g, p.dRg, powersR, dthetaR, p.adj, st));
+    if (prims_only) HIP_TRY(contract_only(R, g, dRg, st));
+    else HIP_TRY(contract_and_adjoint(R, g, dRg, powersR, dthetaR, p.adj, st));
   }
   // primitive blocks of dL/dP = (R W0)^T G
-  if (P.theta_len > 0) {
+  if (P.theta_len > 0 || prims_only) {
     GemmDesc g;
     g.kclass = POET_K_CONTRACT;
     g.compute = act;
@@ -1005,10 +1083,10 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
       }
       g.lda = ldw; g.sA = P.bp; g.a_kmajor = 0;
       g.ldb = ldw; g.sB = P.bp; g.b_kmajor = 0;
-      g.C = p.dPg; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
+      g.C = dPg; g.ldc = P.bp; g.sC = (int64_t)P.bp * P.bp; g.c_dt = F32;
     } else {
       g.M = g.N = P.bp; g.K = m;
-      g.C = p.dPg; g.ldc = P.bp; g.c_dt = F32;
+      g.C = dPg; g.ldc = P.bp; g.c_dt = F32;
       if (fs_bf16(*L, P)) {  // gathered columns as bf16 operands (row pitch ldp) on the fast kernel
         HIP_TRY(launch_gather_cols_to(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, BF16, P.ldp, st));
         HIP_TRY(launch_gather_cols_to(p.G, ldw, m, idxP, P.bp, n, p.Gc, BF16, P.ldp, st));
@@ -1021,9 +1099,30 @@ poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* p
         g.B = p.Gc; g.ldb = P.bp; g.b_dt = F32; g.b_kmajor = 0;
       }
     }
-    HIP_TRY(contract_and_adjoint(P, g, p.dPg, powersP, dthetaP, p.adj, st));
+    if (prims_only) HIP_TRY(contract_only(P, g, dPg, st));
+    else HIP_TRY(contract_and_adjoint(P, g, dPg, powersP, dthetaP, p.adj, st));
   }
   return POET_OK;
+}
+}  // namespace
+
+extern "C" {
+
+poet_status poet_linear_bwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                            const void* powersR, const void* powersP, const int32_t* idxR, const int32_t* idxP,
+                            const void* Win, const void* X, const void* dY, void* dX, float* dthetaR, float* dthetaP,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return bwd_weight(L, W0, primR, primP, powersR, powersP, idxR, idxP, Win, X, dY, dX, dthetaR, dthetaP, nullptr,
+                    nullptr, ws, ws_bytes, stream);
+}
+
+poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                                  const int32_t* idxR, const int32_t* idxP, const void* W, const void* X,
+                                  const void* dY, void* dX, float* dprimR, float* dprimP, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  return bwd_weight(L, W0, primR, primP, nullptr, nullptr, idxR, idxP, W, X, dY, dX, nullptr, nullptr, dprimR, dprimP,
+                    ws, ws_bytes, stream);
 }
 
 int poet_act_path_supported(const poet_layer* L) {
@@ -1160,6 +1259,7 @@ size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
   if (!group_sides(count, sides, &S)) return 0;
   size_t need = 0;
   for (int i = 0; i < count; ++i) need = std::max(need, poet_build_workspace_bytes(&sides[i], 1));
+  for (const auto& c : build_chunks(S, nullptr)) need = std::max(need, build_chunk_part_elems(c) * sizeof(float) + 512);
   return need;
 }
 
@@ -1178,12 +1278,16 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
   }
   if (!check_ws(ws, ws_bytes, poet_build_group_workspace_bytes(count, sides))) return g_last;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // sides on the fused chain (and k = 0 sides, which need only I + Q) share launches; the rest build one by one
+  // sides on the fused chain, k = 0 sides (which need only I + Q) and sides whose chain runs as grouped GEMMs share
+  // the theta launches; the rest build one by one
+  const std::vector<BuildChunk> chunks = build_chunks(S, powers);
+  std::vector<char> in_chunk(count, 0);
+  for (const auto& c : chunks)
+    for (int i : c.idx) in_chunk[i] = 1;
   std::vector<int> grouped;
   auto side_ops = [&](int i) -> __bf16* { return ops ? reinterpret_cast<__bf16*>(ops[i]) : nullptr; };
   for (int i = 0; i < count; ++i) {
-    if (chain_side(S[i], powers[i])) { grouped.push_back(i); continue; }  // the chain also writes the ops
-    if (S[i].k == 0) grouped.push_back(i);
+    if (S[i].k == 0 || chain_side(S[i], powers[i]) || in_chunk[i]) grouped.push_back(i);
     else if (poet_build_orthogonal(&sides[i], theta[i], prim[i], powers[i], nullptr, ws, ws_bytes, stream) != POET_OK)
       return g_last;
   }
@@ -1197,7 +1301,7 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
       PrepSide& a = pg.s[pg.n++];
       a.theta = theta[i]; a.prim = prim[i]; a.q = T.k > 0 ? powers[i] : nullptr; a.q_dt = T.dtype; a.ldq = T.ldp;
       a.mode = T.mode; a.d = T.d; a.bp = T.bp; a.nprim = T.nprim; a.coef = T.k == 0 ? 1.f : 2.f;
-      if (T.k == 0) continue;
+      if (T.k == 0 || in_chunk[i]) continue;
       ChainArgs& c = cg.a[cg.n++];
       c.bp = T.bp; c.nprim = T.nprim; c.steps = T.k; c.build = 1; c.prim = prim[i];
       c.A = reinterpret_cast<const __bf16*>(powers[i]); c.sA = (int64_t)T.bp * T.bp;
@@ -1206,6 +1310,44 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     }
     HIP_TRY(launch_theta_prep_group(pg, st));
     HIP_TRY(launch_power_chain_group(cg, POET_K_CHAIN, st));
+  }
+  // GEMM chains: P_{i+1} = Q P_i for every side of a chunk in one launch per step (the last power straight into
+  // prim in float32), then the rest of the series for all of them
+  for (const auto& c : chunks) {
+    Arena a(ws);
+    const size_t part_elems = build_chunk_part_elems(c);
+    float* part = a.take<float>(part_elems);
+    const int n = (int)c.idx.size();
+    for (int step = 1; step <= c.k; ++step) {
+      GemmDesc pr[MAXG];
+      for (int u = 0; u < n; ++u) {
+        const int i = c.idx[u];
+        const SideInfo& T = S[i];
+        const size_t esz = dtype_size(T.dtype);
+        char* pw = reinterpret_cast<char*>(powers[i]);
+        const int64_t ps = (int64_t)T.bp * T.ldp;
+        GemmDesc& g = pr[u];
+        g.kclass = POET_K_CHAIN;
+        g.compute = BF16; g.M = g.N = g.K = T.bp; g.batch = T.nprim;
+        g.A = pw; g.lda = T.ldp; g.sA = ps; g.a_dt = BF16; g.a_kmajor = 1;
+        g.B = pw + (size_t)(step - 1) * T.plen * esz; g.ldb = T.ldp; g.sB = ps; g.b_dt = BF16; g.b_kmajor = 0;
+        if (step < c.k) { g.C = pw + (size_t)step * T.plen * esz; g.c_dt = BF16; g.ldc = T.ldp; g.sC = ps; }
+        else { g.C = prim[i]; g.c_dt = F32; g.ldc = T.bp; g.sC = (int64_t)T.bp * T.bp; }
+        g.part = part; g.part_elems = part_elems;
+      }
+      if (fast_gemm_group_eligible(pr, n)) {
+        HIP_TRY(launch_fast_gemm_group(pr, n, st));
+      } else {
+        for (int u = 0; u < n; ++u) HIP_TRY(launch_gemm(pr[u], st));
+      }
+    }
+    FinGroup fg;
+    for (int i : c.idx) {
+      FinSide& f = fg.s[fg.n++];
+      f.theta = theta[i]; f.powers = powers[i]; f.prim = prim[i]; f.mode = S[i].mode; f.d = S[i].d; f.bp = S[i].bp;
+      f.nprim = S[i].nprim; f.k = S[i].k; f.dt = S[i].dtype; f.ldp = S[i].ldp;
+    }
+    HIP_TRY(launch_chain_finalize_group(fg, st));
   }
   // the operand copies of sides the chain did not finish (k = 0, or built one by one)
   for (int i = 0; i < count; ++i) {

@@ -142,13 +142,23 @@ class PoetLinear:
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
                               dY, dX, self.dthetaR, self.dthetaP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
-    def backward_act_prims(self, X, Z, dY, dX, stream=None):
-        """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
-        PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
+    def _dprims(self):
         if getattr(self, "dprimR", None) is None:
             torch = _torch()
             self.dprimR = torch.empty(B.poet_prim_len(self.L.R), dtype=torch.float32, device=self.dev)
             self.dprimP = torch.empty(B.poet_prim_len(self.L.P), dtype=torch.float32, device=self.dev)
+
+    def backward_prims(self, X, dY, dX, W=None, stream=None):
+        """Weight-side backward up to the primitive gradients dprimR, dprimP; PoetGroup.finish_backward turns them
+        into dthetaR, dthetaP for many linears at once."""
+        self._dprims()
+        B.poet_linear_bwd_prims(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, W, X, dY, dX,
+                                self.dprimR, self.dprimP, self.ws, stream)
+
+    def backward_act_prims(self, X, Z, dY, dX, stream=None):
+        """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
+        PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
+        self._dprims()
         B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
                                     self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
@@ -167,7 +177,8 @@ class PoetGroup:
 
     ``build`` runs the Cayley-Neumann build of both sides of every linear (poet_build_orthogonal_group);
     ``finish_backward`` runs the Neumann adjoint and skew projection of every side from the primitive gradients
-    that ``PoetLinear.backward_act_prims`` left (poet_adjoint_group). Results match the per-linear calls."""
+    that ``PoetLinear.backward_act_prims`` / ``backward_prims`` left (poet_adjoint_group). Results match the
+    per-linear calls up to the float32 summation order of split products."""
 
     def __init__(self, linears):
         torch = _torch()
@@ -197,7 +208,7 @@ class PoetGroup:
     def finish_backward(self, stream=None):
         for pl in self.linears:
             if getattr(pl, "dprimR", None) is None:
-                raise RuntimeError("finish_backward needs backward_act_prims on every linear of the group first")
+                raise RuntimeError("finish_backward needs backward_prims or backward_act_prims on every linear first")
         dprims = [t for pl in self.linears for t in (pl.dprimR, pl.dprimP)]
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
         dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]

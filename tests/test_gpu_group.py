@@ -26,17 +26,26 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-# (mode, d, b, k, dtype): fused-chain sides of several block sizes (one ragged), an FS side, and sides the group
-# leaves to the one-side path (float32, a block size that is not a multiple of 8) or that need no chain (k = 0)
+# (mode, d, b, k, dtype): fused-chain sides of several block sizes (one ragged), an FS side; sides whose chain runs as
+# grouped GEMMs (FS primitives of 1050 and 300, padded row pitch; BS blocks of 512, ragged); and sides the group
+# leaves to the one-side path (float32, a block of 100) or that need no chain (k = 0)
 SIDES = [
     (PI.MODE_BS, 520, 256, 5, PI.DT_BF16),
     (PI.MODE_BS, 384, 128, 4, PI.DT_BF16),
     (PI.MODE_BS, 200, 64, 3, PI.DT_BF16),
     (PI.MODE_FS, 300, 128, 5, PI.DT_BF16),
+    (PI.MODE_FS, 2100, 1050, 5, PI.DT_BF16),
+    (PI.MODE_FS, 4000, 1050, 5, PI.DT_BF16),
+    (PI.MODE_FS, 700, 300, 5, PI.DT_BF16),
+    (PI.MODE_BS, 1100, 512, 2, PI.DT_BF16),
     (PI.MODE_BS, 200, 64, 3, PI.DT_F32),
     (PI.MODE_BS, 300, 100, 2, PI.DT_BF16),
     (PI.MODE_BS, 256, 64, 0, PI.DT_BF16),
 ]
+# sides whose chain runs as GEMMs: the grouped launches may split K differently from a one-side build, so those
+# results agree to the float32 summation order, not bit for bit
+GEMM_CHAIN = {i for i, (mode, d, b, k, dt) in enumerate(SIDES) if dt == PI.DT_BF16 and k > 0 and b >= 128 and
+              (b > 256 or b % 8)}
 
 
 def _sides():
@@ -45,11 +54,14 @@ def _sides():
 
 
 def _thetas(std, seed=5):
+    """Skew parameters of every side at standard deviation std, capped at 0.25 / sqrt(b) so that ||Q||_2 (about
+    2 std sqrt(b)) stays near 0.5: the truncated series converges, and summation-order differences between launch
+    shapes are not amplified by a diverging chain."""
     rng = np.random.default_rng(seed)
     out = []
     for mode, d, b, k, dt in SIDES:
         n = PI.n_theta(PI.SideSpec(mode, d, b, k, dt))
-        out.append((rng.standard_normal(n) * std).astype(np.float32))
+        out.append((rng.standard_normal(n) * min(std, 0.25 / np.sqrt(b))).astype(np.float32))
     return out
 
 
@@ -88,9 +100,15 @@ def test_build_group_equals_one_side_builds():
            else None for spec, s in zip(SIDES, sides)]
     group = _build_all(sides, thetas_d, grouped=True, ops=ops)
     for i, ((pa, wa), (pb, wb)) in enumerate(zip(single, group)):
-        assert torch.equal(pa, pb), f"prim of side {i} {SIDES[i]}"
-        if wa is not None:
-            assert torch.equal(wa, wb), f"powers of side {i} {SIDES[i]}"
+        if i in GEMM_CHAIN:
+            eye = np.eye(SIDES[i][2]).ravel()
+            d = (to_np(pa).reshape(-1, eye.size) - eye).ravel()
+            assert rel(to_np(pb).reshape(-1, eye.size) - eye, d.reshape(-1, eye.size)) <= 1e-4, f"prim of side {i}"
+            assert rel(to_np(wb), to_np(wa)) <= 1e-2, f"powers of side {i}"
+        else:
+            assert torch.equal(pa, pb), f"prim of side {i} {SIDES[i]}"
+            if wa is not None:
+                assert torch.equal(wa, wb), f"powers of side {i} {SIDES[i]}"
         if ops[i] is None:
             continue
         # ops = bf16(F) and bf16(F^T) per block, zero outside the block's c x c corner, bit for bit
@@ -188,4 +206,51 @@ def test_block_backward_grouped_matches_per_linear():
         oP = rel(to_np(pl.dthetaP)[:nP], ref["dthetaP"])
         announce(f"{lin.name}: grouped vs per-linear {eR:.2e} {eP:.2e}; vs oracle {oR:.2e} {oP:.2e}")
         assert eR <= 1e-5 and eP <= 1e-5, (lin.name, eR, eP)
+        assert oR <= TOL[PI.DT_BF16] and oP <= TOL[PI.DT_BF16], (lin.name, oR, oP)
+
+
+def test_block_backward_grouped_matches_per_linear_weight_path_fs():
+    """Weight-side linears with FS sides (s = 300 and 520 per side, GEMM chains) and one BS linear: grouped build,
+    backward to the primitive gradients and grouped adjoint against the per-linear calls and the oracle."""
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
+    from tests.gpu_util import oracle_indices
+    announce("grouped block backward, weight side, FS")
+    specs = [make_linear("fs0", 600, 1040, 256, PI.MODE_FS, 300, 520, 5, PI.DT_BF16, linear_id=7),
+             make_linear("fs1", 1040, 600, 256, PI.MODE_FS, 520, 300, 5, PI.DT_BF16, linear_id=8),
+             make_linear("bs", 520, 384, 256, PI.MODE_BS, 256, 128, 4, PI.DT_BF16, linear_id=9)]
+    lins, data = [], []
+    for lin in specs:
+        W0, tR, tP, X, dY = PI.gen_linear(94, 0, lin, theta_std=0.01)
+        iR, iP = oracle_indices(lin, 17)
+        pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP, seed=17,
+                        linear_id=lin.linear_id, idxR=iR, idxP=iP, path="weight")
+        Xd, dYd = put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy)
+        lins.append(pl)
+        data.append((lin, W0, tR, tP, X, dY, iR, iP, Xd, dYd, pl.alloc_act(lin.T, pl.L.ldy),
+                     pl.alloc_act(lin.T, pl.L.ldx), pl.alloc_W()))
+    group = PoetGroup(lins)
+    for pl, (lin, W0, tR, tP, X, dY, iR, iP, Xd, dYd, Y, dX, W) in zip(lins, data):
+        pl.build()
+        pl.forward(Xd, Y, W_out=W)
+        pl.backward(Xd, dYd, dX, W=W)
+    torch.cuda.synchronize()
+    per = [(pl.dthetaR.clone(), pl.dthetaP.clone(), d[11].clone()) for pl, d in zip(lins, data)]
+    for pl in lins:
+        pl.dthetaR.fill_(float("nan"))
+        pl.dthetaP.fill_(float("nan"))
+    group.build()
+    for pl, (lin, W0, tR, tP, X, dY, iR, iP, Xd, dYd, Y, dX, W) in zip(lins, data):
+        pl.forward(Xd, Y, W_out=W)
+        pl.backward_prims(Xd, dYd, dX, W=W)
+    group.finish_backward()
+    torch.cuda.synchronize()
+    for pl, p, (lin, W0, tR, tP, X, dY, iR, iP, Xd, dYd, Y, dX, W) in zip(lins, per, data):
+        ref = O.linear_bwd(O.Side.of(lin.R), O.Side.of(lin.P), W0, tR, tP, iR, iP, X, dY)
+        nR, nP = B.poet_theta_len(pl.L.R), B.poet_theta_len(pl.L.P)
+        eR, eP = rel(to_np(pl.dthetaR)[:nR], to_np(p[0])[:nR]), rel(to_np(pl.dthetaP)[:nP], to_np(p[1])[:nP])
+        oR, oP = rel(to_np(pl.dthetaR)[:nR], ref["dthetaR"]), rel(to_np(pl.dthetaP)[:nP], ref["dthetaP"])
+        eX = rel(to_np(dX)[:, :lin.n], to_np(p[2])[:, :lin.n])
+        announce(f"{lin.name}: grouped vs per-linear {eR:.2e} {eP:.2e} dX {eX:.2e}; vs oracle {oR:.2e} {oP:.2e}")
+        assert eR <= 1e-3 and eP <= 1e-3 and eX <= 1e-3, (lin.name, eR, eP, eX)
         assert oR <= TOL[PI.DT_BF16] and oP <= TOL[PI.DT_BF16], (lin.name, oR, oP)
