@@ -7,7 +7,9 @@
 // Operands go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16
 // bytes at the wave's LDS base + 16 l, from any global address it chooses), in a two-stage ring: the DMA of
 // K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile, placed before the last k-step so that the
-// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs. Both stage layouts are 32 KB:
+// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs. A k-step's fragment reads for the
+// next k-step are issued between its MFMAs (one MFMA, two reads), which measured ~3% faster than one burst.
+// Both stage layouts are 32 KB:
 //   K-major operand: 256 rows x 128 B; the 16-byte chunk index is XOR-ed with f(row mod 32) =
 //     (row & 7) ^ ((row >> 3) & 3): 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
 //     groups, so the ds_read_b128 fragments are conflict-free;
@@ -337,12 +339,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int a = 0; a < 4; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
 #pragma unroll
       for (int b = 0; b < 4; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][b], acc[a][b], 0, 0, 0);
+      // the fragment reads go out between the MFMAs (one MFMA, two reads), not as one burst ahead of them
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (kt + 1 < nk) {
