@@ -29,33 +29,75 @@ __device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
 // every primitive before p is a full bp x bp block
 __device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
 
-// prim = I + coef Q and the first saved power Q (dtype q_dt, row pitch ldq) of side blockIdx.y of the table
-__global__ void k_theta_prep(const PrepGroup G) {
+// Q of one 32 x 32 tile pair of a primitive from its packed parameters. Workgroup (256 threads) = tile pair
+// (ti, tj), ti <= tj, of primitive p; thread (col = tid % 32, row0 = tid / 32) holds rows row0 + 8u, u = 0..3.
+// up[u] = Q(32 ti + r, 32 tj + col) (upper tile, read row-wise from the packed strict upper triangle: coalesced),
+// lo[u] = Q(32 tj + r, 32 ti + col) = -Q(32 ti + col, 32 tj + r) (the transpose, through LDS). On a diagonal tile
+// (ti == tj) up holds the whole tile and lo is unused.
+__device__ __forceinline__ void tile_pair_of(int tpair, int bp, int& ti, int& tj) {
+  const int nt = (bp + 31) / 32;
+  int rem = tpair;
+  ti = 0;
+  while (rem >= nt - ti) { rem -= nt - ti; ++ti; }
+  tj = ti + rem;
+}
+__device__ __forceinline__ void q_tile_pair(const float* __restrict__ theta, int64_t toff, int c, int ti, int tj,
+                                            float (*tr)[33], float up[4], float lo[4]) {
+  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = row0 + 8 * u, i = ti * 32 + r, j = tj * 32 + col;
+    up[u] = (i < j && j < c) ? theta[toff + tri_pos(i, j, c)] : 0.f;
+    tr[r][col] = up[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = row0 + 8 * u;
+    if (ti == tj) {
+      if (r > col) up[u] = -tr[col][r];  // the lower half of a diagonal tile
+      lo[u] = 0.f;
+    } else {
+      lo[u] = -tr[col][r];
+    }
+  }
+}
+
+// prim = I + coef Q and the first saved power Q (dtype q_dt, row pitch ldq) of side blockIdx.z of the table,
+// primitive blockIdx.y, tile pair blockIdx.x
+__global__ __launch_bounds__(256) void k_theta_prep(const PrepGroup G) {
+  __shared__ float tr[32][33];
   PrepSide a;
   {
-    const PrepSide& t = G.s[blockIdx.y];
+    const PrepSide& t = G.s[blockIdx.z];
     a.theta = keep_s(t.theta); a.prim = keep_s(t.prim); a.q = keep_s(t.q); a.q_dt = keep_s(t.q_dt);
     a.ldq = keep_s(t.ldq); a.mode = keep_s(t.mode); a.d = keep_s(t.d); a.bp = keep_s(t.bp);
     a.nprim = keep_s(t.nprim); a.coef = keep_s(t.coef);
   }
-  const int bp = a.bp;
-  const int64_t total = (int64_t)a.nprim * bp * bp;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int p = (int)(e / ((int64_t)bp * bp));
-    const int rem = (int)(e - (int64_t)p * bp * bp);
-    const int i = rem / bp, j = rem % bp;
-    const int c = prim_size(a.mode, a.d, bp, p);
-    float q = 0.f;
-    if (i < c && j < c && i != j) {
-      const int64_t off = theta_off(bp, p);
-      q = i < j ? a.theta[off + tri_pos(i, j, c)] : -a.theta[off + tri_pos(j, i, c)];
-    }
-    a.prim[e] = (i == j ? 1.f : 0.f) + a.coef * q;
-    if (a.q) {
-      const int64_t o = ((int64_t)p * bp + i) * a.ldq + j;
-      if (a.q_dt == BF16) reinterpret_cast<__bf16*>(a.q)[o] = (__bf16)q;
-      else reinterpret_cast<float*>(a.q)[o] = q;
+  const int bp = a.bp, p = blockIdx.y, nt = (bp + 31) / 32;
+  if (p >= a.nprim || (int)blockIdx.x >= nt * (nt + 1) / 2) return;
+  int ti, tj;
+  tile_pair_of(blockIdx.x, bp, ti, tj);
+  const int c = prim_size(a.mode, a.d, bp, p);
+  float up[4], lo[4];
+  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);
+  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;
+  float* prim = a.prim + (int64_t)p * bp * bp;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1 && ti == tj) break;
+    const int ri = h ? tj : ti, cj = h ? ti : tj;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = ri * 32 + row0 + 8 * u, j = cj * 32 + col;
+      if (i >= bp || j >= bp) continue;
+      const float q = h ? lo[u] : up[u];
+      prim[(int64_t)i * bp + j] = (i == j ? 1.f : 0.f) + a.coef * q;
+      if (a.q) {
+        const int64_t o = ((int64_t)p * bp + i) * a.ldq + j;
+        if (a.q_dt == BF16) reinterpret_cast<__bf16*>(a.q)[o] = (__bf16)q;
+        else reinterpret_cast<float*>(a.q)[o] = q;
+      }
     }
   }
 }
@@ -346,30 +388,40 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
 }
 
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
-// (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1. Side blockIdx.y of the table.
-__global__ void k_chain_finalize(const FinGroup G) {
+// (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1. Side blockIdx.z, primitive blockIdx.y, tile pair
+// blockIdx.x (the same tiling as k_theta_prep).
+__global__ __launch_bounds__(256) void k_chain_finalize(const FinGroup G) {
+  __shared__ float tr[32][33];
   FinSide a;
   {
-    const FinSide& t = G.s[blockIdx.y];
+    const FinSide& t = G.s[blockIdx.z];
     a.theta = keep_s(t.theta); a.powers = keep_s(t.powers); a.prim = keep_s(t.prim); a.mode = keep_s(t.mode);
     a.d = keep_s(t.d); a.bp = keep_s(t.bp); a.nprim = keep_s(t.nprim); a.k = keep_s(t.k); a.dt = keep_s(t.dt);
     a.ldp = keep_s(t.ldp);
   }
-  const int bp = a.bp, k = a.k, nprim = a.nprim;
-  const int64_t pp = (int64_t)bp * bp, total = (int64_t)nprim * pp;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int p = (int)(e / pp);
-    const int rem = (int)(e - (int64_t)p * pp);
-    const int i = rem / bp, j = rem % bp;
-    const int c = prim_size(a.mode, a.d, bp, p);
-    float q = 0.f;
-    if (i < c && j < c && i != j) {
-      const int64_t off = theta_off(bp, p);
-      q = i < j ? a.theta[off + tri_pos(i, j, c)] : -a.theta[off + tri_pos(j, i, c)];
+  const int bp = a.bp, p = blockIdx.y, nt = (bp + 31) / 32;
+  if (p >= a.nprim || (int)blockIdx.x >= nt * (nt + 1) / 2) return;
+  int ti, tj;
+  tile_pair_of(blockIdx.x, bp, ti, tj);
+  const int c = prim_size(a.mode, a.d, bp, p);
+  float up[4], lo[4];
+  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);
+  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;
+  float* prim = a.prim + (int64_t)p * bp * bp;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1 && ti == tj) break;
+    const int ri = h ? tj : ti, cj = h ? ti : tj;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = ri * 32 + row0 + 8 * u, j = cj * 32 + col;
+      if (i >= bp || j >= bp) continue;
+      float s2 = 0.f;
+      for (int t = 2; t <= a.k; ++t)
+        s2 += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * a.nprim + p) * bp + i) * a.ldp + j);
+      const int64_t e = (int64_t)i * bp + j;
+      prim[e] = (i == j ? 1.f : 0.f) + 2.f * (h ? lo[u] : up[u]) + 2.f * s2 + prim[e];
     }
-    float s = 0.f;
-    for (int t = 2; t <= k; ++t) s += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * nprim + p) * bp + i) * a.ldp + j);
-    a.prim[e] = (i == j ? 1.f : 0.f) + 2.f * q + 2.f * s + a.prim[e];
   }
 }
 
@@ -387,8 +439,12 @@ hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st) {
     bytes += (double)total * (8 + 4 + (a.k - 1) * dtype_size(a.dt));
   }
   if (most == 0) return hipSuccess;
+  int bp = 0, ny = 0;
+  for (int i = 0; i < g.n; ++i) { bp = std::max(bp, g.s[i].bp); ny = std::max(ny, g.s[i].nprim); }
+  if (ny > 65535) return hipErrorInvalidValue;
+  const int nt = (bp + 31) / 32;
   ProfScope prof(7, st, 0, bytes);
-  hipLaunchKernelGGL(k_chain_finalize, dim3(grid_for((size_t)most, kThreads, 4096), g.n), dim3(kThreads), 0, st, g);
+  hipLaunchKernelGGL(k_chain_finalize, dim3(nt * (nt + 1) / 2, ny, g.n), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 
@@ -461,8 +517,12 @@ hipError_t launch_theta_prep_group(const PrepGroup& g, hipStream_t st) {
     bytes += (double)total * (4 + 4 + (a.q ? dtype_size(a.q_dt) : 0));
   }
   if (most == 0) return hipSuccess;
+  int bp = 0, ny = 0;
+  for (int i = 0; i < g.n; ++i) { bp = std::max(bp, g.s[i].bp); ny = std::max(ny, g.s[i].nprim); }
+  if (ny > 65535) return hipErrorInvalidValue;
+  const int nt = (bp + 31) / 32;
   ProfScope prof(7, st, 0, bytes);
-  hipLaunchKernelGGL(k_theta_prep, dim3(grid_for(most, kThreads, 4096), g.n), dim3(kThreads), 0, st, g);
+  hipLaunchKernelGGL(k_theta_prep, dim3(nt * (nt + 1) / 2, ny, g.n), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 
