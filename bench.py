@@ -227,8 +227,11 @@ def main():
         B.poet_profile_enable(rep == 2)
         m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         m0.record()
-        for e in lins:
-            e["pl"].merge()
+        if group is not None:
+            group.merge()
+        else:
+            for e in lins:
+                e["pl"].merge()
         m1.record()
         torch.cuda.synchronize()
         if rep == 1:

@@ -241,6 +241,20 @@ poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* t
                        const float* primR, const float* primP, int32_t* idxR, int32_t* idxP, uint64_t seed,
                        uint32_t linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes, void* stream);
 
+/* poet_merge for count weights (for instance the linears of a transformer block), with the in-place
+ * block-diagonal merges of all of them in shared launches (one split of every factor's deltas, one P pass, one R
+ * pass, one theta reset) and the others (FS sides, blocks above 256) one after another. Entry i of each table
+ * belongs to layers[i], with poet_merge's meaning; W0_shadow, idxR and idxP are nullable tables (NULL: no
+ * shadows, no index sets), and linear_id[i] is linear i's sampler id. The weights and shadows of the group must
+ * not overlap (checked: POET_E_ARG). Results are those of poet_merge on each weight.
+ * ws: at least poet_merge_group_workspace_bytes(count, layers) bytes. */
+size_t poet_merge_group_workspace_bytes(int32_t count, const poet_layer* layers);
+poet_status poet_merge_group(int32_t count, const poet_layer* layers, float* const* W0, void* const* W0_shadow,
+                             float* const* thetaR, float* const* thetaP, const float* const* primR,
+                             const float* const* primP, int32_t* const* idxR, int32_t* const* idxP, uint64_t seed,
+                             const uint32_t* linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* ---- diagnostics ------------------------------------------------------------------------------------ */
 
 /* One internal GEMM of the library, exposed for kernel-level testing (not part of the layer's hot path):

@@ -28,7 +28,8 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
-           "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims")
+           "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
+           "poet_merge_group_workspace_bytes", "poet_merge_group")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE = range(9)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
     L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_merge_group_workspace_bytes.argtypes = [I32, P(poet_layer)]
+    L.poet_merge_group_workspace_bytes.restype = S
+    L.poet_merge_group.argtypes = [I32, P(poet_layer), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), U64,
+                                   P(U32), U32, VP, S, VP]
     for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge",
                "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act"):
         getattr(L, nm).restype = ctypes.c_int
@@ -486,3 +491,51 @@ def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR,
         seed, linear_id, epoch_next, _ptr(ws, "ws", need, allow_none=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_merge")
+
+
+def _layer_array(layers):
+    arr = (poet_layer * max(1, len(layers)))()
+    for i, L in enumerate(layers):
+        arr[i] = L
+    return arr
+
+
+def poet_merge_group_workspace_bytes(layers) -> int:
+    return int(lib().poet_merge_group_workspace_bytes(len(layers), _layer_array(layers)))
+
+
+def poet_merge_group(layers, W0s, shadows, thetaRs, thetaPs, primRs, primPs, idxRs, idxPs, seed: int, linear_ids,
+                     epoch_next: int, ws=None, stream=None):
+    """poet_merge for every layer in ``layers`` (lists of equal length); ``shadows``, ``idxRs`` and ``idxPs`` may
+    be None (no shadows, no index sets) or lists with None entries."""
+    n = len(layers)
+    shadows = [None] * n if shadows is None else shadows
+    idxRs = [None] * n if idxRs is None else idxRs
+    idxPs = [None] * n if idxPs is None else idxPs
+    if not all(len(t) == n for t in (W0s, shadows, thetaRs, thetaPs, primRs, primPs, idxRs, idxPs, linear_ids)):
+        raise ValueError("every table must have one entry per layer")
+    need = poet_merge_group_workspace_bytes(layers)
+    if ws is None and need > 0:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=W0s[0].device)
+    bs = [_layer_bytes(L) for L in layers]
+    idx = lambda i: f"[{i}]"
+    w0 = _ptr_table(W0s, ["W0s" + idx(i) for i in range(n)], [b["W0"] for b in bs], ["float32"] * n, [False] * n)
+    sh = _ptr_table(shadows, ["shadows" + idx(i) for i in range(n)], [b["W"] for b in bs],
+                    [_dt_name(L.act_dtype) for L in layers], [True] * n)
+    tR = _ptr_table(thetaRs, ["thetaRs" + idx(i) for i in range(n)], [4 * poet_theta_len(L.R) for L in layers],
+                    ["float32"] * n, [poet_theta_len(L.R) == 0 for L in layers])
+    tP = _ptr_table(thetaPs, ["thetaPs" + idx(i) for i in range(n)], [4 * poet_theta_len(L.P) for L in layers],
+                    ["float32"] * n, [poet_theta_len(L.P) == 0 for L in layers])
+    pR = _ptr_table(primRs, ["primRs" + idx(i) for i in range(n)], [4 * poet_prim_len(L.R) for L in layers],
+                    ["float32"] * n, [False] * n)
+    pP = _ptr_table(primPs, ["primPs" + idx(i) for i in range(n)], [4 * poet_prim_len(L.P) for L in layers],
+                    ["float32"] * n, [False] * n)
+    iR = _ptr_table(idxRs, ["idxRs" + idx(i) for i in range(n)], [4 * L.R.b for L in layers], ["int32"] * n,
+                    [True] * n)
+    iP = _ptr_table(idxPs, ["idxPs" + idx(i) for i in range(n)], [4 * L.P.b for L in layers], ["int32"] * n,
+                    [True] * n)
+    ids = (ctypes.c_uint32 * max(1, n))(*[int(v) for v in linear_ids])
+    st = lib().poet_merge_group(n, _layer_array(layers), w0, sh, tR, tP, pR, pP, iR, iP, seed, ids, epoch_next,
+                                _ptr(ws, "ws", need, allow_none=True),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_merge_group")

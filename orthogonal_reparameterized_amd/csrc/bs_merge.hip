@@ -21,6 +21,7 @@
 //                     into LDS by DMA (global_load_lds), one strip (64 KB) at a time; two workgroups share a CU.
 // The R pass also writes the bf16 (or float32) shadow copy of the merged weight.
 #include <type_traits>
+#include <vector>
 
 #include "poet.h"
 #include "strip_mma.h"
@@ -45,6 +46,14 @@ struct MergeArgs {
   const char* split;   // pre-split deltas: strip s of block b at split + (b * nstr + s) * STRIP_BYTES
   int nstr;            // strips per block in that buffer: ceil(bp / 64)
   void* shadow; int sh_dt; int64_t ld_sh;  // R pass: copy of the merged weight (nullable)
+  int vec;             // P pass: rows 16-byte aligned and whole 8-column groups in every block (float4 loads)
+  int first;           // first logical workgroup of this entry in its launch
+};
+// The passes of up to MAXG weights (same pass, same k-step class) in one launch: entry e owns logical workgroups
+// [a[e].first, a[e + 1].first), and total is the sum over the entries.
+struct MergeGroup {
+  int n = 0, total = 0;
+  MergeArgs a[MAXG];
 };
 
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& h, bf16x8& l) {
@@ -58,11 +67,28 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& h, bf16x8& l
 // Pre-split factor deltas. For block b (size c = min(bp, d - b bp)) and strip line r, 16-byte chunk q:
 //   value(r, k) = F_b[k][r] - [k == r] (transpose: the P pass streams columns of dP) or F_b[r][k] - [r == k],
 // zero outside r, k < c; hi at line r of the strip's first 32 KB, lo at the same place in its second 32 KB.
-__global__ void k_merge_split(const float* __restrict__ prim, int bp, int d, int nblk, int nstr, int transpose,
-                              char* __restrict__ out) {
+// Grouped over up to 2 MAXG factors: workgroups [a[e].wg0, a[e + 1].wg0) take factor e.
+struct SplitEntry {
+  const float* prim; char* out;
+  int bp, d, nblk, nstr, transpose, wg0;
+};
+struct SplitGroup {
+  int n = 0;
+  SplitEntry a[2 * MAXG];
+};
+__global__ void k_merge_split(const SplitGroup G) {
+  int e = 0;
+  for (int q = 1; q < G.n; ++q)
+    if ((int)blockIdx.x >= G.a[q].wg0) e = q;
+  const SplitEntry& ge = G.a[e];
+  const float* prim = keep_s(ge.prim);
+  char* out = keep_s(ge.out);
+  const int bp = keep_s(ge.bp), d = keep_s(ge.d), nblk = keep_s(ge.nblk), nstr = keep_s(ge.nstr);
+  const int transpose = keep_s(ge.transpose), wg0 = keep_s(ge.wg0);
+  const int nwg = (e + 1 < G.n ? G.a[e + 1].wg0 : (int)gridDim.x) - wg0;
   const int lines = nstr * 64;
   const int64_t total = (int64_t)nblk * lines * 32;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t t = (int64_t)(blockIdx.x - wg0) * blockDim.x + threadIdx.x; t < total; t += (int64_t)nwg * blockDim.x) {
     // transpose: consecutive threads take consecutive lines (coalesced column reads); else consecutive chunks
     int r, q, b;
     if (transpose) { r = (int)(t % lines); q = (int)((t / lines) % 32); b = (int)(t / ((int64_t)lines * 32)); }
@@ -104,19 +130,30 @@ __device__ __forceinline__ void bstore(float v, __amdgpu_buffer_rsrc_t r, uint32
 
 // NK: k-steps of 16 covering the block size (4, 8 or 16); loops over them are fully unrolled with no branches, so
 // every load is issued up front (values outside the block are replaced by zeros)
-template <bool RS, bool VEC, int NK>
-__global__ __launch_bounds__(MT, 2) void merge_pass_kernel(const MergeArgs a) {
+template <bool RS, int NK>
+__global__ __launch_bounds__(MT, 2) void merge_pass_kernel(const MergeGroup G) {
   __shared__ __attribute__((aligned(16))) char buf[STRIP_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pdim = RS ? a.n : a.m;    // panel dimension: W columns (R pass) or rows (P pass)
-  const int bdim = RS ? a.m : a.n;    // block dimension
-  const int npan = (pdim + PANEL - 1) / PANEL, nb = npan * a.nblk;
   // XCD-aware order: hardware workgroup b runs on XCD b % 8; consecutive logical ids (the panels of one block,
   // which stream the same strips) go to one XCD
-  const int per = (nb + 7) / 8;
+  const int per = (G.total + 7) / 8;
   const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (L >= nb) return;
-  const int blk = L / npan, pan = L % npan;
+  if (L >= G.total) return;
+  int e = 0;
+  for (int q = 1; q < G.n; ++q)
+    if (L >= G.a[q].first) e = q;
+  MergeArgs a;
+  {
+    const MergeArgs& ga = G.a[e];
+    a.W = keep_s(ga.W); a.ld = keep_s(ga.ld); a.m = keep_s(ga.m); a.n = keep_s(ga.n);
+    a.bp = keep_s(ga.bp); a.nblk = keep_s(ga.nblk); a.split = keep_s(ga.split); a.nstr = keep_s(ga.nstr);
+    a.shadow = keep_s(ga.shadow); a.sh_dt = keep_s(ga.sh_dt); a.ld_sh = keep_s(ga.ld_sh);
+    a.vec = keep_s(ga.vec); a.first = keep_s(ga.first);
+  }
+  const int pdim = RS ? a.n : a.m;    // panel dimension: W columns (R pass) or rows (P pass)
+  const int bdim = RS ? a.m : a.n;    // block dimension
+  const int npan = (pdim + PANEL - 1) / PANEL;
+  const int blk = (L - a.first) / npan, pan = (L - a.first) % npan;
   const int b0 = blk * a.bp, c = min(a.bp, bdim - b0);
   const int nstr = (c + 63) / 64;
   const int line0 = pan * PANEL + wave * 32;            // this wave's first panel line
@@ -145,7 +182,7 @@ __global__ __launch_bounds__(MT, 2) void merge_pass_kernel(const MergeArgs a) {
           const float f = bload(W, o + v * ld4);
           x[u][v] = pin && k + v < c ? f : 0.f;
         }
-      } else if constexpr (VEC) {  // 16-byte aligned rows, c % 8 == 0: two float4 loads
+      } else if (a.vec) {  // 16-byte aligned rows, c % 8 == 0: two float4 loads
         const uint32_t o = (uint32_t)p * ld4 + (uint32_t)(b0 + k) * 4;
         const f32x4 u0 = bload4(W, o);
         const f32x4 u1 = bload4(W, o + 16);
@@ -281,10 +318,44 @@ __global__ __launch_bounds__(MT, 2) void merge_pass_kernel(const MergeArgs a) {
 }
 
 template <int NK>
-void launch_pass(bool rside, bool vec, unsigned grid, const MergeArgs& a, hipStream_t st) {
-  if (rside) hipLaunchKernelGGL((merge_pass_kernel<true, false, NK>), dim3(grid), dim3(MT), 0, st, a);
-  else if (vec) hipLaunchKernelGGL((merge_pass_kernel<false, true, NK>), dim3(grid), dim3(MT), 0, st, a);
-  else hipLaunchKernelGGL((merge_pass_kernel<false, false, NK>), dim3(grid), dim3(MT), 0, st, a);
+void launch_pass(bool rside, const MergeGroup& g, hipStream_t st) {
+  const unsigned grid = (unsigned)((g.total + 7) / 8 * 8);
+  if (rside) hipLaunchKernelGGL((merge_pass_kernel<true, NK>), dim3(grid), dim3(MT), 0, st, g);
+  else hipLaunchKernelGGL((merge_pass_kernel<false, NK>), dim3(grid), dim3(MT), 0, st, g);
+}
+
+int nk_class(int bp) { return bp <= 64 ? 0 : bp <= 128 ? 1 : 2; }
+
+// one pass (rside) of every item whose factor falls in k-step class cls, MAXG items per launch
+hipError_t launch_pass_class(const MergeItem* it, int n, const std::vector<char*>& split, bool rside, int cls,
+                             hipStream_t st) {
+  MergeGroup g;
+  auto flush = [&]() -> hipError_t {
+    if (g.n == 0) return hipSuccess;
+    if (cls == 0) launch_pass<4>(rside, g, st);
+    else if (cls == 1) launch_pass<8>(rside, g, st);
+    else launch_pass<16>(rside, g, st);
+    g = MergeGroup();
+    return hipGetLastError();
+  };
+  for (int i = 0; i < n; ++i) {
+    const MergeItem& x = it[i];
+    const int bp = rside ? x.bpR : x.bpP, nblk = rside ? x.nR : x.nP;
+    if (x.m <= 0 || x.n <= 0 || nblk <= 0 || nk_class(bp) != cls) continue;
+    MergeArgs& a = g.a[g.n++];
+    a.W = x.W; a.ld = x.ld; a.m = x.m; a.n = x.n; a.bp = bp; a.nblk = nblk; a.split = split[2 * i + (rside ? 1 : 0)];
+    a.nstr = (bp + 63) / 64;
+    a.shadow = rside ? x.shadow : nullptr; a.sh_dt = x.sh_dt; a.ld_sh = x.ld_sh;
+    // float4 loads of the P pass need 16-byte aligned rows and whole 8-column groups in every block
+    a.vec = x.ld % 4 == 0 && reinterpret_cast<uintptr_t>(x.W) % 16 == 0 && bp % 8 == 0 && x.n % 8 == 0;
+    a.first = g.total;
+    g.total += ((rside ? x.n : x.m) + PANEL - 1) / PANEL * nblk;
+    if (g.n == MAXG) {
+      const hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return flush();
 }
 
 }  // namespace
@@ -293,33 +364,57 @@ bool bs_merge_eligible(int bp, int m, int64_t ld) { return bp >= 1 && bp <= MAXB
 
 size_t bs_merge_split_bytes(int bp, int nblk) { return (size_t)nblk * ((bp + 63) / 64) * STRIP_BYTES; }
 
-hipError_t launch_bs_merge_pass(float* W, int64_t ld, int m, int n, int rside, int bp, int nblk, const float* prim,
-                                char* split, void* shadow, int sh_dt, int64_t ld_sh, hipStream_t st) {
-  if (m <= 0 || n <= 0 || nblk <= 0) return hipSuccess;
-  const int nstr = (bp + 63) / 64;
-  const int d = rside ? m : n;
-  const double mn = (double)m * n;
-  ProfScope prof(POET_K_MERGE, st, 6.0 * mn * bp, mn * (8.0 + (rside && shadow ? dtype_size(sh_dt) : 0)));
-  {
-    const int64_t total = (int64_t)nblk * nstr * 64 * 32;
-    const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_merge_split, dim3(grid), dim3(256), 0, st, prim, bp, d, nblk, nstr, rside ? 0 : 1, split);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+size_t bs_merge_group_bytes(const MergeItem* it, int n) {
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += bs_merge_split_bytes(it[i].bpP, it[i].nP) + bs_merge_split_bytes(it[i].bpR, it[i].nR);
+  return b;
+}
+
+hipError_t launch_bs_merge_group(const MergeItem* it, int n, char* split, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < n; ++i) {
+    const double mn = (double)it[i].m * it[i].n;
+    flops += 6.0 * mn * (it[i].bpR + it[i].bpP);
+    bytes += mn * (16.0 + (it[i].shadow ? dtype_size(it[i].sh_dt) : 0));
   }
-  MergeArgs a;
-  a.W = W; a.ld = ld; a.m = m; a.n = n; a.bp = bp; a.nblk = nblk; a.split = split; a.nstr = nstr;
-  a.shadow = rside ? shadow : nullptr; a.sh_dt = sh_dt; a.ld_sh = ld_sh;
-  const int npan = ((rside ? n : m) + PANEL - 1) / PANEL;
-  const int64_t nb = (int64_t)npan * nblk;
-  if (nb > (int64_t)1 << 30) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((nb + 7) / 8 * 8);
-  // float4 loads of the P pass need 16-byte aligned rows and whole 8-column groups in every block
-  const bool vec = ld % 4 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0 && bp % 8 == 0 && n % 8 == 0;
-  if (bp <= 64) launch_pass<4>(rside, vec, grid, a, st);
-  else if (bp <= 128) launch_pass<8>(rside, vec, grid, a, st);
-  else launch_pass<16>(rside, vec, grid, a, st);
-  return hipGetLastError();
+  ProfScope prof(POET_K_MERGE, st, flops, bytes);
+  // every factor's deltas pre-split into its own region of the scratch: P of item i at split[2 i], R at split[2 i + 1]
+  std::vector<char*> sp(2 * (size_t)n);
+  SplitGroup sg;
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    for (int r = 0; r < 2; ++r) {
+      const int bp = r ? it[i].bpR : it[i].bpP, nblk = r ? it[i].nR : it[i].nP;
+      sp[2 * i + r] = split;
+      split += bs_merge_split_bytes(bp, nblk);
+      if (it[i].m <= 0 || it[i].n <= 0 || nblk <= 0) continue;
+      SplitEntry& e = sg.a[sg.n++];
+      e.prim = r ? it[i].primR : it[i].primP; e.out = sp[2 * i + r];
+      e.bp = bp; e.d = r ? it[i].m : it[i].n; e.nblk = nblk; e.nstr = (bp + 63) / 64; e.transpose = r ? 0 : 1;
+      e.wg0 = wg;
+      const int64_t items = (int64_t)nblk * e.nstr * 64 * 32;
+      wg += (int)std::min<int64_t>((items + 255) / 256, 1024);
+      if (sg.n == 2 * MAXG) {
+        hipLaunchKernelGGL(k_merge_split, dim3(wg), dim3(256), 0, st, sg);
+        const hipError_t er = hipGetLastError();
+        if (er != hipSuccess) return er;
+        sg = SplitGroup();
+        wg = 0;
+      }
+    }
+  }
+  if (sg.n > 0) {
+    hipLaunchKernelGGL(k_merge_split, dim3(wg), dim3(256), 0, st, sg);
+    const hipError_t er = hipGetLastError();
+    if (er != hipSuccess) return er;
+  }
+  for (int rside = 0; rside < 2; ++rside)  // every P pass, then every R pass
+    for (int cls = 0; cls < 3; ++cls) {
+      const hipError_t er = launch_pass_class(it, n, sp, rside != 0, cls, st);
+      if (er != hipSuccess) return er;
+    }
+  return hipSuccess;
 }
 
 }  // namespace poet

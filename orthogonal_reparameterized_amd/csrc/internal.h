@@ -142,15 +142,22 @@ struct ApplyArgs {
 bool bs_apply_eligible(int bpR, int bpP, const float* W0, int64_t ldw, const float* primR, const float* primP);
 hipError_t launch_bs_apply(const ApplyArgs& c, hipStream_t st);
 
-// In-place merge pass of a block-diagonal factor (bs_merge.hip), blocks bp <= 256, float32 accuracy:
-//   rside = 0:  W[:, J] <- W[:, J] F_J for every block J of the columns (F = P, blocks along n)
-//   rside = 1:  W[I, :] <- F_I W[I, :] for every block I of the rows (F = R, blocks along m); also writes
-//               shadow (dtype sh_dt, row pitch ld_sh) when non-null
-// prim: nblk float32 bp x bp blocks; split: bs_merge_split_bytes(bp, nblk) bytes of scratch.
+// In-place merge of block-diagonal factors into W0 (bs_merge.hip), blocks bp <= 256, float32 accuracy, for
+// several weights at once: every item's factor deltas are pre-split in one launch, then
+//   P pass:  W[:, J] <- W[:, J] F_J for every block J of the columns (F = P, blocks along n), all items together
+//   R pass:  W[I, :] <- F_I W[I, :] for every block I of the rows (F = R, blocks along m), all items together;
+//            also writes shadow (dtype sh_dt, row pitch ld_sh) when non-null
+// primR / primP: nR / nP float32 bpR x bpR / bpP x bpP blocks. The items' W (and shadows) must not overlap.
+struct MergeItem {
+  float* W = nullptr; int64_t ld = 0; int m = 0, n = 0;
+  int bpR = 0, nR = 0; const float* primR = nullptr;
+  int bpP = 0, nP = 0; const float* primP = nullptr;
+  void* shadow = nullptr; int sh_dt = BF16; int64_t ld_sh = 0;
+};
 bool bs_merge_eligible(int bp, int m, int64_t ld);  // W0 (m x ld floats) under 2 GB
 size_t bs_merge_split_bytes(int bp, int nblk);
-hipError_t launch_bs_merge_pass(float* W, int64_t ld, int m, int n, int rside, int bp, int nblk, const float* prim,
-                                char* split, void* shadow, int sh_dt, int64_t ld_sh, hipStream_t st);
+size_t bs_merge_group_bytes(const MergeItem* it, int n);  // scratch of launch_bs_merge_group
+hipError_t launch_bs_merge_group(const MergeItem* it, int n, char* split, hipStream_t st);
 
 // Block-diagonal factor applied to bf16 activations (act_apply.hip): out[t, block] = in[t, block] B_block for T
 // tokens of dimension d, blocks bp <= 256 (a multiple of 8), with the operand B = F^T (trans) or F given as bf16
@@ -190,6 +197,9 @@ hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d
 hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
                               int d, int bp, int nprim, float* dtheta, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
+struct FillEntry { float* p = nullptr; size_t n = 0; };
+struct FillGroup { int n = 0; FillEntry a[2 * MAXG]; };  // n >= 1 entries filled in one launch
+hipError_t launch_fill_group(const FillGroup& g, float v, hipStream_t st);
 // prim[p] (bp x bp) = diagonal sub-block p % g of super-block p / g (g bp x g bp, row pitch sb = g bp) of sup, zero
 // past a ragged last block (dimension d)
 hipError_t launch_extract_diag(const float* sup, int sb, int g, int bp, int d, int nprim, float* prim, hipStream_t st);
@@ -209,6 +219,14 @@ hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
                                void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st);
+// Three bf16 parts of X (rows x cols, float32) for products to float32 accuracy on bf16 MFMA:
+// X(i, j) = src[r(i) * ld_src + c(j)] - [sub_eye && i == j], r(i) = ridx ? ridx[i] : i, c(j) = cidx ? cidx[j] : j
+// (indices clamped to rlim / clim). Part t = 0, 1, 2 is hi(X) = bf16(X), or lo(X) = bf16(X - hi(X)) where bit t of
+// lo_mask is set, written at dst + t tstride with element (i, j) at i ld_dst + j over prows x pcols (zero outside
+// rows x cols). D (nullable, row pitch ld_d) receives X in float32.
+hipError_t launch_split3(const float* src, int64_t ld_src, const int32_t* ridx, const int32_t* cidx, int rlim, int clim,
+                         int sub_eye, int rows, int cols, int prows, int pcols, __bf16* dst, int64_t ld_dst,
+                         int64_t tstride, int lo_mask, float* D, int64_t ld_d, hipStream_t st);
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1} with prim holding P_{k+1} on entry (k >= 1), Q from theta;
 // powers[t-1] = P_t as bp x ldp blocks
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,

@@ -205,6 +205,14 @@ __global__ void k_fill(float* __restrict__ p, size_t n, float v) {
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) p[e] = v;
 }
 
+// grid (x, entries): blocks of column y fill entry y
+__global__ void k_fill_group(const FillGroup G, float v) {
+  const FillEntry& ge = G.a[blockIdx.y];
+  float* p = keep_s(ge.p);
+  const size_t n = keep_s(ge.n);
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) p[e] = v;
+}
+
 __global__ void k_convert(const float* __restrict__ src, int64_t ld_src, void* __restrict__ dst, int64_t ld_dst,
                           int dst_dt, int rows, int cols) {
   for (int r = blockIdx.y; r < rows; r += gridDim.y)
@@ -224,6 +232,26 @@ __global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int
       const float v = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
       if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + j] = (__bf16)v;
       else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + j] = v;
+    }
+}
+
+__global__ void k_split3(const float* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ ridx,
+                         const int32_t* __restrict__ cidx, int rlim, int clim, int sub_eye, int rows, int cols, int prows,
+                         int pcols, __bf16* __restrict__ dst, int64_t ld_dst, int64_t tstride, int lo_mask,
+                         float* __restrict__ D, int64_t ld_d) {
+  for (int i = blockIdx.y; i < prows; i += gridDim.y)
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < pcols; j += gridDim.x * blockDim.x) {
+      float x = 0.f;
+      const bool in = i < rows && j < cols;
+      if (in) {
+        const int r = ridx ? clampi(ridx[i], rlim) : i, c = cidx ? clampi(cidx[j], clim) : j;
+        x = src[(int64_t)r * ld_src + c] - (sub_eye && i == j ? 1.f : 0.f);
+        if (D) D[(int64_t)i * ld_d + j] = x;
+      }
+      const __bf16 hi = (__bf16)x, lo = (__bf16)(x - (float)hi);
+      __bf16* o = dst + (int64_t)i * ld_dst + j;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) o[t * tstride] = (lo_mask >> t) & 1 ? lo : hi;
     }
 }
 
@@ -615,6 +643,15 @@ hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_fill_group(const FillGroup& g, float v, hipStream_t st) {
+  size_t mx = 0, tot = 0;
+  for (int i = 0; i < g.n; ++i) { mx = std::max(mx, g.a[i].n); tot += g.a[i].n; }
+  if (mx == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)tot * 4);
+  hipLaunchKernelGGL(k_fill_group, dim3(std::min<unsigned>(grid_for(mx), 256), g.n), dim3(kThreads), 0, st, g, v);
+  return hipGetLastError();
+}
+
 static dim3 row_grid(int cols, int rows) { return dim3((cols + kThreads - 1) / kThreads, rows < 65535 ? rows : 65535); }
 
 hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows, int cols,
@@ -637,6 +674,16 @@ hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, con
 hipError_t launch_gather_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim, float* dst,
                               int64_t ld_dst, hipStream_t st) {
   return launch_gather_cols_to(src, ld_src, rows, idx, s, dlim, dst, F32, ld_dst, st);
+}
+
+hipError_t launch_split3(const float* src, int64_t ld_src, const int32_t* ridx, const int32_t* cidx, int rlim, int clim,
+                         int sub_eye, int rows, int cols, int prows, int pcols, __bf16* dst, int64_t ld_dst,
+                         int64_t tstride, int lo_mask, float* D, int64_t ld_d, hipStream_t st) {
+  if (prows <= 0 || pcols <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)rows * cols * (D ? 8 : 4) + 6.0 * prows * pcols);
+  hipLaunchKernelGGL(k_split3, row_grid(pcols, prows), dim3(kThreads), 0, st, src, ld_src, ridx, cidx, rlim, clim,
+                     sub_eye, rows, cols, prows, pcols, dst, ld_dst, tstride, lo_mask, D, ld_d);
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,

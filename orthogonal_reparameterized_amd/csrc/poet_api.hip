@@ -563,9 +563,30 @@ hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, con
   return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF : Fb, trans, out, ldo), st);
 }
 
+// Buffers of the float32-accurate FS merge of one side (reused by the other): the gathered columns (P) or rows (R)
+// of W0 in float32 (Dg) and as three bf16 parts (Xcat), the factor delta's three parts (Fcat), the product (C) and
+// its split-K scratch.
+struct Fs3Bufs {
+  float* Dg = nullptr;
+  __bf16 *Xcat = nullptr, *Fcat = nullptr;
+  float *C = nullptr, *part = nullptr;
+  size_t part_elems = 0;
+};
+
+// float32 scratch the fast kernel's split-K and addend epilogue take for one M x N x K product
+size_t fs3_part_elems(int M, int N, int K) {
+  GemmDesc g;
+  g.M = M; g.N = N; g.K = K;
+  g.part = reinterpret_cast<float*>(256);  // split count with unlimited scratch (nothing is dereferenced)
+  g.part_elems = ~(size_t)0;
+  return (size_t)fast_gemm_splits(g) * M * N;
+}
+
 struct MergePlan {
   bool inplace = false;   // both sides block-diagonal with blocks <= 256: two in-place passes over W0
   char* split = nullptr;  // their pre-split factor deltas
+  bool fs3 = false;       // both sides FS: gather, float32-accurate bf16 product, scatter, in place per side
+  Fs3Bufs f3;
   float *T = nullptr, *Wn = nullptr;
   int32_t* flags = nullptr;
   FsBufs fs;
@@ -576,7 +597,19 @@ size_t plan_merge(const poet_layer& L, const SideInfo& R, const SideInfo& P, voi
                 bs_merge_eligible(P.bp, L.m, L.ldw);
   if (p->inplace) {
     p->split = reinterpret_cast<char*>(
-        a.take_bytes(std::max(bs_merge_split_bytes(R.bp, R.nprim), bs_merge_split_bytes(P.bp, P.nprim))));
+        a.take_bytes(bs_merge_split_bytes(R.bp, R.nprim) + bs_merge_split_bytes(P.bp, P.nprim)));
+    return a.used();
+  }
+  p->fs3 = R.mode == POET_FS && P.mode == POET_FS;
+  if (p->fs3) {
+    const size_t m = L.m, n = L.n, sP = P.bp, sR = R.bp, spP = pad8(P.bp), spR = pad8(R.bp);
+    p->f3.Dg = a.take<float>(std::max(m * sP, sR * n));
+    p->f3.C = a.take<float>(std::max(m * sP, sR * n));
+    p->f3.Xcat = a.take<__bf16>(std::max(m * 3 * spP, 3 * spR * pad8(L.n)));
+    p->f3.Fcat = a.take<__bf16>(std::max(3 * spP * spP, sR * 3 * spR));
+    p->f3.part_elems = std::max(fs3_part_elems(L.m, P.bp, 3 * (int)spP), fs3_part_elems(R.bp, L.n, 3 * (int)spR));
+    p->f3.part = a.take<float>(p->f3.part_elems);
+    p->flags = a.take<int32_t>((size_t)std::max(L.m, L.n));
     return a.used();
   }
   const size_t mn = (size_t)L.m * L.ldw;
@@ -1235,6 +1268,109 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
 }
 }  // namespace
 
+// hipError_t helpers: return the first failing call's error
+#define HIP_RET(expr)                 \
+  do {                                \
+    const hipError_t r_ = (expr);     \
+    if (r_ != hipSuccess) return r_;  \
+  } while (0)
+
+// the in-place block-diagonal merge of one weight, as an item of launch_bs_merge_group
+MergeItem merge_item(const poet_layer& L, const SideInfo& R, const SideInfo& P, float* W0, void* shadow,
+                     const float* primR, const float* primP) {
+  MergeItem it;
+  it.W = W0; it.ld = L.ldw; it.m = L.m; it.n = L.n;
+  it.bpR = R.bp; it.nR = R.nprim; it.primR = primR;
+  it.bpP = P.bp; it.nP = P.nprim; it.primP = primP;
+  it.shadow = shadow; it.sh_dt = L.act_dtype; it.ld_sh = L.ldw;
+  return it;
+}
+
+// In-place FS merge of one side to float32 accuracy on bf16 MFMA. With X the gathered float32 block of W0 (P: the
+// columns I, m x s; R: the rows I, s x n) and dF = F - I the factor's delta, the block becomes X + X dF (P) or
+// X + dF X (R): the identity part is the float32 addend, and the delta product is hi*hi + hi*lo + lo*hi of the
+// two operands' bf16 parts, one product with K = 3 s' (s' = s rounded up to 8, zero padded), the parts stacked
+// along K as [hi | hi | lo] on the left operand and [hi ; lo ; hi] on the right. The result is scattered back.
+hipError_t fs3_merge_side(const poet_layer& L, const SideInfo& S, bool rside, float* W0, const float* prim,
+                          const int32_t* idx, const Fs3Bufs& f, hipStream_t st) {
+  const int m = L.m, n = L.n, s = S.bp, sp = pad8(S.bp);
+  GemmDesc g;
+  g.compute = BF16;
+  g.kclass = POET_K_MERGE;
+  g.part = f.part; g.part_elems = f.part_elems;
+  g.a_dt = g.b_dt = BF16;
+  g.K = 3 * sp;
+  g.beta = 1.f;
+  g.c_dt = F32;
+  if (!rside) {  // columns I: Xcat m x 3s' (K-major left operand), Fcat 3s' x s' (rows of the right operand)
+    HIP_RET(launch_split3(W0, L.ldw, nullptr, idx, m, n, 0, m, s, m, sp, f.Xcat, 3 * sp, sp, 0b100, f.Dg, s, st));
+    HIP_RET(launch_split3(prim, s, nullptr, nullptr, s, s, 1, s, s, sp, sp, f.Fcat, sp, (int64_t)sp * sp, 0b010,
+                          nullptr, 0, st));
+    g.M = m; g.N = s;
+    g.A = f.Xcat; g.lda = 3 * sp; g.a_kmajor = 1;
+    g.B = f.Fcat; g.ldb = sp; g.b_kmajor = 0;
+    g.D = f.Dg; g.ldd = s;
+    g.C = f.C; g.ldc = s;
+    HIP_RET(launch_gemm(g, st));
+    return launch_scatter_cols(f.C, s, m, idx, s, n, W0, L.ldw, st);
+  }
+  // rows I: Fcat s x 3s' (K-major left operand), Xcat 3s' x n' (rows of the right operand, n' = n rounded up to 8)
+  const int np = pad8(n);
+  HIP_RET(launch_split3(W0, L.ldw, idx, nullptr, m, n, 0, s, n, sp, np, f.Xcat, np, (int64_t)sp * np, 0b010, f.Dg, n,
+                        st));
+  HIP_RET(launch_split3(prim, s, nullptr, nullptr, s, s, 1, s, s, s, sp, f.Fcat, 3 * sp, sp, 0b100, nullptr, 0, st));
+  g.M = s; g.N = n;
+  g.A = f.Fcat; g.lda = 3 * sp; g.a_kmajor = 1;
+  g.B = f.Xcat; g.ldb = np; g.b_kmajor = 0;
+  g.D = f.Dg; g.ldd = n;
+  g.C = f.C; g.ldc = n;
+  HIP_RET(launch_gemm(g, st));
+  return launch_scatter_rows(f.C, n, idx, s, m, n, W0, F32, L.ldw, st);
+}
+
+// W0 <- R W0 P of a weight outside the in-place path (FS sides, blocks above 256), through its MergePlan buffers
+hipError_t merge_general(const poet_layer& L, const SideInfo& R, const SideInfo& P, float* W0, void* W0_shadow,
+                         const float* primR, const float* primP, const int32_t* idxR, const int32_t* idxP,
+                         const MergePlan& p, hipStream_t st) {
+  if (p.fs3) {  // W0 <- W0 P on the columns I_P, then W0 <- R W0 on the rows I_R, in place; then the shadow
+    HIP_RET(fs3_merge_side(L, P, false, W0, primP, idxP, p.f3, st));
+    HIP_RET(fs3_merge_side(L, R, true, W0, primR, idxR, p.f3, st));
+    if (W0_shadow) HIP_RET(launch_convert(W0, L.ldw, W0_shadow, L.ldw, L.act_dtype, L.m, L.n, st));
+    return hipSuccess;
+  }
+  HIP_RET(apply_P(L, P, W0, primP, idxP, p.T, F32, p.fs, st));
+  HIP_RET(apply_R(L, R, p.T, primR, idxR, p.Wn, F32, L.ldw, F32, p.fs, st));
+  HIP_RET(launch_convert(p.Wn, L.ldw, W0, L.ldw, F32, L.m, L.n, st));
+  if (W0_shadow) HIP_RET(launch_convert(p.Wn, L.ldw, W0_shadow, L.ldw, L.act_dtype, L.m, L.n, st));
+  return hipSuccess;
+}
+
+// fresh index sets of a weight's FS sides for epoch epoch_next
+hipError_t merge_resample(const SideInfo& R, const SideInfo& P, int32_t* idxR, int32_t* idxP, int32_t* flags,
+                          uint64_t seed, uint32_t linear_id, uint32_t epoch_next, hipStream_t st) {
+  if (R.mode == POET_FS)
+    HIP_RET(launch_sample(R.d, R.bp, sampler_hash(seed, linear_id, POET_SIDE_R, epoch_next), flags, idxR, st));
+  if (P.mode == POET_FS)
+    HIP_RET(launch_sample(P.d, P.bp, sampler_hash(seed, linear_id, POET_SIDE_P, epoch_next), flags, idxP, st));
+  return hipSuccess;
+}
+
+// Workspace of a grouped merge: the pre-split deltas of every in-place weight at once, or the largest single-weight
+// plan of the others (which run one after another, after the in-place ones), whichever is larger.
+size_t merge_group_bytes(int32_t count, const poet_layer* layers) {
+  std::vector<MergeItem> items;
+  size_t solo = 0;
+  for (int i = 0; i < count; ++i) {
+    SideInfo R, P;
+    if (!layer_info(&layers[i], &R, &P)) return 0;
+    MergePlan p;
+    const size_t one = plan_merge(layers[i], R, P, nullptr, &p);
+    if (p.inplace) items.push_back(merge_item(layers[i], R, P, nullptr, nullptr, nullptr, nullptr));
+    else solo = std::max(solo, one);
+  }
+  return std::max(solo, items.empty() ? (size_t)0 : bs_merge_group_bytes(items.data(), (int)items.size()) + 256);
+}
+
 extern "C" {
 
 poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
@@ -1408,21 +1544,85 @@ poet_status poet_merge(const poet_layer* L, float* W0, void* W0_shadow, float* t
   plan_merge(*L, R, P, ws, &p);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (p.inplace) {  // W0 <- W0 P, then W0 <- R W0 (writing the shadow), in place
-    HIP_TRY(launch_bs_merge_pass(W0, L->ldw, L->m, L->n, 0, P.bp, P.nprim, primP, p.split, nullptr, F32, 0, st));
-    HIP_TRY(launch_bs_merge_pass(W0, L->ldw, L->m, L->n, 1, R.bp, R.nprim, primR, p.split, W0_shadow, L->act_dtype,
-                                 L->ldw, st));
+    const MergeItem it = merge_item(*L, R, P, W0, W0_shadow, primR, primP);
+    HIP_TRY(launch_bs_merge_group(&it, 1, p.split, st));
   } else {
-    HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, F32, p.fs, st));
-    HIP_TRY(apply_R(*L, R, p.T, primR, idxR, p.Wn, F32, L->ldw, F32, p.fs, st));
-    HIP_TRY(launch_convert(p.Wn, L->ldw, W0, L->ldw, F32, L->m, L->n, st));
-    if (W0_shadow) HIP_TRY(launch_convert(p.Wn, L->ldw, W0_shadow, L->ldw, L->act_dtype, L->m, L->n, st));
+    HIP_TRY(merge_general(*L, R, P, W0, W0_shadow, primR, primP, idxR, idxP, p, st));
   }
   if (R.theta_len > 0) HIP_TRY(launch_fill(thetaR, R.theta_len, 0.f, st));
   if (P.theta_len > 0) HIP_TRY(launch_fill(thetaP, P.theta_len, 0.f, st));
-  if (R.mode == POET_FS)
-    HIP_TRY(launch_sample(R.d, R.bp, sampler_hash(seed, linear_id, POET_SIDE_R, epoch_next), p.flags, idxR, st));
-  if (P.mode == POET_FS)
-    HIP_TRY(launch_sample(P.d, P.bp, sampler_hash(seed, linear_id, POET_SIDE_P, epoch_next), p.flags, idxP, st));
+  HIP_TRY(merge_resample(R, P, idxR, idxP, p.flags, seed, linear_id, epoch_next, st));
+  return POET_OK;
+}
+
+size_t poet_merge_group_workspace_bytes(int32_t count, const poet_layer* layers) {
+  if (count <= 0 || !layers) return 0;
+  return merge_group_bytes(count, layers);
+}
+
+poet_status poet_merge_group(int32_t count, const poet_layer* layers, float* const* W0, void* const* W0_shadow,
+                             float* const* thetaR, float* const* thetaP, const float* const* primR,
+                             const float* const* primP, int32_t* const* idxR, int32_t* const* idxP, uint64_t seed,
+                             const uint32_t* linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (count < 0) return fail(POET_E_ARG, "count = %d must be >= 0", count);
+  if (count == 0) return POET_OK;
+  if (!layers || !W0 || !thetaR || !thetaP || !primR || !primP || !linear_id)
+    return fail(POET_E_ARG, "null layers, W0, theta, primitive or linear_id table");
+  std::vector<SideInfo> R(count), P(count);
+  std::vector<std::pair<uintptr_t, uintptr_t>> spans;  // byte ranges of every W0 and shadow
+  for (int i = 0; i < count; ++i) {
+    const poet_layer& L = layers[i];
+    if (!layer_info(&L, &R[i], &P[i])) return g_last;
+    if (!W0[i] || !primR[i] || !primP[i]) return fail(POET_E_ARG, "null W0[%d] or primitive", i);
+    if ((R[i].theta_len > 0 && !thetaR[i]) || (P[i].theta_len > 0 && !thetaP[i]))
+      return fail(POET_E_ARG, "null thetaR[%d] or thetaP[%d]", i, i);
+    if (!check_idx(R[i], idxR ? idxR[i] : nullptr, "R") || !check_idx(P[i], idxP ? idxP[i] : nullptr, "P"))
+      return g_last;
+    const uintptr_t w = reinterpret_cast<uintptr_t>(W0[i]);
+    spans.push_back({w, w + ((size_t)(L.m - 1) * L.ldw + L.n) * 4});
+    if (W0_shadow && W0_shadow[i]) {
+      const uintptr_t h = reinterpret_cast<uintptr_t>(W0_shadow[i]);
+      spans.push_back({h, h + ((size_t)(L.m - 1) * L.ldw + L.n) * dtype_size(L.act_dtype)});
+    }
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t u = 1; u < spans.size(); ++u)
+    if (spans[u].first < spans[u - 1].second) return fail(POET_E_ARG, "the weights or shadows of the group overlap");
+  if (!check_ws(ws, ws_bytes, merge_group_bytes(count, layers))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::vector<MergeItem> items;
+  std::vector<int> general;
+  for (int i = 0; i < count; ++i) {
+    MergePlan p;
+    plan_merge(layers[i], R[i], P[i], nullptr, &p);
+    if (p.inplace)
+      items.push_back(merge_item(layers[i], R[i], P[i], W0[i], W0_shadow ? W0_shadow[i] : nullptr, primR[i], primP[i]));
+    else
+      general.push_back(i);
+  }
+  if (!items.empty()) {
+    Arena a(ws);
+    char* split = reinterpret_cast<char*>(a.take_bytes(bs_merge_group_bytes(items.data(), (int)items.size())));
+    HIP_TRY(launch_bs_merge_group(items.data(), (int)items.size(), split, st));
+  }
+  for (int i : general) {  // one at a time, each through the whole workspace
+    MergePlan p;
+    plan_merge(layers[i], R[i], P[i], ws, &p);
+    HIP_TRY(merge_general(layers[i], R[i], P[i], W0[i], W0_shadow ? W0_shadow[i] : nullptr, primR[i], primP[i],
+                          idxR ? idxR[i] : nullptr, idxP ? idxP[i] : nullptr, p, st));
+    HIP_TRY(merge_resample(R[i], P[i], idxR ? idxR[i] : nullptr, idxP ? idxP[i] : nullptr, p.flags, seed,
+                           linear_id[i], epoch_next, st));
+  }
+  FillGroup fg;
+  for (int i = 0; i < count; ++i) {
+    if (R[i].theta_len > 0) fg.a[fg.n++] = FillEntry{thetaR[i], R[i].theta_len};
+    if (P[i].theta_len > 0) fg.a[fg.n++] = FillEntry{thetaP[i], P[i].theta_len};
+    if (fg.n + 2 > 2 * MAXG || i + 1 == count) {
+      if (fg.n > 0) HIP_TRY(launch_fill_group(fg, 0.f, st));
+      fg = FillGroup();
+    }
+  }
   return POET_OK;
 }
 

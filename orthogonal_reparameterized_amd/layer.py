@@ -177,8 +177,9 @@ class PoetGroup:
 
     ``build`` runs the Cayley-Neumann build of both sides of every linear (poet_build_orthogonal_group);
     ``finish_backward`` runs the Neumann adjoint and skew projection of every side from the primitive gradients
-    that ``PoetLinear.backward_act_prims`` / ``backward_prims`` left (poet_adjoint_group). Results match the
-    per-linear calls up to the float32 summation order of split products."""
+    that ``PoetLinear.backward_act_prims`` / ``backward_prims`` left (poet_adjoint_group); ``merge`` runs
+    merge-then-reinitialize of every linear (poet_merge_group). Results match the per-linear calls up to the
+    float32 summation order of split products."""
 
     def __init__(self, linears):
         torch = _torch()
@@ -193,7 +194,8 @@ class PoetGroup:
             if pl.act_path:
                 self._ops[id(pl)] = tuple(torch.empty(2 * B.poet_prim_len(s), dtype=torch.bfloat16, device=dev)
                                           for s in (pl.L.R, pl.L.P))
-        need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides))
+        need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides),
+                   B.poet_merge_group_workspace_bytes([pl.L for pl in self.linears]))
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def build(self, stream=None):
@@ -213,3 +215,16 @@ class PoetGroup:
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
         dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]
         B.poet_adjoint_group(self.sides, dprims, powers, dthetas, self.ws, stream)
+
+    def merge(self, stream=None):
+        """Merge-then-reinitialize of every linear (their sampler seeds and epochs must agree); refreshes each
+        linear's bf16 copy of W0 where it keeps one."""
+        pls = self.linears
+        if len({pl.seed for pl in pls}) != 1 or len({pl.epoch for pl in pls}) != 1:
+            raise ValueError("PoetGroup.merge needs one sampler seed and one epoch across its linears")
+        for pl in pls:
+            pl.epoch += 1
+        B.poet_merge_group([pl.L for pl in pls], [pl.W0 for pl in pls], [pl.W0b for pl in pls],
+                           [pl.thetaR for pl in pls], [pl.thetaP for pl in pls], [pl.primR for pl in pls],
+                           [pl.primP for pl in pls], [pl.idxR for pl in pls], [pl.idxP for pl in pls], pls[0].seed,
+                           [pl.linear_id for pl in pls], pls[0].epoch, self.ws, stream)

@@ -216,3 +216,37 @@ def test_group_calls_reject_bad_arguments():
                                         FAKE, FAKE, wbw, None) == B.POET_E_ARG
     assert lb.poet_linear_bwd_act_prims(ctypes.byref(L), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE,
                                         FAKE, FAKE, wbw - 1024, None) == B.POET_E_WORKSPACE
+
+
+def test_merge_group_rejects_bad_arguments():
+    lb = B.lib()
+    L = _layer()  # block-diagonal, blocks of 32: the in-place path
+    F = _layer(R=B.side(1, 256, 128, 3, 0), P=B.side(1, 128, 64, 3, 0))  # FS sides: the general path
+    arr = (B.poet_layer * 2)(L, L)
+    one = B.poet_merge_group_workspace_bytes([L])
+    two = B.poet_merge_group_workspace_bytes([L, L])
+    assert 0 < one < two  # the in-place weights of a group keep their split deltas side by side
+    assert B.poet_merge_group_workspace_bytes([L, F]) >= B.poet_workspace_bytes(F, B.POET_OP_MERGE)
+    assert lb.poet_merge_group_workspace_bytes(-1, arr) == 0
+    w0 = (ctypes.c_void_p * 2)(0x1000, 0x10000000)
+    same = (ctypes.c_void_p * 2)(0x1000, 0x1000 + 4096)  # the second weight starts inside the first
+    tab = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    ids = (ctypes.c_uint32 * 2)(0, 1)
+
+    def call(count=2, layers=arr, W0=w0, sh=None, tR=tab, tP=tab, pR=tab, pP=tab, iR=None, iP=None, lid=ids,
+             ws=FAKE, wsb=two):
+        return lb.poet_merge_group(count, layers, W0, sh, tR, tP, pR, pP, iR, iP, 0, lid, 1, ws, wsb, None)
+    assert call(count=-1) == B.POET_E_ARG
+    assert call(count=0, layers=None, W0=None, tR=None, tP=None, pR=None, pP=None, lid=None) == B.POET_OK
+    assert call(W0=None) == B.POET_E_ARG
+    assert call(lid=None) == B.POET_E_ARG
+    assert call(pR=(ctypes.c_void_p * 2)(FAKE, None)) == B.POET_E_ARG
+    assert call(W0=same) == B.POET_E_ARG  # overlapping weights would race in the shared passes
+    shadows = (ctypes.c_void_p * 2)(0x1000 + 64, None)  # a shadow inside a weight
+    assert call(sh=shadows) == B.POET_E_ARG
+    assert call(wsb=two - 1) == B.POET_E_WORKSPACE
+    assert call(ws=None) == B.POET_E_ARG
+    fs = (B.poet_layer * 2)(L, F)
+    assert call(layers=fs, wsb=1 << 40) == B.POET_E_ARG  # FS sides need their index sets
+    bad = (B.poet_layer * 2)(L, _layer(m=0))
+    assert call(layers=bad) == B.POET_E_SHAPE
