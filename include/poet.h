@@ -180,9 +180,11 @@ int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below app
 poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream);
 
 /* opsR/opsP (nullable, bf16 in): operand copies of the primitives, 2 * poet_prim_len(side) elements: block p
- * of F at offset p*bp*bp (row-major, F(i, j) at i*bp + j) and its transpose at num_prims*bp*bp + p*bp*bp, both
- * zero outside the block's c x c corner; poet_build_orthogonal_group writes them. NULL: the call makes them
- * in its workspace from primR/primP. */
+ * of F at offset p*bp*bp and its transpose at num_prims*bp*bp + p*bp*bp, both zero outside the block's c x c
+ * corner; poet_build_orthogonal_group writes them. Each bp x bp block M (M = F or F^T) is stored row-major
+ * (M(i, j) at i*bp + j) unless bp is a multiple of 32; then it is stored in the order the MFMA fragments of the
+ * application kernel are loaded: M(i, j) at ((i/32 * bp/16 + j/16) * 64 + (j/8 % 2) * 32 + i % 32) * 8 + j % 8.
+ * NULL: the call makes them in its workspace from primR/primP. */
 
 /* X [T x ldx] in, Y [T x ldy] out, Z [T x ldy] out: X P^T W0^T, kept for the backward (all bf16). */
 poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,

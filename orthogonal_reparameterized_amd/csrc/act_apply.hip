@@ -11,8 +11,9 @@
 // (global_load_lds), three tiles' copies in flight while the current one is multiplied
 // (v_mfma_f32_32x32x16_bf16, 32 tokens x 64 columns per wave per tile); the finished tile goes back through the
 // stage it was read from and leaves as coalesced 16-byte row chunks. Rows past the last token are read from the
-// last token (finite values, never stored); columns of a block narrower than the k-steps cover are zeroed in LDS
-// after the copy lands (row padding may hold any bits, NaN included).
+// last token (finite values, never stored); the columns of a partial last chunk past the block (row padding,
+// any bits, NaN included) are cleared in LDS by the lanes that copied them. The operand comes in fragment order
+// where the block is a multiple of 32 (one wave's load of a fragment reads 1 KB contiguous), else in row order.
 #include <algorithm>
 
 #include "poet.h"
@@ -46,19 +47,30 @@ struct ActArgs {
 };
 
 // Operand rows for the kernel below: Bt[b][j][k] = bf16(B(k, j)) with B(k, j) = F_b[j][k] (trans) or F_b[k][j],
-// for j, k < c (the block's size) and zero elsewhere in the bp x bp block. Consecutive threads take consecutive
-// k (trans: coalesced reads) or consecutive j (no trans: the strided side is the read of F, coalesced in j).
+// for j, k < c (the block's size) and zero elsewhere in the bp x bp block, in fragment order where
+// act_frag_layout(bp), else in row order. Row order: consecutive threads take consecutive k (trans: coalesced
+// reads) or consecutive j (no trans: the strided side is the read of F, coalesced in j). Fragment order:
+// consecutive threads write consecutive elements.
 __global__ void k_act_operand(const float* __restrict__ F, int bp, int d, int nblk, int trans, __bf16* __restrict__ Bt) {
   const int64_t per = (int64_t)bp * bp, total = per * nblk;
+  const bool frag = act_frag_layout(bp);
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int b = (int)(e / per);
     const int rem = (int)(e % per);
     const int c = min(bp, d - b * bp);
     int j, k;
-    if (trans) { j = rem / bp; k = rem % bp; } else { k = rem / bp; j = rem % bp; }
+    if (frag) {  // rem = ((g (bp / 16) + s) 64 + l) 8 + v
+      const int v = rem & 7, l = (rem >> 3) & 63, gs = rem >> 9, s = gs % (bp >> 4), g = gs / (bp >> 4);
+      j = 32 * g + (l & 31);
+      k = 16 * s + 8 * (l >> 5) + v;
+    } else if (trans) {
+      j = rem / bp; k = rem % bp;
+    } else {
+      k = rem / bp; j = rem % bp;
+    }
     const bool in = j < c && k < c;
     const float f = F[(int64_t)b * per + (in ? (trans ? (int64_t)j * bp + k : (int64_t)k * bp + j) : 0)];
-    Bt[(int64_t)b * per + (int64_t)j * bp + k] = (__bf16)(in ? f : 0.f);
+    Bt[(int64_t)b * per + (frag ? rem : (int64_t)j * bp + k)] = (__bf16)(in ? f : 0.f);
   }
 }
 
@@ -67,8 +79,9 @@ __global__ void k_act_operand(const float* __restrict__ F, int bp, int d, int nb
 // current tile's MFMAs). The memory clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// NK: k-steps of 16 covering the block size (4, 8 or 16); every loop over them is unrolled without conditions
-template <int NK>
+// NK: k-steps of 16 covering the block size (4, 8 or 16); every loop over them is unrolled without conditions.
+// FRAG: the operand is in fragment order.
+template <int NK, bool FRAG>
 __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
   __shared__ __attribute__((aligned(16))) char ring[NST * TILE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -107,16 +120,24 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
                                        16, 0, 0);
     }
   };
-  // columns of a staged tile to clear: the tail [c, 8 ceil(c / 8)) of a partial last chunk; for a block narrower
-  // than one chunk, everything from c on (its only chunk is partial, and every copy reads it)
-  const int z0 = c, z1 = c < 8 ? 16 * NK : (c + 7) & ~7;
-  const bool ragged = z1 > z0;
-  auto zero_tail = [&](int st) {
-    char* base = ring + st * TILE_BYTES;
-    const int w = z1 - z0;  // columns to clear per row
-    for (int e = tid; e < TM * w; e += AT) {
-      const int row = e / w, k = z0 + e % w;
-      sts(base, row, k, (__bf16)0.f);
+  // A partial last chunk holds row padding past column c (any bits, NaN included). Every lane that copied it
+  // (for a block narrower than one chunk, also into the positions of the chunks past it) clears its elements from
+  // c % 8 on in its own 16 bytes of the stage, once its copies have landed and before the barrier that publishes
+  // the tile: no extra barrier.
+  // Elements [nv, 8) of the chunk (nv = c % 8 valid) are cleared by at most three aligned writes: one 2-byte write
+  // when nv is odd, one 4-byte write when the next even element is 2 or 6, one 8-byte write of elements 4..7 when
+  // the remainder starts there (the choices are uniform, only the copying lanes write).
+  const bool ragged = (c & 7) != 0;
+  const int nv = c & 7, e1 = nv + (nv & 1), e2 = e1 + (e1 & 2);
+  const bool mine0 = lch[0] == (c >> 3), mine1 = lch[1] == (c >> 3);
+  auto clear_pad = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < TM / 8; ++q) {
+      if (!(q & 1 ? mine1 : mine0)) continue;
+      char* dst = ring + st * TILE_BYTES + (q * 4 + wave) * 1024 + 16 * lane;
+      if (nv & 1) *reinterpret_cast<unsigned short*>(dst + 2 * nv) = 0;
+      if (e1 & 2) *reinterpret_cast<uint32_t*>(dst + 2 * e1) = 0u;
+      if (e2 == 4) *reinterpret_cast<uint64_t*>(dst + 8) = 0ull;
     }
   };
 
@@ -126,18 +147,24 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
     if (tile0 + i < tile1) dma(tile0 + i, i);
 
   // ---- resident operand: B(k, j) for this wave's columns j = 64 wave + 32 u + j32 and k = 16 ks + kh + v, from the
-  // bf16 rows Bt[j][k] = B(k, j) (one 16-byte load per fragment). Bt is zero outside the block's c x c corner and
-  // the fragments are zero for k >= bp, so B vanishes for every k >= c.
+  // bf16 rows Bt[j][k] = B(k, j) (one 16-byte load per fragment: in fragment order the wave's 64 loads of one
+  // fragment are 1 KB contiguous). Bt is zero outside the block's c x c corner and the fragments are zero for
+  // k >= bp, so B vanishes for every k >= c.
   const __bf16* Bt = a.Bt + (int64_t)blk * a.bp * a.bp;
   bf16x8 bfr[2][NK];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int j = min(wave * 64 + u * 32 + j32, a.bp - 1);  // columns past bp: never stored, any finite value
+    const int g = min(wave * 2 + u, a.bp / 32 - 1);          // (fragment order) their column group
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       // k past bp: zero (the staged activations there hold copies of a real chunk, not zeros)
       const int k = ks * 16 + kh;
-      const bf16x8 f = *reinterpret_cast<const bf16x8*>(Bt + (int64_t)j * a.bp + min(k, a.bp - 8));
+      bf16x8 f;
+      if constexpr (FRAG)
+        f = *reinterpret_cast<const bf16x8*>(Bt + ((int64_t)(g * (a.bp >> 4) + min(ks, (a.bp >> 4) - 1)) * 64 + lane) * 8);
+      else
+        f = *reinterpret_cast<const bf16x8*>(Bt + (int64_t)j * a.bp + min(k, a.bp - 8));
       bfr[u][ks] = k < a.bp ? f : bf16x8{};
     }
   }
@@ -149,12 +176,12 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)((uint32_t)a.T * (uint32_t)a.ldo * 2u), RSRC_WORD3);
   const bool whole = (c & 7) == 0;  // every 16-byte chunk of the block is whole: one 16-byte store per chunk
   // Each thread issues, per tile, its copy of tile + NST - 1 (TM/8 instructions) and then its stores of the tile
-  // (SQ per tile: one 16-byte store per row chunk, plus seven 2-byte stores for a partial last chunk). The copy of
-  // tile t was issued three iterations earlier (or before the loop, then complete at the first wait), followed by
-  // the stores of t-3, t-2, t-1 and the copies of t+1, t+2 where those exist: waiting until at most that many are
-  // outstanding retires exactly the copy of t. With a partial chunk that count exceeds what the counter can hold;
-  // the wait then leaves the last tile's stores and one copy outstanding (retiring the copy of t+1 early as well).
-  constexpr int SQ = TM / 8, SQP = 8 * (TM / 8), CP = TM / 8;
+  // (SQ per tile: one 16-byte store per row chunk, plus three (8-, 4- and 2-byte) stores for a partial last chunk).
+  // The copy of tile t was issued three iterations earlier (or before the loop, then complete at the first wait),
+  // followed by the stores of t-3, t-2, t-1 and the copies of t+1, t+2 where those exist: waiting until at most
+  // that many are outstanding retires exactly the copy of t.
+  constexpr int SQ = TM / 8, SQP = 4 * (TM / 8), CP = TM / 8;
+  static_assert(3 * SQP + 2 * CP <= 63, "the outstanding count must fit the counter");
   for (int tile = tile0; tile < tile1; ++tile) {
     const int st = (tile - tile0) % NST;
     const int later = (tile + 1 < tile1) + (tile + 2 < tile1);  // copies issued after this tile's
@@ -165,15 +192,13 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
       else if (later == 1) __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQ + CP));
       else __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQ));
     } else {
-      if (tile + 2 < tile1) __builtin_amdgcn_s_waitcnt(vm_wait(SQP + CP));
-      else __builtin_amdgcn_s_waitcnt(vm_wait(SQP));
+      if (later == 2) __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQP + 2 * CP));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQP + CP));
+      else __builtin_amdgcn_s_waitcnt(vm_wait(3 * SQP));
     }
+    if (ragged) clear_pad(st);
     lds_barrier();  // the tile's copy has landed everywhere; every wave is done with the previous tile's stage
     if (tile + NST - 1 < tile1) dma(tile + NST - 1, (st + NST - 1) % NST);
-    if (ragged) {
-      zero_tail(st);
-      lds_barrier();
-    }
     const char* A = ring + st * TILE_BYTES;
     // fragment address of k-step ks: row (r * 32 + j32), chunk (2 ks + lane / 32) ^ (j32 & 15); the swizzle key passes
     // through an empty asm statement so that the 16 per-step addresses are recomputed (one XOR each), not kept live
@@ -229,17 +254,20 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(O + row * ROWB + ((j32 ^ (row & 15)) << 4));
         const int col = 8 * j32;  // first column of the chunk (logical chunk j32)
         const uint32_t o = ((uint32_t)t * (uint32_t)a.ldo + (uint32_t)(b0 + col)) * 2u;
-        // whole chunks: one 16-byte store; a partial last chunk: its elements one by one (seven at most)
+        // whole chunks: one 16-byte store; a partial last chunk (nv = c % 8 elements): its first nv & 4 elements,
+        // then nv & 2, then nv & 1, in one 8-, 4- and 2-byte store (each aligned: the chunk starts 16-byte aligned)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), Ob, t < a.T && col + 8 <= c ? o : OOB, 0, 0);
         if (!whole) {
-          // element e is the low (e even) or high half of 32-bit word e / 2, extracted with integer shifts (a
-          // direct element extraction from the bf16 vector fed to the 16-bit store lost the high halves)
+          const int nv = c & 7;
           const bool part = t < a.T && col < c && col + 8 > c;
           const u32x4 w = __builtin_bit_cast(u32x4, v);
-#pragma unroll
-          for (int e = 0; e < 7; ++e)
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), Ob,
-                                                  part && col + e < c ? o + 2u * e : OOB, 0, 0);
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, Ob, part && (nv & 4) ? o : OOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(w[(nv & 4) >> 1], Ob, part && (nv & 2) ? o + 2u * (nv & 4) : OOB, 0, 0);
+          // element nv & 6 is even: the low half of its 32-bit word (taken with a shift and mask, not an element
+          // extraction from the bf16 vector, which fed a 16-bit store wrongly)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[(nv & 6) >> 1] & 0xFFFFu), Ob,
+                                                part && (nv & 1) ? o + 2u * (nv & 6) : OOB, 0, 0);
         }
       }
     }
@@ -278,9 +306,15 @@ hipError_t launch_act_apply(const __bf16* in, int64_t ldi, __bf16* out, int64_t 
   const int64_t nb = (int64_t)nblk * a.ngrp;
   ProfScope prof(POET_K_APPLY, st, 2.0 * T * (double)bp * d, 4.0 * T * (double)d);
   const unsigned grid = (unsigned)((nb + 7) / 8 * 8);
-  if (bp <= 64) hipLaunchKernelGGL((act_apply_kernel<4>), dim3(grid), dim3(AT), 0, st, a);
-  else if (bp <= 128) hipLaunchKernelGGL((act_apply_kernel<8>), dim3(grid), dim3(AT), 0, st, a);
-  else hipLaunchKernelGGL((act_apply_kernel<16>), dim3(grid), dim3(AT), 0, st, a);
+  if (act_frag_layout(bp)) {
+    if (bp <= 64) hipLaunchKernelGGL((act_apply_kernel<4, true>), dim3(grid), dim3(AT), 0, st, a);
+    else if (bp <= 128) hipLaunchKernelGGL((act_apply_kernel<8, true>), dim3(grid), dim3(AT), 0, st, a);
+    else hipLaunchKernelGGL((act_apply_kernel<16, true>), dim3(grid), dim3(AT), 0, st, a);
+  } else {
+    if (bp <= 64) hipLaunchKernelGGL((act_apply_kernel<4, false>), dim3(grid), dim3(AT), 0, st, a);
+    else if (bp <= 128) hipLaunchKernelGGL((act_apply_kernel<8, false>), dim3(grid), dim3(AT), 0, st, a);
+    else hipLaunchKernelGGL((act_apply_kernel<16, false>), dim3(grid), dim3(AT), 0, st, a);
+  }
   return hipGetLastError();
 }
 

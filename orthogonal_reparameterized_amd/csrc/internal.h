@@ -161,8 +161,18 @@ hipError_t launch_bs_merge_group(const MergeItem* it, int n, char* split, hipStr
 
 // Block-diagonal factor applied to bf16 activations (act_apply.hip): out[t, block] = in[t, block] B_block for T
 // tokens of dimension d, blocks bp <= 256 (a multiple of 8), with the operand B = F^T (trans) or F given as bf16
-// rows Bt[j][k] = B(k, j) by launch_act_operand from the nblk float32 bp x bp primitives F. Row pitches ldi, ldo
-// multiples of 8, in and out 16-byte aligned, the input under 4 GB.
+// rows Bt[j][k] = B(k, j) (fragment order where act_frag_layout(bp), else row order) by launch_act_operand from
+// the nblk float32 bp x bp primitives F. Row pitches ldi, ldo multiples of 8, in and out 16-byte aligned, the
+// input under 4 GB.
+// Layout of the bf16 operand rows Bt[j][k] = B(k, j) of one bp x bp block:
+//   row order       element (j, k) at j bp + k;
+//   fragment order  (bp a multiple of 32) the MFMA fragments in the order the kernel loads them: column group
+//                   g = j / 32, k-step s = k / 16, lane l = 32 ((k / 8) % 2) + j % 32, element v = k % 8 at
+//                   ((g (bp / 16) + s) 64 + l) 8 + v, so that one fragment load of a wave reads 1 KB contiguous.
+__host__ __device__ inline bool act_frag_layout(int bp) { return bp % 32 == 0; }
+__host__ __device__ inline int64_t act_frag_index(int bp, int j, int k) {
+  return ((int64_t)((j >> 5) * (bp >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (j & 31)) * 8 + (k & 7);
+}
 bool act_apply_eligible(int bp, const void* in, int64_t ldi, const void* out, int64_t ldo, int T);
 hipError_t launch_act_operand(const float* F, int bp, int d, int nblk, bool trans, __bf16* Bt, hipStream_t st);
 hipError_t launch_act_apply(const __bf16* in, int64_t ldi, __bf16* out, int64_t ldo, const __bf16* Bt, int T, int d,

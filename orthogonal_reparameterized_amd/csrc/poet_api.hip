@@ -559,6 +559,8 @@ hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, con
     return launch_act_apply(reinterpret_cast<const __bf16*>(in), ldi, reinterpret_cast<__bf16*>(out), ldo, Bt, T,
                             S.d, S.bp, S.nprim, st);
   }
+  // the batched GEMM takes the operand in row order: the caller's copies only where they are in row order
+  if (opsF && act_frag_layout(S.bp)) opsF = nullptr;
   if (!opsF && (e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
   return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF : Fb, trans, out, ldo), st);
 }

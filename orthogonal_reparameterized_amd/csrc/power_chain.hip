@@ -151,26 +151,55 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
       const int nv = min(SW, bp - n0);  // columns of this strip inside the block
       float* prim = c.prim + (int64_t)p * bp * bp;
       __bf16* opsF = ops ? c.ops + (int64_t)p * bp * bp : nullptr;
+      const bool frag = act_frag_layout(bp);  // operand copies in fragment order (else in row order)
       for (int e = tid; e < bp * (SW / 4); e += NT) {  // rows i, 4-column chunks
         const int i = e / (SW / 4), n4 = (e % (SW / 4)) * 4;
         if (n4 >= nv) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(Rs + i * RP + n4);
         *reinterpret_cast<f32x4*>(prim + (int64_t)i * bp + n0 + n4) = v;
-        if (ops) {
+        if (ops && !frag) {
           bf16x4 w;
 #pragma unroll
           for (int t = 0; t < 4; ++t) w[t] = (__bf16)(i < cb && n0 + n4 + t < cb ? v[t] : 0.f);
           *reinterpret_cast<bf16x4*>(opsF + (int64_t)i * bp + n0 + n4) = w;
         }
       }
-      if (ops) {  // the transpose: rows ops[nprim bp^2 + p bp^2 + n0 + n][0..bp) from the strip buffer
+      if (ops && frag) {  // F's rows (operand row j = i, k = column n) in fragment order: 8 columns per 16 bytes
+        const int nks = nv / 16;  // k-steps this strip covers (nv is a multiple of 32 here)
+        for (int e = tid; e < (bp / 32) * nks * 64; e += NT) {
+          const int l = e & 63, s = (e >> 6) % nks, g = (e >> 6) / nks;
+          const int i = 32 * g + (l & 31), n = 16 * s + 8 * (l >> 5);
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(Rs + i * RP + n);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(Rs + i * RP + n + 4);
+          bf16x8 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            w[t] = (__bf16)(i < cb && n0 + n + t < cb ? v0[t] : 0.f);
+            w[t + 4] = (__bf16)(i < cb && n0 + n + t + 4 < cb ? v1[t] : 0.f);
+          }
+          *reinterpret_cast<bf16x8*>(opsF + act_frag_index(bp, i, n0 + n)) = w;
+        }
+      }
+      if (ops) {  // the transpose: operand row j = n0 + n, k = i (F's column n0 + n), from the strip buffer
         __bf16* opsT = c.ops + (int64_t)c.nprim * bp * bp + (int64_t)p * bp * bp;
         const int nch = bp / 8;
         for (int e = tid; e < SW * nch; e += NT) {
-          const int n = e / nch, ch = e - n * nch;
-          if (n < nv)
-            *reinterpret_cast<u32x4*>(opsT + (int64_t)(n0 + n) * bp + ch * 8) =
-                *reinterpret_cast<const u32x4*>(Xs + n * ROWB + ((ch ^ (n & 15)) << 4));
+          // fragment order: consecutive threads take consecutive lanes of one fragment (16-byte chunks of one
+          // column group and k-step); row order: consecutive chunks of one row
+          int n, ch;
+          if (frag) {
+            const int l = e & 63, gs = e >> 6, s = gs % (bp / 16), gl = gs / (bp / 16);
+            n = 32 * gl + (l & 31);
+            ch = 2 * s + (l >> 5);
+          } else {
+            n = e / nch;
+            ch = e - n * nch;
+          }
+          if (n < nv) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(Xs + n * ROWB + ((ch ^ (n & 15)) << 4));
+            const int64_t o = frag ? act_frag_index(bp, n0 + n, ch * 8) : (int64_t)(n0 + n) * bp + ch * 8;
+            *reinterpret_cast<u32x4*>(opsT + o) = v;
+          }
         }
       }
       break;

@@ -90,6 +90,19 @@ def _build_all(sides, thetas_d, grouped, ops=None):
     return bufs
 
 
+def _operand_order(M):
+    """Blocks M[p] (b x b) flattened as the library stores its operand copies: row-major, or, for b a multiple of
+    32, M(i, j) at ((i // 32 * b // 16 + j // 16) * 64 + (j // 8 % 2) * 32 + i % 32) * 8 + j % 8."""
+    nb, b, _ = M.shape
+    if b % 32:
+        return M.reshape(nb, b * b)
+    i, j = np.meshgrid(np.arange(b), np.arange(b), indexing="ij")
+    pos = ((i // 32 * (b // 16) + j // 16) * 64 + (j // 8 % 2) * 32 + i % 32) * 8 + j % 8
+    out = np.empty((nb, b * b), dtype=M.dtype)
+    out[:, pos.ravel()] = M.reshape(nb, b * b)
+    return out
+
+
 def test_build_group_equals_one_side_builds():
     announce("group build vs one-side builds")
     sides = _sides()
@@ -117,9 +130,10 @@ def test_build_group_equals_one_side_builds():
         want = np.zeros_like(F)
         for p, c in enumerate(O.block_sizes(mode, d, b)):
             want[p, :c, :c] = PI.round_bf16(F[p, :c, :c])
-        got = to_np(ops[i]).reshape(2, -1, b, b)
-        np.testing.assert_array_equal(got[0], want, err_msg=f"ops of side {i} {SIDES[i]}")
-        np.testing.assert_array_equal(got[1], want.transpose(0, 2, 1), err_msg=f"transposed ops of side {i}")
+        got = to_np(ops[i]).reshape(2, -1, b * b)
+        np.testing.assert_array_equal(got[0], _operand_order(want), err_msg=f"ops of side {i} {SIDES[i]}")
+        np.testing.assert_array_equal(got[1], _operand_order(want.transpose(0, 2, 1)),
+                                      err_msg=f"transposed ops of side {i}")
 
 
 def _oracle_dtheta(side_spec, theta, dprim):
