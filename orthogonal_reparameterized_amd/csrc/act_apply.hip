@@ -9,8 +9,8 @@
 // columns of the block's operand (all of K, 16 k-steps x 2 column tiles of bf16x8 fragments: 128 registers),
 // loaded and rounded once. The 32 x 256 activation tiles stream through a four-stage LDS ring by DMA
 // (global_load_lds), three tiles' copies in flight while the current one is multiplied
-// (v_mfma_f32_32x32x16_bf16, 32 tokens x 64 columns per wave per tile); the finished tile goes back through the
-// stage it was read from and leaves as coalesced 16-byte row chunks. Rows past the last token are read from the
+// (v_mfma_f32_32x32x16_bf16, 32 tokens x 64 columns per wave per tile); the finished tile goes through an LDS
+// buffer of its own and leaves as coalesced 16-byte row chunks. Rows past the last token are read from the
 // last token (finite values, never stored); the columns of a partial last chunk past the block (row padding,
 // any bits, NaN included) are cleared in LDS by the lanes that copied them. The operand comes in fragment order
 // where the block is a multiple of 32 (one wave's load of a fragment reads 1 KB contiguous), else in row order.
@@ -84,6 +84,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int NK, bool FRAG>
 __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
   __shared__ __attribute__((aligned(16))) char ring[NST * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char obuf[TILE_BYTES];  // the finished tile, on its way out
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.nblk * a.ngrp;
   // XCD-aware order: hardware workgroup b runs on XCD b % 8 and takes logical id (b % 8) per + b / 8
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
       const uint32_t o = (uint32_t)(r * 32 + j32) * ROWB + ((((uint32_t)(2 * ks) | hb) ^ xkey) << 4);
       return *reinterpret_cast<const bf16x8*>(A + o);
     };
-    bf16x4 outv[2][4];  // [u][i / 4]: four consecutive tokens of one column, rounded to bf16
+    bf16x4 outv[2][4];  // [u][q]: four consecutive columns of one token, rounded to bf16
     {
       f32x16 acc[2];
 #pragma unroll
@@ -217,7 +218,9 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
       // k-steps pipelined by hand: the fragment of step ks + 1 is read while step ks multiplies, and a scheduling
-      // barrier per step keeps the compiler from hoisting every read (and its registers) to the top
+      // barrier per step keeps the compiler from hoisting every read (and its registers) to the top. The product is
+      // taken transposed, out^T = B^T in^T (the operand fragments as the left factor, the token fragments as the
+      // right), so that a lane's accumulators hold four consecutive columns of one token.
       bf16x8 af[2];
       af[0] = frag_at(0, 0);
 #pragma unroll
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
         if (ks + 1 < NK) af[(ks + 1) & 1] = frag_at(0, ks + 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1], bfr[u][ks], acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[u][ks], af[ks & 1], acc[u], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -235,17 +238,15 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) outv[u][q][e] = (__bf16)acc[u][q * 4 + e];
     }
-    // the output tile leaves through LDS: every wave is done reading stage st, which then holds the tile as rows of
-    // 512 B (the same swizzled layout), read back as 16-byte row chunks and stored coalesced
-    lds_barrier();
-    char* O = ring + st * TILE_BYTES;
+    // the output tile leaves through its own LDS buffer (every wave finished reading it for the previous tile before
+    // this tile's first barrier), as rows of 512 B in the swizzled layout: one 8-byte write per four columns, read
+    // back as 16-byte row chunks and stored coalesced
+    char* O = obuf;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)  // token 8q + 4 (lane / 32) + e, column 64 wave + 32 u + j32
-          sts(O, q * 8 + (lane >> 5) * 4 + e, wave * 64 + u * 32 + j32, outv[u][q][e]);
+      for (int q = 0; q < 4; ++q)  // token j32, columns 64 wave + 32 u + 8 q + 4 (lane / 32) + (0..3)
+        *reinterpret_cast<bf16x4*>(O + loff(j32, wave * 64 + u * 32 + 8 * q + 4 * (lane >> 5))) = outv[u][q];
     lds_barrier();
     {
 #pragma unroll
