@@ -217,18 +217,19 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
-      // k-steps pipelined by hand: the fragment of step ks + 1 is read while step ks multiplies, and a scheduling
+      // k-steps pipelined by hand: the fragment of step ks + 2 is read while step ks multiplies, and a scheduling
       // barrier per step keeps the compiler from hoisting every read (and its registers) to the top. The product is
       // taken transposed, out^T = B^T in^T (the operand fragments as the left factor, the token fragments as the
       // right), so that a lane's accumulators hold four consecutive columns of one token.
-      bf16x8 af[2];
+      bf16x8 af[3];
       af[0] = frag_at(0, 0);
+      af[1] = frag_at(0, 1);
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
-        if (ks + 1 < NK) af[(ks + 1) & 1] = frag_at(0, ks + 1);
+        if (ks + 2 < NK) af[(ks + 2) % 3] = frag_at(0, ks + 2);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[u][ks], af[ks & 1], acc[u], 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[u][ks], af[ks % 3], acc[u], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll

@@ -7,8 +7,9 @@
 // Operands go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16
 // bytes at the wave's LDS base + 16 l, from any global address it chooses), in a two-stage ring: the DMA of
 // K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile, placed before the last k-step so that the
-// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs. A k-step's fragment reads for the
-// next k-step are issued between its MFMAs (one MFMA, two reads), which measured ~3% faster than one burst.
+// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs (one DMA instruction and one
+// fragment read after each of its MFMAs). A k-step's fragment reads for the next k-step are issued between its
+// MFMAs (one MFMA, two reads), which measured ~3% faster than one burst.
 // Both stage layouts are 32 KB:
 //   K-major operand: 256 rows x 128 B; the 16-byte chunk index is XOR-ed with f(row mod 32) =
 //     (row & 7) ^ ((row >> 3) & 3): 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
@@ -26,6 +27,7 @@
 // split-K each split writes its float32 partial tile; a second kernel sums the partials in split order (so
 // results do not depend on timing) and applies the epilogue.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -109,20 +111,22 @@ struct Operand {
     }
   }
 
+  // DMA instruction j (of 8) of the tile at k0 into stage st
+  __device__ __forceinline__ void dma_one(char* __restrict__ st, int k0, int j, int wave, int lane) const {
+    char* dst = st + (4 * j + wave) * 1024;
+    uint32_t o;
+    if constexpr (KMAJ) {
+      const int kmax = ((K + 7) / 8) * 8 - 8;  // keep the 16-byte read inside the row's first ceil8(K) elements
+      o = off[j] + (uint32_t)min(k0 + 8 * chk, kmax) * 2;
+    } else {
+      const int kr = min(k0 + 2 * (4 * j + wave) + (lane >> 5), K - 1);
+      o = off[j] + (uint32_t)kr * ld2;
+    }
+    __builtin_amdgcn_global_load_lds((gbl_void*)(base + o), (lds_void*)dst, 16, 0, 0);
+  }
   __device__ __forceinline__ void dma(char* __restrict__ st, int k0, int wave, int lane) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      char* dst = st + (4 * j + wave) * 1024;
-      uint32_t o;
-      if constexpr (KMAJ) {
-        const int kmax = ((K + 7) / 8) * 8 - 8;  // keep the 16-byte read inside the row's first ceil8(K) elements
-        o = off[j] + (uint32_t)min(k0 + 8 * chk, kmax) * 2;
-      } else {
-        const int kr = min(k0 + 2 * (4 * j + wave) + (lane >> 5), K - 1);
-        o = off[j] + (uint32_t)kr * ld2;
-      }
-      __builtin_amdgcn_global_load_lds((gbl_void*)(base + o), (lds_void*)dst, 16, 0, 0);
-    }
+    for (int j = 0; j < 8; ++j) dma_one(st, k0, j, wave, lane);
   }
 
   // zero the part of a staged tile that lies at k >= kend (kv = kend - k0 valid k values, 0 < kv < 64)
@@ -353,15 +357,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) {
+    char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) {
       // tile kt+1 has landed (its DMA is the only one in flight) and every wave has read tile kt
       __builtin_amdgcn_s_waitcnt(WAIT_VM0);
       __syncthreads();
-      char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
-      if (kt + 2 < nk) {
-        oa.dma(sa, kb + (kt + 2) * BK, wave, lane);
-        ob.dma(sb, kb + (kt + 2) * BK, wave, lane);
-      }
       const int kv = ke - (kb + (kt + 1) * BK);
       if (kv < BK) {  // tile kt+1 is the last one and partial
         oa.zero_tail(na, kv, tid);
@@ -372,24 +373,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // last k-step; tile kt+1's first fragments are read behind its first 4 MFMAs (12 MFMAs before their use)
+    // last k-step: its 16 MFMAs each followed by one DMA instruction of tile kt+2 (into the stage tile kt held,
+    // which no wave reads any more) and, from the fifth on, by one fragment read of tile kt+1's first k-step (at
+    // least four MFMAs before their use), so the matrix core keeps running while they issue. They run without
+    // conditions: past the end the copies read clamped (valid) addresses, and in the last tile (no barrier above,
+    // other waves may still read its stage) they go to the other stage, which nothing reads again; the epilogue's
+    // first barrier waits for them. The fragments read past the end are never used.
+    char* da = more ? sa : na;
+    const int k2 = kb + (kt + 2) * BK;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][0], fb[1][b], acc[0][b], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      const char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(na, wr + a * 32, 0, lane);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(na + STAGE, wc + b * 32, 0, lane);
+    for (int q = 0; q < 16; ++q) {
+      const int a = q >> 2, b = q & 3;
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][a], fb[1][b], acc[a][b], 0, 0, 0);
+      if (q < 8) oa.dma_one(da, k2, q, wave, lane);
+      else ob.dma_one(da + STAGE, k2, q - 8, wave, lane);
+      if (q >= 4 && q < 12) {
+        const int r = q - 4;
+        if (r < 4) fa[0][r] = frag<AK>(na, wr + r * 32, 0, lane);
+        else fb[0][r - 4] = frag<BK_>(na + STAGE, wc + (r - 4) * 32, 0, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int a = 1; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][a], fb[1][b], acc[a][b], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // the wave's 128 x 128 tile goes out through LDS (every wave is past its last fragment read first)
