@@ -179,7 +179,9 @@ __device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, 
 // Store a wave's 128 x 128 accumulator tile at out (row pitch ld elements, dtype dt; rlim x clim of it valid)
 // through the wave's EP_BYTES of LDS, one 32-row band at a time: the band is written in accumulator order
 // (row pitch EP floats, so the two half-waves land in disjoint banks) and read back as row-contiguous float4
-// chunks, which go out as 16-byte (float32) or 8-byte (bf16) stores when the row is aligned for them.
+// chunks, which go out as 16-byte (float32) or 8-byte (bf16) stores when the row is aligned for them. The region
+// is the wave's own and one wave's LDS accesses complete in order, so the bands need no barrier: the global
+// stores of one band stay in flight while the next is staged (a workgroup barrier would wait for all of them).
 constexpr int EP = 136, EP_BYTES = 32 * EP * 4;
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* lds, void* out, int dt, int64_t ld,
                                                int rlim, int clim, int lane) {
@@ -191,7 +193,6 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * EP + b * 32 + (lane & 31)] = acc[a][b][r];
-    __syncthreads();
     f32x4 vv[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -227,7 +228,6 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* 
         }
       }
     }
-    __syncthreads();
   }
 }
 
