@@ -287,7 +287,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (m0 >= M || n0 >= N) return;
   const int kb = s * fa_.kchunk, ke = min(K, kb + fa_.kchunk);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: as a scalar, the LDS addresses derived from it (DMA destinations in M0) need no
+  // per-instruction readfirstlane
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
 
   Operand<AK> oa;
