@@ -170,6 +170,9 @@ poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const fl
  *   forward   X' = X P^T,  Z = X' W0^T,  Y = Z R^T
  *   backward  dZ = dY R,  dX' = dZ W0,  dX = dX' P,  dL/dR = blocks of dY^T Z,  dL/dP = blocks of dX'^T X,
  *             then the Neumann adjoint and skew projection as in poet_linear_bwd.
+ * With T >= m the forward folds P into W0 instead (Z = X (W0 P)^T), with T >= n the backward folds R
+ * (dX' = dY (R W0)): the same products associated the other way, each with one bf16 rounding of the folded
+ * weight in place of the rounding of X' or dZ.
  * Both sides POET-BS and bf16 activations (poet_act_path_supported); every product is a bf16 GEMM with float32
  * accumulation and the primitives enter as bf16 copies. W0b is W0 in bf16 (row pitch ldw), made once by
  * poet_weight_shadow and kept current by passing it as poet_merge's W0_shadow. Workspaces: POET_OP_FWD_ACT and
@@ -179,12 +182,13 @@ int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below app
 /* W0_shadow [m x ldw] act dtype out: W0 rounded to the act dtype (round to nearest even). */
 poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream);
 
-/* opsR/opsP (nullable, bf16 in): operand copies of the primitives, 2 * poet_prim_len(side) elements: block p
+/* opsR/opsP (nullable, bf16 in): operand copies of the primitives, 3 * poet_prim_len(side) elements: block p
  * of F at offset p*bp*bp and its transpose at num_prims*bp*bp + p*bp*bp, both zero outside the block's c x c
- * corner; poet_build_orthogonal_group writes them. Each bp x bp block M (M = F or F^T) is stored row-major
- * (M(i, j) at i*bp + j) unless bp is a multiple of 32; then it is stored in the order the MFMA fragments of the
- * application kernel are loaded: M(i, j) at ((i/32 * bp/16 + j/16) * 64 + (j/8 % 2) * 32 + i % 32) * 8 + j % 8.
- * NULL: the call makes them in its workspace from primR/primP. */
+ * corner, then at 2*num_prims*bp*bp + p*bp*bp block p of F as it is (row-major, bf16 of the primitive, padding
+ * included); poet_build_orthogonal_group writes them. Each bp x bp block M (M = F or F^T) of the first two parts is
+ * stored row-major (M(i, j) at i*bp + j) unless bp is a multiple of 32; then it is stored in the order the MFMA
+ * fragments of the application kernel are loaded: M(i, j) at ((i/32 * bp/16 + j/16) * 64 + (j/8 % 2) * 32 +
+ * i % 32) * 8 + j % 8. NULL: the call makes what it needs in its workspace from primR/primP. */
 
 /* X [T x ldx] in, Y [T x ldy] out, Z [T x ldy] out: X P^T W0^T, kept for the backward (all bf16). */
 poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
@@ -207,6 +211,16 @@ poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, cons
                                       const void* opsR, const void* opsP, const void* X, const void* Z,
                                       const void* dY, void* dX, float* dprimR, float* dprimP, void* ws,
                                       size_t ws_bytes, void* stream);
+
+/* The same forward and backward with the factors folded into the weight beforehand (poet_fold_weights_group):
+ * W0P [m x ldw] bf16 = W0 P, RW0 [m x ldw] bf16 = R W0, each one bf16 rounding of the exact product of the bf16
+ * copies. Forward: Z = X W0P^T, Y = Z R^T (Y, Z as in poet_linear_fwd_act). Backward: dX' = dY RW0, dX = dX' P
+ * (dX nullable), dprimR / dprimP as in poet_linear_bwd_act_prims. Workspaces: POET_OP_FWD_ACT, POET_OP_BWD_ACT. */
+poet_status poet_linear_fwd_folded(const poet_layer* L, const void* W0P, const float* primR, const void* opsR,
+                                   const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream);
+poet_status poet_linear_bwd_folded_prims(const poet_layer* L, const void* RW0, const float* primP, const void* opsP,
+                                         const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
+                                         float* dprimP, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- grouped calls ------------------------------------------------------------------------------------
  * The per-block steps of many sides (for instance both sides of every linear of a transformer block) in shared
@@ -232,6 +246,18 @@ size_t poet_adjoint_group_workspace_bytes(int32_t count, const poet_side* sides)
 poet_status poet_adjoint_group(int32_t count, const poet_side* sides, const float* const* dprim,
                                const void* const* powers, float* const* dtheta, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* The factors of count linears folded into their bf16 weights (the weights the folded activation-side calls
+ * take): W0P[i] = W0b[i] P_i and RW0[i] = R_i W0b[i] (bf16, m x ldw, row pitch ldw), one batched product per factor
+ * over its blocks, products of one shape in shared launches. The tables W0P and RW0 are nullable, and so is each
+ * entry (nothing written for it); opsR / opsP (nullable tables and entries) are the operand copies of
+ * poet_build_orthogonal_group, whose row-order part is used; without them the primitives are converted in the
+ * workspace. Both sides POET-BS, bf16 activations. ws: poet_fold_group_workspace_bytes(count, layers) bytes. */
+size_t poet_fold_group_workspace_bytes(int32_t count, const poet_layer* layers);
+poet_status poet_fold_weights_group(int32_t count, const poet_layer* layers, const void* const* W0b,
+                                    const float* const* primR, const float* const* primP, const void* const* opsR,
+                                    const void* const* opsP, void* const* W0P, void* const* RW0, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Merge-then-reinitialize (Approach section; period 400 in the "Measured effects" table):
  *   W0 <- R W0 P in float32 (in place), using the same truncated primitives the forward pass uses;

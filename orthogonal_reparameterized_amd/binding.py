@@ -29,7 +29,8 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
-           "poet_merge_group_workspace_bytes", "poet_merge_group")
+           "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
+           "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE = range(9)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
@@ -106,6 +107,12 @@ def lib() -> ctypes.CDLL:
     L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_linear_fwd_folded.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_bwd_folded_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_fold_group_workspace_bytes.argtypes = [I32, P(poet_layer)]
+    L.poet_fold_group_workspace_bytes.restype = S
+    L.poet_fold_weights_group.argtypes = [I32, P(poet_layer), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), VP, S,
+                                          VP]
     L.poet_merge_group_workspace_bytes.argtypes = [I32, P(poet_layer)]
     L.poet_merge_group_workspace_bytes.restype = S
     L.poet_merge_group.argtypes = [I32, P(poet_layer), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), U64,
@@ -356,8 +363,8 @@ def poet_weight_shadow(L: poet_layer, W0, W0_shadow, stream=None):
 
 
 def _ops(t, name, s: poet_side):
-    """Operand copies of a side's primitives (2 * prim_len bf16), or None."""
-    return _ptr(t, name, 4 * poet_prim_len(s), "bfloat16", allow_none=True)
+    """Operand copies of a side's primitives (3 * prim_len bf16), or None."""
+    return _ptr(t, name, 6 * poet_prim_len(s), "bfloat16", allow_none=True)
 
 
 def poet_linear_fwd_act(L: poet_layer, W0b, primR, primP, X, Y, Z, ws=None, stream=None, opsR=None, opsP=None):
@@ -391,6 +398,35 @@ def poet_linear_bwd_act(L: poet_layer, W0b, primR, primP, powersR, powersP, X, Z
         _ptr(dthetaP, "dthetaP", 4 * poet_theta_len(L.P), "float32"),
         _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_linear_bwd_act")
+
+
+def poet_linear_fwd_folded(L: poet_layer, W0P, primR, X, Y, Z, ws=None, stream=None, opsR=None):
+    """Activation-side forward with P folded into the weight beforehand: Z = X W0P^T, Y = Z R^T."""
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_FWD_ACT)
+    st = lib().poet_linear_fwd_folded(
+        ctypes.byref(L), _ptr(W0P, "W0P", b["W"], act), _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"),
+        _ops(opsR, "opsR", L.R), _ptr(X, "X", b["X"], act, allow_none=L.T == 0),
+        _ptr(Y, "Y", b["Y"], act, allow_none=L.T == 0), _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0),
+        _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_fwd_folded")
+
+
+def poet_linear_bwd_folded_prims(L: poet_layer, RW0, primP, X, Z, dY, dX, dprimR, dprimP, ws=None, stream=None,
+                                 opsP=None):
+    """Activation-side backward with R folded into the weight beforehand (dX' = dY RW0), up to dprimR, dprimP."""
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    need = poet_workspace_bytes(L, POET_OP_BWD_ACT)
+    st = lib().poet_linear_bwd_folded_prims(
+        ctypes.byref(L), _ptr(RW0, "RW0", b["W"], act), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ops(opsP, "opsP", L.P), _ptr(X, "X", b["X"], act, allow_none=L.T == 0),
+        _ptr(Z, "Z", b["Y"], act, allow_none=L.T == 0), _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dX, "dX", b["X"], act, allow_none=True), _ptr(dprimR, "dprimR", 4 * poet_prim_len(L.R), "float32"),
+        _ptr(dprimP, "dprimP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd_folded_prims")
 
 
 def poet_linear_bwd_act_prims(L: poet_layer, W0b, primR, primP, X, Z, dY, dX, dprimR, dprimP, ws=None, stream=None,
@@ -450,7 +486,7 @@ def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=No
                     [poet_powers_len(s) * _esz(s.dtype) for s in sides], [_dt_name(s.dtype) for s in sides],
                     [s.k == 0 for s in sides])
     op = None if ops is None else _ptr_table(ops, [f"ops[{i}]" for i in range(n)],
-                                             [4 * poet_prim_len(s) for s in sides], ["bfloat16"] * n, [True] * n)
+                                             [6 * poet_prim_len(s) for s in sides], ["bfloat16"] * n, [True] * n)
     st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, op, _ptr(ws, "ws", need, allow_none=True),
                                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_build_orthogonal_group")
@@ -539,3 +575,40 @@ def poet_merge_group(layers, W0s, shadows, thetaRs, thetaPs, primRs, primPs, idx
                                 _ptr(ws, "ws", need, allow_none=True),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_merge_group")
+
+
+def poet_fold_group_workspace_bytes(layers) -> int:
+    return int(lib().poet_fold_group_workspace_bytes(len(layers), _layer_array(layers)))
+
+
+def poet_fold_weights_group(layers, W0bs, primRs, primPs, W0Ps, RW0s, ws=None, stream=None, opsRs=None, opsPs=None):
+    """W0P[i] = W0b[i] P_i and RW0[i] = R_i W0b[i] for every layer (bf16, m x ldw); W0Ps / RW0s (and opsRs / opsPs)
+    may be None or lists with None entries."""
+    n = len(layers)
+    W0Ps = [None] * n if W0Ps is None else W0Ps
+    RW0s = [None] * n if RW0s is None else RW0s
+    opsRs = [None] * n if opsRs is None else opsRs
+    opsPs = [None] * n if opsPs is None else opsPs
+    if not all(len(t) == n for t in (W0bs, primRs, primPs, W0Ps, RW0s, opsRs, opsPs)):
+        raise ValueError("every table must have one entry per layer")
+    need = poet_fold_group_workspace_bytes(layers)
+    if ws is None and need > 0:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=W0bs[0].device)
+    bs = [_layer_bytes(L) for L in layers]
+    act = [_dt_name(L.act_dtype) for L in layers]
+    nm = lambda t, i: f"{t}[{i}]"
+    w0 = _ptr_table(W0bs, [nm("W0bs", i) for i in range(n)], [b["W"] for b in bs], act, [False] * n)
+    pR = _ptr_table(primRs, [nm("primRs", i) for i in range(n)], [4 * poet_prim_len(L.R) for L in layers],
+                    ["float32"] * n, [w is None for w in RW0s])
+    pP = _ptr_table(primPs, [nm("primPs", i) for i in range(n)], [4 * poet_prim_len(L.P) for L in layers],
+                    ["float32"] * n, [w is None for w in W0Ps])
+    oR = _ptr_table(opsRs, [nm("opsRs", i) for i in range(n)], [6 * poet_prim_len(L.R) for L in layers],
+                    ["bfloat16"] * n, [True] * n)
+    oP = _ptr_table(opsPs, [nm("opsPs", i) for i in range(n)], [6 * poet_prim_len(L.P) for L in layers],
+                    ["bfloat16"] * n, [True] * n)
+    fP = _ptr_table(W0Ps, [nm("W0Ps", i) for i in range(n)], [b["W"] for b in bs], act, [True] * n)
+    fR = _ptr_table(RW0s, [nm("RW0s", i) for i in range(n)], [b["W"] for b in bs], act, [True] * n)
+    st = lib().poet_fold_weights_group(n, _layer_array(layers), w0, pR, pP, oR, oP, fP, fR,
+                                       _ptr(ws, "ws", need, allow_none=True),
+                                       0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_fold_weights_group")

@@ -512,8 +512,8 @@ bool fast_gemm_group_eligible(const GemmDesc* pr, int n) {
       return false;
     blocks += (size_t)b.batch;
   }
-  // the split-K partials of every problem (at least 2 splits) in the first one's scratch
-  return a.part && a.part_elems >= 2 * blocks * a.M * a.N;
+  // the split-K partials of every problem (at least 2 splits) in the first one's scratch; no scratch: no split
+  return !a.part || a.part_elems >= 2 * blocks * a.M * a.N;
 }
 
 bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b) {

@@ -49,7 +49,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st);
 // Up to 16 problems of one shape (M, N, K, operand orientations, batch strides, output pitch and type) in one
 // launch, each with its own operands, leading dimensions, extents and batch count (e.g. the R- and P-side
 // token-axis contractions of a linear, or one power-chain step of many FS sides); plain epilogue; the split-K
-// partials of all go to the first problem's scratch.
+// partials of all go to the first problem's scratch (none: no split-K).
 bool fast_gemm_group_eligible(const GemmDesc* probs, int n);
 hipError_t launch_fast_gemm_group(const GemmDesc* probs, int n, hipStream_t st);
 bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b);
@@ -69,9 +69,9 @@ struct ChainArgs {
   const float* X0 = nullptr; int64_t ldx0 = 0, sx0 = 0;
   __bf16* Y = nullptr; int64_t ldy = 0, sy = 0, jstep = 0;
   int write_x0 = 0;
-  // build only, nullable: bf16 copies of the finished primitives for the activation-side products, zero outside
-  // each block's c x c corner (c = min(bp, d - p bp) for BS, bp for FS): ops[p][i][j] = R_p(i, j) and, at offset
-  // nprim bp^2, ops[p][j][i] (the transpose)
+  // build only, nullable: bf16 copies of the finished primitives for the activation-side products: R_p and its
+  // transpose as operand rows (zero outside each block's c x c corner, c = min(bp, d - p bp) for BS, bp for FS; in
+  // fragment order where act_frag_layout(bp)), then at offset 2 nprim bp^2 the primitives as they are, row-major
   __bf16* ops = nullptr;
   int d = 0, mode = 0;
 };

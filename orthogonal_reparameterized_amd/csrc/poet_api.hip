@@ -27,6 +27,13 @@ poet_status fail(poet_status st, const char* fmt, ...) {
   return st;
 }
 
+// hipError_t helpers: return the first failing call's error
+#define HIP_RET(expr)                 \
+  do {                                \
+    const hipError_t r_ = (expr);     \
+    if (r_ != hipSuccess) return r_;  \
+  } while (0)
+
 #define HIP_TRY(expr)                                                                        \
   do {                                                                                       \
     hipError_t e_ = (expr);                                                                  \
@@ -439,6 +446,8 @@ size_t plan_bwd(const poet_layer& L, const SideInfo& R, const SideInfo& P, void*
 // the W0 GEMM and W is never formed:
 //   forward   X' = X P^T,  Z = X' W0^T,  Y = Z R^T
 //   backward  dZ = dY R,  dX' = dZ W0,  dX = dX' P;  dL/dR = blocks of dY^T Z,  dL/dP = blocks of dX'^T X
+// With at least as many tokens as W0 has rows (columns), P (R) is folded into the bf16 copy of W0 instead:
+// Z = X (W0 P)^T and dX' = dY (R W0), so X' and dZ are never formed.
 // (the same products as the weight-side path, associated the other way: G W0P^T = dY^T X P^T W0^T = dY^T Z).
 // Every product is a bf16 GEMM with float32 accumulation; the factors enter as bf16 copies of the primitives.
 // ------------------------------------------------------------------------------------------------------------
@@ -446,12 +455,20 @@ bool act_path_ok(const poet_layer& L, const SideInfo& R, const SideInfo& P) {
   return L.act_dtype == BF16 && R.mode == POET_BS && P.mode == POET_BS;
 }
 
+// A factor is folded into the weight (W0 P for the forward's token GEMM, R W0 for the backward's) instead of being
+// applied to the tokens (X P^T, dY R) when there are at least as many tokens as the weight has rows (P) or columns
+// (R): the fold touches m x n elements, the application T x n (or T x m).
+// Blocks below 128 are not folded: the product would run on the generic kernel.
+bool fold_P(const poet_layer& L, const SideInfo& P) { return L.T >= L.m && P.bp >= 128; }
+bool fold_R(const poet_layer& L, const SideInfo& R) { return L.T >= L.n && R.bp >= 128; }
+
 struct ActFwdPlan {
-  __bf16 *Xp = nullptr, *Rb = nullptr, *Pb = nullptr;
+  __bf16 *Xp = nullptr, *W0P = nullptr, *Rb = nullptr, *Pb = nullptr;
 };
 size_t plan_fwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, ActFwdPlan* p) {
   Arena a(ws);
-  p->Xp = a.take<__bf16>((size_t)L.T * L.ldx);
+  if (fold_P(L, P)) p->W0P = a.take<__bf16>((size_t)L.m * L.ldw);
+  else p->Xp = a.take<__bf16>((size_t)L.T * L.ldx);
   p->Rb = a.take<__bf16>(R.prim_len);
   p->Pb = a.take<__bf16>(P.prim_len);
   return a.used();
@@ -469,7 +486,7 @@ size_t super_elems(const SideInfo& S) {
 }
 
 struct ActBwdPlan {
-  __bf16 *dZ = nullptr, *dXp = nullptr, *Rb = nullptr, *Pb = nullptr;
+  __bf16 *dZ = nullptr, *RW0 = nullptr, *dXp = nullptr, *Rb = nullptr, *Pb = nullptr;
   float *dRg = nullptr, *dPg = nullptr;
   float* sup = nullptr;  // super-block products of small blocks
   size_t sup_elems = 0;
@@ -477,7 +494,8 @@ struct ActBwdPlan {
 };
 size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, void* ws, ActBwdPlan* p) {
   Arena a(ws);
-  p->dZ = a.take<__bf16>((size_t)L.T * L.ldy);
+  if (fold_R(L, R)) p->RW0 = a.take<__bf16>((size_t)L.m * L.ldw);
+  else p->dZ = a.take<__bf16>((size_t)L.T * L.ldy);
   p->dXp = a.take<__bf16>((size_t)L.T * L.ldx);
   p->Rb = a.take<__bf16>(R.prim_len);
   p->Pb = a.take<__bf16>(P.prim_len);
@@ -563,6 +581,66 @@ hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, con
   if (opsF && act_frag_layout(S.bp)) opsF = nullptr;
   if (!opsF && (e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
   return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF : Fb, trans, out, ldo), st);
+}
+
+// A factor folded into the bf16 copy of W0 (row pitch ldw): P side out = W0b P (P's blocks along the columns), R side
+// out = R W0b (R's blocks along the rows); one batched bf16 GEMM over the factor's blocks with the full primitives
+// as bf16 operands in row order (the third part of the caller's operand copies, else made in Fb), ragged last
+// blocks through the extents.
+GemmDesc fold_desc(const poet_layer& L, const SideInfo& S, bool rside, const void* W0b, const __bf16* Fb, __bf16* out) {
+  GemmDesc g;
+  g.kclass = POET_K_APPLY;
+  g.compute = BF16;
+  g.batch = S.nprim;
+  g.K = S.bp;
+  g.a_dt = g.b_dt = BF16;
+  g.c_dt = BF16;
+  g.C = out; g.ldc = L.ldw;
+  if (!rside) {  // out[:, J] = W0b[:, J] P_J
+    g.M = L.m; g.N = S.bp; g.Ntot = g.Ktot = L.n;
+    g.A = W0b; g.lda = L.ldw; g.sA = S.bp; g.a_kmajor = 1;
+    g.B = Fb; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_kmajor = 0;  // B(k, j) = P_J[k][j]
+    g.sC = S.bp;
+  } else {  // out[I, :] = R_I W0b[I, :]
+    g.M = S.bp; g.N = L.n; g.Mtot = g.Ktot = L.m;
+    g.A = Fb; g.lda = S.bp; g.sA = (int64_t)S.bp * S.bp; g.a_kmajor = 1;  // A(i, k) = R_I[i][k]
+    g.B = W0b; g.ldb = L.ldw; g.sB = (int64_t)S.bp * L.ldw; g.b_kmajor = 0;
+    g.sC = (int64_t)S.bp * L.ldw;
+  }
+  return g;
+}
+hipError_t fold_factor(const poet_layer& L, const SideInfo& S, bool rside, const void* W0b, const float* prim,
+                       const void* ops, __bf16* Fb, __bf16* out, hipStream_t st) {
+  if (ops) {
+    Fb = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(ops)) + 2 * S.prim_len;
+  } else {
+    const hipError_t e = prims_bf16(S, prim, Fb, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm(fold_desc(L, S, rside, W0b, Fb, out), st);
+}
+
+// products of one shape (sizes, orientations, strides, output pitch and type) share a grouped launch, 16 at most
+bool same_shape(const GemmDesc& a, const GemmDesc& b) {
+  return a.M == b.M && a.N == b.N && a.K == b.K && a.Mtot == b.Mtot && a.Ntot == b.Ntot && a.Ktot == b.Ktot &&
+         a.batch == b.batch && a.a_kmajor == b.a_kmajor && a.b_kmajor == b.b_kmajor && a.lda == b.lda &&
+         a.ldb == b.ldb && a.sA == b.sA && a.sB == b.sB && a.ldc == b.ldc && a.sC == b.sC && a.c_dt == b.c_dt;
+}
+hipError_t launch_grouped(const std::vector<GemmDesc>& all, hipStream_t st) {
+  std::vector<bool> done(all.size(), false);
+  for (size_t i = 0; i < all.size(); ++i) {
+    if (done[i]) continue;
+    GemmDesc pr[MAXG];
+    int n = 0;
+    for (size_t j = i; j < all.size() && n < MAXG; ++j)
+      if (!done[j] && same_shape(all[i], all[j])) { pr[n++] = all[j]; done[j] = true; }
+    if (n > 1 && fast_gemm_group_eligible(pr, n)) {
+      HIP_RET(launch_fast_gemm_group(pr, n, st));
+    } else {
+      for (int u = 0; u < n; ++u) HIP_RET(launch_gemm(pr[u], st));
+    }
+  }
+  return hipSuccess;
 }
 
 // Buffers of the float32-accurate FS merge of one side (reused by the other): the gathered columns (P) or rows (R)
@@ -1175,13 +1253,18 @@ poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_sh
   return POET_OK;
 }
 
-poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
-                                const void* opsR, const void* opsP, const void* X, void* Y, void* Z, void* ws,
-                                size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// the activation-side forward; W0P (nullable) is W0 P made beforehand (poet_fold_weights_group), else P is folded
+// here or applied to the tokens
+poet_status fwd_act(const poet_layer* L, const void* W0b, const void* W0P, const float* primR, const float* primP,
+                    const void* opsR, const void* opsP, const void* X, void* Y, void* Z, void* ws, size_t ws_bytes,
+                    void* stream) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
   if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
-  if (!W0b || !primR || !primP) return fail(POET_E_ARG, "null W0 shadow or primitive");
+  if (!primR || (!W0P && (!W0b || !primP))) return fail(POET_E_ARG, "null W0 shadow or primitive");
   if (L->T > 0 && (!X || !Y || !Z)) return fail(POET_E_ARG, "null X, Y or Z");
   ActFwdPlan p;
   if (!check_ws(ws, ws_bytes, plan_fwd_act(*L, R, P, nullptr, &p))) return g_last;
@@ -1189,32 +1272,51 @@ poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const floa
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (L->T == 0) return POET_OK;
   const int T = L->T;
-  HIP_TRY(act_factor(P, T, X, L->ldx, primP, opsP, p.Pb, true, p.Xp, L->ldx, st));  // X' = X P^T
-  {  // Z = X' W0^T
+  const bool fold = W0P || fold_P(*L, P);
+  if (!W0P) {
+    if (fold) HIP_TRY(fold_factor(*L, P, false, W0b, primP, opsP, p.Pb, p.W0P, st));  // W0P = W0 P
+    else HIP_TRY(act_factor(P, T, X, L->ldx, primP, opsP, p.Pb, true, p.Xp, L->ldx, st));  // X' = X P^T
+  }
+  {  // Z = X (W0 P)^T = X' W0^T
     GemmDesc g;
     g.kclass = POET_K_TOKEN_FWD;
     g.compute = BF16; g.M = T; g.N = L->m; g.K = L->n;
-    g.A = p.Xp; g.lda = L->ldx; g.a_dt = BF16; g.a_kmajor = 1;
-    g.B = W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 1;
+    g.A = fold ? X : p.Xp; g.lda = L->ldx; g.a_dt = BF16; g.a_kmajor = 1;
+    g.B = W0P ? W0P : fold ? p.W0P : W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 1;
     g.C = Z; g.ldc = L->ldy; g.c_dt = BF16;
     HIP_TRY(launch_gemm(g, st));
   }
   HIP_TRY(act_factor(R, T, Z, L->ldy, primR, opsR, p.Rb, true, Y, L->ldy, st));  // Y = Z R^T
   return POET_OK;
 }
+}  // namespace
+
+extern "C" {
+
+poet_status poet_linear_fwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
+                                const void* opsR, const void* opsP, const void* X, void* Y, void* Z, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return fwd_act(L, W0b, nullptr, primR, primP, opsR, opsP, X, Y, Z, ws, ws_bytes, stream);
+}
+
+poet_status poet_linear_fwd_folded(const poet_layer* L, const void* W0P, const float* primR, const void* opsR,
+                                   const void* X, void* Y, void* Z, void* ws, size_t ws_bytes, void* stream) {
+  if (!W0P) return fail(POET_E_ARG, "null folded weight");
+  return fwd_act(L, nullptr, W0P, primR, nullptr, opsR, nullptr, X, Y, Z, ws, ws_bytes, stream);
+}
 
 }  // extern "C"
 
 namespace {
 // the activation-side backward; with dprimR/dprimP given it stops at the primitive gradients
-poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, const float* primP, const void* opsR,
-                    const void* opsP, const void* powersR,
+poet_status bwd_act(const poet_layer* L, const void* W0b, const void* RW0, const float* primR, const float* primP,
+                    const void* opsR, const void* opsP, const void* powersR,
                     const void* powersP, const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
                     float* dthetaP, float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
   if (!act_path_ok(*L, R, P)) return fail(POET_E_UNSUPPORTED, "the activation-side path needs POET-BS sides and bf16 activations");
-  if (!W0b || !primR || !primP) return fail(POET_E_ARG, "null W0 shadow or primitive");
+  if (!primP || (!RW0 && (!W0b || !primR))) return fail(POET_E_ARG, "null W0 shadow or primitive");
   if (L->T > 0 && (!X || !Z || !dY)) return fail(POET_E_ARG, "null X, Z or dY");
   const bool prims_only = dprimR || dprimP;
   if (prims_only) {
@@ -1230,13 +1332,17 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int T = L->T;
   if (T > 0) {
-    HIP_TRY(act_factor(R, T, dY, L->ldy, primR, opsR, p.Rb, false, p.dZ, L->ldy, st));  // dZ = dY R
-    {  // dX' = dZ W0
+    const bool fold = RW0 || fold_R(*L, R);
+    if (!RW0) {
+      if (fold) HIP_TRY(fold_factor(*L, R, true, W0b, primR, opsR, p.Rb, p.RW0, st));  // RW0 = R W0
+      else HIP_TRY(act_factor(R, T, dY, L->ldy, primR, opsR, p.Rb, false, p.dZ, L->ldy, st));  // dZ = dY R
+    }
+    {  // dX' = dY (R W0) = dZ W0
       GemmDesc g;
       g.kclass = POET_K_TOKEN_DX;
       g.compute = BF16; g.M = T; g.N = L->n; g.K = L->m;
-      g.A = p.dZ; g.lda = L->ldy; g.a_dt = BF16; g.a_kmajor = 1;
-      g.B = W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 0;
+      g.A = fold ? dY : p.dZ; g.lda = L->ldy; g.a_dt = BF16; g.a_kmajor = 1;
+      g.B = RW0 ? RW0 : fold ? p.RW0 : W0b; g.ldb = L->ldw; g.b_dt = BF16; g.b_kmajor = 0;
       g.C = p.dXp; g.ldc = L->ldx; g.c_dt = BF16;
       HIP_TRY(launch_gemm(g, st));
     }
@@ -1269,13 +1375,6 @@ poet_status bwd_act(const poet_layer* L, const void* W0b, const float* primR, co
   return POET_OK;
 }
 }  // namespace
-
-// hipError_t helpers: return the first failing call's error
-#define HIP_RET(expr)                 \
-  do {                                \
-    const hipError_t r_ = (expr);     \
-    if (r_ != hipSuccess) return r_;  \
-  } while (0)
 
 // the in-place block-diagonal merge of one weight, as an item of launch_bs_merge_group
 MergeItem merge_item(const poet_layer& L, const SideInfo& R, const SideInfo& P, float* W0, void* shadow,
@@ -1379,8 +1478,8 @@ poet_status poet_linear_bwd_act(const poet_layer* L, const void* W0b, const floa
                                 const void* opsR, const void* opsP, const void* powersR, const void* powersP,
                                 const void* X, const void* Z, const void* dY, void* dX, float* dthetaR,
                                 float* dthetaP, void* ws, size_t ws_bytes, void* stream) {
-  return bwd_act(L, W0b, primR, primP, opsR, opsP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP, nullptr, nullptr,
-                 ws, ws_bytes, stream);
+  return bwd_act(L, W0b, nullptr, primR, primP, opsR, opsP, powersR, powersP, X, Z, dY, dX, dthetaR, dthetaP, nullptr,
+                 nullptr, ws, ws_bytes, stream);
 }
 
 poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, const float* primR, const float* primP,
@@ -1388,8 +1487,71 @@ poet_status poet_linear_bwd_act_prims(const poet_layer* L, const void* W0b, cons
                                       const void* dY, void* dX, float* dprimR, float* dprimP, void* ws,
                                       size_t ws_bytes, void* stream) {
   if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
-  return bwd_act(L, W0b, primR, primP, opsR, opsP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr, dprimR, dprimP,
-                 ws, ws_bytes, stream);
+  return bwd_act(L, W0b, nullptr, primR, primP, opsR, opsP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr, dprimR,
+                 dprimP, ws, ws_bytes, stream);
+}
+
+poet_status poet_linear_bwd_folded_prims(const poet_layer* L, const void* RW0, const float* primP, const void* opsP,
+                                         const void* X, const void* Z, const void* dY, void* dX, float* dprimR,
+                                         float* dprimP, void* ws, size_t ws_bytes, void* stream) {
+  if (!RW0) return fail(POET_E_ARG, "null folded weight");
+  if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  return bwd_act(L, nullptr, RW0, nullptr, primP, nullptr, opsP, nullptr, nullptr, X, Z, dY, dX, nullptr, nullptr,
+                 dprimR, dprimP, ws, ws_bytes, stream);
+}
+
+// Workspace of a grouped fold: bf16 row-order copies of every primitive (used where no operand copies are given).
+size_t poet_fold_group_workspace_bytes(int32_t count, const poet_layer* layers) {
+  if (count <= 0 || !layers) return 0;
+  Arena a(nullptr);
+  for (int i = 0; i < count; ++i) {
+    SideInfo R, P;
+    if (!layer_info(&layers[i], &R, &P)) return 0;
+    a.take<__bf16>(R.prim_len);
+    a.take<__bf16>(P.prim_len);
+  }
+  return a.used();
+}
+
+poet_status poet_fold_weights_group(int32_t count, const poet_layer* layers, const void* const* W0b,
+                                    const float* const* primR, const float* const* primP, const void* const* opsR,
+                                    const void* const* opsP, void* const* W0P, void* const* RW0, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (count < 0) return fail(POET_E_ARG, "count = %d must be >= 0", count);
+  if (count == 0) return POET_OK;
+  if (!layers || !W0b) return fail(POET_E_ARG, "null layers or W0 shadow table");
+  if (!W0P && !RW0) return POET_OK;
+  std::vector<SideInfo> R(count), P(count);
+  for (int i = 0; i < count; ++i) {
+    if (!layer_info(&layers[i], &R[i], &P[i])) return g_last;
+    if (!act_path_ok(layers[i], R[i], P[i]))
+      return fail(POET_E_UNSUPPORTED, "layers[%d]: folding needs POET-BS sides and bf16 activations", i);
+    if (!W0b[i]) return fail(POET_E_ARG, "null W0b[%d]", i);
+    if (W0P && W0P[i] && !(primP && primP[i])) return fail(POET_E_ARG, "null primP[%d]", i);
+    if (RW0 && RW0[i] && !(primR && primR[i])) return fail(POET_E_ARG, "null primR[%d]", i);
+  }
+  if (!check_ws(ws, ws_bytes, poet_fold_group_workspace_bytes(count, layers))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Arena a(ws);
+  std::vector<GemmDesc> gP, gR;
+  for (int i = 0; i < count; ++i) {
+    const poet_layer& L = layers[i];
+    __bf16* fR = a.take<__bf16>(R[i].prim_len);
+    __bf16* fP = a.take<__bf16>(P[i].prim_len);
+    if (W0P && W0P[i]) {  // row-order P: the third part of the operand copies, or converted here
+      const __bf16* Fb = opsP && opsP[i] ? reinterpret_cast<const __bf16*>(opsP[i]) + 2 * P[i].prim_len : fP;
+      if (Fb == fP) HIP_TRY(prims_bf16(P[i], primP[i], fP, st));
+      gP.push_back(fold_desc(L, P[i], false, W0b[i], Fb, reinterpret_cast<__bf16*>(W0P[i])));
+    }
+    if (RW0 && RW0[i]) {
+      const __bf16* Fb = opsR && opsR[i] ? reinterpret_cast<const __bf16*>(opsR[i]) + 2 * R[i].prim_len : fR;
+      if (Fb == fR) HIP_TRY(prims_bf16(R[i], primR[i], fR, st));
+      gR.push_back(fold_desc(L, R[i], true, W0b[i], Fb, reinterpret_cast<__bf16*>(RW0[i])));
+    }
+  }
+  HIP_TRY(launch_grouped(gP, st));
+  HIP_TRY(launch_grouped(gR, st));
+  return POET_OK;
 }
 
 size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
@@ -1493,6 +1655,7 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     if (!o || chain_side(S[i], powers[i])) continue;
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, true, o, st));
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, false, o + S[i].prim_len, st));
+    HIP_TRY(prims_bf16(S[i], prim[i], o + 2 * S[i].prim_len, st));
   }
   return POET_OK;
 }

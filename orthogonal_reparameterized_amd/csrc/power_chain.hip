@@ -157,6 +157,13 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
         if (n4 >= nv) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(Rs + i * RP + n4);
         *reinterpret_cast<f32x4*>(prim + (int64_t)i * bp + n0 + n4) = v;
+        if (ops) {  // the third copy: the primitive as it is, in row order (for folding it into a weight)
+          bf16x4 r;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) r[t] = (__bf16)v[t];
+          *reinterpret_cast<bf16x4*>(c.ops + 2 * (int64_t)c.nprim * bp * bp + (int64_t)p * bp * bp + (int64_t)i * bp +
+                                     n0 + n4) = r;
+        }
         if (ops && !frag) {
           bf16x4 w;
 #pragma unroll

@@ -78,6 +78,9 @@ class PoetLinear:
         # bf16 operand copies of the primitives (both orientations), written by PoetGroup.build; None until then
         # (and after a one-linear build, which leaves them stale)
         self.opsR = self.opsP = None
+        # the factors folded into the bf16 weight (W0 P, R W0), written by PoetGroup.build for large token counts;
+        # None until then (and after a one-linear build, which leaves them stale)
+        self.W0P = self.RW0 = None
         if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
             self.W0b = torch.empty((m, self.L.ldw), dtype=self.act, device=self.dev)
             B.poet_weight_shadow(self.L, self.W0, self.W0b)
@@ -114,6 +117,7 @@ class PoetLinear:
 
     def build(self, stream=None, qnorm: bool = False):
         self.opsR = self.opsP = None  # the one-side build does not write them
+        self.W0P = self.RW0 = None
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
                                 self.ws, stream)
         B.poet_build_orthogonal(self.L.P, self.thetaP, self.primP, self._powers("P"), self.qnormP if qnorm else None,
@@ -134,9 +138,12 @@ class PoetLinear:
 
     def forward_act(self, X, Y, Z, stream=None):
         """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
-        operand copies of the primitives come from the last PoetGroup.build, when one made them."""
-        B.poet_linear_fwd_act(self.L, self.W0b, self.primR, self.primP, X, Y, Z, self.ws, stream,
-                              opsR=self.opsR, opsP=self.opsP)
+        operand copies of the primitives (and W0 P, folded) come from the last PoetGroup.build, when one made them."""
+        if self.W0P is not None:
+            B.poet_linear_fwd_folded(self.L, self.W0P, self.primR, X, Y, Z, self.ws, stream, opsR=self.opsR)
+        else:
+            B.poet_linear_fwd_act(self.L, self.W0b, self.primR, self.primP, X, Y, Z, self.ws, stream,
+                                  opsR=self.opsR, opsP=self.opsP)
 
     def backward_act(self, X, Z, dY, dX, stream=None):
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
@@ -159,8 +166,12 @@ class PoetLinear:
         """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
         PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
         self._dprims()
-        B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
-                                    self.ws, stream, opsR=self.opsR, opsP=self.opsP)
+        if self.RW0 is not None:
+            B.poet_linear_bwd_folded_prims(self.L, self.RW0, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
+                                           self.ws, stream, opsP=self.opsP)
+        else:
+            B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR,
+                                        self.dprimP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
@@ -188,14 +199,25 @@ class PoetGroup:
             raise ValueError("PoetGroup needs at least one linear")
         self.sides = [s for pl in self.linears for s in (pl.L.R, pl.L.P)]
         dev = self.linears[0].dev
-        # operand copies for the activation-side calls of BS sides (2 * prim_len bf16 per side)
+        # operand copies for the activation-side calls of BS sides (3 * prim_len bf16 per side)
         self._ops = {}
         for pl in self.linears:
             if pl.act_path:
-                self._ops[id(pl)] = tuple(torch.empty(2 * B.poet_prim_len(s), dtype=torch.bfloat16, device=dev)
+                self._ops[id(pl)] = tuple(torch.empty(3 * B.poet_prim_len(s), dtype=torch.bfloat16, device=dev)
                                           for s in (pl.L.R, pl.L.P))
+        # factors folded into the bf16 weights of activation-side linears with at least as many tokens as the
+        # weight has rows (P) or columns (R), blocks of 128 or more (smaller blocks would run on the generic kernel)
+        self._fold = {}
+        for pl in self.linears:
+            if pl.act_path:
+                fP = pl.T >= pl.m and pl.L.P.b >= 128
+                fR = pl.T >= pl.n and pl.L.R.b >= 128
+                self._fold[id(pl)] = (torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fP else None,
+                                      torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fR else None)
+        act = [pl for pl in self.linears if pl.act_path]
         need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides),
-                   B.poet_merge_group_workspace_bytes([pl.L for pl in self.linears]))
+                   B.poet_merge_group_workspace_bytes([pl.L for pl in self.linears]),
+                   B.poet_fold_group_workspace_bytes([pl.L for pl in act]) if act else 0)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def build(self, stream=None):
@@ -206,6 +228,15 @@ class PoetGroup:
         B.poet_build_orthogonal_group(self.sides, thetas, prims, powers, self.ws, stream, ops=ops)
         for pl in self.linears:
             pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
+            pl.W0P = pl.RW0 = None
+        act = [pl for pl in self.linears if pl.act_path and any(f is not None for f in self._fold[id(pl)])]
+        if act:
+            B.poet_fold_weights_group([pl.L for pl in act], [pl.W0b for pl in act], [pl.primR for pl in act],
+                                      [pl.primP for pl in act], [self._fold[id(pl)][0] for pl in act],
+                                      [self._fold[id(pl)][1] for pl in act], self.ws, stream,
+                                      opsRs=[pl.opsR for pl in act], opsPs=[pl.opsP for pl in act])
+            for pl in act:
+                pl.W0P, pl.RW0 = self._fold[id(pl)]
 
     def finish_backward(self, stream=None):
         for pl in self.linears:

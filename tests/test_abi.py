@@ -250,3 +250,36 @@ def test_merge_group_rejects_bad_arguments():
     assert call(layers=fs, wsb=1 << 40) == B.POET_E_ARG  # FS sides need their index sets
     bad = (B.poet_layer * 2)(L, _layer(m=0))
     assert call(layers=bad) == B.POET_E_SHAPE
+
+
+def test_folded_calls_reject_bad_arguments():
+    lb = B.lib()
+    L = _layer(act_dtype=1)  # BS sides, bf16 activations
+    wf = B.poet_workspace_bytes(L, B.POET_OP_FWD_ACT)
+    wb = B.poet_workspace_bytes(L, B.POET_OP_BWD_ACT)
+    assert lb.poet_linear_fwd_folded(ctypes.byref(L), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, wf, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_folded(ctypes.byref(L), FAKE, None, None, FAKE, FAKE, FAKE, FAKE, wf, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_folded(ctypes.byref(L), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, wf - 1024,
+                                     None) == B.POET_E_WORKSPACE
+    assert lb.poet_linear_bwd_folded_prims(ctypes.byref(L), None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                           wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_folded_prims(ctypes.byref(L), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                           wb, None) == B.POET_E_ARG
+    F32 = _layer(act_dtype=0)  # float32 activations: no activation-side path
+    assert lb.poet_linear_fwd_folded(ctypes.byref(F32), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                     None) == B.POET_E_UNSUPPORTED
+    arr = (B.poet_layer * 2)(L, L)
+    tab = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    nul = (ctypes.c_void_p * 2)(FAKE, None)
+    need = B.poet_fold_group_workspace_bytes([L, L])
+    assert need > B.poet_fold_group_workspace_bytes([L]) > 0
+    assert lb.poet_fold_weights_group(-1, arr, tab, tab, tab, None, None, tab, tab, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_fold_weights_group(0, None, None, None, None, None, None, None, None, None, 0, None) == B.POET_OK
+    assert lb.poet_fold_weights_group(2, arr, nul, tab, tab, None, None, tab, tab, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_fold_weights_group(2, arr, tab, tab, nul, None, None, tab, None, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_fold_weights_group(2, arr, tab, nul, tab, None, None, None, tab, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_fold_weights_group(2, arr, tab, tab, tab, None, None, tab, tab, FAKE, need - 1,
+                                      None) == B.POET_E_WORKSPACE
+    arr32 = (B.poet_layer * 2)(L, F32)
+    assert lb.poet_fold_weights_group(2, arr32, tab, tab, tab, None, None, tab, tab, FAKE, 1 << 40,
+                                      None) == B.POET_E_UNSUPPORTED

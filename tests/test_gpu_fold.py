@@ -1,0 +1,107 @@
+"""The activation-side path with the factors folded into the weight: W0P = W0 P for the forward's token GEMM and
+RW0 = R W0 for the backward's (poet_fold_weights_group, poet_linear_fwd_folded, poet_linear_bwd_folded_prims).
+
+A block of linears whose token count is at least their rows and columns, blocks of 128 and more (ragged last
+blocks, blocks not a power of two, padded rows), plus one linear with fewer tokens than rows (not folded), run
+through PoetGroup (grouped build, grouped fold, folded forward and backward, grouped adjoint). Checked against:
+  - the one-linear calls (poet_linear_fwd_act / poet_linear_bwd_act_prims, which fold inside the call when the
+    shape asks for it): bit for bit (the same products on the same kernel);
+  - float64 products of the bf16 copies for W0P and RW0 (one bf16 rounding);
+  - the oracle for Y, dX and dtheta (bf16 bar).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import poet_inputs as PI
+from tests.gpu_util import TOL, announce, make_linear, put_act, rel, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+# name, m, n, bR, bP, T, k, row padding
+SPECS = [
+    ("q", 512, 512, 256, 256, 1024, 5, 0),
+    ("k", 512, 512, 256, 256, 1024, 5, 0),
+    ("gate", 600, 384, 256, 128, 1024, 5, 8),   # ragged last R block (88), padded rows
+    ("down", 384, 600, 128, 256, 1024, 5, 8),   # ragged last P block
+    ("odd", 300, 272, 136, 136, 1024, 4, 4),    # blocks not a power of two
+    ("wide", 1100, 512, 256, 256, 1024, 5, 0),  # T < m: P is applied to the tokens, R still folded
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _linear(spec, i):
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetLinear
+    name, m, n, bR, bP, T, k, pad = spec
+    lin = make_linear(name, m, n, T, PI.MODE_BS, bR, bP, k, PI.DT_BF16, linear_id=i)
+    W0, tR, tP, X, dY = PI.gen_linear(31, 0, lin, theta_std=0.01)
+    mk = lambda: PoetLinear(m, n, T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP, linear_id=i,
+                            ldw=n + pad, ldx=n + pad, ldy=m + pad, path="act")
+    return lin, (W0, tR, tP, X, dY), mk(), mk()
+
+
+def test_folded_group_matches_one_linear_calls_and_oracle():
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    cases = [_linear(spec, i) for i, spec in enumerate(SPECS)]
+    group = PoetGroup([g for _, _, _, g in cases])
+    announce("fold: one-linear calls")
+    one_out, acts = [], []
+    for lin, (W0, tR, tP, X, dY), one, _ in cases:
+        Xd, dYd = put_act(one, X, one.L.ldx), put_act(one, dY, one.L.ldy)
+        acts.append((Xd, dYd))
+        Y, Z, dX = (one.alloc_act(lin.T, one.L.ldy), one.alloc_act(lin.T, one.L.ldy), one.alloc_act(lin.T, one.L.ldx))
+        one.build()
+        one.forward_act(Xd, Y, Z)
+        one.backward_act_prims(Xd, Z, dYd, dX)
+        one_out.append((Y, Z, dX))
+    torch.cuda.synchronize()
+    announce("fold: grouped build, fold, folded forward and backward")
+    group.build()
+    grp_out = []
+    for (lin, _, _, pl), (Xd, dYd) in zip(cases, acts):
+        Y, Z, dX = (pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx))
+        pl.forward_act(Xd, Y, Z)
+        pl.backward_act_prims(Xd, Z, dYd, dX)
+        grp_out.append((Y, Z, dX))
+    group.finish_backward()
+    torch.cuda.synchronize()
+    for (lin, (W0, tR, tP, X, dY), one, pl), o1, o2 in zip(cases, one_out, grp_out):
+        foldP, foldR = lin.T >= lin.m, lin.T >= lin.n
+        assert (pl.W0P is not None) == foldP and (pl.RW0 is not None) == foldR, lin.name
+        for a, b, nm, w in zip(o1, o2, ("Y", "Z", "dX"), (lin.m, lin.m, lin.n)):  # (row padding is never written)
+            assert torch.equal(a[:, :w], b[:, :w]), (lin.name, nm)
+        assert torch.equal(one.dprimR, pl.dprimR) and torch.equal(one.dprimP, pl.dprimP), lin.name
+        # the folded weights: one bf16 rounding of the products of the bf16 copies
+        W0b = to_np(pl.W0b)[:, :lin.n].astype(np.float64)
+        if foldP:
+            Pb = np.zeros((lin.n, lin.n))
+            for p, c in enumerate(O.block_sizes(PI.MODE_BS, lin.n, lin.P.b)):
+                blk = PI.round_bf16(to_np(pl.primP).reshape(-1, lin.P.b, lin.P.b)[p, :c, :c]).astype(np.float64)
+                Pb[p * lin.P.b:p * lin.P.b + c, p * lin.P.b:p * lin.P.b + c] = blk
+            e = rel(to_np(pl.W0P)[:, :lin.n], W0b @ Pb)
+            assert e <= 2 ** -8, (lin.name, "W0P", e)
+        if foldR:
+            Rb = np.zeros((lin.m, lin.m))
+            for p, c in enumerate(O.block_sizes(PI.MODE_BS, lin.m, lin.R.b)):
+                blk = PI.round_bf16(to_np(pl.primR).reshape(-1, lin.R.b, lin.R.b)[p, :c, :c]).astype(np.float64)
+                Rb[p * lin.R.b:p * lin.R.b + c, p * lin.R.b:p * lin.R.b + c] = blk
+            e = rel(to_np(pl.RW0)[:, :lin.n], Rb @ W0b)
+            assert e <= 2 ** -8, (lin.name, "RW0", e)
+        # the layer against the oracle
+        sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+        f = O.linear_fwd(sR, sP, W0, tR, tP, None, None, X)
+        g = O.linear_bwd(sR, sP, W0, tR, tP, None, None, X, dY)
+        errs = {"Y": rel(to_np(o2[0])[:, :lin.m], f["Y"]), "dX": rel(to_np(o2[2])[:, :lin.n], g["dX"]),
+                "dthetaR": rel(to_np(pl.dthetaR)[:len(tR)], g["dthetaR"]),
+                "dthetaP": rel(to_np(pl.dthetaP)[:len(tP)], g["dthetaP"])}
+        announce(f"fold {lin.name} (P folded {foldP}, R folded {foldR}): {errs}")
+        for k, v in errs.items():
+            assert v <= TOL[PI.DT_BF16], (lin.name, k, v)

@@ -109,7 +109,7 @@ def test_build_group_equals_one_side_builds():
     thetas_d = [torch.from_numpy(t).cuda() for t in _thetas(0.02)]
     single = _build_all(sides, thetas_d, grouped=False)
     # operand copies for the BS sides (written by the chain kernel, or by the conversion for the other sides)
-    ops = [torch.full((2 * B_prim_len(s),), float("nan"), dtype=torch.bfloat16, device="cuda") if spec[0] == PI.MODE_BS
+    ops = [torch.full((3 * B_prim_len(s),), float("nan"), dtype=torch.bfloat16, device="cuda") if spec[0] == PI.MODE_BS
            else None for spec, s in zip(SIDES, sides)]
     group = _build_all(sides, thetas_d, grouped=True, ops=ops)
     for i, ((pa, wa), (pb, wb)) in enumerate(zip(single, group)):
@@ -130,10 +130,12 @@ def test_build_group_equals_one_side_builds():
         want = np.zeros_like(F)
         for p, c in enumerate(O.block_sizes(mode, d, b)):
             want[p, :c, :c] = PI.round_bf16(F[p, :c, :c])
-        got = to_np(ops[i]).reshape(2, -1, b * b)
+        got = to_np(ops[i]).reshape(3, -1, b * b)
         np.testing.assert_array_equal(got[0], _operand_order(want), err_msg=f"ops of side {i} {SIDES[i]}")
         np.testing.assert_array_equal(got[1], _operand_order(want.transpose(0, 2, 1)),
                                       err_msg=f"transposed ops of side {i}")
+        # the third part: the primitive as it is (padding included), row-major
+        np.testing.assert_array_equal(got[2], PI.round_bf16(F).reshape(-1, b * b), err_msg=f"row ops of side {i}")
 
 
 def _oracle_dtheta(side_spec, theta, dprim):
