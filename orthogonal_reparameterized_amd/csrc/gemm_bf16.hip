@@ -412,29 +412,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // Sum the split-K partials of every output element in split order, then apply the epilogue.
+// Work item: four adjacent columns of one partial row (one column where N is not a multiple of 4), read from every
+// split as one 16-byte load; 32-bit indices (the partials of one launch are far below 2^31 elements).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) {
   const GemmDesc& g = fa_.g;
-  const int64_t mn = (int64_t)g.M * g.N, total = (int64_t)g.batch * mn;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int zg = (int)(e / mn);
-    const int64_t rc = e - (int64_t)zg * mn;
-    const int row = (int)(rc / g.N), col = (int)(rc - (int64_t)row * g.N);
+  const int64_t mn = (int64_t)g.M * g.N;
+  const bool v4 = (g.N & 3) == 0;
+  const int nq = v4 ? g.N >> 2 : g.N, rows = g.batch * g.M, items = rows * nq;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < items; e += gridDim.x * blockDim.x) {
+    const int r = e / nq, q = e - r * nq;
+    const int zg = r / g.M, row = r - zg * g.M, col = v4 ? 4 * q : q;
     int p = 0;  // problem of a grouped launch (plain epilogue)
-    for (int q = 1; q < fa_.nprob; ++q)
-      if (zg >= fa_.prob[q].b0) p = q;
+    for (int u = 1; u < fa_.nprob; ++u)
+      if (zg >= fa_.prob[u].b0) p = u;
     const int z = fa_.nprob > 0 ? zg - fa_.prob[p].b0 : zg;
     int M = g.M, N = g.N;
     const int Mtot = fa_.nprob > 0 ? fa_.prob[p].Mtot : g.Mtot, Ntot = fa_.nprob > 0 ? fa_.prob[p].Ntot : g.Ntot;
     if (Mtot > 0) M = min(M, Mtot - z * g.M);
     if (Ntot > 0) N = min(N, Ntot - z * g.N);
     if (row >= M || col >= N) continue;
-    float sum = 0.f;
-    for (int s = 0; s < fa_.splits; ++s) sum += g.part[(int64_t)(s * g.batch + zg) * mn + rc];
-    if (fa_.nprob > 0) {
-      char* cb = reinterpret_cast<char*>(g.C) + fa_.prob[p].offC;
-      store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col, sum);
+    const int64_t rc = (int64_t)row * g.N + col;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (v4) {
+      for (int sp = 0; sp < fa_.splits; ++sp)
+        sum += *reinterpret_cast<const f32x4*>(g.part + (int64_t)(sp * g.batch + zg) * mn + rc);
     } else {
-      epilogue_one(g, z, row, col, sum);
+      for (int sp = 0; sp < fa_.splits; ++sp) sum[0] += g.part[(int64_t)(sp * g.batch + zg) * mn + rc];
+    }
+    const int nc = v4 ? min(4, N - col) : 1;
+    for (int t = 0; t < nc; ++t) {
+      if (fa_.nprob > 0) {
+        char* cb = reinterpret_cast<char*>(g.C) + fa_.prob[p].offC;
+        store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col + t, sum[t]);
+      } else {
+        epilogue_one(g, z, row, col + t, sum[t]);
+      }
     }
   }
 }
@@ -494,7 +506,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fa.use_part || g.defer_reduce) return e;
-  const int64_t total = (int64_t)g.batch * g.M * g.N;
+  const int64_t total = (int64_t)g.batch * g.M * (g.N % 4 == 0 ? g.N / 4 : g.N);
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
   return hipGetLastError();
@@ -555,7 +567,7 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   else hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 0, true>), grid, block, 0, st, fa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !fa.use_part) return e;
-  const int64_t total = (int64_t)g.batch * g.M * g.N;
+  const int64_t total = (int64_t)g.batch * g.M * (g.N % 4 == 0 ? g.N / 4 : g.N);
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
   return hipGetLastError();
