@@ -248,11 +248,16 @@ hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf
 // and columns past bp zero): block j = sum_{t} a_{t+j+1} (-1)^{t+j} Q^t over t = 0..k-j (t >= 1 for j = 0),
 // Q^0 = I, Q^t = powers[t-1] (bp x ldp blocks), with a_i = 2 for i <= k and a_{k+1} = 1. Dtype dt (the powers').
 hipError_t launch_adjoint_coefs(const void* powers, int dt, int nprim, int bp, int ldp, int k, void* out, hipStream_t st);
-// gathers into a typed destination (dst_dt)
+// gathers into a typed destination (dst_dt) and, when dst2 is given, also into a bf16 copy (same read)
 hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
-                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
+                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2 = nullptr,
+                                 int64_t ld_dst2 = 0);
 hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
-                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
+                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2 = nullptr,
+                                 int64_t ld_dst2 = 0);
+// dst[r][idx[j]] = src[r][j] into a typed destination (dst_dt)
+hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                                  void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch);
 
 }  // namespace poet

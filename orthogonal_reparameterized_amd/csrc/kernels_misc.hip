@@ -226,12 +226,14 @@ __global__ void k_convert(const float* __restrict__ src, int64_t ld_src, void* _
 __device__ __forceinline__ int clampi(int v, int lim) { return v < 0 ? 0 : (v >= lim ? lim - 1 : v); }
 
 __global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
-                              int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
+                              int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst,
+                              __bf16* __restrict__ dst2, int64_t ld_dst2) {
   for (int r = blockIdx.y; r < rows; r += gridDim.y)
     for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x) {
       const float v = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
       if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + j] = (__bf16)v;
       else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + j] = v;
+      if (dst2) dst2[(int64_t)r * ld_dst2 + j] = (__bf16)v;
     }
 }
 
@@ -256,14 +258,19 @@ __global__ void k_split3(const float* __restrict__ src, int64_t ld_src, const in
 }
 
 __global__ void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
-                               int s, int dlim, float* __restrict__ dst, int64_t ld_dst) {
+                               int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
   for (int r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x)
-      dst[(int64_t)r * ld_dst + clampi(idx[j], dlim)] = src[(int64_t)r * ld_src + j];
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x) {
+      const float v = src[(int64_t)r * ld_src + j];
+      const int64_t o = (int64_t)r * ld_dst + clampi(idx[j], dlim);
+      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[o] = (__bf16)v;
+      else reinterpret_cast<float*>(dst)[o] = v;
+    }
 }
 
 __global__ void k_gather_rows(const void* __restrict__ src, int src_dt, int64_t ld_src, const int32_t* __restrict__ idx,
-                              int s, int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
+                              int s, int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst,
+                              __bf16* __restrict__ dst2, int64_t ld_dst2) {
   for (int i = blockIdx.y; i < s; i += gridDim.y) {
     const int64_t row = (int64_t)clampi(idx[i], dlim) * ld_src;
     for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
@@ -271,6 +278,7 @@ __global__ void k_gather_rows(const void* __restrict__ src, int src_dt, int64_t 
                                      : reinterpret_cast<const float*>(src)[row + c];
       if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)i * ld_dst + c] = (__bf16)v;
       else reinterpret_cast<float*>(dst)[(int64_t)i * ld_dst + c] = v;
+      if (dst2) dst2[(int64_t)i * ld_dst2 + c] = (__bf16)v;
     }
   }
 }
@@ -296,25 +304,36 @@ __host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   return x ^ (x >> 31);
 }
 
-// flags[i] = 1 when fewer than s indices j have (key_j, j) < (key_i, i)
-__global__ void k_sample_rank(int d, int s, uint64_t h, int32_t* __restrict__ flags) {
-  __shared__ uint64_t kj[kThreads];
-  const int i = blockIdx.x * kThreads + threadIdx.x;
+// flags[i] = 1 when fewer than s indices j have (key_j, j) < (key_i, i). A workgroup of kRankWaves waves ranks 64
+// indices (lane = i): each chunk of kRankChunk keys is hashed into LDS once, wave w compares against its 64-key slice
+// of the chunk, and the waves' integer counts are summed at the end (the order of an integer sum does not matter).
+constexpr int kRankWaves = 16, kRankChunk = kRankWaves * 64;
+__global__ void __launch_bounds__(kRankChunk) k_sample_rank(int d, int s, uint64_t h, int32_t* __restrict__ flags) {
+  __shared__ uint64_t kj[kRankChunk];
+  __shared__ int part[kRankWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   const uint64_t ki = splitmix64(h ^ (uint64_t)(i < d ? i : 0));
   int rank = 0;
-  for (int j0 = 0; j0 < d; j0 += kThreads) {
+  for (int j0 = 0; j0 < d; j0 += kRankChunk) {
     const int j = j0 + threadIdx.x;
     kj[threadIdx.x] = j < d ? splitmix64(h ^ (uint64_t)j) : 0ull;
     __syncthreads();
-    const int jn = min(kThreads, d - j0);
-    for (int t = 0; t < jn; ++t) {
+    const int t0 = w * 64, t1 = min(t0 + 64, d - j0);
+    for (int t = t0; t < t1; ++t) {
       const uint64_t kv = kj[t];
       const int jj = j0 + t;
       rank += (kv < ki) || (kv == ki && jj < i);
     }
     __syncthreads();
   }
-  if (i < d) flags[i] = rank < s ? 1 : 0;
+  part[w][lane] = rank;
+  __syncthreads();
+  if (w == 0) {
+    int r = 0;
+    for (int q = 0; q < kRankWaves; ++q) r += part[q][lane];
+    if (i < d) flags[i] = r < s ? 1 : 0;
+  }
 }
 
 // one workgroup: stream compaction of the flagged indices in ascending order
@@ -663,11 +682,11 @@ hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t l
 }
 
 hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
-                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
+                                 void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2, int64_t ld_dst2) {
   if (rows <= 0 || s <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
+  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt) + (dst2 ? 2 : 0)));
   hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
-                     dst_dt, ld_dst);
+                     dst_dt, ld_dst, dst2, ld_dst2);
   return hipGetLastError();
 }
 
@@ -686,20 +705,27 @@ hipError_t launch_split3(const float* src, int64_t ld_src, const int32_t* ridx, 
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
-                               float* dst, int64_t ld_dst, hipStream_t st) {
+hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                                  void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
   if (rows <= 0 || s <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)rows * s * 8);
-  hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst, ld_dst);
+  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
+  hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
+                     dst_dt, ld_dst);
   return hipGetLastError();
 }
 
+hipError_t launch_scatter_cols(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
+                               float* dst, int64_t ld_dst, hipStream_t st) {
+  return launch_scatter_cols_to(src, ld_src, rows, idx, s, dlim, dst, F32, ld_dst, st);
+}
+
 hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
-                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
+                                 int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2,
+                                 int64_t ld_dst2) {
   if (s <= 0 || cols <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt)));
+  ProfScope prof(7, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt) + (dst2 ? 2 : 0)));
   hipLaunchKernelGGL(k_gather_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, src_dt, ld_src, idx, s, dlim, cols,
-                     dst, dst_dt, ld_dst);
+                     dst, dst_dt, ld_dst, dst2, ld_dst2);
   return hipGetLastError();
 }
 
@@ -727,7 +753,7 @@ uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st) {
   if (d <= 0 || s <= 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)d * 4 + (double)s * 4);
-  hipLaunchKernelGGL(k_sample_rank, dim3((d + kThreads - 1) / kThreads), dim3(kThreads), 0, st, d, s, h, flags);
+  hipLaunchKernelGGL(k_sample_rank, dim3((d + 63) / 64), dim3(kRankChunk), 0, st, d, s, h, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sample_compact, dim3(1), dim3(1024), 0, st, d, flags, idx);

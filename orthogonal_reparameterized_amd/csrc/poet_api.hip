@@ -156,13 +156,13 @@ hipError_t apply_P(const poet_layer& L, const SideInfo& P, const float* W0, cons
     return launch_gemm(g, st);
   }
   const int s = P.bp;
-  hipError_t e = launch_gather_cols(W0, L.ldw, m, idx, s, n, f.Ac, s, st);
+  const bool fast = f.Acb && compute == BF16;  // W0[:, I] in float32 (addend) and, for the fast kernel, in bf16
+  hipError_t e = launch_gather_cols_to(W0, L.ldw, m, idx, s, n, f.Ac, F32, s, st, fast ? f.Acb : nullptr, P.ldp);
   if (e != hipSuccess) return e;
   g.M = m; g.N = s; g.K = s;
   g.D = f.Ac; g.ldd = s; g.beta = 1.f;
   g.C = f.C1; g.ldc = s; g.c_dt = F32;
-  if (f.Acb && compute == BF16) {  // C1 = W0[:, I] + bf16(W0[:, I]) bf16(G_P - I) on the fast kernel
-    if ((e = launch_gather_cols_to(W0, L.ldw, m, idx, s, n, f.Acb, BF16, P.ldp, st)) != hipSuccess) return e;
+  if (fast) {  // C1 = W0[:, I] + bf16(W0[:, I]) bf16(G_P - I) on the fast kernel
     if ((e = launch_delta_bf16(prim, 1, s, P.ldp, f.dPb, st)) != hipSuccess) return e;
     g.A = f.Acb; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 1;
     g.B = f.dPb; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
@@ -191,13 +191,13 @@ hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, con
     return launch_gemm(g, st);
   }
   const int s = R.bp;
-  hipError_t e = launch_gather_rows(src, F32, L.ldw, idx, s, m, n, f.Br, n, st);
+  const bool fast = f.Brb && compute == BF16;  // src[I, :] in float32 (addend) and, for the fast kernel, in bf16
+  hipError_t e = launch_gather_rows_to(src, F32, L.ldw, idx, s, m, n, f.Br, F32, n, st, fast ? f.Brb : nullptr, pad8(n));
   if (e != hipSuccess) return e;
   g.M = s; g.N = n; g.K = s;
   g.D = f.Br; g.ldd = n; g.beta = 1.f;
   g.C = f.C2; g.ldc = n; g.c_dt = F32;
-  if (f.Brb && compute == BF16) {  // C2 = src[I, :] + bf16(G_R - I) bf16(src[I, :]) on the fast kernel
-    if ((e = launch_gather_rows_to(src, F32, L.ldw, idx, s, m, n, f.Brb, BF16, pad8(n), st)) != hipSuccess) return e;
+  if (fast) {  // C2 = src[I, :] + bf16(G_R - I) bf16(src[I, :]) on the fast kernel
     if ((e = launch_delta_bf16(prim, 1, s, R.ldp, f.dRb, st)) != hipSuccess) return e;
     g.A = f.dRb; g.lda = R.ldp; g.a_dt = BF16; g.a_kmajor = 1;
     g.B = f.Brb; g.ldb = pad8(n); g.b_dt = BF16; g.b_kmajor = 0;
@@ -209,6 +209,45 @@ hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, con
   if ((e = launch_gemm(g, st)) != hipSuccess) return e;
   if ((e = launch_convert(src, L.ldw, out, ldo, out_dt, m, n, st)) != hipSuccess) return e;
   return launch_scatter_rows(f.C2, n, idx, s, m, n, out, out_dt, ldo, st);
+}
+
+// Both sides POET-FS with bf16 operands: the gradient's two operands, Z[I_R, :] (Z = W0 P) and (R W0)[:, I_P],
+// formed from W0 directly instead of from the whole of W0 P and R W0. Off the sampled rows (columns) both are W0; on
+// the sampled block W0[I_R, I_P] they are W0[I_R, I_P] G_P and G_R W0[I_R, I_P], each as the float32 block plus one
+// bf16 product of its delta (the same form as apply_P / apply_R):
+//   Zr  (sR x ldn,  bf16) = W0[I_R, :] with columns I_P replaced by W0[I_R, I_P] + bf16(W0[I_R, I_P]) bf16(G_P - I)
+//   Acp (m x ldpP, bf16)  = W0[:, I_P] with rows I_R replaced by W0[I_R, I_P] + bf16(G_R - I) bf16(W0[I_R, I_P])
+hipError_t fs_grad_operands(const poet_layer& L, const SideInfo& R, const SideInfo& P, const float* W0,
+                            const float* primR, const float* primP, const int32_t* idxR, const int32_t* idxP,
+                            __bf16* Zr, __bf16* Acp, const FsBufs& f, hipStream_t st) {
+  const int m = L.m, n = L.n, sR = R.bp, sP = P.bp, ldn = pad8(n);
+  hipError_t e;
+  // W0[I_R, :] in float32 (Br) and bf16 (Zr); the block W0[I_R, I_P] in float32 (Ac, pitch sP) and bf16 (Acb)
+  if ((e = launch_gather_rows_to(W0, F32, L.ldw, idxR, sR, m, n, f.Br, F32, n, st, Zr, ldn)) != hipSuccess) return e;
+  if ((e = launch_gather_cols_to(f.Br, n, sR, idxP, sP, n, f.Ac, F32, sP, st, f.Acb, P.ldp)) != hipSuccess) return e;
+  if ((e = launch_gather_cols_to(W0, L.ldw, m, idxP, sP, n, Acp, BF16, P.ldp, st)) != hipSuccess) return e;
+  if ((e = launch_delta_bf16(primP, 1, sP, P.ldp, f.dPb, st)) != hipSuccess) return e;
+  if ((e = launch_delta_bf16(primR, 1, sR, R.ldp, f.dRb, st)) != hipSuccess) return e;
+  GemmDesc g;
+  g.compute = BF16;
+  g.kclass = POET_K_APPLY;
+  g.part = f.part; g.part_elems = f.part_elems;
+  g.D = f.Ac; g.ldd = sP; g.beta = 1.f;
+  g.c_dt = F32; g.ldc = sP;
+  // C1 = W0[I_R, I_P] G_P
+  g.M = sR; g.N = sP; g.K = sP;
+  g.A = f.Acb; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = f.dPb; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.C = f.C1;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  if ((e = launch_scatter_cols_to(f.C1, sP, sR, idxP, sP, n, Zr, BF16, ldn, st)) != hipSuccess) return e;
+  // C2 = G_R W0[I_R, I_P]
+  g.M = sR; g.N = sP; g.K = sR;
+  g.A = f.dRb; g.lda = R.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = f.Acb; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.C = f.C2;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  return launch_scatter_rows(f.C2, sP, idxR, sR, m, sP, Acp, BF16, P.ldp, st);
 }
 
 // ------------------------------------------------------------------------------------------------------------
@@ -1098,6 +1137,8 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
   const int64_t ldw = L->ldw;
   const bool fast = bs_bf16(*L, R, P);
   const void* W = Win;
+  // both sides FS in bf16 with W given: the gradient's operands come from W0 and the sampled blocks alone
+  const bool fs_pair = W && fs_bf16(*L, R) && fs_bf16(*L, P) && p.fs.Acb && p.fs.Brb;
   if (fast && bs_apply_eligible(R.bp, P.bp, W0, ldw, primR, primP)) {
     // bf16 operands of the gradient: Z = W0 P (R side), R W0 (P side), and W when it is not given
     void* Wout = W ? nullptr : p.W;
@@ -1114,6 +1155,10 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
       W = p.W;
     }
     HIP_TRY(apply_R_b(*L, R, p.W0b, W0, p.dRb, p.RW0b, BF16, Part{p.adj.part, p.adj.part_elems}, st));
+  } else if (fs_pair) {
+    // Z[I_R, :] and (R W0)[:, I_P], the only parts of Z = W0 P and R W0 the gradient reads
+    HIP_TRY(fs_grad_operands(*L, R, P, W0, primR, primP, idxR, idxP, reinterpret_cast<__bf16*>(p.Zr),
+                             reinterpret_cast<__bf16*>(p.Acp), p.fs, st));
   } else {
     // Z = W0 P (needed by the R-side gradient) and, when not given, W = R Z
     HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
@@ -1168,7 +1213,7 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
       if (fs_bf16(*L, R)) {  // gathered rows as bf16 operands (row pitch padded to 8) on the fast kernel
         const int ldn = pad8(n);
         HIP_TRY(launch_gather_rows_to(p.G, F32, ldw, idxR, R.bp, m, n, p.Gr, BF16, ldn, st));
-        HIP_TRY(launch_gather_rows_to(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, BF16, ldn, st));
+        if (!fs_pair) HIP_TRY(launch_gather_rows_to(p.T, F32, ldw, idxR, R.bp, m, n, p.Zr, BF16, ldn, st));
         g.A = p.Gr; g.lda = ldn; g.a_dt = BF16; g.a_kmajor = 1;
         g.B = p.Zr; g.ldb = ldn; g.b_dt = BF16; g.b_kmajor = 1;
       } else {
@@ -1201,7 +1246,7 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
       g.M = g.N = P.bp; g.K = m;
       g.C = dPg; g.ldc = P.bp; g.c_dt = F32;
       if (fs_bf16(*L, P)) {  // gathered columns as bf16 operands (row pitch ldp) on the fast kernel
-        HIP_TRY(launch_gather_cols_to(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, BF16, P.ldp, st));
+        if (!fs_pair) HIP_TRY(launch_gather_cols_to(p.RW0, ldw, m, idxP, P.bp, n, p.Acp, BF16, P.ldp, st));
         HIP_TRY(launch_gather_cols_to(p.G, ldw, m, idxP, P.bp, n, p.Gc, BF16, P.ldp, st));
         g.A = p.Acp; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 0;
         g.B = p.Gc; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
