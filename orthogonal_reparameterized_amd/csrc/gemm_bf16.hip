@@ -27,6 +27,7 @@
 // split-K each split writes its float32 partial tile; a second kernel sums the partials in split order (so
 // results do not depend on timing) and applies the epilogue.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "internal.h"
@@ -465,15 +466,24 @@ bool fast_gemm_eligible(const GemmDesc& g) {
 }
 
 int fast_gemm_splits(const GemmDesc& g) {
-  // split K until one round of the machine (256 CUs, one workgroup each) is covered, keeping >= 2 K-tiles per
-  // split and the partials within the scratch the caller provided
+  // Split K only where it shortens the launch. A work item (one output tile, nk / S K-tiles) holds one CU (256 CUs,
+  // one workgroup each), so the items take ceil(tiles S / 256) rounds of about nk / S + 1.5 K-tile times (the 1.5
+  // is the pipeline fill and the epilogue). S > 1 adds float32 partials, written by the items and read back by the
+  // reduction: about 8 S + 4 bytes per output element, counted at one K-tile time per 10 MB. Candidates keep at
+  // least two K-tiles per split and fit the scratch the caller provided; a larger S must win by 3% or more.
   const int tiles = g.batch * ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int nk = (g.K + BK - 1) / BK;
-  int S = 1;
-  while (tiles * S < 200 && nk >= 4 * S && S < 16 &&
-         (size_t)(2 * S) * g.batch * (size_t)g.M * g.N <= g.part_elems && g.part)
-    S *= 2;
-  return S;
+  const double outs = (double)g.batch * g.M * g.N;
+  int best_s = 1;
+  double best = 0.0;
+  for (int S = 1; S <= 16; S *= 2) {
+    if (S > 1 && (!g.part || nk < 2 * S || (size_t)S * (size_t)outs > g.part_elems)) break;
+    const double rounds = std::ceil((double)tiles * S / 256.0);
+    double cost = rounds * ((double)nk / S + 1.5);
+    if (S > 1) cost += (8.0 * S + 4.0) * outs / 10.0e6;
+    if (S == 1 || cost < 0.97 * best) { best = cost; best_s = S; }
+  }
+  return best_s;
 }
 
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
