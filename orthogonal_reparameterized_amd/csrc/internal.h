@@ -255,6 +255,9 @@ hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, con
 hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, const int32_t* idx, int s, int dlim,
                                  int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2 = nullptr,
                                  int64_t ld_dst2 = 0);
+// dst[i][cidx[j]] = C[ridx[i]][j] for i < sr, j < sc, and its bf16 copy dst2[i][cidx[j]]
+hipError_t launch_patch_block(const float* C, int64_t ldc, const int32_t* ridx, int rlim, const int32_t* cidx, int clim,
+                              int sr, int sc, float* dst, int64_t ld_dst, __bf16* dst2, int64_t ld_dst2, hipStream_t st);
 // dst[r][idx[j]] = src[r][j] into a typed destination (dst_dt)
 hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
                                   void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);

@@ -283,6 +283,21 @@ __global__ void k_gather_rows(const void* __restrict__ src, int src_dt, int64_t 
   }
 }
 
+// dst[i][cidx[j]] = C[ridx[i]][j] (i < sr, j < sc), with a bf16 copy into dst2[i][cidx[j]]
+__global__ void k_patch_block(const float* __restrict__ C, int64_t ldc, const int32_t* __restrict__ ridx, int rlim,
+                              const int32_t* __restrict__ cidx, int clim, int sr, int sc, float* __restrict__ dst,
+                              int64_t ld_dst, __bf16* __restrict__ dst2, int64_t ld_dst2) {
+  for (int i = blockIdx.y; i < sr; i += gridDim.y) {
+    const int64_t row = (int64_t)clampi(ridx[i], rlim) * ldc;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < sc; j += gridDim.x * blockDim.x) {
+      const float v = C[row + j];
+      const int c = clampi(cidx[j], clim);
+      dst[(int64_t)i * ld_dst + c] = v;
+      dst2[(int64_t)i * ld_dst2 + c] = (__bf16)v;
+    }
+  }
+}
+
 __global__ void k_scatter_rows(const float* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ idx, int s,
                                int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
   for (int i = blockIdx.y; i < s; i += gridDim.y) {
@@ -711,6 +726,15 @@ hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, co
   ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
   hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
                      dst_dt, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_patch_block(const float* C, int64_t ldc, const int32_t* ridx, int rlim, const int32_t* cidx, int clim,
+                              int sr, int sc, float* dst, int64_t ld_dst, __bf16* dst2, int64_t ld_dst2, hipStream_t st) {
+  if (sr <= 0 || sc <= 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)sr * sc * 10);
+  hipLaunchKernelGGL(k_patch_block, row_grid(sc, sr), dim3(kThreads), 0, st, C, ldc, ridx, rlim, cidx, clim, sr, sc, dst,
+                     ld_dst, dst2, ld_dst2);
   return hipGetLastError();
 }
 

@@ -211,6 +211,41 @@ hipError_t apply_R(const poet_layer& L, const SideInfo& R, const float* src, con
   return launch_scatter_rows(f.C2, n, idx, s, m, n, out, out_dt, ldo, st);
 }
 
+// Both sides POET-FS with bf16 operands and activations: W = R W0 P straight into bf16, with no float32 copy of
+// W0 P. Off the sampled rows I_R, W is W0 P, which differs from W0 only in the columns I_P (C1 = (W0 P)[:, I_P],
+// float32 block plus one bf16 product as in apply_P); the rows I_R are apply_R's product on the rows I_R of W0 P,
+// whose float32 (Br) and bf16 (Brb) copies are the rows of W0 patched with C1[I_R, :]. The same products and
+// roundings as apply_P followed by apply_R.
+hipError_t fs_weight_bf16(const poet_layer& L, const SideInfo& R, const SideInfo& P, const float* W0,
+                          const float* primR, const float* primP, const int32_t* idxR, const int32_t* idxP, void* W,
+                          const FsBufs& f, hipStream_t st) {
+  const int m = L.m, n = L.n, sR = R.bp, sP = P.bp, ldn = pad8(n);
+  hipError_t e;
+  if ((e = launch_gather_cols_to(W0, L.ldw, m, idxP, sP, n, f.Ac, F32, sP, st, f.Acb, P.ldp)) != hipSuccess) return e;
+  if ((e = launch_delta_bf16(primP, 1, sP, P.ldp, f.dPb, st)) != hipSuccess) return e;
+  GemmDesc g;
+  g.compute = BF16;
+  g.kclass = POET_K_APPLY;
+  g.part = f.part; g.part_elems = f.part_elems;
+  g.beta = 1.f; g.c_dt = F32;
+  g.M = m; g.N = sP; g.K = sP;  // C1 = W0[:, I_P] + bf16(W0[:, I_P]) bf16(G_P - I)
+  g.A = f.Acb; g.lda = P.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = f.dPb; g.ldb = P.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.D = f.Ac; g.ldd = sP; g.C = f.C1; g.ldc = sP;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  if ((e = launch_convert(W0, L.ldw, W, L.ldw, BF16, m, n, st)) != hipSuccess) return e;
+  if ((e = launch_scatter_cols_to(f.C1, sP, m, idxP, sP, n, W, BF16, L.ldw, st)) != hipSuccess) return e;
+  if ((e = launch_gather_rows_to(W0, F32, L.ldw, idxR, sR, m, n, f.Br, F32, n, st, f.Brb, ldn)) != hipSuccess) return e;
+  if ((e = launch_patch_block(f.C1, sP, idxR, m, idxP, n, sR, sP, f.Br, n, f.Brb, ldn, st)) != hipSuccess) return e;
+  if ((e = launch_delta_bf16(primR, 1, sR, R.ldp, f.dRb, st)) != hipSuccess) return e;
+  g.M = sR; g.N = n; g.K = sR;  // C2 = Br + bf16(G_R - I) Brb
+  g.A = f.dRb; g.lda = R.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = f.Brb; g.ldb = ldn; g.b_dt = BF16; g.b_kmajor = 0;
+  g.D = f.Br; g.ldd = n; g.C = f.C2; g.ldc = n;
+  if ((e = launch_gemm(g, st)) != hipSuccess) return e;
+  return launch_scatter_rows(f.C2, n, idxR, sR, m, n, W, BF16, L.ldw, st);
+}
+
 // Both sides POET-FS with bf16 operands: the gradient's two operands, Z[I_R, :] (Z = W0 P) and (R W0)[:, I_P],
 // formed from W0 directly instead of from the whole of W0 P and R W0. Off the sampled rows (columns) both are W0; on
 // the sampled block W0[I_R, I_P] they are W0[I_R, I_P] G_P and G_R W0[I_R, I_P], each as the float32 block plus one
@@ -1091,6 +1126,8 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
     HIP_TRY(launch_delta_bf16(primP, P.nprim, P.bp, P.bp, p.dPb, st));
     HIP_TRY(apply_P_b(*L, P, W0, p.W0b, p.dPb, p.Tb, p.T, p.part, st));
     HIP_TRY(apply_R_b(*L, R, p.Tb, p.T, p.dRb, W, act, p.part, st));
+  } else if (act == BF16 && fs_bf16(*L, R) && fs_bf16(*L, P) && p.fs.Acb && p.fs.Brb) {
+    HIP_TRY(fs_weight_bf16(*L, R, P, W0, primR, primP, idxR, idxP, W, p.fs, st));
   } else {
     HIP_TRY(apply_P(*L, P, W0, primP, idxP, p.T, act, p.fs, st));
     HIP_TRY(apply_R(*L, R, p.T, primR, idxR, W, act, L->ldw, act, p.fs, st));
