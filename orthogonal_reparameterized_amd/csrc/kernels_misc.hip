@@ -213,17 +213,40 @@ __global__ void k_fill_group(const FillGroup G, float v) {
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) p[e] = v;
 }
 
-__global__ void k_convert(const float* __restrict__ src, int64_t ld_src, void* __restrict__ dst, int64_t ld_dst,
-                          int dst_dt, int rows, int cols) {
-  for (int r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
-      const float v = src[(int64_t)r * ld_src + c];
-      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + c] = (__bf16)v;
-      else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + c] = v;
-    }
-}
-
 __device__ __forceinline__ int clampi(int v, int lim) { return v < 0 ? 0 : (v >= lim ? lim - 1 : v); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Row copies from float32, four consecutive elements per thread: dst[dr][c] = src[sr][c] (dst float32 or bf16) and,
+// when dst2 is given, dst2[dr][c] = bf16(src[sr][c]), for rows i < rows with sr = sidx[i] (gather) or i, dr =
+// didx[i] (scatter) or i. vec: every pitch a multiple of 4 elements and every base 16-byte aligned, so whole
+// groups of four move as one 16-byte load and one 16- or 8-byte store; the row's last partial group goes
+// element by element.
+__global__ __launch_bounds__(256) void k_rows4(const float* __restrict__ src, int64_t ld_src,
+                                               const int32_t* __restrict__ sidx, const int32_t* __restrict__ didx,
+                                               int dlim, int rows, int cols, void* __restrict__ dst, int dst_dt,
+                                               int64_t ld_dst, __bf16* __restrict__ dst2, int64_t ld_dst2, int vec) {
+  for (int i = blockIdx.y; i < rows; i += gridDim.y) {
+    const int64_t sr = sidx ? clampi(sidx[i], dlim) : i, dr = didx ? clampi(didx[i], dlim) : i;
+    const float* srow = src + sr * ld_src;
+    for (int c = 4 * (blockIdx.x * blockDim.x + threadIdx.x); c < cols; c += 4 * gridDim.x * blockDim.x) {
+      if (vec && c + 4 <= cols) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + c);
+        const bf16x4_t b = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+        if (dst_dt == BF16) *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(dst) + dr * ld_dst + c) = b;
+        else *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + dr * ld_dst + c) = v;
+        if (dst2) *reinterpret_cast<bf16x4_t*>(dst2 + dr * ld_dst2 + c) = b;
+      } else {
+        for (int u = 0; u < 4 && c + u < cols; ++u) {
+          const float v = srow[c + u];
+          if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[dr * ld_dst + c + u] = (__bf16)v;
+          else reinterpret_cast<float*>(dst)[dr * ld_dst + c + u] = v;
+          if (dst2) dst2[dr * ld_dst2 + c + u] = (__bf16)v;
+        }
+      }
+    }
+  }
+}
 
 __global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
                               int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst,
@@ -294,18 +317,6 @@ __global__ void k_patch_block(const float* __restrict__ C, int64_t ldc, const in
       const int c = clampi(cidx[j], clim);
       dst[(int64_t)i * ld_dst + c] = v;
       dst2[(int64_t)i * ld_dst2 + c] = (__bf16)v;
-    }
-  }
-}
-
-__global__ void k_scatter_rows(const float* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ idx, int s,
-                               int dlim, int cols, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
-  for (int i = blockIdx.y; i < s; i += gridDim.y) {
-    const int64_t row = (int64_t)clampi(idx[i], dlim) * ld_dst;
-    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x) {
-      const float v = src[(int64_t)i * ld_src + c];
-      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[row + c] = (__bf16)v;
-      else reinterpret_cast<float*>(dst)[row + c] = v;
     }
   }
 }
@@ -688,12 +699,24 @@ hipError_t launch_fill_group(const FillGroup& g, float v, hipStream_t st) {
 
 static dim3 row_grid(int cols, int rows) { return dim3((cols + kThreads - 1) / kThreads, rows < 65535 ? rows : 65535); }
 
+static bool al16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static hipError_t launch_rows4(const float* src, int64_t ld_src, const int32_t* sidx, const int32_t* didx, int dlim,
+                               int rows, int cols, void* dst, int dst_dt, int64_t ld_dst, __bf16* dst2, int64_t ld_dst2,
+                               hipStream_t st) {
+  const bool vec = ld_src % 4 == 0 && ld_dst % 4 == 0 && (!dst2 || ld_dst2 % 4 == 0) && al16(src) &&
+                   (dst_dt == BF16 ? (reinterpret_cast<uintptr_t>(dst) & 7) == 0 : al16(dst)) &&
+                   (reinterpret_cast<uintptr_t>(dst2) & 7) == 0;
+  hipLaunchKernelGGL(k_rows4, row_grid((cols + 3) / 4, rows), dim3(kThreads), 0, st, src, ld_src, sidx, didx, dlim, rows,
+                     cols, dst, dst_dt, ld_dst, dst2, ld_dst2, vec ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t ld_dst, int dst_dt, int rows, int cols,
                           hipStream_t st) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)rows * cols * (4 + dtype_size(dst_dt)));
-  hipLaunchKernelGGL(k_convert, row_grid(cols, rows), dim3(kThreads), 0, st, src, ld_src, dst, ld_dst, dst_dt, rows, cols);
-  return hipGetLastError();
+  return launch_rows4(src, ld_src, nullptr, nullptr, rows, rows, cols, dst, dst_dt, ld_dst, nullptr, 0, st);
 }
 
 hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
@@ -748,6 +771,9 @@ hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, co
                                  int64_t ld_dst2) {
   if (s <= 0 || cols <= 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt) + (dst2 ? 2 : 0)));
+  if (src_dt == F32)
+    return launch_rows4(reinterpret_cast<const float*>(src), ld_src, idx, nullptr, dlim, s, cols, dst, dst_dt, ld_dst,
+                        dst2, ld_dst2, st);
   hipLaunchKernelGGL(k_gather_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, src_dt, ld_src, idx, s, dlim, cols,
                      dst, dst_dt, ld_dst, dst2, ld_dst2);
   return hipGetLastError();
@@ -762,9 +788,7 @@ hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* 
                                int dst_dt, int64_t ld_dst, hipStream_t st) {
   if (s <= 0 || cols <= 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)s * cols * (4 + dtype_size(dst_dt)));
-  hipLaunchKernelGGL(k_scatter_rows, row_grid(cols, s), dim3(kThreads), 0, st, src, ld_src, idx, s, dlim, cols, dst,
-                     dst_dt, ld_dst);
-  return hipGetLastError();
+  return launch_rows4(src, ld_src, nullptr, idx, dlim, s, cols, dst, dst_dt, ld_dst, nullptr, 0, st);
 }
 
 uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch) {
