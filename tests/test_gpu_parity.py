@@ -189,7 +189,7 @@ def test_determinism_bitwise():
 
 # -------------------------------------------------------------------------------------------------- sampler
 @pytest.mark.parametrize("d,s", [(1, 1), (7, 3), (256, 128), (1000, 1), (2048, 1024), (5461, 2730), (6848, 3424),
-                                 (300, 300)])
+                                 (300, 300), (64, 63), (65, 32), (1024, 512), (1025, 1024), (1088, 1)])
 def test_sampler_bit_exact(d, s):
     from orthogonal_reparameterized_amd import binding as B
     announce(f"sampler d={d} s={s}")
