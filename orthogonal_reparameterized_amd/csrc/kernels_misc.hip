@@ -426,9 +426,16 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
     for (int u = 0; u < VEC; ++u) q[t - 1][u] = 0.f;
     if (t <= k && r < bp) {
       const T* src = powers + ((size_t)(t - 1) * nprim + p) * bp * ldp + (size_t)r * ldp + c0;
+      if (c0 + VEC <= bp) {  // whole group inside the block: one VEC-wide load (the launcher checked the alignment)
+        T w[VEC];
+        __builtin_memcpy(w, __builtin_assume_aligned(src, sizeof(T) * VEC), sizeof(w));
 #pragma unroll
-      for (int u = 0; u < VEC; ++u)
-        if (c0 + u < bp) q[t - 1][u] = (float)src[u];
+        for (int u = 0; u < VEC; ++u) q[t - 1][u] = (float)w[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+          if (c0 + u < bp) q[t - 1][u] = (float)src[u];
+      }
     }
   }
   // C_j = [j > 0] a_{j+1} (-1)^j I + sum_{t=1}^{k-j} a_{t+j+1} (-1)^{t+j} Q^t, with a_i = 2 (i <= k), a_{k+1} = 1
@@ -455,8 +462,10 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
       }
     }
     T* dst = out + ((size_t)p * (k + 1) + j) * pq + rc0;
+    T w[VEC];
 #pragma unroll
-    for (int u = 0; u < VEC; ++u) dst[u] = (T)v[u];
+    for (int u = 0; u < VEC; ++u) w[u] = (T)v[u];
+    __builtin_memcpy(__builtin_assume_aligned(dst, sizeof(T) * VEC), w, sizeof(w));
   }
 }
 
@@ -557,12 +566,24 @@ hipError_t launch_adjoint_coefs_group(const CoefGroup& g, int dt, hipStream_t st
 #define POET_COEF(T_, V_, KM_)                                                                          \
   hipLaunchKernelGGL((k_adjoint_coefs<T_, V_, KM_>), dim3((pq / V_ + kThreads - 1) / kThreads, ny, g.n), \
                      dim3(kThreads), 0, st, g)
-  if (dt == BF16 && ldp % 4 == 0) {
+  // VEC elements of a row per thread, moved as one load / store: VEC divides ldp and every side's powers and
+  // output are aligned to VEC elements
+  uintptr_t bits = 0;
+  for (int i = 0; i < g.n; ++i)
+    bits |= reinterpret_cast<uintptr_t>(g.s[i].powers) | reinterpret_cast<uintptr_t>(g.s[i].out);
+  const bool a16 = (bits & 15) == 0, a8 = (bits & 7) == 0;
+  if (dt == BF16 && ldp % 8 == 0 && a16) {
+    if (k <= 8) POET_COEF(__bf16, 8, 8);
+    else POET_COEF(__bf16, 8, 16);
+  } else if (dt == BF16 && ldp % 4 == 0 && a8) {
     if (k <= 8) POET_COEF(__bf16, 4, 8);
     else POET_COEF(__bf16, 4, 16);
   } else if (dt == BF16) {
     if (k <= 8) POET_COEF(__bf16, 1, 8);
     else POET_COEF(__bf16, 1, 16);
+  } else if (ldp % 4 == 0 && a16) {
+    if (k <= 8) POET_COEF(float, 4, 8);
+    else POET_COEF(float, 4, 16);
   } else {
     if (k <= 8) POET_COEF(float, 1, 8);
     else POET_COEF(float, 1, 16);
