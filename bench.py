@@ -4,14 +4,17 @@ parameters for every linear of a LLaMA-shaped block, with merge-then-reinitializ
 
 Prints one JSON line: whole-job tokens/s (inputs resident in HBM), the roofline of the dominant kernel measured
 live with HIP events on the launch stream, and the CPU oracle timed on a bounded sample of the same workload.
+The default run (the LLaMA-1.3B POET-BS block) also times the LLaMA-1.3B POET-FS block and reports it under
+"fs_block" (skip with --no-fs).
 
-  python bench.py [--steps K] [--warmup W] [--workload 3|4|2|1] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload 3|4|5|2|1] [--no-cpu-baseline] [--no-fs]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,10 +32,10 @@ def log(msg):
     sys.stderr.flush()
 
 
-def build_block(wl, torch, B, PI, PoetLinear, path="auto"):
+def build_block(wl, torch, B, PI, PoetLinear, path="auto", layer=0):
     lins = []
-    for lin in wl.linears(0):
-        W0, tR, tP = PI.gen_weights(wl.cfg_id, 0, lin)
+    for lin in wl.linears(layer):
+        W0, tR, tP = PI.gen_weights(wl.cfg_id, layer, lin)
         ldw, ldx, ldy = PI.pad_ld(lin.n), PI.pad_ld(lin.n), PI.pad_ld(lin.m)
         pl = PoetLinear(lin.m, lin.n, lin.T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
                         seed=wl.seed, linear_id=lin.linear_id, ldw=ldw, ldx=ldx, ldy=ldy, path=path)
@@ -87,15 +90,35 @@ def measured_traffic(tag: str):
         return None
 
 
-def algorithmic_flops(lins):
-    """2MNK of the three token GEMMs of every linear (Y, dX and the weight gradient)."""
-    return sum(3 * 2.0 * e["spec"].T * e["spec"].m * e["spec"].n for e in lins)
+def _prim_sums(side):
+    """Sum of c^2 and of c^3 over the primitives of one side (c = block size, or s for FS)."""
+    if side.mode == 1:
+        return side.b ** 2, side.b ** 3
+    cs = [min(side.b, side.d - o) for o in range(0, side.d, side.b)]
+    return sum(c * c for c in cs), sum(c ** 3 for c in cs)
+
+
+def algorithmic_flops(specs):
+    """Floating-point work of one fwd+bwd step of these linears, counted on the method's definition and not on the
+    kernels that run (2MNK per product):
+      path A (materialize W):  6Tmn (Y, dX, weight gradient) + 2x(2n sum c_R^2 + 2m sum c_P^2) (apply + contraction)
+      path B (factors on the activations):  4Tmn + 6T(sum c_R^2 + sum c_P^2)
+    both plus the Cayley-Neumann chain 2k sum c^3 per side and its adjoint (twice the chain). The step's
+    algorithmic MFU takes the smaller of the two, so that extra work done by the chosen path cannot raise it."""
+    a = b = 0.0
+    for l in specs:
+        (r2, r3), (p2, p3) = _prim_sums(l.R), _prim_sums(l.P)
+        chain = 2.0 * l.R.k * r3 + 2.0 * l.P.k * p3
+        a += 6.0 * l.T * l.m * l.n + 2 * (2.0 * l.n * r2 + 2.0 * l.m * p2) + 3 * chain
+        b += 4.0 * l.T * l.m * l.n + 6.0 * l.T * (r2 + p2) + 3 * chain
+    return {"path_A": a, "path_B": b, "min": min(a, b)}
 
 
 def cpu_baseline(wl, budget_s: float = 25.0):
     """The oracle (float64 NumPy, as it stands) on the same workload: forward + backward of the block's linears
     at the full token count, in order, until the time budget is spent. If it stops early, the block time is
-    extrapolated from the linears done by the block's sum of m*n (and the sample string says so)."""
+    extrapolated from the linears done by the block's sum of m*n (and the sample string says so). A stack of
+    several layers is timed on one layer and multiplied by the layer count (also said in the sample string)."""
     import oracle as O
     import poet_inputs as PI
     try:
@@ -125,8 +148,291 @@ def cpu_baseline(wl, budget_s: float = 25.0):
         sample += f"; block time extrapolated by the block's sum of m*n ({scale:.2f}x)"
     else:
         sample += " (the whole block step)"
-    return {"value": round(wl.T / (spent * scale), 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample}
+    if wl.layers > 1:
+        sample += f"; one layer of {wl.layers}, the stack's time extrapolated as {wl.layers}x that layer"
+    return {"value": round(wl.T / (spent * scale * wl.layers), 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample}
+
+
+def _profile(B, fn, steps):
+    """Run fn() `steps` times with the library's launch profiler on and return the per-class kernel records."""
+    import torch
+    B.poet_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
+    B.poet_profile_enable(False)
+    return prof
+
+
+def _timed(fn, steps, torch):
+    """K calls of fn with nothing else on the stream, bracketed by synchronization; per-step event pairs on the
+    current stream (the library launches on it) give the median and the minimum next to the mean."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per, wall
+
+
+def _roofline(prof, peak, traffic=None):
+    """Roofline line of the dominant token-GEMM class: its algorithmic flops over its launch durations."""
+    token = {k: prof[k] for k in ("token_fwd", "token_dx", "token_gw")}
+    dom = max(token, key=lambda k: token[k]["ms"])
+    d = token[dom]
+    achieved = d["flops"] / (d["ms"] / 1e3) / 1e12 if d["ms"] > 0 else 0.0
+    return dom, {"bound": "mfma", "kernel": f"gemm ({dom})", "achieved": round(achieved, 1), "peak": peak,
+                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                 "avg_launch_ms": round(d["ms"] / max(d["launches"], 1), 4), "launches": d["launches"],
+                 "flops_per_launch": d["flops"] / max(d["launches"], 1)}
+
+
+def _hbm_class(p):
+    """Achieved GB/s of a data-movement kernel class on its algorithmic bytes."""
+    if not p["launches"] or p["ms"] <= 0:
+        return None
+    gbs = p["bytes"] / (p["ms"] / 1e3) / 1e9
+    return {"ms": round(p["ms"], 4), "launches": p["launches"], "algorithmic_bytes": p["bytes"],
+            "achieved_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def _merge_leg(B, torch, build, merge, nbytes, period):
+    """Merge-then-reinitialize of every linear, timed on its own and amortized over its period. Each of three
+    merges follows a build (untimed: the merge folds built factors); the first pays each kernel's first load, the
+    second is timed, the third runs under the launch profiler."""
+    ms_merge, mprof = None, None
+    for rep in range(3):
+        build()
+        torch.cuda.synchronize()
+        B.poet_profile_enable(rep == 2)
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        merge()
+        m1.record()
+        torch.cuda.synchronize()
+        if rep == 1:
+            ms_merge = m0.elapsed_time(m1)
+    mprof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
+    B.poet_profile_enable(False)
+    info = {"ms_all_linears": round(ms_merge, 4), "algorithmic_bytes": nbytes,
+            "achieved_GBps": round(nbytes / (ms_merge / 1e3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms_merge / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel_ms": {k: round(v["ms"], 4) for k, v in mprof.items() if v["launches"]},
+            "kernel_launches": {k: v["launches"] for k, v in mprof.items() if v["launches"]}}
+    mk = _hbm_class(mprof["merge"])
+    if mk is not None:
+        info["merge_kernels"] = mk
+    return ms_merge, info
+
+
+def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
+    """One block of 7 linears (or the single-linear workload): timed steps, profiled steps, merge leg."""
+    log(f"workload {wl.name}: allocating")
+    lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
+    group = None if args.no_group else PoetGroup([e["pl"] for e in lins])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(lins, group)
+    torch.cuda.synchronize()
+
+    # one step captured into a HIP graph (torch's CUDAGraph over the HIP stream the library launches on): replays
+    # issue the same kernels with the same arguments without the host's per-launch cost
+    graph = None
+    if args.graph:
+        log("capturing one step into a graph")
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step(lins, group)  # a step on the capture stream first (the library's first launch on a stream)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(lins, group)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    log(f"timed {args.steps} steps")
+    ms_step, per, wall = _timed((lambda: graph.replay()) if graph is not None else (lambda: step(lins, group)),
+                                args.steps, torch)
+    # the same K steps again with the library's launch profiler on (an event pair around every launch, on the
+    # launch stream): per-class kernel times and the dominant kernel's launch duration. The events add gaps
+    # between launches, not kernel time, so this pass is kept out of the timed region above.
+    log(f"profiled {args.steps} steps")
+    prof = _profile(B, lambda: step(lins, group), args.steps)
+
+    log("merge")
+    # algorithmic HBM bytes: every element of W0 read and written once in float32, plus the bf16 copy of W0 the
+    # activation-side path reads, written by the same merge
+    merge_bytes = sum((10.0 if e["pl"].act_path else 8.0) * e["spec"].m * e["spec"].n for e in lins)
+    if group is not None:
+        ms_merge, merge_info = _merge_leg(B, torch, group.build, group.merge, merge_bytes, args.merge_period)
+    else:
+        def build_all():
+            for e in lins:
+                e["pl"].build()
+
+        def merge_all():
+            for e in lins:
+                e["pl"].merge()
+        ms_merge, merge_info = _merge_leg(B, torch, build_all, merge_all, merge_bytes, args.merge_period)
+
+    ms_total = ms_step + ms_merge / args.merge_period
+    peak = PEAK_BF16_TFLOPS if wl.dtype == PI.DT_BF16 else PEAK_F32_TFLOPS
+    act = all(e["pl"].act_path for e in lins)
+    dom, roof = _roofline(prof, peak)
+    if wl.cfg_id == 3 and act:
+        roof["traffic"] = measured_traffic(dom)
+    token = [prof[k] for k in ("token_fwd", "token_dx", "token_gw")]
+    gemm_ms, gemm_fl = sum(v["ms"] for v in token), sum(v["flops"] for v in token)
+    fl = algorithmic_flops([e["spec"] for e in lins])
+    res = {
+        "value": round(wl.T / (ms_total / 1e3), 1), "ms_per_step": round(ms_total, 4),
+        "ms_fwd_bwd": round(ms_step, 4), "ms_fwd_bwd_median": round(statistics.median(per), 4),
+        "ms_fwd_bwd_min": round(min(per), 4), "ms_merge_all_linears": round(ms_merge, 4),
+        "config": {"workload": wl.name, "hidden": wl.hidden, "ffn": wl.ffn, "tokens": wl.T,
+                   "mode": "BS" if wl.mode == PI.MODE_BS else "FS",
+                   "block": wl.b, "fraction": wl.frac, "k": wl.k, "linears": len(lins),
+                   "factor_application": "activations" if act else
+                   ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
+                   "grouped_side_steps": group is not None, "merge_period": args.merge_period},
+        "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
+        "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
+        "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
+        "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
+        "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / peak, 4),
+        "stage_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
+        "stage_launches_per_step": {k: v["launches"] // args.steps for k, v in prof.items()},
+    }
+    g = _hbm_class({k: v / args.steps if k != "launches" else v // args.steps for k, v in prof["gather"].items()})
+    if g is not None:
+        res["gather_scatter"] = g
+    del lins, group, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
+    """The LLaMA-3B POET-FS stack: every layer's state resident at once (float32 W0, skew parameters, primitives,
+    saved powers, index sets, the materialized weights and the layer inputs kept for the backward); one step =
+    grouped build and forward of every layer in order, then the backward of every layer in reverse order to the
+    primitive gradients and the grouped adjoint per layer. Weights and activations are drawn on the device with
+    the recipe's distributions (W0 row-normalized Gaussian, theta ~ N(0, 1e-3^2), X and dY ~ N(0, 1) in bf16).
+    Inputs of one shape are shared the way a transformer layer shares them (q/k/v read one input, gate/up one)."""
+    T = wl.T
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    specs = [wl.linears(layer) for layer in range(wl.layers)]
+    shapes = specs[0]
+    ws_lin = max(PoetLinear.workspace_bytes(l.m, l.n, T, B.side_of(l.R), B.side_of(l.P), l.act_dtype,
+                                            PI.pad_ld(l.n), PI.pad_ld(l.n), PI.pad_ld(l.m)) for l in shapes)
+    ws = torch.empty(ws_lin, dtype=torch.uint8, device="cuda")
+    wide = max(PI.pad_ld(max(l.m, l.n)) for l in shapes)
+    Ybuf = torch.empty((T, wide), dtype=torch.bfloat16, device="cuda")
+    dXbuf = torch.empty((T, wide), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000)
+    dYs = {}  # one upstream gradient per output width, shared by the layers
+    for l in shapes:
+        ldy = PI.pad_ld(l.m)
+        if ldy not in dYs:
+            dYs[ldy] = torch.randn((T, ldy), generator=g, device="cuda").to(torch.bfloat16)
+    share = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+    layers = []
+    for layer, lins in enumerate(specs):
+        xs, es = {}, []
+        for lin in lins:
+            W0 = torch.randn((lin.m, lin.n), generator=g, device="cuda")
+            W0 /= W0.norm(dim=1, keepdim=True)
+            tR = torch.randn(B.poet_theta_len(B.side_of(lin.R)), generator=g, device="cuda") * PI.THETA_STD
+            tP = torch.randn(B.poet_theta_len(B.side_of(lin.P)), generator=g, device="cuda") * PI.THETA_STD
+            ldx, ldy = PI.pad_ld(lin.n), PI.pad_ld(lin.m)
+            pl = PoetLinear(lin.m, lin.n, T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
+                            seed=wl.seed, linear_id=lin.linear_id, ldw=PI.pad_ld(lin.n), ldx=ldx, ldy=ldy, ws=ws,
+                            path="weight")
+            del W0, tR, tP
+            key = share[lin.name]
+            if key not in xs:
+                xs[key] = torch.randn((T, ldx), generator=g, device="cuda").to(torch.bfloat16)
+            es.append({"spec": lin, "pl": pl, "X": xs[key], "W": pl.alloc_W(),
+                       "Y": Ybuf.view(-1)[:T * ldy].view(T, ldy), "dX": dXbuf.view(-1)[:T * ldx].view(T, ldx),
+                       "dY": dYs[ldy]})
+        layers.append(es)
+        log(f"stack: layer {layer} allocated, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]]), 1), dtype=torch.uint8,
+                      device="cuda")
+    groups = [PoetGroup([e["pl"] for e in es], ws=gws) for es in layers]
+    state_bytes = torch.cuda.memory_allocated() - base
+
+    def stack_step():
+        for es, grp in zip(layers, groups):
+            grp.build()
+            for e in es:
+                e["pl"].forward(e["X"], e["Y"], W_out=e["W"])
+        for es, grp in zip(reversed(layers), reversed(groups)):
+            for e in reversed(es):
+                e["pl"].backward_prims(e["X"], e["dY"], e["dX"], W=e["W"])
+            grp.finish_backward()
+
+    log(f"stack warmup {args.warmup}")
+    for _ in range(args.warmup):
+        stack_step()
+    torch.cuda.synchronize()
+    log(f"stack timed {args.steps} steps")
+    ms_step, per, wall = _timed(stack_step, args.steps, torch)
+    log("stack profiled step")
+    prof = _profile(B, stack_step, 1)
+    log("stack merge")
+    all_specs = [e["spec"] for es in layers for e in es]
+    merge_bytes = sum(8.0 * l.m * l.n for l in all_specs)
+
+    def build_all():
+        for grp in groups:
+            grp.build()
+
+    def merge_all():
+        for grp in groups:
+            grp.merge()
+    ms_merge, merge_info = _merge_leg(B, torch, build_all, merge_all, merge_bytes, args.merge_period)
+    ms_total = ms_step + ms_merge / args.merge_period
+    peak_bytes = torch.cuda.max_memory_allocated() - base
+    n_params = sum(l.m * l.n for l in all_specs)
+    n_theta = sum(B.poet_theta_len(B.side_of(l.R)) + B.poet_theta_len(B.side_of(l.P)) for l in all_specs)
+    fl = algorithmic_flops(all_specs)
+    dom, roof = _roofline(prof, PEAK_BF16_TFLOPS)
+    res = {
+        "value": round(T / (ms_total / 1e3), 1), "ms_per_step": round(ms_total, 4), "ms_fwd_bwd": round(ms_step, 4),
+        "ms_fwd_bwd_median": round(statistics.median(per), 4), "ms_fwd_bwd_min": round(min(per), 4),
+        "ms_merge_all_linears": round(ms_merge, 4),
+        "config": {"workload": wl.name, "hidden": wl.hidden, "ffn": wl.ffn, "tokens": T, "mode": "FS",
+                   "fraction": wl.frac, "k": wl.k, "layers": wl.layers, "linears": len(all_specs),
+                   "factor_application": "weight", "grouped_side_steps": True, "merge_period": args.merge_period},
+        "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3),
+        "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
+        "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stage_ms_per_step": {k: round(v["ms"], 4) for k, v in prof.items()},
+        # device memory: measured peak of the whole run, and the resident state before the first step (W0 float32,
+        # theta, primitives, saved powers, index sets, kept weights and inputs, workspaces); the dense figure is the
+        # float32 weight, its gradient and the two AdamW moments of the same linears (16 bytes per weight element,
+        # arithmetic, not measured)
+        "memory": {"peak_hbm_gib": round(peak_bytes / 2**30, 2), "resident_state_gib": round(state_bytes / 2**30, 2),
+                   "linear_weight_elements": n_params, "trainable_skew_params": n_theta,
+                   "dense_adamw_weight_grad_moments_gib": round(16.0 * n_params / 2**30, 2)},
+    }
+    g = _hbm_class(prof["gather"])
+    if g is not None:
+        res["gather_scatter"] = g
+    return res
 
 
 def main():
@@ -134,9 +440,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--merge-period", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fs", action="store_true",
+                    help="with the default workload, skip the extra LLaMA-1.3B POET-FS block measurement")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (the default launches every step)")
     ap.add_argument("--path", default="auto", choices=["auto", "weight", "act"],
@@ -162,127 +470,20 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     wl = PI.WORKLOADS[args.workload]
-    log(f"workload {wl.name}: allocating")
-    lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
-    group = None if args.no_group else PoetGroup([e["pl"] for e in lins])
-    torch.cuda.synchronize()
-    T = wl.T
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step(lins, group)
-    torch.cuda.synchronize()
-
-    # one step captured into a HIP graph (torch's CUDAGraph over the HIP stream the library launches on): replays
-    # issue the same kernels with the same arguments without the host's per-launch cost
-    graph = None
-    if args.graph:
-        log("capturing one step into a graph")
-        s_cap = torch.cuda.Stream()
-        s_cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s_cap):
-            step(lins, group)  # a step on the capture stream first (the library's first launch on a stream)
-        torch.cuda.current_stream().wait_stream(s_cap)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(lins, group)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-
-    # timed region: K steps (graph replays, or eager launches) with nothing else on the stream
-    log(f"timed {args.steps} steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step(lins, group)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    # the same K steps again with the library's launch profiler on (an event pair around every launch, on the
-    # launch stream): per-class kernel times and the dominant kernel's launch duration. The events add gaps
-    # between launches, not kernel time, so this pass is kept out of the timed region above.
-    log(f"profiled {args.steps} steps")
-    B.poet_profile_enable(True)
-    for _ in range(args.steps):
-        step(lins, group)
-    torch.cuda.synchronize()
-    prof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
-    B.poet_profile_enable(False)
-
-    # merge-then-reinitialize of every linear, timed on its own and amortized over its period; its kernels are
-    # profiled separately (algorithmic HBM bytes: every element of W0 read and written once, float32)
-    # (one untimed merge first: the first call of each kernel pays its load; the work of a merge does not depend
-    # on the state it leaves, and a third, profiled merge gives the per-class kernel times)
-    log("merge")
-    for rep in range(3):
-        torch.cuda.synchronize()
-        B.poet_profile_enable(rep == 2)
-        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        m0.record()
-        if group is not None:
-            group.merge()
-        else:
-            for e in lins:
-                e["pl"].merge()
-        m1.record()
-        torch.cuda.synchronize()
-        if rep == 1:
-            ms_merge = m0.elapsed_time(m1)
-    mprof = {B.KCLASS_NAMES[c]: B.poet_profile_query(c) for c in range(len(B.KCLASS_NAMES))}
-    B.poet_profile_enable(False)
-    # (plus the bf16 copy of W0 the activation-side path reads, written by the same merge)
-    merge_bytes = sum((10.0 if e["pl"].act_path else 8.0) * e["spec"].m * e["spec"].n for e in lins)
-    merge_info = {"ms_all_linears": round(ms_merge, 4), "algorithmic_bytes": merge_bytes,
-                  "achieved_GBps": round(merge_bytes / (ms_merge / 1e3) / 1e9, 1),
-                  "hbm_frac": round(merge_bytes / (ms_merge / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "kernel_ms": {k: round(v["ms"], 4) for k, v in mprof.items() if v["launches"]},
-                  "kernel_launches": {k: v["launches"] for k, v in mprof.items() if v["launches"]}}
-
-    ms_total = ms_step + ms_merge / args.merge_period
-    tokens_per_s = T / (ms_total / 1e3)
-
-    # roofline of the dominant kernel class
-    token = {k: prof[k] for k in ("token_fwd", "token_dx", "token_gw")}
-    dom = max(token, key=lambda k: token[k]["ms"])
-    d = token[dom]
-    avg_ms = d["ms"] / max(d["launches"], 1)
-    achieved = d["flops"] / (d["ms"] / 1e3) / 1e12 if d["ms"] > 0 else 0.0
-    peak = PEAK_BF16_TFLOPS if wl.dtype == PI.DT_BF16 else PEAK_F32_TFLOPS
-    gemm_ms = sum(v["ms"] for v in token.values())
-    gemm_fl = sum(v["flops"] for v in token.values())
-
-    out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_total, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == PI.DT_BF16 else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "hidden": wl.hidden, "ffn": wl.ffn, "tokens": T,
-                   "mode": "BS" if wl.mode == PI.MODE_BS else "FS",
-                   "block": wl.b, "fraction": wl.frac, "k": wl.k, "linears": len(lins),
-                   "factor_application": "activations" if all(e["pl"].act_path for e in lins) else
-                   ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
-                   "grouped_side_steps": group is not None, "merge_period": args.merge_period},
-        "roofline": {"bound": "mfma", "kernel": f"gemm ({dom})", "achieved": round(achieved, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(dom) if wl.cfg_id == 3 and all(e["pl"].act_path for e in lins) else None,
-                     "avg_launch_ms": round(avg_ms, 4), "launches": d["launches"],
-                     "flops_per_launch": d["flops"] / max(d["launches"], 1)},
-        "ms_fwd_bwd": round(ms_step, 4), "ms_merge_all_linears": round(ms_merge, 4), "merge": merge_info,
-        "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
-        "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
-        "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
-        "step_mfu": round(algorithmic_flops(lins) / (ms_total / 1e3) / 1e12 / peak, 4),
-        "stage_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
-        "stage_launches_per_step": {k: v["launches"] // args.steps for k, v in prof.items()},
-    }
+    if wl.layers > 1:
+        res = run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup)
+    else:
+        res = run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup)
+    out = {"metric": METRIC, "value": res.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == PI.DT_BF16 else "f32",
+           "data": "synthetic", "config": res.pop("config"), "roofline": res.pop("roofline")}
+    out.update(res)
+    if args.workload == 3 and not args.no_fs:
+        fs = PI.WORKLOADS[4]
+        log("extra: the POET-FS block")
+        r4 = run_block(fs, args, torch, B, PI, PoetLinear, PoetGroup)
+        out["fs_block"] = {"unit": "tokens/s", **r4}
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)

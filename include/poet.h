@@ -317,9 +317,10 @@ enum {
   POET_K_ADJOINT = 4,    /* Neumann adjoint */
   POET_K_APPLY = 5,      /* applying R and P to W0 (materialize, merge) */
   POET_K_CONTRACT = 6,   /* primitive-gradient contractions */
-  POET_K_MISC = 7,       /* packing, projection, gather/scatter, conversion, sampling */
+  POET_K_MISC = 7,       /* packing, projection, conversion, sampling */
   POET_K_MERGE = 8,      /* merge passes W0 <- R W0 P */
-  POET_K_NCLASS = 9
+  POET_K_GATHER = 9,     /* FS gathers and scatters of sampled rows / columns (and the sampled-block patch) */
+  POET_K_NCLASS = 10
 };
 /* Start (on != 0: clears previous records) or stop recording a HIP event pair around every kernel launch the
  * library issues, on the launch's own stream. Process-wide; intended for benchmarking, adds one event pair

@@ -32,8 +32,9 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
            "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group")
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
-    POET_K_MISC, POET_K_MERGE = range(9)
-KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge")
+    POET_K_MISC, POET_K_MERGE, POET_K_GATHER = range(10)
+KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge",
+                "gather")
 
 
 class PoetError(RuntimeError):

@@ -3,6 +3,7 @@
 // All are memory-bound; threads walk the contiguous dimension so that every wavefront access is coalesced.
 #include <algorithm>
 
+#include "../../include/poet.h"
 #include "internal.h"
 
 namespace poet {
@@ -743,7 +744,7 @@ hipError_t launch_convert(const float* src, int64_t ld_src, void* dst, int64_t l
 hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
                                  void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2, int64_t ld_dst2) {
   if (rows <= 0 || s <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt) + (dst2 ? 2 : 0)));
+  ProfScope prof(POET_K_GATHER, st, 0, (double)rows * s * (4 + dtype_size(dst_dt) + (dst2 ? 2 : 0)));
   hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
                      dst_dt, ld_dst, dst2, ld_dst2);
   return hipGetLastError();
@@ -767,7 +768,7 @@ hipError_t launch_split3(const float* src, int64_t ld_src, const int32_t* ridx, 
 hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, const int32_t* idx, int s, int dlim,
                                   void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
   if (rows <= 0 || s <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
+  ProfScope prof(POET_K_GATHER, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
   hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
                      dst_dt, ld_dst);
   return hipGetLastError();
@@ -776,7 +777,7 @@ hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, co
 hipError_t launch_patch_block(const float* C, int64_t ldc, const int32_t* ridx, int rlim, const int32_t* cidx, int clim,
                               int sr, int sc, float* dst, int64_t ld_dst, __bf16* dst2, int64_t ld_dst2, hipStream_t st) {
   if (sr <= 0 || sc <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)sr * sc * 10);
+  ProfScope prof(POET_K_GATHER, st, 0, (double)sr * sc * 10);
   hipLaunchKernelGGL(k_patch_block, row_grid(sc, sr), dim3(kThreads), 0, st, C, ldc, ridx, rlim, cidx, clim, sr, sc, dst,
                      ld_dst, dst2, ld_dst2);
   return hipGetLastError();
@@ -791,7 +792,7 @@ hipError_t launch_gather_rows_to(const void* src, int src_dt, int64_t ld_src, co
                                  int cols, void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2,
                                  int64_t ld_dst2) {
   if (s <= 0 || cols <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt) + (dst2 ? 2 : 0)));
+  ProfScope prof(POET_K_GATHER, st, 0, (double)s * cols * (dtype_size(dst_dt) + dtype_size(src_dt) + (dst2 ? 2 : 0)));
   if (src_dt == F32)
     return launch_rows4(reinterpret_cast<const float*>(src), ld_src, idx, nullptr, dlim, s, cols, dst, dst_dt, ld_dst,
                         dst2, ld_dst2, st);
@@ -808,7 +809,7 @@ hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols, void* dst,
                                int dst_dt, int64_t ld_dst, hipStream_t st) {
   if (s <= 0 || cols <= 0) return hipSuccess;
-  ProfScope prof(7, st, 0, (double)s * cols * (4 + dtype_size(dst_dt)));
+  ProfScope prof(POET_K_GATHER, st, 0, (double)s * cols * (4 + dtype_size(dst_dt)));
   return launch_rows4(src, ld_src, nullptr, idx, dlim, s, cols, dst, dst_dt, ld_dst, nullptr, 0, st);
 }
 

@@ -81,6 +81,8 @@ class PoetLinear:
         # the factors folded into the bf16 weight (W0 P, R W0), written by PoetGroup.build for large token counts;
         # None until then (and after a one-linear build, which leaves them stale)
         self.W0P = self.RW0 = None
+        # True between a build and the next merge: the primitives (and folds, operand copies) match theta and W0
+        self.built = False
         if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
             self.W0b = torch.empty((m, self.L.ldw), dtype=self.act, device=self.dev)
             B.poet_weight_shadow(self.L, self.W0, self.W0b)
@@ -118,10 +120,17 @@ class PoetLinear:
     def build(self, stream=None, qnorm: bool = False):
         self.opsR = self.opsP = None  # the one-side build does not write them
         self.W0P = self.RW0 = None
+        self.built = False
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
                                 self.ws, stream)
         B.poet_build_orthogonal(self.L.P, self.thetaP, self.primP, self._powers("P"), self.qnormP if qnorm else None,
                                 self.ws, stream)
+        self.built = True
+
+    def _need_build(self, what: str):
+        if not self.built:
+            raise RuntimeError(f"{what} needs built factors: call build() (or PoetGroup.build()) after construction "
+                               "and after every merge")
 
     def alloc_act(self, rows: int, ld: int):
         return _torch().empty((rows, ld), dtype=self.act, device=self.dev)
@@ -130,15 +139,18 @@ class PoetLinear:
         return _torch().empty((self.m, self.L.ldw), dtype=self.act, device=self.dev)
 
     def forward(self, X, Y, W_out=None, stream=None):
+        self._need_build("forward")
         B.poet_linear_fwd(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, X, Y, W_out, self.ws, stream)
 
     def backward(self, X, dY, dX, W=None, stream=None):
+        self._need_build("backward")
         B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
 
     def forward_act(self, X, Y, Z, stream=None):
         """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
         operand copies of the primitives (and W0 P, folded) come from the last PoetGroup.build, when one made them."""
+        self._need_build("forward_act")
         if self.W0P is not None:
             B.poet_linear_fwd_folded(self.L, self.W0P, self.primR, X, Y, Z, self.ws, stream, opsR=self.opsR)
         else:
@@ -146,6 +158,7 @@ class PoetLinear:
                                   opsR=self.opsR, opsP=self.opsP)
 
     def backward_act(self, X, Z, dY, dX, stream=None):
+        self._need_build("backward_act")
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
                               dY, dX, self.dthetaR, self.dthetaP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
 
@@ -158,6 +171,7 @@ class PoetLinear:
     def backward_prims(self, X, dY, dX, W=None, stream=None):
         """Weight-side backward up to the primitive gradients dprimR, dprimP; PoetGroup.finish_backward turns them
         into dthetaR, dthetaP for many linears at once."""
+        self._need_build("backward_prims")
         self._dprims()
         B.poet_linear_bwd_prims(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, W, X, dY, dX,
                                 self.dprimR, self.dprimP, self.ws, stream)
@@ -165,6 +179,7 @@ class PoetLinear:
     def backward_act_prims(self, X, Z, dY, dX, stream=None):
         """Activation-side backward up to the primitive gradients dprimR, dprimP (the blocks of dL/dR and dL/dP);
         PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
+        self._need_build("backward_act_prims")
         self._dprims()
         if self.RW0 is not None:
             B.poet_linear_bwd_folded_prims(self.L, self.RW0, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
@@ -175,12 +190,22 @@ class PoetLinear:
 
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
-        when given, receives the merged W0 in the act dtype as well)."""
-        self.epoch += 1
+        when given, receives the merged W0 in the act dtype as well). The merge folds the primitives of the last
+        build; afterwards theta is zero and the next step must build again."""
+        self._need_build("merge")
         B.poet_merge(self.L, self.W0, self.W0b if shadow is None else shadow, self.thetaR, self.thetaP, self.primR,
-                     self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch, self.ws, stream)
+                     self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch + 1, self.ws, stream)
+        self._merged()
         if shadow is not None and self.W0b is not None:
             B.poet_weight_shadow(self.L, self.W0, self.W0b, stream)
+
+    def _merged(self):
+        """State after a merge was enqueued: the next epoch, and the primitives, operand copies and folded weights
+        of the last build are stale (they belong to the parameters before the reset)."""
+        self.epoch += 1
+        self.built = False
+        self.opsR = self.opsP = None
+        self.W0P = self.RW0 = None
 
 
 class PoetGroup:
@@ -192,7 +217,9 @@ class PoetGroup:
     merge-then-reinitialize of every linear (poet_merge_group). Results match the per-linear calls up to the
     float32 summation order of split products."""
 
-    def __init__(self, linears):
+    def __init__(self, linears, ws=None):
+        """``ws`` (optional): a uint8 device tensor shared with other groups whose calls run one after another on one
+        stream (``PoetGroup.workspace_bytes`` gives the size this group needs)."""
         torch = _torch()
         self.linears = list(linears)
         if not self.linears:
@@ -214,11 +241,22 @@ class PoetGroup:
                 fR = pl.T >= pl.n and pl.L.R.b >= 128
                 self._fold[id(pl)] = (torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fP else None,
                                       torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fR else None)
-        act = [pl for pl in self.linears if pl.act_path]
-        need = max(B.poet_build_group_workspace_bytes(self.sides), B.poet_adjoint_group_workspace_bytes(self.sides),
-                   B.poet_merge_group_workspace_bytes([pl.L for pl in self.linears]),
+        need = PoetGroup.workspace_bytes(self.linears)
+        if ws is None:
+            self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        else:
+            if ws.numel() * ws.element_size() < need:
+                raise ValueError(f"shared workspace holds {ws.numel() * ws.element_size()} bytes, this group needs {need}")
+            self.ws = ws
+
+    @staticmethod
+    def workspace_bytes(linears) -> int:
+        """Bytes of the workspace the grouped calls of these linears need."""
+        sides = [s for pl in linears for s in (pl.L.R, pl.L.P)]
+        act = [pl for pl in linears if pl.act_path]
+        return max(B.poet_build_group_workspace_bytes(sides), B.poet_adjoint_group_workspace_bytes(sides),
+                   B.poet_merge_group_workspace_bytes([pl.L for pl in linears]),
                    B.poet_fold_group_workspace_bytes([pl.L for pl in act]) if act else 0)
-        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def build(self, stream=None):
         thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]
@@ -229,6 +267,7 @@ class PoetGroup:
         for pl in self.linears:
             pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
             pl.W0P = pl.RW0 = None
+            pl.built = True
         act = [pl for pl in self.linears if pl.act_path and any(f is not None for f in self._fold[id(pl)])]
         if act:
             B.poet_fold_weights_group([pl.L for pl in act], [pl.W0b for pl in act], [pl.primR for pl in act],
@@ -254,8 +293,10 @@ class PoetGroup:
         if len({pl.seed for pl in pls}) != 1 or len({pl.epoch for pl in pls}) != 1:
             raise ValueError("PoetGroup.merge needs one sampler seed and one epoch across its linears")
         for pl in pls:
-            pl.epoch += 1
+            pl._need_build("PoetGroup.merge")
         B.poet_merge_group([pl.L for pl in pls], [pl.W0 for pl in pls], [pl.W0b for pl in pls],
                            [pl.thetaR for pl in pls], [pl.thetaP for pl in pls], [pl.primR for pl in pls],
                            [pl.primP for pl in pls], [pl.idxR for pl in pls], [pl.idxP for pl in pls], pls[0].seed,
-                           [pl.linear_id for pl in pls], pls[0].epoch, self.ws, stream)
+                           [pl.linear_id for pl in pls], pls[0].epoch + 1, self.ws, stream)
+        for pl in pls:
+            pl._merged()

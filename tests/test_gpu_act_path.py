@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import poet_inputs as PI
-from tests.gpu_util import TOL, announce, make_linear, put_act, rel, to_np
+from tests.gpu_util import check, theta_groups, TOL, announce, make_linear, put_act, rel, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -45,15 +45,19 @@ def run_act(lin, pad=0, theta_std=PI.THETA_STD, tag="", check_merge=False):
     pl.backward_act(Xd, Z, dYd, dX)
     torch.cuda.synchronize()
     tol = TOL[lin.act_dtype]
-    out = {
-        "Y": rel(to_np(Y)[:, :lin.m], ref_f["Y"]) if lin.T else 0.0,
-        "dX": rel(to_np(dX)[:, :lin.n], ref_b["dX"]) if lin.T else 0.0,
-        "dthetaR": rel(to_np(pl.dthetaR)[:len(tR)], ref_b["dthetaR"]) if len(tR) else 0.0,
-        "dthetaP": rel(to_np(pl.dthetaP)[:len(tP)], ref_b["dthetaP"]) if len(tP) else 0.0,
-    }
-    announce(f"act-path {tag} errors {out}")
-    for key, v in out.items():
-        assert v <= tol, (key, v, tol)
+    out = {}
+    try:
+        if lin.T:
+            check(out, "Y", to_np(Y)[:, :lin.m], ref_f["Y"], tol)
+            check(out, "dX", to_np(dX)[:, :lin.n], ref_b["dX"], tol)
+        if len(tR):
+            check(out, "dthetaR", to_np(pl.dthetaR)[:len(tR)], ref_b["dthetaR"], tol,
+                  theta_groups(lin.R.mode, lin.R.d, lin.R.b))
+        if len(tP):
+            check(out, "dthetaP", to_np(pl.dthetaP)[:len(tP)], ref_b["dthetaP"], tol,
+                  theta_groups(lin.P.mode, lin.P.d, lin.P.b))
+    finally:
+        announce(f"act-path {tag} errors {out}")
     if check_merge:  # merge, rebuild the (now identity) factors, forward again: Y = X W0_merged^T
         pl.merge()
         pl.build()

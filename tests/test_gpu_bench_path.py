@@ -1,0 +1,126 @@
+"""GPU parity of exactly the step the benchmark times, on whole LLaMA-1.3B blocks at full size.
+
+The block is made by ``bench.build_block`` and stepped by ``bench.step``, the same functions the benchmark's timed
+region calls, so the launch sequence checked here is the timed one:
+
+- POET-BS b = 256, k = 5 (the default workload): activation-side path, one grouped build of all 14 sides (which
+  writes the bf16 operand copies), grouped folds of P into W0 and of R into W0, per linear the folded forward and
+  the folded backward to the primitive gradients, one grouped Neumann adjoint of all 14 sides (152 blocks of 256);
+- POET-FS b = 1/2, k = 5: weight-side path, grouped build of the 14 FS chains (s = 1024 and 2730), per linear the
+  FS forward (materialized W) and the backward to the primitive gradients, one grouped adjoint;
+
+then the grouped merge-then-reinitialize of the whole block (``PoetGroup.merge``), as the benchmark's merge leg
+runs it.
+
+Inputs: W0 and the skew parameters come from the seeded host recipe; the activations X and upstream gradients dY
+are the ones the benchmark draws on the device, copied back so that the oracle sees exactly the values the GPU
+used. The step is run twice and must give bit-identical outputs (split-K sums are fixed-order).
+
+Bars: token outputs Y and dX on 256 sampled rows per linear (tokens are independent rows, so the sample is exact),
+d theta of every side in full, both against the float64 oracle at the bf16 bar 2e-2 (relative Frobenius, and the
+same bar per row / per primitive); the merged W0 of every linear in full at the float32 bar 1e-5; the bf16 copy of
+W0 equal to the merged W0 rounded; theta reset to zero; FS index sets equal to the oracle's for epoch 1.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import poet_inputs as PI
+from tests.gpu_util import TOL, announce, check, theta_groups, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _outputs(lins):
+    """The written part of each linear's outputs (row padding and spare gradient slots are never written)."""
+    from orthogonal_reparameterized_amd import binding as B
+    out = []
+    for e in lins:
+        lin, pl = e["spec"], e["pl"]
+        out.append((e["Y"][:, :lin.m].clone(), e["dX"][:, :lin.n].clone(),
+                    pl.dthetaR[:B.poet_theta_len(pl.L.R)].clone(), pl.dthetaP[:B.poet_theta_len(pl.L.P)].clone()))
+    return out
+
+
+def _block_as_benched(cfg_id):
+    import bench
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
+    wl = PI.WORKLOADS[cfg_id]
+    announce(f"bench path {wl.name}: allocating the block as the benchmark does")
+    lins = bench.build_block(wl, torch, B, PI, PoetLinear, "auto")
+    group = PoetGroup([e["pl"] for e in lins])
+    announce(f"bench path {wl.name}: step 1")
+    bench.step(lins, group)
+    torch.cuda.synchronize()
+    first = _outputs(lins)
+    announce(f"bench path {wl.name}: step 2 (determinism)")
+    bench.step(lins, group)
+    torch.cuda.synchronize()
+    for e, a in zip(lins, first):
+        for x, y, nm in zip(a, _outputs([e])[0], ("Y", "dX", "dthetaR", "dthetaP")):
+            assert torch.equal(x, y), (e["spec"].name, nm, "differs between two runs of the same step")
+    return wl, lins, group
+
+
+def _check_block(cfg_id, act_path):
+    wl, lins, group = _block_as_benched(cfg_id)
+    assert all(e["pl"].act_path == act_path for e in lins)
+    host = []
+    for e in lins:  # the values the GPU used, before the merge changes W0 and theta
+        lin, pl = e["spec"], e["pl"]
+        W0, tR, tP = PI.gen_weights(wl.cfg_id, 0, lin)
+        host.append({"W0": W0, "tR": tR, "tP": tP, "X": to_np(e["X"])[:, :lin.n], "dY": to_np(e["dY"])[:, :lin.m],
+                     "iR": None if pl.idxR is None else pl.idxR.cpu().numpy().copy(),
+                     "iP": None if pl.idxP is None else pl.idxP.cpu().numpy().copy()})
+        if lin.R.mode == PI.MODE_FS:  # the epoch-0 draw of the benchmark's linears is the oracle's
+            iR, iP = (O.sample_indices(d, s.b, wl.seed, lin.linear_id, side, 0)
+                      for d, s, side in ((lin.m, lin.R, O.SIDE_R), (lin.n, lin.P, O.SIDE_P)))
+            np.testing.assert_array_equal(host[-1]["iR"], iR)
+            np.testing.assert_array_equal(host[-1]["iP"], iP)
+    announce(f"bench path {wl.name}: grouped merge")
+    group.merge()
+    torch.cuda.synchronize()
+    tol = TOL[PI.DT_BF16]
+    rows = np.sort(np.random.default_rng(31).choice(wl.T, 256, replace=False))
+    for e, h in zip(lins, host):
+        lin, pl = e["spec"], e["pl"]
+        sR, sP = O.Side.of(lin.R), O.Side.of(lin.P)
+        f = O.linear_fwd(sR, sP, h["W0"], h["tR"], h["tP"], h["iR"], h["iP"], h["X"][rows])
+        g = O.linear_bwd(sR, sP, h["W0"], h["tR"], h["tP"], h["iR"], h["iP"], h["X"], h["dY"])
+        mg = O.merge(sR, sP, h["W0"], h["tR"], h["tP"], h["iR"], h["iP"], wl.seed, lin.linear_id, 1)
+        errs = {}
+        try:
+            check(errs, "Y_rows", to_np(e["Y"])[rows, :lin.m], f["Y"], tol)
+            check(errs, "dX_rows", to_np(e["dX"])[rows, :lin.n], g["dX"][rows], tol)
+            check(errs, "dthetaR", to_np(pl.dthetaR)[:len(h["tR"])], g["dthetaR"], tol,
+                  theta_groups(lin.R.mode, lin.R.d, lin.R.b))
+            check(errs, "dthetaP", to_np(pl.dthetaP)[:len(h["tP"])], g["dthetaP"], tol,
+                  theta_groups(lin.P.mode, lin.P.d, lin.P.b))
+            check(errs, "merged_W0", to_np(pl.W0)[:, :lin.n], mg["W0"], 1e-5)
+        finally:
+            announce(f"bench path {wl.name} {lin.name}: {errs}")
+        assert float(pl.thetaR.abs().max()) == 0.0 and float(pl.thetaP.abs().max()) == 0.0, lin.name
+        assert pl.epoch == 1
+        if pl.W0b is not None:  # the bf16 copy the activation side reads is the merged W0, rounded
+            np.testing.assert_array_equal(to_np(pl.W0b)[:, :lin.n], PI.round_bf16(to_np(pl.W0)[:, :lin.n]))
+        for got, want in ((pl.idxR, mg["idxR"]), (pl.idxP, mg["idxP"])):
+            if want is not None:
+                np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def test_llama1p3b_bs256_block_as_benched():
+    """LLaMA-1.3B block, POET-BS b = 256, k = 5, bf16, 16384 tokens: the benchmark's default step and merge."""
+    _check_block(3, act_path=True)
+
+
+def test_llama1p3b_fs_half_block_as_benched():
+    """LLaMA-1.3B block, POET-FS b = 1/2, k = 5, bf16, 16384 tokens: the FS workload's step and merge."""
+    _check_block(4, act_path=False)

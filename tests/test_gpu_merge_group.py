@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import poet_inputs as PI
-from tests.gpu_util import announce, make_linear, rel, to_np
+from tests.gpu_util import announce, check, make_linear, rel, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -73,9 +73,11 @@ def test_merge_group_matches_per_weight_merges_and_oracle():
         assert float(grp.thetaR.abs().max()) == 0.0 and float(grp.thetaP.abs().max()) == 0.0, lin.name
         assert grp.epoch == one.epoch == 1
         mg = O.merge(O.Side.of(lin.R), O.Side.of(lin.P), W0, tR, tP, iR, iP, SEED, lin.linear_id, 1)
-        err = rel(to_np(grp.W0)[:, :lin.n], mg["W0"])
-        announce(f"merge group {lin.name}: rel {err:.2e}")
-        assert err <= 1e-5, (lin.name, err)
+        errs = {}
+        try:
+            check(errs, "W0", to_np(grp.W0)[:, :lin.n], mg["W0"], 1e-5)
+        finally:
+            announce(f"merge group {lin.name}: {errs}")
         if grp.W0b is not None:  # the shadow is the merged W0 in the act dtype
             ref = torch.from_numpy(to_np(grp.W0)).to(grp.W0b.dtype)
             assert torch.equal(grp.W0b.cpu()[:, :lin.n], ref[:, :lin.n]), lin.name

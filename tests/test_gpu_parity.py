@@ -10,7 +10,8 @@ import pytest
 
 import oracle as O
 import poet_inputs as PI
-from tests.gpu_util import TOL, announce, gpu_linear, make_linear, oracle_indices, put_act, rel, to_np
+from tests.gpu_util import (TOL, announce, check, gpu_linear, make_linear, oracle_indices, put_act, rel,
+                            theta_groups, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,23 +47,25 @@ def run_case(lin, cfg_id=99, seed=7, pad=0, theta_std=PI.THETA_STD, check_merge=
     # primitives against the oracle's (padded) primitives
     for nm, side, th, prim in (("R", lin.R, tR, pl.primR), ("P", lin.P, tP, pl.primP)):
         ref = O.pack_prims(side.mode, side.d, side.b, O.build_orthogonal(side.mode, side.d, side.b, side.k, th))
-        e = rel(to_np(prim).reshape(ref.shape), ref)
-        out["prim" + nm] = e
-        assert e <= (1e-5 if side.dtype == PI.DT_F32 else 1e-4), (nm, e)
-    out["W"] = rel(to_np(W)[:, :lin.n], ref_f["W"])
-    out["Y"] = rel(to_np(Y)[:, :lin.m], ref_f["Y"]) if lin.T else 0.0
-    out["dX"] = rel(to_np(dX)[:, :lin.n], ref_b["dX"]) if lin.T else 0.0
-    out["dthetaR"] = rel(to_np(pl.dthetaR)[:len(tR)], ref_b["dthetaR"]) if len(tR) else 0.0
-    out["dthetaP"] = rel(to_np(pl.dthetaP)[:len(tP)], ref_b["dthetaP"]) if len(tP) else 0.0
-    for key in ("W", "Y", "dX", "dthetaR", "dthetaP"):
-        assert out[key] <= tol, (key, out[key], tol)
+        check(out, "prim" + nm, to_np(prim).reshape(ref.shape).ravel(), ref.ravel(),
+              1e-5 if side.dtype == PI.DT_F32 else 1e-4, [ref.shape[1] * ref.shape[2]] * ref.shape[0])
+    # both bars on every output: relative Frobenius error and the local bound per row / per primitive
+    check(out, "W", to_np(W)[:, :lin.n], ref_f["W"], tol)
+    if lin.T:
+        check(out, "Y", to_np(Y)[:, :lin.m], ref_f["Y"], tol)
+        check(out, "dX", to_np(dX)[:, :lin.n], ref_b["dX"], tol)
+    if len(tR):
+        check(out, "dthetaR", to_np(pl.dthetaR)[:len(tR)], ref_b["dthetaR"], tol,
+              theta_groups(lin.R.mode, lin.R.d, lin.R.b))
+    if len(tP):
+        check(out, "dthetaP", to_np(pl.dthetaP)[:len(tP)], ref_b["dthetaP"], tol,
+              theta_groups(lin.P.mode, lin.P.d, lin.P.b))
     if check_merge:
         shadow = pl.alloc_W()
         pl.merge(shadow=shadow)
         torch.cuda.synchronize()
         mg = O.merge(sR, sP, W0, tR, tP, iR, iP, seed, lin.linear_id, 1)
-        out["merge"] = rel(to_np(pl.W0)[:, :lin.n], mg["W0"])
-        assert out["merge"] <= 1e-5, out["merge"]  # the merge is float32 for every act dtype
+        check(out, "merge", to_np(pl.W0)[:, :lin.n], mg["W0"], 1e-5)  # the merge is float32 for every act dtype
         assert np.all(to_np(pl.thetaR) == 0) and np.all(to_np(pl.thetaP) == 0)
         if lin.R.mode == PI.MODE_FS:
             np.testing.assert_array_equal(pl.idxR.cpu().numpy(), mg["idxR"])

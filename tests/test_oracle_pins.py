@@ -163,6 +163,31 @@ def test_bs_assembly_blocks():
     np.testing.assert_array_equal(F, block_diag(*G))
 
 
+def test_pack_prims_padded_layout_by_hand():
+    # storage layout of the primitives: each one in a b x b slot, identity outside its c x c corner. Written out
+    # element by element for a side of d = 7 with b = 3 (blocks 3, 3, 1) and checked against the packing.
+    g0 = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0], [7.0, 8.0, 9.0]])
+    g1 = -g0.T
+    g2 = np.array([[0.5]])
+    want = np.array([
+        [[1, 2, 3], [4, 5, 6], [7, 8, 9]],
+        [[-1, -4, -7], [-2, -5, -8], [-3, -6, -9]],
+        [[0.5, 0, 0], [0, 1, 0], [0, 0, 1]],
+    ], dtype=np.float64)
+    np.testing.assert_array_equal(O.pack_prims(O.MODE_BS, 7, 3, [g0, g1, g2]), want)
+    # FS: one s x s primitive fills its slot exactly
+    np.testing.assert_array_equal(O.pack_prims(O.MODE_FS, 9, 3, [g0]), g0[None])
+    # the packed slots of built primitives hold the blocks of the assembled factor
+    th = np.random.default_rng(8).standard_normal(O.theta_len(O.MODE_BS, 7, 3)) * 0.1
+    prims = O.build_orthogonal(O.MODE_BS, 7, 3, 2, th)
+    F = O.assemble(O.MODE_BS, 7, prims)
+    packed = O.pack_prims(O.MODE_BS, 7, 3, prims)
+    np.testing.assert_array_equal(packed[0], F[0:3, 0:3])
+    np.testing.assert_array_equal(packed[1], F[3:6, 3:6])
+    assert packed[2, 0, 0] == F[6, 6] and np.array_equal(packed[2, 1:, 1:], np.eye(2))
+    assert not packed[2, 0, 1:].any() and not packed[2, 1:, 0].any()
+
+
 # ---------------------------------------------------------------- P6: gradients
 def _loss(sR, sP, W0, tR, tP, iR, iP, X, dY):
     return float(np.sum(dY * O.linear_fwd(sR, sP, W0, tR, tP, iR, iP, X)["Y"]))
