@@ -121,6 +121,9 @@ hipError_t launch_reduce_skew_group(const SkewGroup& g, int nsplit, hipStream_t 
 // prim += I + 2 Q + 2 (P_2 + .. + P_k) for the sides of a GEMM-built chain (prim holds P_{k+1} on entry)
 struct FinSide {
   const float* theta = nullptr; const void* powers = nullptr; float* prim = nullptr;
+  // q2 (nullable, float32, bp x bp per primitive): (2Q)^2 formed to float32 accuracy; when given it replaces the
+  // saved bf16 power Q^2 in the series, and for k == 1 prim holds no chain product to add
+  const float* q2 = nullptr;
   int mode = 0, d = 0, bp = 0, nprim = 0, k = 0, dt = BF16, ldp = 0;
 };
 struct FinGroup { int n = 0; FinSide s[MAXG]; };
@@ -238,9 +241,10 @@ hipError_t launch_split3(const float* src, int64_t ld_src, const int32_t* ridx, 
                          int sub_eye, int rows, int cols, int prows, int pcols, __bf16* dst, int64_t ld_dst,
                          int64_t tstride, int lo_mask, float* D, int64_t ld_d, hipStream_t st);
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1} with prim holding P_{k+1} on entry (k >= 1), Q from theta;
-// powers[t-1] = P_t as bp x ldp blocks
+// powers[t-1] = P_t as bp x ldp blocks. With q2 ((2Q)^2 in float32, bp x bp per primitive) the Q^2 term is q2 / 4
+// instead of P_2, and for k == 1 prim's entry value is not used (the series ends at Q^2).
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
-                                 int dt, int ldp, float* prim, hipStream_t st);
+                                 int dt, int ldp, float* prim, hipStream_t st, const float* q2 = nullptr);
 // out = bf16(prim - I) for nprim bp x bp primitives (the delta of a factor as an MFMA operand), written as bp x ldo
 // blocks with zero columns past bp
 hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf16* out, hipStream_t st);

@@ -480,7 +480,7 @@ __global__ __launch_bounds__(256) void k_chain_finalize(const FinGroup G) {
     const FinSide& t = G.s[blockIdx.z];
     a.theta = keep_s(t.theta); a.powers = keep_s(t.powers); a.prim = keep_s(t.prim); a.mode = keep_s(t.mode);
     a.d = keep_s(t.d); a.bp = keep_s(t.bp); a.nprim = keep_s(t.nprim); a.k = keep_s(t.k); a.dt = keep_s(t.dt);
-    a.ldp = keep_s(t.ldp);
+    a.ldp = keep_s(t.ldp); a.q2 = keep_s(t.q2);
   }
   const int bp = a.bp, p = blockIdx.y, nt = (bp + 31) / 32;
   if (p >= a.nprim || (int)blockIdx.x >= nt * (nt + 1) / 2) return;
@@ -500,10 +500,17 @@ __global__ __launch_bounds__(256) void k_chain_finalize(const FinGroup G) {
       const int i = ri * 32 + row0 + 8 * u, j = cj * 32 + col;
       if (i >= bp || j >= bp) continue;
       float s2 = 0.f;
-      for (int t = 2; t <= a.k; ++t)
+      for (int t = a.q2 ? 3 : 2; t <= a.k; ++t)
         s2 += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * a.nprim + p) * bp + i) * a.ldp + j);
       const int64_t e = (int64_t)i * bp + j;
-      prim[e] = (i == j ? 1.f : 0.f) + 2.f * (h ? lo[u] : up[u]) + 2.f * s2 + prim[e];
+      float v = (i == j ? 1.f : 0.f) + 2.f * (h ? lo[u] : up[u]) + 2.f * s2;
+      if (a.q2) {  // Q^2 = q2 / 4, coefficient 2 (k >= 2) or 1 (k == 1: the last term of the series)
+        v += (a.k >= 2 ? 0.5f : 0.25f) * a.q2[(int64_t)p * bp * bp + e];
+        if (a.k >= 2) v += prim[e];
+      } else {
+        v += prim[e];
+      }
+      prim[e] = v;
     }
   }
 }
@@ -519,7 +526,7 @@ hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st) {
     const FinSide& a = g.s[i];
     const int64_t total = (int64_t)a.nprim * a.bp * a.bp;
     most = std::max(most, total);
-    bytes += (double)total * (8 + 4 + (a.k - 1) * dtype_size(a.dt));
+    bytes += (double)total * (8 + 4 + (a.k - 1) * dtype_size(a.dt) + (a.q2 ? 4 : 0));
   }
   if (most == 0) return hipSuccess;
   int bp = 0, ny = 0;
@@ -532,10 +539,11 @@ hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st) {
 }
 
 hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, int nprim, int k, const void* powers,
-                                 int dt, int ldp, float* prim, hipStream_t st) {
+                                 int dt, int ldp, float* prim, hipStream_t st, const float* q2) {
   FinGroup g;
   g.n = 1;
   FinSide& a = g.s[0];
+  a.q2 = q2;
   a.theta = theta; a.powers = powers; a.prim = prim; a.mode = mode; a.d = d; a.bp = bp; a.nprim = nprim; a.k = k;
   a.dt = dt; a.ldp = ldp;
   return launch_chain_finalize_group(g, st);

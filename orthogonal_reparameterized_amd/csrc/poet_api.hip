@@ -827,6 +827,61 @@ std::vector<BuildChunk> build_chunks(const std::vector<SideInfo>& S, void* const
 // split-K scratch of a chunk's power products: up to 4 splits of every block
 size_t build_chunk_part_elems(const BuildChunk& c) { return 8 * c.prim_elems; }
 
+// split-K scratch of the build's power-chain GEMMs: bf16 sides the fused chain kernel does not take (FS, or BS
+// blocks above 256 or not a multiple of 8); room for up to 8 splits of one power
+size_t build_part_elems(const SideInfo& i) {
+  const bool gemm_chain = i.dtype == BF16 && i.k > 0 && !(i.ldp == i.bp && i.bp <= 256 && i.bp % 8 == 0);
+  return gemm_chain ? 8 * i.prim_len : 0;
+}
+
+// Accurate square term of a bf16 chain that runs as separate products. The bf16 chain rounds Q to bf16 as a product
+// operand and keeps Q^2 in bf16: two relative errors of 2^-9 on the series' largest term beyond the linear one, which
+// the float32 merge then folds into W0 (about 7e-6 relative on a merged LLaMA-1.3B weight at s = 1024 and 2e-5 at
+// s = 2730). So (2Q)^2 is formed to float32 accuracy from three bf16 parts of 2Q = prim - I (exact in float32 after
+// theta_prep): hi = bf16(x), lo = bf16(x - hi), stacked along K as [hi | hi | lo] times [hi ; lo ; hi], one bf16
+// product with K = 3 ldp giving hi*hi + hi*lo + lo*hi. The chain finalize takes it in place of the saved P_2;
+// the bf16 powers still serve the higher terms and the adjoint.
+bool sq_side(const SideInfo& S) { return build_part_elems(S) > 0; }
+struct SqBufs {
+  __bf16* A3 = nullptr;  // per primitive bp x 3 ldp (K-major left operand)
+  __bf16* B3 = nullptr;  // per primitive 3 ldp x ldp (rows of the right operand)
+  float* q2 = nullptr;   // per primitive bp x bp
+};
+void plan_sq(Arena& a, const SideInfo& S, SqBufs* b) {
+  const size_t np = S.nprim, bp = S.bp, lp = S.ldp;
+  b->A3 = a.take<__bf16>(np * bp * 3 * lp);
+  b->B3 = a.take<__bf16>(np * 3 * lp * lp);
+  b->q2 = a.take<float>(np * bp * bp);
+}
+size_t sq_bytes(const SideInfo& S) {
+  Arena a(nullptr);
+  SqBufs b;
+  plan_sq(a, S, &b);
+  return a.used();
+}
+// the three-part operands of 2Q = prim - I, block by block (the identity is subtracted on each block's diagonal)
+hipError_t sq_split(const SideInfo& S, const float* prim, const SqBufs& b, hipStream_t st) {
+  const int bp = S.bp, lp = S.ldp;
+  for (int p = 0; p < S.nprim; ++p) {
+    const float* src = prim + (int64_t)p * bp * bp;
+    HIP_RET(launch_split3(src, bp, nullptr, nullptr, bp, bp, 1, bp, bp, bp, lp, b.A3 + (int64_t)p * bp * 3 * lp,
+                          3 * lp, lp, 0b100, nullptr, 0, st));
+    HIP_RET(launch_split3(src, bp, nullptr, nullptr, bp, bp, 1, bp, bp, lp, lp, b.B3 + (int64_t)p * 3 * lp * lp, lp,
+                          (int64_t)lp * lp, 0b010, nullptr, 0, st));
+  }
+  return hipSuccess;
+}
+GemmDesc sq_gemm(const SideInfo& S, const SqBufs& b, float* part, size_t part_elems) {
+  GemmDesc g;
+  g.kclass = POET_K_CHAIN;
+  g.compute = BF16; g.M = g.N = S.bp; g.K = 3 * S.ldp; g.batch = S.nprim;
+  g.A = b.A3; g.lda = 3 * S.ldp; g.sA = (int64_t)S.bp * 3 * S.ldp; g.a_dt = BF16; g.a_kmajor = 1;
+  g.B = b.B3; g.ldb = S.ldp; g.sB = (int64_t)3 * S.ldp * S.ldp; g.b_dt = BF16; g.b_kmajor = 0;
+  g.C = b.q2; g.c_dt = F32; g.ldc = S.bp; g.sC = (int64_t)S.bp * S.bp;
+  g.part = part; g.part_elems = part_elems;
+  return g;
+}
+
 // adjoint chunks: sides sharing (bp, k) whose adjoint runs on the fused chain, at most MAXG per chunk
 // fused: the H chain runs on the fused chain kernel (blocks <= 256, ldp = bp); otherwise as grouped GEMMs (ldp >= bp)
 struct AdjChunk {
@@ -1011,20 +1066,14 @@ size_t poet_powers_len(const poet_side* s) {
   SideInfo i;
   return side_info(s, &i, "side") ? i.powers_len : 0;
 }
-// split-K scratch of the build's power-chain GEMMs: bf16 sides the fused chain kernel does not take (FS, or BS
-// blocks above 256 or not a multiple of 8); room for up to 8 splits of one power
-size_t build_part_elems(const SideInfo& i) {
-  const bool gemm_chain = i.dtype == BF16 && i.k > 0 && !(i.ldp == i.bp && i.bp <= 256 && i.bp % 8 == 0);
-  return gemm_chain ? 8 * i.prim_len : 0;
-}
-
 size_t poet_build_workspace_bytes(const poet_side* s, int with_powers) {
   SideInfo i;
   if (!side_info(s, &i, "side")) return 0;
   if (i.k == 0) return 0;
   const size_t pw = with_powers ? 0 : align_up(i.powers_len * dtype_size(i.dtype), 256);
   const size_t part = build_part_elems(i) * sizeof(float);
-  return pw + part == 0 ? 0 : pw + part + 512;
+  const size_t sq = sq_side(i) ? sq_bytes(i) : 0;
+  return pw + part == 0 ? 0 : pw + part + sq + 512;
 }
 size_t poet_sample_workspace_bytes(int32_t d) { return d > 0 ? align_up((size_t)d * 4, 256) + 256 : 0; }
 
@@ -1059,6 +1108,8 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   if (!powers && S.k > 0) pw = reinterpret_cast<char*>(a.take_bytes(S.powers_len * esz));
   const size_t part_elems = build_part_elems(S);
   float* part = part_elems ? a.take<float>(part_elems) : nullptr;
+  SqBufs sq;
+  if (sq_side(S)) plan_sq(a, S, &sq);
   if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
   // prim = I + coef Q (coef 2 for k >= 1) with Q exact from theta, and the first saved power Q
   HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype,
@@ -1075,7 +1126,13 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   if (S.k == 0) return POET_OK;  // R_0 = I + Q
   const int64_t pp = (int64_t)S.bp * S.bp;
   const int64_t ps = (int64_t)S.bp * S.ldp;
-  for (int i = 1; i <= S.k; ++i) {  // P_{i+1} = Q P_i; the last power goes straight into prim (float32)
+  if (sq.q2) {  // (2Q)^2 to float32 accuracy while prim still holds I + 2Q
+    HIP_TRY(sq_split(S, prim, sq, st));
+    HIP_TRY(launch_gemm(sq_gemm(S, sq, part, part_elems), st));
+  }
+  // P_{i+1} = Q P_i; the last power goes straight into prim (float32). With the accurate square and k == 1 the series
+  // ends at Q^2 and no chain product is needed.
+  for (int i = 1; i <= S.k && !(sq.q2 && S.k == 1); ++i) {
     GemmDesc g;
     g.kclass = POET_K_CHAIN;
     g.compute = S.dtype; g.M = g.N = g.K = S.bp; g.batch = S.nprim;
@@ -1086,8 +1143,8 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
     g.part = part; g.part_elems = part_elems;
     HIP_TRY(launch_gemm(g, st));
   }
-  // prim = I + 2Q + 2(P_2 + ... + P_k) + P_{k+1}, the linear term exact from theta
-  HIP_TRY(launch_chain_finalize(theta, S.mode, S.d, S.bp, S.nprim, S.k, pw, S.dtype, S.ldp, prim, st));
+  // prim = I + 2Q + 2(P_2 + ... + P_k) + P_{k+1}, the linear term exact from theta (P_2 from q2 when formed)
+  HIP_TRY(launch_chain_finalize(theta, S.mode, S.d, S.bp, S.nprim, S.k, pw, S.dtype, S.ldp, prim, st, sq.q2));
   return POET_OK;
 }
 
@@ -1641,7 +1698,11 @@ size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
   if (!group_sides(count, sides, &S)) return 0;
   size_t need = 0;
   for (int i = 0; i < count; ++i) need = std::max(need, poet_build_workspace_bytes(&sides[i], 1));
-  for (const auto& c : build_chunks(S, nullptr)) need = std::max(need, build_chunk_part_elems(c) * sizeof(float) + 512);
+  for (const auto& c : build_chunks(S, nullptr)) {
+    size_t sq = 0;
+    for (int i : c.idx) sq += sq_bytes(S[i]);
+    need = std::max(need, build_chunk_part_elems(c) * sizeof(float) + sq + 512);
+  }
   return need;
 }
 
@@ -1700,7 +1761,22 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     const size_t part_elems = build_chunk_part_elems(c);
     float* part = a.take<float>(part_elems);
     const int n = (int)c.idx.size();
-    for (int step = 1; step <= c.k; ++step) {
+    // (2Q)^2 of every side to float32 accuracy (prim holds I + 2Q after the theta launch), one grouped product
+    std::vector<SqBufs> sq(n);
+    {
+      GemmDesc pr[MAXG];
+      for (int u = 0; u < n; ++u) {
+        plan_sq(a, S[c.idx[u]], &sq[u]);
+        HIP_TRY(sq_split(S[c.idx[u]], prim[c.idx[u]], sq[u], st));
+        pr[u] = sq_gemm(S[c.idx[u]], sq[u], part, part_elems);
+      }
+      if (fast_gemm_group_eligible(pr, n)) {
+        HIP_TRY(launch_fast_gemm_group(pr, n, st));
+      } else {
+        for (int u = 0; u < n; ++u) HIP_TRY(launch_gemm(pr[u], st));
+      }
+    }
+    for (int step = 1; step <= c.k && c.k > 1; ++step) {  // k == 1: the series ends at the accurate Q^2
       GemmDesc pr[MAXG];
       for (int u = 0; u < n; ++u) {
         const int i = c.idx[u];
@@ -1724,8 +1800,10 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
       }
     }
     FinGroup fg;
-    for (int i : c.idx) {
+    for (int u = 0; u < n; ++u) {
+      const int i = c.idx[u];
       FinSide& f = fg.s[fg.n++];
+      f.q2 = sq[u].q2;
       f.theta = theta[i]; f.powers = powers[i]; f.prim = prim[i]; f.mode = S[i].mode; f.d = S[i].d; f.bp = S[i].bp;
       f.nprim = S[i].nprim; f.k = S[i].k; f.dt = S[i].dtype; f.ldp = S[i].ldp;
     }
