@@ -70,6 +70,7 @@ enum { POET_OP_BUILD = 0, POET_OP_FWD = 1, POET_OP_BWD = 2, POET_OP_MERGE = 3, P
 /* Maximum supported Neumann terms and primitive size (a primitive must fit the kernels' tiling). */
 #define POET_MAX_K 16
 #define POET_MAX_PRIM 8192
+#define POET_NOALLOC_MAX_D 65536
 
 /* One orthogonal factor. mode: POET_BS or POET_FS. d: its dimension (m for R, n for P).
  * b: BS block size (1 <= b <= d) or FS sample count s (1 <= s <= d). k: Neumann terms, 0 <= k <= POET_MAX_K.
@@ -131,6 +132,16 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
  * Bit-exact and deterministic. ws: at least poet_sample_workspace_bytes(d) bytes. */
 poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
                                 uint32_t epoch, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* poet_sample_indices for callers that cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight loops, harnesses that forbid allocation): the same index set, bit for bit, with the per-index
+ * scratch taken from a device array inside the library (d * 4 bytes of POET_NOALLOC_MAX_D * 4; each GPU the
+ * library runs on holds its own copy until the process ends). d > POET_NOALLOC_MAX_D gives POET_E_SHAPE before any
+ * launch. Calls on one GPU share that scratch: calls that overlap in time on one GPU (different streams, other
+ * threads) race and give unspecified index sets; calls ordered on one stream are safe. Allocates nothing and
+ * launches only kernels. */
+poet_status poet_sample_indices_noalloc(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
+                                        uint32_t epoch, int32_t* idx, void* stream);
 
 /* Forward of one POET linear (one-line method summary: W = R W0 P): materializes W (act dtype) and
  * computes Y = X W^T.

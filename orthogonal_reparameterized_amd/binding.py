@@ -30,7 +30,9 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
            "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
-           "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group")
+           "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group",
+           "poet_sample_indices_noalloc")
+POET_NOALLOC_MAX_D = 65536  # largest d poet_sample_indices_noalloc accepts (its device scratch holds d int32 flags)
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE, POET_K_GATHER = range(10)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge",
@@ -93,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.poet_build_workspace_bytes.restype = S
     L.poet_build_orthogonal.argtypes = [P(poet_side), VP, VP, VP, VP, VP, S, VP]
     L.poet_sample_indices.argtypes = [I32, I32, U64, U32, U32, U32, VP, VP, S, VP]
+    L.poet_sample_indices_noalloc.argtypes = [I32, I32, U64, U32, U32, U32, VP, VP]
     L.poet_linear_fwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_merge.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, U64, U32, U32, VP, S, VP]
@@ -118,8 +121,8 @@ def lib() -> ctypes.CDLL:
     L.poet_merge_group_workspace_bytes.restype = S
     L.poet_merge_group.argtypes = [I32, P(poet_layer), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), P(VP), U64,
                                    P(U32), U32, VP, S, VP]
-    for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge",
-               "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act"):
+    for nm in ("poet_build_orthogonal", "poet_sample_indices", "poet_sample_indices_noalloc", "poet_linear_fwd",
+               "poet_linear_bwd", "poet_merge", "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act"):
         getattr(L, nm).restype = ctypes.c_int
     L.poet_status_string.argtypes = [ctypes.c_int]
     L.poet_status_string.restype = ctypes.c_char_p
@@ -288,6 +291,15 @@ def poet_sample_indices(d: int, s: int, seed: int, linear_id: int, side_id: int,
     st = lib().poet_sample_indices(d, s, seed, linear_id, side_id, epoch, _ptr(idx, "idx", 4 * s, "int32"),
                                    _ptr(ws, "ws", need), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_sample_indices")
+
+
+def poet_sample_indices_noalloc(d: int, s: int, seed: int, linear_id: int, side_id: int, epoch: int, idx,
+                                stream=None):
+    """poet_sample_indices without a workspace (the library's own device scratch; d <= POET_NOALLOC_MAX_D).
+    Calls that overlap on one GPU share that scratch and race."""
+    st = lib().poet_sample_indices_noalloc(d, s, seed, linear_id, side_id, epoch, _ptr(idx, "idx", 4 * s, "int32"),
+                                           _stream(stream))
+    _check(st, "poet_sample_indices_noalloc")
 
 
 def _layer_bytes(L: poet_layer):

@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1047,6 +1048,32 @@ bool check_idx(const SideInfo& S, const void* idx, const char* name) {
 
 }  // namespace
 
+// ---- allocation-free sampler ----------------------------------------------------------------------------
+// The sampler's per-index flags live in a file-scope device array instead of a caller workspace. Each device holds
+// its own copy of the array at its own address, looked up once per device with the device current and kept; kernels
+// only ever see that address (the array's name is a host-side stand-in in host code).
+static __device__ __align__(256) int32_t scratch[POET_NOALLOC_MAX_D];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device id; nullptr until looked up
+
+hipError_t scratch_address(int32_t** out) {
+  int dev = 0;
+  HIP_RET(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_RET(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = reinterpret_cast<int32_t*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+}  // namespace
+
 // ============================================================================================================
 extern "C" {
 
@@ -1155,6 +1182,21 @@ poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t li
   if (!check_ws(ws, ws_bytes, poet_sample_workspace_bytes(d))) return g_last;
   Arena a(ws);
   int32_t* flags = a.take<int32_t>((size_t)d);
+  HIP_TRY(launch_sample(d, s, sampler_hash(seed, linear_id, side, epoch), flags, idx,
+                        reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
+poet_status poet_sample_indices_noalloc(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
+                                        uint32_t epoch, int32_t* idx, void* stream) {
+  if (d < 1 || s < 0 || s > d) return fail(POET_E_SHAPE, "need d >= 1 and 0 <= s <= d (d=%d s=%d)", d, s);
+  if (d > POET_NOALLOC_MAX_D)
+    return fail(POET_E_SHAPE, "d = %d exceeds the allocation-free sampler's maximum %d (use poet_sample_indices)", d,
+                POET_NOALLOC_MAX_D);
+  if (!idx && s > 0) return fail(POET_E_ARG, "null idx");
+  int32_t* flags = nullptr;
+  HIP_TRY(scratch_address(&flags));
+  // every flag of [0, d) is written by the ranking kernel before the compaction reads it: nothing to clear
   HIP_TRY(launch_sample(d, s, sampler_hash(seed, linear_id, side, epoch), flags, idx,
                         reinterpret_cast<hipStream_t>(stream)));
   return POET_OK;
