@@ -25,9 +25,10 @@ Everything is float64 NumPy. Matrix products use ``@`` (a library GEMM) as plain
 reordering is done beyond what the definitions state.
 
 Parity status: every function here is pinned by tests against closed forms, textbook routines, finite
-differences or values printed on the pages, except the FS index sampler's specific draws (the pages name no
-random generator; see ``sample_indices``) and the block-size remainder reading (see ``block_sizes``), which are
-"parity unpinned" beyond their structural invariants.
+differences, an independent library implementation (AdamW) or values printed on the pages, except the FS index
+sampler's specific draws (the pages name no random generator; see ``sample_indices``), the block-size remainder
+reading (see ``block_sizes``) and the optimizer state across a merge (see ``optimizer_state_after_merge``), which
+are "parity unpinned" beyond their structural invariants.
 """
 from __future__ import annotations
 
@@ -315,3 +316,100 @@ def merge(sR: Side, sP: Side, W0, thetaR, thetaP, idxR, idxP, seed: int, linear_
     if sP.mode == MODE_FS:
         out["idxP"] = sample_indices(sP.d, sP.b, seed, linear_id, SIDE_P, epoch_next)
     return out
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Optimizer step on the skew parameters, and its state across a merge
+# ----------------------------------------------------------------------------------------------------------
+
+def adamw_step(theta, grad, m, v, step: int, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float):
+    """One AdamW update of packed skew parameters (Loshchilov and Hutter, "Decoupled Weight Decay
+    Regularization", ICLR 2019), written out from its definition:
+
+        m_t = beta1 m_{t-1} + (1 - beta1) g            first moment
+        v_t = beta2 v_{t-1} + (1 - beta2) g^2          second moment
+        m^  = m_t / (1 - beta1^t),  v^ = v_t / (1 - beta2^t)
+        theta_t = theta_{t-1} - lr (m^ / (sqrt(v^) + eps) + weight_decay theta_{t-1})
+
+    with t = step >= 1 counted from the last reset. The pages train R and P through their skew generators
+    (Approach section) and compare against AdamW (Key results) but do not name the optimizer of the generators.
+    Reading: AdamW, elementwise on the packed parameters. Returns (theta_t, m_t, v_t) in float64.
+    """
+    if step < 1:
+        raise ValueError("step counts from 1")
+    theta = np.asarray(theta, dtype=np.float64)
+    g = np.asarray(grad, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** step)
+    vhat = v / (1.0 - beta2 ** step)
+    theta = theta - lr * (mhat / (np.sqrt(vhat) + eps) + weight_decay * theta)
+    return theta, m, v
+
+
+def optimizer_state_after_merge(m, v):
+    """Moments and step count of the skew parameters after merge-then-reinitialize.
+
+    The pages reset the generators at each merge and, for POET-FS, resample which index pairs they act on
+    (Approach section); they say nothing of the optimizer state. Reading: the moments are reinitialized with the
+    parameters (zero, and the bias-correction count restarts at 0), since after the merge a parameter describes a
+    rotation about a new reference W0 and, for POET-FS, a different index pair."""
+    return np.zeros(len(m)), np.zeros(len(v)), 0
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Exact Cayley primitives (the map the truncated series approximates)
+# ----------------------------------------------------------------------------------------------------------
+
+def build_orthogonal_exact(mode: int, d: int, b: int, theta: np.ndarray) -> List[np.ndarray]:
+    """All primitives of one side through the exact Cayley map (I + Q)(I - Q)^{-1} of their skew generators: the
+    limit k -> infinity of the truncated series, used as an accuracy reference ("Builds on ... Cayley
+    parameterization", Experimental setup)."""
+    theta = np.asarray(theta, dtype=np.float64)
+    out, off = [], 0
+    for c in block_sizes(mode, d, b):
+        nt = c * (c - 1) // 2
+        out.append(cayley_exact(skew_from_theta(theta[off:off + nt], c)))
+        off += nt
+    return out
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Spectral diagnostics of a weight (Experimental setup, Metrics: hyperspherical energy, singular-value entropy)
+# ----------------------------------------------------------------------------------------------------------
+
+def hyperspherical_energy(W, s: float = 1.0) -> float:
+    """Hyperspherical energy of the neurons of W (Liu et al., "Learning towards Minimum Hyperspherical Energy",
+    NeurIPS 2018): with w^_i the rows of W scaled to unit norm (one row per output neuron),
+
+        E_s = sum over ordered pairs i != j of ||w^_i - w^_j||^(-s)      (s > 0).
+
+    The pages name the metric without its parameters. Reading: s = 1, rows as neurons, the plain sum over ordered
+    pairs (no normalization)."""
+    return float(np.sum(hyperspherical_energy_rows(W, s)))
+
+
+def hyperspherical_energy_rows(W, s: float = 1.0, rows=None) -> np.ndarray:
+    """Per-neuron terms of the hyperspherical energy: E_i = sum over j != i of ||w^_i - w^_j||^(-s), for the
+    neurons i in `rows` (all by default); E_s is their sum over all i."""
+    W = np.asarray(W, dtype=np.float64)
+    Wn = W / np.linalg.norm(W, axis=1, keepdims=True)
+    rows = range(Wn.shape[0]) if rows is None else rows
+    out = []
+    for i in rows:
+        dist = np.linalg.norm(Wn[i][None, :] - Wn, axis=1)
+        dist[i] = np.inf  # the pair (i, i) is excluded
+        out.append(float(np.sum(dist ** (-s))))
+    return np.asarray(out)
+
+
+def singular_value_entropy(W) -> float:
+    """Shannon entropy of the normalized singular values of W (Roy and Vetterli, "The effective rank", EUSIPCO
+    2007): p_i = sigma_i / sum_j sigma_j, H = -sum_i p_i log p_i (natural log, 0 log 0 = 0). The singular values
+    come from LAPACK's SVD. Reading: the pages name the metric only; the effective-rank normalization by the sum
+    of the singular values is taken."""
+    sig = np.linalg.svd(np.asarray(W, dtype=np.float64), compute_uv=False)
+    p = sig / sig.sum()
+    p = p[p > 0]
+    return float(-np.sum(p * np.log(p)))

@@ -9,7 +9,7 @@ import oracle as O
 import oracle.poet_oracle as PO
 import tests.test_oracle_pins as pins
 
-_ORIG = {f: getattr(PO, f) for f in ("neumann_adjoint", "linear_bwd", "assemble", "sample_indices")}
+_ORIG = {f: getattr(PO, f) for f in ("neumann_adjoint", "linear_bwd", "assemble", "sample_indices", "adamw_step")}
 
 
 def _cn_drop_last(Q, k):
@@ -83,6 +83,43 @@ def _sampler_descending(d, s, seed, linear_id, side, epoch):
     return _ORIG["sample_indices"](d, s, seed, linear_id, side, epoch)[::-1].copy()
 
 
+def _adamw_no_bias_correction(theta, grad, m, v, step, lr, beta1, beta2, eps, weight_decay):
+    theta = np.asarray(theta, float)
+    m = beta1 * np.asarray(m, float) + (1 - beta1) * grad
+    v = beta2 * np.asarray(v, float) + (1 - beta2) * grad * grad
+    return theta - lr * (m / (np.sqrt(v) + eps) + weight_decay * theta), m, v
+
+
+def _adamw_coupled_decay(theta, grad, m, v, step, lr, beta1, beta2, eps, weight_decay):
+    # L2 regularization folded into the gradient (Adam with weight decay) instead of the decoupled decay
+    g = np.asarray(grad, float) + weight_decay * np.asarray(theta, float)
+    return _ORIG["adamw_step"](theta, g, m, v, step, lr, beta1, beta2, eps, 0.0)
+
+
+def _cayley_exact_inverted(Q):
+    I = np.eye(Q.shape[0])
+    return (I - Q) @ np.linalg.solve(I + Q, I)
+
+
+def _he_rows_columns_normalized(W, s=1.0, rows=None):
+    W = np.asarray(W, float)
+    Wn = W / np.linalg.norm(W, axis=0, keepdims=True)  # wrong axis
+    rows = range(Wn.shape[0]) if rows is None else rows
+    out = []
+    for i in rows:
+        dist = np.linalg.norm(Wn[i][None, :] - Wn, axis=1)
+        dist[i] = np.inf
+        out.append(float(np.sum(dist ** (-s))))
+    return np.asarray(out)
+
+
+def _sv_entropy_squared(W):
+    sig = np.linalg.svd(np.asarray(W, float), compute_uv=False) ** 2  # energy, not the singular values
+    p = sig / sig.sum()
+    p = p[p > 0]
+    return float(-np.sum(p * np.log(p)))
+
+
 MUTATIONS = {
     "neumann_drops_last_term": ("cayley_neumann", _cn_drop_last,
                                 [lambda: pins.test_2x2_distance_to_rotation(0.3, 2),
@@ -105,6 +142,18 @@ MUTATIONS = {
                             [lambda: pins.test_fs_assembly_is_permuted_block()]),
     "sampler_order": ("sample_indices", _sampler_descending,
                       [lambda: pins.test_sampler_structure(64, 32)]),
+    "adamw_no_bias_correction": ("adamw_step", _adamw_no_bias_correction,
+                                 [lambda: pins.test_adamw_matches_torch_reference(),
+                                  lambda: pins.test_adamw_first_step_closed_form()]),
+    "adamw_coupled_decay": ("adamw_step", _adamw_coupled_decay,
+                            [lambda: pins.test_adamw_matches_torch_reference(),
+                             lambda: pins.test_adamw_first_step_closed_form()]),
+    "cayley_exact_inverted": ("cayley_exact", _cayley_exact_inverted,
+                              [lambda: pins.test_exact_cayley_2x2_is_rotation(0.3)]),
+    "he_wrong_normalization": ("hyperspherical_energy_rows", _he_rows_columns_normalized,
+                               [lambda: pins.test_hyperspherical_energy_closed_forms()]),
+    "sv_entropy_of_energies": ("singular_value_entropy", _sv_entropy_squared,
+                               [lambda: pins.test_singular_value_entropy_closed_forms()]),
 }
 
 

@@ -349,3 +349,112 @@ def test_sampler_uniform_inclusion():
     chi2 = np.sum((counts - E * p) ** 2 / (E * p * (1 - p)))
     from scipy.stats import chi2 as chi2d
     assert chi2 < chi2d.ppf(0.9999, d - 1)
+
+
+# ---------------------------------------------------------------- optimizer on the skew parameters
+def test_adamw_matches_torch_reference():
+    # an independent implementation: torch.optim.AdamW on the CPU in float64, several steps with fresh gradients
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    n = 37
+    hp = dict(lr=3e-3, beta1=0.85, beta2=0.98, eps=1e-7, weight_decay=0.05)
+    theta = rng.standard_normal(n) * 1e-3
+    t = torch.tensor(theta.copy(), dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.AdamW([t], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    m, v = np.zeros(n), np.zeros(n)
+    for step in range(1, 7):
+        g = rng.standard_normal(n) * (10.0 ** -step)
+        t.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        theta, m, v = O.adamw_step(theta, g, m, v, step, **hp)
+        np.testing.assert_allclose(theta, t.detach().numpy(), rtol=1e-12, atol=1e-15)
+        st = opt.state[t]
+        np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-12, atol=0)
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=0)
+
+
+def test_adamw_first_step_closed_form():
+    # from zero moments the bias corrections give m^ = g and v^ = g^2: the first step moves each parameter by
+    # lr * g / (|g| + eps) (plus the decoupled decay lr * wd * theta), whatever beta1 and beta2 are
+    g = np.array([2.0, -0.5, 1e-3, 0.0])
+    th = np.array([0.1, 0.2, -0.3, 0.4])
+    for b1, b2 in ((0.9, 0.999), (0.5, 0.7)):
+        out, m, v = O.adamw_step(th, g, np.zeros(4), np.zeros(4), 1, 0.01, b1, b2, 1e-8, 0.1)
+        want = th - 0.01 * (g / (np.abs(g) + 1e-8) + 0.1 * th)
+        np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-17)
+        np.testing.assert_allclose(m, (1 - b1) * g)
+        np.testing.assert_allclose(v, (1 - b2) * g * g)
+
+
+def test_optimizer_state_reset_at_merge():
+    m, v, step = O.optimizer_state_after_merge(np.ones(5), np.ones(5))
+    assert step == 0 and not m.any() and not v.any() and len(m) == len(v) == 5
+
+
+# ---------------------------------------------------------------- exact Cayley primitives
+@pytest.mark.parametrize("t", [0.3, -1.7])
+def test_exact_cayley_2x2_is_rotation(t):
+    # (I + Q)(I - Q)^{-1} for Q = [[0, t], [-t, 0]] is the rotation by 2 atan(t), in closed form
+    prims = O.build_orthogonal_exact(O.MODE_BS, 2, 2, np.array([t]))
+    c, s_ = (1 - t * t) / (1 + t * t), 2 * t / (1 + t * t)
+    np.testing.assert_allclose(prims[0], [[c, s_], [-s_, c]], rtol=0, atol=1e-15)
+
+
+def test_exact_cayley_orthogonal_and_limit():
+    rng = np.random.default_rng(12)
+    th = rng.standard_normal(O.theta_len(O.MODE_BS, 13, 5)) * 0.05
+    ex = O.build_orthogonal_exact(O.MODE_BS, 13, 5, th)
+    tr = O.build_orthogonal(O.MODE_BS, 13, 5, 40, th)
+    for a, b in zip(ex, tr):
+        np.testing.assert_allclose(a.T @ a, np.eye(a.shape[0]), atol=1e-14)
+        np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+# ---------------------------------------------------------------- spectral diagnostics
+def test_hyperspherical_energy_closed_forms():
+    # orthonormal neurons: every pair at distance sqrt 2, so E_1 = N (N - 1) / sqrt 2
+    Qm, _ = np.linalg.qr(np.random.default_rng(2).standard_normal((9, 9)))
+    assert O.hyperspherical_energy(Qm[:6] * 3.0) == pytest.approx(6 * 5 / np.sqrt(2), rel=1e-13)
+    # two antipodal neurons: distance 2 both ways, E_1 = 1/2 + 1/2; E_2 = 1/4 + 1/4
+    W = np.array([[1.0, 2.0], [-2.0, -4.0]])
+    assert O.hyperspherical_energy(W) == pytest.approx(1.0, rel=1e-14)
+    assert O.hyperspherical_energy(W, s=2.0) == pytest.approx(0.5, rel=1e-14)
+    # three neurons at 120 degrees in a plane: distances sqrt 3, E_1 = 6 / sqrt 3
+    a = 2 * np.pi / 3
+    W = np.array([[1, 0, 0], [np.cos(a), np.sin(a), 0], [np.cos(2 * a), np.sin(2 * a), 0]]) * [[1.0], [5.0], [0.2]]
+    assert O.hyperspherical_energy(W) == pytest.approx(6 / np.sqrt(3), rel=1e-13)
+
+
+def test_hyperspherical_energy_invariances():
+    # row scaling and an orthogonal factor on the input side (W0 P) leave every neuron's distances unchanged
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((12, 7))
+    P = O.cayley_exact(O.skew_from_theta(rng.standard_normal(21) * 0.3, 7))
+    e = O.hyperspherical_energy_rows(W)
+    np.testing.assert_allclose(O.hyperspherical_energy_rows(W @ P), e, rtol=1e-12)
+    np.testing.assert_allclose(O.hyperspherical_energy_rows(W * rng.uniform(0.1, 9, (12, 1))), e, rtol=1e-12)
+    np.testing.assert_allclose(O.hyperspherical_energy_rows(W, rows=[3, 0]), e[[3, 0]], rtol=0)
+    assert O.hyperspherical_energy(W) == pytest.approx(e.sum(), rel=1e-15)
+
+
+def test_singular_value_entropy_closed_forms():
+    n = 8
+    Qm, _ = np.linalg.qr(np.random.default_rng(3).standard_normal((n, n)))
+    assert O.singular_value_entropy(2.5 * Qm) == pytest.approx(np.log(n), rel=1e-13)  # flat spectrum
+    u, v = np.arange(1.0, 6.0), np.arange(2.0, 5.0)
+    assert O.singular_value_entropy(np.outer(u, v)) == pytest.approx(0.0, abs=1e-7)  # rank one
+    # singular values 1, 2, 3 (a diagonal matrix with signs and a permutation): p = 1/6, 2/6, 3/6
+    D = np.zeros((4, 3))
+    D[2, 0], D[0, 1], D[1, 2] = -3.0, 1.0, 2.0
+    p = np.array([1, 2, 3]) / 6
+    assert O.singular_value_entropy(D) == pytest.approx(-np.sum(p * np.log(p)), rel=1e-13)
+
+
+def test_singular_value_entropy_is_orthogonally_invariant():
+    # the spectrum claim: R W0 P with exactly orthogonal factors keeps every singular value, hence the entropy
+    rng = np.random.default_rng(6)
+    W0 = rng.standard_normal((9, 6))
+    R = O.cayley_exact(O.skew_from_theta(rng.standard_normal(36) * 0.4, 9))
+    P = O.cayley_exact(O.skew_from_theta(rng.standard_normal(15) * 0.4, 6))
+    assert O.singular_value_entropy(R @ W0 @ P) == pytest.approx(O.singular_value_entropy(W0), rel=1e-13)
