@@ -1,6 +1,7 @@
 #!/usr/bin/env python3
-"""Throughput of the POET layer on one MI355X: one step = build R and P, forward, and backward to the skew
-parameters for every linear of a LLaMA-shaped block, with merge-then-reinitialize amortized over its period.
+"""Throughput of the POET layer on one MI355X: one step = build R and P, forward, backward to the skew
+parameters and the AdamW update of them, for every linear of a LLaMA-shaped block, with merge-then-reinitialize
+amortized over its period.
 
 Prints one JSON line: whole-job tokens/s (inputs resident in HBM), the roofline of the dominant kernel measured
 live with HIP events on the launch stream, and the CPU oracle timed on a bounded sample of the same workload.
@@ -50,7 +51,19 @@ def build_block(wl, torch, B, PI, PoetLinear, path="auto", layer=0):
     return lins
 
 
-def step(lins, group=None):
+# AdamW on the skew parameters, as a training step takes it (a small learning rate keeps the generators in the
+# Neumann series' convergence range over the benchmark's few dozen steps; timing does not depend on the values)
+OPTIMIZER = dict(lr=1e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def optimizer():
+    from orthogonal_reparameterized_amd import binding as B
+    return B.adamw(**OPTIMIZER)
+
+
+def step(lins, group=None, hp=None):
+    """One training step of the block: build R and P, forward, backward to the skew parameters, AdamW update."""
+    hp = optimizer() if hp is None else hp
     if group is not None:  # the block's per-side steps in shared launches: build, then per linear, then adjoint
         group.build()
         for e in lins:
@@ -62,6 +75,7 @@ def step(lins, group=None):
                 pl.forward(e["X"], e["Y"], W_out=e["keep"])
                 pl.backward_prims(e["X"], e["dY"], e["dX"], W=e["keep"])
         group.finish_backward()
+        group.optimizer_step(hp)
         return
     for e in lins:
         pl = e["pl"]
@@ -72,6 +86,7 @@ def step(lins, group=None):
         else:
             pl.forward(e["X"], e["Y"], W_out=e["keep"])
             pl.backward(e["X"], e["dY"], e["dX"], W=e["keep"])
+        pl.optimizer_step(hp)
 
 
 def measured_traffic(tag: str):
@@ -119,6 +134,7 @@ def cpu_baseline(wl, budget_s: float = 25.0):
     at the full token count, in order, until the time budget is spent. If it stops early, the block time is
     extrapolated from the linears done by the block's sum of m*n (and the sample string says so). A stack of
     several layers is timed on one layer and multiplied by the layer count (also said in the sample string)."""
+    import numpy as np
     import oracle as O
     import poet_inputs as PI
     try:
@@ -135,7 +151,9 @@ def cpu_baseline(wl, budget_s: float = 25.0):
         sR, sP = O.Side.of(q.R), O.Side.of(q.P)
         t0 = time.perf_counter()
         O.linear_fwd(sR, sP, W0, tR, tP, iR, iP, X)
-        O.linear_bwd(sR, sP, W0, tR, tP, iR, iP, X, dY)
+        g = O.linear_bwd(sR, sP, W0, tR, tP, iR, iP, X, dY)
+        for th, dth in ((tR, g["dthetaR"]), (tP, g["dthetaP"])):
+            O.adamw_step(th, dth, np.zeros(len(th)), np.zeros(len(th)), 1, **OPTIMIZER)
         spent += time.perf_counter() - t0
         done.append(q)
         log(f"oracle {q.name}: {spent:.1f} s so far")
@@ -143,7 +161,7 @@ def cpu_baseline(wl, budget_s: float = 25.0):
             break
     scale = sum(l.m * l.n for l in lins) / sum(l.m * l.n for l in done)
     names = "+".join(l.name for l in done)
-    sample = f"linears {names} forward+backward at {wl.T} tokens in float64: {spent:.1f} s"
+    sample = f"linears {names} forward+backward+AdamW at {wl.T} tokens in float64: {spent:.1f} s"
     if len(done) < len(lins):
         sample += f"; block time extrapolated by the block's sum of m*n ({scale:.2f}x)"
     else:
@@ -326,7 +344,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     """The LLaMA-3B POET-FS stack: every layer's state resident at once (float32 W0, skew parameters, primitives,
     saved powers, index sets, the materialized weights and the layer inputs kept for the backward); one step =
     grouped build and forward of every layer in order, then the backward of every layer in reverse order to the
-    primitive gradients and the grouped adjoint per layer. Weights and activations are drawn on the device with
+    primitive gradients, the grouped adjoint and the AdamW update per layer. Weights and activations are drawn on the device with
     the recipe's distributions (W0 row-normalized Gaussian, theta ~ N(0, 1e-3^2), X and dY ~ N(0, 1) in bf16).
     Inputs of one shape are shared the way a transformer layer shares them (q/k/v read one input, gate/up one)."""
     T = wl.T
@@ -374,6 +392,8 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     groups = [PoetGroup([e["pl"] for e in es], ws=gws) for es in layers]
     state_bytes = torch.cuda.memory_allocated() - base
 
+    hp = optimizer()
+
     def stack_step():
         for es, grp in zip(layers, groups):
             grp.build()
@@ -383,6 +403,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
             for e in reversed(es):
                 e["pl"].backward_prims(e["X"], e["dY"], e["dX"], W=e["W"])
             grp.finish_backward()
+            grp.optimizer_step(hp)
 
     log(f"stack warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -294,6 +294,30 @@ poet_status poet_merge_group(int32_t count, const poet_layer* layers, float* con
                              const uint32_t* linear_id, uint32_t epoch_next, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* ---- optimizer step on the skew parameters -------------------------------------------------------------
+ * The pages train R and P through their skew generators (Approach section) and name AdamW only as the baseline
+ * optimizer of dense training (Key results); the generators' optimizer is not stated. This library provides AdamW
+ * (Loshchilov and Hutter, ICLR 2019) on the packed parameters, elementwise:
+ *     m <- b1 m + (1 - b1) g ;  v <- b2 v + (1 - b2) g^2 ;
+ *     theta <- theta - lr ( (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps) + weight_decay theta ),
+ * and reinitializes the moments with the parameters at each merge (poet_optimizer_reset_group; the step count t
+ * then restarts at 1): after a merge a parameter describes a rotation about the new W0 and, for POET-FS, a newly
+ * sampled index pair, so old moments no longer refer to it. */
+typedef struct poet_adamw {
+  float lr, beta1, beta2, eps, weight_decay;  /* lr >= 0, 0 <= beta < 1, eps > 0, weight_decay >= 0 */
+} poet_adamw;
+
+/* One AdamW step on count sides in shared launches: theta[i], m[i], v[i] [poet_theta_len(sides[i])] float32 in/out
+ * (updated in place), dtheta[i] float32 in (the gradient from poet_adjoint_group or poet_linear_bwd*). step >= 1 is
+ * t, the number of steps since the last reset. Sides with no parameters are skipped (their pointers may be NULL).
+ * Bad hyperparameters or step < 1: POET_E_ARG before any launch. */
+poet_status poet_adamw_group(int32_t count, const poet_side* sides, float* const* theta, const float* const* dtheta,
+                             float* const* m, float* const* v, const poet_adamw* hp, int32_t step, void* stream);
+
+/* The moments m[i], v[i] of count sides set to zero (the optimizer state after merge-then-reinitialize). */
+poet_status poet_optimizer_reset_group(int32_t count, const poet_side* sides, float* const* m, float* const* v,
+                                       void* stream);
+
 /* ---- diagnostics ------------------------------------------------------------------------------------ */
 
 /* One internal GEMM of the library, exposed for kernel-level testing (not part of the layer's hot path):
@@ -331,7 +355,8 @@ enum {
   POET_K_MISC = 7,       /* packing, projection, conversion, sampling */
   POET_K_MERGE = 8,      /* merge passes W0 <- R W0 P */
   POET_K_GATHER = 9,     /* FS gathers and scatters of sampled rows / columns (and the sampled-block patch) */
-  POET_K_NCLASS = 10
+  POET_K_OPTIM = 10,     /* optimizer step on the skew parameters and its moment reset */
+  POET_K_NCLASS = 11
 };
 /* Start (on != 0: clears previous records) or stop recording a HIP event pair around every kernel launch the
  * library issues, on the launch's own stream. Process-wide; intended for benchmarking, adds one event pair

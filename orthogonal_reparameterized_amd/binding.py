@@ -31,18 +31,28 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
            "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
            "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group",
-           "poet_sample_indices_noalloc")
+           "poet_sample_indices_noalloc", "poet_adamw_group", "poet_optimizer_reset_group")
 POET_NOALLOC_MAX_D = 65536  # largest d poet_sample_indices_noalloc accepts (its device scratch holds d int32 flags)
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
-    POET_K_MISC, POET_K_MERGE, POET_K_GATHER = range(10)
+    POET_K_MISC, POET_K_MERGE, POET_K_GATHER, POET_K_OPTIM = range(11)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge",
-                "gather")
+                "gather", "optim")
 
 
 class PoetError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: status {status} ({detail})")
         self.status = status
+
+
+class poet_adamw(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float)]
+
+
+def adamw(lr: float = 1e-5, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+          weight_decay: float = 0.0) -> poet_adamw:
+    return poet_adamw(lr, beta1, beta2, eps, weight_decay)
 
 
 class poet_side(ctypes.Structure):
@@ -111,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_adamw_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), P(poet_adamw), I32, VP]
+    L.poet_optimizer_reset_group.argtypes = [I32, P(poet_side), P(VP), P(VP), VP]
     L.poet_linear_fwd_folded.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_folded_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_fold_group_workspace_bytes.argtypes = [I32, P(poet_layer)]
@@ -524,6 +536,32 @@ def poet_adjoint_group(sides, dprims, powers, dthetas, ws=None, stream=None):
     st = lib().poet_adjoint_group(n, _side_array(sides), dp, pw, dt, _ptr(ws, "ws", need, allow_none=True),
                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_adjoint_group")
+
+
+def poet_adamw_group(sides, thetas, dthetas, ms, vs, hp: poet_adamw, step: int, stream=None):
+    """One AdamW step on the packed skew parameters of every side (theta, m, v updated in place); ``step`` counts
+    the steps since the last reset, from 1."""
+    n = len(sides)
+    if not (len(thetas) == len(dthetas) == len(ms) == len(vs) == n):
+        raise ValueError("sides, thetas, dthetas, ms and vs must have the same length")
+    skip = [poet_theta_len(s) == 0 for s in sides]
+    sz = [4 * poet_theta_len(s) for s in sides]
+    tabs = [_ptr_table(t, [f"{nm}[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
+            for t, nm in ((thetas, "thetas"), (dthetas, "dthetas"), (ms, "ms"), (vs, "vs"))]
+    st = lib().poet_adamw_group(n, _side_array(sides), *tabs, ctypes.byref(hp), int(step), _stream(stream))
+    _check(st, "poet_adamw_group")
+
+
+def poet_optimizer_reset_group(sides, ms, vs, stream=None):
+    """Zero the AdamW moments of every side (the optimizer state after merge-then-reinitialize)."""
+    n = len(sides)
+    if not (len(ms) == len(vs) == n):
+        raise ValueError("sides, ms and vs must have the same length")
+    skip = [poet_theta_len(s) == 0 for s in sides]
+    sz = [4 * poet_theta_len(s) for s in sides]
+    mt = _ptr_table(ms, [f"ms[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
+    vt = _ptr_table(vs, [f"vs[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
+    _check(lib().poet_optimizer_reset_group(n, _side_array(sides), mt, vt, _stream(stream)), "poet_optimizer_reset_group")
 
 
 def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR, idxP, seed: int, linear_id: int,

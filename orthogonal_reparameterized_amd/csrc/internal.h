@@ -129,6 +129,15 @@ struct FinSide {
 struct FinGroup { int n = 0; FinSide s[MAXG]; };
 hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st);
 
+// AdamW on the packed skew parameters of up to MAXG sides in one launch (optim.hip): theta, m, v updated in place
+// from grad; inv_bc1 / inv_bc2 are the bias-correction factors 1 / (1 - beta^t) of the step
+struct OptSide { float* theta = nullptr; const float* grad = nullptr; float* m = nullptr; float* v = nullptr; int64_t n = 0; };
+struct OptGroup { int n = 0; OptSide s[MAXG]; };
+hipError_t launch_adamw_group(const OptGroup& g, float lr, float b1, float b2, float eps, float wd, double inv_bc1,
+                              double inv_bc2, hipStream_t st);
+// m, v <- 0 for every side of the group (the optimizer state after merge-then-reinitialize)
+hipError_t launch_moments_reset_group(const OptGroup& g, hipStream_t st);
+
 
 // Fused application of block-diagonal factors on both sides (bs_apply.hip), blocks bpR, bpP <= 256, W0 float32
 // m x n with row pitch ldw (rows readable up to a multiple of 4 columns), primitives float32 bp x bp blocks:

@@ -1,5 +1,6 @@
 // C ABI of the POET layer: host-side validation, workspace planning and the launch sequence of each call.
 // Nothing here computes on the host; every step of the method runs in the kernels of this library.
+#include <cmath>
 #include <cstdarg>
 #include <algorithm>
 #include <cstdio>
@@ -1858,6 +1859,63 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, true, o, st));
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, false, o + S[i].prim_len, st));
     HIP_TRY(prims_bf16(S[i], prim[i], o + 2 * S[i].prim_len, st));
+  }
+  return POET_OK;
+}
+
+poet_status poet_adamw_group(int32_t count, const poet_side* sides, float* const* theta, const float* const* dtheta,
+                             float* const* m, float* const* v, const poet_adamw* hp, int32_t step, void* stream) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return g_last;
+  if (!hp) return fail(POET_E_ARG, "null hyperparameters");
+  const auto finite = [](float x) { return x == x && x - x == 0.f; };
+  if (!finite(hp->lr) || hp->lr < 0.f) return fail(POET_E_ARG, "lr = %g must be finite and >= 0", hp->lr);
+  if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+    return fail(POET_E_ARG, "betas (%g, %g) must be in [0, 1)", hp->beta1, hp->beta2);
+  if (!finite(hp->eps) || !(hp->eps > 0.f)) return fail(POET_E_ARG, "eps = %g must be finite and > 0", hp->eps);
+  if (!finite(hp->weight_decay) || hp->weight_decay < 0.f)
+    return fail(POET_E_ARG, "weight_decay = %g must be finite and >= 0", hp->weight_decay);
+  if (step < 1) return fail(POET_E_ARG, "step = %d must be >= 1 (steps since the last reset)", step);
+  if (count == 0) return POET_OK;
+  if (!theta || !dtheta || !m || !v) return fail(POET_E_ARG, "null pointer table");
+  for (int i = 0; i < count; ++i)
+    if (S[i].theta_len > 0 && (!theta[i] || !dtheta[i] || !m[i] || !v[i]))
+      return fail(POET_E_ARG, "null theta, dtheta, m or v for side %d", i);
+  // the bias corrections 1 / (1 - beta^t) in double
+  const double inv_bc1 = 1.0 / (1.0 - std::pow((double)hp->beta1, (double)step));
+  const double inv_bc2 = 1.0 / (1.0 - std::pow((double)hp->beta2, (double)step));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  OptGroup g;
+  for (int i = 0; i <= count; ++i) {
+    if (g.n == MAXG || (i == count && g.n > 0)) {
+      HIP_TRY(launch_adamw_group(g, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, inv_bc1, inv_bc2, st));
+      g.n = 0;
+    }
+    if (i == count || S[i].theta_len == 0) continue;
+    OptSide& o = g.s[g.n++];
+    o.theta = theta[i]; o.grad = dtheta[i]; o.m = m[i]; o.v = v[i]; o.n = (int64_t)S[i].theta_len;
+  }
+  return POET_OK;
+}
+
+poet_status poet_optimizer_reset_group(int32_t count, const poet_side* sides, float* const* m, float* const* v,
+                                       void* stream) {
+  std::vector<SideInfo> S;
+  if (!group_sides(count, sides, &S)) return g_last;
+  if (count == 0) return POET_OK;
+  if (!m || !v) return fail(POET_E_ARG, "null pointer table");
+  for (int i = 0; i < count; ++i)
+    if (S[i].theta_len > 0 && (!m[i] || !v[i])) return fail(POET_E_ARG, "null m or v for side %d", i);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  OptGroup g;
+  for (int i = 0; i <= count; ++i) {
+    if (g.n == MAXG || (i == count && g.n > 0)) {
+      HIP_TRY(launch_moments_reset_group(g, st));
+      g.n = 0;
+    }
+    if (i == count || S[i].theta_len == 0) continue;
+    OptSide& o = g.s[g.n++];
+    o.m = m[i]; o.v = v[i]; o.n = (int64_t)S[i].theta_len;
   }
   return POET_OK;
 }

@@ -66,6 +66,13 @@ class PoetLinear:
         self.qnormP = torch.empty(B.poet_num_prims(P), dtype=torch.float32, device=self.dev)
         self.dthetaR = torch.empty(max(nR, 1), dtype=torch.float32, device=self.dev)
         self.dthetaP = torch.empty(max(nP, 1), dtype=torch.float32, device=self.dev)
+        # AdamW moments of the skew parameters and the steps taken since the last reset (a merge resets them)
+        self.mR = torch.zeros(max(nR, 1), dtype=torch.float32, device=self.dev)
+        self.vR = torch.zeros(max(nR, 1), dtype=torch.float32, device=self.dev)
+        self.mP = torch.zeros(max(nP, 1), dtype=torch.float32, device=self.dev)
+        self.vP = torch.zeros(max(nP, 1), dtype=torch.float32, device=self.dev)
+        self.opt_steps = 0
+        self.grad_ready = False  # dthetaR / dthetaP hold the gradient of the current parameters
         wsb = PoetLinear.workspace_bytes(m, n, T, R, P, act_dtype, self.L.ldw, self.L.ldx, self.L.ldy,
                                          "act" if self.act_path else "weight")
         if ws is None:
@@ -146,6 +153,7 @@ class PoetLinear:
         self._need_build("backward")
         B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
+        self.grad_ready = True
 
     def forward_act(self, X, Y, Z, stream=None):
         """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
@@ -161,6 +169,7 @@ class PoetLinear:
         self._need_build("backward_act")
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
                               dY, dX, self.dthetaR, self.dthetaP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
+        self.grad_ready = True
 
     def _dprims(self):
         if getattr(self, "dprimR", None) is None:
@@ -173,6 +182,7 @@ class PoetLinear:
         into dthetaR, dthetaP for many linears at once."""
         self._need_build("backward_prims")
         self._dprims()
+        self.grad_ready = False  # dthetaR / dthetaP come from PoetGroup.finish_backward
         B.poet_linear_bwd_prims(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, W, X, dY, dX,
                                 self.dprimR, self.dprimP, self.ws, stream)
 
@@ -181,12 +191,26 @@ class PoetLinear:
         PoetGroup.finish_backward turns them into dthetaR, dthetaP for many linears at once."""
         self._need_build("backward_act_prims")
         self._dprims()
+        self.grad_ready = False  # dthetaR / dthetaP come from PoetGroup.finish_backward
         if self.RW0 is not None:
             B.poet_linear_bwd_folded_prims(self.L, self.RW0, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
                                            self.ws, stream, opsP=self.opsP)
         else:
             B.poet_linear_bwd_act_prims(self.L, self.W0b, self.primR, self.primP, X, Z, dY, dX, self.dprimR,
                                         self.dprimP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
+
+    def optimizer_step(self, hp: B.poet_adamw, stream=None):
+        """One AdamW step on thetaR, thetaP from dthetaR, dthetaP (the parameters change: the next step builds)."""
+        if not self.grad_ready:
+            raise RuntimeError("optimizer_step needs the gradient of the current parameters: run the backward first")
+        B.poet_adamw_group([self.L.R, self.L.P], [self.thetaR, self.thetaP], [self.dthetaR, self.dthetaP],
+                           [self.mR, self.mP], [self.vR, self.vP], hp, self.opt_steps + 1, stream)
+        self._stepped()
+
+    def _stepped(self):
+        self.opt_steps += 1
+        self.grad_ready = False
+        self.built = False
 
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
@@ -195,6 +219,7 @@ class PoetLinear:
         self._need_build("merge")
         B.poet_merge(self.L, self.W0, self.W0b if shadow is None else shadow, self.thetaR, self.thetaP, self.primR,
                      self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch + 1, self.ws, stream)
+        B.poet_optimizer_reset_group([self.L.R, self.L.P], [self.mR, self.mP], [self.vR, self.vP], stream)
         self._merged()
         if shadow is not None and self.W0b is not None:
             B.poet_weight_shadow(self.L, self.W0, self.W0b, stream)
@@ -204,6 +229,8 @@ class PoetLinear:
         of the last build are stale (they belong to the parameters before the reset)."""
         self.epoch += 1
         self.built = False
+        self.grad_ready = False
+        self.opt_steps = 0
         self.opsR = self.opsP = None
         self.W0P = self.RW0 = None
 
@@ -285,6 +312,22 @@ class PoetGroup:
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
         dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]
         B.poet_adjoint_group(self.sides, dprims, powers, dthetas, self.ws, stream)
+        for pl in self.linears:
+            pl.grad_ready = True
+
+    def optimizer_step(self, hp: B.poet_adamw, stream=None):
+        """One AdamW step on the skew parameters of every linear in shared launches (their step counts must agree)."""
+        pls = self.linears
+        if len({pl.opt_steps for pl in pls}) != 1:
+            raise ValueError("PoetGroup.optimizer_step needs one step count across its linears")
+        for pl in pls:
+            if not pl.grad_ready:
+                raise RuntimeError("optimizer_step needs the gradient of the current parameters: run the backward first")
+        B.poet_adamw_group(self.sides, [t for pl in pls for t in (pl.thetaR, pl.thetaP)],
+                           [t for pl in pls for t in (pl.dthetaR, pl.dthetaP)], [t for pl in pls for t in (pl.mR, pl.mP)],
+                           [t for pl in pls for t in (pl.vR, pl.vP)], hp, pls[0].opt_steps + 1, stream)
+        for pl in pls:
+            pl._stepped()
 
     def merge(self, stream=None):
         """Merge-then-reinitialize of every linear (their sampler seeds and epochs must agree); refreshes each
@@ -298,5 +341,7 @@ class PoetGroup:
                            [pl.thetaR for pl in pls], [pl.thetaP for pl in pls], [pl.primR for pl in pls],
                            [pl.primP for pl in pls], [pl.idxR for pl in pls], [pl.idxP for pl in pls], pls[0].seed,
                            [pl.linear_id for pl in pls], pls[0].epoch + 1, self.ws, stream)
+        B.poet_optimizer_reset_group(self.sides, [t for pl in pls for t in (pl.mR, pl.mP)],
+                                     [t for pl in pls for t in (pl.vR, pl.vP)], stream)
         for pl in pls:
             pl._merged()

@@ -283,3 +283,27 @@ def test_folded_calls_reject_bad_arguments():
     arr32 = (B.poet_layer * 2)(L, F32)
     assert lb.poet_fold_weights_group(2, arr32, tab, tab, tab, None, None, tab, tab, FAKE, 1 << 40,
                                       None) == B.POET_E_UNSUPPORTED
+
+
+def test_adamw_rejects_bad_arguments_on_the_host():
+    lb = B.lib()
+    sides = (B.poet_side * 1)(B.side(0, 64, 32, 2, 0))
+    tab = (ctypes.c_void_p * 1)(0x1000)
+    good = B.adamw(lr=1e-3)
+
+    def call(hp=good, step=1, t=tab, count=1):
+        return lb.poet_adamw_group(count, sides, t, t, t, t, None if hp is None else ctypes.byref(hp), step, None)
+
+    assert call(hp=None) == B.POET_E_ARG
+    assert call(step=0) == B.POET_E_ARG
+    for bad in (dict(lr=-1.0), dict(lr=float("nan")), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0),
+                dict(weight_decay=float("inf"))):
+        kw = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+        kw.update(bad)
+        assert call(hp=B.poet_adamw(**kw)) == B.POET_E_ARG, bad
+        assert B.poet_last_error() != ""
+    assert call(t=(ctypes.c_void_p * 1)(None)) == B.POET_E_ARG  # a side with parameters needs every buffer
+    assert call(t=None) == B.POET_E_ARG
+    assert call(count=-1) == B.POET_E_ARG
+    assert lb.poet_optimizer_reset_group(1, sides, None, tab, None) == B.POET_E_ARG
+    assert lb.poet_optimizer_reset_group(1, sides, (ctypes.c_void_p * 1)(None), tab, None) == B.POET_E_ARG

@@ -52,3 +52,19 @@ def test_merge_marks_the_build_stale():
     assert pl.W0P is None and pl.RW0 is None and pl.opsR is None and pl.opsP is None
     with pytest.raises(RuntimeError, match="build"):
         pl.forward(torch.zeros((8, 48)), torch.zeros((8, 64)))
+
+
+def test_optimizer_step_needs_a_fresh_gradient():
+    pl = _cpu_linear()
+    with pytest.raises(RuntimeError, match="gradient"):
+        pl.optimizer_step(B.adamw())
+    with pytest.raises(RuntimeError, match="gradient"):
+        PoetGroup([pl]).optimizer_step(B.adamw())
+    pl.grad_ready = True  # as after a backward; the binding then rejects the CPU tensors before any launch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pl.optimizer_step(B.adamw())
+    assert pl.opt_steps == 0 and pl.grad_ready
+    pl._stepped()
+    assert pl.opt_steps == 1 and not pl.grad_ready and not pl.built
+    pl._merged()
+    assert pl.opt_steps == 0 and pl.epoch == 1
