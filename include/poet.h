@@ -318,6 +318,25 @@ poet_status poet_adamw_group(int32_t count, const poet_side* sides, float* const
 poet_status poet_optimizer_reset_group(int32_t count, const poet_side* sides, float* const* m, float* const* v,
                                        void* stream);
 
+/* ---- spectral diagnostics of a weight ---------------------------------------------------------------------
+ * The metrics the POET pages report next to the spectrum claim (Experimental setup, Metrics: hyperspherical energy
+ * and singular-value entropy), computed on the GPU from a float32 m x n weight W (row pitch ldw >= n), for instance
+ * W0 before and after a merge or a materialized W = R W0 P. Both form a Gram matrix in float64 and work in float64
+ * from there; outputs are float64 device buffers. Rows of W must be nonzero for the energy.
+ *   hyperspherical energy (Liu et al., NeurIPS 2018) of the neurons (rows): with w^_i = w_i / ||w_i||,
+ *     E_i = sum over j != i of ||w^_i - w^_j||^(-s),  energy = sum_i E_i  (s > 0; the pages' parameters are not
+ *     given, s = 1 is the usual choice);
+ *   singular-value entropy (the effective-rank entropy of Roy and Vetterli, 2007): with sigma the r = min(m, n)
+ *     singular values and p = sigma / sum sigma, entropy = -sum p log p; sigma (nullable) receives them, descending.
+ * ws: at least poet_spectral_workspace_bytes(m, n) bytes (either call). */
+size_t poet_spectral_workspace_bytes(int32_t m, int32_t n);
+poet_status poet_hyperspherical_energy(int32_t m, int32_t n, const float* W, int64_t ldw, float s,
+                                       double* energy_rows /* [m], nullable */, double* energy /* [1] */, void* ws,
+                                       size_t ws_bytes, void* stream);
+poet_status poet_singular_value_entropy(int32_t m, int32_t n, const float* W, int64_t ldw,
+                                        double* sigma /* [min(m, n)], nullable */, double* entropy /* [1] */,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* ---- diagnostics ------------------------------------------------------------------------------------ */
 
 /* One internal GEMM of the library, exposed for kernel-level testing (not part of the layer's hot path):
@@ -356,7 +375,8 @@ enum {
   POET_K_MERGE = 8,      /* merge passes W0 <- R W0 P */
   POET_K_GATHER = 9,     /* FS gathers and scatters of sampled rows / columns (and the sampled-block patch) */
   POET_K_OPTIM = 10,     /* optimizer step on the skew parameters and its moment reset */
-  POET_K_NCLASS = 11
+  POET_K_DIAG = 11,      /* spectral diagnostics (hyperspherical energy, singular-value entropy) */
+  POET_K_NCLASS = 12
 };
 /* Start (on != 0: clears previous records) or stop recording a HIP event pair around every kernel launch the
  * library issues, on the launch's own stream. Process-wide; intended for benchmarking, adds one event pair

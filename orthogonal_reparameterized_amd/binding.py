@@ -31,12 +31,13 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
            "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
            "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group",
-           "poet_sample_indices_noalloc", "poet_adamw_group", "poet_optimizer_reset_group")
+           "poet_sample_indices_noalloc", "poet_adamw_group", "poet_optimizer_reset_group",
+           "poet_spectral_workspace_bytes", "poet_hyperspherical_energy", "poet_singular_value_entropy")
 POET_NOALLOC_MAX_D = 65536  # largest d poet_sample_indices_noalloc accepts (its device scratch holds d int32 flags)
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
-    POET_K_MISC, POET_K_MERGE, POET_K_GATHER, POET_K_OPTIM = range(11)
+    POET_K_MISC, POET_K_MERGE, POET_K_GATHER, POET_K_OPTIM, POET_K_DIAG = range(12)
 KCLASS_NAMES = ("token_fwd", "token_dx", "token_gw", "chain", "adjoint", "apply", "contract", "misc", "merge",
-                "gather", "optim")
+                "gather", "optim", "diag")
 
 
 class PoetError(RuntimeError):
@@ -122,6 +123,10 @@ def lib() -> ctypes.CDLL:
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
     L.poet_adamw_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), P(poet_adamw), I32, VP]
+    L.poet_spectral_workspace_bytes.argtypes = [I32, I32]
+    L.poet_spectral_workspace_bytes.restype = S
+    L.poet_hyperspherical_energy.argtypes = [I32, I32, VP, ctypes.c_int64, ctypes.c_float, VP, VP, VP, S, VP]
+    L.poet_singular_value_entropy.argtypes = [I32, I32, VP, ctypes.c_int64, VP, VP, VP, S, VP]
     L.poet_optimizer_reset_group.argtypes = [I32, P(poet_side), P(VP), P(VP), VP]
     L.poet_linear_fwd_folded.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_folded_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
@@ -562,6 +567,36 @@ def poet_optimizer_reset_group(sides, ms, vs, stream=None):
     mt = _ptr_table(ms, [f"ms[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
     vt = _ptr_table(vs, [f"vs[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
     _check(lib().poet_optimizer_reset_group(n, _side_array(sides), mt, vt, _stream(stream)), "poet_optimizer_reset_group")
+
+
+def poet_spectral_workspace_bytes(m: int, n: int) -> int:
+    return int(lib().poet_spectral_workspace_bytes(m, n))
+
+
+def poet_hyperspherical_energy(m: int, n: int, W, ldw: int, s: float, energy, energy_rows=None, ws=None, stream=None):
+    """Hyperspherical energy of the m neurons (rows) of the float32 weight W (row pitch ldw): energy [1] float64
+    out, energy_rows [m] float64 out (optional)."""
+    need = poet_spectral_workspace_bytes(m, n)
+    if ws is None:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=W.device)
+    st = lib().poet_hyperspherical_energy(m, n, _ptr(W, "W", 4 * ((m - 1) * ldw + n), "float32"), ldw, s,
+                                          _ptr(energy_rows, "energy_rows", 8 * m, "float64", allow_none=True),
+                                          _ptr(energy, "energy", 8, "float64"), _ptr(ws, "ws", need),
+                                          ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_hyperspherical_energy")
+
+
+def poet_singular_value_entropy(m: int, n: int, W, ldw: int, entropy, sigma=None, ws=None, stream=None):
+    """Entropy of the normalized singular values of the float32 weight W (row pitch ldw): entropy [1] float64 out,
+    sigma [min(m, n)] float64 out, descending (optional)."""
+    need = poet_spectral_workspace_bytes(m, n)
+    if ws is None:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=W.device)
+    st = lib().poet_singular_value_entropy(m, n, _ptr(W, "W", 4 * ((m - 1) * ldw + n), "float32"), ldw,
+                                           _ptr(sigma, "sigma", 8 * min(m, n), "float64", allow_none=True),
+                                           _ptr(entropy, "entropy", 8, "float64"), _ptr(ws, "ws", need),
+                                           ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_singular_value_entropy")
 
 
 def poet_merge(L: poet_layer, W0, W0_shadow, thetaR, thetaP, primR, primP, idxR, idxP, seed: int, linear_id: int,

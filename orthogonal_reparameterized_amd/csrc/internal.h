@@ -138,6 +138,17 @@ hipError_t launch_adamw_group(const OptGroup& g, float lr, float b1, float b2, f
 // m, v <- 0 for every side of the group (the optimizer state after merge-then-reinitialize)
 hipError_t launch_moments_reset_group(const OptGroup& g, hipStream_t st);
 
+// Spectral diagnostics (spectral.hip). C (r x r float64, row pitch ldc) = W W^T (trans false, r = rows) or W^T W
+// (trans true, r = cols) of the float32 rows x cols W (row pitch ldw).
+hipError_t launch_gram_f64(const float* W, int64_t ldw, int rows, int cols, bool trans, double* C, int64_t ldc,
+                           hipStream_t st);
+// E[i] = sum_{j != i} (2 - 2 C_ij / sqrt(C_ii C_jj))^(-s/2) and total[0] = sum_i E[i]
+hipError_t launch_he_rows(const double* C, int64_t ldc, int r, double s, double* E, double* total, hipStream_t st);
+// Eigenvalues of the symmetric C (overwritten) by Householder tridiagonalization and bisection; sigma (nullable,
+// r, descending) = sqrt of them, entropy[0] = -sum p log p of p = sigma / sum sigma. u, p, d, e, lam: r doubles each.
+hipError_t launch_sym_eig_entropy(double* C, int64_t ldc, int r, double* u, double* p, double* d, double* e,
+                                  double* lam, double* sigma, double* entropy, hipStream_t st);
+
 
 // Fused application of block-diagonal factors on both sides (bs_apply.hip), blocks bpR, bpP <= 256, W0 float32
 // m x n with row pitch ldw (rows readable up to a multiple of 4 columns), primitives float32 bp x bp blocks:

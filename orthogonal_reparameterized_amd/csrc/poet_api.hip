@@ -1920,6 +1920,53 @@ poet_status poet_optimizer_reset_group(int32_t count, const poet_side* sides, fl
   return POET_OK;
 }
 
+size_t poet_spectral_workspace_bytes(int32_t m, int32_t n) {
+  if (m < 1 || n < 1) return fail(POET_E_SHAPE, "m = %d and n = %d must be >= 1", m, n), 0;
+  const size_t r = (size_t)std::min(m, n);
+  const size_t he = align_up((size_t)m * m * 8, 256) + align_up((size_t)m * 8, 256);
+  const size_t sv = align_up(r * r * 8, 256) + 5 * align_up(r * 8, 256);
+  return std::max(he, sv) + 256;
+}
+
+poet_status poet_hyperspherical_energy(int32_t m, int32_t n, const float* W, int64_t ldw, float s,
+                                       double* energy_rows, double* energy, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  if (m < 1 || n < 1 || ldw < n) return fail(POET_E_SHAPE, "need m, n >= 1 and ldw >= n (m=%d n=%d ldw=%lld)", m, n,
+                                             (long long)ldw);
+  if (!(s > 0.f) || !(s < 1e30f)) return fail(POET_E_ARG, "s = %g must be finite and > 0", s);
+  if (!W || !energy) return fail(POET_E_ARG, "null W or energy");
+  if ((int64_t)m * m > ((int64_t)1 << 40)) return fail(POET_E_UNSUPPORTED, "m = %d too large", m);
+  if (!check_ws(ws, ws_bytes, poet_spectral_workspace_bytes(m, n))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Arena a(ws);
+  double* C = a.take<double>((size_t)m * m);
+  double* E = a.take<double>((size_t)m);
+  HIP_TRY(launch_gram_f64(W, ldw, m, n, false, C, m, st));
+  HIP_TRY(launch_he_rows(C, m, m, (double)s, energy_rows ? energy_rows : E, energy, st));
+  return POET_OK;
+}
+
+poet_status poet_singular_value_entropy(int32_t m, int32_t n, const float* W, int64_t ldw, double* sigma,
+                                        double* entropy, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1 || n < 1 || ldw < n) return fail(POET_E_SHAPE, "need m, n >= 1 and ldw >= n (m=%d n=%d ldw=%lld)", m, n,
+                                             (long long)ldw);
+  if (!W || !entropy) return fail(POET_E_ARG, "null W or entropy");
+  if (!check_ws(ws, ws_bytes, poet_spectral_workspace_bytes(m, n))) return g_last;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int r = std::min(m, n);
+  Arena a(ws);
+  double* C = a.take<double>((size_t)r * r);
+  double* u = a.take<double>(r);
+  double* p = a.take<double>(r);
+  double* d = a.take<double>(r);
+  double* e = a.take<double>(r);
+  double* lam = a.take<double>(r);
+  // the smaller Gram: W^T W (n x n) for a tall W, W W^T (m x m) otherwise
+  HIP_TRY(launch_gram_f64(W, ldw, m, n, n <= m, C, r, st));
+  HIP_TRY(launch_sym_eig_entropy(C, r, r, u, p, d, e, lam, sigma, entropy, st));
+  return POET_OK;
+}
+
 size_t poet_adjoint_group_workspace_bytes(int32_t count, const poet_side* sides) {
   std::vector<SideInfo> S;
   if (!group_sides(count, sides, &S)) return 0;

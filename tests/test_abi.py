@@ -307,3 +307,16 @@ def test_adamw_rejects_bad_arguments_on_the_host():
     assert call(count=-1) == B.POET_E_ARG
     assert lb.poet_optimizer_reset_group(1, sides, None, tab, None) == B.POET_E_ARG
     assert lb.poet_optimizer_reset_group(1, sides, (ctypes.c_void_p * 1)(None), tab, None) == B.POET_E_ARG
+
+
+def test_spectral_diagnostics_reject_bad_arguments_on_the_host():
+    lb = B.lib()
+    need = B.poet_spectral_workspace_bytes(64, 32)
+    assert need >= 64 * 64 * 8 and B.poet_spectral_workspace_bytes(0, 5) == 0
+    assert lb.poet_hyperspherical_energy(64, 32, FAKE, 16, 1.0, None, FAKE, FAKE, need, None) == B.POET_E_SHAPE
+    assert lb.poet_hyperspherical_energy(64, 32, FAKE, 32, 0.0, None, FAKE, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_hyperspherical_energy(64, 32, FAKE, 32, 1.0, None, None, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_hyperspherical_energy(64, 32, FAKE, 32, 1.0, None, FAKE, FAKE, need - 1024, None) == B.POET_E_WORKSPACE
+    assert lb.poet_singular_value_entropy(64, 32, None, 32, None, FAKE, FAKE, need, None) == B.POET_E_ARG
+    assert lb.poet_singular_value_entropy(64, 0, FAKE, 32, None, FAKE, FAKE, need, None) == B.POET_E_SHAPE
+    assert lb.poet_singular_value_entropy(64, 32, FAKE, 32, None, FAKE, FAKE, 8, None) == B.POET_E_WORKSPACE
