@@ -125,6 +125,13 @@ size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
 poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float* prim, void* powers,
                                   float* qnorm, void* ws, size_t ws_bytes, void* stream);
 
+/* The exact Cayley primitives R = (I + Q)(I - Q)^{-1} of one side (the map the truncated series approximates;
+ * "Builds on ... Cayley parameterization", Experimental setup), an accuracy reference for poet_build_orthogonal:
+ * prim [poet_prim_len] float32 out, padded with the identity like the built primitives. Primitives up to 256
+ * (POET_E_UNSUPPORTED above). Float32 Gauss-Jordan inversion of I - Q without pivoting (its symmetric part is the
+ * identity), one workgroup per primitive; no workspace. */
+poet_status poet_build_orthogonal_exact(const poet_side* s, const float* theta, float* prim, void* stream);
+
 /* Sample the FS index set of one side (the sampled sub-block of stochastic primitive optimization,
  * Approach section; POET-FS with b = 1/2 in Key results). Counter-based: with SM one SplitMix64 output
  * step (Steele, Lea and Flood, OOPSLA 2014), h = SM(SM(SM(SM(seed) ^ linear_id) ^ side) ^ epoch),

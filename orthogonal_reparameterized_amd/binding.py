@@ -32,7 +32,8 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_merge_group_workspace_bytes", "poet_merge_group", "poet_linear_fwd_folded",
            "poet_linear_bwd_folded_prims", "poet_fold_group_workspace_bytes", "poet_fold_weights_group",
            "poet_sample_indices_noalloc", "poet_adamw_group", "poet_optimizer_reset_group",
-           "poet_spectral_workspace_bytes", "poet_hyperspherical_energy", "poet_singular_value_entropy")
+           "poet_spectral_workspace_bytes", "poet_hyperspherical_energy", "poet_singular_value_entropy",
+           "poet_build_orthogonal_exact")
 POET_NOALLOC_MAX_D = 65536  # largest d poet_sample_indices_noalloc accepts (its device scratch holds d int32 flags)
 POET_K_TOKEN_FWD, POET_K_TOKEN_DX, POET_K_TOKEN_GW, POET_K_CHAIN, POET_K_ADJOINT, POET_K_APPLY, POET_K_CONTRACT, \
     POET_K_MISC, POET_K_MERGE, POET_K_GATHER, POET_K_OPTIM, POET_K_DIAG = range(12)
@@ -123,6 +124,7 @@ def lib() -> ctypes.CDLL:
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
     L.poet_adamw_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), P(poet_adamw), I32, VP]
+    L.poet_build_orthogonal_exact.argtypes = [P(poet_side), VP, VP, VP]
     L.poet_spectral_workspace_bytes.argtypes = [I32, I32]
     L.poet_spectral_workspace_bytes.restype = S
     L.poet_hyperspherical_energy.argtypes = [I32, I32, VP, ctypes.c_int64, ctypes.c_float, VP, VP, VP, S, VP]
@@ -567,6 +569,13 @@ def poet_optimizer_reset_group(sides, ms, vs, stream=None):
     mt = _ptr_table(ms, [f"ms[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
     vt = _ptr_table(vs, [f"vs[{i}]" for i in range(n)], sz, ["float32"] * n, skip)
     _check(lib().poet_optimizer_reset_group(n, _side_array(sides), mt, vt, _stream(stream)), "poet_optimizer_reset_group")
+
+
+def poet_build_orthogonal_exact(s: poet_side, theta, prim, stream=None):
+    """Exact Cayley primitives (I + Q)(I - Q)^{-1} of one side (primitives up to 256), float32, identity-padded."""
+    st = lib().poet_build_orthogonal_exact(ctypes.byref(s), _ptr(theta, "theta", 4 * poet_theta_len(s), "float32"),
+                                           _ptr(prim, "prim", 4 * poet_prim_len(s), "float32"), _stream(stream))
+    _check(st, "poet_build_orthogonal_exact")
 
 
 def poet_spectral_workspace_bytes(m: int, n: int) -> int:

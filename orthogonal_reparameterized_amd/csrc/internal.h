@@ -9,6 +9,18 @@ namespace poet {
 
 enum DType : int { F32 = 0, BF16 = 1 };
 
+// Packed skew-parameter layout of a side (shared by the kernels that read theta):
+// size of primitive p (the last BS block may be short)
+__device__ __forceinline__ int prim_size(int mode, int d, int bp, int p) {
+  return mode == 1 ? bp : min(bp, d - p * bp);
+}
+// packed position of (i, j), i < j < c, in row-major strict-upper order
+__device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
+  return (int64_t)i * c - (int64_t)i * (i + 1) / 2 + (j - i - 1);
+}
+// offset of primitive p's parameters (every primitive before p is a full bp x bp block)
+__device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
+
 __host__ __device__ inline size_t dtype_size(int dt) { return dt == BF16 ? 2 : 4; }
 
 // A batched GEMM  out = alpha * op(A) op(B) + beta * D ;  C <- out (if C) ;  Acc += gamma * out (if Acc).
@@ -137,6 +149,9 @@ hipError_t launch_adamw_group(const OptGroup& g, float lr, float b1, float b2, f
                               double inv_bc2, hipStream_t st);
 // m, v <- 0 for every side of the group (the optimizer state after merge-then-reinitialize)
 hipError_t launch_moments_reset_group(const OptGroup& g, hipStream_t st);
+
+// prim = (I + Q)(I - Q)^{-1} of every primitive of a side (bp <= 256), float32, padded with the identity (cayley.hip)
+hipError_t launch_cayley_exact(const float* theta, int mode, int d, int bp, int nprim, float* prim, hipStream_t st);
 
 // Spectral diagnostics (spectral.hip). C (r x r float64, row pitch ldc) = W W^T (trans false, r = rows) or W^T W
 // (trans true, r = cols) of the float32 rows x cols W (row pitch ldw).

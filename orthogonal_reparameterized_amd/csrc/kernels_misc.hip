@@ -17,18 +17,6 @@ inline int grid_for(size_t n, int per_block = kThreads, int cap = 65535 * 8) {
   return (int)(g > (size_t)cap ? cap : g);
 }
 
-// size of primitive p of a side
-__device__ __forceinline__ int prim_size(int mode, int d, int bp, int p) {
-  return mode == 1 ? bp : min(bp, d - p * bp);
-}
-
-// packed position of (i, j), i < j < c, in row-major strict-upper order
-__device__ __forceinline__ int64_t tri_pos(int i, int j, int c) {
-  return (int64_t)i * c - (int64_t)i * (i + 1) / 2 + (j - i - 1);
-}
-
-// every primitive before p is a full bp x bp block
-__device__ __forceinline__ int64_t theta_off(int bp, int p) { return (int64_t)p * bp * (bp - 1) / 2; }
 
 // Q of one 32 x 32 tile pair of a primitive from its packed parameters. Workgroup (256 threads) = tile pair
 // (ti, tj), ti <= tj, of primitive p; thread (col = tid % 32, row0 = tid / 32) holds rows row0 + 8u, u = 0..3.

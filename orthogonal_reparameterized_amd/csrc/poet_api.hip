@@ -1176,6 +1176,18 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   return POET_OK;
 }
 
+poet_status poet_build_orthogonal_exact(const poet_side* s, const float* theta, float* prim, void* stream) {
+  SideInfo S;
+  if (!side_info(s, &S, "side")) return g_last;
+  if (!prim) return fail(POET_E_ARG, "null prim");
+  if (!theta && S.theta_len > 0) return fail(POET_E_ARG, "null theta");
+  if (S.bp > 256)
+    return fail(POET_E_UNSUPPORTED, "exact Cayley primitives of size %d: this build takes primitives up to 256", S.bp);
+  if (S.nprim > 65535) return fail(POET_E_UNSUPPORTED, "%d primitives exceed one launch", S.nprim);
+  HIP_TRY(launch_cayley_exact(theta, S.mode, S.d, S.bp, S.nprim, prim, reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
 poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
                                 uint32_t epoch, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   if (d < 1 || s < 0 || s > d) return fail(POET_E_SHAPE, "need d >= 1 and 0 <= s <= d (d=%d s=%d)", d, s);

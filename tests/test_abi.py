@@ -320,3 +320,13 @@ def test_spectral_diagnostics_reject_bad_arguments_on_the_host():
     assert lb.poet_singular_value_entropy(64, 32, None, 32, None, FAKE, FAKE, need, None) == B.POET_E_ARG
     assert lb.poet_singular_value_entropy(64, 0, FAKE, 32, None, FAKE, FAKE, need, None) == B.POET_E_SHAPE
     assert lb.poet_singular_value_entropy(64, 32, FAKE, 32, None, FAKE, FAKE, 8, None) == B.POET_E_WORKSPACE
+
+
+def test_exact_cayley_rejects_large_primitives_on_the_host():
+    lb = B.lib()
+    big = B.side(1, 2048, 1024, 5, 1)
+    assert lb.poet_build_orthogonal_exact(ctypes.byref(big), FAKE, FAKE, None) == B.POET_E_UNSUPPORTED
+    assert "256" in B.poet_last_error()
+    ok = B.side(0, 512, 256, 5, 1)
+    assert lb.poet_build_orthogonal_exact(ctypes.byref(ok), FAKE, None, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_exact(ctypes.byref(ok), None, FAKE, None) == B.POET_E_ARG
