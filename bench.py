@@ -129,7 +129,7 @@ def algorithmic_flops(specs):
     return {"path_A": a, "path_B": b, "min": min(a, b)}
 
 
-def cpu_baseline(wl, budget_s: float = 25.0):
+def cpu_baseline(wl, budget_s: float = 25.0, layers: int = 0):
     """The oracle (float64 NumPy, as it stands) on the same workload: forward + backward of the block's linears
     at the full token count, in order, until the time budget is spent. If it stops early, the block time is
     extrapolated from the linears done by the block's sum of m*n (and the sample string says so). A stack of
@@ -166,9 +166,10 @@ def cpu_baseline(wl, budget_s: float = 25.0):
         sample += f"; block time extrapolated by the block's sum of m*n ({scale:.2f}x)"
     else:
         sample += " (the whole block step)"
-    if wl.layers > 1:
-        sample += f"; one layer of {wl.layers}, the stack's time extrapolated as {wl.layers}x that layer"
-    return {"value": round(wl.T / (spent * scale * wl.layers), 2), "unit": "tokens/s", "cores": int(threads),
+    layers = layers or wl.layers
+    if layers > 1:
+        sample += f"; one layer of {layers}, the stack's time extrapolated as {layers}x that layer"
+    return {"value": round(wl.T / (spent * scale * layers), 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle", "sample": sample}
 
 
@@ -340,36 +341,54 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     return res
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
-    """The LLaMA-3B POET-FS stack: every layer's state resident at once (float32 W0, skew parameters, primitives,
-    saved powers, index sets, the materialized weights and the layer inputs kept for the backward); one step =
-    grouped build and forward of every layer in order, then the backward of every layer in reverse order to the
-    primitive gradients, the grouped adjoint and the AdamW update per layer. Weights and activations are drawn on the device with
-    the recipe's distributions (W0 row-normalized Gaussian, theta ~ N(0, 1e-3^2), X and dY ~ N(0, 1) in bf16).
-    Inputs of one shape are shared the way a transformer layer shares them (q/k/v read one input, gate/up one)."""
+    """A stack of `layers` LLaMA blocks with every layer's state resident at once: float32 W0 (and the bf16 copy the
+    activation side reads), skew parameters with their gradients and AdamW moments, primitives and operand copies,
+    saved Neumann powers, index sets, and what each linear keeps for its backward (the layer inputs, and Z on the
+    activation side or the materialized W on the weight side). One step = grouped build and forward of every layer
+    in order, then in reverse order the backward of every layer to the primitive gradients, the grouped adjoint and
+    the AdamW update. Weights and activations are drawn on the device with the recipe's distributions (W0
+    row-normalized Gaussian, theta ~ N(0, 1e-3^2), X and dY ~ N(0, 1) in bf16). Inputs of one shape are shared the
+    way a transformer layer shares them (q/k/v read one input, gate/up one).
+
+    Store or recompute (--recompute): "powers" keeps one set of saved-power buffers for all layers and rebuilds each
+    layer's factors before its backward (a second Cayley-Neumann chain per layer instead of k saved powers per side);
+    "weights" lets the weight-side backward form W = R W0 P again instead of keeping it from the forward."""
     T = wl.T
+    nl = args.layers or wl.layers
+    rec = set(x for x in args.recompute.split(",") if x and x != "none")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    specs = [wl.linears(layer) for layer in range(wl.layers)]
+    specs = [wl.linears(layer) for layer in range(nl)]
     shapes = specs[0]
     ws_lin = max(PoetLinear.workspace_bytes(l.m, l.n, T, B.side_of(l.R), B.side_of(l.P), l.act_dtype,
-                                            PI.pad_ld(l.n), PI.pad_ld(l.n), PI.pad_ld(l.m)) for l in shapes)
+                                            PI.pad_ld(l.n), PI.pad_ld(l.n), PI.pad_ld(l.m), args.path) for l in shapes)
     ws = torch.empty(ws_lin, dtype=torch.uint8, device="cuda")
     wide = max(PI.pad_ld(max(l.m, l.n)) for l in shapes)
     Ybuf = torch.empty((T, wide), dtype=torch.bfloat16, device="cuda")
     dXbuf = torch.empty((T, wide), dtype=torch.bfloat16, device="cuda")
     g = torch.Generator(device="cuda")
-    g.manual_seed(5000)
+    g.manual_seed(1000 * wl.cfg_id + 17)
     dYs = {}  # one upstream gradient per output width, shared by the layers
     for l in shapes:
         ldy = PI.pad_ld(l.m)
         if ldy not in dYs:
             dYs[ldy] = torch.randn((T, ldy), generator=g, device="cuda").to(torch.bfloat16)
     share = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+    mem = dict.fromkeys(("W0_f32", "W0_bf16_copy", "theta_grad_moments", "primitives_and_operand_copies",
+                         "saved_powers", "index_sets", "kept_inputs", "kept_Z_or_W", "folded_weights",
+                         "workspaces_and_transients"), 0)
+    shared_pw = {}  # position in the layer -> saved-power buffers reused by every layer (recompute "powers")
     layers = []
     for layer, lins in enumerate(specs):
         xs, es = {}, []
-        for lin in lins:
+        for j, lin in enumerate(lins):
             W0 = torch.randn((lin.m, lin.n), generator=g, device="cuda")
             W0 /= W0.norm(dim=1, keepdim=True)
             tR = torch.randn(B.poet_theta_len(B.side_of(lin.R)), generator=g, device="cuda") * PI.THETA_STD
@@ -377,12 +396,33 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
             ldx, ldy = PI.pad_ld(lin.n), PI.pad_ld(lin.m)
             pl = PoetLinear(lin.m, lin.n, T, B.side_of(lin.R), B.side_of(lin.P), lin.act_dtype, W0, tR, tP,
                             seed=wl.seed, linear_id=lin.linear_id, ldw=PI.pad_ld(lin.n), ldx=ldx, ldy=ldy, ws=ws,
-                            path="weight")
+                            path=args.path)
             del W0, tR, tP
+            if "powers" in rec:
+                if j not in shared_pw:
+                    shared_pw[j] = (pl.powersR, pl.powersP)
+                else:
+                    pl.powersR, pl.powersP = shared_pw[j]
             key = share[lin.name]
             if key not in xs:
                 xs[key] = torch.randn((T, ldx), generator=g, device="cuda").to(torch.bfloat16)
-            es.append({"spec": lin, "pl": pl, "X": xs[key], "W": pl.alloc_W(),
+                mem["kept_inputs"] += _nbytes(xs[key])
+            keep = None
+            if pl.act_path:
+                keep = pl.alloc_act(T, ldy)  # Z = X P^T W0^T
+            elif "weights" not in rec:
+                keep = pl.alloc_W()
+            mem["kept_Z_or_W"] += _nbytes(keep)
+            mem["W0_f32"] += _nbytes(pl.W0)
+            mem["W0_bf16_copy"] += _nbytes(pl.W0b)
+            mem["theta_grad_moments"] += sum(_nbytes(t) for t in (pl.thetaR, pl.thetaP, pl.dthetaR, pl.dthetaP, pl.mR,
+                                                                  pl.mP, pl.vR, pl.vP))
+            mem["primitives_and_operand_copies"] += sum(_nbytes(t) for t in (pl.primR, pl.primP, pl.qnormR,
+                                                                             pl.qnormP))
+            if "powers" not in rec or layer == 0:
+                mem["saved_powers"] += _nbytes(pl.powersR) + _nbytes(pl.powersP)
+            mem["index_sets"] += _nbytes(pl.idxR) + _nbytes(pl.idxP)
+            es.append({"spec": lin, "pl": pl, "X": xs[key], "keep": keep,
                        "Y": Ybuf.view(-1)[:T * ldy].view(T, ldy), "dX": dXbuf.view(-1)[:T * ldx].view(T, ldx),
                        "dY": dYs[ldy]})
         layers.append(es)
@@ -390,18 +430,39 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]]), 1), dtype=torch.uint8,
                       device="cuda")
     groups = [PoetGroup([e["pl"] for e in es], ws=gws) for es in layers]
+    for grp in groups:  # the group's operand copies and folded weights
+        for v in grp._ops.values():
+            mem["primitives_and_operand_copies"] += sum(_nbytes(t) for t in v)
+        for v in grp._fold.values():
+            mem["folded_weights"] += sum(_nbytes(t) for t in v)
     state_bytes = torch.cuda.memory_allocated() - base
-
+    mem["workspaces_and_transients"] = state_bytes - sum(mem.values())
     hp = optimizer()
+
+    def fwd(e):
+        pl = e["pl"]
+        if pl.act_path:
+            pl.forward_act(e["X"], e["Y"], e["keep"])
+        else:
+            pl.forward(e["X"], e["Y"], W_out=e["keep"])
+
+    def bwd(e):
+        pl = e["pl"]
+        if pl.act_path:
+            pl.backward_act_prims(e["X"], e["keep"], e["dY"], e["dX"])
+        else:
+            pl.backward_prims(e["X"], e["dY"], e["dX"], W=e["keep"])
 
     def stack_step():
         for es, grp in zip(layers, groups):
             grp.build()
             for e in es:
-                e["pl"].forward(e["X"], e["Y"], W_out=e["W"])
+                fwd(e)
         for es, grp in zip(reversed(layers), reversed(groups)):
+            if "powers" in rec:  # the saved powers were overwritten by later layers: form them again
+                grp.build()
             for e in reversed(es):
-                e["pl"].backward_prims(e["X"], e["dY"], e["dX"], W=e["W"])
+                bwd(e)
             grp.finish_backward()
             grp.optimizer_step(hp)
 
@@ -415,7 +476,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     prof = _profile(B, stack_step, 1)
     log("stack merge")
     all_specs = [e["spec"] for es in layers for e in es]
-    merge_bytes = sum(8.0 * l.m * l.n for l in all_specs)
+    merge_bytes = sum((10.0 if e["pl"].act_path else 8.0) * e["spec"].m * e["spec"].n for es in layers for e in es)
 
     def build_all():
         for grp in groups:
@@ -431,28 +492,38 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     n_theta = sum(B.poet_theta_len(B.side_of(l.R)) + B.poet_theta_len(B.side_of(l.P)) for l in all_specs)
     fl = algorithmic_flops(all_specs)
     dom, roof = _roofline(prof, PEAK_BF16_TFLOPS)
+    act = all(e["pl"].act_path for es in layers for e in es)
+    gib = 1.0 / 2 ** 30
     res = {
         "value": round(T / (ms_total / 1e3), 1), "ms_per_step": round(ms_total, 4), "ms_fwd_bwd": round(ms_step, 4),
         "ms_fwd_bwd_median": round(statistics.median(per), 4), "ms_fwd_bwd_min": round(min(per), 4),
         "ms_merge_all_linears": round(ms_merge, 4),
-        "config": {"workload": wl.name, "hidden": wl.hidden, "ffn": wl.ffn, "tokens": T, "mode": "FS",
-                   "fraction": wl.frac, "k": wl.k, "layers": wl.layers, "linears": len(all_specs),
-                   "factor_application": "weight", "grouped_side_steps": True, "merge_period": args.merge_period},
+        "config": {"workload": wl.name if nl == wl.layers else f"{wl.name}_x{nl}layers", "hidden": wl.hidden,
+                   "ffn": wl.ffn, "tokens": T, "mode": "BS" if wl.mode == PI.MODE_BS else "FS", "block": wl.b,
+                   "fraction": wl.frac, "k": wl.k, "layers": nl, "linears": len(all_specs),
+                   "factor_application": "activations" if act else "weight", "grouped_side_steps": True,
+                   "merge_period": args.merge_period, "recompute": sorted(rec) or ["none"]},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3),
         "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
         "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stage_ms_per_step": {k: round(v["ms"], 4) for k, v in prof.items()},
-        # device memory: measured peak of the whole run, and the resident state before the first step (W0 float32,
-        # theta, primitives, saved powers, index sets, kept weights and inputs, workspaces); the dense figure is the
-        # float32 weight, its gradient and the two AdamW moments of the same linears (16 bytes per weight element,
-        # arithmetic, not measured)
-        "memory": {"peak_hbm_gib": round(peak_bytes / 2**30, 2), "resident_state_gib": round(state_bytes / 2**30, 2),
+        # device memory: the measured peak of the whole run and the resident state before the first step, by kind
+        # (every allocation of the run, summed from the tensors' sizes); for comparison, the weight-state of dense
+        # AdamW training of the same linears: float32 weight, its gradient and the two moments, 16 bytes per weight
+        # element (arithmetic, not measured; the activations a layer keeps are the same for both)
+        "memory": {"peak_hbm_gib": round(peak_bytes * gib, 2), "resident_state_gib": round(state_bytes * gib, 2),
+                   "resident_by_kind_gib": {k: round(v * gib, 3) for k, v in mem.items()},
                    "linear_weight_elements": n_params, "trainable_skew_params": n_theta,
-                   "dense_adamw_weight_grad_moments_gib": round(16.0 * n_params / 2**30, 2)},
+                   "poet_weight_state_gib": round((mem["W0_f32"] + mem["W0_bf16_copy"] + mem["theta_grad_moments"])
+                                                  * gib, 2),
+                   "dense_adamw_weight_grad_moments_gib": round(16.0 * n_params * gib, 2)},
     }
     g = _hbm_class(prof["gather"])
     if g is not None:
         res["gather_scatter"] = g
+    del layers, groups
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res
 
 
@@ -462,6 +533,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="run the workload's block as a stack of this many layers, all resident (the LLaMA-3B "
+                         "workload is a 24-layer stack by default)")
+    ap.add_argument("--recompute", default="none",
+                    help="with a stack: comma-separated parts formed again in the backward instead of kept from "
+                         "the forward: powers (the saved Neumann powers), weights (the materialized W)")
     ap.add_argument("--merge-period", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fs", action="store_true",
@@ -491,7 +568,7 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     wl = PI.WORKLOADS[args.workload]
-    if wl.layers > 1:
+    if (args.layers or wl.layers) > 1:
         res = run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup)
     else:
         res = run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup)
@@ -500,7 +577,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == PI.DT_BF16 else "f32",
            "data": "synthetic", "config": res.pop("config"), "roofline": res.pop("roofline")}
     out.update(res)
-    if args.workload == 3 and not args.no_fs:
+    if args.workload == 3 and args.layers <= 1 and not args.no_fs:
         fs = PI.WORKLOADS[4]
         log("extra: the POET-FS block")
         r4 = run_block(fs, args, torch, B, PI, PoetLinear, PoetGroup)
@@ -515,7 +592,7 @@ def main():
         out["calib_copy_bytes"] = nbytes
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, layers=args.layers)
     print(json.dumps(out), flush=True)
 
 
