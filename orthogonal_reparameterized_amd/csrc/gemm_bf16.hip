@@ -3,13 +3,14 @@
 //   weight side        factors applied to W0, primitive-gradient contractions, Cayley-Neumann power chain
 //                      and its adjoint (batched over the primitives of a side)
 //
-// Workgroup tile 256 x 256 x 64, 4 waves in a 2 x 2 grid, each wave 128 x 128 as 4 x 4 v_mfma_f32_32x32x16_bf16.
+// Workgroup tile 256 x 256 x 64, 8 waves in a 2 x 4 grid (two per SIMD), each wave 128 x 64 as 4 x 2
+// v_mfma_f32_32x32x16_bf16.
 // Operands go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a wave writes the 16
 // bytes at the wave's LDS base + 16 l, from any global address it chooses), in a two-stage ring: the DMA of
 // K-tile t+1 runs while the MFMAs consume tile t, one barrier per tile, placed before the last k-step so that the
-// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs (one DMA instruction and one
-// fragment read after each of its MFMAs). A k-step's fragment reads for the next k-step are issued between its
-// MFMAs (one MFMA, two reads), which measured ~3% faster than one burst.
+// next DMA and the next tile's first fragment reads overlap that k-step's MFMAs (one DMA instruction after each of
+// its MFMAs, and the next tile's first fragment reads from the second MFMA on). A k-step's fragment reads for the
+// next k-step are issued between its MFMAs (one MFMA, two reads), which measured ~3% faster than one burst.
 // Both stage layouts are 32 KB:
 //   K-major operand: 256 rows x 128 B; the 16-byte chunk index is XOR-ed with f(row mod 32) =
 //     (row & 7) ^ ((row >> 3) & 3): 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
@@ -19,7 +20,7 @@
 //     group, lane j supplies the address of 4 consecutive elements of k-row j/4; lane i receives the elements
 //     of column i of those 4 k-rows: an MFMA fragment of the transposed operand).
 // Rows or columns past M / N are fetched from a clamped (valid) address: they only reach outputs that are
-// never stored. The K tail of the last tile is zeroed in LDS after its DMA lands. A wave's finished 128 x 128
+// never stored. The K tail of the last tile is zeroed in LDS after its DMA lands. A wave's finished 128 x 64
 // tile leaves through LDS as row-contiguous vector stores.
 //
 // Work decomposition: (batch, split, tile) triples in one 1-D grid. Workgroup id w runs on XCD w % 8, so each
@@ -77,7 +78,7 @@ constexpr int WAIT_LGKM0 = 0xC07F;  // lgkmcnt(0)
 constexpr int WAIT_VM0 = 0x0F70;    // vmcnt(0)
 
 // Direct global->LDS DMA of one 256 x 64 operand tile. Per-thread source offsets are fixed for the K loop.
-template <bool KMAJ>
+template <bool KMAJ, int NW>
 struct Operand {
   const char* base;  // operand base (bytes)
   uint32_t ld2;      // leading dimension in bytes
@@ -90,17 +91,17 @@ struct Operand {
     ld2 = (uint32_t)(ld * 2);
     R = R_; K = K_;
     if constexpr (KMAJ) {
-      // instruction j of wave w fills rows 8 (4 j + w) + lane / 8, physical chunk lane % 8, whose logical
+      // instruction j of wave w fills rows 8 (NW j + w) + lane / 8, physical chunk lane % 8, whose logical
       // chunk (k offset / 8 inside the tile) is chk
-      const int r32 = 8 * wave + (lane >> 3);
+      const int r32 = (8 * wave + (lane >> 3)) & 31;
       chk = (lane & 7) ^ swz(r32);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = min(r0 + 32 * j + r32, R - 1);
+      for (int j = 0; j < 32 / NW; ++j) {
+        const int row = min(r0 + 8 * (NW * j + wave) + (lane >> 3), R - 1);
         off[j] = (uint32_t)row * ld2;
       }
     } else {
-      // instruction j of wave w fills k-rows 2 (4 j + w) + lane / 32, physical 16-byte chunk lane % 32
+      // instruction j of wave w fills k-rows 2 (NW j + w) + lane / 32, physical 16-byte chunk lane % 32
       const int pc = lane & 31;
       const int kr4 = (2 * wave + (lane >> 5)) & 3;
       const int lch = (((pc >> 2) ^ kr4) << 2) | (pc & 3);
@@ -114,30 +115,31 @@ struct Operand {
 
   // DMA instruction j (of 8) of the tile at k0 into stage st
   __device__ __forceinline__ void dma_one(char* __restrict__ st, int k0, int j, int wave, int lane) const {
-    char* dst = st + (4 * j + wave) * 1024;
+    char* dst = st + (NW * j + wave) * 1024;
     uint32_t o;
     if constexpr (KMAJ) {
       const int kmax = ((K + 7) / 8) * 8 - 8;  // keep the 16-byte read inside the row's first ceil8(K) elements
       o = off[j] + (uint32_t)min(k0 + 8 * chk, kmax) * 2;
     } else {
-      const int kr = min(k0 + 2 * (4 * j + wave) + (lane >> 5), K - 1);
+      const int kr = min(k0 + 2 * (NW * j + wave) + (lane >> 5), K - 1);
       o = off[j] + (uint32_t)kr * ld2;
     }
     __builtin_amdgcn_global_load_lds((gbl_void*)(base + o), (lds_void*)dst, 16, 0, 0);
   }
   __device__ __forceinline__ void dma(char* __restrict__ st, int k0, int wave, int lane) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma_one(st, k0, j, wave, lane);
+    for (int j = 0; j < 32 / NW; ++j) dma_one(st, k0, j, wave, lane);
   }
 
   // zero the part of a staged tile that lies at k >= kend (kv = kend - k0 valid k values, 0 < kv < 64)
   __device__ __forceinline__ void zero_tail(char* __restrict__ st, int kv, int tid) const {
     if constexpr (KMAJ) {
+      if (tid >= 256) return;
       const int row = tid, s = swz(row & 31);
       for (int k = kv; k < BK; ++k)
         *reinterpret_cast<short*>(st + row * 128 + (((k >> 3) ^ s) << 4) + (k & 7) * 2) = 0;
     } else {
-      for (int e = kv * 32 + tid; e < BK * 32; e += 256)
+      for (int e = kv * 32 + tid; e < BK * 32; e += 64 * NW)
         *reinterpret_cast<u32x4*>(st + e * 16) = u32x4{0, 0, 0, 0};
     }
   }
@@ -177,32 +179,37 @@ __device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, 
   if (g.Acc) g.Acc[(int64_t)z * g.sAcc + (int64_t)row * g.ldacc + col] += g.gamma * out;
 }
 
-// Store a wave's 128 x 128 accumulator tile at out (row pitch ld elements, dtype dt; rlim x clim of it valid)
-// through the wave's EP_BYTES of LDS, one 32-row band at a time: the band is written in accumulator order
+// Store a wave's (32 WM) x (32 WN) accumulator tile at out (row pitch ld elements, dtype dt; rlim x clim of it valid)
+// through the wave's Ep<WN>::BYTES of LDS, one 32-row band at a time: the band is written in accumulator order
 // (row pitch EP floats, so the two half-waves land in disjoint banks) and read back as row-contiguous float4
 // chunks, which go out as 16-byte (float32) or 8-byte (bf16) stores when the row is aligned for them. The region
 // is the wave's own and one wave's LDS accesses complete in order, so the bands need no barrier: the global
 // stores of one band stay in flight while the next is staged (a workgroup barrier would wait for all of them).
-constexpr int EP = 136, EP_BYTES = 32 * EP * 4;
-__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* lds, void* out, int dt, int64_t ld,
+template <int WN>
+struct Ep {
+  static constexpr int EP = 32 * WN + 8, BYTES = 32 * EP * 4;
+};
+template <int WM, int WN>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char* lds, void* out, int dt, int64_t ld,
                                                int rlim, int clim, int lane) {
+  constexpr int EP = Ep<WN>::EP, NV = 4 * WN, PR = 8 * WN;  // float4 per lane per band, float4 per row
   float* ep = reinterpret_cast<float*>(lds);
   const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(out) % (dt == BF16 ? 8 : 16)) == 0;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < WM; ++a) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < WN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * EP + b * 32 + (lane & 31)] = acc[a][b][r];
-    f32x4 vv[16];
+    f32x4 vv[NV];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int c = lane + 64 * u;
-      vv[u] = *reinterpret_cast<const f32x4*>(ep + (c >> 5) * EP + (c & 31) * 4);
+      vv[u] = *reinterpret_cast<const f32x4*>(ep + (c / PR) * EP + (c % PR) * 4);
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = lane + 64 * u, rr = c >> 5, c4 = (c & 31) * 4, row = a * 32 + rr;
+    for (int u = 0; u < NV; ++u) {
+      const int c = lane + 64 * u, rr = c / PR, c4 = (c % PR) * 4, row = a * 32 + rr;
       if (row >= rlim || c4 >= clim) continue;
       const f32x4 v = vv[u];
       const int64_t o = (int64_t)row * ld + c4;
@@ -234,9 +241,23 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], char* 
 
 // TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
 // GROUP: the launch holds several problems of one shape (FastArgs nprob and prob).
-template <bool AK, bool BK_, int TAG, bool GROUP = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(const FastArgs fa_) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
+// Waves per workgroup and their grid over the 256 x 256 tile. Eight waves (two per SIMD, wave tile 128 x 64) measured
+// 7-12% faster than four (one per SIMD, 128 x 128) on every token-GEMM shape, bit-identical: with one wave per SIMD
+// each barrier and copy wait stalls the matrix core, while a second wave keeps issuing MFMAs (sixteen waves, 64 x 64,
+// ran the same as eight). The extra fragment reads (LDS active ~13% of the cycles with four waves) do not bind.
+constexpr int KNW = 8;
+template <int NW> struct WaveGrid;
+template <> struct WaveGrid<4> { static constexpr int GR = 2, GC = 2; };   // wave tile 128 x 128
+template <> struct WaveGrid<8> { static constexpr int GR = 2, GC = 4; };   // 128 x 64
+constexpr int smem_bytes(int nw) {
+  return 4 * STAGE > nw * Ep<8 / WaveGrid<KNW>::GC>::BYTES ? 4 * STAGE : nw * Ep<8 / WaveGrid<KNW>::GC>::BYTES;
+}
+
+template <bool AK, bool BK_, int TAG, bool GROUP = false, int NW = KNW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(const FastArgs fa_) {
+  constexpr int WM = 8 / WaveGrid<NW>::GR, WN = 8 / WaveGrid<NW>::GC;  // 32 x 32 blocks per wave
+  constexpr int NDMA = 32 / NW;        // DMA instructions per operand per wave and tile
+  __shared__ __attribute__((aligned(1024))) char smem[smem_bytes(NW)];
   const GemmDesc& g = fa_.g;
   const int ntm = fa_.ntm, ntn = fa_.ntn, splits = fa_.splits;
   const int ntiles = g.batch * splits * ntm * ntn;
@@ -291,18 +312,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the wave index is uniform: as a scalar, the LDS addresses derived from it (DMA destinations in M0) need no
   // per-instruction readfirstlane
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = (wave >> 1) * 128, wc = (wave & 1) * 128;
+  const int wr = (wave / WaveGrid<NW>::GC) * 32 * WM, wc = (wave % WaveGrid<NW>::GC) * 32 * WN;
 
-  Operand<AK> oa;
-  Operand<BK_> ob;
+  Operand<AK, NW> oa;
+  Operand<BK_, NW> ob;
   oa.init(reinterpret_cast<const __bf16*>(Ab) + (int64_t)z * g.sA, lda, m0, M, ke, wave, lane);
   ob.init(reinterpret_cast<const __bf16*>(Bb) + (int64_t)z * g.sB, ldb, n0, N, ke, wave, lane);
 
-  f32x16 acc[4][4];
+  f32x16 acc[WM][WN];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WM; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < WN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Two-stage ring: the DMA of tile t+1 is in flight while tile t is multiplied. The barrier that retires tile
   // t's stage (and confirms tile t+1) sits before the MFMAs of tile t's last k-step, so the DMA of tile t+2 and
   // the LDS reads of tile t+1's first fragments are issued while those MFMAs run.
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][WM], fb[2][WN];
   if (nk > 0) {
     oa.dma(smem, kb, wave, lane);
     ob.dma(smem + STAGE, kb, wave, lane);
@@ -327,9 +348,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       ob.dma(smem + 3 * STAGE, kb + BK, wave, lane);
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) fa[0][a] = frag<AK>(smem, wr + a * 32, 0, lane);
+    for (int a = 0; a < WM; ++a) fa[0][a] = frag<AK>(smem, wr + a * 32, 0, lane);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) fb[0][b] = frag<BK_>(smem + STAGE, wc + b * 32, 0, lane);
+    for (int b = 0; b < WN; ++b) fb[0][b] = frag<BK_>(smem + STAGE, wc + b * 32, 0, lane);
   }
   for (int kt = 0; kt < nk; ++kt) {
     char* sa = smem + (kt & 1) * 2 * STAGE;
@@ -343,21 +364,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
+      for (int a = 0; a < WM; ++a) fa[c ^ 1][a] = frag<AK>(sa, wr + a * 32, ks + 1, lane);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
+      for (int b = 0; b < WN; ++b) fb[c ^ 1][b] = frag<BK_>(sb, wc + b * 32, ks + 1, lane);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < WM; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < WN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][b], acc[a][b], 0, 0, 0);
       // the fragment reads go out between the MFMAs (one MFMA, two reads), not as one burst ahead of them
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < (WM + WN) / 2; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, WM * WN - (WM + WN) / 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     char* na = smem + ((kt + 1) & 1) * 2 * STAGE;
@@ -376,40 +397,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // last k-step: its 16 MFMAs each followed by one DMA instruction of tile kt+2 (into the stage tile kt held,
-    // which no wave reads any more) and, from the fifth on, by one fragment read of tile kt+1's first k-step (at
-    // least four MFMAs before their use), so the matrix core keeps running while they issue. They run without
+    // last k-step: its MFMAs each followed by one DMA instruction of tile kt+2 (into the stage tile kt held, which
+    // no wave reads any more) and, from MFMA Q0 on, by the fragment reads of tile kt+1's first k-step, so the matrix
+    // core keeps running while they issue (with eight waves the other wave of the SIMD covers the shorter gap
+    // between the last reads and their use). They run without
     // conditions: past the end the copies read clamped (valid) addresses, and in the last tile (no barrier above,
     // other waves may still read its stage) they go to the other stage, which nothing reads again; the epilogue's
     // first barrier waits for them. The fragments read past the end are never used.
     char* da = more ? sa : na;
     const int k2 = kb + (kt + 2) * BK;
+    constexpr int Q0 = NW == 4 ? 4 : (NW == 8 ? 1 : 0);  // first MFMA followed by a fragment read of the next tile
+    constexpr int NR = WM + WN, PER = NR > WM * WN ? 2 : 1;   // next-tile fragment reads, per MFMA
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int a = q >> 2, b = q & 3;
+    for (int q = 0; q < WM * WN; ++q) {
+      const int a = q / WN, b = q % WN;
       acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][a], fb[1][b], acc[a][b], 0, 0, 0);
-      if (q < 8) oa.dma_one(da, k2, q, wave, lane);
-      else ob.dma_one(da + STAGE, k2, q - 8, wave, lane);
-      if (q >= 4 && q < 12) {
-        const int r = q - 4;
-        if (r < 4) fa[0][r] = frag<AK>(na, wr + r * 32, 0, lane);
-        else fb[0][r - 4] = frag<BK_>(na + STAGE, wc + (r - 4) * 32, 0, lane);
+      if (q < NDMA) oa.dma_one(da, k2, q, wave, lane);
+      else if (q < 2 * NDMA) ob.dma_one(da + STAGE, k2, q - NDMA, wave, lane);
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int r = (q - Q0) * PER + t;
+        if (q >= Q0 && r < NR) {
+          if (r < WM) fa[0][r] = frag<AK>(na, wr + r * 32, 0, lane);
+          else fb[0][r - WM] = frag<BK_>(na + STAGE, wc + (r - WM) * 32, 0, lane);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // the wave's 128 x 128 tile goes out through LDS (every wave is past its last fragment read first)
+  // the wave's tile goes out through LDS (every wave is past its last fragment read first)
   __syncthreads();
   const int wrow0 = m0 + wr, wcol0 = n0 + wc;
   if (fa_.use_part) {  // raw partial tile; the reduction kernel sums the splits and applies the epilogue
     float* pb = g.part + ((int64_t)(s * g.batch + zg) * g.M + wrow0) * g.N + wcol0;
-    store_tile_lds(acc, smem + wave * EP_BYTES, pb, F32, g.N, M - wrow0, N - wcol0, lane);
+    store_tile_lds<WM, WN>(acc, smem + wave * Ep<WN>::BYTES, pb, F32, g.N, M - wrow0, N - wcol0, lane);
     return;
   }
   if (!g.C) return;
   char* cb = Cb + ((int64_t)z * g.sC + (int64_t)wrow0 * g.ldc + wcol0) * dtype_size(g.c_dt);
-  store_tile_lds(acc, smem + wave * EP_BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane);
+  store_tile_lds<WM, WN>(acc, smem + wave * Ep<WN>::BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane);
 }
 
 // Sum the split-K partials of every output element in split order, then apply the epilogue.
@@ -503,7 +530,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
                                   (double)g.M * g.N * ((g.C ? dtype_size(g.c_dt) : 0) + (g.D ? 4 : 0) +
                                                        (g.C2 ? dtype_size(g.c2_dt) : 0) + (g.Acc ? 8 : 0)));
   ProfScope prof(g.kclass, st, flops, bytes);
-  const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
+  const dim3 grid(((tiles * S + 7) / 8) * 8), block(64 * KNW);
   if (g.kclass == 0 && g.a_kmajor && g.b_kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 1>), grid, block, 0, st, fa);
   else if (g.kclass == 1 && g.a_kmajor && !g.b_kmajor)
@@ -570,7 +597,7 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
   const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (double)g.M * g.N * dtype_size(g.c_dt));
   ProfScope prof(g.kclass, st, flops, bytes);
-  const dim3 grid(((tiles * S + 7) / 8) * 8), block(256);
+  const dim3 grid(((tiles * S + 7) / 8) * 8), block(64 * KNW);
   if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 0, true>), grid, block, 0, st, fa);
   else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 0, true>), grid, block, 0, st, fa);
   else if (g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<false, true, 0, true>), grid, block, 0, st, fa);
