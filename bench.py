@@ -213,6 +213,30 @@ def _roofline(prof, peak, traffic=None):
                  "flops_per_launch": d["flops"] / max(d["launches"], 1)}
 
 
+def mfma_probe(torch, B, workgroups: int = 2048, iters: int = 1024, warm_launches: int = 100):
+    """The bf16 matrix-core rate this GPU sustains (poet_mfma_probe: MFMAs on registers only, eight waves per
+    workgroup, eight rounds of workgroups per CU), timed with events on the current stream, the library's launch
+    stream: the ceiling that the clock held under full matrix load leaves a GEMM, next to the published peak. The
+    clock rises only under sustained load (a burst of 1 ms after idle runs about a fifth slower), so about 100 ms of
+    probe launches run first; the median of the next 9 is reported."""
+    out = torch.empty(workgroups * 8, dtype=torch.float32, device="cuda")
+    for _ in range(warm_launches):
+        B.poet_mfma_probe(iters, workgroups, out)
+    torch.cuda.synchronize()
+    times, flops = [], 0.0
+    for _ in range(9):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = B.poet_mfma_probe(iters, workgroups, out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    tf = flops / (ms / 1e3) / 1e12
+    return {"achieved": round(tf, 1), "unit": "TFLOP/s", "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "ms_median": round(ms, 4), "workgroups": workgroups, "mfma_per_wave": 4 * iters}
+
+
 def _hbm_class(p):
     """Achieved GB/s of a data-movement kernel class on its algorithmic bytes."""
     if not p["launches"] or p["ms"] <= 0:
@@ -582,6 +606,11 @@ def main():
         log("extra: the POET-FS block")
         r4 = run_block(fs, args, torch, B, PI, PoetLinear, PoetGroup)
         out["fs_block"] = {"unit": "tokens/s", **r4}
+    log("matrix-core probe")
+    out["mfma_probe"] = mfma_probe(torch, B)
+    for r in [out["roofline"]] + ([out["fs_block"]["roofline"]] if "fs_block" in out else []):
+        if r.get("peak") == PEAK_BF16_TFLOPS and out["mfma_probe"]["achieved"] > 0:
+            r["frac_of_sustained"] = round(r["achieved"] / out["mfma_probe"]["achieved"], 4)
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)

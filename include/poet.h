@@ -192,7 +192,9 @@ poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const fl
  * (dX' = dY (R W0)): the same products associated the other way, each with one bf16 rounding of the folded
  * weight in place of the rounding of X' or dZ.
  * Both sides POET-BS and bf16 activations (poet_act_path_supported); every product is a bf16 GEMM with float32
- * accumulation and the primitives enter as bf16 copies. W0b is W0 in bf16 (row pitch ldw), made once by
+ * accumulation, and every factor is applied as identity + delta: the bf16 copy of the delta F - I is the MFMA
+ * operand and the identity part adds the factor's input (X, Z, dY, dX' or W0b) in float32 before the output's one
+ * rounding. W0b is W0 in bf16 (row pitch ldw), made once by
  * poet_weight_shadow and kept current by passing it as poet_merge's W0_shadow. Workspaces: POET_OP_FWD_ACT and
  * POET_OP_BWD_ACT of poet_workspace_bytes. */
 int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below apply to L, else 0 */
@@ -200,10 +202,10 @@ int poet_act_path_supported(const poet_layer* L);  /* 1 when the calls below app
 /* W0_shadow [m x ldw] act dtype out: W0 rounded to the act dtype (round to nearest even). */
 poet_status poet_weight_shadow(const poet_layer* L, const float* W0, void* W0_shadow, void* stream);
 
-/* opsR/opsP (nullable, bf16 in): operand copies of the primitives, 3 * poet_prim_len(side) elements: block p
- * of F at offset p*bp*bp and its transpose at num_prims*bp*bp + p*bp*bp, both zero outside the block's c x c
- * corner, then at 2*num_prims*bp*bp + p*bp*bp block p of F as it is (row-major, bf16 of the primitive, padding
- * included); poet_build_orthogonal_group writes them. Each bp x bp block M (M = F or F^T) of the first two parts is
+/* opsR/opsP (nullable, bf16 in): operand copies of the deltas D = F - I of the primitives F, 3 * poet_prim_len(side)
+ * elements: block p of D at offset p*bp*bp and its transpose at num_prims*bp*bp + p*bp*bp, both zero outside the
+ * block's c x c corner, then at 2*num_prims*bp*bp + p*bp*bp block p of D over the whole padded block (row-major,
+ * bf16 of F - I; zero in the identity padding); poet_build_orthogonal_group writes them. Each bp x bp block M (M = F or F^T) of the first two parts is
  * stored row-major (M(i, j) at i*bp + j) unless bp is a multiple of 32; then it is stored in the order the MFMA
  * fragments of the application kernel are loaded: M(i, j) at ((i/32 * bp/16 + j/16) * 64 + (j/8 % 2) * 32 +
  * i % 32) * 8 + j % 8. NULL: the call makes what it needs in its workspace from primR/primP. */
@@ -267,7 +269,8 @@ poet_status poet_adjoint_group(int32_t count, const poet_side* sides, const floa
 
 /* The factors of count linears folded into their bf16 weights (the weights the folded activation-side calls
  * take): W0P[i] = W0b[i] P_i and RW0[i] = R_i W0b[i] (bf16, m x ldw, row pitch ldw), one batched product per factor
- * over its blocks, products of one shape in shared launches. The tables W0P and RW0 are nullable, and so is each
+ * over its blocks, products of one shape in shared launches; the factor enters as identity + delta (W0b plus the
+ * product with the bf16 delta, one rounding). The tables W0P and RW0 are nullable, and so is each
  * entry (nothing written for it); opsR / opsP (nullable tables and entries) are the operand copies of
  * poet_build_orthogonal_group, whose row-order part is used; without them the primitives are converted in the
  * workspace. Both sides POET-BS, bf16 activations. ws: poet_fold_group_workspace_bytes(count, layers) bytes. */
@@ -368,6 +371,14 @@ typedef struct poet_gemm_desc {
   float* part; size_t part_elems;
 } poet_gemm_desc;
 poet_status poet_debug_gemm(const poet_gemm_desc* d, int force_generic, int* used_fast, void* stream);
+
+/* Measurement aid, not an operation of the method: the sustained rate of the bf16 matrix cores. Launches
+ * `workgroups` workgroups of 8 waves (two per SIMD); each wave issues 4 * iters v_mfma_f32_32x32x16_bf16 on register
+ * operands (32768 flops each) with no memory traffic, then writes one float of its sums to out (device, float32,
+ * workgroups * 8 elements, caller-owned). The caller times it (events on `stream`): flops / time is the ceiling
+ * that the clock held under full matrix load allows a GEMM; a counter run over it shows what a fully busy matrix
+ * core reads. iters >= 1, 1 <= workgroups <= 65535, out non-null, else POET_E_ARG. */
+poet_status poet_mfma_probe(int64_t iters, int32_t workgroups, float* out, void* stream);
 
 /* Kernel classes timed by the optional launch profiler. */
 enum {

@@ -26,6 +26,8 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
+           "poet_mfma_probe",
+           "poet_mfma_probe",
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
@@ -154,6 +156,10 @@ def lib() -> ctypes.CDLL:
     L.poet_profile_query.restype = ctypes.c_int
     L.poet_debug_gemm.argtypes = [P(poet_gemm_desc), ctypes.c_int, P(ctypes.c_int), VP]
     L.poet_debug_gemm.restype = ctypes.c_int
+    L.poet_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, VP, VP]
+    L.poet_mfma_probe.restype = ctypes.c_int
+    L.poet_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, VP, VP]
+    L.poet_mfma_probe.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -227,6 +233,22 @@ def poet_debug_gemm(desc: poet_gemm_desc, force_generic: bool = False, stream=No
     _check(lib().poet_debug_gemm(ctypes.byref(desc), int(bool(force_generic)), ctypes.byref(used), _stream(stream)),
            "poet_debug_gemm")
     return bool(used.value)
+
+
+def poet_mfma_probe(iters: int, workgroups: int, out, stream=None) -> float:
+    """Launch the matrix-core rate probe (workgroups x 8 waves, 4 * iters 32x32x16 bf16 MFMAs per wave; out: float32
+    device tensor of at least workgroups * 8 elements). Returns the flops it issues; the caller times the launch."""
+    _need(out, "out", workgroups * 8, ("float32",))
+    _check(lib().poet_mfma_probe(int(iters), int(workgroups), _ptr(out), _stream(stream)), "poet_mfma_probe")
+    return 32768.0 * 4 * iters * 8 * workgroups
+
+
+def poet_mfma_probe(iters: int, workgroups: int, out, stream=None) -> float:
+    """Launch the matrix-core rate probe (workgroups x 8 waves, 4 * iters 32x32x16 bf16 MFMAs per wave; out: float32
+    device tensor of at least workgroups * 8 elements). Returns the flops it issues; the caller times the launch."""
+    _check(lib().poet_mfma_probe(int(iters), int(workgroups), _ptr(out, "out", 4 * 8 * int(workgroups), "float32"),
+                                 _stream(stream)), "poet_mfma_probe")
+    return 32768.0 * 4 * iters * 8 * workgroups
 
 
 def poet_profile_query(kclass: int) -> dict:

@@ -1,9 +1,11 @@
 // Block-diagonal factor applied to bf16 activations (POET reparameterization W = R W0 P with the factors moved
 // onto the activations: X P^T, Z R^T, dY R, dX' P):
 //   out[t, block] = in[t, block] F_block^T   (trans)   or   in[t, block] F_block,
-// for every block of the factor (size c = min(bp, d - b bp), bp <= 256) and every token t. F is the float32
-// primitive, rounded to bf16 as the MFMA operand (k_act_operand writes it as bf16 rows); accumulation is float32
-// and the output is rounded to bf16.
+// for every block of the factor (size c = min(bp, d - b bp), bp <= 256) and every token t, with F taken as identity
+// + delta: the MFMA operand is the delta F - I rounded to bf16 (k_act_operand writes it as bf16 rows), the float32
+// accumulators start from the input element itself (the identity part, exact), and only the output is rounded to
+// bf16. Rounding the whole factor instead would cost a rounding of its diagonal 1 + O(|Q|^2)
+// at the bf16 step of 2^-8 near 1, an error as large as the output's own rounding.
 //
 // Weight-stationary: a workgroup owns one block and a run of 32-token tiles. Its 4 waves each hold 64 output
 // columns of the block's operand (all of K, 16 k-steps x 2 column tiles of bf16x8 fragments: 128 registers),
@@ -46,8 +48,8 @@ struct ActArgs {
   int ngrp;         // token groups: ceil(ceil(T / TM) / tiles_per_wg)
 };
 
-// Operand rows for the kernel below: Bt[b][j][k] = bf16(B(k, j)) with B(k, j) = F_b[j][k] (trans) or F_b[k][j],
-// for j, k < c (the block's size) and zero elsewhere in the bp x bp block, in fragment order where
+// Operand rows for the kernel below: Bt[b][j][k] = bf16(B(k, j)) with B the delta F_b - I, B(k, j) = F_b[j][k] - [j = k]
+// (trans) or F_b[k][j] - [j = k], for j, k < c (the block's size) and zero elsewhere in the bp x bp block, in fragment order where
 // act_frag_layout(bp), else in row order. Row order: consecutive threads take consecutive k (trans: coalesced
 // reads) or consecutive j (no trans: the strided side is the read of F, coalesced in j). Fragment order:
 // consecutive threads write consecutive elements.
@@ -70,7 +72,7 @@ __global__ void k_act_operand(const float* __restrict__ F, int bp, int d, int nb
     }
     const bool in = j < c && k < c;
     const float f = F[(int64_t)b * per + (in ? (trans ? (int64_t)j * bp + k : (int64_t)k * bp + j) : 0)];
-    Bt[(int64_t)b * per + (frag ? rem : (int64_t)j * bp + k)] = (__bf16)(in ? f : 0.f);
+    Bt[(int64_t)b * per + (frag ? rem : (int64_t)j * bp + k)] = (__bf16)(in ? f - (j == k ? 1.f : 0.f) : 0.f);
   }
 }
 
@@ -212,11 +214,24 @@ __global__ __launch_bounds__(AT, 2) void act_apply_kernel(const ActArgs a) {
     };
     bf16x4 outv[2][4];  // [u][q]: four consecutive columns of one token, rounded to bf16
     {
+      // the identity part: the accumulators start from the input element of the same token and column, read from the
+      // staged tile (row j32, logical chunk 8 wave + 4 u + q, elements 4 (lane / 32) .. 4 (lane / 32) + 3: one 8-byte
+      // read, in flight together with the first fragment reads); the products of the delta add to it in float32
+      bf16x4 xid[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t ch = (uint32_t)(8 * wave + 4 * u + q);
+          xid[u][q] = *reinterpret_cast<const bf16x4*>(A + (uint32_t)j32 * ROWB + (((ch ^ xkey) << 4) | (hb << 3)));
+        }
       f32x16 acc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][q * 4 + e] = (float)xid[u][q][e];
       // k-steps pipelined by hand: the fragment of step ks + 2 is read while step ks multiplies, and a scheduling
       // barrier per step keeps the compiler from hoisting every read (and its registers) to the top. The product is
       // taken transposed, out^T = B^T in^T (the operand fragments as the left factor, the token fragments as the

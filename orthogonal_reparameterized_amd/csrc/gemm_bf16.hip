@@ -52,7 +52,7 @@ constexpr int STAGE = 256 * BK * 2;  // bytes of one operand's stage (both layou
 
 constexpr int MAXGP = 16;
 struct GroupEntry {
-  int64_t offA = 0, offB = 0, offC = 0, lda = 0, ldb = 0;
+  int64_t offA = 0, offB = 0, offC = 0, offE = 0, lda = 0, ldb = 0;
   int b0 = 0, Mtot = 0, Ntot = 0, pad = 0;
 };
 
@@ -174,6 +174,7 @@ __device__ __forceinline__ void store_out(void* C, int dt, int64_t i, float v) {
 __device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, int col, float acc) {
   float out = g.alpha * acc;
   if (g.D) out += g.beta * g.D[(int64_t)z * g.sD + (int64_t)row * g.ldd + col];
+  if (g.E) out += (float)reinterpret_cast<const __bf16*>(g.E)[(int64_t)z * g.sE + (int64_t)row * g.lde + col];
   if (g.C) store_out(g.C, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col, out);
   if (g.C2) store_out(g.C2, g.c2_dt, (int64_t)z * g.sC2 + (int64_t)row * g.ldc2 + col, out);
   if (g.Acc) g.Acc[(int64_t)z * g.sAcc + (int64_t)row * g.ldacc + col] += g.gamma * out;
@@ -185,18 +186,31 @@ __device__ __forceinline__ void epilogue_one(const GemmDesc& g, int z, int row, 
 // chunks, which go out as 16-byte (float32) or 8-byte (bf16) stores when the row is aligned for them. The region
 // is the wave's own and one wave's LDS accesses complete in order, so the bands need no barrier: the global
 // stores of one band stay in flight while the next is staged (a workgroup barrier would wait for all of them).
+// e (nullable): a bf16 addend at the output's coordinates (row pitch lde), added before the output is rounded; its
+// loads for a band are issued before the band's trip through LDS, which covers their latency.
 template <int WN>
 struct Ep {
   static constexpr int EP = 32 * WN + 8, BYTES = 32 * EP * 4;
 };
 template <int WM, int WN>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char* lds, void* out, int dt, int64_t ld,
-                                               int rlim, int clim, int lane) {
+                                               int rlim, int clim, int lane, const __bf16* e = nullptr,
+                                               int64_t lde = 0) {
   constexpr int EP = Ep<WN>::EP, NV = 4 * WN, PR = 8 * WN;  // float4 per lane per band, float4 per row
   float* ep = reinterpret_cast<float*>(lds);
   const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(out) % (dt == BF16 ? 8 : 16)) == 0;
+  const bool evec = lde % 4 == 0 && (reinterpret_cast<uintptr_t>(e) & 7) == 0;
 #pragma unroll
   for (int a = 0; a < WM; ++a) {
+    bf16x4 ex[NV];
+    if (e) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int c = lane + 64 * u, c4 = (c % PR) * 4, row = a * 32 + c / PR;
+        ex[u] = bf16x4{};
+        if (evec && row < rlim && c4 + 4 <= clim) ex[u] = *reinterpret_cast<const bf16x4*>(e + (int64_t)row * lde + c4);
+      }
+    }
 #pragma unroll
     for (int b = 0; b < WN; ++b)
 #pragma unroll
@@ -211,7 +225,18 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char
     for (int u = 0; u < NV; ++u) {
       const int c = lane + 64 * u, rr = c / PR, c4 = (c % PR) * 4, row = a * 32 + rr;
       if (row >= rlim || c4 >= clim) continue;
-      const f32x4 v = vv[u];
+      f32x4 v = vv[u];
+      if (e) {
+        const __bf16* q = e + (int64_t)row * lde + c4;
+        if (evec && c4 + 4 <= clim) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] += (float)ex[u][t];
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (c4 + t < clim) v[t] += (float)q[t];
+        }
+      }
       const int64_t o = (int64_t)row * ld + c4;
       if (dt == BF16) {
         __bf16* q = reinterpret_cast<__bf16*>(out) + o;
@@ -290,6 +315,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const char* Ab = reinterpret_cast<const char*>(g.A);
   const char* Bb = reinterpret_cast<const char*>(g.B);
   char* Cb = reinterpret_cast<char*>(g.C);
+  const char* Eb = reinterpret_cast<const char*>(g.E);
   int64_t lda = g.lda, ldb = g.ldb;
   int Mtot = g.Mtot, Ntot = g.Ntot;
   if constexpr (GROUP) {
@@ -299,6 +325,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const GroupEntry& e = fa_.prob[p];
     z = zg - keep_s(e.b0);
     Ab += keep_s(e.offA); Bb += keep_s(e.offB); Cb += keep_s(e.offC);
+    if (Eb) Eb += keep_s(e.offE);
     lda = keep_s(e.lda); ldb = keep_s(e.ldb); Mtot = keep_s(e.Mtot); Ntot = keep_s(e.Ntot);
   }
   int M = g.M, N = g.N, K = g.K;
@@ -436,7 +463,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   if (!g.C) return;
   char* cb = Cb + ((int64_t)z * g.sC + (int64_t)wrow0 * g.ldc + wcol0) * dtype_size(g.c_dt);
-  store_tile_lds<WM, WN>(acc, smem + wave * Ep<WN>::BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane);
+  // the bf16 addend serves only the non-token products (TAG 0): the token GEMMs' epilogue keeps no code for it
+  const __bf16* eb = TAG == 0 && Eb ? reinterpret_cast<const __bf16*>(Eb) + (int64_t)z * g.sE + (int64_t)wrow0 * g.lde + wcol0
+                                    : nullptr;
+  store_tile_lds<WM, WN>(acc, smem + wave * Ep<WN>::BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane, eb, g.lde);
 }
 
 // Sum the split-K partials of every output element in split order, then apply the epilogue.
@@ -471,7 +501,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) 
     for (int t = 0; t < nc; ++t) {
       if (fa_.nprob > 0) {
         char* cb = reinterpret_cast<char*>(g.C) + fa_.prob[p].offC;
-        store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col + t, sum[t]);
+        float o = sum[t];
+        if (g.E)
+          o += (float)reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(g.E) + fa_.prob[p].offE)
+                   [(int64_t)z * g.sE + (int64_t)row * g.lde + col + t];
+        store_out(cb, g.c_dt, (int64_t)z * g.sC + (int64_t)row * g.ldc + col + t, o);
       } else {
         epilogue_one(g, z, row, col + t, sum[t]);
       }
@@ -527,15 +561,15 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   fa.use_part = (S > 1 || !plain_epilogue(g) || g.defer_reduce) ? 1 : 0;
   const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
   const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) +
-                                  (double)g.M * g.N * ((g.C ? dtype_size(g.c_dt) : 0) + (g.D ? 4 : 0) +
+                                  (double)g.M * g.N * ((g.C ? dtype_size(g.c_dt) : 0) + (g.D ? 4 : 0) + (g.E ? 2 : 0) +
                                                        (g.C2 ? dtype_size(g.c2_dt) : 0) + (g.Acc ? 8 : 0)));
   ProfScope prof(g.kclass, st, flops, bytes);
   const dim3 grid(((tiles * S + 7) / 8) * 8), block(64 * KNW);
-  if (g.kclass == 0 && g.a_kmajor && g.b_kmajor)
+  if (g.kclass == 0 && !g.E && g.a_kmajor && g.b_kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 1>), grid, block, 0, st, fa);
-  else if (g.kclass == 1 && g.a_kmajor && !g.b_kmajor)
+  else if (g.kclass == 1 && !g.E && g.a_kmajor && !g.b_kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 2>), grid, block, 0, st, fa);
-  else if (g.kclass == 2 && !g.a_kmajor && !g.b_kmajor)
+  else if (g.kclass == 2 && !g.E && !g.a_kmajor && !g.b_kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<false, false, 3>), grid, block, 0, st, fa);
   else if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 0>), grid, block, 0, st, fa);
   else if (g.a_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, false, 0>), grid, block, 0, st, fa);
@@ -557,7 +591,8 @@ bool fast_gemm_group_eligible(const GemmDesc* pr, int n) {
     const GemmDesc& b = pr[i];
     if (!fast_gemm_eligible(b) || !plain_epilogue(b) || b.defer_reduce) return false;
     if (b.a_kmajor != a.a_kmajor || b.b_kmajor != a.b_kmajor || b.M != a.M || b.N != a.N || b.K != a.K ||
-        b.Ktot != a.Ktot || b.sA != a.sA || b.sB != a.sB || b.ldc != a.ldc || b.sC != a.sC || b.c_dt != a.c_dt)
+        b.Ktot != a.Ktot || b.sA != a.sA || b.sB != a.sB || b.ldc != a.ldc || b.sC != a.sC || b.c_dt != a.c_dt ||
+        !b.E != !a.E || b.lde != a.lde || b.sE != a.sE)
       return false;
     blocks += (size_t)b.batch;
   }
@@ -581,6 +616,7 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
     e.offA = reinterpret_cast<const char*>(pr[i].A) - reinterpret_cast<const char*>(pr[0].A);
     e.offB = reinterpret_cast<const char*>(pr[i].B) - reinterpret_cast<const char*>(pr[0].B);
     e.offC = reinterpret_cast<const char*>(pr[i].C) - reinterpret_cast<const char*>(pr[0].C);
+    e.offE = pr[0].E ? reinterpret_cast<const char*>(pr[i].E) - reinterpret_cast<const char*>(pr[0].E) : 0;
     e.lda = pr[i].lda; e.ldb = pr[i].ldb; e.Mtot = pr[i].Mtot; e.Ntot = pr[i].Ntot;
     g.batch += pr[i].batch;
   }
@@ -595,7 +631,8 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   fa.kchunk = ((nk + S - 1) / S) * BK;
   fa.use_part = S > 1 ? 1 : 0;
   const double flops = 2.0 * g.M * g.N * (double)g.K * g.batch;
-  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) + (double)g.M * g.N * dtype_size(g.c_dt));
+  const double bytes = g.batch * (2.0 * ((double)g.M * g.K + (double)g.K * g.N) +
+                                  (double)g.M * g.N * (dtype_size(g.c_dt) + (g.E ? 2 : 0)));
   ProfScope prof(g.kclass, st, flops, bytes);
   const dim3 grid(((tiles * S + 7) / 8) * 8), block(64 * KNW);
   if (g.a_kmajor && g.b_kmajor) hipLaunchKernelGGL((gemm_bf16_kernel<true, true, 0, true>), grid, block, 0, st, fa);

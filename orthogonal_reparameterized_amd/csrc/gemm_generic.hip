@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const GemmDesc g) {
         if (i < M && j < N) {
           float out = g.alpha * acc[a][b][r];
           if (g.D) out += g.beta * g.D[zd + (int64_t)i * g.ldd + j];
+          if (g.E) out += (float)reinterpret_cast<const __bf16*>(g.E)[(int64_t)z * g.sE + (int64_t)i * g.lde + j];
           if (g.C) {
             const int64_t ci = zc + (int64_t)i * g.ldc + j;
             if (g.c_dt == BF16) reinterpret_cast<__bf16*>(g.C)[ci] = (__bf16)out;
@@ -172,7 +173,7 @@ hipError_t launch_generic_gemm(const GemmDesc& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   const double mn = (double)g.M * g.N, bt = g.batch;
   const double bytes = bt * ((double)g.M * g.K * dtype_size(g.a_dt) + (double)g.K * g.N * dtype_size(g.b_dt) +
-                             (g.C ? mn * dtype_size(g.c_dt) : 0.0) + (g.C2 ? mn * dtype_size(g.c2_dt) : 0.0) + (g.D ? mn * 4.0 : 0.0) + (g.Acc ? mn * 8.0 : 0.0));
+                             (g.C ? mn * dtype_size(g.c_dt) : 0.0) + (g.C2 ? mn * dtype_size(g.c2_dt) : 0.0) + (g.D ? mn * 4.0 : 0.0) + (g.E ? mn * 2.0 : 0.0) + (g.Acc ? mn * 8.0 : 0.0));
   ProfScope prof(g.kclass, st, 2.0 * mn * g.K * bt, bytes);
   const bool small = g.M <= 64 || g.N <= 64;
   if (g.compute == BF16) return small ? launch_t<64, 64, true>(g, st) : launch_t<128, 128, true>(g, st);

@@ -39,6 +39,9 @@ struct GemmDesc {
   const void* A = nullptr; int64_t lda = 0, sA = 0; int a_dt = F32; int a_kmajor = 1; int a_sub_eye = 0;
   const void* B = nullptr; int64_t ldb = 0, sB = 0; int b_dt = F32; int b_kmajor = 1; int b_sub_eye = 0;
   void* C = nullptr; int64_t ldc = 0, sC = 0; int c_dt = F32;
+  // optional bf16 addend in the output's coordinates, added to the product before the output is rounded (the
+  // identity part of a factor applied as identity + delta): out(i, j) = alpha AB(i, j) + beta D(i, j) + E(i, j)
+  const void* E = nullptr; int64_t lde = 0, sE = 0;
   const float* D = nullptr; int64_t ldd = 0, sD = 0;
   float* Acc = nullptr; int64_t ldacc = 0, sAcc = 0;
   float alpha = 1.f, beta = 0.f, gamma = 0.f;
@@ -81,9 +84,10 @@ struct ChainArgs {
   const float* X0 = nullptr; int64_t ldx0 = 0, sx0 = 0;
   __bf16* Y = nullptr; int64_t ldy = 0, sy = 0, jstep = 0;
   int write_x0 = 0;
-  // build only, nullable: bf16 copies of the finished primitives for the activation-side products: R_p and its
-  // transpose as operand rows (zero outside each block's c x c corner, c = min(bp, d - p bp) for BS, bp for FS; in
-  // fragment order where act_frag_layout(bp)), then at offset 2 nprim bp^2 the primitives as they are, row-major
+  // build only, nullable: bf16 copies of the deltas R_p - I of the finished primitives for the activation-side
+  // products: the delta and its transpose as operand rows (zero outside each block's c x c corner, c = min(bp, d - p
+  // bp) for BS, bp for FS; in fragment order where act_frag_layout(bp)), then at offset 2 nprim bp^2 the deltas of
+  // the whole padded blocks, row-major
   __bf16* ops = nullptr;
   int d = 0, mode = 0;
 };
@@ -197,11 +201,11 @@ size_t bs_merge_split_bytes(int bp, int nblk);
 size_t bs_merge_group_bytes(const MergeItem* it, int n);  // scratch of launch_bs_merge_group
 hipError_t launch_bs_merge_group(const MergeItem* it, int n, char* split, hipStream_t st);
 
-// Block-diagonal factor applied to bf16 activations (act_apply.hip): out[t, block] = in[t, block] B_block for T
-// tokens of dimension d, blocks bp <= 256 (a multiple of 8), with the operand B = F^T (trans) or F given as bf16
-// rows Bt[j][k] = B(k, j) (fragment order where act_frag_layout(bp), else row order) by launch_act_operand from
-// the nblk float32 bp x bp primitives F. Row pitches ldi, ldo multiples of 8, in and out 16-byte aligned, the
-// input under 4 GB.
+// Block-diagonal factor applied to bf16 activations (act_apply.hip) as identity + delta: out[t, block] =
+// in[t, block] + in[t, block] B_block for T tokens of dimension d, blocks bp <= 256 (a multiple of 8), with the
+// operand B = (F - I)^T (trans) or F - I given as bf16 rows Bt[j][k] = B(k, j) (fragment order where
+// act_frag_layout(bp), else row order) by launch_act_operand from the nblk float32 bp x bp primitives F. Row
+// pitches ldi, ldo multiples of 8, in and out 16-byte aligned, the input under 4 GB.
 // Layout of the bf16 operand rows Bt[j][k] = B(k, j) of one bp x bp block:
 //   row order       element (j, k) at j bp + k;
 //   fragment order  (bp a multiple of 32) the MFMA fragments in the order the kernel loads them: column group
@@ -283,6 +287,10 @@ hipError_t launch_chain_finalize(const float* theta, int mode, int d, int bp, in
 // out = bf16(prim - I) for nprim bp x bp primitives (the delta of a factor as an MFMA operand), written as bp x ldo
 // blocks with zero columns past bp
 hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf16* out, hipStream_t st);
+
+// Matrix-core rate probe (mfma_probe.hip): workgroups x 8 waves, each issuing 4 x iters bf16 MFMAs of 32 x 32 x 16 on
+// registers; out receives one float per wave (workgroups x 8).
+hipError_t launch_mfma_probe(int64_t iters, int workgroups, float* out, hipStream_t st);
 // Coefficient polynomials of the two-phase Neumann adjoint, stacked per primitive as (k+1) ldp x ldp blocks (rows
 // and columns past bp zero): block j = sum_{t} a_{t+j+1} (-1)^{t+j} Q^t over t = 0..k-j (t >= 1 for j = 0),
 // Q^0 = I, Q^t = powers[t-1] (bp x ldp blocks), with a_i = 2 for i <= k and a_{k+1} = 1. Dtype dt (the powers').

@@ -589,16 +589,18 @@ size_t plan_bwd_act(const poet_layer& L, const SideInfo& R, const SideInfo& P, v
   return a.used();
 }
 
-// out[:, block] = in[:, block] F_block^T (trans) or in[:, block] F_block, over the blocks of side S (T rows)
-GemmDesc act_apply(const SideInfo& S, int T, const void* in, int64_t ldi, const __bf16* Fb, bool trans, void* out,
+// out[:, block] = in[:, block] F_block^T (trans) or in[:, block] F_block, over the blocks of side S (T rows), with F
+// as identity + delta: Db holds the bf16 deltas F - I in row order and the identity part adds in itself
+GemmDesc act_apply(const SideInfo& S, int T, const void* in, int64_t ldi, const __bf16* Db, bool trans, void* out,
                    int64_t ldo) {
   GemmDesc g;
   g.kclass = POET_K_APPLY;
   g.compute = BF16;
   g.M = T; g.N = S.bp; g.K = S.bp; g.Ntot = g.Ktot = S.d; g.batch = S.nprim;
   g.A = in; g.lda = ldi; g.sA = S.bp; g.a_dt = BF16; g.a_kmajor = 1;
-  g.B = Fb; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_dt = BF16; g.b_kmajor = trans ? 1 : 0;
+  g.B = Db; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_dt = BF16; g.b_kmajor = trans ? 1 : 0;
   g.C = out; g.ldc = ldo; g.sC = S.bp; g.c_dt = BF16;
+  g.E = in; g.lde = ldi; g.sE = S.bp;
   return g;
 }
 
@@ -635,14 +637,15 @@ hipError_t act_contract_adjoint(const SideInfo& S, int T, const void* A, int64_t
   return dtheta ? neumann_adjoint(S, dF, powers, dtheta, p.adj, st) : hipSuccess;
 }
 
-// bf16 copies of a side's primitives (the full factor, identity included)
-hipError_t prims_bf16(const SideInfo& S, const float* prim, __bf16* out, hipStream_t st) {
-  return launch_convert(prim, S.bp, out, S.bp, BF16, S.nprim * S.bp, S.bp, st);
+// bf16 deltas F - I of a side's primitives, row-major bp x bp blocks (zero in the identity padding of ragged blocks)
+hipError_t deltas_bf16(const SideInfo& S, const float* prim, __bf16* out, hipStream_t st) {
+  return launch_delta_bf16(prim, S.nprim, S.bp, S.bp, out, st);
 }
 
 // out = in F^T (trans) or in F over the blocks of side S: the weight-stationary kernel where it applies, else a
-// batched GEMM. Its bf16 operand comes from ops (the caller's copies of F and F^T, zero outside each block's
-// corner) or is written to the scratch Fb first.
+// batched GEMM. Both apply F as identity + delta: the bf16 operand is the delta F - I, from ops (the caller's copies
+// of the deltas of F and F^T, zero outside each block's corner) or written to the scratch Fb first, and the identity
+// part adds the input in float32 before the output is rounded.
 hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, const float* prim, const void* ops,
                       __bf16* Fb, bool trans, void* out, int64_t ldo, hipStream_t st) {
   hipError_t e;
@@ -653,17 +656,17 @@ hipError_t act_factor(const SideInfo& S, int T, const void* in, int64_t ldi, con
     return launch_act_apply(reinterpret_cast<const __bf16*>(in), ldi, reinterpret_cast<__bf16*>(out), ldo, Bt, T,
                             S.d, S.bp, S.nprim, st);
   }
-  // the batched GEMM takes the operand in row order: the caller's copies only where they are in row order
-  if (opsF && act_frag_layout(S.bp)) opsF = nullptr;
-  if (!opsF && (e = prims_bf16(S, prim, Fb, st)) != hipSuccess) return e;
-  return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF : Fb, trans, out, ldo), st);
+  // the batched GEMM takes the deltas in row order: the third part of the caller's copies
+  if (!opsF && (e = deltas_bf16(S, prim, Fb, st)) != hipSuccess) return e;
+  return launch_gemm(act_apply(S, T, in, ldi, opsF ? opsF + 2 * S.prim_len : Fb, trans, out, ldo), st);
 }
 
 // A factor folded into the bf16 copy of W0 (row pitch ldw): P side out = W0b P (P's blocks along the columns), R side
-// out = R W0b (R's blocks along the rows); one batched bf16 GEMM over the factor's blocks with the full primitives
-// as bf16 operands in row order (the third part of the caller's operand copies, else made in Fb), ragged last
-// blocks through the extents.
-GemmDesc fold_desc(const poet_layer& L, const SideInfo& S, bool rside, const void* W0b, const __bf16* Fb, __bf16* out) {
+// out = R W0b (R's blocks along the rows), with the factor as identity + delta: one batched bf16 GEMM over the
+// factor's blocks with the deltas F - I as bf16 operands in row order (the third part of the caller's operand
+// copies, else made in Db), W0b itself added in float32 before the one rounding of the output; ragged last blocks
+// through the extents.
+GemmDesc fold_desc(const poet_layer& L, const SideInfo& S, bool rside, const void* W0b, const __bf16* Db, __bf16* out) {
   GemmDesc g;
   g.kclass = POET_K_APPLY;
   g.compute = BF16;
@@ -672,16 +675,17 @@ GemmDesc fold_desc(const poet_layer& L, const SideInfo& S, bool rside, const voi
   g.a_dt = g.b_dt = BF16;
   g.c_dt = BF16;
   g.C = out; g.ldc = L.ldw;
+  g.E = W0b; g.lde = L.ldw;  // the identity part: W0b at the output's position
   if (!rside) {  // out[:, J] = W0b[:, J] P_J
     g.M = L.m; g.N = S.bp; g.Ntot = g.Ktot = L.n;
     g.A = W0b; g.lda = L.ldw; g.sA = S.bp; g.a_kmajor = 1;
-    g.B = Fb; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_kmajor = 0;  // B(k, j) = P_J[k][j]
-    g.sC = S.bp;
+    g.B = Db; g.ldb = S.bp; g.sB = (int64_t)S.bp * S.bp; g.b_kmajor = 0;  // B(k, j) = P_J[k][j] - I
+    g.sC = g.sE = S.bp;
   } else {  // out[I, :] = R_I W0b[I, :]
     g.M = S.bp; g.N = L.n; g.Mtot = g.Ktot = L.m;
-    g.A = Fb; g.lda = S.bp; g.sA = (int64_t)S.bp * S.bp; g.a_kmajor = 1;  // A(i, k) = R_I[i][k]
+    g.A = Db; g.lda = S.bp; g.sA = (int64_t)S.bp * S.bp; g.a_kmajor = 1;  // A(i, k) = R_I[i][k] - I
     g.B = W0b; g.ldb = L.ldw; g.sB = (int64_t)S.bp * L.ldw; g.b_kmajor = 0;
-    g.sC = (int64_t)S.bp * L.ldw;
+    g.sC = g.sE = (int64_t)S.bp * L.ldw;
   }
   return g;
 }
@@ -690,7 +694,7 @@ hipError_t fold_factor(const poet_layer& L, const SideInfo& S, bool rside, const
   if (ops) {
     Fb = const_cast<__bf16*>(reinterpret_cast<const __bf16*>(ops)) + 2 * S.prim_len;
   } else {
-    const hipError_t e = prims_bf16(S, prim, Fb, st);
+    const hipError_t e = deltas_bf16(S, prim, Fb, st);
     if (e != hipSuccess) return e;
   }
   return launch_gemm(fold_desc(L, S, rside, W0b, Fb, out), st);
@@ -1732,14 +1736,14 @@ poet_status poet_fold_weights_group(int32_t count, const poet_layer* layers, con
     const poet_layer& L = layers[i];
     __bf16* fR = a.take<__bf16>(R[i].prim_len);
     __bf16* fP = a.take<__bf16>(P[i].prim_len);
-    if (W0P && W0P[i]) {  // row-order P: the third part of the operand copies, or converted here
+    if (W0P && W0P[i]) {  // row-order deltas of P: the third part of the operand copies, or converted here
       const __bf16* Fb = opsP && opsP[i] ? reinterpret_cast<const __bf16*>(opsP[i]) + 2 * P[i].prim_len : fP;
-      if (Fb == fP) HIP_TRY(prims_bf16(P[i], primP[i], fP, st));
+      if (Fb == fP) HIP_TRY(deltas_bf16(P[i], primP[i], fP, st));
       gP.push_back(fold_desc(L, P[i], false, W0b[i], Fb, reinterpret_cast<__bf16*>(W0P[i])));
     }
     if (RW0 && RW0[i]) {
       const __bf16* Fb = opsR && opsR[i] ? reinterpret_cast<const __bf16*>(opsR[i]) + 2 * R[i].prim_len : fR;
-      if (Fb == fR) HIP_TRY(prims_bf16(R[i], primR[i], fR, st));
+      if (Fb == fR) HIP_TRY(deltas_bf16(R[i], primR[i], fR, st));
       gR.push_back(fold_desc(L, R[i], true, W0b[i], Fb, reinterpret_cast<__bf16*>(RW0[i])));
     }
   }
@@ -1870,7 +1874,7 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     if (!o || chain_side(S[i], powers[i])) continue;
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, true, o, st));
     HIP_TRY(launch_act_operand(prim[i], S[i].bp, S[i].d, S[i].nprim, false, o + S[i].prim_len, st));
-    HIP_TRY(prims_bf16(S[i], prim[i], o + 2 * S[i].prim_len, st));
+    HIP_TRY(deltas_bf16(S[i], prim[i], o + 2 * S[i].prim_len, st));
   }
   return POET_OK;
 }
@@ -2129,6 +2133,14 @@ poet_status poet_debug_gemm(const poet_gemm_desc* d, int force_generic, int* use
   if (used_fast) *used_fast = fast ? 1 : 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(fast ? launch_gemm(g, st) : launch_generic_gemm(g, st));
+  return POET_OK;
+}
+
+poet_status poet_mfma_probe(int64_t iters, int32_t workgroups, float* out, void* stream) {
+  if (iters < 1) return fail(POET_E_ARG, "iters = %lld must be >= 1", (long long)iters);
+  if (workgroups < 1 || workgroups > 65535) return fail(POET_E_ARG, "workgroups = %d must be in [1, 65535]", workgroups);
+  if (!out) return fail(POET_E_ARG, "null out");
+  HIP_TRY(launch_mfma_probe(iters, workgroups, out, reinterpret_cast<hipStream_t>(stream)));
   return POET_OK;
 }
 

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
             const int i = acc_row(wr, a, r, lane), n = acc_col(b, lane);
             const float v = S[a][b][r] + acc[a][b][r];
             Rs[i * RP + n] = v;
-            if (ops && i < bp) sts(Xs, n, i, (__bf16)(i < cb && n0 + n < cb ? v : 0.f));
+            if (ops && i < bp) sts(Xs, n, i, (__bf16)(i < cb && n0 + n < cb ? v - (i == n0 + n ? 1.f : 0.f) : 0.f));
           }
       lds_barrier();
       const int nv = min(SW, bp - n0);  // columns of this strip inside the block
@@ -157,17 +157,18 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
         if (n4 >= nv) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(Rs + i * RP + n4);
         *reinterpret_cast<f32x4*>(prim + (int64_t)i * bp + n0 + n4) = v;
-        if (ops) {  // the third copy: the primitive as it is, in row order (for folding it into a weight)
+        if (ops) {  // the third copy: the delta F - I of the whole block (padding included), in row order
           bf16x4 r;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) r[t] = (__bf16)v[t];
+          for (int t = 0; t < 4; ++t) r[t] = (__bf16)(v[t] - (i == n0 + n4 + t ? 1.f : 0.f));
           *reinterpret_cast<bf16x4*>(c.ops + 2 * (int64_t)c.nprim * bp * bp + (int64_t)p * bp * bp + (int64_t)i * bp +
                                      n0 + n4) = r;
         }
         if (ops && !frag) {
           bf16x4 w;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) w[t] = (__bf16)(i < cb && n0 + n4 + t < cb ? v[t] : 0.f);
+          for (int t = 0; t < 4; ++t)
+            w[t] = (__bf16)(i < cb && n0 + n4 + t < cb ? v[t] - (i == n0 + n4 + t ? 1.f : 0.f) : 0.f);
           *reinterpret_cast<bf16x4*>(opsF + (int64_t)i * bp + n0 + n4) = w;
         }
       }
@@ -181,8 +182,8 @@ __global__ __launch_bounds__(NT) void power_chain_kernel(const ChainGroup G) {
           bf16x8 w;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            w[t] = (__bf16)(i < cb && n0 + n + t < cb ? v0[t] : 0.f);
-            w[t + 4] = (__bf16)(i < cb && n0 + n + t + 4 < cb ? v1[t] : 0.f);
+            w[t] = (__bf16)(i < cb && n0 + n + t < cb ? v0[t] - (i == n0 + n + t ? 1.f : 0.f) : 0.f);
+            w[t + 4] = (__bf16)(i < cb && n0 + n + t + 4 < cb ? v1[t] - (i == n0 + n + t + 4 ? 1.f : 0.f) : 0.f);
           }
           *reinterpret_cast<bf16x8*>(opsF + act_frag_index(bp, i, n0 + n)) = w;
         }

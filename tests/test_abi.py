@@ -330,3 +330,11 @@ def test_exact_cayley_rejects_large_primitives_on_the_host():
     ok = B.side(0, 512, 256, 5, 1)
     assert lb.poet_build_orthogonal_exact(ctypes.byref(ok), FAKE, None, None) == B.POET_E_ARG
     assert lb.poet_build_orthogonal_exact(ctypes.byref(ok), None, FAKE, None) == B.POET_E_ARG
+
+
+def test_mfma_probe_rejects_bad_arguments_on_the_host():
+    lb = B.lib()
+    assert lb.poet_mfma_probe(0, 8, FAKE, None) == B.POET_E_ARG
+    assert lb.poet_mfma_probe(10, 0, FAKE, None) == B.POET_E_ARG
+    assert lb.poet_mfma_probe(10, 65536, FAKE, None) == B.POET_E_ARG
+    assert lb.poet_mfma_probe(10, 8, None, None) == B.POET_E_ARG

@@ -124,18 +124,20 @@ def test_build_group_equals_one_side_builds():
                 assert torch.equal(wa, wb), f"powers of side {i} {SIDES[i]}"
         if ops[i] is None:
             continue
-        # ops = bf16(F) and bf16(F^T) per block, zero outside the block's c x c corner, bit for bit
+        # ops = bf16(F - I) and bf16((F - I)^T) per block, zero outside the block's c x c corner, bit for bit (the
+        # float32 subtraction of 1 from a diagonal entry near 1 is exact)
         mode, d, b, k, dt = SIDES[i]
         F = to_np(pa).reshape(-1, b, b)
+        D = F - np.eye(b, dtype=np.float32)
         want = np.zeros_like(F)
         for p, c in enumerate(O.block_sizes(mode, d, b)):
-            want[p, :c, :c] = PI.round_bf16(F[p, :c, :c])
+            want[p, :c, :c] = PI.round_bf16(D[p, :c, :c])
         got = to_np(ops[i]).reshape(3, -1, b * b)
         np.testing.assert_array_equal(got[0], _operand_order(want), err_msg=f"ops of side {i} {SIDES[i]}")
         np.testing.assert_array_equal(got[1], _operand_order(want.transpose(0, 2, 1)),
                                       err_msg=f"transposed ops of side {i}")
-        # the third part: the primitive as it is (padding included), row-major
-        np.testing.assert_array_equal(got[2], PI.round_bf16(F).reshape(-1, b * b), err_msg=f"row ops of side {i}")
+        # the third part: the delta of the whole padded block (zero in the identity padding), row-major
+        np.testing.assert_array_equal(got[2], PI.round_bf16(D).reshape(-1, b * b), err_msg=f"row ops of side {i}")
 
 
 def _oracle_dtheta(side_spec, theta, dprim):
