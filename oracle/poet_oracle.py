@@ -26,9 +26,10 @@ reordering is done beyond what the definitions state.
 
 Parity status: every function here is pinned by tests against closed forms, textbook routines, finite
 differences, an independent library implementation (AdamW) or values printed on the pages, except the FS index
-sampler's specific draws (the pages name no random generator; see ``sample_indices``), the block-size remainder
-reading (see ``block_sizes``) and the optimizer state across a merge (see ``optimizer_state_after_merge``), which
-are "parity unpinned" beyond their structural invariants.
+sampler's specific draws (the pages name no random generator; see ``sample_indices``) and the permutation drawn
+from the same keys (``sample_permutation``), the block-size remainder reading (see ``block_sizes``) and the
+optimizer state across a merge (see ``optimizer_state_after_merge``), which are "parity unpinned" beyond their
+structural invariants.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-MODE_BS, MODE_FS = 0, 1
+MODE_BS, MODE_FS, MODE_BSP = 0, 1, 2
 SIDE_R, SIDE_P = 0, 1
 
 _MASK64 = (1 << 64) - 1
@@ -91,6 +92,24 @@ def sample_indices(d: int, s: int, seed: int, linear_id: int, side: int, epoch: 
     return np.sort(order[:s]).astype(np.int32)
 
 
+def sample_permutation(d: int, seed: int, linear_id: int, side: int, epoch: int) -> np.ndarray:
+    """The random permutation of permuted POET-BS: perm[r] = the index of rank r among the keys of
+    ``sample_indices`` (the same (seed, linear_id, side, epoch) hash and SplitMix64 keys, ordered by (key_i, i)).
+
+    Reading: the pages call the primitives sampled sub-blocks and leave open whether POET-BS blocks are contiguous;
+    the permuted variant draws a uniformly random partition into blocks, fresh at each merge, as a random
+    permutation of [0, d) cut into consecutive runs of b ranks. Drawn from the FS keys, so that the s lowest ranks
+    are exactly the FS index set of the same draw. Parity unpinned beyond its invariants (no generator is given).
+    """
+    h = splitmix64(seed & _MASK64)
+    h = splitmix64(h ^ (linear_id & 0xFFFFFFFF))
+    h = splitmix64(h ^ (side & 0xFFFFFFFF))
+    h = splitmix64(h ^ (epoch & 0xFFFFFFFF))
+    i = np.arange(d, dtype=np.uint64)
+    keys = splitmix64(np.uint64(h) ^ i)
+    return np.lexsort((i, keys)).astype(np.int32)
+
+
 # ----------------------------------------------------------------------------------------------------------
 # Primitive layout of one side
 # ----------------------------------------------------------------------------------------------------------
@@ -99,7 +118,8 @@ def block_sizes(mode: int, d: int, b: int) -> List[int]:
     """Sizes of the primitives of one side.
 
     POET-BS: consecutive diagonal blocks of size b. Reading: when b does not divide d the last block has size
-    d mod b (plain chunking of a block-diagonal matrix). POET-FS: one primitive of size s = b.
+    d mod b (plain chunking of a block-diagonal matrix). Permuted POET-BS: the same sizes, taken over the ranks of
+    a permutation. POET-FS: one primitive of size s = b.
     """
     if mode == MODE_FS:
         return [b]
@@ -197,12 +217,18 @@ def assemble(mode: int, d: int, prims: Sequence[np.ndarray], idx: Optional[np.nd
     """The full d x d orthogonal factor.
 
     POET-BS: block-diagonal of the primitives. POET-FS: identity with the primitive placed on the sampled
-    index set, F[idx, idx] = G (the other rows and columns are left untouched).
+    index set, F[idx, idx] = G (the other rows and columns are left untouched). Permuted POET-BS (idx = the
+    permutation perm): primitive p sits on the index set I_p = perm[p b : p b + c], F[I_p, I_p] = G_p, i.e.
+    F = Pi^T blockdiag(G) Pi with (Pi x)_r = x_perm[r]; the blocks cover every index.
     """
     F = np.eye(d)
     if mode == MODE_FS:
         idx = np.asarray(idx, dtype=np.int64)
         F[np.ix_(idx, idx)] = prims[0]
+        return F
+    if mode == MODE_BSP:
+        for I, G in zip(prim_blocks(mode, d, prims_b(prims), idx), prims):
+            F[np.ix_(I, I)] = G
         return F
     off = 0
     for G in prims:
@@ -212,13 +238,20 @@ def assemble(mode: int, d: int, prims: Sequence[np.ndarray], idx: Optional[np.nd
     return F
 
 
+def prims_b(prims: Sequence[np.ndarray]) -> int:
+    """The block size b of a list of BS primitives (all b x b but a smaller last one)."""
+    return max(G.shape[0] for G in prims)
+
+
 def prim_blocks(mode: int, d: int, b: int, idx: Optional[np.ndarray] = None) -> List[np.ndarray]:
-    """Index set of each primitive: consecutive ranges (BS) or the sampled indices (FS)."""
+    """Index set of each primitive: consecutive ranges (BS), consecutive runs of the permutation idx (permuted
+    BS), or the sampled indices (FS)."""
     if mode == MODE_FS:
         return [np.asarray(idx, dtype=np.int64)]
     out, off = [], 0
     for c in block_sizes(mode, d, b):
-        out.append(np.arange(off, off + c))
+        r = np.arange(off, off + c)
+        out.append(np.asarray(idx, dtype=np.int64)[r] if mode == MODE_BSP else r)
         off += c
     return out
 
@@ -304,7 +337,8 @@ def merge(sR: Side, sP: Side, W0, thetaR, thetaP, idxR, idxP, seed: int, linear_
     parameters to zero (so R = P = I afterwards) and, for POET-FS, draw fresh index sets for the next epoch.
 
     Reading: the merge folds the same truncated R_k, P_k the forward pass uses, so the layer's function is
-    unchanged by the merge itself.
+    unchanged by the merge itself. Permuted POET-BS draws a fresh permutation for the next epoch as FS draws a
+    fresh index set.
     """
     R = factor(sR, thetaR, idxR)
     P = factor(sP, thetaP, idxP)
@@ -315,6 +349,10 @@ def merge(sR: Side, sP: Side, W0, thetaR, thetaP, idxR, idxP, seed: int, linear_
         out["idxR"] = sample_indices(sR.d, sR.b, seed, linear_id, SIDE_R, epoch_next)
     if sP.mode == MODE_FS:
         out["idxP"] = sample_indices(sP.d, sP.b, seed, linear_id, SIDE_P, epoch_next)
+    if sR.mode == MODE_BSP:
+        out["idxR"] = sample_permutation(sR.d, seed, linear_id, SIDE_R, epoch_next)
+    if sP.mode == MODE_BSP:
+        out["idxP"] = sample_permutation(sP.d, seed, linear_id, SIDE_P, epoch_next)
     return out
 
 

@@ -9,7 +9,8 @@ import oracle as O
 import oracle.poet_oracle as PO
 import tests.test_oracle_pins as pins
 
-_ORIG = {f: getattr(PO, f) for f in ("neumann_adjoint", "linear_bwd", "assemble", "sample_indices", "adamw_step")}
+_ORIG = {f: getattr(PO, f) for f in ("neumann_adjoint", "linear_bwd", "assemble", "sample_indices", "adamw_step",
+                                     "prim_blocks", "sample_permutation")}
 
 
 def _cn_drop_last(Q, k):
@@ -79,6 +80,17 @@ def _assemble_fs_rows_only(mode, d, prims, idx=None):
     return F
 
 
+def _bsp_blocks_inverse(mode, d, b, idx=None):
+    # permuted BS blocks taken from the inverse permutation (positions instead of indices)
+    if mode != O.MODE_BSP:
+        return _ORIG["prim_blocks"](mode, d, b, idx)
+    return _ORIG["prim_blocks"](mode, d, b, np.argsort(np.asarray(idx)))
+
+
+def _permutation_reversed(d, seed, linear_id, side, epoch):
+    return _ORIG["sample_permutation"](d, seed, linear_id, side, epoch)[::-1].copy()
+
+
 def _sampler_descending(d, s, seed, linear_id, side, epoch):
     return _ORIG["sample_indices"](d, s, seed, linear_id, side, epoch)[::-1].copy()
 
@@ -140,6 +152,10 @@ MUTATIONS = {
                               [lambda: pins.test_finite_difference_theta(pins.FD_CASES[1], 2)]),
     "fs_assembly_columns": ("assemble", _assemble_fs_rows_only,
                             [lambda: pins.test_fs_assembly_is_permuted_block()]),
+    "bsp_blocks_inverse_permutation": ("prim_blocks", _bsp_blocks_inverse,
+                                       [lambda: pins.test_bsp_assembly_is_conjugated_blockdiag()]),
+    "permutation_reversed": ("sample_permutation", _permutation_reversed,
+                             [lambda: pins.test_permutation_sampler_structure_and_fs_tie(64)]),
     "sampler_order": ("sample_indices", _sampler_descending,
                       [lambda: pins.test_sampler_structure(64, 32)]),
     "adamw_no_bias_correction": ("adamw_step", _adamw_no_bias_correction,

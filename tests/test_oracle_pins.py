@@ -33,16 +33,19 @@ def test_q_zero_identity(k):
         assert np.array_equal(O.cayley_neumann(np.zeros((c, c)), k), np.eye(c))
 
 
-@pytest.mark.parametrize("mode", [O.MODE_BS, O.MODE_FS])
+@pytest.mark.parametrize("mode", [O.MODE_BS, O.MODE_FS, O.MODE_BSP])
 def test_q_zero_layer_is_w0(mode):
     rng = np.random.default_rng(1)
     m, n, T = 12, 10, 7
     W0 = rng.standard_normal((m, n))
     X = rng.standard_normal((T, n))
-    bR, bP = (5, 4) if mode == O.MODE_BS else (6, 5)
+    bR, bP = (6, 5) if mode == O.MODE_FS else (5, 4)
     sR, sP = O.Side(mode, m, bR, 3), O.Side(mode, n, bP, 3)
-    idxR = O.sample_indices(m, bR, 7, 0, 0, 0) if mode == O.MODE_FS else None
-    idxP = O.sample_indices(n, bP, 7, 0, 1, 0) if mode == O.MODE_FS else None
+    idxR = idxP = None
+    if mode == O.MODE_FS:
+        idxR, idxP = O.sample_indices(m, bR, 7, 0, 0, 0), O.sample_indices(n, bP, 7, 0, 1, 0)
+    elif mode == O.MODE_BSP:
+        idxR, idxP = O.sample_permutation(m, 7, 0, 0, 0), O.sample_permutation(n, 7, 0, 1, 0)
     out = O.linear_fwd(sR, sP, W0, np.zeros(O.theta_len(mode, m, bR)), np.zeros(O.theta_len(mode, n, bP)),
                        idxR, idxP, X)
     assert np.array_equal(out["W"], W0)
@@ -116,12 +119,18 @@ def _layer_case(mode, m, n, bR, bP, k, seed, scale):
     sR, sP = O.Side(mode, m, bR, k), O.Side(mode, n, bP, k)
     tR = rng.standard_normal(O.theta_len(mode, m, bR)) * scale
     tP = rng.standard_normal(O.theta_len(mode, n, bP)) * scale
-    idxR = O.sample_indices(m, bR, seed, 3, O.SIDE_R, 0) if mode == O.MODE_FS else None
-    idxP = O.sample_indices(n, bP, seed, 3, O.SIDE_P, 0) if mode == O.MODE_FS else None
+    idxR = idxP = None
+    if mode == O.MODE_FS:
+        idxR = O.sample_indices(m, bR, seed, 3, O.SIDE_R, 0)
+        idxP = O.sample_indices(n, bP, seed, 3, O.SIDE_P, 0)
+    elif mode == O.MODE_BSP:
+        idxR = O.sample_permutation(m, seed, 3, O.SIDE_R, 0)
+        idxP = O.sample_permutation(n, seed, 3, O.SIDE_P, 0)
     return sR, sP, W0, tR, tP, idxR, idxP
 
 
-@pytest.mark.parametrize("mode,bR,bP", [(O.MODE_BS, 4, 3), (O.MODE_BS, 12, 10), (O.MODE_FS, 6, 5)])
+@pytest.mark.parametrize("mode,bR,bP", [(O.MODE_BS, 4, 3), (O.MODE_BS, 12, 10), (O.MODE_FS, 6, 5),
+                                        (O.MODE_BSP, 4, 3)])
 def test_spectrum_preserved_layer(mode, bR, bP):
     m, n = 12, 10
     # with enough terms the factors are orthogonal to roundoff and the spectrum is kept exactly
@@ -153,6 +162,45 @@ def test_fs_assembly_is_permuted_block():
     B = np.eye(d)
     B[:s, :s] = G
     np.testing.assert_array_equal(O.assemble(O.MODE_FS, d, [G], idx), Pi.T @ B @ Pi)
+
+
+def test_bsp_assembly_is_conjugated_blockdiag():
+    # permuted BS: F = Pi^T blockdiag(G) Pi with Pi the permutation matrix whose row r is e_perm[r] (built here from
+    # an identity matrix, independently of the oracle's index bookkeeping), blocks of 4, 4, 2 over d = 10
+    rng = np.random.default_rng(5)
+    G = [rng.standard_normal((c, c)) for c in (4, 4, 2)]
+    perm = rng.permutation(10)
+    Pi = np.eye(10)[perm]
+    from scipy.linalg import block_diag
+    np.testing.assert_array_equal(O.assemble(O.MODE_BSP, 10, G, perm), Pi.T @ block_diag(*G) @ Pi)
+    # the index sets are the consecutive runs of the permutation and partition [0, d)
+    blocks = O.prim_blocks(O.MODE_BSP, 10, 4, perm)
+    assert [list(b) for b in blocks] == [list(perm[0:4]), list(perm[4:8]), list(perm[8:10])]
+    assert sorted(np.concatenate(blocks)) == list(range(10))
+
+
+def test_bsp_identity_permutation_is_bs():
+    # with the identity permutation the permuted variant is plain POET-BS, bit for bit
+    sR, sP, W0, tR, tP, _, _ = _layer_case(O.MODE_BS, 9, 7, 4, 3, 3, 13, 0.2)
+    qR, qP = O.Side(O.MODE_BSP, 9, 4, 3), O.Side(O.MODE_BSP, 7, 3, 3)
+    rng = np.random.default_rng(14)
+    X, dY = rng.standard_normal((5, 7)), rng.standard_normal((5, 9))
+    a = O.linear_fwd(sR, sP, W0, tR, tP, None, None, X)
+    b = O.linear_fwd(qR, qP, W0, tR, tP, np.arange(9), np.arange(7), X)
+    np.testing.assert_array_equal(a["Y"], b["Y"])
+    ga = O.linear_bwd(sR, sP, W0, tR, tP, None, None, X, dY)
+    gb = O.linear_bwd(qR, qP, W0, tR, tP, np.arange(9), np.arange(7), X, dY)
+    for key in ("dX", "dthetaR", "dthetaP"):
+        np.testing.assert_array_equal(ga[key], gb[key])
+
+
+def test_bsp_is_bs_on_relabeled_coordinates():
+    # Pi_R W Pi_P^T of the permuted layer equals the plain BS layer on the relabeled weight Pi_R W0 Pi_P^T
+    sR, sP, W0, tR, tP, iR, iP = _layer_case(O.MODE_BSP, 9, 7, 4, 3, 3, 15, 0.2)
+    W = O.linear_fwd(sR, sP, W0, tR, tP, iR, iP, np.zeros((1, 7)))["W"]
+    bR, bP = O.Side(O.MODE_BS, 9, 4, 3), O.Side(O.MODE_BS, 7, 3, 3)
+    Wb = O.linear_fwd(bR, bP, W0[np.ix_(iR, iP)], tR, tP, None, None, np.zeros((1, 7)))["W"]
+    np.testing.assert_allclose(W[np.ix_(iR, iP)], Wb, rtol=0, atol=1e-14)
 
 
 def test_bs_assembly_blocks():
@@ -199,6 +247,7 @@ FD_CASES = [
     (O.MODE_BS, 4, 4, 4, 4),
     (O.MODE_FS, 7, 6, 3, 4),
     (O.MODE_FS, 5, 8, 2, 3),
+    (O.MODE_BSP, 7, 6, 3, 4),  # permuted blocks with remainders
 ]
 
 
@@ -276,7 +325,7 @@ def test_bs_single_block_equals_fs_full(k):
 
 
 # ---------------------------------------------------------------- P8: merge continuity
-@pytest.mark.parametrize("mode,bR,bP", [(O.MODE_BS, 4, 3), (O.MODE_FS, 6, 5)])
+@pytest.mark.parametrize("mode,bR,bP", [(O.MODE_BS, 4, 3), (O.MODE_FS, 6, 5), (O.MODE_BSP, 4, 3)])
 def test_merge_continuity(mode, bR, bP):
     m, n = 12, 10
     sR, sP, W0, tR, tP, iR, iP = _layer_case(mode, m, n, bR, bP, 3, 60, 0.05)
@@ -291,6 +340,9 @@ def test_merge_continuity(mode, bR, bP):
     if mode == O.MODE_FS:
         np.testing.assert_array_equal(mg["idxR"], O.sample_indices(m, bR, 60, 3, O.SIDE_R, 1))
         assert not np.array_equal(mg["idxR"], iR) or not np.array_equal(mg["idxP"], iP)
+    if mode == O.MODE_BSP:
+        np.testing.assert_array_equal(mg["idxP"], O.sample_permutation(n, 60, 3, O.SIDE_P, 1))
+        assert not np.array_equal(mg["idxR"], iR) and not np.array_equal(mg["idxP"], iP)
 
 
 def test_merge_spectrum_exact_factors():
@@ -332,6 +384,17 @@ def test_sampler_structure(d, s):
     assert np.all(np.diff(idx) > 0) if s > 1 else True
     assert (s == 0) or (idx[0] >= 0 and idx[-1] < d)
     np.testing.assert_array_equal(idx, O.sample_indices(d, s, 1234, 5, 1, 2))
+
+
+@pytest.mark.parametrize("d", [1, 7, 64, 300, 5461])
+def test_permutation_sampler_structure_and_fs_tie(d):
+    perm = O.sample_permutation(d, 9, 4, O.SIDE_P, 2)
+    assert perm.dtype == np.int32 and sorted(perm) == list(range(d))
+    # the s lowest ranks are the FS index set of the same draw, for every s
+    for s in sorted({0, 1, d // 3, d // 2, d}):
+        np.testing.assert_array_equal(np.sort(perm[:s]), O.sample_indices(d, s, 9, 4, O.SIDE_P, 2))
+    if d > 1:
+        assert not np.array_equal(perm, O.sample_permutation(d, 9, 4, O.SIDE_P, 3))
 
 
 def test_sampler_inputs_matter():
