@@ -575,6 +575,9 @@ def main():
     ap.add_argument("--no-group", action="store_true",
                     help="build and finish the backward of each linear on its own (the default runs the per-side "
                          "steps of all linears of the block in shared launches)")
+    ap.add_argument("--permuted", action="store_true",
+                    help="permuted POET-BS: each side's blocks on a random permutation, fresh at every merge "
+                         "(PermutedPoetLinear; implies --no-group and skips the extra FS block)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -587,7 +590,13 @@ def main():
     import torch
     import poet_inputs as PI
     from orthogonal_reparameterized_amd import binding as B
-    from orthogonal_reparameterized_amd.layer import PoetGroup, PoetLinear
+    from orthogonal_reparameterized_amd.layer import PermutedPoetLinear, PoetGroup, PoetLinear
+    if args.permuted:
+        if PI.WORKLOADS[args.workload].mode != PI.MODE_BS or args.layers > 1 or PI.WORKLOADS[args.workload].layers > 1:
+            print("--permuted applies to the one-block POET-BS workloads (1, 2, 3)", file=sys.stderr)
+            sys.exit(2)
+        args.no_group, args.no_fs = True, True
+        PoetLinear = PermutedPoetLinear
 
     torch.cuda.set_device(0)
     B.lib()
@@ -601,6 +610,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == PI.DT_BF16 else "f32",
            "data": "synthetic", "config": res.pop("config"), "roofline": res.pop("roofline")}
     out.update(res)
+    out["config"]["permuted_blocks"] = bool(args.permuted)
     if args.workload == 3 and args.layers <= 1 and not args.no_fs:
         fs = PI.WORKLOADS[4]
         log("extra: the POET-FS block")

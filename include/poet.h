@@ -150,6 +150,25 @@ poet_status poet_sample_indices(int32_t d, int32_t s, uint64_t seed, uint32_t li
 poet_status poet_sample_indices_noalloc(int32_t d, int32_t s, uint64_t seed, uint32_t linear_id, uint32_t side,
                                         uint32_t epoch, int32_t* idx, void* stream);
 
+/* Permuted POET-BS (a reading of the sampled sub-block primitives of stochastic primitive optimization, Approach
+ * section of the method summary): the blocks of a side sit on consecutive runs of b ranks of a random permutation
+ * of [0, d), fresh at each merge. The permutation comes from the same keys as poet_sample_indices: perm[r] = the
+ * index of rank r in the order of (key_i, i), so the s lowest ranks are that call's index set; inv[i] = the rank of
+ * index i (nullable). perm, inv: [d] int32 device, caller-owned. Bit-exact; one launch, no workspace. d >= 1 and
+ * non-null perm, else POET_E_SHAPE / POET_E_ARG. */
+poet_status poet_sample_permutation(int32_t d, uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch,
+                                    int32_t* perm, int32_t* inv, void* stream);
+
+/* Row and column gather, the relabeling that carries permuted POET-BS (a block-diagonal layer on the permuted
+ * coordinates Pi_R W0 Pi_P^T, with the activations gathered into and out of them):
+ *   out[i][j] = in[row_idx[i]][col_idx[j]]  for i < rows, j < cols,
+ * a NULL index array meaning the identity. Elements of elem_bytes = 2 or 4 are moved bit for bit (bf16 activations,
+ * float32 weights, int32 index arrays). in [in_rows x ldi], out [rows x ldo] device, caller-owned, not overlapping;
+ * indices are clamped into [0, in_rows) / [0, in_cols). Bad sizes give POET_E_SHAPE, null pointers POET_E_ARG. */
+poet_status poet_gather2d(int32_t rows, int32_t cols, int32_t elem_bytes, const void* in, int64_t ldi, int32_t in_rows,
+                          int32_t in_cols, const int32_t* row_idx, const int32_t* col_idx, void* out, int64_t ldo,
+                          void* stream);
+
 /* Forward of one POET linear (one-line method summary: W = R W0 P): materializes W (act dtype) and
  * computes Y = X W^T.
  *   W0     [m x ldw] float32 in.    primR/primP: built primitives of R and P (float32 in).

@@ -26,8 +26,7 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
-           "poet_mfma_probe",
-           "poet_mfma_probe",
+           "poet_mfma_probe", "poet_sample_permutation", "poet_gather2d",
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
@@ -158,8 +157,10 @@ def lib() -> ctypes.CDLL:
     L.poet_debug_gemm.restype = ctypes.c_int
     L.poet_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, VP, VP]
     L.poet_mfma_probe.restype = ctypes.c_int
-    L.poet_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, VP, VP]
-    L.poet_mfma_probe.restype = ctypes.c_int
+    L.poet_sample_permutation.argtypes = [I32, U64, U32, U32, U32, VP, VP, VP]
+    L.poet_sample_permutation.restype = ctypes.c_int
+    L.poet_gather2d.argtypes = [I32, I32, I32, VP, ctypes.c_int64, I32, I32, VP, VP, VP, ctypes.c_int64, VP]
+    L.poet_gather2d.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -235,12 +236,37 @@ def poet_debug_gemm(desc: poet_gemm_desc, force_generic: bool = False, stream=No
     return bool(used.value)
 
 
-def poet_mfma_probe(iters: int, workgroups: int, out, stream=None) -> float:
-    """Launch the matrix-core rate probe (workgroups x 8 waves, 4 * iters 32x32x16 bf16 MFMAs per wave; out: float32
-    device tensor of at least workgroups * 8 elements). Returns the flops it issues; the caller times the launch."""
-    _need(out, "out", workgroups * 8, ("float32",))
-    _check(lib().poet_mfma_probe(int(iters), int(workgroups), _ptr(out), _stream(stream)), "poet_mfma_probe")
-    return 32768.0 * 4 * iters * 8 * workgroups
+def poet_sample_permutation(d: int, seed: int, linear_id: int, side: int, epoch: int, perm, inv=None,
+                            stream=None) -> None:
+    """perm[r] = the index of rank r (int32 device tensor [d]); inv[i] = the rank of index i (nullable)."""
+    _check(lib().poet_sample_permutation(int(d), int(seed), int(linear_id), int(side), int(epoch),
+                                         _ptr(perm, "perm", 4 * d, "int32"),
+                                         _ptr(inv, "inv", 4 * d, "int32", allow_none=True), _stream(stream)),
+           "poet_sample_permutation")
+
+
+def poet_gather2d(inp, out, row_idx=None, col_idx=None, stream=None) -> None:
+    """out[i][j] = inp[row_idx[i]][col_idx[j]] for 2-D device tensors of 2- or 4-byte elements (rows written: the
+    length of row_idx, else inp's rows; columns: the length of col_idx, else inp's columns)."""
+    torch = _torch()
+    if inp.dim() != 2 or out.dim() != 2 or inp.element_size() != out.element_size():
+        raise ValueError("inp and out must be 2-D tensors of one element size")
+    if inp.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("inp and out must have unit column stride")
+    if not (inp.is_cuda and out.is_cuda):
+        raise ValueError("inp and out must be GPU tensors")
+    rows = row_idx.numel() if row_idx is not None else inp.shape[0]
+    cols = col_idx.numel() if col_idx is not None else inp.shape[1]
+    if out.shape[0] < rows or out.shape[1] < cols:
+        raise ValueError(f"out is {tuple(out.shape)}, the gather writes {rows} x {cols}")
+    for t, nm in ((row_idx, "row_idx"), (col_idx, "col_idx")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise TypeError(f"{nm} must be a contiguous int32 GPU tensor")
+    _check(lib().poet_gather2d(rows, cols, inp.element_size(), ctypes.c_void_p(inp.data_ptr()), inp.stride(0),
+                               inp.shape[0], inp.shape[1],
+                               None if row_idx is None else ctypes.c_void_p(row_idx.data_ptr()),
+                               None if col_idx is None else ctypes.c_void_p(col_idx.data_ptr()),
+                               ctypes.c_void_p(out.data_ptr()), out.stride(0), _stream(stream)), "poet_gather2d")
 
 
 def poet_mfma_probe(iters: int, workgroups: int, out, stream=None) -> float:

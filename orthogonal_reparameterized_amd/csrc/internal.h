@@ -271,6 +271,11 @@ hipError_t launch_gather_rows(const void* src, int src_dt, int64_t ld_src, const
 hipError_t launch_scatter_rows(const float* src, int64_t ld_src, const int32_t* idx, int s, int dlim, int cols,
                                void* dst, int dst_dt, int64_t ld_dst, hipStream_t st);
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st);
+// perm[r] = the index of rank r of the same keys (inv[i] = rank of i, nullable): permuted POET-BS
+hipError_t launch_sample_permutation(int d, uint64_t h, int32_t* perm, int32_t* inv, hipStream_t st);
+// out[i][j] = in[row_idx[i]][col_idx[j]] (null index arrays: identity), elements of 2 or 4 bytes, indices clamped
+hipError_t launch_gather2d(int rows, int cols, int elem_bytes, const void* in, int64_t ldi, int in_rows, int in_cols,
+                           const int32_t* row_idx, const int32_t* col_idx, void* out, int64_t ldo, hipStream_t st);
 // Three bf16 parts of X (rows x cols, float32) for products to float32 accuracy on bf16 MFMA:
 // X(i, j) = src[r(i) * ld_src + c(j)] - [sub_eye && i == j], r(i) = ridx ? ridx[i] : i, c(j) = cidx ? cidx[j] : j
 // (indices clamped to rlim / clim). Part t = 0, 1, 2 is hi(X) = bf16(X), or lo(X) = bf16(X - hi(X)) where bit t of

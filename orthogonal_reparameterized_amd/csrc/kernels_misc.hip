@@ -319,11 +319,14 @@ __host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   return x ^ (x >> 31);
 }
 
-// flags[i] = 1 when fewer than s indices j have (key_j, j) < (key_i, i). A workgroup of kRankWaves waves ranks 64
+// The rank of index i is the number of indices j with (key_j, j) < (key_i, i). Index set mode (perm null):
+// flags[i] = 1 when the rank is below s. Permutation mode: perm[rank] = i and, when inv is given, inv[i] = rank (the
+// ranks are a bijection onto [0, d), so every entry is written once). A workgroup of kRankWaves waves ranks 64
 // indices (lane = i): each chunk of kRankChunk keys is hashed into LDS once, wave w compares against its 64-key slice
 // of the chunk, and the waves' integer counts are summed at the end (the order of an integer sum does not matter).
 constexpr int kRankWaves = 16, kRankChunk = kRankWaves * 64;
-__global__ void __launch_bounds__(kRankChunk) k_sample_rank(int d, int s, uint64_t h, int32_t* __restrict__ flags) {
+__global__ void __launch_bounds__(kRankChunk) k_sample_rank(int d, int s, uint64_t h, int32_t* __restrict__ flags,
+                                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ uint64_t kj[kRankChunk];
   __shared__ int part[kRankWaves][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -347,7 +350,74 @@ __global__ void __launch_bounds__(kRankChunk) k_sample_rank(int d, int s, uint64
   if (w == 0) {
     int r = 0;
     for (int q = 0; q < kRankWaves; ++q) r += part[q][lane];
-    if (i < d) flags[i] = r < s ? 1 : 0;
+    if (i < d) {
+      if (perm) {
+        perm[r] = i;
+        if (inv) inv[i] = r;
+      } else {
+        flags[i] = r < s ? 1 : 0;
+      }
+    }
+  }
+}
+
+// out[i][j] = in[ri][cj] with ri = row_idx[i] (or i) and cj = col_idx[j] (or j), both clamped into the source;
+// E is the element type (2 or 4 bytes: the bits are moved as they are). Rows of the output over blockIdx.y (grid
+// stride), columns over threads: the stores are coalesced, the reads scatter within one source row. The general
+// form (long rows, row gathers); k_gather_cols_lds below takes the column gathers of activations.
+template <typename E>
+__global__ __launch_bounds__(256) void k_gather2d(int rows, int cols, const E* __restrict__ in, int64_t ldi, int in_rows,
+                                                  int in_cols, const int32_t* __restrict__ row_idx,
+                                                  const int32_t* __restrict__ col_idx, E* __restrict__ out, int64_t ldo) {
+  for (int i = blockIdx.y; i < rows; i += gridDim.y) {
+    const int64_t src = (int64_t)(row_idx ? clampi(row_idx[i], in_rows) : i) * ldi;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < cols; j += gridDim.x * blockDim.x)
+      out[(int64_t)i * ldo + j] = in[src + (col_idx ? clampi(col_idx[j], in_cols) : j)];
+  }
+}
+
+// Column gather of 2-byte elements through LDS: a workgroup keeps the (clamped) column indices in LDS and, for each
+// of its rows, copies the source row into LDS with 16-byte loads, then writes 8 gathered elements per thread as one
+// 16-byte store. Needs in_cols <= GC_MAX_IN and cols <= GC_MAX_OUT (LDS) and 16-byte aligned rows (base, ldi and ldo
+// multiples of 8 elements); a partial last chunk of a row is read and written element by element, so nothing past
+// in_cols of a source row or cols of an output row is touched.
+constexpr int GC_MAX_IN = 8192, GC_MAX_OUT = 8192, GC_ROWS = 16;
+__global__ __launch_bounds__(256) void k_gather_cols_lds(int rows, int cols, const uint16_t* __restrict__ in,
+                                                         int64_t ldi, int in_rows, int in_cols,
+                                                         const int32_t* __restrict__ row_idx,
+                                                         const int32_t* __restrict__ col_idx,
+                                                         uint16_t* __restrict__ out, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t rowbuf[GC_MAX_IN];
+  __shared__ int32_t cidx[GC_MAX_OUT];
+  for (int j = threadIdx.x; j < cols; j += blockDim.x) cidx[j] = clampi(col_idx[j], in_cols);
+  const int nch_in = (in_cols + 7) / 8, nch_out = (cols + 7) / 8;
+  const int r0 = blockIdx.x * GC_ROWS, r1 = min(rows, r0 + GC_ROWS);
+  for (int i = r0; i < r1; ++i) {
+    const uint16_t* src = in + (int64_t)(row_idx ? clampi(row_idx[i], in_rows) : i) * ldi;
+    __syncthreads();  // the previous row's gathers are done with rowbuf (and cidx is written)
+    for (int q = threadIdx.x; q < nch_in; q += blockDim.x) {
+      if (8 * q + 8 <= in_cols) {
+        *reinterpret_cast<uint4*>(rowbuf + 8 * q) = *reinterpret_cast<const uint4*>(src + 8 * q);
+      } else {
+        for (int j = 8 * q; j < in_cols; ++j) rowbuf[j] = src[j];
+      }
+    }
+    __syncthreads();
+    uint16_t* dst = out + (int64_t)i * ldo;
+    for (int q = threadIdx.x; q < nch_out; q += blockDim.x) {
+      const int j0 = 8 * q;
+      if (j0 + 8 <= cols) {
+        uint16_t v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = rowbuf[cidx[j0 + t]];
+        uint4 w;
+        w.x = v[0] | ((uint32_t)v[1] << 16); w.y = v[2] | ((uint32_t)v[3] << 16);
+        w.z = v[4] | ((uint32_t)v[5] << 16); w.w = v[6] | ((uint32_t)v[7] << 16);
+        *reinterpret_cast<uint4*>(dst + j0) = w;
+      } else {
+        for (int j = j0; j < cols; ++j) dst[j] = rowbuf[cidx[j]];
+      }
+    }
   }
 }
 
@@ -819,10 +889,39 @@ uint64_t sampler_hash(uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t
 hipError_t launch_sample(int d, int s, uint64_t h, int32_t* flags, int32_t* idx, hipStream_t st) {
   if (d <= 0 || s <= 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)d * 4 + (double)s * 4);
-  hipLaunchKernelGGL(k_sample_rank, dim3((d + 63) / 64), dim3(kRankChunk), 0, st, d, s, h, flags);
+  hipLaunchKernelGGL(k_sample_rank, dim3((d + 63) / 64), dim3(kRankChunk), 0, st, d, s, h, flags, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sample_compact, dim3(1), dim3(1024), 0, st, d, flags, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_permutation(int d, uint64_t h, int32_t* perm, int32_t* inv, hipStream_t st) {
+  if (d <= 0) return hipSuccess;
+  ProfScope prof(POET_K_GATHER, st, 0, (double)d * 8);
+  hipLaunchKernelGGL(k_sample_rank, dim3((d + 63) / 64), dim3(kRankChunk), 0, st, d, 0, h, nullptr, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather2d(int rows, int cols, int elem_bytes, const void* in, int64_t ldi, int in_rows, int in_cols,
+                           const int32_t* row_idx, const int32_t* col_idx, void* out, int64_t ldo, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  ProfScope prof(POET_K_GATHER, st, 0, 2.0 * elem_bytes * (double)rows * cols);
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (elem_bytes == 2 && col_idx && in_cols <= GC_MAX_IN && cols <= GC_MAX_OUT && ldi % 8 == 0 && ldo % 8 == 0 &&
+      a16(in) && a16(out)) {
+    hipLaunchKernelGGL(k_gather_cols_lds, dim3((rows + GC_ROWS - 1) / GC_ROWS), dim3(256), 0, st, rows, cols,
+                       reinterpret_cast<const uint16_t*>(in), ldi, in_rows, in_cols, row_idx, col_idx,
+                       reinterpret_cast<uint16_t*>(out), ldo);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)std::min(65535, (cols + 255) / 256), (unsigned)std::min(rows, 65535));
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_gather2d<uint16_t>, grid, dim3(256), 0, st, rows, cols, reinterpret_cast<const uint16_t*>(in),
+                       ldi, in_rows, in_cols, row_idx, col_idx, reinterpret_cast<uint16_t*>(out), ldo);
+  else
+    hipLaunchKernelGGL(k_gather2d<uint32_t>, grid, dim3(256), 0, st, rows, cols, reinterpret_cast<const uint32_t*>(in),
+                       ldi, in_rows, in_cols, row_idx, col_idx, reinterpret_cast<uint32_t*>(out), ldo);
   return hipGetLastError();
 }
 

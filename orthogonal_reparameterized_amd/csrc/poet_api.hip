@@ -1219,6 +1219,31 @@ poet_status poet_sample_indices_noalloc(int32_t d, int32_t s, uint64_t seed, uin
   return POET_OK;
 }
 
+poet_status poet_sample_permutation(int32_t d, uint64_t seed, uint32_t linear_id, uint32_t side, uint32_t epoch,
+                                    int32_t* perm, int32_t* inv, void* stream) {
+  if (d < 1) return fail(POET_E_SHAPE, "need d >= 1 (d=%d)", d);
+  if (!perm) return fail(POET_E_ARG, "null perm");
+  HIP_TRY(launch_sample_permutation(d, sampler_hash(seed, linear_id, side, epoch), perm, inv,
+                                    reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
+poet_status poet_gather2d(int32_t rows, int32_t cols, int32_t elem_bytes, const void* in, int64_t ldi, int32_t in_rows,
+                          int32_t in_cols, const int32_t* row_idx, const int32_t* col_idx, void* out, int64_t ldo,
+                          void* stream) {
+  if (rows < 0 || cols < 0 || in_rows < 1 || in_cols < 1)
+    return fail(POET_E_SHAPE, "need rows, cols >= 0 and in_rows, in_cols >= 1");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(POET_E_ARG, "elem_bytes = %d must be 2 or 4", elem_bytes);
+  if (ldi < in_cols || ldo < cols) return fail(POET_E_SHAPE, "leading dimensions below the row lengths");
+  if (!row_idx && rows > in_rows) return fail(POET_E_SHAPE, "rows > in_rows without a row index");
+  if (!col_idx && cols > in_cols) return fail(POET_E_SHAPE, "cols > in_cols without a column index");
+  if (rows == 0 || cols == 0) return POET_OK;
+  if (!in || !out) return fail(POET_E_ARG, "null in or out");
+  HIP_TRY(launch_gather2d(rows, cols, elem_bytes, in, ldi, in_rows, in_cols, row_idx, col_idx, out, ldo,
+                          reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
 poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* primR, const float* primP,
                             const int32_t* idxR, const int32_t* idxP, const void* X, void* Y, void* W_out, void* ws,
                             size_t ws_bytes, void* stream) {

@@ -235,6 +235,137 @@ class PoetLinear:
         self.W0P = self.RW0 = None
 
 
+class PermutedPoetLinear:
+    """Permuted POET-BS on the GPU: R = Pi_R^T B_R Pi_R and P = Pi_P^T B_P Pi_P, with B_R, B_P block-diagonal (the
+    POET-BS primitives) and Pi_R, Pi_P random permutations of the output and input dimensions, drawn by
+    ``poet_sample_permutation`` and fresh at every merge (a reading of the sampled sub-block primitives, Approach
+    section of the method summary).
+
+    Realized as a plain POET-BS ``PoetLinear`` (``inner``) on the relabeled weight W0' = Pi_R W0 Pi_P^T: W = R W0 P
+    = Pi_R^T (B_R W0' B_P) Pi_P, so with X' = X Pi_P^T (the columns of X gathered by perm_P) the inner layer gives
+    Y' = X' (B_R W0' B_P)^T and Y = Y' Pi_R (the columns of Y' gathered by inv_R); the backward gathers dY by perm_R
+    and returns dX' gathered by inv_P; the inner layer's dtheta are the permuted layer's. A merge merges W0' on the
+    inner layer and relabels it for the next epoch's permutations (rows by inv_R_old[perm_R_new], columns alike).
+    Every step runs in the library's kernels (``poet_gather2d`` moves the data); this class holds buffers only.
+    The same calls as ``PoetLinear`` (build, forward/backward, forward_act/backward_act, optimizer_step, merge);
+    each backward takes the gathered X' of the forward just before it (its X argument must be that forward's).
+    """
+
+    def __init__(self, m: int, n: int, T: int, R: B.poet_side, P: B.poet_side, act_dtype: int, W0,
+                 thetaR=None, thetaP=None, seed: int = 0, linear_id: int = 0, ldw: Optional[int] = None,
+                 ldx: Optional[int] = None, ldy: Optional[int] = None, device: str = "cuda", path: str = "weight"):
+        if R.mode != B.POET_BS or P.mode != B.POET_BS:
+            raise ValueError("permuted POET-BS needs POET-BS sides")
+        torch = _torch()
+        dev = torch.device(device)
+        self.m, self.n, self.T = m, n, T
+        self.seed, self.linear_id, self.epoch = seed, linear_id, 0
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.permR, self.invR = torch.empty(m, **i32), torch.empty(m, **i32)
+        self.permP, self.invP = torch.empty(n, **i32), torch.empty(n, **i32)
+        self._sample(self.epoch)
+        W0d = torch.as_tensor(W0, dtype=torch.float32).to(dev).contiguous()
+        W0p = torch.empty_like(W0d)
+        B.poet_gather2d(W0d, W0p, self.permR, self.permP)
+        self.inner = PoetLinear(m, n, T, R, P, act_dtype, W0p, thetaR, thetaP, seed=seed, linear_id=linear_id,
+                                ldw=ldw, ldx=ldx, ldy=ldy, device=device, path=path)
+        del W0d, W0p
+        inner = self.inner
+        self.L, self.act, self.act_path, self.dev = inner.L, inner.act, inner.act_path, dev
+        self.Xp, self.Yp = inner.alloc_act(T, inner.L.ldx), inner.alloc_act(T, inner.L.ldy)
+        self.dYp, self.dXp = inner.alloc_act(T, inner.L.ldy), inner.alloc_act(T, inner.L.ldx)
+        self._W0alt = torch.zeros_like(inner.W0)  # the other buffer of the relabeling at a merge
+        self._xp_ready = False
+
+    def _sample(self, epoch: int, stream=None):
+        B.poet_sample_permutation(self.m, self.seed, self.linear_id, B.POET_SIDE_R, epoch, self.permR, self.invR,
+                                  stream)
+        B.poet_sample_permutation(self.n, self.seed, self.linear_id, B.POET_SIDE_P, epoch, self.permP, self.invP,
+                                  stream)
+
+    # the layer's parameters and gradients are the inner layer's
+    def __getattr__(self, name):
+        if name in ("thetaR", "thetaP", "dthetaR", "dthetaP", "primR", "primP", "mR", "vR", "mP", "vP",
+                    "opt_steps", "grad_ready", "built", "W0b"):
+            return getattr(self.inner, name)
+        raise AttributeError(name)
+
+    def alloc_act(self, rows: int, ld: int):
+        return self.inner.alloc_act(rows, ld)
+
+    def alloc_W(self):
+        return self.inner.alloc_W()
+
+    def build(self, stream=None):
+        self.inner.build(stream)
+
+    def _in(self, X, stream):
+        B.poet_gather2d(X, self.Xp, col_idx=self.permP, stream=stream)
+        self._xp_ready = True
+
+    def _take_xp(self):
+        if not self._xp_ready:
+            raise RuntimeError("the backward of a permuted layer needs the forward just before it (its gathered X')")
+        self._xp_ready = False
+
+    def forward(self, X, Y, W_out=None, stream=None):
+        """Weight side. W_out (optional) receives the inner layer's W' = B_R W0' B_P (relabeled coordinates)."""
+        self._in(X, stream)
+        self.inner.forward(self.Xp, self.Yp, W_out, stream)
+        B.poet_gather2d(self.Yp, Y, col_idx=self.invR, stream=stream)
+
+    def backward(self, X, dY, dX, W=None, stream=None):
+        self._take_xp()
+        B.poet_gather2d(dY, self.dYp, col_idx=self.permR, stream=stream)
+        self.inner.backward(self.Xp, self.dYp, self.dXp, W, stream)
+        B.poet_gather2d(self.dXp, dX, col_idx=self.invP, stream=stream)
+
+    def forward_act(self, X, Y, Z, stream=None):
+        """Activation side; Z (kept for backward_act) is the inner layer's, in relabeled coordinates."""
+        self._in(X, stream)
+        self.inner.forward_act(self.Xp, self.Yp, Z, stream)
+        B.poet_gather2d(self.Yp, Y, col_idx=self.invR, stream=stream)
+
+    def backward_act(self, X, Z, dY, dX, stream=None):
+        self._take_xp()
+        B.poet_gather2d(dY, self.dYp, col_idx=self.permR, stream=stream)
+        self.inner.backward_act(self.Xp, Z, self.dYp, self.dXp, stream)
+        B.poet_gather2d(self.dXp, dX, col_idx=self.invP, stream=stream)
+
+    def optimizer_step(self, hp: B.poet_adamw, stream=None):
+        self.inner.optimizer_step(hp, stream)
+
+    def merge(self, stream=None):
+        """Merge-then-reinitialize: the inner merge folds B_R, B_P into W0' and resets theta and the moments;
+        then the next epoch's permutations are drawn and W0' is relabeled to them (and its bf16 copy refreshed)."""
+        self.inner.merge(stream=stream)
+        self.relabel(stream)
+
+    def relabel(self, stream=None):
+        """Draw the next epoch's permutations and relabel W0' to them (after a merge of the inner layer, e.g. by
+        PoetGroup.merge over inner layers)."""
+        torch = _torch()
+        oldR, oldP = self.invR.clone(), self.invP.clone()
+        self.epoch += 1
+        self._sample(self.epoch, stream)
+        sigR = torch.empty(1, self.m, dtype=torch.int32, device=self.dev)
+        sigP = torch.empty(1, self.n, dtype=torch.int32, device=self.dev)
+        B.poet_gather2d(oldR.view(1, -1), sigR, col_idx=self.permR, stream=stream)  # inv_R_old[perm_R_new[i]]
+        B.poet_gather2d(oldP.view(1, -1), sigP, col_idx=self.permP, stream=stream)
+        inner = self.inner
+        B.poet_gather2d(inner.W0[:, :self.n], self._W0alt, sigR.view(-1), sigP.view(-1), stream=stream)
+        inner.W0, self._W0alt = self._W0alt, inner.W0
+        if inner.W0b is not None:
+            B.poet_weight_shadow(inner.L, inner.W0, inner.W0b, stream)
+
+    def original_weight(self, stream=None):
+        """W0 in the original coordinates (float32 m x n): W0[x][y] = W0'[inv_R[x]][inv_P[y]]."""
+        torch = _torch()
+        out = torch.empty((self.m, self.n), dtype=torch.float32, device=self.dev)
+        B.poet_gather2d(self.inner.W0[:, :self.n], out, self.invR, self.invP, stream=stream)
+        return out
+
+
 class PoetGroup:
     """The per-block steps of several POET linears (e.g. the seven of a transformer block) in shared launches.
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "poet.h")
 def header_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(poet_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(poet_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_library_loads_and_exports_header_symbols():
@@ -28,7 +28,7 @@ def test_library_loads_and_exports_header_symbols():
     for nm in names:
         assert hasattr(L, nm), nm
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (poet_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (poet_[a-z0-9_]+)\b", out))
     assert set(names) <= exported
     assert set(B.EXPORTS) == set(names)
 
@@ -338,3 +338,18 @@ def test_mfma_probe_rejects_bad_arguments_on_the_host():
     assert lb.poet_mfma_probe(10, 0, FAKE, None) == B.POET_E_ARG
     assert lb.poet_mfma_probe(10, 65536, FAKE, None) == B.POET_E_ARG
     assert lb.poet_mfma_probe(10, 8, None, None) == B.POET_E_ARG
+
+
+def test_permutation_sampler_and_gather_reject_bad_arguments_on_the_host():
+    lb = B.lib()
+    assert lb.poet_sample_permutation(0, 1, 2, 3, 4, FAKE, None, None) == B.POET_E_SHAPE
+    assert lb.poet_sample_permutation(10, 1, 2, 3, 4, None, FAKE, None) == B.POET_E_ARG
+    g = lb.poet_gather2d
+    assert g(4, 4, 3, FAKE, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_ARG  # element size
+    assert g(4, 4, 2, FAKE, 3, 4, 4, None, None, FAKE, 4, None) == B.POET_E_SHAPE  # ldi < in_cols
+    assert g(4, 4, 2, FAKE, 4, 4, 4, None, None, FAKE, 3, None) == B.POET_E_SHAPE  # ldo < cols
+    assert g(5, 4, 2, FAKE, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_SHAPE  # rows beyond the source
+    assert g(4, 5, 4, FAKE, 4, 4, 4, None, None, FAKE, 5, None) == B.POET_E_SHAPE  # columns beyond the source
+    assert g(4, 4, 4, None, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_ARG
+    assert g(-1, 4, 4, FAKE, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_SHAPE
+    assert g(0, 4, 4, None, 4, 4, 4, None, None, None, 4, None) == B.POET_OK  # nothing to move
