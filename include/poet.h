@@ -121,9 +121,19 @@ size_t poet_build_workspace_bytes(const poet_side* s, int with_powers);
  *          are unspecified), needed by poet_linear_bwd when k >= 1.
  *   qnorm  [num_prims]       float32 out, nullable: Frobenius norm of each primitive's Q. The series
  *          converges for ||Q||_2 < 1; the pages warn it can diverge without enough terms (Limitations).
+ *   flags  POET_BUILD_STEP or POET_BUILD_MERGE (below).
  *   ws     at least poet_build_workspace_bytes(s, powers != NULL) bytes (may be NULL when that is 0). */
 poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float* prim, void* powers,
-                                  float* qnorm, void* ws, size_t ws_bytes, void* stream);
+                                  float* qnorm, int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* Build precision. A bf16 chain that runs as separate products (FS sides, BS blocks above 256 or not a multiple
+ * of 8; poet_build_workspace_bytes(s, 1) > 0 exactly for those) keeps Q^2 in bf16 for the training step, whose
+ * products round their operands to bf16 anyway (POET_BUILD_STEP). A merge folds the primitives into the float32
+ * W0, so a build that precedes one forms the square term to float32 accuracy from three bf16 parts of 2Q
+ * (POET_BUILD_MERGE): two more products and the splits per side. Other sides build the same either way. Any
+ * other flag value gives POET_E_ARG. */
+#define POET_BUILD_STEP 0
+#define POET_BUILD_MERGE 1
 
 /* The exact Cayley primitives R = (I + Q)(I - Q)^{-1} of one side (the map the truncated series approximates;
  * "Builds on ... Cayley parameterization", Experimental setup), an accuracy reference for poet_build_orthogonal:
@@ -267,14 +277,15 @@ poet_status poet_linear_bwd_folded_prims(const poet_layer* L, const void* RW0, c
  * own buffers; the tables are host arrays of count device pointers, entry i belonging to sides[i]. Results are
  * those of the one-side calls (the adjoint's split-K summation order may differ). */
 
-/* poet_build_orthogonal for count sides (no qnorm). powers[i] is required for every side with k >= 1.
+/* poet_build_orthogonal for count sides (no qnorm; flags as there). powers[i] is required for every side with
+ * k >= 1.
  * ops: nullable table; where ops[i] is non-NULL (BS sides only) it receives the bf16 operand copies of side i's
  * primitives that the activation-side calls take (layout above poet_linear_fwd_act).
  * ws: at least poet_build_group_workspace_bytes(count, sides) bytes (may be NULL when that is 0). */
 size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides);
 poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
-                                        float* const* prim, void* const* powers, void* const* ops, void* ws,
-                                        size_t ws_bytes, void* stream);
+                                        float* const* prim, void* const* powers, void* const* ops, int32_t flags,
+                                        void* ws, size_t ws_bytes, void* stream);
 
 /* The Neumann adjoint and skew projection of count sides (the last step of the backward to the skew
  * parameters, Approach section): dprim[i] float32 in (poet_linear_bwd_act_prims), powers[i] the saved powers

@@ -21,6 +21,7 @@ POET_F32, POET_BF16 = 0, 1
 POET_SIDE_R, POET_SIDE_P = 0, 1
 POET_OP_BUILD, POET_OP_FWD, POET_OP_BWD, POET_OP_MERGE, POET_OP_FWD_ACT, POET_OP_BWD_ACT = range(6)
 POET_MAX_K, POET_MAX_PRIM = 16, 8192
+POET_BUILD_STEP, POET_BUILD_MERGE = 0, 1
 
 EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len", "poet_workspace_bytes",
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
@@ -106,7 +107,7 @@ def lib() -> ctypes.CDLL:
     L.poet_sample_workspace_bytes.restype = S
     L.poet_build_workspace_bytes.argtypes = [P(poet_side), ctypes.c_int]
     L.poet_build_workspace_bytes.restype = S
-    L.poet_build_orthogonal.argtypes = [P(poet_side), VP, VP, VP, VP, VP, S, VP]
+    L.poet_build_orthogonal.argtypes = [P(poet_side), VP, VP, VP, VP, I32, VP, S, VP]
     L.poet_sample_indices.argtypes = [I32, I32, U64, U32, U32, U32, VP, VP, S, VP]
     L.poet_sample_indices_noalloc.argtypes = [I32, I32, U64, U32, U32, U32, VP, VP]
     L.poet_linear_fwd.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
@@ -120,7 +121,7 @@ def lib() -> ctypes.CDLL:
     L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_build_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_build_group_workspace_bytes.restype = S
-    L.poet_build_orthogonal_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), VP, S, VP]
+    L.poet_build_orthogonal_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), P(VP), I32, VP, S, VP]
     L.poet_adjoint_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_adjoint_group_workspace_bytes.restype = S
     L.poet_adjoint_group.argtypes = [I32, P(poet_side), P(VP), P(VP), P(VP), VP, S, VP]
@@ -339,7 +340,10 @@ def _side_sizes(s: poet_side):
 
 # ---- calls ----------------------------------------------------------------------------------------------
 
-def poet_build_orthogonal(s: poet_side, theta, prim, powers=None, qnorm=None, ws=None, stream=None):
+def poet_build_orthogonal(s: poet_side, theta, prim, powers=None, qnorm=None, ws=None, stream=None,
+                          for_merge: bool = False):
+    """Build one side's primitives; for_merge forms the square term of a separate-product bf16 chain to float32
+    accuracy (POET_BUILD_MERGE), as a build that precedes a merge takes it."""
     nth, npr, npl, npw = _side_sizes(s)
     need_ws = poet_build_workspace_bytes(s, powers is not None)
     if ws is None and need_ws > 0:  # scratch for the caller that passes none (device memory from torch)
@@ -347,7 +351,8 @@ def poet_build_orthogonal(s: poet_side, theta, prim, powers=None, qnorm=None, ws
     st = lib().poet_build_orthogonal(
         ctypes.byref(s), _ptr(theta, "theta", 4 * nth, "float32"), _ptr(prim, "prim", 4 * npl, "float32"),
         _ptr(powers, "powers", npw * _esz(s.dtype), _dt_name(s.dtype), allow_none=True),
-        _ptr(qnorm, "qnorm", 4 * npr, "float32", allow_none=True), _ptr(ws, "ws", need_ws, allow_none=True),
+        _ptr(qnorm, "qnorm", 4 * npr, "float32", allow_none=True),
+        POET_BUILD_MERGE if for_merge else POET_BUILD_STEP, _ptr(ws, "ws", need_ws, allow_none=True),
         need_ws if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_build_orthogonal")
 
@@ -549,9 +554,10 @@ def poet_adjoint_group_workspace_bytes(sides) -> int:
     return int(lib().poet_adjoint_group_workspace_bytes(len(sides), _side_array(sides)))
 
 
-def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=None, ops=None):
+def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=None, ops=None, for_merge=False):
     """poet_build_orthogonal for every side in ``sides`` (lists of equal length; powers required for k >= 1);
-    ``ops`` (optional list, entries may be None) receives the bf16 operand copies of the BS sides' primitives."""
+    ``ops`` (optional list, entries may be None) receives the bf16 operand copies of the BS sides' primitives;
+    for_merge as in poet_build_orthogonal."""
     n = len(sides)
     if not (len(thetas) == len(prims) == len(powers) == n) or (ops is not None and len(ops) != n):
         raise ValueError("sides, thetas, prims, powers (and ops) must have the same length")
@@ -567,7 +573,9 @@ def poet_build_orthogonal_group(sides, thetas, prims, powers, ws=None, stream=No
                     [s.k == 0 for s in sides])
     op = None if ops is None else _ptr_table(ops, [f"ops[{i}]" for i in range(n)],
                                              [6 * poet_prim_len(s) for s in sides], ["bfloat16"] * n, [True] * n)
-    st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, op, _ptr(ws, "ws", need, allow_none=True),
+    st = lib().poet_build_orthogonal_group(n, _side_array(sides), th, pr, pw, op,
+                                           POET_BUILD_MERGE if for_merge else POET_BUILD_STEP,
+                                           _ptr(ws, "ws", need, allow_none=True),
                                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_build_orthogonal_group")
 

@@ -1124,9 +1124,10 @@ size_t poet_workspace_bytes(const poet_layer* L, int op) {
 }
 
 poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float* prim, void* powers, float* qnorm,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  int32_t flags, void* ws, size_t ws_bytes, void* stream) {
   SideInfo S;
   if (!side_info(s, &S, "side")) return g_last;
+  if (flags != POET_BUILD_STEP && flags != POET_BUILD_MERGE) return fail(POET_E_ARG, "bad build flags %d", flags);
   if (!prim) return fail(POET_E_ARG, "null prim");
   if (!theta && S.theta_len > 0) return fail(POET_E_ARG, "null theta");
   const size_t need = poet_build_workspace_bytes(s, powers != nullptr);
@@ -1141,7 +1142,7 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
   const size_t part_elems = build_part_elems(S);
   float* part = part_elems ? a.take<float>(part_elems) : nullptr;
   SqBufs sq;
-  if (sq_side(S)) plan_sq(a, S, &sq);
+  if (sq_side(S) && flags == POET_BUILD_MERGE) plan_sq(a, S, &sq);
   if (qnorm) HIP_TRY(launch_qnorm(theta, S.mode, S.d, S.bp, S.nprim, qnorm, st));
   // prim = I + coef Q (coef 2 for k >= 1) with Q exact from theta, and the first saved power Q
   HIP_TRY(launch_theta_prep(theta, S.mode, S.d, S.bp, S.nprim, S.k, prim, S.k > 0 ? (void*)pw : nullptr, S.dtype,
@@ -1791,10 +1792,11 @@ size_t poet_build_group_workspace_bytes(int32_t count, const poet_side* sides) {
 }
 
 poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, const float* const* theta,
-                                        float* const* prim, void* const* powers, void* const* ops, void* ws,
-                                        size_t ws_bytes, void* stream) {
+                                        float* const* prim, void* const* powers, void* const* ops, int32_t flags,
+                                        void* ws, size_t ws_bytes, void* stream) {
   std::vector<SideInfo> S;
   if (!group_sides(count, sides, &S)) return g_last;
+  if (flags != POET_BUILD_STEP && flags != POET_BUILD_MERGE) return fail(POET_E_ARG, "bad build flags %d", flags);
   if (count == 0) return POET_OK;
   if (!theta || !prim || !powers) return fail(POET_E_ARG, "null pointer table");
   for (int i = 0; i < count; ++i) {
@@ -1815,7 +1817,8 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
   auto side_ops = [&](int i) -> __bf16* { return ops ? reinterpret_cast<__bf16*>(ops[i]) : nullptr; };
   for (int i = 0; i < count; ++i) {
     if (S[i].k == 0 || chain_side(S[i], powers[i]) || in_chunk[i]) grouped.push_back(i);
-    else if (poet_build_orthogonal(&sides[i], theta[i], prim[i], powers[i], nullptr, ws, ws_bytes, stream) != POET_OK)
+    else if (poet_build_orthogonal(&sides[i], theta[i], prim[i], powers[i], nullptr, flags, ws, ws_bytes, stream) !=
+             POET_OK)
       return g_last;
   }
   for (size_t c0 = 0; c0 < grouped.size(); c0 += MAXG) {
@@ -1845,9 +1848,11 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
     const size_t part_elems = build_chunk_part_elems(c);
     float* part = a.take<float>(part_elems);
     const int n = (int)c.idx.size();
-    // (2Q)^2 of every side to float32 accuracy (prim holds I + 2Q after the theta launch), one grouped product
+    // for a merge: (2Q)^2 of every side to float32 accuracy (prim holds I + 2Q after the theta launch), one grouped
+    // product
+    const bool accurate_sq = flags == POET_BUILD_MERGE;
     std::vector<SqBufs> sq(n);
-    {
+    if (accurate_sq) {
       GemmDesc pr[MAXG];
       for (int u = 0; u < n; ++u) {
         plan_sq(a, S[c.idx[u]], &sq[u]);
@@ -1860,7 +1865,7 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
         for (int u = 0; u < n; ++u) HIP_TRY(launch_gemm(pr[u], st));
       }
     }
-    for (int step = 1; step <= c.k && c.k > 1; ++step) {  // k == 1: the series ends at the accurate Q^2
+    for (int step = 1; step <= c.k && !(accurate_sq && c.k == 1); ++step) {  // k == 1: ends at the accurate Q^2
       GemmDesc pr[MAXG];
       for (int u = 0; u < n; ++u) {
         const int i = c.idx[u];

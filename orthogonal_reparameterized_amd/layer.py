@@ -21,6 +21,12 @@ def _tdt(dt: int):
     return torch.bfloat16 if dt == B.POET_BF16 else torch.float32
 
 
+def _merge_grade_differs(side: B.poet_side) -> bool:
+    """True for sides whose chain runs as separate bf16 products: only their build differs between the step's
+    precision and the merge's (poet_build_workspace_bytes(side, 1) > 0 exactly for those)."""
+    return B.poet_build_workspace_bytes(side, True) > 0
+
+
 class PoetLinear:
     """One POET linear W = R W0 P on the GPU.
 
@@ -215,8 +221,12 @@ class PoetLinear:
     def merge(self, shadow=None, stream=None):
         """Merge-then-reinitialize; refreshes the bf16 copy of W0 of the activation-side path (and `shadow`,
         when given, receives the merged W0 in the act dtype as well). The merge folds the primitives of the last
-        build; afterwards theta is zero and the next step must build again."""
+        build, built again first at the merge's precision where that differs (POET_BUILD_MERGE); afterwards theta is
+        zero and the next step must build again."""
         self._need_build("merge")
+        for side, th, pr, x in ((self.L.R, self.thetaR, self.primR, "R"), (self.L.P, self.thetaP, self.primP, "P")):
+            if _merge_grade_differs(side):
+                B.poet_build_orthogonal(side, th, pr, self._powers(x), None, self.ws, stream, for_merge=True)
         B.poet_merge(self.L, self.W0, self.W0b if shadow is None else shadow, self.thetaR, self.thetaP, self.primR,
                      self.primP, self.idxR, self.idxP, self.seed, self.linear_id, self.epoch + 1, self.ws, stream)
         B.poet_optimizer_reset_group([self.L.R, self.L.P], [self.mR, self.mP], [self.vR, self.vP], stream)
@@ -468,6 +478,13 @@ class PoetGroup:
             raise ValueError("PoetGroup.merge needs one sampler seed and one epoch across its linears")
         for pl in pls:
             pl._need_build("PoetGroup.merge")
+        # the sides whose build differs at the merge's precision are built again at it first
+        redo = [(s, t, p, w) for pl in pls for s, t, p, w in ((pl.L.R, pl.thetaR, pl.primR, pl._powers("R")),
+                                                             (pl.L.P, pl.thetaP, pl.primP, pl._powers("P")))
+                if _merge_grade_differs(s)]
+        if redo:
+            B.poet_build_orthogonal_group([r[0] for r in redo], [r[1] for r in redo], [r[2] for r in redo],
+                                          [r[3] for r in redo], self.ws, stream, for_merge=True)
         B.poet_merge_group([pl.L for pl in pls], [pl.W0 for pl in pls], [pl.W0b for pl in pls],
                            [pl.thetaR for pl in pls], [pl.thetaP for pl in pls], [pl.primR for pl in pls],
                            [pl.primP for pl in pls], [pl.idxR for pl in pls], [pl.idxP for pl in pls], pls[0].seed,

@@ -145,10 +145,11 @@ def test_bwd_and_merge_reject_bad_arguments():
 def test_build_and_sampler_reject_bad_arguments():
     lb = B.lib()
     s = B.side(0, 256, 32, 3, 0)
-    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, None, FAKE, None, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, FAKE, None, None, None, 0, None) == B.POET_E_WORKSPACE
+    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, None, FAKE, None, 0, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, FAKE, None, None, 0, None, 0, None) == B.POET_E_WORKSPACE
+    assert lb.poet_build_orthogonal(ctypes.byref(s), FAKE, FAKE, FAKE, None, 2, None, 0, None) == B.POET_E_ARG  # flags
     bad = B.side(0, 256, 0, 3, 0)
-    assert lb.poet_build_orthogonal(ctypes.byref(bad), FAKE, FAKE, FAKE, None, None, 0, None) == B.POET_E_SHAPE
+    assert lb.poet_build_orthogonal(ctypes.byref(bad), FAKE, FAKE, FAKE, None, 0, None, 0, None) == B.POET_E_SHAPE
     assert lb.poet_sample_indices(10, 11, 1, 2, 3, 4, FAKE, FAKE, 1 << 20, None) == B.POET_E_SHAPE
     assert lb.poet_sample_indices(0, 0, 1, 2, 3, 4, FAKE, FAKE, 1 << 20, None) == B.POET_E_SHAPE
     assert lb.poet_sample_indices(100, 10, 1, 2, 3, 4, FAKE, FAKE, 4, None) == B.POET_E_WORKSPACE
@@ -198,14 +199,15 @@ def test_group_calls_reject_bad_arguments():
     assert lb.poet_build_group_workspace_bytes(1, bad) == 0
     tab = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
     nul = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
-    assert lb.poet_build_orthogonal_group(-1, arr, tab, tab, tab, None, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(0, None, None, None, None, None, None, 0, None) == B.POET_OK
-    assert lb.poet_build_orthogonal_group(3, arr, None, tab, tab, None, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(3, arr, tab, nul, tab, None, None, 0, None) == B.POET_E_ARG
-    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, nul, None, None, 0, None) == B.POET_E_ARG  # powers for k >= 1
-    assert lb.poet_build_orthogonal_group(1, bad, tab, tab, tab, None, None, 0, None) == B.POET_E_SHAPE
+    assert lb.poet_build_orthogonal_group(-1, arr, tab, tab, tab, None, 0, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(0, None, None, None, None, None, 0, None, 0, None) == B.POET_OK
+    assert lb.poet_build_orthogonal_group(3, arr, None, tab, tab, None, 0, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, nul, tab, None, 0, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, nul, None, 0, None, 0, None) == B.POET_E_ARG  # powers for k >= 1
+    assert lb.poet_build_orthogonal_group(1, bad, tab, tab, tab, None, 0, None, 0, None) == B.POET_E_SHAPE
     fs_ops = (ctypes.c_void_p * 3)(None, None, FAKE)  # operand copies exist for BS sides only
-    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, tab, fs_ops, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, tab, fs_ops, 0, None, 0, None) == B.POET_E_ARG
+    assert lb.poet_build_orthogonal_group(3, arr, tab, tab, tab, None, 7, None, 0, None) == B.POET_E_ARG  # flags
     assert lb.poet_adjoint_group(3, arr, tab, tab, nul, FAKE, wa, None) == B.POET_E_ARG
     assert lb.poet_adjoint_group(3, arr, tab, nul, tab, FAKE, wa, None) == B.POET_E_ARG
     assert lb.poet_adjoint_group(3, arr, tab, tab, tab, FAKE, wa - 1, None) == B.POET_E_WORKSPACE
