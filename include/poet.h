@@ -435,7 +435,9 @@ void poet_profile_enable(int on);
  * data-movement classes) and algorithmic bytes (operands read once, results written once).
  * Returns POET_E_ARG for a bad class, POET_E_HIP if an event query fails. */
 poet_status poet_profile_query(int kclass, int64_t* launches, double* total_ms, double* flops, double* bytes);
-const char* poet_status_string(poet_status st);
+/* Text of a status code; any other int gives an "unknown status" text (an int, so that a code from outside the
+ * enum's range is a valid argument). */
+const char* poet_status_string(int status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* poet_last_error(void);
 const char* poet_version(void);

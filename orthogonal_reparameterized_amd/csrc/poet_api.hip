@@ -2174,8 +2174,8 @@ poet_status poet_mfma_probe(int64_t iters, int32_t workgroups, float* out, void*
   return POET_OK;
 }
 
-const char* poet_status_string(poet_status st) {
-  switch (st) {
+const char* poet_status_string(int status) {
+  switch (status) {
     case POET_OK: return "POET_OK";
     case POET_E_ARG: return "POET_E_ARG: invalid argument";
     case POET_E_SHAPE: return "POET_E_SHAPE: inconsistent or unsupported shape";
