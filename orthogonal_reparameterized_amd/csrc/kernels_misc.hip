@@ -237,16 +237,34 @@ __global__ __launch_bounds__(256) void k_rows4(const float* __restrict__ src, in
   }
 }
 
-__global__ void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
-                              int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst,
-                              __bf16* __restrict__ dst2, int64_t ld_dst2) {
-  for (int r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x) {
-      const float v = src[(int64_t)r * ld_src + clampi(idx[j], dlim)];
-      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + j] = (__bf16)v;
-      else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + j] = v;
-      if (dst2) dst2[(int64_t)r * ld_dst2 + j] = (__bf16)v;
+// dst[r][j] = src[r][idx[j]] (float32 or bf16 dst) and, when dst2 is given, dst2[r][j] = bf16 of it. Four consecutive
+// output columns per thread (four reads near each other: the indices ascend) and, with vec (pitches multiples of 4,
+// bases aligned), one 16-byte (float32) or 8-byte (bf16) store per output; several rows per workgroup.
+__global__ __launch_bounds__(256) void k_gather_cols(const float* __restrict__ src, int64_t ld_src, int rows,
+                                                     const int32_t* __restrict__ idx, int s, int dlim,
+                                                     void* __restrict__ dst, int dst_dt, int64_t ld_dst,
+                                                     __bf16* __restrict__ dst2, int64_t ld_dst2, int vec) {
+  for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float* srow = src + (int64_t)r * ld_src;
+    for (int j = 4 * (blockIdx.x * blockDim.x + threadIdx.x); j < s; j += 4 * gridDim.x * blockDim.x) {
+      if (vec && j + 4 <= s) {
+        const int4 c = *reinterpret_cast<const int4*>(idx + j);
+        const float4 v = {srow[clampi(c.x, dlim)], srow[clampi(c.y, dlim)], srow[clampi(c.z, dlim)],
+                          srow[clampi(c.w, dlim)]};
+        const bf16x4_t b = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+        if (dst_dt == BF16) *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(dst) + (int64_t)r * ld_dst + j) = b;
+        else *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + (int64_t)r * ld_dst + j) = v;
+        if (dst2) *reinterpret_cast<bf16x4_t*>(dst2 + (int64_t)r * ld_dst2 + j) = b;
+      } else {
+        for (int u = 0; u < 4 && j + u < s; ++u) {
+          const float v = srow[clampi(idx[j + u], dlim)];
+          if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[(int64_t)r * ld_dst + j + u] = (__bf16)v;
+          else reinterpret_cast<float*>(dst)[(int64_t)r * ld_dst + j + u] = v;
+          if (dst2) dst2[(int64_t)r * ld_dst2 + j + u] = (__bf16)v;
+        }
+      }
     }
+  }
 }
 
 __global__ void k_split3(const float* __restrict__ src, int64_t ld_src, const int32_t* __restrict__ ridx,
@@ -269,14 +287,29 @@ __global__ void k_split3(const float* __restrict__ src, int64_t ld_src, const in
     }
 }
 
-__global__ void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, int rows, const int32_t* __restrict__ idx,
-                               int s, int dlim, void* __restrict__ dst, int dst_dt, int64_t ld_dst) {
+// dst[r][idx[j]] = src[r][j]: four consecutive source columns per thread (one 16-byte load with vec), several rows
+// per workgroup.
+__global__ __launch_bounds__(256) void k_scatter_cols(const float* __restrict__ src, int64_t ld_src, int rows,
+                                                      const int32_t* __restrict__ idx, int s, int dlim,
+                                                      void* __restrict__ dst, int dst_dt, int64_t ld_dst, int vec) {
   for (int r = blockIdx.y; r < rows; r += gridDim.y)
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < s; j += gridDim.x * blockDim.x) {
-      const float v = src[(int64_t)r * ld_src + j];
-      const int64_t o = (int64_t)r * ld_dst + clampi(idx[j], dlim);
-      if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[o] = (__bf16)v;
-      else reinterpret_cast<float*>(dst)[o] = v;
+    for (int j = 4 * (blockIdx.x * blockDim.x + threadIdx.x); j < s; j += 4 * gridDim.x * blockDim.x) {
+      float v[4];
+      int c[4];
+      const int nv = min(4, s - j);
+      if (vec && nv == 4) {
+        const float4 f = *reinterpret_cast<const float4*>(src + (int64_t)r * ld_src + j);
+        const int4 q = *reinterpret_cast<const int4*>(idx + j);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        c[0] = q.x; c[1] = q.y; c[2] = q.z; c[3] = q.w;
+      } else {
+        for (int u = 0; u < nv; ++u) { v[u] = src[(int64_t)r * ld_src + j + u]; c[u] = idx[j + u]; }
+      }
+      for (int u = 0; u < nv; ++u) {
+        const int64_t o = (int64_t)r * ld_dst + clampi(c[u], dlim);
+        if (dst_dt == BF16) reinterpret_cast<__bf16*>(dst)[o] = (__bf16)v[u];
+        else reinterpret_cast<float*>(dst)[o] = v[u];
+      }
     }
 }
 
@@ -445,13 +478,27 @@ __global__ void k_sample_compact(int d, const int32_t* __restrict__ flags, int32
 }
 
 // out (bp x ldo rows per primitive, columns past bp zero) = bf16(prim - I); blockIdx.y = primitive
+// four consecutive elements of a row per thread (bp and ldo multiples of 4: one 16-byte load, one 8-byte store)
 __global__ void k_delta_bf16(const float* __restrict__ prim, int bp, int ldo, __bf16* __restrict__ out) {
   const int p = blockIdx.y;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int e = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   if (e >= bp * ldo) return;
   const int i = e / ldo, j = e - i * ldo;
-  const float v = j < bp ? prim[((int64_t)p * bp + i) * bp + j] - (i == j ? 1.f : 0.f) : 0.f;
-  out[(int64_t)p * bp * ldo + e] = (__bf16)v;
+  const float* row = prim + ((int64_t)p * bp + i) * bp;
+  bf16x4_t w;
+  if ((bp & 3) == 0 && (ldo & 3) == 0) {
+    const float4 v = j < bp ? *reinterpret_cast<const float4*>(row + j) : float4{0.f, 0.f, 0.f, 0.f};
+    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = (__bf16)(j + u < bp ? f[u] - (i == j + u ? 1.f : 0.f) : 0.f);
+    *reinterpret_cast<bf16x4_t*>(out + (int64_t)p * bp * ldo + e) = w;
+  } else {
+    for (int u = 0; u < 4 && e + u < bp * ldo; ++u) {
+      const int ii = (e + u) / ldo, jj = (e + u) - ii * ldo;
+      const float v = jj < bp ? prim[((int64_t)p * bp + ii) * bp + jj] - (ii == jj ? 1.f : 0.f) : 0.f;
+      out[(int64_t)p * bp * ldo + e + u] = (__bf16)v;
+    }
+  }
 }
 
 __device__ __forceinline__ float ld_dt(const void* p, int dt, int64_t i) {
@@ -611,7 +658,7 @@ hipError_t launch_delta_bf16(const float* prim, int nprim, int bp, int ldo, __bf
   if (nprim <= 0 || bp <= 0) return hipSuccess;
   if (nprim > 65535 || (int64_t)bp * ldo > (1 << 30)) return hipErrorInvalidValue;
   ProfScope prof(7, st, 0, (double)nprim * bp * (4.0 * bp + 2.0 * ldo));
-  const dim3 grid((bp * ldo + kThreads - 1) / kThreads, nprim);
+  const dim3 grid((bp * ldo / 4 + kThreads) / kThreads, nprim);
   hipLaunchKernelGGL(k_delta_bf16, grid, dim3(kThreads), 0, st, prim, bp, ldo, out);
   return hipGetLastError();
 }
@@ -785,7 +832,8 @@ hipError_t launch_fill_group(const FillGroup& g, float v, hipStream_t st) {
   return hipGetLastError();
 }
 
-static dim3 row_grid(int cols, int rows) { return dim3((cols + kThreads - 1) / kThreads, rows < 65535 ? rows : 65535); }
+// (column blocks, rows): at most 1024 row slots, so that a workgroup of a tall copy takes several rows
+static dim3 row_grid(int cols, int rows) { return dim3((cols + kThreads - 1) / kThreads, rows < 1024 ? rows : 1024); }
 
 static bool al16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -811,8 +859,11 @@ hipError_t launch_gather_cols_to(const float* src, int64_t ld_src, int rows, con
                                  void* dst, int dst_dt, int64_t ld_dst, hipStream_t st, __bf16* dst2, int64_t ld_dst2) {
   if (rows <= 0 || s <= 0) return hipSuccess;
   ProfScope prof(POET_K_GATHER, st, 0, (double)rows * s * (4 + dtype_size(dst_dt) + (dst2 ? 2 : 0)));
-  hipLaunchKernelGGL(k_gather_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
-                     dst_dt, ld_dst, dst2, ld_dst2);
+  const bool vec = ld_dst % 4 == 0 && (!dst2 || ld_dst2 % 4 == 0) && al16(idx) &&
+                   (dst_dt == BF16 ? (reinterpret_cast<uintptr_t>(dst) & 7) == 0 : al16(dst)) &&
+                   (reinterpret_cast<uintptr_t>(dst2) & 7) == 0;
+  hipLaunchKernelGGL(k_gather_cols, row_grid((s + 3) / 4, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim,
+                     dst, dst_dt, ld_dst, dst2, ld_dst2, vec ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -835,8 +886,9 @@ hipError_t launch_scatter_cols_to(const float* src, int64_t ld_src, int rows, co
                                   void* dst, int dst_dt, int64_t ld_dst, hipStream_t st) {
   if (rows <= 0 || s <= 0) return hipSuccess;
   ProfScope prof(POET_K_GATHER, st, 0, (double)rows * s * (4 + dtype_size(dst_dt)));
-  hipLaunchKernelGGL(k_scatter_cols, row_grid(s, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim, dst,
-                     dst_dt, ld_dst);
+  const bool vec = ld_src % 4 == 0 && al16(src) && al16(idx);
+  hipLaunchKernelGGL(k_scatter_cols, row_grid((s + 3) / 4, rows), dim3(kThreads), 0, st, src, ld_src, rows, idx, s, dlim,
+                     dst, dst_dt, ld_dst, vec ? 1 : 0);
   return hipGetLastError();
 }
 
