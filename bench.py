@@ -279,7 +279,12 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     """One block of 7 linears (or the single-linear workload): timed steps, profiled steps, merge leg."""
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
-    group = None if args.no_group else PoetGroup([e["pl"] for e in lins])
+    group = None if args.no_group else PoetGroup([e["pl"] for e in lins], form_fs=not args.no_form,
+                                                 form_streams=args.form_streams)
+    if group is not None:
+        for e in lins:  # the group keeps the W it forms for FS pairs
+            if id(e["pl"]) in group._formed:
+                e["keep"] = None
     torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -347,7 +352,9 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    "block": wl.b, "fraction": wl.frac, "k": wl.k, "linears": len(lins),
                    "factor_application": "activations" if act else
                    ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
-                   "grouped_side_steps": group is not None, "merge_period": args.merge_period},
+                   "grouped_side_steps": group is not None, "merge_period": args.merge_period,
+                   "fs_formed_in_build": bool(group is not None and group._formed),
+                   "form_streams": len(group._form_streams) if group is not None else 0},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
         "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
         "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
@@ -407,7 +414,10 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     share = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
     mem = dict.fromkeys(("W0_f32", "W0_bf16_copy", "theta_grad_moments", "primitives_and_operand_copies",
                          "saved_powers", "index_sets", "kept_inputs", "kept_Z_or_W", "folded_weights",
-                         "workspaces_and_transients"), 0)
+                         "fs_gradient_operands", "workspaces_and_transients"), 0)
+    # FS pairs formed in the group build (W and the gradient operands kept from the build to the backward), unless
+    # W is formed again in the backward
+    form = not args.no_form and "weights" not in rec
     shared_pw = {}  # position in the layer -> saved-power buffers reused by every layer (recompute "powers")
     layers = []
     for layer, lins in enumerate(specs):
@@ -434,7 +444,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
             keep = None
             if pl.act_path:
                 keep = pl.alloc_act(T, ldy)  # Z = X P^T W0^T
-            elif "weights" not in rec:
+            elif "weights" not in rec and not (form and PoetGroup._formable(pl)):
                 keep = pl.alloc_W()
             mem["kept_Z_or_W"] += _nbytes(keep)
             mem["W0_f32"] += _nbytes(pl.W0)
@@ -453,8 +463,17 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
         log(f"stack: layer {layer} allocated, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
     gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]]), 1), dtype=torch.uint8,
                       device="cuda")
-    groups = [PoetGroup([e["pl"] for e in es], ws=gws) for es in layers]
-    for grp in groups:  # the group's operand copies and folded weights
+    fws = None  # the formation streams' workspaces, shared by the groups (their builds run one after another)
+    if form:
+        fneed = PoetGroup.form_workspace_bytes([e["pl"] for e in layers[0]])
+        if fneed:
+            fws = [torch.empty(fneed, dtype=torch.uint8, device="cuda") for _ in range(args.form_streams)]
+    groups = [PoetGroup([e["pl"] for e in es], ws=gws, form_fs=form, form_streams=args.form_streams, form_ws=fws)
+              for es in layers]
+    for grp in groups:  # the group's operand copies, folded weights and formed FS operands
+        for W, Zr, Acp in grp._formed.values():
+            mem["kept_Z_or_W"] += _nbytes(W)
+            mem["fs_gradient_operands"] += _nbytes(Zr) + _nbytes(Acp)
         for v in grp._ops.values():
             mem["primitives_and_operand_copies"] += sum(_nbytes(t) for t in v)
         for v in grp._fold.values():
@@ -526,7 +545,8 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    "ffn": wl.ffn, "tokens": T, "mode": "BS" if wl.mode == PI.MODE_BS else "FS", "block": wl.b,
                    "fraction": wl.frac, "k": wl.k, "layers": nl, "linears": len(all_specs),
                    "factor_application": "activations" if act else "weight", "grouped_side_steps": True,
-                   "merge_period": args.merge_period, "recompute": sorted(rec) or ["none"]},
+                   "merge_period": args.merge_period, "recompute": sorted(rec) or ["none"],
+                   "fs_formed_in_build": form and any(grp._formed for grp in groups)},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3),
         "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
         "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -575,6 +595,12 @@ def main():
     ap.add_argument("--no-group", action="store_true",
                     help="build and finish the backward of each linear on its own (the default runs the per-side "
                          "steps of all linears of the block in shared launches)")
+    ap.add_argument("--no-form", action="store_true",
+                    help="form W and the FS gradient operands in each linear's forward and backward (the default "
+                         "forms them for every weight-side POET-FS linear in the group build, overlapped on side "
+                         "streams)")
+    ap.add_argument("--form-streams", type=int, default=2,
+                    help="side streams the group build forms the FS pairs on")
     ap.add_argument("--permuted", action="store_true",
                     help="permuted POET-BS: each side's blocks on a random permutation, fresh at every merge "
                          "(PermutedPoetLinear; implies --no-group and skips the extra FS block)")

@@ -211,6 +211,27 @@ poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const fl
                                   const void* dY, void* dX, float* dprimR, float* dprimP, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* The POET-FS weight side with its operands formed ahead of the token products (both sides POET-FS, bf16 sides and
+ * activations). W = R W0 P depends only on W0, the primitives and the index sets, so a step can form every linear's W
+ * (and the two gradient operands) right after the build, before any activation exists, and several linears' forms
+ * can run at once on separate streams:
+ *   poet_fs_form:  W [m x ldw] bf16 out (the W poet_linear_fwd materializes, bit for bit), Zr [R.b x pad8(n)] bf16
+ *                  out = (W0 P)[I_R, :], Acp [m x pad8(P.b)] bf16 out = (R W0)[:, I_P] (the operands
+ *                  poet_linear_bwd forms, bit for bit); ws: poet_fs_form_workspace_bytes(L) bytes.
+ *   poet_linear_fwd_formed:  Y = X W^T with that W (no workspace).
+ *   poet_linear_bwd_formed_prims:  as poet_linear_bwd_prims with that W, Zr and Acp (W0 and the primitives are not
+ *                  read); ws: poet_workspace_bytes(L, POET_OP_BWD) bytes.
+ * Layers that are not both-FS bf16 give POET_E_UNSUPPORTED. */
+size_t poet_fs_form_workspace_bytes(const poet_layer* L);
+poet_status poet_fs_form(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                         const int32_t* idxR, const int32_t* idxP, void* W, void* Zr, void* Acp, void* ws,
+                         size_t ws_bytes, void* stream);
+poet_status poet_linear_fwd_formed(const poet_layer* L, const void* W, const void* X, void* Y, void* stream);
+poet_status poet_linear_bwd_formed_prims(const poet_layer* L, const void* W, const void* Zr, const void* Acp,
+                                         const int32_t* idxR, const int32_t* idxP, const void* X, const void* dY,
+                                         void* dX, float* dprimR, float* dprimP, void* ws, size_t ws_bytes,
+                                         void* stream);
+
 /* ---- activation-side application ---------------------------------------------------------------------
  * The same layer with the factors applied to the activations around the W0 GEMM (W is never formed); the
  * products of the weight-side calls above, associated the other way (W = R W0 P from the method summary):

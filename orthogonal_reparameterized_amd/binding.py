@@ -27,7 +27,8 @@ EXPORTS = ("poet_theta_len", "poet_num_prims", "poet_prim_len", "poet_powers_len
            "poet_sample_workspace_bytes", "poet_build_workspace_bytes", "poet_build_orthogonal",
            "poet_sample_indices", "poet_linear_fwd", "poet_linear_bwd", "poet_merge", "poet_status_string",
            "poet_last_error", "poet_version", "poet_profile_enable", "poet_profile_query", "poet_debug_gemm",
-           "poet_mfma_probe", "poet_sample_permutation", "poet_gather2d",
+           "poet_mfma_probe", "poet_sample_permutation", "poet_gather2d", "poet_fs_form_workspace_bytes",
+           "poet_fs_form", "poet_linear_fwd_formed", "poet_linear_bwd_formed_prims",
            "poet_act_path_supported", "poet_weight_shadow", "poet_linear_fwd_act", "poet_linear_bwd_act",
            "poet_linear_bwd_act_prims", "poet_build_group_workspace_bytes", "poet_build_orthogonal_group",
            "poet_adjoint_group_workspace_bytes", "poet_adjoint_group", "poet_linear_bwd_prims",
@@ -118,6 +119,11 @@ def lib() -> ctypes.CDLL:
     L.poet_linear_fwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_act.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_fs_form_workspace_bytes.argtypes = [P(poet_layer)]
+    L.poet_fs_form_workspace_bytes.restype = S
+    L.poet_fs_form.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
+    L.poet_linear_fwd_formed.argtypes = [P(poet_layer), VP, VP, VP, VP]
+    L.poet_linear_bwd_formed_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_linear_bwd_act_prims.argtypes = [P(poet_layer), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]
     L.poet_build_group_workspace_bytes.argtypes = [I32, P(poet_side)]
     L.poet_build_group_workspace_bytes.restype = S
@@ -434,6 +440,59 @@ def poet_linear_bwd_prims(L: poet_layer, W0, primR, primP, idxR, idxP, W, X, dY,
         _ptr(ws, "ws", need if W is None else 0, allow_none=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "poet_linear_bwd_prims")
+
+
+def fs_operand_shapes(L: poet_layer) -> dict:
+    """Shapes (rows, row pitch) of the bf16 operands poet_fs_form writes besides W: Zr = (W0 P)[I_R, :] and
+    Acp = (R W0)[:, I_P]."""
+    pad8 = lambda x: (x + 7) // 8 * 8  # noqa: E731
+    return {"Zr": (L.R.b, pad8(L.n)), "Acp": (L.m, pad8(L.P.b))}
+
+
+def poet_fs_form_workspace_bytes(L: poet_layer) -> int:
+    return int(lib().poet_fs_form_workspace_bytes(ctypes.byref(L)))
+
+
+def poet_fs_form(L: poet_layer, W0, primR, primP, idxR, idxP, W, Zr, Acp, ws=None, stream=None):
+    """W = R W0 P (bf16) and the FS gradient operands Zr, Acp, formed ahead of the token products."""
+    b = _layer_bytes(L)
+    sh = fs_operand_shapes(L)
+    need = poet_fs_form_workspace_bytes(L)
+    st = lib().poet_fs_form(
+        ctypes.byref(L), _ptr(W0, "W0", b["W0"], "float32"),
+        _ptr(primR, "primR", 4 * poet_prim_len(L.R), "float32"), _ptr(primP, "primP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32"), _ptr(idxP, "idxP", 4 * L.P.b, "int32"),
+        _ptr(W, "W", b["W"], "bfloat16"), _ptr(Zr, "Zr", 2 * sh["Zr"][0] * sh["Zr"][1], "bfloat16"),
+        _ptr(Acp, "Acp", 2 * sh["Acp"][0] * sh["Acp"][1], "bfloat16"), _ptr(ws, "ws", need, allow_none=need == 0),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_fs_form")
+
+
+def poet_linear_fwd_formed(L: poet_layer, W, X, Y, stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    st = lib().poet_linear_fwd_formed(ctypes.byref(L), _ptr(W, "W", b["W"], act),
+                                      _ptr(X, "X", b["X"], act, allow_none=L.T == 0),
+                                      _ptr(Y, "Y", b["Y"], act, allow_none=L.T == 0), _stream(stream))
+    _check(st, "poet_linear_fwd_formed")
+
+
+def poet_linear_bwd_formed_prims(L: poet_layer, W, Zr, Acp, idxR, idxP, X, dY, dX, dprimR, dprimP, ws=None,
+                                 stream=None):
+    b = _layer_bytes(L)
+    act = _dt_name(L.act_dtype)
+    sh = fs_operand_shapes(L)
+    need = poet_workspace_bytes(L, POET_OP_BWD)
+    st = lib().poet_linear_bwd_formed_prims(
+        ctypes.byref(L), _ptr(W, "W", b["W"], act), _ptr(Zr, "Zr", 2 * sh["Zr"][0] * sh["Zr"][1], "bfloat16"),
+        _ptr(Acp, "Acp", 2 * sh["Acp"][0] * sh["Acp"][1], "bfloat16"),
+        _ptr(idxR, "idxR", 4 * L.R.b, "int32"), _ptr(idxP, "idxP", 4 * L.P.b, "int32"),
+        _ptr(X, "X", b["X"], act, allow_none=L.T == 0), _ptr(dY, "dY", b["Y"], act, allow_none=L.T == 0),
+        _ptr(dX, "dX", b["X"], act, allow_none=True),
+        _ptr(dprimR, "dprimR", 4 * poet_prim_len(L.R), "float32"),
+        _ptr(dprimP, "dprimP", 4 * poet_prim_len(L.P), "float32"),
+        _ptr(ws, "ws", need, allow_none=True), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "poet_linear_bwd_formed_prims")
 
 
 def poet_act_path_supported(L: poet_layer) -> bool:

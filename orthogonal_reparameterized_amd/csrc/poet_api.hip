@@ -1290,13 +1290,17 @@ poet_status poet_linear_fwd(const poet_layer* L, const float* W0, const float* p
 
 namespace {
 // the weight-side backward; with dprimR/dprimP given it stops at the primitive gradients
+// ZrIn / AcpIn (both or neither): the FS gradient operands formed beforehand by poet_fs_form (with Win its W); then
+// W0 and the primitives are not read
 poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR, const float* primP,
                        const void* powersR, const void* powersP, const int32_t* idxR, const int32_t* idxP,
                        const void* Win, const void* X, const void* dY, void* dX, float* dthetaR, float* dthetaP,
-                       float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream) {
+                       float* dprimR, float* dprimP, void* ws, size_t ws_bytes, void* stream,
+                       const void* ZrIn = nullptr, const void* AcpIn = nullptr) {
   SideInfo R, P;
   if (!layer_info(L, &R, &P)) return g_last;
-  if (!W0 || !primR || !primP) return fail(POET_E_ARG, "null W0 or primitive");
+  const bool formed = ZrIn && AcpIn;
+  if (!formed && (!W0 || !primR || !primP)) return fail(POET_E_ARG, "null W0 or primitive");
   if (L->T > 0 && (!X || !dY)) return fail(POET_E_ARG, "null X or dY");
   const bool prims_only = dprimR || dprimP;
   if (prims_only) {
@@ -1318,6 +1322,11 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
   const void* W = Win;
   // both sides FS in bf16 with W given: the gradient's operands come from W0 and the sampled blocks alone
   const bool fs_pair = W && fs_bf16(*L, R) && fs_bf16(*L, P) && p.fs.Acb && p.fs.Brb;
+  if (formed && !fs_pair) return fail(POET_E_UNSUPPORTED, "formed operands need both sides POET-FS in bf16 and W");
+  if (formed) {  // the gradient's operands as formed beforehand (the same values fs_grad_operands writes)
+    p.Zr = reinterpret_cast<float*>(const_cast<void*>(ZrIn));
+    p.Acp = reinterpret_cast<float*>(const_cast<void*>(AcpIn));
+  }
   if (fast && bs_apply_eligible(R.bp, P.bp, W0, ldw, primR, primP)) {
     // bf16 operands of the gradient: Z = W0 P (R side), R W0 (P side), and W when it is not given
     void* Wout = W ? nullptr : p.W;
@@ -1334,6 +1343,8 @@ poet_status bwd_weight(const poet_layer* L, const float* W0, const float* primR,
       W = p.W;
     }
     HIP_TRY(apply_R_b(*L, R, p.W0b, W0, p.dRb, p.RW0b, BF16, Part{p.adj.part, p.adj.part_elems}, st));
+  } else if (fs_pair && formed) {
+    // nothing to form: Zr and Acp were given
   } else if (fs_pair) {
     // Z[I_R, :] and (R W0)[:, I_P], the only parts of Z = W0 P and R W0 the gradient reads
     HIP_TRY(fs_grad_operands(*L, R, P, W0, primR, primP, idxR, idxP, reinterpret_cast<__bf16*>(p.Zr),
@@ -1460,6 +1471,61 @@ poet_status poet_linear_bwd_prims(const poet_layer* L, const float* W0, const fl
   if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
   return bwd_weight(L, W0, primR, primP, nullptr, nullptr, idxR, idxP, W, X, dY, dX, nullptr, nullptr, dprimR, dprimP,
                     ws, ws_bytes, stream);
+}
+
+size_t poet_fs_form_workspace_bytes(const poet_layer* L) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return 0;
+  Arena a(nullptr);
+  FsBufs f;
+  plan_fs(a, *L, R, P, &f);
+  return a.used();
+}
+
+poet_status poet_fs_form(const poet_layer* L, const float* W0, const float* primR, const float* primP,
+                         const int32_t* idxR, const int32_t* idxP, void* W, void* Zr, void* Acp, void* ws,
+                         size_t ws_bytes, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!(fs_bf16(*L, R) && fs_bf16(*L, P)))
+    return fail(POET_E_UNSUPPORTED, "poet_fs_form needs both sides POET-FS with bf16 sides and activations");
+  if (!W0 || !primR || !primP || !W || !Zr || !Acp) return fail(POET_E_ARG, "null W0, primitive or output");
+  if (!check_idx(R, idxR, "R") || !check_idx(P, idxP, "P")) return g_last;
+  if (!check_ws(ws, ws_bytes, poet_fs_form_workspace_bytes(L))) return g_last;
+  Arena a(ws);
+  FsBufs f;
+  plan_fs(a, *L, R, P, &f);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(fs_weight_bf16(*L, R, P, W0, primR, primP, idxR, idxP, W, f, st));
+  HIP_TRY(fs_grad_operands(*L, R, P, W0, primR, primP, idxR, idxP, reinterpret_cast<__bf16*>(Zr),
+                           reinterpret_cast<__bf16*>(Acp), f, st));
+  return POET_OK;
+}
+
+poet_status poet_linear_fwd_formed(const poet_layer* L, const void* W, const void* X, void* Y, void* stream) {
+  SideInfo R, P;
+  if (!layer_info(L, &R, &P)) return g_last;
+  if (!W) return fail(POET_E_ARG, "null W");
+  if (L->T > 0 && (!X || !Y)) return fail(POET_E_ARG, "null X or Y");
+  if (L->T == 0) return POET_OK;
+  GemmDesc g;  // Y = X W^T
+  g.kclass = POET_K_TOKEN_FWD;
+  g.compute = L->act_dtype; g.M = L->T; g.N = L->m; g.K = L->n;
+  g.A = X; g.lda = L->ldx; g.a_dt = L->act_dtype; g.a_kmajor = 1;
+  g.B = W; g.ldb = L->ldw; g.b_dt = L->act_dtype; g.b_kmajor = 1;
+  g.C = Y; g.ldc = L->ldy; g.c_dt = L->act_dtype;
+  HIP_TRY(launch_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+  return POET_OK;
+}
+
+poet_status poet_linear_bwd_formed_prims(const poet_layer* L, const void* W, const void* Zr, const void* Acp,
+                                         const int32_t* idxR, const int32_t* idxP, const void* X, const void* dY,
+                                         void* dX, float* dprimR, float* dprimP, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  if (!dprimR || !dprimP) return fail(POET_E_ARG, "null dprim");
+  if (!W || !Zr || !Acp) return fail(POET_E_ARG, "null W, Zr or Acp");
+  return bwd_weight(L, nullptr, nullptr, nullptr, nullptr, nullptr, idxR, idxP, W, X, dY, dX, nullptr, nullptr, dprimR,
+                    dprimP, ws, ws_bytes, stream, Zr, Acp);
 }
 
 int poet_act_path_supported(const poet_layer* L) {

@@ -21,6 +21,16 @@ def _tdt(dt: int):
     return torch.bfloat16 if dt == B.POET_BF16 else torch.float32
 
 
+def _torch_stream(stream, dev):
+    """The torch stream object for a stream argument (None: the current stream; an int: a raw HIP stream handle)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=dev)
+    return stream
+
+
 def _merge_grade_differs(side: B.poet_side) -> bool:
     """True for sides whose chain runs as separate bf16 products: only their build differs between the step's
     precision and the merge's (poet_build_workspace_bytes(side, 1) > 0 exactly for those)."""
@@ -94,6 +104,10 @@ class PoetLinear:
         # the factors folded into the bf16 weight (W0 P, R W0), written by PoetGroup.build for large token counts;
         # None until then (and after a one-linear build, which leaves them stale)
         self.W0P = self.RW0 = None
+        # FS pairs on the weight side: (W, Zr, Acp) = R W0 P and the gradient operands (W0 P)[I_R, :], (R W0)[:, I_P]
+        # formed by PoetGroup.build (poet_fs_form); None until then (and after a one-linear build)
+        self.formed = None
+        self._form_event = None  # recorded on the formation stream after this linear's operands were formed
         # True between a build and the next merge: the primitives (and folds, operand copies) match theta and W0
         self.built = False
         if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
@@ -131,8 +145,10 @@ class PoetLinear:
         return self.powersR if side == "R" else self.powersP
 
     def build(self, stream=None, qnorm: bool = False):
+        self._await_formed(stream)  # a formation still reading the primitives
         self.opsR = self.opsP = None  # the one-side build does not write them
         self.W0P = self.RW0 = None
+        self.formed = self._form_event = None
         self.built = False
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
                                 self.ws, stream)
@@ -152,7 +168,15 @@ class PoetLinear:
         return _torch().empty((self.m, self.L.ldw), dtype=self.act, device=self.dev)
 
     def forward(self, X, Y, W_out=None, stream=None):
+        """Weight-side forward Y = X W^T. W_out (optional) receives W = R W0 P for the backward; where the last
+        PoetGroup.build formed W (``formed``), the product reads that W and the layer keeps it (W_out must be None)."""
         self._need_build("forward")
+        if self.formed is not None:
+            if W_out is not None:
+                raise ValueError("this linear keeps the W its group build formed: call forward without W_out")
+            self._await_formed(stream)
+            B.poet_linear_fwd_formed(self.L, self.formed[0], X, Y, stream)
+            return
         B.poet_linear_fwd(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, X, Y, W_out, self.ws, stream)
 
     def backward(self, X, dY, dX, W=None, stream=None):
@@ -160,6 +184,13 @@ class PoetLinear:
         B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
         self.grad_ready = True
+
+    def _await_formed(self, stream):
+        """The launch stream waits for this linear's formation, once (and for nothing else on the formation stream);
+        work on other streams is ordered after it through the launch stream, by the caller."""
+        if self._form_event is not None:
+            _torch_stream(stream, self.dev).wait_event(self._form_event)
+            self._form_event = None
 
     def forward_act(self, X, Y, Z, stream=None):
         """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
@@ -189,6 +220,11 @@ class PoetLinear:
         self._need_build("backward_prims")
         self._dprims()
         self.grad_ready = False  # dthetaR / dthetaP come from PoetGroup.finish_backward
+        if self.formed is not None:  # the operands formed by the group build (W is not used)
+            self._await_formed(stream)
+            B.poet_linear_bwd_formed_prims(self.L, *self.formed, self.idxR, self.idxP, X, dY, dX, self.dprimR,
+                                           self.dprimP, self.ws, stream)
+            return
         B.poet_linear_bwd_prims(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, W, X, dY, dX,
                                 self.dprimR, self.dprimP, self.ws, stream)
 
@@ -224,6 +260,7 @@ class PoetLinear:
         build, built again first at the merge's precision where that differs (POET_BUILD_MERGE); afterwards theta is
         zero and the next step must build again."""
         self._need_build("merge")
+        self._await_formed(stream)
         for side, th, pr, x in ((self.L.R, self.thetaR, self.primR, "R"), (self.L.P, self.thetaP, self.primP, "P")):
             if _merge_grade_differs(side):
                 B.poet_build_orthogonal(side, th, pr, self._powers(x), None, self.ws, stream, for_merge=True)
@@ -243,6 +280,7 @@ class PoetLinear:
         self.opt_steps = 0
         self.opsR = self.opsP = None
         self.W0P = self.RW0 = None
+        self.formed = self._form_event = None
 
 
 class PermutedPoetLinear:
@@ -385,9 +423,17 @@ class PoetGroup:
     merge-then-reinitialize of every linear (poet_merge_group). Results match the per-linear calls up to the
     float32 summation order of split products."""
 
-    def __init__(self, linears, ws=None):
+    def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 2, form_ws=None):
         """``ws`` (optional): a uint8 device tensor shared with other groups whose calls run one after another on one
-        stream (``PoetGroup.workspace_bytes`` gives the size this group needs)."""
+        stream (``PoetGroup.workspace_bytes`` gives the size this group needs).
+
+        ``form_fs``: the build also forms, for every weight-side linear with two bf16 POET-FS sides, W = R W0 P and
+        the FS gradient operands (poet_fs_form), which the linear's forward and backward_prims then read instead of
+        forming them there. The formations of different linears are independent: they run on up to
+        ``form_streams`` side streams (default priority) that fork from the build's stream and join it again, so
+        that their small kernels overlap; each stream has a workspace of its own (``form_ws``, optional: a list of
+        uint8 device tensors, e.g. shared with other groups whose builds run one after another, each of at least
+        ``PoetGroup.form_workspace_bytes`` bytes)."""
         torch = _torch()
         self.linears = list(linears)
         if not self.linears:
@@ -409,6 +455,26 @@ class PoetGroup:
                 fR = pl.T >= pl.n and pl.L.R.b >= 128
                 self._fold[id(pl)] = (torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fP else None,
                                       torch.empty((pl.m, pl.L.ldw), dtype=pl.act, device=dev) if fR else None)
+        # W, Zr, Acp of the FS pairs formed by the build
+        self._formed = {}
+        if form_fs:
+            for pl in self.linears:
+                if PoetGroup._formable(pl):
+                    sh = B.fs_operand_shapes(pl.L)
+                    self._formed[id(pl)] = (pl.alloc_W(), torch.empty(sh["Zr"], dtype=torch.bfloat16, device=dev),
+                                            torch.empty(sh["Acp"], dtype=torch.bfloat16, device=dev))
+        self._form_streams, self._form_ws = [], []
+        if self._formed:
+            ns = max(1, min(form_streams, len(self._formed)))
+            fneed = PoetGroup.form_workspace_bytes(self.linears)
+            if form_ws is None:
+                form_ws = [torch.empty(max(fneed, 1), dtype=torch.uint8, device=dev) for _ in range(ns)]
+            ns = min(ns, len(form_ws))
+            if ns == 0 or any(w.numel() * w.element_size() < fneed for w in form_ws[:ns]):
+                raise ValueError(f"the formations of this group need workspaces of {fneed} bytes")
+            self._form_ws = list(form_ws[:ns])
+            self._form_streams = [torch.cuda.Stream(device=dev) for _ in range(ns)]
+            self._form_events = {k: torch.cuda.Event() for k in self._formed}
         need = PoetGroup.workspace_bytes(self.linears)
         if ws is None:
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -416,6 +482,17 @@ class PoetGroup:
             if ws.numel() * ws.element_size() < need:
                 raise ValueError(f"shared workspace holds {ws.numel() * ws.element_size()} bytes, this group needs {need}")
             self.ws = ws
+
+    @staticmethod
+    def _formable(pl) -> bool:
+        L = pl.L
+        return (not pl.act_path and L.R.mode == B.POET_FS and L.P.mode == B.POET_FS and L.act_dtype == B.POET_BF16
+                and L.R.dtype == B.POET_BF16 and L.P.dtype == B.POET_BF16)
+
+    @staticmethod
+    def form_workspace_bytes(linears) -> int:
+        """Bytes of the workspace one formation stream needs for these linears (the largest poet_fs_form)."""
+        return max([B.poet_fs_form_workspace_bytes(pl.L) for pl in linears if PoetGroup._formable(pl)] or [0])
 
     @staticmethod
     def workspace_bytes(linears) -> int:
@@ -427,6 +504,8 @@ class PoetGroup:
                    B.poet_fold_group_workspace_bytes([pl.L for pl in act]) if act else 0)
 
     def build(self, stream=None):
+        for pl in self.linears:  # formations (of this group or another) still reading the primitives
+            pl._await_formed(stream)
         thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]
         prims = [t for pl in self.linears for t in (pl.primR, pl.primP)]
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
@@ -435,7 +514,10 @@ class PoetGroup:
         for pl in self.linears:
             pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
             pl.W0P = pl.RW0 = None
+            pl.formed = pl._form_event = None
             pl.built = True
+        if self._formed:
+            self._form(stream)
         act = [pl for pl in self.linears if pl.act_path and any(f is not None for f in self._fold[id(pl)])]
         if act:
             B.poet_fold_weights_group([pl.L for pl in act], [pl.W0b for pl in act], [pl.primR for pl in act],
@@ -445,6 +527,28 @@ class PoetGroup:
             for pl in act:
                 pl.W0P, pl.RW0 = self._fold[id(pl)]
 
+    def _form(self, stream):
+        """Fork the formation streams from the build's stream and form every FS pair, round robin. The launch stream
+        waits for a linear's formation in that linear's forward (or backward), so that formations of later linears
+        overlap the token products of earlier ones; finish_backward and merge join the formation streams."""
+        main = _torch_stream(stream, self.linears[0].dev)
+        pls = [pl for pl in self.linears if id(pl) in self._formed]
+        for s in self._form_streams:
+            s.wait_stream(main)
+        for i, pl in enumerate(pls):
+            j = i % len(self._form_streams)
+            W, Zr, Acp = self._formed[id(pl)]
+            B.poet_fs_form(pl.L, pl.W0, pl.primR, pl.primP, pl.idxR, pl.idxP, W, Zr, Acp, self._form_ws[j],
+                           self._form_streams[j])
+            self._form_events[id(pl)].record(self._form_streams[j])
+            pl.formed, pl._form_event = (W, Zr, Acp), self._form_events[id(pl)]
+
+    def _join_forms(self, stream):
+        if self._form_streams:
+            main = _torch_stream(stream, self.linears[0].dev)
+            for s in self._form_streams:
+                main.wait_stream(s)
+
     def finish_backward(self, stream=None):
         for pl in self.linears:
             if getattr(pl, "dprimR", None) is None:
@@ -452,6 +556,7 @@ class PoetGroup:
         dprims = [t for pl in self.linears for t in (pl.dprimR, pl.dprimP)]
         powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
         dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]
+        self._join_forms(stream)
         B.poet_adjoint_group(self.sides, dprims, powers, dthetas, self.ws, stream)
         for pl in self.linears:
             pl.grad_ready = True
@@ -478,6 +583,7 @@ class PoetGroup:
             raise ValueError("PoetGroup.merge needs one sampler seed and one epoch across its linears")
         for pl in pls:
             pl._need_build("PoetGroup.merge")
+        self._join_forms(stream)
         # the sides whose build differs at the merge's precision are built again at it first
         redo = [(s, t, p, w) for pl in pls for s, t, p, w in ((pl.L.R, pl.thetaR, pl.primR, pl._powers("R")),
                                                              (pl.L.P, pl.thetaP, pl.primP, pl._powers("P")))

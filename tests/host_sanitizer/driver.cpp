@@ -98,6 +98,16 @@ int main() {
   EXPECT(poet_linear_bwd_prims(&L, F, F, F, nullptr, nullptr, nullptr, FAKE, FAKE, FAKE, nullptr, F, FAKE, big,
                                nullptr) == POET_E_ARG);
   const poet_layer La = layers[0];
+  const poet_layer Lf = layers[3];  // both sides FS in bf16
+  int32_t* I = static_cast<int32_t*>(FAKE);
+  EXPECT(poet_fs_form_workspace_bytes(&Lf) > 0);
+  EXPECT(poet_fs_form(&La, F, F, F, nullptr, nullptr, FAKE, FAKE, FAKE, FAKE, big, nullptr) == POET_E_UNSUPPORTED);
+  EXPECT(poet_fs_form(&Lf, F, F, F, I, I, FAKE, FAKE, FAKE, FAKE, 16, nullptr) == POET_E_WORKSPACE);
+  EXPECT(poet_linear_fwd_formed(&Lf, nullptr, FAKE, FAKE, nullptr) == POET_E_ARG);
+  EXPECT(poet_linear_bwd_formed_prims(&Lf, FAKE, nullptr, FAKE, I, I, FAKE, FAKE, FAKE, F, F, FAKE, big, nullptr) ==
+         POET_E_ARG);
+  EXPECT(poet_linear_bwd_formed_prims(&La, FAKE, FAKE, FAKE, nullptr, nullptr, FAKE, FAKE, FAKE, F, F, FAKE, big,
+                                      nullptr) == POET_E_UNSUPPORTED);
   EXPECT(poet_weight_shadow(&La, nullptr, FAKE, nullptr) == POET_E_ARG);
   EXPECT(poet_linear_fwd_act(&L, FAKE, F, F, nullptr, nullptr, FAKE, FAKE, FAKE, FAKE, big, nullptr) != POET_OK);
   EXPECT(poet_linear_fwd_act(&La, FAKE, F, F, nullptr, nullptr, FAKE, FAKE, FAKE, FAKE, 16, nullptr) ==

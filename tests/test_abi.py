@@ -355,3 +355,41 @@ def test_permutation_sampler_and_gather_reject_bad_arguments_on_the_host():
     assert g(4, 4, 4, None, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_ARG
     assert g(-1, 4, 4, FAKE, 4, 4, 4, None, None, FAKE, 4, None) == B.POET_E_SHAPE
     assert g(0, 4, 4, None, 4, 4, 4, None, None, None, 4, None) == B.POET_OK  # nothing to move
+
+
+def test_fs_formed_calls_reject_bad_arguments():
+    lb = B.lib()
+    fs = B.side(1, 256, 128, 3, 1)
+    L = _layer(n=256, act_dtype=1, R=fs, P=fs)
+    Lbs = _layer(act_dtype=1, R=B.side(0, 256, 32, 3, 1), P=B.side(0, 128, 32, 3, 1))
+    wf = B.poet_fs_form_workspace_bytes(L)
+    assert wf > 0
+    assert B.poet_fs_form_workspace_bytes(_layer(m=0)) == 0
+    # poet_fs_form: both sides FS in bf16, every pointer, the index sets, the workspace
+    assert lb.poet_fs_form(ctypes.byref(Lbs), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                           None) == B.POET_E_UNSUPPORTED
+    assert lb.poet_fs_form(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, wf,
+                           None) == B.POET_E_ARG
+    assert lb.poet_fs_form(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wf,
+                           None) == B.POET_E_ARG
+    assert lb.poet_fs_form(ctypes.byref(L), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, wf,
+                           None) == B.POET_E_ARG
+    assert lb.poet_fs_form(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wf - 1,
+                           None) == B.POET_E_WORKSPACE
+    # the forward on a formed W: W, and X and Y with tokens
+    assert lb.poet_linear_fwd_formed(ctypes.byref(L), None, FAKE, FAKE, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_formed(ctypes.byref(L), FAKE, None, FAKE, None) == B.POET_E_ARG
+    assert lb.poet_linear_fwd_formed(ctypes.byref(_layer(m=0)), FAKE, FAKE, FAKE, None) == B.POET_E_SHAPE
+    # the backward on formed operands: W, Zr, Acp, dprims, index sets, workspace, and an FS pair
+    wb = B.poet_workspace_bytes(L, B.POET_OP_BWD)
+    assert lb.poet_linear_bwd_formed_prims(ctypes.byref(L), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_formed_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                           FAKE, FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_formed_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, wb, None) == B.POET_E_ARG
+    assert lb.poet_linear_bwd_formed_prims(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, 16, None) == B.POET_E_WORKSPACE
+    wbs = B.poet_workspace_bytes(Lbs, B.POET_OP_BWD)
+    assert lb.poet_linear_bwd_formed_prims(ctypes.byref(Lbs), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, wbs, None) == B.POET_E_UNSUPPORTED
