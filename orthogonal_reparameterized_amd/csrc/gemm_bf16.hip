@@ -200,6 +200,50 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char
   float* ep = reinterpret_cast<float*>(lds);
   const bool vec = ld % 4 == 0 && (reinterpret_cast<uintptr_t>(out) % (dt == BF16 ? 8 : 16)) == 0;
   const bool evec = lde % 4 == 0 && (reinterpret_cast<uintptr_t>(e) & 7) == 0;
+  // one 32-row band of the accumulators through the wave's LDS region: written in accumulator order, read back as
+  // row-contiguous float4 chunks (chunk u of the lane: row c / PR, columns 4 (c % PR) .. + 3, c = lane + 64 u)
+  auto stage = [&](int a, f32x4 (&vv)[NV]) {
+#pragma unroll
+    for (int b = 0; b < WN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * EP + b * 32 + (lane & 31)] = acc[a][b][r];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int c = lane + 64 * u;
+      vv[u] = *reinterpret_cast<const f32x4*>(ep + (c / PR) * EP + (c % PR) * 4);
+    }
+  };
+  // a whole, aligned tile without an addend (every token GEMM but the edges): straight-line code, no per-element
+  // checks (the checked version below costs a few percent of a token GEMM in instruction issue)
+  if (__builtin_expect(!e && vec && rlim >= 32 * WM && clim >= 32 * WN, 1)) {
+    if (dt == BF16) {
+#pragma unroll
+      for (int a = 0; a < WM; ++a) {
+        f32x4 vv[NV];
+        stage(a, vv);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int c = lane + 64 * u, row = a * 32 + c / PR, c4 = (c % PR) * 4;
+          bf16x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = (__bf16)vv[u][t];
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + (int64_t)row * ld + c4) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < WM; ++a) {
+        f32x4 vv[NV];
+        stage(a, vv);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int c = lane + 64 * u, row = a * 32 + c / PR, c4 = (c % PR) * 4;
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (int64_t)row * ld + c4) = vv[u];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < WM; ++a) {
     bf16x4 ex[NV];
@@ -211,16 +255,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char
         if (evec && row < rlim && c4 + 4 <= clim) ex[u] = *reinterpret_cast<const bf16x4*>(e + (int64_t)row * lde + c4);
       }
     }
-#pragma unroll
-    for (int b = 0; b < WN; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ep[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * EP + b * 32 + (lane & 31)] = acc[a][b][r];
     f32x4 vv[NV];
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int c = lane + 64 * u;
-      vv[u] = *reinterpret_cast<const f32x4*>(ep + (c / PR) * EP + (c % PR) * 4);
-    }
+    stage(a, vv);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int c = lane + 64 * u, rr = c / PR, c4 = (c % PR) * 4, row = a * 32 + rr;
