@@ -300,6 +300,39 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[WM][WN], char
   }
 }
 
+// A symmetric / skew-symmetric product (GemmDesc::tri) computes only the tiles on and above the diagonal; an
+// off-diagonal tile also goes out transposed, times the sign, into its mirror tile below the diagonal, straight from
+// the accumulators: a lane's four consecutive rows of one column are four consecutive columns of one row of the
+// mirror tile (8-byte bf16 stores, 16 contiguous bytes per row per instruction).
+template <int WM, int WN>
+__device__ __forceinline__ void store_mirror(const f32x16 (&acc)[WM][WN], char* cz, int dt, int64_t ld, int row0,
+                                             int col0, int n, float sign, int lane) {
+#pragma unroll
+  for (int a = 0; a < WM; ++a)
+#pragma unroll
+    for (int b = 0; b < WN; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int drow = col0 + b * 32 + (lane & 31), dcol = row0 + a * 32 + q * 8 + (lane >> 5) * 4;
+        if (drow >= n || dcol >= n) continue;
+        const int64_t o = (int64_t)drow * ld + dcol;
+        if (dt == BF16) {
+          __bf16* p = reinterpret_cast<__bf16*>(cz) + o;
+          if (dcol + 4 <= n && (o & 3) == 0) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(sign * acc[a][b][4 * q + e]);
+            *reinterpret_cast<bf16x4*>(p) = w;
+          } else {
+            for (int e = 0; e < 4 && dcol + e < n; ++e) p[e] = (__bf16)(sign * acc[a][b][4 * q + e]);
+          }
+        } else {
+          float* p = reinterpret_cast<float*>(cz) + o;
+          for (int e = 0; e < 4 && dcol + e < n; ++e) p[e] = sign * acc[a][b][4 * q + e];
+        }
+      }
+}
+
 // TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
 // GROUP: the launch holds several problems of one shape (FastArgs nprob and prob).
 // Waves per workgroup and their grid over the 256 x 256 tile. Eight waves (two per SIMD, wave tile 128 x 64) measured
@@ -321,7 +354,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   __shared__ __attribute__((aligned(1024))) char smem[smem_bytes(NW)];
   const GemmDesc& g = fa_.g;
   const int ntm = fa_.ntm, ntn = fa_.ntn, splits = fa_.splits;
-  const int ntiles = g.batch * splits * ntm * ntn;
+  // tiles of one (batch, split): all of them, or for a symmetric / skew-symmetric product (tri) only those on and
+  // above the diagonal, row after row (each off-diagonal one also fills its mirror tile below, store_mirror)
+  const int per_entry = g.tri ? ntm * (ntm + 1) / 2 : ntm * ntn;
+  const int ntiles = g.batch * splits * per_entry;
   const int per = (ntiles + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (t >= ntiles) return;
@@ -329,9 +365,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // then the next GM row bands. An XCD's workgroups run a contiguous range of this order together, so they share
   // the K-slices of a few A row bands and a few B column tiles in its L2 (column-fastest order over a wide N
   // would stream all of B once per row band)
-  const int zs = t / (ntn * ntm), tl = t % (ntn * ntm);
+  const int zs = t / per_entry, tl = t % per_entry;
   int tm, tn;
-  {
+  if (g.tri) {
+    tm = 0;
+    int rest = tl;
+    while (rest >= ntm - tm) rest -= ntm - tm++;
+    tn = tm + rest;
+  } else {
     constexpr int GM = 4, GN = 8;
     const int sr = tl / (GM * ntn), rem = tl % (GM * ntn);
     const int rows = min(GM, ntm - GM * sr);
@@ -503,6 +544,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const __bf16* eb = TAG == 0 && Eb ? reinterpret_cast<const __bf16*>(Eb) + (int64_t)z * g.sE + (int64_t)wrow0 * g.lde + wcol0
                                     : nullptr;
   store_tile_lds<WM, WN>(acc, smem + wave * Ep<WN>::BYTES, cb, g.c_dt, g.ldc, M - wrow0, N - wcol0, lane, eb, g.lde);
+  if constexpr (TAG == 0) {  // the token GEMMs (TAG 1-3) keep no code for it
+    if (g.tri && tm != tn)
+      store_mirror<WM, WN>(acc, Cb + (int64_t)z * g.sC * dtype_size(g.c_dt), g.c_dt, g.ldc, wrow0, wcol0, M,
+                           (float)g.tri, lane);
+  }
 }
 
 // Sum the split-K partials of every output element in split order, then apply the epilogue.
@@ -555,6 +601,7 @@ bool fast_gemm_eligible(const GemmDesc& g) {
   auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (g.compute != BF16 || g.a_dt != BF16 || g.b_dt != BF16 || g.a_sub_eye || g.b_sub_eye) return false;
   if (g.M < 128 || g.N < 128 || g.batch < 1) return false;
+  if (g.tri && (g.M != g.N || !plain_epilogue(g) || g.defer_reduce || g.kclass <= 2)) return false;
   if ((!plain_epilogue(g) || g.defer_reduce) && (!g.part || g.part_elems < (size_t)g.batch * g.M * g.N)) return false;
   if (g.lda % 8 || g.ldb % 8 || g.sA % 8 || g.sB % 8 || !al(g.A) || !al(g.B)) return false;
   // 32-bit byte offsets inside one batch's operands
@@ -568,6 +615,7 @@ int fast_gemm_splits(const GemmDesc& g) {
   // is the pipeline fill and the epilogue). S > 1 adds float32 partials, written by the items and read back by the
   // reduction: about 8 S + 4 bytes per output element, counted at one K-tile time per 10 MB. Candidates keep at
   // least two K-tiles per split and fit the scratch the caller provided; a larger S must win by 3% or more.
+  if (g.tri) return 1;  // the tiles on and above the diagonal store their mirror tiles themselves: no partials
   const int tiles = g.batch * ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int nk = (g.K + BK - 1) / BK;
   const double outs = (double)g.batch * g.M * g.N;
@@ -589,7 +637,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   fa.g = g;
   fa.ntm = (g.M + BM - 1) / BM;
   fa.ntn = (g.N + BN - 1) / BN;
-  const int tiles = g.batch * fa.ntm * fa.ntn;
+  const int tiles = g.batch * (g.tri ? fa.ntm * (fa.ntm + 1) / 2 : fa.ntm * fa.ntn);
   const int nk = (g.K + BK - 1) / BK;
   const int S = fast_gemm_splits(g);
   fa.splits = S;
@@ -628,7 +676,7 @@ bool fast_gemm_group_eligible(const GemmDesc* pr, int n) {
     if (!fast_gemm_eligible(b) || !plain_epilogue(b) || b.defer_reduce) return false;
     if (b.a_kmajor != a.a_kmajor || b.b_kmajor != a.b_kmajor || b.M != a.M || b.N != a.N || b.K != a.K ||
         b.Ktot != a.Ktot || b.sA != a.sA || b.sB != a.sB || b.ldc != a.ldc || b.sC != a.sC || b.c_dt != a.c_dt ||
-        !b.E != !a.E || b.lde != a.lde || b.sE != a.sE)
+        !b.E != !a.E || b.lde != a.lde || b.sE != a.sE || b.tri != a.tri)
       return false;
     blocks += (size_t)b.batch;
   }
@@ -660,7 +708,7 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   fa.g = g;
   fa.ntm = (g.M + BM - 1) / BM;
   fa.ntn = (g.N + BN - 1) / BN;
-  const int tiles = g.batch * fa.ntm * fa.ntn;
+  const int tiles = g.batch * (g.tri ? fa.ntm * (fa.ntm + 1) / 2 : fa.ntm * fa.ntn);
   const int nk = (g.K + BK - 1) / BK;
   const int S = fast_gemm_splits(g);
   fa.splits = S;

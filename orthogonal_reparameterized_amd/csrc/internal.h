@@ -54,6 +54,11 @@ struct GemmDesc {
   // fast path only: leave the raw split-K partials in part (split s of batch z at part + (s*batch + z)*M*N, rows of
   // N floats; only the valid extent of each batch is written) for the caller to reduce; no epilogue is applied
   int defer_reduce = 0;
+  // square batch entries (M == N): the product is known to be symmetric (tri = +1) or skew-symmetric (tri = -1),
+  // e.g. a power of a skew-symmetric matrix. The fast path computes only the 256 x 256 output tiles on and above
+  // the diagonal (no split-K) and writes each off-diagonal one a second time, transposed and times tri, below it;
+  // the generic path computes every tile.
+  int tri = 0;
 };
 
 // Fast path for bf16 x bf16 products (gemm_bf16.hip): 256x256x64 tiles, batched, split-K. Returns false (and

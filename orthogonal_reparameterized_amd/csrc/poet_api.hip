@@ -1174,6 +1174,7 @@ poet_status poet_build_orthogonal(const poet_side* s, const float* theta, float*
     if (i < S.k) { g.C = pw + (size_t)i * S.plen * esz; g.c_dt = S.dtype; g.ldc = S.ldp; g.sC = ps; }
     else { g.C = prim; g.c_dt = F32; g.ldc = S.bp; g.sC = pp; }
     g.part = part; g.part_elems = part_elems;
+    g.tri = (i + 1) % 2 == 0 ? 1 : -1;  // Q^(i+1): symmetric or skew-symmetric, as in the grouped build
     HIP_TRY(launch_gemm(g, st));
   }
   // prim = I + 2Q + 2(P_2 + ... + P_k) + P_{k+1}, the linear term exact from theta (P_2 from q2 when formed)
@@ -1947,6 +1948,9 @@ poet_status poet_build_orthogonal_group(int32_t count, const poet_side* sides, c
         if (step < c.k) { g.C = pw + (size_t)step * T.plen * esz; g.c_dt = BF16; g.ldc = T.ldp; g.sC = ps; }
         else { g.C = prim[i]; g.c_dt = F32; g.ldc = T.bp; g.sC = (int64_t)T.bp * T.bp; }
         g.part = part; g.part_elems = part_elems;
+        // Q^(step+1) of a skew-symmetric Q is symmetric (even power) or skew-symmetric (odd): the tiles on and
+        // above the diagonal, each off-diagonal one also written transposed below it
+        g.tri = (step + 1) % 2 == 0 ? 1 : -1;
       }
       if (fast_gemm_group_eligible(pr, n)) {
         HIP_TRY(launch_fast_gemm_group(pr, n, st));
