@@ -475,6 +475,14 @@ class PoetGroup:
             self._form_ws = list(form_ws[:ns])
             self._form_streams = [torch.cuda.Stream(device=dev) for _ in range(ns)]
             self._form_events = {k: torch.cuda.Event() for k in self._formed}
+            # the caching allocator reuses these buffers only after the formation streams' work that precedes
+            # their release
+            for s in self._form_streams:
+                for bufs in self._formed.values():
+                    for t in bufs:
+                        t.record_stream(s)
+                for w in self._form_ws:
+                    w.record_stream(s)
         need = PoetGroup.workspace_bytes(self.linears)
         if ws is None:
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
