@@ -503,7 +503,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                 fwd(e)
         for es, grp in zip(reversed(layers), reversed(groups)):
             if "powers" in rec:  # the saved powers were overwritten by later layers: form them again
-                grp.build()
+                grp.build(again=True)
             for e in reversed(es):
                 bwd(e)
             grp.finish_backward()

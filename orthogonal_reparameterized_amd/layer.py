@@ -511,7 +511,22 @@ class PoetGroup:
                    B.poet_merge_group_workspace_bytes([pl.L for pl in linears]),
                    B.poet_fold_group_workspace_bytes([pl.L for pl in act]) if act else 0)
 
-    def build(self, stream=None):
+    def build(self, stream=None, again: bool = False):
+        """The grouped Cayley-Neumann build of every side (and the operand copies), then the folds and the formed FS
+        operands. ``again``: the parameters have not changed since the last build (every linear is still built), and
+        the build runs only to form the saved Neumann powers once more (a stack that shares one set of power buffers
+        among its layers rebuilds each layer before its backward): the primitives come out the same, so the folds
+        and formed operands of that build stay as they are."""
+        if again:
+            if not all(pl.built for pl in self.linears):
+                raise RuntimeError("build(again=True) needs every linear built since its parameters last changed")
+            for pl in self.linears:
+                pl._await_formed(stream)
+            B.poet_build_orthogonal_group(self.sides, [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)],
+                                          [t for pl in self.linears for t in (pl.primR, pl.primP)],
+                                          [pl._powers(x) for pl in self.linears for x in ("R", "P")], self.ws, stream,
+                                          ops=[o for pl in self.linears for o in self._ops.get(id(pl), (None, None))])
+            return
         for pl in self.linears:  # formations (of this group or another) still reading the primitives
             pl._await_formed(stream)
         thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]

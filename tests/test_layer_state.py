@@ -68,3 +68,13 @@ def test_optimizer_step_needs_a_fresh_gradient():
     assert pl.opt_steps == 1 and not pl.grad_ready and not pl.built
     pl._merged()
     assert pl.opt_steps == 0 and pl.epoch == 1
+
+
+def test_build_again_needs_unchanged_parameters():
+    pl = _cpu_linear()
+    with pytest.raises(RuntimeError, match="again"):
+        PoetGroup([pl]).build(again=True)  # never built
+    pl.built = True
+    pl._stepped()  # the parameters changed: the folds and formed operands of the last build are stale
+    with pytest.raises(RuntimeError, match="again"):
+        PoetGroup([pl]).build(again=True)
