@@ -254,6 +254,9 @@ hipError_t launch_skew_project(const float* dQ, const float* G1, int mode, int d
 hipError_t launch_reduce_skew(const float* part, int nsplit, int64_t split_stride, const float* D, float beta, int mode,
                               int d, int bp, int nprim, float* dtheta, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
+// zeros the gap columns [bp, ldp) of nblk side-by-side blocks (block j at column j ldp) in each of rows rows of a
+// bf16 matrix with row pitch ld
+hipError_t launch_zero_gaps(__bf16* H, int64_t rows, int64_t ld, int ldp, int bp, int nblk, hipStream_t st);
 struct FillEntry { float* p = nullptr; size_t n = 0; };
 struct FillGroup { int n = 0; FillEntry a[2 * MAXG]; };  // n >= 1 entries filled in one launch
 hipError_t launch_fill_group(const FillGroup& g, float v, hipStream_t st);

@@ -816,6 +816,26 @@ hipError_t launch_extract_diag(const float* sup, int sb, int g, int bp, int d, i
   return hipGetLastError();
 }
 
+// zero the gap columns [bp, ldp) of the nblk side-by-side blocks (block j at column j ldp) of rows rows of a bf16
+// matrix with row pitch ld
+__global__ void k_zero_gaps(__bf16* __restrict__ H, int64_t rows, int64_t ld, int ldp, int bp, int nblk) {
+  const int gw = ldp - bp;
+  const int64_t n = rows * nblk * gw;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / (nblk * gw);
+    const int rem = (int)(e % (nblk * gw)), j = rem / gw, gcol = rem % gw;
+    H[r * ld + (int64_t)j * ldp + bp + gcol] = (__bf16)0.f;
+  }
+}
+
+hipError_t launch_zero_gaps(__bf16* H, int64_t rows, int64_t ld, int ldp, int bp, int nblk, hipStream_t st) {
+  const size_t n = (size_t)rows * nblk * (ldp - bp);
+  if (n == 0) return hipSuccess;
+  ProfScope prof(7, st, 0, (double)n * 2);
+  hipLaunchKernelGGL(k_zero_gaps, dim3(grid_for(n)), dim3(kThreads), 0, st, H, rows, ld, ldp, bp, nblk);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st) {
   if (n == 0) return hipSuccess;
   ProfScope prof(7, st, 0, (double)n * 4);

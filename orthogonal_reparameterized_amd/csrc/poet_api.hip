@@ -374,10 +374,11 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
     c.Y = reinterpret_cast<__bf16*>(H); c.ldy = ldh; c.sy = hs; c.jstep = bp; c.write_x0 = 1;
     e = launch_power_chain(c, POET_K_ADJOINT, st);
   } else {
-    if (ldp > bp) {  // zero the gap columns once (the products below write only the first bp of each block)
-      // (zero bits; ldh is even, so the bf16 block is a whole number of floats)
-      if (S.dtype == BF16) e = launch_fill(reinterpret_cast<float*>(H), (size_t)S.nprim * hs / 2, 0.f, st);
-      if (e != hipSuccess) return e;
+    if (ldp > bp && S.dtype == BF16) {  // zero the gap columns (the products below write only the first bp of each
+      // block, and the workspace holds other data between calls)
+      if ((e = launch_zero_gaps(reinterpret_cast<__bf16*>(H), (int64_t)S.nprim * bp, ldh, ldp, bp, k + 1, st)) !=
+          hipSuccess)
+        return e;
     }
     e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
     for (int j = 0; j < k && e == hipSuccess; ++j) {  // H_{j+1} = Q H_j
@@ -975,8 +976,8 @@ hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, cons
     }
     if ((e = launch_power_chain_group(g, POET_K_ADJOINT, st)) != hipSuccess) return e;
   } else {  // H_0 = bf16(dR), then one grouped product per step: H_{j+1} = Q H_j with each side's own Q
-    if (ldp > bp && (e = launch_fill(reinterpret_cast<float*>(b.H), (size_t)c.nb * hs / 2, 0.f, st)) != hipSuccess)
-      return e;  // the gap columns past bp stay zero (zero bits; hs is even)
+    if (ldp > bp && (e = launch_zero_gaps(b.H, (int64_t)c.nb * bp, ldh, ldp, bp, k + 1, st)) != hipSuccess)
+      return e;  // the gap columns past bp stay zero
     int boff = 0;
     for (int i : c.idx) {
       if ((e = launch_convert(dprim[i], bp, b.H + (size_t)boff * hs, ldh, BF16, S[i].nprim * bp, bp, st)) != hipSuccess)
