@@ -280,7 +280,8 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
     group = None if args.no_group else PoetGroup([e["pl"] for e in lins], form_fs=not args.no_form,
-                                                 form_streams=args.form_streams)
+                                                 form_streams=args.form_streams,
+                                                 side_chains=not args.no_side_chains)
     if group is not None:
         for e in lins:  # the group keeps the W it forms for FS pairs
             if id(e["pl"]) in group._formed:
@@ -354,7 +355,8 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    ("weight" if not any(e["pl"].act_path for e in lins) else "mixed"),
                    "grouped_side_steps": group is not None, "merge_period": args.merge_period,
                    "fs_formed_in_build": bool(group is not None and group._formed),
-                   "form_streams": len(group._form_streams) if group is not None else 0},
+                   "form_streams": len(group._form_streams) if group is not None else 0,
+                   "side_chain_sides": len(group._side_idx) if group is not None else 0},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
         "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
         "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
@@ -461,14 +463,19 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                        "dY": dYs[ldy]})
         layers.append(es)
         log(f"stack: layer {layer} allocated, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
-    gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]]), 1), dtype=torch.uint8,
-                      device="cuda")
+    gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]], not args.no_side_chains), 1),
+                      dtype=torch.uint8, device="cuda")
     fws = None  # the formation streams' workspaces, shared by the groups (their builds run one after another)
     if form:
         fneed = PoetGroup.form_workspace_bytes([e["pl"] for e in layers[0]])
         if fneed:
             fws = [torch.empty(fneed, dtype=torch.uint8, device="cuda") for _ in range(args.form_streams)]
-    groups = [PoetGroup([e["pl"] for e in es], ws=gws, form_fs=form, form_streams=args.form_streams, form_ws=fws)
+    side = None  # the side stream and its workspace, shared by the groups (their calls run one after another)
+    sneed = PoetGroup.side_workspace_bytes([e["pl"] for e in layers[0]])
+    if sneed and not args.no_side_chains:
+        side = (torch.cuda.Stream(), torch.empty(sneed, dtype=torch.uint8, device="cuda"))
+    groups = [PoetGroup([e["pl"] for e in es], ws=gws, form_fs=form, form_streams=args.form_streams, form_ws=fws,
+                        side_chains=not args.no_side_chains, side=side)
               for es in layers]
     for grp in groups:  # the group's operand copies, folded weights and formed FS operands
         for W, Zr, Acp in grp._formed.values():
@@ -546,7 +553,8 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    "fraction": wl.frac, "k": wl.k, "layers": nl, "linears": len(all_specs),
                    "factor_application": "activations" if act else "weight", "grouped_side_steps": True,
                    "merge_period": args.merge_period, "recompute": sorted(rec) or ["none"],
-                   "fs_formed_in_build": form and any(grp._formed for grp in groups)},
+                   "fs_formed_in_build": form and any(grp._formed for grp in groups),
+                   "side_chain_sides": sum(len(grp._side_idx) for grp in groups)},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3),
         "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
         "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -601,6 +609,10 @@ def main():
                          "streams)")
     ap.add_argument("--form-streams", type=int, default=2,
                     help="side streams the group build forms the FS pairs on")
+    ap.add_argument("--no-side-chains", action="store_true",
+                    help="build and differentiate all sides of a group in one call per step (the default runs the "
+                         "class of large primitives with the most product work, e.g. the MLP's s = 2730 POET-FS "
+                         "sides, on a side stream beside the rest)")
     ap.add_argument("--permuted", action="store_true",
                     help="permuted POET-BS: each side's blocks on a random permutation, fresh at every merge "
                          "(PermutedPoetLinear; implies --no-group and skips the extra FS block)")

@@ -108,6 +108,7 @@ class PoetLinear:
         # formed by PoetGroup.build (poet_fs_form); None until then (and after a one-linear build)
         self.formed = None
         self._form_event = None  # recorded on the formation stream after this linear's operands were formed
+        self._build_event = None  # recorded on a group's side stream after it built some of this linear's sides
         # True between a build and the next merge: the primitives (and folds, operand copies) match theta and W0
         self.built = False
         if self.act_path:  # W0 in the act dtype, the operand of the activation-side GEMMs
@@ -145,10 +146,10 @@ class PoetLinear:
         return self.powersR if side == "R" else self.powersP
 
     def build(self, stream=None, qnorm: bool = False):
-        self._await_formed(stream)  # a formation still reading the primitives
+        self._await_group(stream)  # a formation still reading the primitives, a side build still writing them
         self.opsR = self.opsP = None  # the one-side build does not write them
         self.W0P = self.RW0 = None
-        self.formed = self._form_event = None
+        self.formed = None
         self.built = False
         B.poet_build_orthogonal(self.L.R, self.thetaR, self.primR, self._powers("R"), self.qnormR if qnorm else None,
                                 self.ws, stream)
@@ -174,28 +175,33 @@ class PoetLinear:
         if self.formed is not None:
             if W_out is not None:
                 raise ValueError("this linear keeps the W its group build formed: call forward without W_out")
-            self._await_formed(stream)
+            self._await_group(stream)
             B.poet_linear_fwd_formed(self.L, self.formed[0], X, Y, stream)
             return
+        self._await_group(stream)
         B.poet_linear_fwd(self.L, self.W0, self.primR, self.primP, self.idxR, self.idxP, X, Y, W_out, self.ws, stream)
 
     def backward(self, X, dY, dX, W=None, stream=None):
         self._need_build("backward")
+        self._await_group(stream)
         B.poet_linear_bwd(self.L, self.W0, self.primR, self.primP, self._powers("R"), self._powers("P"), self.idxR,
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
         self.grad_ready = True
 
-    def _await_formed(self, stream):
-        """The launch stream waits for this linear's formation, once (and for nothing else on the formation stream);
-        work on other streams is ordered after it through the launch stream, by the caller."""
-        if self._form_event is not None:
-            _torch_stream(stream, self.dev).wait_event(self._form_event)
-            self._form_event = None
+    def _await_group(self, stream):
+        """The launch stream waits, once, for this linear's work that a PoetGroup left on its other streams: the
+        formation of its FS operands and the build of its sides that ran on the group's side stream (and for nothing
+        else on those streams); work on other streams is ordered after it through the launch stream, by the caller."""
+        for ev in (self._form_event, self._build_event):
+            if ev is not None:
+                _torch_stream(stream, self.dev).wait_event(ev)
+        self._form_event = self._build_event = None
 
     def forward_act(self, X, Y, Z, stream=None):
         """Activation-side forward: Y = ((X P^T) W0^T) R^T; Z = X P^T W0^T is kept for backward_act. The bf16
         operand copies of the primitives (and W0 P, folded) come from the last PoetGroup.build, when one made them."""
         self._need_build("forward_act")
+        self._await_group(stream)
         if self.W0P is not None:
             B.poet_linear_fwd_folded(self.L, self.W0P, self.primR, X, Y, Z, self.ws, stream, opsR=self.opsR)
         else:
@@ -204,6 +210,7 @@ class PoetLinear:
 
     def backward_act(self, X, Z, dY, dX, stream=None):
         self._need_build("backward_act")
+        self._await_group(stream)
         B.poet_linear_bwd_act(self.L, self.W0b, self.primR, self.primP, self._powers("R"), self._powers("P"), X, Z,
                               dY, dX, self.dthetaR, self.dthetaP, self.ws, stream, opsR=self.opsR, opsP=self.opsP)
         self.grad_ready = True
@@ -220,8 +227,8 @@ class PoetLinear:
         self._need_build("backward_prims")
         self._dprims()
         self.grad_ready = False  # dthetaR / dthetaP come from PoetGroup.finish_backward
+        self._await_group(stream)
         if self.formed is not None:  # the operands formed by the group build (W is not used)
-            self._await_formed(stream)
             B.poet_linear_bwd_formed_prims(self.L, *self.formed, self.idxR, self.idxP, X, dY, dX, self.dprimR,
                                            self.dprimP, self.ws, stream)
             return
@@ -234,6 +241,7 @@ class PoetLinear:
         self._need_build("backward_act_prims")
         self._dprims()
         self.grad_ready = False  # dthetaR / dthetaP come from PoetGroup.finish_backward
+        self._await_group(stream)
         if self.RW0 is not None:
             B.poet_linear_bwd_folded_prims(self.L, self.RW0, self.primP, X, Z, dY, dX, self.dprimR, self.dprimP,
                                            self.ws, stream, opsP=self.opsP)
@@ -245,6 +253,7 @@ class PoetLinear:
         """One AdamW step on thetaR, thetaP from dthetaR, dthetaP (the parameters change: the next step builds)."""
         if not self.grad_ready:
             raise RuntimeError("optimizer_step needs the gradient of the current parameters: run the backward first")
+        self._await_group(stream)
         B.poet_adamw_group([self.L.R, self.L.P], [self.thetaR, self.thetaP], [self.dthetaR, self.dthetaP],
                            [self.mR, self.mP], [self.vR, self.vP], hp, self.opt_steps + 1, stream)
         self._stepped()
@@ -260,7 +269,7 @@ class PoetLinear:
         build, built again first at the merge's precision where that differs (POET_BUILD_MERGE); afterwards theta is
         zero and the next step must build again."""
         self._need_build("merge")
-        self._await_formed(stream)
+        self._await_group(stream)
         for side, th, pr, x in ((self.L.R, self.thetaR, self.primR, "R"), (self.L.P, self.thetaP, self.primP, "P")):
             if _merge_grade_differs(side):
                 B.poet_build_orthogonal(side, th, pr, self._powers(x), None, self.ws, stream, for_merge=True)
@@ -280,7 +289,7 @@ class PoetLinear:
         self.opt_steps = 0
         self.opsR = self.opsP = None
         self.W0P = self.RW0 = None
-        self.formed = self._form_event = None
+        self.formed = self._form_event = self._build_event = None  # the merge's stream has joined that work
 
 
 class PermutedPoetLinear:
@@ -423,7 +432,8 @@ class PoetGroup:
     merge-then-reinitialize of every linear (poet_merge_group). Results match the per-linear calls up to the
     float32 summation order of split products."""
 
-    def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 2, form_ws=None):
+    def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 2, form_ws=None,
+                 side_chains: bool = True, side=None):
         """``ws`` (optional): a uint8 device tensor shared with other groups whose calls run one after another on one
         stream (``PoetGroup.workspace_bytes`` gives the size this group needs).
 
@@ -433,7 +443,16 @@ class PoetGroup:
         ``form_streams`` side streams (default priority) that fork from the build's stream and join it again, so
         that their small kernels overlap; each stream has a workspace of its own (``form_ws``, optional: a list of
         uint8 device tensors, e.g. shared with other groups whose builds run one after another, each of at least
-        ``PoetGroup.form_workspace_bytes`` bytes)."""
+        ``PoetGroup.form_workspace_bytes`` bytes).
+
+        ``side_chains``: where the sides fall in more than one class of ``_chain_class`` (e.g. the s = d/2 POET-FS
+        primitives of a transformer block: s = 1024 on the attention linears, 2730 on the MLP's wide side), the class
+        with the most product work builds, and later runs its adjoint, on a side stream (default priority) beside
+        the rest: each class alone leaves CUs idle (its products have a few hundred tiles or fewer), and the
+        linears whose sides are all in the other classes can start their forward before that class is built. Each
+        linear waits for its sides' build at its next use. ``side`` (optional): a (stream, uint8 device tensor) pair
+        shared with other groups whose calls run one after another, the tensor of at least
+        ``PoetGroup.side_workspace_bytes`` bytes. The results are those of one grouped call per step, bit for bit."""
         torch = _torch()
         self.linears = list(linears)
         if not self.linears:
@@ -483,7 +502,20 @@ class PoetGroup:
                         t.record_stream(s)
                 for w in self._form_ws:
                     w.record_stream(s)
-        need = PoetGroup.workspace_bytes(self.linears)
+        # the side class: its sides' indices in self.sides (side 2i is linear i's R, 2i + 1 its P)
+        self._side_idx = PoetGroup._side_class(self.sides) if side_chains else []
+        self._main_idx = [i for i in range(len(self.sides)) if i not in set(self._side_idx)]
+        self._side_stream = self._side_ws = self._side_event = None
+        if self._side_idx:
+            sneed = PoetGroup.side_workspace_bytes(self.linears)
+            if side is None:
+                side = (torch.cuda.Stream(device=dev), torch.empty(max(sneed, 1), dtype=torch.uint8, device=dev))
+            self._side_stream, self._side_ws = side
+            if self._side_ws.numel() * self._side_ws.element_size() < sneed:
+                raise ValueError(f"the side stream's calls of this group need a workspace of {sneed} bytes")
+            self._side_ws.record_stream(self._side_stream)
+            self._side_event = torch.cuda.Event()
+        need = PoetGroup.workspace_bytes(self.linears, side_chains)
         if ws is None:
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         else:
@@ -503,9 +535,90 @@ class PoetGroup:
         return max([B.poet_fs_form_workspace_bytes(pl.L) for pl in linears if PoetGroup._formable(pl)] or [0])
 
     @staticmethod
-    def workspace_bytes(linears) -> int:
-        """Bytes of the workspace the grouped calls of these linears need."""
+    def _chain_class(side):
+        """The class of a side whose Cayley-Neumann chain and Neumann adjoint run as products of whole bf16
+        primitives above 256 (POET-FS primitives, large POET-BS blocks): (mode, b, k); None for the other sides."""
+        if side.dtype == B.POET_BF16 and side.k > 0 and side.b > 256:
+            return (side.mode, side.b, side.k)
+        return None
+
+    @staticmethod
+    def _side_class(sides):
+        """Indices of the sides that build and run their adjoint on the side stream: the class of _chain_class with
+        the most product work (primitives x b^3 x k), when some side falls outside it; else none."""
+        classes = {}
+        for i, s in enumerate(sides):
+            classes.setdefault(PoetGroup._chain_class(s), []).append(i)
+        work = [(sum(B.poet_num_prims(sides[i]) for i in v) * c[1] ** 3 * c[2], c) for c, v in classes.items()
+                if c is not None]
+        if len(classes) < 2 or not work:
+            return []
+        return classes[max(work)[1]]
+
+    @staticmethod
+    def side_workspace_bytes(linears) -> int:
+        """Bytes of the workspace of the side stream's calls (build and adjoint of the side class); 0 without one."""
         sides = [s for pl in linears for s in (pl.L.R, pl.L.P)]
+        sub = [sides[i] for i in PoetGroup._side_class(sides)]
+        if not sub:
+            return 0
+        return max(B.poet_build_group_workspace_bytes(sub), B.poet_adjoint_group_workspace_bytes(sub))
+
+    def _of(self, i, r, p):
+        """Attribute r (side i is an R side) or p of the linear that side i belongs to."""
+        return getattr(self.linears[i // 2], r if i % 2 == 0 else p)
+
+    def _record_side(self, tensors):
+        """The caching allocator reuses these tensors' memory only after the side stream's work enqueued so far
+        (nothing to do under graph capture, whose memory outlives the graph)."""
+        torch = _torch()
+        if torch.cuda.is_current_stream_capturing():
+            return
+        for t in tensors:
+            if t is not None:
+                t.record_stream(self._side_stream)
+
+    def _build_sides(self, idx, ws, stream, for_merge=False):
+        pls = self.linears
+        if not idx:
+            return
+        B.poet_build_orthogonal_group([self.sides[i] for i in idx], [self._of(i, "thetaR", "thetaP") for i in idx],
+                                      [self._of(i, "primR", "primP") for i in idx],
+                                      [pls[i // 2]._powers("RP"[i % 2]) for i in idx], ws, stream,
+                                      ops=None if for_merge else [self._ops.get(id(pls[i // 2]), (None, None))[i % 2]
+                                                                  for i in idx], for_merge=for_merge)
+
+    def _build_all(self, stream):
+        """The grouped build of every side: one call, or the side class on the side stream (forked from the launch
+        stream) beside one call for the rest; each linear with a side in that class waits for it at its next use."""
+        if not self._side_idx:
+            self._build_sides(range(len(self.sides)), self.ws, stream)
+            return
+        main = _torch_stream(stream, self.linears[0].dev)
+        self._side_stream.wait_stream(main)
+        self._build_sides(self._side_idx, self._side_ws, self._side_stream)
+        self._side_event.record(self._side_stream)
+        self._record_side([self._of(i, a, b) for i in self._side_idx for a, b in (("thetaR", "thetaP"),
+                                                                                    ("primR", "primP"))] +
+                          [self.linears[i // 2]._powers("RP"[i % 2]) for i in self._side_idx])
+        self._build_sides(self._main_idx, self.ws, stream)
+        for i in self._side_idx:
+            self.linears[i // 2]._build_event = self._side_event
+
+    def _join_side(self, stream):
+        if self._side_stream is not None:
+            _torch_stream(stream, self.linears[0].dev).wait_stream(self._side_stream)
+            for pl in self.linears:
+                pl._build_event = None
+
+    @staticmethod
+    def workspace_bytes(linears, side_chains: bool = True) -> int:
+        """Bytes of the workspace the grouped calls of these linears need on the launch stream (with
+        ``side_chains``, the side class builds and runs its adjoint in a workspace of its own)."""
+        sides = [s for pl in linears for s in (pl.L.R, pl.L.P)]
+        if side_chains:
+            off = set(PoetGroup._side_class(sides))
+            sides = [s for i, s in enumerate(sides) if i not in off]
         act = [pl for pl in linears if pl.act_path]
         return max(B.poet_build_group_workspace_bytes(sides), B.poet_adjoint_group_workspace_bytes(sides),
                    B.poet_merge_group_workspace_bytes([pl.L for pl in linears]),
@@ -521,19 +634,12 @@ class PoetGroup:
             if not all(pl.built for pl in self.linears):
                 raise RuntimeError("build(again=True) needs every linear built since its parameters last changed")
             for pl in self.linears:
-                pl._await_formed(stream)
-            B.poet_build_orthogonal_group(self.sides, [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)],
-                                          [t for pl in self.linears for t in (pl.primR, pl.primP)],
-                                          [pl._powers(x) for pl in self.linears for x in ("R", "P")], self.ws, stream,
-                                          ops=[o for pl in self.linears for o in self._ops.get(id(pl), (None, None))])
+                pl._await_group(stream)
+            self._build_all(stream)
             return
         for pl in self.linears:  # formations (of this group or another) still reading the primitives
-            pl._await_formed(stream)
-        thetas = [t for pl in self.linears for t in (pl.thetaR, pl.thetaP)]
-        prims = [t for pl in self.linears for t in (pl.primR, pl.primP)]
-        powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
-        ops = [o for pl in self.linears for o in self._ops.get(id(pl), (None, None))]
-        B.poet_build_orthogonal_group(self.sides, thetas, prims, powers, self.ws, stream, ops=ops)
+            pl._await_group(stream)
+        self._build_all(stream)
         for pl in self.linears:
             pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
             pl.W0P = pl.RW0 = None
@@ -542,6 +648,8 @@ class PoetGroup:
         if self._formed:
             self._form(stream)
         act = [pl for pl in self.linears if pl.act_path and any(f is not None for f in self._fold[id(pl)])]
+        for pl in act:  # the folds read the primitives
+            pl._await_group(stream)
         if act:
             B.poet_fold_weights_group([pl.L for pl in act], [pl.W0b for pl in act], [pl.primR for pl in act],
                                       [pl.primP for pl in act], [self._fold[id(pl)][0] for pl in act],
@@ -560,6 +668,9 @@ class PoetGroup:
             s.wait_stream(main)
         for i, pl in enumerate(pls):
             j = i % len(self._form_streams)
+            if pl._build_event is not None:  # a side built on the side stream (the formation's event covers it)
+                self._form_streams[j].wait_event(pl._build_event)
+                pl._build_event = None
             W, Zr, Acp = self._formed[id(pl)]
             B.poet_fs_form(pl.L, pl.W0, pl.primR, pl.primP, pl.idxR, pl.idxP, W, Zr, Acp, self._form_ws[j],
                            self._form_streams[j])
@@ -576,11 +687,22 @@ class PoetGroup:
         for pl in self.linears:
             if getattr(pl, "dprimR", None) is None:
                 raise RuntimeError("finish_backward needs backward_prims or backward_act_prims on every linear first")
-        dprims = [t for pl in self.linears for t in (pl.dprimR, pl.dprimP)]
-        powers = [pl._powers(x) for pl in self.linears for x in ("R", "P")]
-        dthetas = [t for pl in self.linears for t in (pl.dthetaR, pl.dthetaP)]
         self._join_forms(stream)
-        B.poet_adjoint_group(self.sides, dprims, powers, dthetas, self.ws, stream)
+
+        def adjoint(idx, ws, st):
+            B.poet_adjoint_group([self.sides[i] for i in idx], [self._of(i, "dprimR", "dprimP") for i in idx],
+                                 [self.linears[i // 2]._powers("RP"[i % 2]) for i in idx],
+                                 [self._of(i, "dthetaR", "dthetaP") for i in idx], ws, st)
+        if self._side_idx:  # the side class on the side stream, forked after the last backward, then joined
+            self._side_stream.wait_stream(_torch_stream(stream, self.linears[0].dev))
+            adjoint(self._side_idx, self._side_ws, self._side_stream)
+            self._record_side([self._of(i, a, b) for i in self._side_idx for a, b in (("dprimR", "dprimP"),
+                                                                                        ("dthetaR", "dthetaP"))] +
+                              [self.linears[i // 2]._powers("RP"[i % 2]) for i in self._side_idx])
+            adjoint(self._main_idx, self.ws, stream)
+            self._join_side(stream)
+        else:
+            adjoint(range(len(self.sides)), self.ws, stream)
         for pl in self.linears:
             pl.grad_ready = True
 
@@ -607,13 +729,16 @@ class PoetGroup:
         for pl in pls:
             pl._need_build("PoetGroup.merge")
         self._join_forms(stream)
-        # the sides whose build differs at the merge's precision are built again at it first
-        redo = [(s, t, p, w) for pl in pls for s, t, p, w in ((pl.L.R, pl.thetaR, pl.primR, pl._powers("R")),
-                                                             (pl.L.P, pl.thetaP, pl.primP, pl._powers("P")))
-                if _merge_grade_differs(s)]
-        if redo:
-            B.poet_build_orthogonal_group([r[0] for r in redo], [r[1] for r in redo], [r[2] for r in redo],
-                                          [r[3] for r in redo], self.ws, stream, for_merge=True)
+        self._join_side(stream)
+        # the sides whose build differs at the merge's precision are built again at it first (the side class on the
+        # side stream, joined before the merge)
+        redo = [i for i in range(len(self.sides)) if _merge_grade_differs(self.sides[i])]
+        side = set(self._side_idx)
+        if any(i in side for i in redo):
+            self._side_stream.wait_stream(_torch_stream(stream, self.linears[0].dev))
+            self._build_sides([i for i in redo if i in side], self._side_ws, self._side_stream, for_merge=True)
+        self._build_sides([i for i in redo if i not in side], self.ws, stream, for_merge=True)
+        self._join_side(stream)
         B.poet_merge_group([pl.L for pl in pls], [pl.W0 for pl in pls], [pl.W0b for pl in pls],
                            [pl.thetaR for pl in pls], [pl.thetaP for pl in pls], [pl.primR for pl in pls],
                            [pl.primP for pl in pls], [pl.idxR for pl in pls], [pl.idxP for pl in pls], pls[0].seed,

@@ -11,7 +11,11 @@ run the same kernels on the same values as the forward and backward that form th
 - Y and dtheta also meet the bf16 bar against the oracle;
 - the formed operands are dropped by a one-linear build and by a merge, and a forward that asks for W_out is refused;
 - a formed grouped step captured into a HIP graph (the fork to the side streams and the join captured with it)
-  replays bit for bit like the eager step, three times, with eager work in between.
+  replays bit for bit like the eager step, three times, with eager work in between;
+- with the sides in three classes (s = 520 and s = 300 built as products, the rest on the fused chain), the group
+  builds and differentiates the s = 520 class on its side stream beside the rest: Y, dX and dtheta equal those of
+  the group that makes one call per step (side_chains=False), bit for bit, formed and inline; so do the merged W0
+  and the resampled index sets of a merge, whose build at the merge's precision also splits.
 """
 import pytest
 
@@ -178,3 +182,46 @@ def test_formed_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(eager, outs())):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step (output {i})"
+
+
+def test_side_chains_match_one_call():
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("FS side-class stream vs one grouped call")
+    blk = _block(96)
+    lins = [e["pl"] for e in blk]
+    one = PoetGroup(lins, side_chains=False)
+    assert not one._side_idx
+    _step(one, blk, False)
+    torch.cuda.synchronize()
+    want = _outs(blk)
+    names = ("Y", "dX", "dprimR", "dprimP", "dthetaR", "dthetaP")
+    for form in (False, True):
+        g = PoetGroup(lins, form_fs=form)
+        assert g._side_idx == [1, 2]  # fs0's P and fs1's R: s = 520
+        for e in blk:
+            for t in (e["Y"], e["dX"], e["pl"].dthetaR, e["pl"].dthetaP):
+                t.fill_(float("nan"))
+        _step(g, blk, form)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(want, _outs(blk))):
+            e = blk[i // len(names)]
+            assert torch.equal(a, b), f"form={form} {e['lin'].name}: {names[i % len(names)]} differs from one call"
+
+
+def test_side_chains_merge_matches_one_call():
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("FS side-class stream: merge vs one grouped call")
+    out = []
+    for side_chains in (False, True):
+        blk = _block(97)  # the same linears twice
+        lins = [e["pl"] for e in blk]
+        g = PoetGroup(lins, side_chains=side_chains)
+        assert bool(g._side_idx) == side_chains
+        g.build()
+        g.merge()
+        torch.cuda.synchronize()
+        out.append([t.clone() for pl in lins for t in (pl.W0, pl.idxR, pl.idxP, pl.thetaR, pl.thetaP)
+                    if t is not None])
+    assert len(out[0]) == len(out[1])
+    for i, (a, b) in enumerate(zip(*out)):
+        assert torch.equal(a, b), f"merged state {i} differs from one call"

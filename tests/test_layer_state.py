@@ -78,3 +78,24 @@ def test_build_again_needs_unchanged_parameters():
     pl._stepped()  # the parameters changed: the folds and formed operands of the last build are stale
     with pytest.raises(RuntimeError, match="again"):
         PoetGroup([pl]).build(again=True)
+
+
+def test_side_class_is_the_gemm_chain_class_with_the_most_work():
+    """PoetGroup's side stream takes the sides of one class of bf16 primitives above 256 (equal mode, size and k),
+    the one with the most product work, and only when other sides remain for the launch stream."""
+    def fs(d, k=5, dt=B.POET_BF16):
+        return B.side(B.POET_FS, d, d // 2, k, dt)
+    # a LLaMA-1.3B block with s = d/2: q, k, v, o (2048 x 2048), gate and up (5461 x 2048), down (2048 x 5461)
+    block = [fs(2048), fs(2048)] * 4 + [fs(5461), fs(2048), fs(5461), fs(2048), fs(2048), fs(5461)]
+    assert PoetGroup._side_class(block) == [8, 10, 13]
+    assert PoetGroup._side_class([B.side(B.POET_BS, 2048, 256, 5, B.POET_BF16)] * 14) == []  # fused chains only
+    assert PoetGroup._side_class([fs(5461)] * 3) == []  # a single class
+    assert PoetGroup._side_class([B.side(B.POET_BS, 2048, 256, 5, B.POET_BF16), fs(2048)]) == [1]
+    # float32 sides and k = 0 sides do not run as bf16 products
+    assert PoetGroup._side_class([fs(2048, dt=B.POET_F32), fs(2048)]) == [1]
+    assert PoetGroup._side_class([fs(2048, k=0), fs(2048)]) == [1]
+    # more work wins: one 1536-primitive (1536^3 x 5) against three of 1024 (3 x 1024^3 x 5), not against four
+    assert PoetGroup._side_class([fs(2048)] * 3 + [fs(3072)]) == [3]
+    assert PoetGroup._side_class([fs(2048)] * 4 + [fs(3072)]) == [0, 1, 2, 3]
+    # a large POET-BS block size is a class of its own
+    assert PoetGroup._side_class([B.side(B.POET_BS, 1024, 512, 3, B.POET_BF16)] * 2 + [fs(2048, k=3)]) == [2]
