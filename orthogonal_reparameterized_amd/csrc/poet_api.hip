@@ -352,6 +352,26 @@ struct AdjBufs {
 size_t adj_h_elems(const SideInfo& S) { return (size_t)S.nprim * S.bp * S.ldp * (S.k + 1); }
 size_t adj_c_elems(const SideInfo& S) { return (size_t)S.nprim * S.ldp * S.ldp * (S.k + 1); }
 
+hipError_t launch_grouped(const std::vector<GemmDesc>& all, hipStream_t st);
+
+// H_j = Q^j H_0 (j = 1..k) of the nprim blocks of one side, from its saved powers Q^1 = Q .. Q^k (power t - 1 at
+// element (t - 1) plen, block stride bp ldp): k products that do not depend on one another, so they share grouped
+// launches instead of running as a chain of k launches. H rows have pitch ldh = (k+1) ldp, H_j at column j ldp.
+void h_products(const SideInfo& S, const void* powers, char* H, std::vector<GemmDesc>* out) {
+  const int bp = S.bp, k = S.k, ldp = S.ldp, ldh = (k + 1) * ldp;
+  const size_t esz = dtype_size(S.dtype);
+  for (int j = 1; j <= k; ++j) {
+    GemmDesc g;
+    g.kclass = POET_K_ADJOINT;
+    g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
+    g.A = reinterpret_cast<const char*>(powers) + (size_t)(j - 1) * S.plen * esz; g.lda = ldp;
+    g.sA = (int64_t)bp * ldp; g.a_dt = S.dtype; g.a_kmajor = 1;
+    g.B = H; g.ldb = ldh; g.sB = (int64_t)bp * ldh; g.b_dt = S.dtype; g.b_kmajor = 0;
+    g.C = H + (size_t)j * ldp * esz; g.ldc = ldh; g.sC = (int64_t)bp * ldh; g.c_dt = S.dtype;
+    out->push_back(g);  // no split-K scratch: the launch holds k times the tiles of one product
+  }
+}
+
 // H_j sits at column j ldp of the H rows (16-byte aligned operands for the bf16 kernel); with ldp > bp the gap
 // columns are zeroed, and the matching rows of the coefficient stack are zero, so the phase-2 product can run
 // over K = (k+1) ldp.
@@ -361,8 +381,7 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
   const int64_t pp = (int64_t)S.bp * S.bp;
   if (S.k == 0) return launch_skew_project(dRg, nullptr, S.mode, S.d, S.bp, S.nprim, dtheta, st);
   const int bp = S.bp, k = S.k, ldp = S.ldp, ldh = (k + 1) * ldp;
-  const int64_t hs = (int64_t)bp * ldh, ps = (int64_t)bp * ldp;
-  const size_t esz = dtype_size(S.dtype);
+  const int64_t hs = (int64_t)bp * ldh;
   char* H = reinterpret_cast<char*>(b.H);
   hipError_t e = hipSuccess;
   const bool chain = ldp == bp && power_chain_eligible(bp, S.dtype, powers);
@@ -381,15 +400,10 @@ hipError_t neumann_adjoint(const SideInfo& S, const float* dRg, const void* powe
         return e;
     }
     e = launch_convert(dRg, bp, H, ldh, S.dtype, S.nprim * bp, bp, st);  // H_0 = dR
-    for (int j = 0; j < k && e == hipSuccess; ++j) {  // H_{j+1} = Q H_j
-      GemmDesc g;
-      g.kclass = POET_K_ADJOINT;
-      g.compute = S.dtype; g.M = g.N = g.K = bp; g.batch = S.nprim;
-      g.A = powers; g.lda = ldp; g.sA = ps; g.a_dt = S.dtype; g.a_kmajor = 1;
-      g.B = H + (size_t)j * ldp * esz; g.ldb = ldh; g.sB = hs; g.b_dt = S.dtype; g.b_kmajor = 0;
-      g.C = H + (size_t)(j + 1) * ldp * esz; g.ldc = ldh; g.sC = hs; g.c_dt = S.dtype;
-      g.part = b.part; g.part_elems = b.part_elems;  // split K when the grid is small
-      e = launch_gemm(g, st);
+    if (e == hipSuccess) {  // H_j = Q^j H_0 from the saved powers
+      std::vector<GemmDesc> pr;
+      h_products(S, powers, H, &pr);
+      e = launch_grouped(pr, st);
     }
   }
   if (e != hipSuccess) return e;
@@ -961,7 +975,7 @@ size_t adjoint_group_bytes(const std::vector<SideInfo>& S, const void* const* po
 hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, const float* const* dprim,
                          const void* const* powers, float* const* dtheta, const AdjChunkBufs& b, hipStream_t st) {
   const int bp = c.bp, k = c.k, ldp = c.ldp, ldh = (k + 1) * ldp;
-  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh, ps = (int64_t)bp * ldp;
+  const int64_t pp = (int64_t)bp * bp, hs = (int64_t)bp * ldh;
   hipError_t e;
   if (c.fused) {  // H_0 = dR and H_{j+1} = Q H_j for every block of the chunk in one launch
     ChainGroup g;
@@ -975,37 +989,19 @@ hipError_t adjoint_chunk(const AdjChunk& c, const std::vector<SideInfo>& S, cons
       boff += S[i].nprim;
     }
     if ((e = launch_power_chain_group(g, POET_K_ADJOINT, st)) != hipSuccess) return e;
-  } else {  // H_0 = bf16(dR), then one grouped product per step: H_{j+1} = Q H_j with each side's own Q
+  } else {  // H_0 = bf16(dR), then H_j = Q^j H_0 from each side's saved powers, k products per side in grouped
+    // launches
     if (ldp > bp && (e = launch_zero_gaps(b.H, (int64_t)c.nb * bp, ldh, ldp, bp, k + 1, st)) != hipSuccess)
       return e;  // the gap columns past bp stay zero
     int boff = 0;
+    std::vector<GemmDesc> pr;
     for (int i : c.idx) {
-      if ((e = launch_convert(dprim[i], bp, b.H + (size_t)boff * hs, ldh, BF16, S[i].nprim * bp, bp, st)) != hipSuccess)
-        return e;
+      __bf16* Hi = b.H + (size_t)boff * hs;
+      if ((e = launch_convert(dprim[i], bp, Hi, ldh, BF16, S[i].nprim * bp, bp, st)) != hipSuccess) return e;
+      h_products(S[i], powers[i], reinterpret_cast<char*>(Hi), &pr);
       boff += S[i].nprim;
     }
-    const int n = (int)c.idx.size();
-    for (int j = 0; j < k; ++j) {
-      GemmDesc pr[MAXG];
-      boff = 0;
-      for (int u = 0; u < n; ++u) {
-        const int i = c.idx[u];
-        GemmDesc& g = pr[u];
-        g.kclass = POET_K_ADJOINT;
-        g.compute = BF16; g.M = g.N = g.K = bp; g.batch = S[i].nprim;
-        g.A = powers[i]; g.lda = ldp; g.sA = ps; g.a_dt = BF16; g.a_kmajor = 1;
-        g.B = b.H + (size_t)boff * hs + (size_t)j * ldp; g.ldb = ldh; g.sB = hs; g.b_dt = BF16; g.b_kmajor = 0;
-        g.C = b.H + (size_t)boff * hs + (size_t)(j + 1) * ldp; g.ldc = ldh; g.sC = hs; g.c_dt = BF16;
-        g.part = b.part; g.part_elems = b.part_elems;
-        boff += S[i].nprim;
-      }
-      if (fast_gemm_group_eligible(pr, n)) {
-        if ((e = launch_fast_gemm_group(pr, n, st)) != hipSuccess) return e;
-      } else {
-        for (int u = 0; u < n; ++u)
-          if ((e = launch_gemm(pr[u], st)) != hipSuccess) return e;
-      }
-    }
+    if ((e = launch_grouped(pr, st)) != hipSuccess) return e;
   }
   {  // the coefficient stacks C_0..C_k from the saved powers
     CoefGroup g;
