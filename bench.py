@@ -61,8 +61,10 @@ def optimizer():
     return B.adamw(**OPTIMIZER)
 
 
-def step(lins, group=None, hp=None):
-    """One training step of the block: build R and P, forward, backward to the skew parameters, AdamW update."""
+def step(lins, group=None, hp=None, pipeline=True):
+    """One training step of the block: build R and P, forward, backward to the skew parameters, AdamW update.
+    ``pipeline``: a group with a side class leaves that class's adjoint and update on its side stream, where they
+    overlap the next step's build and the linears that do not need them (off for graph capture)."""
     hp = optimizer() if hp is None else hp
     if group is not None:  # the block's per-side steps in shared launches: build, then per linear, then adjoint
         group.build()
@@ -74,7 +76,7 @@ def step(lins, group=None, hp=None):
             else:
                 pl.forward(e["X"], e["Y"], W_out=e["keep"])
                 pl.backward_prims(e["X"], e["dY"], e["dX"], W=e["keep"])
-        group.finish_backward()
+        group.finish_backward(join=not pipeline)
         group.optimizer_step(hp)
         return
     for e in lins:
@@ -185,15 +187,18 @@ def _profile(B, fn, steps):
     return prof
 
 
-def _timed(fn, steps, torch):
+def _timed(fn, steps, torch, join=None):
     """K calls of fn with nothing else on the stream, bracketed by synchronization; per-step event pairs on the
-    current stream (the library launches on it) give the median and the minimum next to the mean."""
+    current stream (the library launches on it) give the median and the minimum next to the mean. ``join`` makes
+    the current stream wait for work the last step left on other streams, before the closing event."""
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(steps):
         fn()
+        if join is not None and i == steps - 1:
+            join()
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -286,10 +291,11 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
         for e in lins:  # the group keeps the W it forms for FS pairs
             if id(e["pl"]) in group._formed:
                 e["keep"] = None
+    pipe = not args.no_pipeline
     torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        step(lins, group)
+        step(lins, group, pipeline=pipe)
     torch.cuda.synchronize()
 
     # one step captured into a HIP graph (torch's CUDAGraph over the HIP stream the library launches on): replays
@@ -300,24 +306,25 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
         s_cap = torch.cuda.Stream()
         s_cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s_cap):
-            step(lins, group)  # a step on the capture stream first (the library's first launch on a stream)
+            step(lins, group, pipeline=False)  # a step on the capture stream first (the library's first launch on
+            # a stream)
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(lins, group)
+            step(lins, group, pipeline=False)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
 
     log(f"timed {args.steps} steps")
-    ms_step, per, wall = _timed((lambda: graph.replay()) if graph is not None else (lambda: step(lins, group)),
-                                args.steps, torch)
+    run = (lambda: graph.replay()) if graph is not None else (lambda: step(lins, group, pipeline=pipe))
+    ms_step, per, wall = _timed(run, args.steps, torch, join=group.join if group is not None else None)
     # the same K steps again with the library's launch profiler on (an event pair around every launch, on the
     # launch stream): per-class kernel times and the dominant kernel's launch duration. The events add gaps
     # between launches, not kernel time, so this pass is kept out of the timed region above.
     log(f"profiled {args.steps} steps")
-    prof = _profile(B, lambda: step(lins, group), args.steps)
+    prof = _profile(B, lambda: step(lins, group, pipeline=pipe), args.steps)
 
     log("merge")
     # algorithmic HBM bytes: every element of W0 read and written once in float32, plus the bf16 copy of W0 the
@@ -356,7 +363,8 @@ def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    "grouped_side_steps": group is not None, "merge_period": args.merge_period,
                    "fs_formed_in_build": bool(group is not None and group._formed),
                    "form_streams": len(group._form_streams) if group is not None else 0,
-                   "side_chain_sides": len(group._side_idx) if group is not None else 0},
+                   "side_chain_sides": len(group._side_idx) if group is not None else 0,
+                   "side_class_pipelined": bool(group is not None and group._side_idx and pipe and not args.graph)},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3), "graph_replay": graph is not None,
         "kernel_ms_per_step": round(sum(v["ms"] for v in prof.values()) / args.steps, 4),
         "token_gemm_tflops": round(gemm_fl / (gemm_ms / 1e3) / 1e12, 1) if gemm_ms else None,
@@ -513,7 +521,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                 grp.build(again=True)
             for e in reversed(es):
                 bwd(e)
-            grp.finish_backward()
+            grp.finish_backward(join=args.no_pipeline)
             grp.optimizer_step(hp)
 
     log(f"stack warmup {args.warmup}")
@@ -521,7 +529,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
         stack_step()
     torch.cuda.synchronize()
     log(f"stack timed {args.steps} steps")
-    ms_step, per, wall = _timed(stack_step, args.steps, torch)
+    ms_step, per, wall = _timed(stack_step, args.steps, torch, join=lambda: [grp.join() for grp in groups])
     log("stack profiled step")
     prof = _profile(B, stack_step, 1)
     log("stack merge")
@@ -554,7 +562,8 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                    "factor_application": "activations" if act else "weight", "grouped_side_steps": True,
                    "merge_period": args.merge_period, "recompute": sorted(rec) or ["none"],
                    "fs_formed_in_build": form and any(grp._formed for grp in groups),
-                   "side_chain_sides": sum(len(grp._side_idx) for grp in groups)},
+                   "side_chain_sides": sum(len(grp._side_idx) for grp in groups),
+                   "side_class_pipelined": not args.no_pipeline and any(grp._side_idx for grp in groups)},
         "roofline": roof, "merge": merge_info, "host_wall_s": round(wall, 3),
         "algorithmic_tflop_per_step": {k: round(v / 1e12, 4) for k, v in fl.items()},
         "step_mfu": round(fl["min"] / (ms_total / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -609,6 +618,9 @@ def main():
                          "streams)")
     ap.add_argument("--form-streams", type=int, default=2,
                     help="side streams the group build forms the FS pairs on")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="join the side class's adjoint at the end of the backward (the default leaves it and the "
+                         "class's AdamW update running on the side stream into the next step)")
     ap.add_argument("--no-side-chains", action="store_true",
                     help="build and differentiate all sides of a group in one call per step (the default runs the "
                          "class of large primitives with the most product work, e.g. the MLP's s = 2730 POET-FS "

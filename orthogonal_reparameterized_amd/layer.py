@@ -188,6 +188,13 @@ class PoetLinear:
                           self.idxP, W, X, dY, dX, self.dthetaR, self.dthetaP, self.ws, stream)
         self.grad_ready = True
 
+    def _await_form(self, stream):
+        """The launch stream waits, once, for this linear's formation only (a group build: its side stream orders
+        itself after the work it left there)."""
+        if self._form_event is not None:
+            _torch_stream(stream, self.dev).wait_event(self._form_event)
+            self._form_event = None
+
     def _await_group(self, stream):
         """The launch stream waits, once, for this linear's work that a PoetGroup left on its other streams: the
         formation of its FS operands and the build of its sides that ran on the group's side stream (and for nothing
@@ -506,6 +513,7 @@ class PoetGroup:
         self._side_idx = PoetGroup._side_class(self.sides) if side_chains else []
         self._main_idx = [i for i in range(len(self.sides)) if i not in set(self._side_idx)]
         self._side_stream = self._side_ws = self._side_event = None
+        self._side_open = False  # a finish_backward(join=False) left the side class's gradient on the side stream
         if self._side_idx:
             sneed = PoetGroup.side_workspace_bytes(self.linears)
             if side is None:
@@ -605,11 +613,18 @@ class PoetGroup:
         for i in self._side_idx:
             self.linears[i // 2]._build_event = self._side_event
 
+    def join(self, stream=None):
+        """The launch stream waits for all work this group left on its other streams (formations, the side class's
+        build, an open finish_backward and the update after it)."""
+        self._join_forms(stream)
+        self._join_side(stream)
+
     def _join_side(self, stream):
         if self._side_stream is not None:
             _torch_stream(stream, self.linears[0].dev).wait_stream(self._side_stream)
             for pl in self.linears:
                 pl._build_event = None
+        self._side_open = False
 
     @staticmethod
     def workspace_bytes(linears, side_chains: bool = True) -> int:
@@ -634,11 +649,13 @@ class PoetGroup:
             if not all(pl.built for pl in self.linears):
                 raise RuntimeError("build(again=True) needs every linear built since its parameters last changed")
             for pl in self.linears:
-                pl._await_group(stream)
+                pl._await_form(stream)
             self._build_all(stream)
             return
-        for pl in self.linears:  # formations (of this group or another) still reading the primitives
-            pl._await_group(stream)
+        # formations (of this group or another) still reading the primitives; work this group left on its side
+        # stream (an open finish_backward, the optimizer step after it) precedes the side class's build there
+        for pl in self.linears:
+            pl._await_form(stream)
         self._build_all(stream)
         for pl in self.linears:
             pl.opsR, pl.opsP = self._ops.get(id(pl), (None, None))
@@ -683,7 +700,16 @@ class PoetGroup:
             for s in self._form_streams:
                 main.wait_stream(s)
 
-    def finish_backward(self, stream=None):
+    def finish_backward(self, stream=None, join: bool = True):
+        """The Neumann adjoint and skew projection of every side (dthetaR, dthetaP from dprimR, dprimP).
+
+        ``join=False`` (groups with a side class): the side class's adjoint is left running on the side stream, and
+        ``optimizer_step`` updates that class there too, so both overlap the launch stream's next work (the next
+        layer's backward, the next step's build of the other classes and the linears that need only those). Each
+        linear with a side in that class waits for it at its next use (its next group build orders the side
+        class's build after it on the side stream); ``merge`` joins it. Until then the side class's dtheta, theta
+        and moments are not ready on the launch stream: synchronize (or join) before reading them, keep the call
+        out of graph capture, and let groups that share parameter or power buffers share one side stream."""
         for pl in self.linears:
             if getattr(pl, "dprimR", None) is None:
                 raise RuntimeError("finish_backward needs backward_prims or backward_act_prims on every linear first")
@@ -700,11 +726,21 @@ class PoetGroup:
                                                                                         ("dthetaR", "dthetaP"))] +
                               [self.linears[i // 2]._powers("RP"[i % 2]) for i in self._side_idx])
             adjoint(self._main_idx, self.ws, stream)
-            self._join_side(stream)
+            if join:
+                self._join_side(stream)
+            else:
+                self._side_open = True
+                self._mark_side()
         else:
             adjoint(range(len(self.sides)), self.ws, stream)
         for pl in self.linears:
             pl.grad_ready = True
+
+    def _mark_side(self):
+        """Each linear with a side in the side class waits, at its next use, for the side stream's work so far."""
+        self._side_event.record(self._side_stream)
+        for i in self._side_idx:
+            self.linears[i // 2]._build_event = self._side_event
 
     def optimizer_step(self, hp: B.poet_adamw, stream=None):
         """One AdamW step on the skew parameters of every linear in shared launches (their step counts must agree)."""
@@ -714,9 +750,18 @@ class PoetGroup:
         for pl in pls:
             if not pl.grad_ready:
                 raise RuntimeError("optimizer_step needs the gradient of the current parameters: run the backward first")
-        B.poet_adamw_group(self.sides, [t for pl in pls for t in (pl.thetaR, pl.thetaP)],
-                           [t for pl in pls for t in (pl.dthetaR, pl.dthetaP)], [t for pl in pls for t in (pl.mR, pl.mP)],
-                           [t for pl in pls for t in (pl.vR, pl.vP)], hp, pls[0].opt_steps + 1, stream)
+        def adamw(idx, st):
+            B.poet_adamw_group([self.sides[i] for i in idx], [self._of(i, "thetaR", "thetaP") for i in idx],
+                               [self._of(i, "dthetaR", "dthetaP") for i in idx], [self._of(i, "mR", "mP") for i in idx],
+                               [self._of(i, "vR", "vP") for i in idx], hp, pls[0].opt_steps + 1, st)
+        if self._side_open:  # the side class's gradient is still on the side stream: update it there
+            adamw(self._side_idx, self._side_stream)
+            self._record_side([self._of(i, a, b) for i in self._side_idx
+                               for a, b in (("thetaR", "thetaP"), ("mR", "mP"), ("vR", "vP"))])
+            self._mark_side()
+            adamw(self._main_idx, stream)
+        else:
+            adamw(range(len(self.sides)), stream)
         for pl in pls:
             pl._stepped()
 

@@ -15,7 +15,10 @@ run the same kernels on the same values as the forward and backward that form th
 - with the sides in three classes (s = 520 and s = 300 built as products, the rest on the fused chain), the group
   builds and differentiates the s = 520 class on its side stream beside the rest: Y, dX and dtheta equal those of
   the group that makes one call per step (side_chains=False), bit for bit, formed and inline; so do the merged W0
-  and the resampled index sets of a merge, whose build at the merge's precision also splits.
+  and the resampled index sets of a merge, whose build at the merge's precision also splits;
+- three training steps with finish_backward(join=False), which leaves the side class's adjoint and AdamW update on
+  the side stream into the next step's build, end with the same theta, moments, Y and dX as three steps of the
+  group that makes one call per step, bit for bit, formed and inline.
 """
 import pytest
 
@@ -225,3 +228,32 @@ def test_side_chains_merge_matches_one_call():
     assert len(out[0]) == len(out[1])
     for i, (a, b) in enumerate(zip(*out)):
         assert torch.equal(a, b), f"merged state {i} differs from one call"
+
+
+def test_open_finish_backward_matches_joined_steps():
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("FS side-class stream: steps with the adjoint and update left open vs one call per step")
+    hp = B.adamw(lr=1e-3)
+    out = {}
+    for mode in ("one", "open", "open_formed"):
+        blk = _block(98)  # the same linears each time
+        lins = [e["pl"] for e in blk]
+        form = mode == "open_formed"
+        g = PoetGroup(lins, side_chains=mode != "one", form_fs=form)
+        for _ in range(3):
+            g.build()
+            for e in blk:
+                pl = e["pl"]
+                keep = None if (form and pl.formed is not None) else e["W"]
+                pl.forward(e["Xd"], e["Y"], W_out=keep)
+                pl.backward_prims(e["Xd"], e["dYd"], e["dX"], W=keep)
+            g.finish_backward(join=mode == "one")
+            assert g._side_open == (mode != "one")
+            g.optimizer_step(hp)
+        torch.cuda.synchronize()
+        out[mode] = [t.clone() for e in blk for t in (e["pl"].thetaR, e["pl"].thetaP, e["pl"].mR, e["pl"].vP,
+                                                        e["Y"][:, :e["pl"].m], e["dX"][:, :e["pl"].n])]
+    for mode in ("open", "open_formed"):
+        for i, (a, b) in enumerate(zip(out["one"], out[mode])):
+            assert torch.equal(a, b), f"{mode}: state {i} differs from one call per step"
