@@ -280,13 +280,26 @@ def _merge_leg(B, torch, build, merge, nbytes, period):
     return ms_merge, info
 
 
+def side_linears(lins, args):
+    """The MLP linears of a POET-BS block (their sides are the same size as the attention linears', so no class of
+    sizes sets them apart): the group's side stream takes them, last in the step order."""
+    if args.side_linears == "none" or args.no_side_chains:
+        return None
+    from orthogonal_reparameterized_amd import binding as B
+    if not all(e["pl"].L.R.mode == B.POET_BS and e["pl"].L.P.mode == B.POET_BS for e in lins):
+        return None
+    idx = [i for i, e in enumerate(lins) if e["spec"].name in ("gate", "up", "down")]
+    return idx if 0 < len(idx) < len(lins) else None
+
+
 def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     """One block of 7 linears (or the single-linear workload): timed steps, profiled steps, merge leg."""
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
     group = None if args.no_group else PoetGroup([e["pl"] for e in lins], form_fs=not args.no_form,
                                                  form_streams=args.form_streams,
-                                                 side_chains=not args.no_side_chains)
+                                                 side_chains=not args.no_side_chains,
+                                                 side_linears=side_linears(lins, args))
     if group is not None:
         for e in lins:  # the group keeps the W it forms for FS pairs
             if id(e["pl"]) in group._formed:
@@ -471,7 +484,8 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
                        "dY": dYs[ldy]})
         layers.append(es)
         log(f"stack: layer {layer} allocated, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
-    gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]], not args.no_side_chains), 1),
+    sl = side_linears(layers[0], args)
+    gws = torch.empty(max(PoetGroup.workspace_bytes([e["pl"] for e in layers[0]], not args.no_side_chains, sl), 1),
                       dtype=torch.uint8, device="cuda")
     fws = None  # the formation streams' workspaces, shared by the groups (their builds run one after another)
     if form:
@@ -479,11 +493,11 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
         if fneed:
             fws = [torch.empty(fneed, dtype=torch.uint8, device="cuda") for _ in range(args.form_streams)]
     side = None  # the side stream and its workspace, shared by the groups (their calls run one after another)
-    sneed = PoetGroup.side_workspace_bytes([e["pl"] for e in layers[0]])
+    sneed = PoetGroup.side_workspace_bytes([e["pl"] for e in layers[0]], sl)
     if sneed and not args.no_side_chains:
         side = (torch.cuda.Stream(), torch.empty(sneed, dtype=torch.uint8, device="cuda"))
     groups = [PoetGroup([e["pl"] for e in es], ws=gws, form_fs=form, form_streams=args.form_streams, form_ws=fws,
-                        side_chains=not args.no_side_chains, side=side)
+                        side_chains=not args.no_side_chains, side=side, side_linears=sl)
               for es in layers]
     for grp in groups:  # the group's operand copies, folded weights and formed FS operands
         for W, Zr, Acp in grp._formed.values():
@@ -621,6 +635,9 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="join the side class's adjoint at the end of the backward (the default leaves it and the "
                          "class's AdamW update running on the side stream into the next step)")
+    ap.add_argument("--side-linears", default="mlp", choices=["mlp", "none"],
+                    help="POET-BS blocks: the MLP linears build, fold and run their adjoint on the side stream "
+                         "(POET-FS blocks take their wide primitives there by size)")
     ap.add_argument("--no-side-chains", action="store_true",
                     help="build and differentiate all sides of a group in one call per step (the default runs the "
                          "class of large primitives with the most product work, e.g. the MLP's s = 2730 POET-FS "

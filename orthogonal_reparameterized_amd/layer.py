@@ -440,7 +440,7 @@ class PoetGroup:
     float32 summation order of split products."""
 
     def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 2, form_ws=None,
-                 side_chains: bool = True, side=None):
+                 side_chains: bool = True, side=None, side_linears=None):
         """``ws`` (optional): a uint8 device tensor shared with other groups whose calls run one after another on one
         stream (``PoetGroup.workspace_bytes`` gives the size this group needs).
 
@@ -459,7 +459,11 @@ class PoetGroup:
         linears whose sides are all in the other classes can start their forward before that class is built. Each
         linear waits for its sides' build at its next use. ``side`` (optional): a (stream, uint8 device tensor) pair
         shared with other groups whose calls run one after another, the tensor of at least
-        ``PoetGroup.side_workspace_bytes`` bytes. The results are those of one grouped call per step, bit for bit."""
+        ``PoetGroup.side_workspace_bytes`` bytes. The results are those of one grouped call per step, bit for bit.
+
+        ``side_linears`` (optional, with ``side_chains``): indices into ``linears`` whose sides form the side class
+        instead, e.g. the MLP linears of a POET-BS block, whose sides are all one size (their folds then run on the
+        side stream too). Best taken from the end of the step order: their gradients come last."""
         torch = _torch()
         self.linears = list(linears)
         if not self.linears:
@@ -510,12 +514,17 @@ class PoetGroup:
                 for w in self._form_ws:
                     w.record_stream(s)
         # the side class: its sides' indices in self.sides (side 2i is linear i's R, 2i + 1 its P)
-        self._side_idx = PoetGroup._side_class(self.sides) if side_chains else []
+        if side_linears is not None:
+            sl = sorted(set(int(i) for i in side_linears))
+            if not sl or sl[0] < 0 or sl[-1] >= len(self.linears) or len(sl) == len(self.linears):
+                raise ValueError("side_linears must name some, not all, of the group's linears")
+        self._side_lin = sl if side_linears is not None else None
+        self._side_idx = (PoetGroup._side_class(self.sides, self._side_lin) if side_chains else [])
         self._main_idx = [i for i in range(len(self.sides)) if i not in set(self._side_idx)]
         self._side_stream = self._side_ws = self._side_event = None
         self._side_open = False  # a finish_backward(join=False) left the side class's gradient on the side stream
         if self._side_idx:
-            sneed = PoetGroup.side_workspace_bytes(self.linears)
+            sneed = PoetGroup.side_workspace_bytes(self.linears, self._side_lin)
             if side is None:
                 side = (torch.cuda.Stream(device=dev), torch.empty(max(sneed, 1), dtype=torch.uint8, device=dev))
             self._side_stream, self._side_ws = side
@@ -523,7 +532,7 @@ class PoetGroup:
                 raise ValueError(f"the side stream's calls of this group need a workspace of {sneed} bytes")
             self._side_ws.record_stream(self._side_stream)
             self._side_event = torch.cuda.Event()
-        need = PoetGroup.workspace_bytes(self.linears, side_chains)
+        need = PoetGroup.workspace_bytes(self.linears, side_chains, self._side_lin)
         if ws is None:
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         else:
@@ -551,9 +560,12 @@ class PoetGroup:
         return None
 
     @staticmethod
-    def _side_class(sides):
-        """Indices of the sides that build and run their adjoint on the side stream: the class of _chain_class with
-        the most product work (primitives x b^3 x k), when some side falls outside it; else none."""
+    def _side_class(sides, side_linears=None):
+        """Indices of the sides that build and run their adjoint on the side stream: both sides of the linears in
+        side_linears when given; else the class of _chain_class with the most product work (primitives x b^3 x k),
+        when some side falls outside it; else none."""
+        if side_linears is not None:
+            return [2 * i + r for i in side_linears for r in (0, 1)]
         classes = {}
         for i, s in enumerate(sides):
             classes.setdefault(PoetGroup._chain_class(s), []).append(i)
@@ -564,13 +576,17 @@ class PoetGroup:
         return classes[max(work)[1]]
 
     @staticmethod
-    def side_workspace_bytes(linears) -> int:
-        """Bytes of the workspace of the side stream's calls (build and adjoint of the side class); 0 without one."""
+    def side_workspace_bytes(linears, side_linears=None) -> int:
+        """Bytes of the workspace of the side stream's calls (build, folds and adjoint of the side class); 0 without
+        one."""
         sides = [s for pl in linears for s in (pl.L.R, pl.L.P)]
-        sub = [sides[i] for i in PoetGroup._side_class(sides)]
-        if not sub:
+        idx = PoetGroup._side_class(sides, side_linears)
+        if not idx:
             return 0
-        return max(B.poet_build_group_workspace_bytes(sub), B.poet_adjoint_group_workspace_bytes(sub))
+        sub = [sides[i] for i in idx]
+        act = [linears[j].L for j in sorted({i // 2 for i in idx}) if linears[j].act_path]
+        return max(B.poet_build_group_workspace_bytes(sub), B.poet_adjoint_group_workspace_bytes(sub),
+                   B.poet_fold_group_workspace_bytes(act) if act else 0)
 
     def _of(self, i, r, p):
         """Attribute r (side i is an R side) or p of the linear that side i belongs to."""
@@ -627,12 +643,12 @@ class PoetGroup:
         self._side_open = False
 
     @staticmethod
-    def workspace_bytes(linears, side_chains: bool = True) -> int:
+    def workspace_bytes(linears, side_chains: bool = True, side_linears=None) -> int:
         """Bytes of the workspace the grouped calls of these linears need on the launch stream (with
         ``side_chains``, the side class builds and runs its adjoint in a workspace of its own)."""
         sides = [s for pl in linears for s in (pl.L.R, pl.L.P)]
         if side_chains:
-            off = set(PoetGroup._side_class(sides))
+            off = set(PoetGroup._side_class(sides, side_linears))
             sides = [s for i, s in enumerate(sides) if i not in off]
         act = [pl for pl in linears if pl.act_path]
         return max(B.poet_build_group_workspace_bytes(sides), B.poet_adjoint_group_workspace_bytes(sides),
@@ -665,15 +681,25 @@ class PoetGroup:
         if self._formed:
             self._form(stream)
         act = [pl for pl in self.linears if pl.act_path and any(f is not None for f in self._fold[id(pl)])]
-        for pl in act:  # the folds read the primitives
-            pl._await_group(stream)
-        if act:
-            B.poet_fold_weights_group([pl.L for pl in act], [pl.W0b for pl in act], [pl.primR for pl in act],
-                                      [pl.primP for pl in act], [self._fold[id(pl)][0] for pl in act],
-                                      [self._fold[id(pl)][1] for pl in act], self.ws, stream,
-                                      opsRs=[pl.opsR for pl in act], opsPs=[pl.opsP for pl in act])
-            for pl in act:
+        # the folds read the primitives: those of linears with a side in the side class run on the side stream,
+        # after its build and the launch stream's (for the linear's other side)
+        on_side = {i // 2 for i in self._side_idx}
+        side_act = [pl for j, pl in enumerate(self.linears) if j in on_side and pl in act]
+        main_act = [pl for pl in act if not any(pl is q for q in side_act)]
+        for pls, st, ws, on in ((main_act, stream, self.ws, False), (side_act, self._side_stream, self._side_ws, True)):
+            if not pls:
+                continue
+            if on:
+                st.wait_stream(_torch_stream(stream, self.linears[0].dev))
+            B.poet_fold_weights_group([pl.L for pl in pls], [pl.W0b for pl in pls], [pl.primR for pl in pls],
+                                      [pl.primP for pl in pls], [self._fold[id(pl)][0] for pl in pls],
+                                      [self._fold[id(pl)][1] for pl in pls], ws, st,
+                                      opsRs=[pl.opsR for pl in pls], opsPs=[pl.opsP for pl in pls])
+            for pl in pls:
                 pl.W0P, pl.RW0 = self._fold[id(pl)]
+        if side_act:
+            self._record_side([t for pl in side_act for t in self._fold[id(pl)] + (pl.W0b, pl.opsR, pl.opsP)])
+            self._mark_side()
 
     def _form(self, stream):
         """Fork the formation streams from the build's stream and form every FS pair, round robin. The launch stream

@@ -110,3 +110,35 @@ def test_folded_group_matches_one_linear_calls_and_oracle():
                   theta_groups(lin.P.mode, lin.P.d, lin.P.b))
         finally:
             announce(f"fold {lin.name} (P folded {foldP}, R folded {foldR}): {errs}")
+
+
+def test_side_linears_pipelined_steps_match_one_call():
+    """PoetGroup(side_linears=...): the named linears build, fold and run their adjoint and AdamW update on the side
+    stream (finish_backward(join=False) leaves the last two open into the next step); three training steps end in
+    the same theta, moments, Y, Z and dX as three steps of one call per step on the launch stream, bit for bit."""
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("fold: side-stream linears, pipelined steps vs one call per step")
+    cases = [_linear(spec, i) for i, spec in enumerate(SPECS)]
+    hp = B.adamw(lr=1e-3)
+    out = []
+    for pick, open_ in ((lambda c: c[2], False), (lambda c: c[3], True)):
+        pls = [pick(c) for c in cases]
+        g = PoetGroup(pls, side_linears=[2, 3, 5]) if open_ else PoetGroup(pls, side_chains=False)
+        assert bool(g._side_idx) == open_
+        bufs = []
+        for (lin, (W0, tR, tP, X, dY), _, _), pl in zip(cases, pls):
+            bufs.append((put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldy),
+                         pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx)))
+        for _ in range(3):
+            g.build()
+            for pl, (Xd, dYd, Y, Z, dX) in zip(pls, bufs):
+                pl.forward_act(Xd, Y, Z)
+                pl.backward_act_prims(Xd, Z, dYd, dX)
+            g.finish_backward(join=not open_)
+            g.optimizer_step(hp)
+        torch.cuda.synchronize()
+        out.append([t.clone() for (lin, _, _, _), pl, (_, _, Y, Z, dX) in zip(cases, pls, bufs)
+                    for t in (pl.thetaR, pl.thetaP, pl.mR, pl.vP, Y[:, :lin.m], Z[:, :lin.m], dX[:, :lin.n])])
+    for i, (a, b) in enumerate(zip(*out)):
+        assert torch.equal(a, b), f"state {i} ({SPECS[i // 7][0]}) differs from one call per step"
