@@ -52,8 +52,73 @@ __device__ __forceinline__ void q_tile_pair(const float* __restrict__ theta, int
   }
 }
 
+// Q at row r, column cc of half h of a tile pair from the staged upper tile tr (zero at and below the diagonal
+// and past the primitive's size): h = 0 the tile (ti, tj), h = 1 its mirror (tj, ti) = -(ti, tj)^T; below the
+// diagonal of a diagonal tile, minus the transposed element (the values q_tile_pair gives, signed zeros included)
+__device__ __forceinline__ float q_of(const float (*tr)[33], int h, bool diag, int r, int cc) {
+  return (h || (diag && r > cc)) ? -tr[cc][r] : tr[r][cc];
+}
+
+// V consecutive elements of a row as one load or store (V = 4, 2 or 1; the caller checks alignment)
+template <int V>
+__device__ __forceinline__ void ld_row(const void* p, int dt, int64_t i, float (&o)[V]) {
+  if (dt == BF16) {
+    const __bf16* b = reinterpret_cast<const __bf16*>(p) + i;
+    if constexpr (V == 4) {
+      typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+      const v4 x = *reinterpret_cast<const v4*>(b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (float)x[e];
+    } else if constexpr (V == 2) {
+      typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+      const v2 x = *reinterpret_cast<const v2*>(b);
+      o[0] = (float)x[0]; o[1] = (float)x[1];
+    } else {
+      o[0] = (float)b[0];
+    }
+  } else {
+    const float* f = reinterpret_cast<const float*>(p) + i;
+    if constexpr (V == 4) {
+      const float4 x = *reinterpret_cast<const float4*>(f);
+      o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    } else if constexpr (V == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(f);
+      o[0] = x.x; o[1] = x.y;
+    } else {
+      o[0] = f[0];
+    }
+  }
+}
+template <int V>
+__device__ __forceinline__ void st_row(void* p, int dt, int64_t i, const float (&v)[V]) {
+  if (dt == BF16) {
+    __bf16* b = reinterpret_cast<__bf16*>(p) + i;
+    if constexpr (V == 4) {
+      typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+      v4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (__bf16)v[e];
+      *reinterpret_cast<v4*>(b) = x;
+    } else if constexpr (V == 2) {
+      typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+      v2 x;
+      x[0] = (__bf16)v[0]; x[1] = (__bf16)v[1];
+      *reinterpret_cast<v2*>(b) = x;
+    } else {
+      b[0] = (__bf16)v[0];
+    }
+  } else {
+    float* f = reinterpret_cast<float*>(p) + i;
+    if constexpr (V == 4) *reinterpret_cast<float4*>(f) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (V == 2) *reinterpret_cast<float2*>(f) = make_float2(v[0], v[1]);
+    else f[0] = v[0];
+  }
+}
+
 // prim = I + coef Q and the first saved power Q (dtype q_dt, row pitch ldq) of side blockIdx.z of the table,
-// primitive blockIdx.y, tile pair blockIdx.x
+// primitive blockIdx.y, tile pair blockIdx.x. A thread takes V consecutive columns of a row (32 / V threads per tile
+// row), so prim and Q leave as V-element stores where the row holds them.
+template <int V>
 __global__ __launch_bounds__(256) void k_theta_prep(const PrepGroup G) {
   __shared__ float tr[32][33];
   PrepSide a;
@@ -69,23 +134,36 @@ __global__ __launch_bounds__(256) void k_theta_prep(const PrepGroup G) {
   tile_pair_of(blockIdx.x, bp, ti, tj);
   const int c = prim_size(a.mode, a.d, bp, p);
   float up[4], lo[4];
-  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);
-  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;
+  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);  // stages the upper tile in tr
+  constexpr int TPR = 32 / V, RPP = 256 / TPR;
+  const int cv = (threadIdx.x % TPR) * V, r0 = threadIdx.x / TPR;
+  const bool diag = ti == tj;
   float* prim = a.prim + (int64_t)p * bp * bp;
-#pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (h == 1 && ti == tj) break;
+    if (h == 1 && diag) break;
     const int ri = h ? tj : ti, cj = h ? ti : tj;
+    for (int r = r0; r < 32; r += RPP) {
+      const int i = ri * 32 + r, j0 = cj * 32 + cv;
+      if (i >= bp || j0 >= bp) continue;
+      const int64_t e0 = (int64_t)i * bp + j0, o0 = ((int64_t)p * bp + i) * a.ldq + j0;
+      if (j0 + V <= bp) {
+        float q[V], pv[V];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = ri * 32 + row0 + 8 * u, j = cj * 32 + col;
-      if (i >= bp || j >= bp) continue;
-      const float q = h ? lo[u] : up[u];
-      prim[(int64_t)i * bp + j] = (i == j ? 1.f : 0.f) + a.coef * q;
-      if (a.q) {
-        const int64_t o = ((int64_t)p * bp + i) * a.ldq + j;
-        if (a.q_dt == BF16) reinterpret_cast<__bf16*>(a.q)[o] = (__bf16)q;
-        else reinterpret_cast<float*>(a.q)[o] = q;
+        for (int e = 0; e < V; ++e) {
+          q[e] = q_of(tr, h, diag, r, cv + e);
+          pv[e] = (i == j0 + e ? 1.f : 0.f) + a.coef * q[e];
+        }
+        st_row<V>(prim, F32, e0, pv);
+        if (a.q) st_row<V>(a.q, a.q_dt, o0, q);
+      } else {  // the last columns of a ragged block, one at a time
+        for (int e = 0; e < V && j0 + e < bp; ++e) {
+          const float q = q_of(tr, h, diag, r, cv + e);
+          prim[e0 + e] = (i == j0 + e ? 1.f : 0.f) + a.coef * q;
+          if (a.q) {
+            if (a.q_dt == BF16) reinterpret_cast<__bf16*>(a.q)[o0 + e] = (__bf16)q;
+            else reinterpret_cast<float*>(a.q)[o0 + e] = q;
+          }
+        }
       }
     }
   }
@@ -577,7 +655,10 @@ __global__ void k_adjoint_coefs(const CoefGroup G) {
 
 // prim = I + 2 Q + 2 (P_2 + ... + P_k) + P_{k+1}, where prim holds P_{k+1} on entry, Q comes from theta
 // (float32, exact) and P_t = powers[t-1] (dtype dt); k >= 1. Side blockIdx.z, primitive blockIdx.y, tile pair
-// blockIdx.x (the same tiling as k_theta_prep).
+// blockIdx.x (the same tiling as k_theta_prep). A thread takes V consecutive columns of a row (32 / V threads per
+// tile row), so the powers, prim and q2 move as V-element loads and stores where the row holds them; every
+// element's sum is formed in the same order as one element at a time.
+template <int V>
 __global__ __launch_bounds__(256) void k_chain_finalize(const FinGroup G) {
   __shared__ float tr[32][33];
   FinSide a;
@@ -593,32 +674,61 @@ __global__ __launch_bounds__(256) void k_chain_finalize(const FinGroup G) {
   tile_pair_of(blockIdx.x, bp, ti, tj);
   const int c = prim_size(a.mode, a.d, bp, p);
   float up[4], lo[4];
-  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);
-  const int col = threadIdx.x & 31, row0 = threadIdx.x >> 5;
+  q_tile_pair(a.theta, theta_off(bp, p), c, ti, tj, tr, up, lo);  // stages the upper tile in tr
+  constexpr int TPR = 32 / V, RPP = 256 / TPR;
+  const int cv = (threadIdx.x % TPR) * V, r0 = threadIdx.x / TPR;
+  const bool diag = ti == tj;
   float* prim = a.prim + (int64_t)p * bp * bp;
-#pragma unroll
+  const float* q2 = a.q2 ? a.q2 + (int64_t)p * bp * bp : nullptr;
   for (int h = 0; h < 2; ++h) {
-    if (h == 1 && ti == tj) break;
+    if (h == 1 && diag) break;
     const int ri = h ? tj : ti, cj = h ? ti : tj;
+    for (int r = r0; r < 32; r += RPP) {
+      const int i = ri * 32 + r, j0 = cj * 32 + cv;
+      if (i >= bp || j0 >= bp) continue;
+      const int64_t e0 = (int64_t)i * bp + j0;
+      if (j0 + V <= bp) {
+        float s2[V], x[V], v[V], pv[V];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = ri * 32 + row0 + 8 * u, j = cj * 32 + col;
-      if (i >= bp || j >= bp) continue;
-      float s2 = 0.f;
-      for (int t = a.q2 ? 3 : 2; t <= a.k; ++t)
-        s2 += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * a.nprim + p) * bp + i) * a.ldp + j);
-      const int64_t e = (int64_t)i * bp + j;
-      float v = (i == j ? 1.f : 0.f) + 2.f * (h ? lo[u] : up[u]) + 2.f * s2;
-      if (a.q2) {  // Q^2 = q2 / 4, coefficient 2 (k >= 2) or 1 (k == 1: the last term of the series)
-        v += (a.k >= 2 ? 0.5f : 0.25f) * a.q2[(int64_t)p * bp * bp + e];
-        if (a.k >= 2) v += prim[e];
-      } else {
-        v += prim[e];
+        for (int e = 0; e < V; ++e) s2[e] = 0.f;
+        for (int t = a.q2 ? 3 : 2; t <= a.k; ++t) {
+          ld_row<V>(a.powers, a.dt, (((int64_t)(t - 1) * a.nprim + p) * bp + i) * a.ldp + j0, x);
+#pragma unroll
+          for (int e = 0; e < V; ++e) s2[e] += x[e];
+        }
+        ld_row<V>(prim, F32, e0, pv);
+        if (q2) ld_row<V>(q2, F32, e0, x);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          v[e] = (i == j0 + e ? 1.f : 0.f) + 2.f * q_of(tr, h, diag, r, cv + e) + 2.f * s2[e];
+          if (q2) {
+            v[e] += (a.k >= 2 ? 0.5f : 0.25f) * x[e];
+            if (a.k >= 2) v[e] += pv[e];
+          } else {
+            v[e] += pv[e];
+          }
+        }
+        st_row<V>(prim, F32, e0, v);
+      } else {  // the last columns of a ragged block, one at a time
+        for (int e = 0; e < V && j0 + e < bp; ++e) {
+          const int j = j0 + e;
+          float s2 = 0.f;
+          for (int t = a.q2 ? 3 : 2; t <= a.k; ++t)
+            s2 += ld_dt(a.powers, a.dt, (((int64_t)(t - 1) * a.nprim + p) * bp + i) * a.ldp + j);
+          float v = (i == j ? 1.f : 0.f) + 2.f * q_of(tr, h, diag, r, cv + e) + 2.f * s2;
+          if (q2) {
+            v += (a.k >= 2 ? 0.5f : 0.25f) * q2[e0 + e];
+            if (a.k >= 2) v += prim[e0 + e];
+          } else {
+            v += prim[e0 + e];
+          }
+          prim[e0 + e] = v;
+        }
       }
-      prim[e] = v;
     }
   }
 }
+
 
 }  // namespace
 
@@ -638,8 +748,22 @@ hipError_t launch_chain_finalize_group(const FinGroup& g, hipStream_t st) {
   for (int i = 0; i < g.n; ++i) { bp = std::max(bp, g.s[i].bp); ny = std::max(ny, g.s[i].nprim); }
   if (ny > 65535) return hipErrorInvalidValue;
   const int nt = (bp + 31) / 32;
+  // V: the widest of 4, 2, 1 consecutive elements that every side's rows hold at aligned addresses
+  auto fits = [&](int V) {
+    for (int i = 0; i < g.n; ++i) {
+      const FinSide& a = g.s[i];
+      if (a.bp % V || a.ldp % V) return false;
+      if (reinterpret_cast<uintptr_t>(a.prim) % (4 * V) || reinterpret_cast<uintptr_t>(a.q2) % (4 * V) ||
+          reinterpret_cast<uintptr_t>(a.powers) % (dtype_size(a.dt) * V))
+        return false;
+    }
+    return true;
+  };
   ProfScope prof(7, st, 0, bytes);
-  hipLaunchKernelGGL(k_chain_finalize, dim3(nt * (nt + 1) / 2, ny, g.n), dim3(kThreads), 0, st, g);
+  const dim3 grid(nt * (nt + 1) / 2, ny, g.n);
+  if (fits(4)) hipLaunchKernelGGL(k_chain_finalize<4>, grid, dim3(kThreads), 0, st, g);
+  else if (fits(2)) hipLaunchKernelGGL(k_chain_finalize<2>, grid, dim3(kThreads), 0, st, g);
+  else hipLaunchKernelGGL(k_chain_finalize<1>, grid, dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 
@@ -729,8 +853,20 @@ hipError_t launch_theta_prep_group(const PrepGroup& g, hipStream_t st) {
   for (int i = 0; i < g.n; ++i) { bp = std::max(bp, g.s[i].bp); ny = std::max(ny, g.s[i].nprim); }
   if (ny > 65535) return hipErrorInvalidValue;
   const int nt = (bp + 31) / 32;
+  auto fits = [&](int V) {  // as in launch_chain_finalize_group
+    for (int i = 0; i < g.n; ++i) {
+      const PrepSide& a = g.s[i];
+      if (a.bp % V || (a.q && a.ldq % V)) return false;
+      if (reinterpret_cast<uintptr_t>(a.prim) % (4 * V) || reinterpret_cast<uintptr_t>(a.q) % (dtype_size(a.q_dt) * V))
+        return false;
+    }
+    return true;
+  };
   ProfScope prof(7, st, 0, bytes);
-  hipLaunchKernelGGL(k_theta_prep, dim3(nt * (nt + 1) / 2, ny, g.n), dim3(kThreads), 0, st, g);
+  const dim3 grid(nt * (nt + 1) / 2, ny, g.n);
+  if (fits(4)) hipLaunchKernelGGL(k_theta_prep<4>, grid, dim3(kThreads), 0, st, g);
+  else if (fits(2)) hipLaunchKernelGGL(k_theta_prep<2>, grid, dim3(kThreads), 0, st, g);
+  else hipLaunchKernelGGL(k_theta_prep<1>, grid, dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 

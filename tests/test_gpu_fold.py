@@ -142,3 +142,50 @@ def test_side_linears_pipelined_steps_match_one_call():
                     for t in (pl.thetaR, pl.thetaP, pl.mR, pl.vP, Y[:, :lin.m], Z[:, :lin.m], dX[:, :lin.n])])
     for i, (a, b) in enumerate(zip(*out)):
         assert torch.equal(a, b), f"state {i} ({SPECS[i // 7][0]}) differs from one call per step"
+
+
+def test_shared_side_stream_stack_then_merge_matches_one_call():
+    """Two groups (layers) sharing one workspace and one side stream with its workspace, as a stack runs them:
+    forward through both, backward in reverse with finish_backward(join=False) and the update per layer, two steps,
+    then a merge of each group. theta, moments, outputs and the merged W0 equal those of groups that make one call
+    per step on the launch stream, bit for bit."""
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("fold: two layers sharing one side stream, pipelined, then merge")
+    specs = SPECS[:4]
+    layers = [[_linear(spec, 10 * l + i) for i, spec in enumerate(specs)] for l in range(2)]
+    hp = B.adamw(lr=1e-3)
+    out = []
+    for use in (2, 3):  # the same linears twice: tuple slot 2 and slot 3 of each case
+        open_ = use == 3
+        pls = [[c[use] for c in cs] for cs in layers]
+        ws = torch.empty(max(PoetGroup.workspace_bytes(p, open_, [2, 3] if open_ else None) for p in pls),
+                         dtype=torch.uint8, device="cuda")
+        side = None
+        if open_:
+            sneed = max(PoetGroup.side_workspace_bytes(p, [2, 3]) for p in pls)
+            side = (torch.cuda.Stream(), torch.empty(sneed, dtype=torch.uint8, device="cuda"))
+        groups = [PoetGroup(p, ws=ws, side_linears=[2, 3], side=side) if open_ else
+                  PoetGroup(p, ws=ws, side_chains=False) for p in pls]
+        bufs = [[(put_act(pl, X, pl.L.ldx), put_act(pl, dY, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldy),
+                  pl.alloc_act(lin.T, pl.L.ldy), pl.alloc_act(lin.T, pl.L.ldx))
+                 for (lin, (W0, tR, tP, X, dY), _, _), pl in zip(cs, p)] for cs, p in zip(layers, pls)]
+        for _ in range(2):
+            for g, p, b in zip(groups, pls, bufs):
+                g.build()
+                for pl, (Xd, dYd, Y, Z, dX) in zip(p, b):
+                    pl.forward_act(Xd, Y, Z)
+            for g, p, b in zip(reversed(groups), reversed(pls), reversed(bufs)):
+                for pl, (Xd, dYd, Y, Z, dX) in zip(reversed(p), reversed(b)):
+                    pl.backward_act_prims(Xd, Z, dYd, dX)
+                g.finish_backward(join=not open_)
+                g.optimizer_step(hp)
+        state = [t.clone() for p, b in zip(pls, bufs) for pl, (_, _, Y, Z, dX) in zip(p, b)
+                 for t in (pl.thetaR, pl.thetaP, pl.mR, pl.vP, Y[:, :pl.m], Z[:, :pl.m], dX[:, :pl.n])]
+        for g in groups:
+            g.build()
+            g.merge()
+        torch.cuda.synchronize()
+        out.append(state + [pl.W0.clone() for p in pls for pl in p])
+    for i, (a, b) in enumerate(zip(*out)):
+        assert torch.equal(a, b), f"state {i} differs from one call per step"
