@@ -514,13 +514,15 @@ class PoetGroup:
                 for w in self._form_ws:
                     w.record_stream(s)
         # the side class: its sides' indices in self.sides (side 2i is linear i's R, 2i + 1 its P)
+        self._side_lin = None
         if side_linears is not None:
             sl = sorted(set(int(i) for i in side_linears))
             if not sl or sl[0] < 0 or sl[-1] >= len(self.linears) or len(sl) == len(self.linears):
                 raise ValueError("side_linears must name some, not all, of the group's linears")
-        self._side_lin = sl if side_linears is not None else None
-        self._side_idx = (PoetGroup._side_class(self.sides, self._side_lin) if side_chains else [])
-        self._main_idx = [i for i in range(len(self.sides)) if i not in set(self._side_idx)]
+            self._side_lin = sl
+        self._side_idx = PoetGroup._side_class(self.sides, self._side_lin) if side_chains else []
+        off = set(self._side_idx)
+        self._main_idx = [i for i in range(len(self.sides)) if i not in off]
         self._side_stream = self._side_ws = self._side_event = None
         self._side_open = False  # a finish_backward(join=False) left the side class's gradient on the side stream
         if self._side_idx:

@@ -99,3 +99,12 @@ def test_side_class_is_the_gemm_chain_class_with_the_most_work():
     assert PoetGroup._side_class([fs(2048)] * 4 + [fs(3072)]) == [0, 1, 2, 3]
     # a large POET-BS block size is a class of its own
     assert PoetGroup._side_class([B.side(B.POET_BS, 1024, 512, 3, B.POET_BF16)] * 2 + [fs(2048, k=3)]) == [2]
+
+
+def test_side_linears_must_name_some_not_all():
+    lins = [_cpu_linear(), _cpu_linear()]
+    for bad in ([], [0, 1], [2], [-1]):
+        with pytest.raises(ValueError, match="side_linears"):
+            PoetGroup(lins, side_linears=bad)
+    # both sides of each named linear; the class rule is not consulted
+    assert PoetGroup._side_class([lins[0].L.R, lins[0].L.P, lins[1].L.R, lins[1].L.P], [1]) == [2, 3]
