@@ -292,18 +292,24 @@ def side_linears(lins, args):
     return idx if 0 < len(idx) < len(lins) else None
 
 
+def block_group(lins, PoetGroup, args):
+    """The group the benchmark steps a block with (None with --no-group); linears whose FS pair the group forms
+    keep their W there."""
+    if args.no_group:
+        return None
+    group = PoetGroup([e["pl"] for e in lins], form_fs=not args.no_form, form_streams=args.form_streams,
+                      side_chains=not args.no_side_chains, side_linears=side_linears(lins, args))
+    for e in lins:
+        if id(e["pl"]) in group._formed:
+            e["keep"] = None
+    return group
+
+
 def run_block(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     """One block of 7 linears (or the single-linear workload): timed steps, profiled steps, merge leg."""
     log(f"workload {wl.name}: allocating")
     lins = build_block(wl, torch, B, PI, PoetLinear, args.path)
-    group = None if args.no_group else PoetGroup([e["pl"] for e in lins], form_fs=not args.no_form,
-                                                 form_streams=args.form_streams,
-                                                 side_chains=not args.no_side_chains,
-                                                 side_linears=side_linears(lins, args))
-    if group is not None:
-        for e in lins:  # the group keeps the W it forms for FS pairs
-            if id(e["pl"]) in group._formed:
-                e["keep"] = None
+    group = block_group(lins, PoetGroup, args)
     pipe = not args.no_pipeline
     torch.cuda.synchronize()
     log(f"warmup {args.warmup}")
@@ -602,7 +608,7 @@ def run_stack(wl, args, torch, B, PI, PoetLinear, PoetGroup):
     return res
 
 
-def main():
+def parser():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -648,7 +654,11 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy kernel of known size "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = parser().parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the POET layer path is single-GPU (data-parallel sharding is a "
               "design note only); rerun with --gpus 1", file=sys.stderr)

@@ -1,13 +1,17 @@
 """GPU parity of exactly the step the benchmark times, on whole LLaMA-1.3B blocks at full size.
 
-The block is made by ``bench.build_block`` and stepped by ``bench.step``, the same functions the benchmark's timed
-region calls, so the launch sequence checked here is the timed one:
+The block is made by ``bench.build_block``, grouped by ``bench.block_group`` with the benchmark's default flags
+and stepped by ``bench.step``, the same functions the benchmark's timed region calls, so the launch sequence
+checked here is the timed one:
 
-- POET-BS b = 256, k = 5 (the default workload): activation-side path, one grouped build of all 14 sides (which
-  writes the bf16 operand copies), grouped folds of P into W0 and of R into W0, per linear the folded forward and
-  the folded backward to the primitive gradients, one grouped Neumann adjoint of all 14 sides (152 blocks of 256);
-- POET-FS b = 1/2, k = 5: weight-side path, grouped build of the 14 FS chains (s = 1024 and 2730), per linear the
-  FS forward (materialized W) and the backward to the primitive gradients, one grouped adjoint;
+- POET-BS b = 256, k = 5 (the default workload): activation-side path, the grouped build of the attention
+  linears' 8 sides on the launch stream and of the MLP linears' 6 on the side stream (each writing the bf16 operand
+  copies), grouped folds of P into W0 and of R into W0 on each stream, per linear the folded forward and the folded
+  backward to the primitive gradients, the grouped Neumann adjoint of each class (152 blocks of 256), the MLP
+  class's adjoint and update left on the side stream as in the pipelined benchmark;
+- POET-FS b = 1/2, k = 5: weight-side path, grouped build of the 14 FS chains (s = 1024 on the launch stream, 2730
+  on the side stream), W and the FS gradient operands formed in the build on the formation streams, per linear the
+  forward and the backward to the primitive gradients from them, the grouped adjoint of each class;
 
 each step ending with the grouped AdamW update of every side's skew parameters; then the grouped
 merge-then-reinitialize of the whole block (``PoetGroup.merge``), as the benchmark's merge leg runs it (a build, then
@@ -73,15 +77,18 @@ def _block_as_benched(cfg_id):
     wl = PI.WORKLOADS[cfg_id]
     announce(f"bench path {wl.name}: allocating the block as the benchmark does")
     lins = bench.build_block(wl, torch, B, PI, PoetLinear, "auto")
-    group = PoetGroup([e["pl"] for e in lins])
+    args = bench.parser().parse_args([])
+    group = bench.block_group(lins, PoetGroup, args)
+    assert group._side_idx, "the benchmark's block has a side class"
+    pipe = not args.no_pipeline
     before = _state(lins)
     announce(f"bench path {wl.name}: step 1")
-    bench.step(lins, group)
+    bench.step(lins, group, pipeline=pipe)
     torch.cuda.synchronize()
     first, after = _outputs(lins), _state(lins)
     announce(f"bench path {wl.name}: step 2 from the same state (determinism)")
     _restore(lins, before, 0)
-    bench.step(lins, group)
+    bench.step(lins, group, pipeline=pipe)
     torch.cuda.synchronize()
     for e, a, b, c in zip(lins, first, _outputs(lins), _state(lins)):
         for x, y, nm in zip(a, b, ("Y", "dX", "dthetaR", "dthetaP")):
