@@ -257,3 +257,45 @@ def test_open_finish_backward_matches_joined_steps():
     for mode in ("open", "open_formed"):
         for i, (a, b) in enumerate(zip(out["one"], out[mode])):
             assert torch.equal(a, b), f"{mode}: state {i} differs from one call per step"
+
+
+def test_shared_side_stream_layers_match_one_call():
+    """Two layers (groups) of FS linears sharing one workspace, the formation workspaces, and one side stream with
+    its workspace, stepped as a stack: forward through both (FS operands formed in each build), backward in reverse
+    with finish_backward(join=False) and the update per layer, two steps. theta, moments, Y and dX equal those of
+    groups making one call per step with inline formation, bit for bit."""
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.layer import PoetGroup
+    announce("FS: two layers sharing one side stream, pipelined")
+    hp = B.adamw(lr=1e-3)
+    out = []
+    for open_ in (False, True):
+        layers = [_block(99)[:3], _block(100)[:3]]  # the FS linears of two blocks
+        pls = [[e["pl"] for e in blk] for blk in layers]
+        ws = torch.empty(max(PoetGroup.workspace_bytes(p, open_) for p in pls), dtype=torch.uint8, device="cuda")
+        kw = {}
+        if open_:
+            fneed = max(PoetGroup.form_workspace_bytes(p) for p in pls)
+            sneed = max(PoetGroup.side_workspace_bytes(p) for p in pls)
+            kw = dict(form_fs=True, form_ws=[torch.empty(fneed, dtype=torch.uint8, device="cuda") for _ in range(2)],
+                      side=(torch.cuda.Stream(), torch.empty(sneed, dtype=torch.uint8, device="cuda")))
+        groups = [PoetGroup(p, ws=ws, side_chains=open_, **kw) for p in pls]
+        assert all(bool(g._side_idx) == open_ for g in groups)
+        for _ in range(2):
+            for g, blk in zip(groups, layers):
+                g.build()
+                for e in blk:
+                    pl = e["pl"]
+                    pl.forward(e["Xd"], e["Y"], W_out=None if pl.formed is not None else e["W"])
+            for g, blk in zip(reversed(groups), reversed(layers)):
+                for e in reversed(blk):
+                    pl = e["pl"]
+                    pl.backward_prims(e["Xd"], e["dYd"], e["dX"], W=None if pl.formed is not None else e["W"])
+                g.finish_backward(join=not open_)
+                g.optimizer_step(hp)
+        torch.cuda.synchronize()
+        out.append([t.clone() for blk in layers for e in blk
+                    for t in (e["pl"].thetaR, e["pl"].thetaP, e["pl"].mR, e["pl"].vP, e["Y"][:, :e["pl"].m],
+                              e["dX"][:, :e["pl"].n])])
+    for i, (a, b) in enumerate(zip(*out)):
+        assert torch.equal(a, b), f"state {i} differs from one call per step"
