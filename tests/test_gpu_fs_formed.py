@@ -18,7 +18,8 @@ run the same kernels on the same values as the forward and backward that form th
   and the resampled index sets of a merge, whose build at the merge's precision also splits;
 - three training steps with finish_backward(join=False), which leaves the side class's adjoint and AdamW update on
   the side stream into the next step's build, end with the same theta, moments, Y and dX as three steps of the
-  group that makes one call per step, bit for bit, formed and inline.
+  group that makes one call per step, bit for bit, formed and inline; so do two layers stepped as a stack that
+  share one side stream and every workspace.
 """
 import pytest
 
