@@ -636,7 +636,7 @@ def parser():
                     help="form W and the FS gradient operands in each linear's forward and backward (the default "
                          "forms them for every weight-side POET-FS linear in the group build, overlapped on side "
                          "streams)")
-    ap.add_argument("--form-streams", type=int, default=2,
+    ap.add_argument("--form-streams", type=int, default=1,
                     help="side streams the group build forms the FS pairs on")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="join the side class's adjoint at the end of the backward (the default leaves it and the "

@@ -439,7 +439,7 @@ class PoetGroup:
     merge-then-reinitialize of every linear (poet_merge_group). Results match the per-linear calls up to the
     float32 summation order of split products."""
 
-    def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 2, form_ws=None,
+    def __init__(self, linears, ws=None, form_fs: bool = False, form_streams: int = 1, form_ws=None,
                  side_chains: bool = True, side=None, side_linears=None):
         """``ws`` (optional): a uint8 device tensor shared with other groups whose calls run one after another on one
         stream (``PoetGroup.workspace_bytes`` gives the size this group needs).
