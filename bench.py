@@ -288,7 +288,8 @@ def side_linears(lins, args):
     from orthogonal_reparameterized_amd import binding as B
     if not all(e["pl"].L.R.mode == B.POET_BS and e["pl"].L.P.mode == B.POET_BS for e in lins):
         return None
-    idx = [i for i, e in enumerate(lins) if e["spec"].name in ("gate", "up", "down")]
+    names = ("gate", "up", "down") if args.side_linears == "mlp" else tuple(args.side_linears.split(","))
+    idx = [i for i, e in enumerate(lins) if e["spec"].name in names]
     return idx if 0 < len(idx) < len(lins) else None
 
 
@@ -641,9 +642,10 @@ def parser():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="join the side class's adjoint at the end of the backward (the default leaves it and the "
                          "class's AdamW update running on the side stream into the next step)")
-    ap.add_argument("--side-linears", default="mlp", choices=["mlp", "none"],
-                    help="POET-BS blocks: the MLP linears build, fold and run their adjoint on the side stream "
-                         "(POET-FS blocks take their wide primitives there by size)")
+    ap.add_argument("--side-linears", default="mlp",
+                    help="POET-BS blocks: the linears that build, fold and run their adjoint on the side stream: "
+                         "mlp (gate, up, down), none, or a comma-separated list of names (POET-FS blocks take their "
+                         "wide primitives there by size)")
     ap.add_argument("--no-side-chains", action="store_true",
                     help="build and differentiate all sides of a group in one call per step (the default runs the "
                          "class of large primitives with the most product work, e.g. the MLP's s = 2730 POET-FS "
