@@ -6,9 +6,9 @@ amortized over its period.
 Prints one JSON line: whole-job tokens/s (inputs resident in HBM), the roofline of the dominant kernel measured
 live with HIP events on the launch stream, and the CPU oracle timed on a bounded sample of the same workload.
 The default run (the LLaMA-1.3B POET-BS block) also times the LLaMA-1.3B POET-FS block and reports it under
-"fs_block" (skip with --no-fs).
+"fs_block" (skip with --no-fs), and the LLaMA-3B 24-layer POET-FS stack under "stack_3b" (skip with --no-stack).
 
-  python bench.py [--steps K] [--warmup W] [--workload 3|4|5|2|1] [--no-cpu-baseline] [--no-fs]
+  python bench.py [--steps K] [--warmup W] [--workload 3|4|5|2|1] [--no-cpu-baseline] [--no-fs] [--no-stack]
 """
 from __future__ import annotations
 
@@ -625,6 +625,10 @@ def parser():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fs", action="store_true",
                     help="with the default workload, skip the extra LLaMA-1.3B POET-FS block measurement")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="with the default workload, skip the extra LLaMA-3B 24-layer POET-FS stack measurement")
+    ap.add_argument("--stack-steps", type=int, default=5,
+                    help="timed steps of the extra LLaMA-3B stack measurement (its warmup is 2 steps)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (the default launches every step)")
     ap.add_argument("--path", default="auto", choices=["auto", "weight", "act"],
@@ -695,9 +699,17 @@ def main():
         log("extra: the POET-FS block")
         r4 = run_block(fs, args, torch, B, PI, PoetLinear, PoetGroup)
         out["fs_block"] = {"unit": "tokens/s", **r4}
+    if args.workload == 3 and args.layers <= 1 and not args.no_stack and not args.permuted:
+        # the LLaMA-3B 24-layer POET-FS stack at 32768 tokens, every layer resident (about 72 GiB), with fewer
+        # steps than the block: one step takes about half a second
+        log("extra: the LLaMA-3B 24-layer POET-FS stack")
+        sargs = argparse.Namespace(**vars(args))
+        sargs.steps, sargs.warmup, sargs.layers = max(1, args.stack_steps), min(args.warmup, 2), 0
+        r5 = run_stack(PI.WORKLOADS[5], sargs, torch, B, PI, PoetLinear, PoetGroup)
+        out["stack_3b"] = {"unit": "tokens/s", "steps": sargs.steps, "warmup": sargs.warmup, **r5}
     log("matrix-core probe")
     out["mfma_probe"] = mfma_probe(torch, B)
-    for r in [out["roofline"]] + ([out["fs_block"]["roofline"]] if "fs_block" in out else []):
+    for r in [out["roofline"]] + [out[k]["roofline"] for k in ("fs_block", "stack_3b") if k in out]:
         if r.get("peak") == PEAK_BF16_TFLOPS and out["mfma_probe"]["achieved"] > 0:
             r["frac_of_sustained"] = round(r["achieved"] / out["mfma_probe"]["achieved"], 4)
     if args.calib_copy_mib > 0:
