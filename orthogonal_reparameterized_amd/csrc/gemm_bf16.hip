@@ -56,7 +56,11 @@ struct GroupEntry {
   int b0 = 0, Mtot = 0, Ntot = 0, pad = 0;
 };
 
-struct FastArgs {
+// Kernel arguments, passed by value. NP is the capacity of the problem table: MAXGP for grouped launches, 1 for
+// the others (a single-problem launch carries no 1 KB table: the runtime stages every launch's arguments, and a
+// stream of many small launches with large arguments stalls the host's enqueue until that stream drains).
+template <int NP>
+struct FastArgsT {
   GemmDesc g;
   int ntm, ntn, splits, kchunk;
   int use_part;  // write float32 partial tiles; a second kernel reduces them and applies the epilogue
@@ -64,7 +68,7 @@ struct FastArgs {
   // entries [prob[p].b0, prob[p + 1].b0) and reads / writes its operands at byte offsets from g's, with its own
   // leading dimensions and extents
   int nprob = 0;
-  GroupEntry prob[MAXGP];
+  GroupEntry prob[NP];
 };
 
 // an epilogue the main kernel stores directly: out = acc into C (no addend, scale, second copy or accumulate)
@@ -334,7 +338,7 @@ __device__ __forceinline__ void store_mirror(const f32x16 (&acc)[WM][WN], char* 
 }
 
 // TAG only separates kernel symbols for profiling: 1, 2, 3 = the token GEMMs Y, dX, G; 0 = everything else.
-// GROUP: the launch holds several problems of one shape (FastArgs nprob and prob).
+// GROUP: the launch holds several problems of one shape (nprob and prob of the arguments).
 // Waves per workgroup and their grid over the 256 x 256 tile. Eight waves (two per SIMD, wave tile 128 x 64) measured
 // 7-12% faster than four (one per SIMD, 128 x 128) on every token-GEMM shape, bit-identical: with one wave per SIMD
 // each barrier and copy wait stalls the matrix core, while a second wave keeps issuing MFMAs (sixteen waves, 64 x 64,
@@ -348,7 +352,7 @@ constexpr int smem_bytes(int nw) {
 }
 
 template <bool AK, bool BK_, int TAG, bool GROUP = false, int NW = KNW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(const FastArgs fa_) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(const FastArgsT<GROUP ? MAXGP : 1> fa_) {
   constexpr int WM = 8 / WaveGrid<NW>::GR, WN = 8 / WaveGrid<NW>::GC;  // 32 x 32 blocks per wave
   constexpr int NDMA = 32 / NW;        // DMA instructions per operand per wave and tile
   __shared__ __attribute__((aligned(1024))) char smem[smem_bytes(NW)];
@@ -554,7 +558,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // Sum the split-K partials of every output element in split order, then apply the epilogue.
 // Work item: four adjacent columns of one partial row (one column where N is not a multiple of 4), read from every
 // split as one 16-byte load; 32-bit indices (the partials of one launch are far below 2^31 elements).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgs fa_) {
+template <int NP>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const FastArgsT<NP> fa_) {
   const GemmDesc& g = fa_.g;
   const int64_t mn = (int64_t)g.M * g.N;
   const bool v4 = (g.N & 3) == 0;
@@ -633,7 +638,7 @@ int fast_gemm_splits(const GemmDesc& g) {
 
 hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  FastArgs fa;
+  FastArgsT<1> fa;
   fa.g = g;
   fa.ntm = (g.M + BM - 1) / BM;
   fa.ntn = (g.N + BN - 1) / BN;
@@ -663,7 +668,7 @@ hipError_t launch_fast_gemm(const GemmDesc& g, hipStream_t st) {
   if (e != hipSuccess || !fa.use_part || g.defer_reduce) return e;
   const int64_t total = (int64_t)g.batch * g.M * (g.N % 4 == 0 ? g.N / 4 : g.N);
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
+  hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(rg), dim3(256), 0, st, fa);
   return hipGetLastError();
 }
 
@@ -692,7 +697,7 @@ bool fast_gemm_pair_eligible(const GemmDesc& a, const GemmDesc& b) {
 hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   GemmDesc g = pr[0];
   g.batch = 0;
-  FastArgs fa;
+  FastArgsT<MAXGP> fa;
   fa.nprob = n;
   for (int i = 0; i < n; ++i) {
     GroupEntry& e = fa.prob[i];
@@ -727,7 +732,7 @@ hipError_t launch_fast_gemm_group(const GemmDesc* pr, int n, hipStream_t st) {
   if (e != hipSuccess || !fa.use_part) return e;
   const int64_t total = (int64_t)g.batch * g.M * (g.N % 4 == 0 ? g.N / 4 : g.N);
   const int rg = (int)std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rg), dim3(256), 0, st, fa);
+  hipLaunchKernelGGL(splitk_reduce_kernel<MAXGP>, dim3(rg), dim3(256), 0, st, fa);
   return hipGetLastError();
 }
 
