@@ -618,7 +618,7 @@ int fast_gemm_splits(const GemmDesc& g) {
   // Split K only where it shortens the launch. A work item (one output tile, nk / S K-tiles) holds one CU (256 CUs,
   // one workgroup each), so the items take ceil(tiles S / 256) rounds of about nk / S + 1.5 K-tile times (the 1.5
   // is the pipeline fill and the epilogue). S > 1 adds float32 partials, written by the items and read back by the
-  // reduction: about 8 S + 4 bytes per output element, counted at one K-tile time per 10 MB. Candidates keep at
+  // reduction: about 8 S + 4 bytes per output element, counted at one K-tile time per 5 MB. Candidates keep at
   // least two K-tiles per split and fit the scratch the caller provided; a larger S must win by 3% or more.
   if (g.tri) return 1;  // the tiles on and above the diagonal store their mirror tiles themselves: no partials
   const int tiles = g.batch * ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -630,7 +630,7 @@ int fast_gemm_splits(const GemmDesc& g) {
     if (S > 1 && (!g.part || nk < 2 * S || (size_t)S * (size_t)outs > g.part_elems)) break;
     const double rounds = std::ceil((double)tiles * S / 256.0);
     double cost = rounds * ((double)nk / S + 1.5);
-    if (S > 1) cost += (8.0 * S + 4.0) * outs / 10.0e6;
+    if (S > 1) cost += (8.0 * S + 4.0) * outs / 5.0e6;
     if (S == 1 || cost < 0.97 * best) { best = cost; best_s = S; }
   }
   return best_s;
